@@ -1,0 +1,140 @@
+"""ctypes binding of ``libhisparse.so`` (the C ABI declared in include/hs.h).
+
+Argument marshalling only: every function takes torch tensors (device memory,
+or pinned host memory for the host pool), passes their addresses and sizes to
+the library, and raises ``HsError`` on a nonzero status.  All work runs in the
+library's HIP kernels on the given stream (torch's current stream by
+default).  Loading fails loudly if the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().parent / "libhisparse.so"
+
+HS_F32, HS_BF16, HS_E4M3 = 0, 1, 2
+DTYPES = {"f32": HS_F32, "bf16": HS_BF16, "e4m3": HS_E4M3}
+HS_OP_INDEXER, HS_OP_TOPK, HS_OP_RESOLVE, HS_OP_MLA = 0, 1, 2, 3
+DEVERR_VICTIMS, DEVERR_NO_HOST = 1, 2
+
+EXPORTS = ["hs_indexer_scores", "hs_topk", "hs_resolve_rows", "hs_sparse_mla_decode",
+           "hs_workspace_bytes", "hs_host_device_ptr", "hs_last_error", "hs_abi_version"]
+
+
+class HsError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"hs status {status}: {msg}")
+        self.status = status
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("P", c_int32), ("T_stride", c_int32), ("max_blocks", c_int32),
+                ("ctx_len", c_void_p)]
+
+
+class Residency(ctypes.Structure):
+    _fields_ = [("C", c_int32), ("L", c_int32), ("kv_t", c_int32), ("pad_", c_int32),
+                ("pool_layer_rows", c_int64), ("host_layer_rows", c_int64),
+                ("bt", c_void_p), ("hot_blocks", c_void_p), ("tok2slot", c_void_p),
+                ("slot2tok", c_void_p), ("stamp", c_void_p), ("step", c_void_p),
+                ("err", c_void_p), ("pool", c_void_p), ("row_scale", c_void_p),
+                ("host_rows", c_void_p), ("host_scale", c_void_p), ("host_bt", c_void_p)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """The loaded library (raises ImportError if it was never built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise ImportError(f"{LIB_PATH} not found: build it with "
+                          "`python -m decode_indexer_logits_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    P = c_void_p
+    lib.hs_indexer_scores.argtypes = [P, c_int32, c_int32, c_int32, P, P, c_int32, P, P, P, P, P, P]
+    lib.hs_topk.argtypes = [P, c_int32, P, P, P, c_size_t, P]
+    lib.hs_resolve_rows.argtypes = [P, c_int32, P, P, P, P, P, P, c_size_t, P]
+    lib.hs_sparse_mla_decode.argtypes = [P, c_int32, c_int32, c_int32, P, c_int32, P, P, P,
+                                         c_float, P, P, P, c_size_t, P]
+    for f in ("hs_indexer_scores", "hs_topk", "hs_resolve_rows", "hs_sparse_mla_decode",
+              "hs_host_device_ptr"):
+        getattr(lib, f).restype = c_int32
+    lib.hs_workspace_bytes.argtypes = [c_int32] * 6
+    lib.hs_workspace_bytes.restype = c_size_t
+    lib.hs_host_device_ptr.argtypes = [P, ctypes.POINTER(c_void_p)]
+    lib.hs_last_error.restype = ctypes.c_char_p
+    lib.hs_abi_version.restype = c_int32
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(st: int):
+    if st != 0:
+        raise HsError(st, load().hs_last_error().decode())
+
+
+def abi_version() -> int:
+    return load().hs_abi_version()
+
+
+def last_error() -> str:
+    return load().hs_last_error().decode()
+
+
+def workspace_bytes(op: int, B: int, P: int, T_stride: int, K: int, Hq: int = 16) -> int:
+    return load().hs_workspace_bytes(op, B, P, T_stride, K, Hq)
+
+
+def host_device_ptr(pinned) -> int:
+    out = c_void_p()
+    _check(load().hs_host_device_ptr(pinned.data_ptr(), ctypes.byref(out)))
+    return out.value
+
+
+def make_batch(B: int, P: int, T_stride: int, ctx_len) -> Batch:
+    return Batch(B, P, T_stride, T_stride // 64, _ptr(ctx_len))
+
+
+def indexer_scores(batch: Batch, H: int, D: int, q_t: str, q_idx, w, k_t: str, idx_pool,
+                   idx_scale, idx_bt, bias, scores, stream=None):
+    _check(load().hs_indexer_scores(ctypes.byref(batch), H, D, DTYPES[q_t], _ptr(q_idx), _ptr(w),
+                                    DTYPES[k_t], _ptr(idx_pool), _ptr(idx_scale), _ptr(idx_bt),
+                                    _ptr(bias), _ptr(scores), _stream(stream)))
+
+
+def topk(batch: Batch, K: int, scores, out, ws, stream=None):
+    _check(load().hs_topk(ctypes.byref(batch), K, _ptr(scores), _ptr(out), _ptr(ws),
+                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def resolve_rows(batch: Batch, K: int, topk_t, res: Residency, row_ids, faults, counts,
+                 stream=None):
+    _check(load().hs_resolve_rows(ctypes.byref(batch), K, _ptr(topk_t), ctypes.byref(res),
+                                  _ptr(row_ids), _ptr(faults), _ptr(counts), None, 0,
+                                  _stream(stream)))
+
+
+def sparse_mla_decode(batch: Batch, K: int, Hq: int, q_t: str, q, kv_t: str, pool, row_scale,
+                      row_ids, sm_scale: float, out, lse, ws, stream=None):
+    _check(load().hs_sparse_mla_decode(ctypes.byref(batch), K, Hq, DTYPES[q_t], _ptr(q),
+                                       DTYPES[kv_t], _ptr(pool), _ptr(row_scale), _ptr(row_ids),
+                                       float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                       0 if ws is None else ws.numel() * ws.element_size(),
+                                       _stream(stream)))

@@ -1,0 +1,219 @@
+// C ABI of the decode step: host-side argument checks, then kernel launches.
+// Nothing here allocates, synchronizes, reads device memory or issues a
+// memset, so every entry point can be recorded into a HIP graph.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/hs.h"
+#include "hs_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hs_status fail(hs_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hs_status check_batch(const hs_batch* b, hs::BatchDims* d) {
+  if (!b) return fail(HS_ERR_NULL, "batch is NULL");
+  if (!b->ctx_len) return fail(HS_ERR_NULL, "batch.ctx_len is NULL");
+  if (b->B < 1 || b->B > 65535) return fail(HS_ERR_SHAPE, "B=%d out of [1, 65535]", b->B);
+  if (b->P < 1 || b->P > 4) return fail(HS_ERR_SHAPE, "P=%d out of [1, 4]", b->P);
+  if (b->T_stride < 64 || b->T_stride > (1 << 24) || b->T_stride % 64)
+    return fail(HS_ERR_SHAPE, "T_stride=%d must be a multiple of 64 in [64, 2^24]", b->T_stride);
+  if (b->max_blocks != b->T_stride / 64)
+    return fail(HS_ERR_SHAPE, "max_blocks=%d must equal T_stride/64=%d", b->max_blocks,
+                b->T_stride / 64);
+  d->B = b->B;
+  d->P = b->P;
+  d->T_stride = b->T_stride;
+  d->max_blocks = b->max_blocks;
+  d->ctx_len = b->ctx_len;
+  return HS_OK;
+}
+
+hs_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(HS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = 0;
+  return HS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_indexer_scores(const hs_batch* batch, int32_t H_idx, int32_t D_idx, hs_dtype q_t,
+                            const void* q_idx, const float* w, hs_dtype k_t,
+                            const void* idx_pool, const float* idx_scale, const int32_t* idx_bt,
+                            const float* bias, float* scores, void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!q_idx || !w || !idx_pool || !idx_bt || !scores)
+    return fail(HS_ERR_NULL, "hs_indexer_scores: q_idx, w, idx_pool, idx_bt and scores are required");
+  if (D_idx != 64 && D_idx != 128) return fail(HS_ERR_SHAPE, "D_idx=%d must be 64 or 128", D_idx);
+  if (!aligned16(q_idx) || !aligned16(idx_pool) || !aligned16(scores))
+    return fail(HS_ERR_ALIGN, "hs_indexer_scores: q_idx, idx_pool and scores need 16-byte alignment");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (q_t == HS_BF16 && k_t == HS_E4M3) {
+    if (H_idx < 16 || H_idx > 64 || H_idx % 16)
+      return fail(HS_ERR_SHAPE, "H_idx=%d must be 16, 32, 48 or 64 on the bf16/e4m3 path", H_idx);
+    return launched(hs::launch_indexer_bf16_e4m3(d, H_idx, D_idx, static_cast<const uint16_t*>(q_idx),
+                                                 w, static_cast<const uint8_t*>(idx_pool), idx_scale,
+                                                 idx_bt, bias, scores, s),
+                    "indexer");
+  }
+  if (q_t == HS_F32 && k_t == HS_F32) {
+    if (H_idx < 1 || H_idx > 64) return fail(HS_ERR_SHAPE, "H_idx=%d out of [1, 64]", H_idx);
+    if (idx_scale) return fail(HS_ERR_DTYPE, "fp32 keys take no scale (idx_scale must be NULL)");
+    return launched(hs::launch_indexer_f32(d, H_idx, D_idx, static_cast<const float*>(q_idx), w,
+                                           static_cast<const float*>(idx_pool), idx_bt, bias,
+                                           scores, s),
+                    "indexer");
+  }
+  return fail(HS_ERR_DTYPE, "indexer supports (q, k) = (BF16, E4M3) or (F32, F32)");
+}
+
+hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t* topk, void* ws,
+                  size_t ws_bytes, void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!scores || !topk) return fail(HS_ERR_NULL, "hs_topk: scores and topk are required");
+  if (K < 1 || K > 8192) return fail(HS_ERR_SHAPE, "K=%d out of [1, 8192]", K);
+  const size_t need = hs::topk_workspace_bytes(d.B, d.P, d.T_stride, K);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "hs_topk needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace needs 16-byte alignment");
+  return launched(hs::launch_topk(d, K, scores, topk, ws, static_cast<hipStream_t>(stream)), "topk");
+}
+
+hs_status hs_resolve_rows(const hs_batch* batch, int32_t K, const int32_t* topk,
+                          const hs_residency* res, int32_t* row_ids, int32_t* faults,
+                          int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!topk || !res || !row_ids || !faults || !counts)
+    return fail(HS_ERR_NULL, "hs_resolve_rows: topk, res, row_ids, faults and counts are required");
+  if (K < 1 || d.P * K > 8192) return fail(HS_ERR_SHAPE, "P*K=%d out of [1, 8192]", d.P * K);
+  if (!res->bt || !res->step || !res->err || !res->pool)
+    return fail(HS_ERR_NULL, "residency: bt, step, err and pool are required");
+  if (res->L < 1 || res->L > 16) return fail(HS_ERR_SHAPE, "L=%d out of [1, 16]", res->L);
+  if (res->C < 0 || res->C % 64 || res->C > (1 << 20))
+    return fail(HS_ERR_SHAPE, "C=%d must be a multiple of 64 (0 = no hot buffers)", res->C);
+  if (res->C > 0 && res->C < d.P * K)
+    return fail(HS_ERR_CAPACITY, "C=%d below P*K=%d: a step's faults could exceed its victims",
+                res->C, d.P * K);
+  if (res->C > 0 && (!res->hot_blocks || !res->tok2slot || !res->slot2tok || !res->stamp))
+    return fail(HS_ERR_NULL, "residency: hot_blocks, tok2slot, slot2tok and stamp are required when C > 0");
+  int kv_bytes;
+  if (res->kv_t == HS_E4M3) {
+    kv_bytes = 1;
+    if (!res->row_scale) return fail(HS_ERR_NULL, "E4M3 rows need row_scale");
+    if (res->host_rows && !res->host_scale) return fail(HS_ERR_NULL, "E4M3 host rows need host_scale");
+  } else if (res->kv_t == HS_F32) {
+    kv_bytes = 4;
+    if (res->row_scale || res->host_scale) return fail(HS_ERR_DTYPE, "F32 rows take no scales");
+  } else {
+    return fail(HS_ERR_DTYPE, "residency kv_t must be E4M3 or F32");
+  }
+  if (res->host_rows && !res->host_bt) return fail(HS_ERR_NULL, "host_rows given without host_bt");
+  if (res->C > 0 && res->host_bt && !res->host_rows)
+    return fail(HS_ERR_NULL, "host_bt given without host_rows");
+  if (!aligned16(res->pool) || (res->host_rows && !aligned16(res->host_rows)))
+    return fail(HS_ERR_ALIGN, "pool and host_rows need 16-byte alignment");
+  if (res->pool_layer_rows < 0 || res->host_layer_rows < 0)
+    return fail(HS_ERR_SHAPE, "layer strides must be non-negative");
+  hs::ResidencyArgs r;
+  r.C = res->C;
+  r.L = res->L;
+  r.kv_bytes = kv_bytes;
+  r.pool_layer_rows = res->pool_layer_rows;
+  r.host_layer_rows = res->host_layer_rows;
+  r.bt = res->bt;
+  r.hot_blocks = res->hot_blocks;
+  r.tok2slot = res->tok2slot;
+  r.slot2tok = res->slot2tok;
+  r.stamp = res->stamp;
+  r.step = res->step;
+  r.err = res->err;
+  r.pool = res->pool;
+  r.row_scale = res->row_scale;
+  r.host_rows = res->host_rows;
+  r.host_scale = res->host_scale;
+  r.host_bt = res->host_bt;
+  return launched(hs::launch_resolve(d, K, topk, r, row_ids, faults, counts,
+                                     static_cast<hipStream_t>(stream)),
+                  "resolve");
+}
+
+hs_status hs_sparse_mla_decode(const hs_batch* batch, int32_t K, int32_t Hq, hs_dtype q_t,
+                               const void* q, hs_dtype kv_t, const void* pool,
+                               const float* row_scale, const int32_t* row_ids, float sm_scale,
+                               float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!q || !pool || !row_ids || !out)
+    return fail(HS_ERR_NULL, "hs_sparse_mla_decode: q, pool, row_ids and out are required");
+  if (K < 1 || K > 8192) return fail(HS_ERR_SHAPE, "K=%d out of [1, 8192]", K);
+  if (Hq != 16) return fail(HS_ERR_SHAPE, "Hq=%d: one shard of 16 heads per call", Hq);
+  if (!aligned16(q) || !aligned16(pool) || !aligned16(out))
+    return fail(HS_ERR_ALIGN, "q, pool and out need 16-byte alignment");
+  const size_t need = hs::mla_workspace_bytes(d.B, d.P, K, Hq);
+  if (need && (!ws || ws_bytes < need))
+    return fail(HS_ERR_WORKSPACE, "hs_sparse_mla_decode needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  if (need && !aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace needs 16-byte alignment");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (q_t == HS_BF16 && kv_t == HS_E4M3) {
+    if (!row_scale) return fail(HS_ERR_NULL, "E4M3 rows need row_scale");
+    return launched(hs::launch_mla_bf16_e4m3(d, K, static_cast<const uint16_t*>(q),
+                                             static_cast<const uint8_t*>(pool), row_scale, row_ids,
+                                             sm_scale, out, lse, ws, s),
+                    "sparse_mla");
+  }
+  if (q_t == HS_F32 && kv_t == HS_F32) {
+    if (row_scale) return fail(HS_ERR_DTYPE, "F32 rows take no row_scale");
+    return launched(hs::launch_mla_f32(d, K, static_cast<const float*>(q),
+                                       static_cast<const float*>(pool), row_ids, sm_scale, out,
+                                       lse, ws, s),
+                    "sparse_mla");
+  }
+  return fail(HS_ERR_DTYPE, "sparse MLA supports (q, kv) = (BF16, E4M3) or (F32, F32)");
+}
+
+size_t hs_workspace_bytes(int32_t op, int32_t B, int32_t P, int32_t T_stride, int32_t K,
+                          int32_t Hq) {
+  if (B < 1 || P < 1 || K < 1) return 0;
+  switch (op) {
+    case HS_OP_TOPK: return hs::topk_workspace_bytes(B, P, T_stride, K);
+    case HS_OP_MLA: return hs::mla_workspace_bytes(B, P, K, Hq);
+    default: return 0;
+  }
+}
+
+hs_status hs_host_device_ptr(const void* pinned_host, const void** dev_ptr) {
+  if (!pinned_host || !dev_ptr) return fail(HS_ERR_NULL, "hs_host_device_ptr: NULL argument");
+  void* dp = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&dp, const_cast<void*>(pinned_host), 0);
+  if (e != hipSuccess) return fail(HS_ERR_HIP, "hipHostGetDevicePointer: %s", hipGetErrorString(e));
+  *dev_ptr = dp;
+  g_err[0] = 0;
+  return HS_OK;
+}
+
+const char* hs_last_error(void) { return g_err; }
+
+int32_t hs_abi_version(void) { return HS_ABI_VERSION; }
+
+}  // extern "C"

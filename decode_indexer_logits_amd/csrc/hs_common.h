@@ -1,0 +1,104 @@
+// Device-side helpers shared by the gfx950 kernels of the decode step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs {
+
+constexpr int kBlock = 64;      // tokens per page
+constexpr int kDLat = 576;      // latent row: 512 compressed + 64 rotary
+constexpr int kDVal = 512;      // value part of a latent row
+constexpr int kWave = 64;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+// Two OCP E4M3FN codes (bytes 0,1 of `w`, or bytes 2,3 when `hi`) -> two bf16
+// packed in one dword.  Every E4M3 value is exact in bf16 (3 mantissa bits,
+// exponents 2^-9 .. 2^8), so taking the upper half of the fp32 is exact.
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
+  f32x2_t f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true)
+                 : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+}
+
+// Eight E4M3 codes (two dwords) -> eight bf16 (an MFMA operand fragment).
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4_t r;
+  r[0] = e4m3x2_to_bf16x2(lo, false);
+  r[1] = e4m3x2_to_bf16x2(lo, true);
+  r[2] = e4m3x2_to_bf16x2(hi, false);
+  r[3] = e4m3x2_to_bf16x2(hi, true);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+  u32x4_t r = {v.x, v.y, v.z, v.w};
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// 16x16x32 bf16 matrix-core product with fp32 accumulation:
+//   D[16x16] = A[16x32] * B[32x16] + C.
+// Lane l holds A[l%16][8*(l/16) .. +8], B[8*(l/16) .. +8][l%16] and
+// D[4*(l/16) + i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Order-preserving map of an fp32 score to uint32 (larger score -> larger key);
+// -0.0 is folded onto +0.0 so that equal scores get equal keys.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int from) {
+  for (int o = from; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Exclusive prefix sum over a block of NT threads; `scratch` holds NT/64 + 1
+// ints.  Returns the thread's exclusive prefix; *total receives the block sum.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = lane_id();
+  const int wid = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) scratch[wid] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < NT / kWave; ++i) {
+      int t = scratch[i];
+      scratch[i] = run;
+      run += t;
+    }
+    scratch[NT / kWave] = run;
+  }
+  __syncthreads();
+  int r = scratch[wid] + x - v;
+  *total = scratch[NT / kWave];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace hs

@@ -1,0 +1,58 @@
+// Internal launchers of the decode-step kernels (host side).  Argument checks
+// happen in hs_api.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hs {
+
+struct BatchDims {
+  int B, P, T_stride, max_blocks;
+  const int32_t* ctx_len;
+};
+
+// Indexer: bf16 queries x E4M3 keys on the matrix cores.
+hipError_t launch_indexer_bf16_e4m3(const BatchDims& d, int H, int DK, const uint16_t* q,
+                                   const float* w, const uint8_t* pool, const float* scale,
+                                   const int32_t* bt, const float* bias, float* scores,
+                                   hipStream_t s);
+// Indexer: fp32 queries x fp32 keys on the vector ALUs.
+hipError_t launch_indexer_f32(const BatchDims& d, int H, int DK, const float* q, const float* w,
+                              const float* pool, const int32_t* bt, const float* bias,
+                              float* scores, hipStream_t s);
+
+size_t topk_workspace_bytes(int B, int P, int T_stride, int K);
+hipError_t launch_topk(const BatchDims& d, int K, const float* scores, int32_t* topk, void* ws,
+                       hipStream_t s);
+
+struct ResidencyArgs {
+  int C, L, kv_bytes;               // kv_bytes: bytes per latent element (1 or 4)
+  int64_t pool_layer_rows, host_layer_rows;
+  const int32_t* bt;
+  const int32_t* hot_blocks;
+  int32_t* tok2slot;
+  int32_t* slot2tok;
+  int32_t* stamp;
+  int32_t* step;
+  int32_t* err;
+  void* pool;
+  float* row_scale;
+  const void* host_rows;
+  const float* host_scale;
+  const int64_t* host_bt;
+};
+hipError_t launch_resolve(const BatchDims& d, int K, const int32_t* topk, const ResidencyArgs& r,
+                          int32_t* row_ids, int32_t* faults, int32_t* counts, hipStream_t s);
+
+int mla_num_splits(int B, int P, int K);
+size_t mla_workspace_bytes(int B, int P, int K, int Hq);
+hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, const uint16_t* q, const uint8_t* pool,
+                                const float* row_scale, const int32_t* row_ids, float sm_scale,
+                                float* out, float* lse, void* ws, hipStream_t s);
+hipError_t launch_mla_f32(const BatchDims& d, int K, const float* q, const float* pool,
+                          const int32_t* row_ids, float sm_scale, float* out, float* lse,
+                          void* ws, hipStream_t s);
+
+}  // namespace hs

@@ -1,0 +1,228 @@
+// Indexer scores on gfx950.
+//
+// scores[b,p,t] = sum_h w[b,p,h] * max(0, q[b,p,h,:] . k[b,t,:]) + bias[b,t]
+// for the visible tokens t <= T_b - P + p (indexer of page "Un contexte d'un
+// million sur huit H200", section "Ce qui se passe"; the formula itself is the
+// reading this library implements, as the page gives none).
+//
+// bf16 x E4M3 path.  For each (request, position) the contraction
+// [H heads x D] . [D x T tokens] runs on the matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation) with heads as the M dimension
+// and tokens as N, so that after the product each lane holds four heads of
+// one token and the ReLU / weighted head sum needs only two cross-lane adds.
+// Keys are streamed once from HBM: a wave reads 16 tokens x D bytes, every
+// lane loading D/4 contiguous bytes of its token (the contraction index is
+// permuted consistently in both operands, which a sum allows), converts
+// E4M3 -> bf16 in registers (exact) and issues the products.  The next group's
+// loads are issued before the current group's products.  A block's dequant
+// scale factors out of ReLU (positive scale), so it multiplies the head sum.
+//
+// Waves of a workgroup: with P positions, P groups of 4/P waves; each group
+// keeps its position's queries in registers (H x D bf16 spread over the wave)
+// and splits the tile's tokens.  Keys shared by the positions are re-read
+// from the vector cache, not from HBM.
+#include "hs_common.h"
+#include "hs_launch.h"
+
+namespace hs {
+namespace {
+
+template <int P>
+struct IdxCfg {
+  static constexpr int WPP = (P == 1) ? 4 : (P == 2 ? 2 : 1);   // waves per position
+  static constexpr int NW = P * WPP;
+  static constexpr int NT = NW * kWave;
+  static constexpr int TILE = (P <= 2) ? 512 : 256;             // tokens per workgroup
+};
+
+template <int P, int DK, int HT>
+__global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
+    const int32_t* __restrict__ ctx_len, int T_stride, int max_blocks,
+    const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const uint8_t* __restrict__ pool, const float* __restrict__ scale,
+    const int32_t* __restrict__ bt, const float* __restrict__ bias,
+    float* __restrict__ scores) {
+  using Cfg = IdxCfg<P>;
+  constexpr int H = 16 * HT;
+  constexpr int KS = DK / 32;   // k-steps of 32
+  constexpr int SEG = DK / 4;   // contiguous key bytes per lane
+  constexpr int NV = SEG / 16;  // 16-byte loads per lane per token group
+  const int b = blockIdx.y;
+  const int T = ctx_len[b];
+  const int tile0 = blockIdx.x * Cfg::TILE;
+  if (tile0 >= T) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int p = wave / Cfg::WPP, sub = wave % Cfg::WPP;
+  const int lim = T - P + p;
+  if (lim < tile0) return;
+
+  // query fragments: head 16*mt + n, dims SEG*g + 8*s .. +8
+  bf16x8_t qa[HT][KS];
+  const uint16_t* qp = q + (size_t)(b * P + p) * H * DK;
+#pragma unroll
+  for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qa[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + (16 * mt + n) * DK + SEG * g + 8 * s));
+  float wv[HT][4];
+  const float* wp = w + (size_t)(b * P + p) * H;
+#pragma unroll
+  for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[mt][i] = wp[16 * mt + 4 * g + i];
+
+  const int gend = min(Cfg::TILE / 16, (lim - tile0) / 16 + 1);
+  const int32_t* btb = bt + (size_t)b * max_blocks;
+  float* out = scores + (size_t)(b * P + p) * T_stride;
+  const float* biasb = bias ? bias + (size_t)b * T_stride : nullptr;
+
+  uint4 cur[NV], nxt[NV];
+  int cur_blk = 0, nxt_blk = 0;
+  int gi = sub;
+  if (gi < gend) {
+    const int t0 = tile0 + 16 * gi;
+    cur_blk = btb[t0 >> 6];
+    const uint8_t* kp = pool + ((size_t)cur_blk * kBlock + (t0 & 63) + n) * DK + SEG * g;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) cur[v] = *reinterpret_cast<const uint4*>(kp + 16 * v);
+  }
+  for (; gi < gend; gi += Cfg::WPP) {
+    const int gn = gi + Cfg::WPP;
+    if (gn < gend) {
+      const int t0 = tile0 + 16 * gn;
+      nxt_blk = btb[t0 >> 6];
+      const uint8_t* kp = pool + ((size_t)nxt_blk * kBlock + (t0 & 63) + n) * DK + SEG * g;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) nxt[v] = *reinterpret_cast<const uint4*>(kp + 16 * v);
+    }
+    bf16x8_t kb[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 c = cur[s >> 1];
+      const uint32_t lo = (s & 1) ? c.z : c.x;
+      const uint32_t hi = (s & 1) ? c.w : c.y;
+      kb[s] = e4m3x8_to_bf16x8(lo, hi);
+    }
+    f32x4_t acc[HT];
+#pragma unroll
+    for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(qa[mt][s], kb[s], acc[mt]);
+    float v = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v = fmaf(wv[mt][i], fmaxf(acc[mt][i], 0.f), v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    const int t = tile0 + 16 * gi + n;
+    if (g == 0 && t <= lim) {
+      float sc = scale ? v * scale[cur_blk] : v;
+      if (biasb) sc += biasb[t];
+      out[t] = sc;
+    }
+#pragma unroll
+    for (int vv = 0; vv < NV; ++vv) cur[vv] = nxt[vv];
+    cur_blk = nxt_blk;
+  }
+}
+
+// fp32 path (vector ALUs): one thread per (position, token).
+__global__ __launch_bounds__(256) void indexer_f32_kernel(
+    const int32_t* __restrict__ ctx_len, int T_stride, int max_blocks, int P, int H, int DK,
+    const float* __restrict__ q, const float* __restrict__ w, const float* __restrict__ pool,
+    const int32_t* __restrict__ bt, const float* __restrict__ bias, float* __restrict__ scores) {
+  extern __shared__ float sq[];   // H*DK queries then H weights
+  const int bp = blockIdx.y;
+  const int b = bp / P, p = bp % P;
+  const int T = ctx_len[b];
+  const int lim = T - P + p;
+  const int t0 = blockIdx.x * 256;
+  if (t0 > lim) return;
+  for (int i = threadIdx.x; i < H * DK; i += 256) sq[i] = q[(size_t)bp * H * DK + i];
+  for (int i = threadIdx.x; i < H; i += 256) sq[H * DK + i] = w[(size_t)bp * H + i];
+  __syncthreads();
+  const int t = t0 + threadIdx.x;
+  if (t > lim) return;
+  const int blk = bt[(size_t)b * max_blocks + (t >> 6)];
+  const float4* kp = reinterpret_cast<const float4*>(pool + ((size_t)blk * kBlock + (t & 63)) * DK);
+  float acc = 0.f;
+  for (int h = 0; h < H; ++h) {
+    const float* qh = sq + h * DK;
+    float dot = 0.f;
+    for (int d4 = 0; d4 < DK / 4; ++d4) {
+      const float4 k = kp[d4];
+      dot = fmaf(qh[4 * d4 + 0], k.x, dot);
+      dot = fmaf(qh[4 * d4 + 1], k.y, dot);
+      dot = fmaf(qh[4 * d4 + 2], k.z, dot);
+      dot = fmaf(qh[4 * d4 + 3], k.w, dot);
+    }
+    acc = fmaf(sq[H * DK + h], fmaxf(dot, 0.f), acc);
+  }
+  if (bias) acc += bias[(size_t)b * T_stride + t];
+  scores[(size_t)bp * T_stride + t] = acc;
+}
+
+template <int P, int DK, int HT>
+hipError_t launch_mfma(const BatchDims& d, const uint16_t* q, const float* w, const uint8_t* pool,
+                       const float* scale, const int32_t* bt, const float* bias, float* scores,
+                       hipStream_t s) {
+  using Cfg = IdxCfg<P>;
+  dim3 grid((d.T_stride + Cfg::TILE - 1) / Cfg::TILE, d.B);
+  hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT>), grid, dim3(Cfg::NT), 0, s, d.ctx_len,
+                     d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias, scores);
+  return hipGetLastError();
+}
+
+template <int P, int DK>
+hipError_t dispatch_ht(int HT, const BatchDims& d, const uint16_t* q, const float* w,
+                       const uint8_t* pool, const float* scale, const int32_t* bt,
+                       const float* bias, float* scores, hipStream_t s) {
+  switch (HT) {
+    case 1: return launch_mfma<P, DK, 1>(d, q, w, pool, scale, bt, bias, scores, s);
+    case 2: return launch_mfma<P, DK, 2>(d, q, w, pool, scale, bt, bias, scores, s);
+    case 3: return launch_mfma<P, DK, 3>(d, q, w, pool, scale, bt, bias, scores, s);
+    case 4: return launch_mfma<P, DK, 4>(d, q, w, pool, scale, bt, bias, scores, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int P>
+hipError_t dispatch_dk(int DK, int HT, const BatchDims& d, const uint16_t* q, const float* w,
+                       const uint8_t* pool, const float* scale, const int32_t* bt,
+                       const float* bias, float* scores, hipStream_t s) {
+  if (DK == 64) return dispatch_ht<P, 64>(HT, d, q, w, pool, scale, bt, bias, scores, s);
+  if (DK == 128) return dispatch_ht<P, 128>(HT, d, q, w, pool, scale, bt, bias, scores, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_indexer_bf16_e4m3(const BatchDims& d, int H, int DK, const uint16_t* q,
+                                   const float* w, const uint8_t* pool, const float* scale,
+                                   const int32_t* bt, const float* bias, float* scores,
+                                   hipStream_t s) {
+  const int HT = H / 16;
+  switch (d.P) {
+    case 1: return dispatch_dk<1>(DK, HT, d, q, w, pool, scale, bt, bias, scores, s);
+    case 2: return dispatch_dk<2>(DK, HT, d, q, w, pool, scale, bt, bias, scores, s);
+    case 3: return dispatch_dk<3>(DK, HT, d, q, w, pool, scale, bt, bias, scores, s);
+    case 4: return dispatch_dk<4>(DK, HT, d, q, w, pool, scale, bt, bias, scores, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_indexer_f32(const BatchDims& d, int H, int DK, const float* q, const float* w,
+                              const float* pool, const int32_t* bt, const float* bias,
+                              float* scores, hipStream_t s) {
+  dim3 grid((d.T_stride + 255) / 256, d.B * d.P);
+  const size_t shm = (size_t)(H * DK + H) * sizeof(float);
+  hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), shm, s, d.ctx_len, d.T_stride,
+                     d.max_blocks, d.P, H, DK, q, w, pool, bt, bias, scores);
+  return hipGetLastError();
+}
+
+}  // namespace hs

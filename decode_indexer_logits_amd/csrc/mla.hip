@@ -1,0 +1,371 @@
+// Sparse MLA decode attention on gfx950, absorbed (MQA) form: every head
+// attends over the same selected 576-value latent rows, which serve as keys,
+// and over their first 512 values, which serve as values (page "vLLM sert
+// GLM-5.3 en contexte 1M sur 16 H200", section "Comment s'y prendre", option
+// sparse_mla_force_mqa; the selected rows come from the indexer's top-K, page
+// "Un contexte d'un million sur huit H200", section "Ce qui se passe").
+//
+// bf16 x E4M3 path, one workgroup = 4 waves on one (request, position) and a
+// contiguous slice of its K selected rows, in 64-row tiles:
+//   QK   wave w takes rows 16w..16w+15 of the tile: S^T[rows x 16 heads] on
+//        the matrix cores (18 steps of v_mfma_f32_16x16x32_bf16 over the 576
+//        values).  Each lane reads 144 contiguous bytes of its row straight
+//        from HBM (the gather by row id), converts E4M3 -> bf16 in registers
+//        and also stores the 512 value entries transposed into LDS.
+//   softmax  online, per head; the tile maximum is combined across the four
+//        waves through LDS; the row's scale is folded into the logit and
+//        into the probability that multiplies its value codes.
+//   PV   wave w owns output dims 128w..128w+127: O^T[dims x heads] +=
+//        V^T[dims x 64 rows] . P^T[64 rows x heads], operands read from LDS
+//        (V^T chunks XOR-swizzled to keep both the transposing writes and
+//        the 16-byte reads free of bank conflicts).
+// A workgroup covers rows [split*R, split*R + R) in ascending k.  With one
+// slice it writes out/lse directly; otherwise the combine kernel merges the
+// slices' (O, max, sum) in slice order, so the reduction order depends only on
+// the order of row_ids, never on where a row is stored.
+#include "hs_common.h"
+#include "hs_launch.h"
+
+namespace hs {
+namespace {
+
+constexpr int kMlaNT = 256;
+constexpr int kTile = 64;
+constexpr int kVtStride = 72;   // bf16 per dim row: 64 rows + 8 pad (144 bytes)
+constexpr int kPtStride = 72;
+constexpr int kHq = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int vt_index(int dim, int row) {
+  const int chunk = (row >> 3) ^ ((dim >> 3) & 7);
+  return dim * kVtStride + chunk * 8 + (row & 7);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <bool SPLIT>
+__global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ pool,
+    const float* __restrict__ row_scale, const int32_t* __restrict__ row_ids, int K,
+    int rows_per_split, int nsplit, float qk_scale_log2, float* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kDVal * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Pt[kHq * kPtStride];
+  __shared__ float red[4][kHq];
+
+  const int bp = blockIdx.y, split = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int kb = split * rows_per_split;
+  const int ke = min(K, kb + rows_per_split);
+
+  // Q^T fragments: head n, dims 144g + 8s .. +8
+  bf16x8_t qf[18];
+  {
+    const uint16_t* qp = q + ((size_t)bp * kHq + n) * kDLat + 144 * g;
+#pragma unroll
+    for (int s = 0; s < 18; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 8 * s));
+  }
+  f32x4_t o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+  const int32_t* rid_p = row_ids + (size_t)bp * K;
+  const int r_local = 16 * wave + n;
+
+  for (int kt = kb; kt < ke; kt += kTile) {
+    const int kk = kt + r_local;
+    const int rid = (kk < ke) ? rid_p[kk] : -1;
+    uint4 raw[9];
+    float rs = 0.f;
+    if (rid >= 0) {
+      const uint4* src = reinterpret_cast<const uint4*>(pool + (size_t)rid * kDLat + 144 * g);
+#pragma unroll
+      for (int v = 0; v < 9; ++v) raw[v] = src[v];
+      rs = row_scale ? row_scale[rid] : 1.f;
+    } else {
+#pragma unroll
+      for (int v = 0; v < 9; ++v) raw[v] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    // S^T = X . Q^T over 576 values; stash the value part transposed
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 18; ++s) {
+      const uint4 c = raw[s >> 1];
+      const uint32_t lo = (s & 1) ? c.z : c.x;
+      const uint32_t hi = (s & 1) ? c.w : c.y;
+      u32x4_t xb;
+      xb[0] = e4m3x2_to_bf16x2(lo, false);
+      xb[1] = e4m3x2_to_bf16x2(lo, true);
+      xb[2] = e4m3x2_to_bf16x2(hi, false);
+      xb[3] = e4m3x2_to_bf16x2(hi, true);
+      acc = mfma16x16x32(as_bf16x8(xb), qf[s], acc);
+      const int dim0 = 144 * g + 8 * s;
+      if (dim0 < kDVal) {
+        uint16_t* dst = Vt + vt_index(dim0, r_local);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dst[(2 * i) * kVtStride] = (uint16_t)(xb[i] & 0xFFFFu);
+          dst[(2 * i + 1) * kVtStride] = (uint16_t)(xb[i] >> 16);
+        }
+      }
+    }
+    // logits of this lane's rows 4g+i (head n), log2 domain
+    float z[4];
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int src_lane = 4 * g + i;
+      const int r_i = __shfl(rid, src_lane);
+      sc[i] = __shfl(rs, src_lane);
+      z[i] = (r_i >= 0) ? acc[i] * qk_scale_log2 * sc[i] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (g == 0) red[wave][n] = mx;
+    __syncthreads();
+    const float mt = fmaxf(fmaxf(red[0][n], red[1][n]), fmaxf(red[2][n], red[3][n]));
+    const float m_new = fmaxf(m_run, mt);
+    float alpha = 1.f, p[4] = {0.f, 0.f, 0.f, 0.f};
+    if (m_new != -INFINITY) {
+      alpha = exp2f(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = exp2f(z[i] - m_new);
+    }
+    l_part = l_part * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    {
+      const uint32_t w0 = f32_to_bf16_rne(p[0] * sc[0]) | (f32_to_bf16_rne(p[1] * sc[1]) << 16);
+      const uint32_t w1 = f32_to_bf16_rne(p[2] * sc[2]) | (f32_to_bf16_rne(p[3] * sc[3]) << 16);
+      *reinterpret_cast<uint2*>(Pt + n * kPtStride + 16 * wave + 4 * g) = make_uint2(w0, w1);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    m_run = m_new;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8_t pb = as_bf16x8(*reinterpret_cast<const uint4*>(Pt + n * kPtStride + 32 * c + 8 * g));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int dim = 128 * wave + 16 * dt + n;
+        const bf16x8_t va = as_bf16x8(*reinterpret_cast<const uint4*>(Vt + vt_index(dim, 32 * c + 8 * g)));
+        o[dt] = mfma16x16x32(va, pb, o[dt]);
+      }
+    }
+    __syncthreads();
+  }
+
+  float lp = l_part;
+  lp += __shfl_xor(lp, 16);
+  lp += __shfl_xor(lp, 32);
+  if (g == 0) red[wave][n] = lp;
+  __syncthreads();
+  const float l_tot = (red[0][n] + red[1][n]) + (red[2][n] + red[3][n]);
+  if (!SPLIT) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* op = out + ((size_t)bp * kHq + n) * kDVal + 128 * wave + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(op + 16 * dt) =
+          make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    if (lse && wave == 0 && g == 0)
+      lse[(size_t)bp * kHq + n] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    const size_t base = ((size_t)bp * nsplit + split) * kHq + n;
+    float* op = part_o + base * kDVal + 128 * wave + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (wave == 0 && g == 0) {
+      part_ml[base * 2] = m_run;
+      part_ml[base * 2 + 1] = l_tot;
+    }
+  }
+}
+
+// fp32 path (vector ALUs), 16-row tiles; same online softmax in log2 domain.
+__global__ __launch_bounds__(kMlaNT) void mla_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ pool, const int32_t* __restrict__ row_ids,
+    int K, int rows_per_split, int nsplit, float qk_scale_log2, int split_mode,
+    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  __shared__ float Qs[kHq][kDLat];
+  __shared__ float Xs[16][kDLat];
+  __shared__ float Ps[kHq][16];
+  __shared__ int Rs[16];
+  const int bp = blockIdx.y, split = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int h = tid >> 4, r = tid & 15;       // logits: (head, row); PV: (head, dim group)
+  const int kb = split * rows_per_split;
+  const int ke = min(K, kb + rows_per_split);
+  for (int i = tid; i < kHq * kDLat; i += kMlaNT) Qs[i / kDLat][i % kDLat] = q[(size_t)bp * kHq * kDLat + i];
+  float acc[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int32_t* rid_p = row_ids + (size_t)bp * K;
+  for (int kt = kb; kt < ke; kt += 16) {
+    __syncthreads();
+    if (tid < 16) Rs[tid] = (kt + tid < ke) ? rid_p[kt + tid] : -1;
+    __syncthreads();
+    for (int i = tid; i < 16 * kDLat; i += kMlaNT) {
+      const int rr = i / kDLat, d = i % kDLat;
+      const int rid = Rs[rr];
+      Xs[rr][d] = rid >= 0 ? pool[(size_t)rid * kDLat + d] : 0.f;
+    }
+    __syncthreads();
+    float z = -INFINITY;
+    if (Rs[r] >= 0) {
+      float dot = 0.f;
+      for (int d = 0; d < kDLat; ++d) dot = fmaf(Qs[h][d], Xs[r][d], dot);
+      z = dot * qk_scale_log2;
+    }
+    float mt = z;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
+    const float m_new = fmaxf(m_run, mt);
+    float alpha = 1.f, p = 0.f;
+    if (m_new != -INFINITY) {
+      alpha = exp2f(m_run - m_new);
+      p = exp2f(z - m_new);
+    }
+    float ps = p;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    Ps[h][r] = p;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      float a = acc[j] * alpha;
+      const int d = r + 16 * j;
+      for (int rr = 0; rr < 16; ++rr) a = fmaf(Ps[h][rr], Xs[rr][d], a);
+      acc[j] = a;
+    }
+  }
+  if (!split_mode) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) out[((size_t)bp * kHq + h) * kDVal + r + 16 * j] = acc[j] * inv;
+    if (lse && r == 0) lse[(size_t)bp * kHq + h] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  } else {
+    const size_t base = ((size_t)bp * nsplit + split) * kHq + h;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) part_o[base * kDVal + r + 16 * j] = acc[j];
+    if (r == 0) {
+      part_ml[base * 2] = m_run;
+      part_ml[base * 2 + 1] = l_run;
+    }
+  }
+}
+
+// Merges the slices of each (request, position) in slice order.
+__global__ __launch_bounds__(kMlaNT) void mla_combine_kernel(int nsplit, const float* __restrict__ part_o,
+                                                             const float* __restrict__ part_ml,
+                                                             float* __restrict__ out,
+                                                             float* __restrict__ lse) {
+  const int bp = blockIdx.x;
+  const int h = threadIdx.x >> 4, dq = threadIdx.x & 15;   // dims 32*dq .. +32
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(((size_t)bp * nsplit + s) * kHq + h) * 2]);
+  float acc[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+  float L = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const size_t base = ((size_t)bp * nsplit + s) * kHq + h;
+      const float ms = part_ml[base * 2];
+      if (ms == -INFINITY) continue;
+      const float wgt = exp2f(ms - M);
+      L += part_ml[base * 2 + 1] * wgt;
+      const float4* src = reinterpret_cast<const float4*>(part_o + base * kDVal + 32 * dq);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float4 v = src[j];
+        acc[4 * j + 0] = fmaf(v.x, wgt, acc[4 * j + 0]);
+        acc[4 * j + 1] = fmaf(v.y, wgt, acc[4 * j + 1]);
+        acc[4 * j + 2] = fmaf(v.z, wgt, acc[4 * j + 2]);
+        acc[4 * j + 3] = fmaf(v.w, wgt, acc[4 * j + 3]);
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float4* dst = reinterpret_cast<float4*>(out + ((size_t)bp * kHq + h) * kDVal + 32 * dq);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    dst[j] = make_float4(acc[4 * j] * inv, acc[4 * j + 1] * inv, acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
+  if (lse && dq == 0) lse[(size_t)bp * kHq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+__host__ inline int rows_per_split_for(int K, int nsplit) {
+  int r = (K + nsplit - 1) / nsplit;
+  return (r + kTile - 1) / kTile * kTile;
+}
+
+}  // namespace
+
+int mla_num_splits(int B, int P, int K) {
+  const int BP = B * P;
+  const int max_split = (K + kTile - 1) / kTile;
+  int ns = (512 + BP - 1) / BP;
+  if (ns > max_split) ns = max_split;
+  if (ns < 1) ns = 1;
+  const int rps = rows_per_split_for(K, ns);
+  return (K + rps - 1) / rps;
+}
+
+size_t mla_workspace_bytes(int B, int P, int K, int Hq) {
+  const int ns = mla_num_splits(B, P, K);
+  if (ns <= 1) return 0;
+  const size_t parts = (size_t)B * P * ns * Hq;
+  return parts * kDVal * 4 + parts * 2 * 4;
+}
+
+hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, const uint16_t* q, const uint8_t* pool,
+                                const float* row_scale, const int32_t* row_ids, float sm_scale,
+                                float* out, float* lse, void* ws, hipStream_t s) {
+  const int BP = d.B * d.P;
+  const int ns = mla_num_splits(d.B, d.P, K);
+  const int rps = rows_per_split_for(K, ns);
+  const float qk = sm_scale * kLog2e;
+  if (ns == 1) {
+    hipLaunchKernelGGL((mla_bf16_e4m3_kernel<false>), dim3(1, BP), dim3(kMlaNT), 0, s, q, pool,
+                       row_scale, row_ids, K, rps, 1, qk, out, lse, nullptr, nullptr);
+    return hipGetLastError();
+  }
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o + (size_t)BP * ns * kHq * kDVal;
+  hipLaunchKernelGGL((mla_bf16_e4m3_kernel<true>), dim3(ns, BP), dim3(kMlaNT), 0, s, q, pool,
+                     row_scale, row_ids, K, rps, ns, qk, out, lse, part_o, part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP), dim3(kMlaNT), 0, s, ns, part_o, part_ml, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_f32(const BatchDims& d, int K, const float* q, const float* pool,
+                          const int32_t* row_ids, float sm_scale, float* out, float* lse,
+                          void* ws, hipStream_t s) {
+  const int BP = d.B * d.P;
+  const int ns = mla_num_splits(d.B, d.P, K);
+  const int rps = rows_per_split_for(K, ns);
+  const float qk = sm_scale * kLog2e;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = ns > 1 ? part_o + (size_t)BP * ns * kHq * kDVal : nullptr;
+  hipLaunchKernelGGL(mla_f32_kernel, dim3(ns, BP), dim3(kMlaNT), 0, s, q, pool, row_ids, K, rps, ns,
+                     qk, ns > 1 ? 1 : 0, out, lse, part_o, part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP), dim3(kMlaNT), 0, s, ns, part_o, part_ml, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace hs

@@ -1,0 +1,386 @@
+// Fused resolve of the selected tokens on gfx950 (page "Un contexte d'un
+// million sur huit H200", section "Les trois états de résidence": resident
+// tokens are read in place, hot tokens refresh their LRU entry, a fault copies
+// a single row from pinned host memory, and no CPU decision sits on the path).
+//
+// Two kernels, both decided entirely on the device:
+//   resolve    one 1024-thread workgroup per request owns that request's
+//              tables, so no state is shared between workgroups:
+//              1. U = sorted distinct union of the P positions' selections
+//                 (each list is sorted: ranks by binary search, then dedup);
+//              2. classify U in ascending order: resident page / hot hit
+//                 (stamp <- s) / fault, faults compacted in token order;
+//              3. victims: the |F| smallest (stamp, slot) keys among slots
+//                 with stamp < s, found by an MSD radix select over the key
+//                 bits that differ, then sorted in LDS (bitonic);
+//              4. fault i takes victim i: evict, insert, stamp, record;
+//              5. row ids of every (position, k) from the updated tables.
+//   fault copy a grid over (request, fault): each 576-value row is read
+//              straight from pinned host memory (zero-copy, 16-byte lanes)
+//              and written to its slot's pool row in every layer, with its
+//              scale; it also advances the step counter.
+#include "hs_common.h"
+#include "hs_launch.h"
+
+namespace hs {
+namespace {
+
+constexpr int kResNT = 1024;
+constexpr int kMaxSel = 8192;   // P*K
+constexpr int kCopyNT = 256;
+constexpr int kFaultsPerWG = 8;
+
+__device__ __forceinline__ int lower_bound_lds(const int32_t* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int upper_bound_lds(const int32_t* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Finds the bin d of h[0..256) with before(d) < k <= before(d) + h[d],
+// scanning from bin 0 upward (a tiny serial scan by one wave).
+__device__ void find_bin256_lo(const uint32_t* h, uint32_t k, int* d_out, uint32_t* before_out) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    uint32_t c[4], loc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = h[lane * 4 + j];
+      loc += c[j];
+    }
+    uint32_t x = loc;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    uint32_t before = x - loc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (before < k && before + c[j] >= k) {
+        *d_out = lane * 4 + j;
+        *before_out = before;
+      }
+      before += c[j];
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kResNT) void resolve_kernel(
+    int T_stride, int max_blocks, int P, int K, const int32_t* __restrict__ topk, int C,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ hot_blocks,
+    int32_t* __restrict__ tok2slot, int32_t* __restrict__ slot2tok, int32_t* __restrict__ stamp,
+    const int32_t* __restrict__ step, int32_t* __restrict__ err,
+    const int64_t* __restrict__ host_bt, int32_t* __restrict__ row_ids,
+    int32_t* __restrict__ faults, int32_t* __restrict__ counts) {
+  __shared__ uint64_t sA64[kMaxSel];      // merge lists + merged run; later victim keys
+  __shared__ int32_t sF[kMaxSel];         // faulting tokens, ascending
+  __shared__ int scratch[kResNT / kWave + 1];
+  __shared__ uint32_t h256[256];
+  __shared__ int s_nlist[4];
+  __shared__ int s_res, s_hit, s_ev, s_cnt, s_vcnt, s_d;
+  __shared__ uint32_t s_before;
+  __shared__ unsigned long long s_kmin, s_kmax;
+  int32_t* sA = reinterpret_cast<int32_t*>(sA64);
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int s = step[0] + 1;
+  const int PK = P * K;
+  const int32_t* tk = topk + (size_t)b * PK;
+  const int32_t* btb = bt + (size_t)b * max_blocks;
+  const int64_t* hbt = host_bt + (size_t)b * max_blocks;
+  int32_t* t2s = tok2slot + (size_t)b * T_stride;
+  int32_t* s2t = slot2tok + (size_t)b * C;
+  int32_t* stp = stamp + (size_t)b * C;
+
+  if (tid < 4) s_nlist[tid] = 0;
+  if (tid == 0) {
+    s_res = 0;
+    s_hit = 0;
+    s_ev = 0;
+    s_cnt = 0;
+    s_vcnt = 0;
+    s_kmin = ~0ull;
+    s_kmax = 0ull;
+  }
+  __syncthreads();
+
+  // 1. U: sorted distinct selected tokens
+  int32_t* Lin = sA;             // P lists of K, each sorted with a -1 tail
+  int32_t* M = sA + kMaxSel;     // merged run with duplicates
+  for (int e = tid; e < PK; e += kResNT) {
+    const int x = tk[e];
+    Lin[e] = x;
+    if (x >= 0) atomicAdd(&s_nlist[e / K], 1);
+  }
+  __syncthreads();
+  int nU;
+  if (P == 1) {
+    nU = s_nlist[0];
+  } else {
+    int total = 0;
+    for (int p = 0; p < P; ++p) total += s_nlist[p];
+    for (int e = tid; e < PK; e += kResNT) {
+      const int p = e / K, i = e - p * K;
+      if (i >= s_nlist[p]) continue;
+      const int x = Lin[e];
+      int pos = i;
+      for (int q = 0; q < P; ++q) {
+        if (q == p) continue;
+        pos += (q < p) ? upper_bound_lds(Lin + q * K, s_nlist[q], x)
+                       : lower_bound_lds(Lin + q * K, s_nlist[q], x);
+      }
+      M[pos] = x;
+    }
+    __syncthreads();
+    int run = 0;
+    for (int base = 0; base < total; base += kResNT) {
+      const int idx = base + tid;
+      const bool keep = idx < total && (idx == 0 || M[idx] != M[idx - 1]);
+      const int x = idx < total ? M[idx] : 0;
+      int tot;
+      const int ex = block_exclusive_scan<kResNT>(keep ? 1 : 0, scratch, &tot);
+      if (keep) Lin[run + ex] = x;
+      run += tot;
+    }
+    nU = run;
+    __syncthreads();
+  }
+  const int32_t* U = Lin;
+
+  // 2. classify in ascending token order
+  int my_res = 0, my_hit = 0, nF = 0;
+  for (int base = 0; base < nU; base += kResNT) {
+    const int idx = base + tid;
+    bool is_f = false;
+    int t = 0;
+    if (idx < nU) {
+      t = U[idx];
+      const int j = t >> 6;
+      if (btb[j] >= 0) {
+        ++my_res;
+      } else {
+        const int v = C > 0 ? t2s[t] : -1;
+        if (v >= 0) {
+          ++my_hit;
+          stp[v] = s;
+        } else if (host_bt == nullptr || hbt[j] < 0) {
+          atomicOr(err, 2);
+        } else {
+          is_f = true;
+        }
+      }
+    }
+    int tot;
+    const int ex = block_exclusive_scan<kResNT>(is_f ? 1 : 0, scratch, &tot);
+    if (is_f) sF[nF + ex] = t;
+    nF += tot;
+  }
+  if (my_res) atomicAdd(&s_res, my_res);
+  if (my_hit) atomicAdd(&s_hit, my_hit);
+  __threadfence();
+  __syncthreads();
+
+  // 3. victims
+  int n_serve = 0;
+  if (nF > 0 && C > 0) {
+    int my_c = 0;
+    unsigned long long kmin = ~0ull, kmax = 0ull;
+    for (int v = tid; v < C; v += kResNT) {
+      const int st = stp[v];
+      if (st < s) {
+        const unsigned long long key = ((unsigned long long)(uint32_t)st << 32) | (uint32_t)v;
+        ++my_c;
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
+    }
+    if (my_c) {
+      atomicAdd(&s_cnt, my_c);
+      atomicMin(&s_kmin, kmin);
+      atomicMax(&s_kmax, kmax);
+    }
+    __syncthreads();
+    const int n_cand = s_cnt;
+    n_serve = min(nF, n_cand);
+    unsigned long long thr = s_kmax;
+    if (n_serve > 0 && n_serve < n_cand) {
+      // MSD radix select of the n_serve-th smallest key, from the highest
+      // byte in which candidate keys differ
+      const unsigned long long diff = s_kmin ^ s_kmax;
+      const int top_byte = (63 - __builtin_clzll(diff)) >> 3;
+      unsigned long long prefix = (top_byte == 7) ? 0ull : (s_kmin >> (8 * (top_byte + 1)));
+      uint32_t need = (uint32_t)n_serve;
+      for (int pos = top_byte; pos >= 0; --pos) {
+        if (tid < 256) h256[tid] = 0;
+        __syncthreads();
+        for (int v = tid; v < C; v += kResNT) {
+          const int st = stp[v];
+          if (st >= s) continue;
+          const unsigned long long key = ((unsigned long long)(uint32_t)st << 32) | (uint32_t)v;
+          if (pos == 7 || (key >> (8 * (pos + 1))) == prefix)
+            atomicAdd(&h256[(key >> (8 * pos)) & 0xFFu], 1u);
+        }
+        __syncthreads();
+        find_bin256_lo(h256, need, &s_d, &s_before);
+        prefix = (prefix << 8) | (unsigned long long)s_d;
+        need -= s_before;
+        __syncthreads();
+      }
+      thr = prefix;
+    }
+    // gather the victims (exactly n_serve keys <= thr) and sort them
+    uint64_t* V = sA64;
+    if (n_serve > 0) {
+      for (int v = tid; v < C; v += kResNT) {
+        const int st = stp[v];
+        if (st >= s) continue;
+        const unsigned long long key = ((unsigned long long)(uint32_t)st << 32) | (uint32_t)v;
+        if (key <= thr) {
+          const int at = atomicAdd(&s_vcnt, 1);
+          if (at < kMaxSel) V[at] = key;
+        }
+      }
+      int np = 1;
+      while (np < n_serve) np <<= 1;
+      __syncthreads();
+      for (int i = n_serve + tid; i < np; i += kResNT) V[i] = ~0ull;
+      __syncthreads();
+      for (int size = 2; size <= np; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int i = tid; i < np / 2; i += kResNT) {
+            const int lo = 2 * i - (i & (stride - 1));
+            const int hi = lo + stride;
+            const bool asc = (lo & size) == 0;
+            const uint64_t a = V[lo], c = V[hi];
+            if ((a > c) == asc) {
+              V[lo] = c;
+              V[hi] = a;
+            }
+          }
+          __syncthreads();
+        }
+      }
+      // 4. fault i -> victim i
+      int my_ev = 0;
+      int32_t* fb = faults + (size_t)b * PK * 2;
+      for (int i = tid; i < n_serve; i += kResNT) {
+        const int v = (int)(uint32_t)V[i];
+        const int t = sF[i];
+        const int old = s2t[v];
+        if (old >= 0) {
+          t2s[old] = -1;
+          ++my_ev;
+        }
+        s2t[v] = t;
+        t2s[t] = v;
+        stp[v] = s;
+        fb[2 * i] = t;
+        fb[2 * i + 1] = v;
+      }
+      if (my_ev) atomicAdd(&s_ev, my_ev);
+    }
+  }
+  if (tid == 0 && n_serve < nF) atomicOr(err, 1);
+  __threadfence();
+  __syncthreads();
+
+  // 5. row ids
+  const int32_t* hb = hot_blocks + (size_t)b * (C >> 6);
+  int32_t* rid = row_ids + (size_t)b * PK;
+  for (int e = tid; e < PK; e += kResNT) {
+    const int t = tk[e];
+    int r = -1;
+    if (t >= 0) {
+      const int j = t >> 6;
+      const int rb = btb[j];
+      if (rb >= 0) {
+        r = rb * kBlock + (t & 63);
+      } else if (C > 0) {
+        const int v = t2s[t];
+        if (v >= 0) r = hb[v >> 6] * kBlock + (v & 63);
+      }
+    }
+    rid[e] = r;
+  }
+  if (tid == 0) {
+    counts[b * 4 + 0] = s_res;
+    counts[b * 4 + 1] = s_hit;
+    counts[b * 4 + 2] = n_serve;
+    counts[b * 4 + 3] = s_ev;
+  }
+}
+
+__global__ __launch_bounds__(kCopyNT) void fault_copy_kernel(
+    int PK, int C, int L, int row_bytes, int max_blocks, const int32_t* __restrict__ faults,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ hot_blocks,
+    const int64_t* __restrict__ host_bt, const uint8_t* __restrict__ host_rows,
+    const float* __restrict__ host_scale, int64_t host_layer_rows, uint8_t* __restrict__ pool,
+    float* __restrict__ row_scale, int64_t pool_layer_rows, int32_t* __restrict__ step) {
+  const int b = blockIdx.y;
+  if (blockIdx.x == 0 && b == 0 && threadIdx.x == 0) step[0] = step[0] + 1;
+  const int nf = counts[b * 4 + 2];
+  const int f0 = blockIdx.x * kFaultsPerWG;
+  if (f0 >= nf) return;
+  const int nloc = min(kFaultsPerWG, nf - f0);
+  const int cpr = row_bytes / 16;           // 16-byte chunks per row
+  const int32_t* fb = faults + ((size_t)b * PK + f0) * 2;
+  const int32_t* hb = hot_blocks + (size_t)b * (C >> 6);
+  const int64_t* hbt = host_bt + (size_t)b * max_blocks;
+  const int per_fault = L * cpr;
+  for (int idx = threadIdx.x; idx < nloc * per_fault; idx += kCopyNT) {
+    const int fl = idx / per_fault;
+    const int rem = idx - fl * per_fault;
+    const int l = rem / cpr;
+    const int c = rem - l * cpr;
+    const int t = fb[2 * fl], v = fb[2 * fl + 1];
+    const int64_t hr = hbt[t >> 6] + (t & 63);
+    const int64_t pr = (int64_t)hb[v >> 6] * kBlock + (v & 63);
+    const uint4* src = reinterpret_cast<const uint4*>(host_rows + ((size_t)l * host_layer_rows + hr) * row_bytes) + c;
+    uint4* dst = reinterpret_cast<uint4*>(pool + ((size_t)l * pool_layer_rows + pr) * row_bytes) + c;
+    *dst = *src;
+  }
+  if (host_scale) {
+    for (int idx = threadIdx.x; idx < nloc * L; idx += kCopyNT) {
+      const int fl = idx / L, l = idx - fl * L;
+      const int t = fb[2 * fl], v = fb[2 * fl + 1];
+      const int64_t hr = hbt[t >> 6] + (t & 63);
+      const int64_t pr = (int64_t)hb[v >> 6] * kBlock + (v & 63);
+      row_scale[(size_t)l * pool_layer_rows + pr] = host_scale[(size_t)l * host_layer_rows + hr];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_resolve(const BatchDims& d, int K, const int32_t* topk, const ResidencyArgs& r,
+                          int32_t* row_ids, int32_t* faults, int32_t* counts, hipStream_t s) {
+  const int PK = d.P * K;
+  hipLaunchKernelGGL(resolve_kernel, dim3(d.B), dim3(kResNT), 0, s, d.T_stride, d.max_blocks, d.P,
+                     K, topk, r.C, r.bt, r.hot_blocks, r.tok2slot, r.slot2tok, r.stamp, r.step,
+                     r.err, r.host_bt, row_ids, faults, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int row_bytes = kDLat * r.kv_bytes;
+  dim3 grid((PK + kFaultsPerWG - 1) / kFaultsPerWG, d.B);
+  hipLaunchKernelGGL(fault_copy_kernel, grid, dim3(kCopyNT), 0, s, PK, r.C, r.L, row_bytes,
+                     d.max_blocks, faults, counts, r.hot_blocks, r.host_bt,
+                     static_cast<const uint8_t*>(r.host_rows), r.host_scale, r.host_layer_rows,
+                     static_cast<uint8_t*>(r.pool), r.row_scale, r.pool_layer_rows, r.step);
+  return hipGetLastError();
+}
+
+}  // namespace hs

@@ -1,0 +1,296 @@
+// Exact top-K per query position on gfx950 (K best tokens of the indexer,
+// page "Un contexte d'un million sur huit H200", section "Ce qui se passe";
+// K = 2048 on "vLLM sert GLM-5.3 en contexte 1M sur 16 H200", section
+// "Comment s'y prendre").
+//
+// Scores map to order-preserving uint32 keys.  A row (one request position,
+// up to 2^24 tokens) is spread over many workgroups so that a handful of very
+// long rows still fills the chip:
+//   1. zero      per-row histogram and counters
+//   2. histogram of the top 11 key bits, per 8192-token chunk: LDS counts,
+//                then one global atomic per non-empty bin
+//   3. filter    every chunk re-derives the bin b1 holding the K-th largest
+//                key; keys above b1 are selected outright, keys in b1 become
+//                candidates (wave ballots aggregate the global appends)
+//   4. finalize  one workgroup per row finishes the radix select on the
+//                candidates (11 + 10 more bits), resolves ties at the
+//                threshold toward the lower token (radix select on the token
+//                index), collects the K tokens and sorts them ascending in LDS.
+// The selection is exact: the same tokens as a full sort by (score desc,
+// token asc), written in ascending token order, -1 padded for short rows.
+#include "hs_common.h"
+#include "hs_launch.h"
+
+namespace hs {
+namespace {
+
+constexpr int kBins1 = 2048;   // top 11 key bits
+constexpr int kChunk = 8192;   // tokens per workgroup in passes 2 and 3
+constexpr int kScanNT = 256;
+constexpr int kFinNT = 1024;
+constexpr int kMaxK = 8192;
+
+struct TopkWs {
+  uint32_t* hist;   // [R][2048]
+  uint32_t* cnt;    // [R][4]: selected-above count, candidate count, b1, count above b1
+  int32_t* sel;     // [R][K]
+  uint32_t* ckey;   // [R][T_stride]
+  int32_t* ctok;    // [R][T_stride]
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline TopkWs topk_ws(void* base, int R, int T_stride, int K) {
+  char* p = static_cast<char*>(base);
+  TopkWs w;
+  w.hist = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)R * kBins1 * 4);
+  w.cnt = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)R * 4 * 4);
+  w.sel = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)R * K * 4);
+  w.ckey = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)R * T_stride * 4);
+  w.ctok = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+__device__ __forceinline__ int row_visible(const int32_t* ctx_len, int P, int r) {
+  const int b = r / P, p = r % P;
+  return max(ctx_len[b] - P + p + 1, 0);
+}
+
+// Finds the bin d with before(d) < k <= before(d) + h[d], where before(d) sums
+// the bins preceding d in scan order (descending bins when from_top).  Bins in
+// LDS; the result is written to *d_out / *before_out by the one thread that
+// finds it.  Every thread of the block must call it.
+template <int NT>
+__device__ void find_bin(const uint32_t* h, int nbins, uint32_t k, bool from_top, int* scratch,
+                         int* d_out, uint32_t* before_out) {
+  const int bpt = nbins >= NT ? nbins / NT : 1;
+  const int owners = nbins / bpt;
+  const int tid = threadIdx.x;
+  uint32_t local = 0;
+  if (tid < owners)
+    for (int j = 0; j < bpt; ++j) {
+      const int pos = tid * bpt + j;
+      local += h[from_top ? nbins - 1 - pos : pos];
+    }
+  int total;
+  const uint32_t excl = (uint32_t)block_exclusive_scan<NT>((int)local, scratch, &total);
+  if (tid < owners) {
+    uint32_t before = excl;
+    for (int j = 0; j < bpt; ++j) {
+      const int pos = tid * bpt + j;
+      const int bin = from_top ? nbins - 1 - pos : pos;
+      const uint32_t c = h[bin];
+      if (before < k && before + c >= k) {
+        *d_out = bin;
+        *before_out = before;
+      }
+      before += c;
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kScanNT) void topk_zero_kernel(TopkWs ws) {
+  const int r = blockIdx.x;
+  for (int i = threadIdx.x; i < kBins1; i += kScanNT) ws.hist[(size_t)r * kBins1 + i] = 0;
+  if (threadIdx.x < 4) ws.cnt[r * 4 + threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(kScanNT) void topk_hist_kernel(const int32_t* __restrict__ ctx_len,
+                                                            int P, int T_stride, int K,
+                                                            const float* __restrict__ scores,
+                                                            TopkWs ws) {
+  __shared__ uint32_t h[kBins1];
+  const int r = blockIdx.y;
+  const int n = row_visible(ctx_len, P, r);
+  const int base = blockIdx.x * kChunk;
+  if (n <= K || base >= n) return;
+  for (int i = threadIdx.x; i < kBins1; i += kScanNT) h[i] = 0;
+  __syncthreads();
+  const float* row = scores + (size_t)r * T_stride;
+  const int end = min(base + kChunk, n);
+  for (int t = base + threadIdx.x; t < end; t += kScanNT) atomicAdd(&h[score_key(row[t]) >> 21], 1u);
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins1; i += kScanNT)
+    if (h[i]) atomicAdd(&ws.hist[(size_t)r * kBins1 + i], h[i]);
+}
+
+__global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __restrict__ ctx_len,
+                                                              int P, int T_stride, int K,
+                                                              const float* __restrict__ scores,
+                                                              TopkWs ws) {
+  __shared__ uint32_t h[kBins1];
+  __shared__ int scratch[kScanNT / kWave + 1];
+  __shared__ int s_b1;
+  __shared__ uint32_t s_above;
+  const int r = blockIdx.y;
+  const int n = row_visible(ctx_len, P, r);
+  const int base = blockIdx.x * kChunk;
+  if (n <= K || base >= n) return;
+  for (int i = threadIdx.x; i < kBins1; i += kScanNT) h[i] = ws.hist[(size_t)r * kBins1 + i];
+  __syncthreads();
+  find_bin<kScanNT>(h, kBins1, (uint32_t)K, true, scratch, &s_b1, &s_above);
+  const uint32_t b1 = (uint32_t)s_b1;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ws.cnt[r * 4 + 2] = b1;
+    ws.cnt[r * 4 + 3] = s_above;
+  }
+  const float* row = scores + (size_t)r * T_stride;
+  const int end = min(base + kChunk, n);
+  const int lane = lane_id();
+  for (int t0 = base; t0 < end; t0 += kScanNT) {
+    const int t = t0 + threadIdx.x;
+    const bool valid = t < end;
+    const uint32_t key = valid ? score_key(row[t]) : 0u;
+    const uint32_t bin = key >> 21;
+    const bool is_sel = valid && bin > b1;
+    const bool is_cand = valid && bin == b1;
+    const uint64_t ms = __ballot(is_sel);
+    const uint64_t mc = __ballot(is_cand);
+    uint32_t bs = 0, bc = 0;
+    if (lane == 0) {
+      if (ms) bs = atomicAdd(&ws.cnt[r * 4 + 0], (uint32_t)__popcll(ms));
+      if (mc) bc = atomicAdd(&ws.cnt[r * 4 + 1], (uint32_t)__popcll(mc));
+    }
+    bs = __shfl(bs, 0);
+    bc = __shfl(bc, 0);
+    if (is_sel) ws.sel[(size_t)r * K + bs + lanes_below(ms)] = t;
+    if (is_cand) {
+      const size_t o = (size_t)r * T_stride + bc + lanes_below(mc);
+      ws.ckey[o] = key;
+      ws.ctok[o] = t;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __restrict__ ctx_len,
+                                                               int P, int T_stride, int K,
+                                                               TopkWs ws, int32_t* __restrict__ topk) {
+  __shared__ uint32_t h[kBins1];
+  __shared__ int32_t outl[kMaxK];
+  __shared__ int scratch[kFinNT / kWave + 1];
+  __shared__ int s_d;
+  __shared__ uint32_t s_before;
+  __shared__ int s_pos;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = row_visible(ctx_len, P, r);
+  int32_t* out = topk + (size_t)r * K;
+  if (n <= K) {
+    for (int k = tid; k < K; k += kFinNT) out[k] = k < n ? k : -1;
+    return;
+  }
+  const uint32_t b1 = ws.cnt[r * 4 + 2];
+  const uint32_t above = ws.cnt[r * 4 + 3];
+  const int nc = (int)ws.cnt[r * 4 + 1];
+  const uint32_t* ck = ws.ckey + (size_t)r * T_stride;
+  const int32_t* ct = ws.ctok + (size_t)r * T_stride;
+  uint32_t kk = (uint32_t)K - above;   // candidates still needed, >= 1
+
+  // key bits 20..10
+  for (int i = tid; i < kBins1; i += kFinNT) h[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < nc; i += kFinNT) atomicAdd(&h[(ck[i] >> 10) & 0x7FFu], 1u);
+  __syncthreads();
+  find_bin<kFinNT>(h, kBins1, kk, true, scratch, &s_d, &s_before);
+  const uint32_t dA = (uint32_t)s_d;
+  kk -= s_before;
+  // key bits 9..0
+  for (int i = tid; i < 1024; i += kFinNT) h[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < nc; i += kFinNT) {
+    const uint32_t key = ck[i];
+    if (((key >> 10) & 0x7FFu) == dA) atomicAdd(&h[key & 0x3FFu], 1u);
+  }
+  __syncthreads();
+  find_bin<kFinNT>(h, 1024, kk, true, scratch, &s_d, &s_before);
+  const uint32_t dB = (uint32_t)s_d;
+  kk -= s_before;                        // ties at the threshold to take
+  const uint32_t n_eq = h[dB];
+  const uint32_t tau = (b1 << 21) | (dA << 10) | dB;
+  __syncthreads();
+  // ties: keep the kk lowest tokens among keys == tau
+  int t_cut = 0x7FFFFFFF;
+  if (n_eq > kk) {
+    uint32_t prefix = 0, need = kk;
+    for (int sh = 16; sh >= 0; sh -= 8) {
+      for (int i = tid; i < 256; i += kFinNT) h[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < nc; i += kFinNT) {
+        if (ck[i] != tau) continue;
+        const uint32_t t = (uint32_t)ct[i];
+        if (sh == 16 || (t >> (sh + 8)) == prefix) atomicAdd(&h[(t >> sh) & 0xFFu], 1u);
+      }
+      __syncthreads();
+      find_bin<kFinNT>(h, 256, need, false, scratch, &s_d, &s_before);
+      prefix = (prefix << 8) | (uint32_t)s_d;
+      need -= s_before;
+      __syncthreads();
+    }
+    t_cut = (int)prefix;
+  }
+  // collect: the tokens selected outright, then the chosen candidates
+  const int32_t* sel = ws.sel + (size_t)r * K;
+  for (int i = tid; i < (int)above; i += kFinNT) outl[i] = sel[i];
+  if (tid == 0) s_pos = (int)above;
+  __syncthreads();
+  for (int i = tid; i < nc; i += kFinNT) {
+    const uint32_t key = ck[i];
+    const int t = ct[i];
+    if (key > tau || (key == tau && t <= t_cut)) {
+      const int at = atomicAdd(&s_pos, 1);
+      if (at < kMaxK) outl[at] = t;
+    }
+  }
+  int np = 1;
+  while (np < K) np <<= 1;
+  __syncthreads();
+  for (int i = K + tid; i < np; i += kFinNT) outl[i] = 0x7FFFFFFF;
+  __syncthreads();
+  // bitonic sort, ascending
+  for (int size = 2; size <= np; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < np / 2; i += kFinNT) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool asc = (lo & size) == 0;
+        const int a = outl[lo], c = outl[hi];
+        if ((a > c) == asc) {
+          outl[lo] = c;
+          outl[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int k = tid; k < K; k += kFinNT) out[k] = outl[k];
+}
+
+}  // namespace
+
+size_t topk_workspace_bytes(int B, int P, int T_stride, int K) {
+  const size_t R = (size_t)B * P;
+  return align256(R * kBins1 * 4) + align256(R * 16) + align256(R * K * 4) +
+         align256(R * T_stride * 4) + align256(R * T_stride * 4);
+}
+
+hipError_t launch_topk(const BatchDims& d, int K, const float* scores, int32_t* topk, void* ws,
+                       hipStream_t s) {
+  const int R = d.B * d.P;
+  TopkWs w = topk_ws(ws, R, d.T_stride, K);
+  const int nchunk = (d.T_stride + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL(topk_zero_kernel, dim3(R), dim3(kScanNT), 0, s, w);
+  hipLaunchKernelGGL(topk_hist_kernel, dim3(nchunk, R), dim3(kScanNT), 0, s, d.ctx_len, d.P,
+                     d.T_stride, K, scores, w);
+  hipLaunchKernelGGL(topk_filter_kernel, dim3(nchunk, R), dim3(kScanNT), 0, s, d.ctx_len, d.P,
+                     d.T_stride, K, scores, w);
+  hipLaunchKernelGGL(topk_finalize_kernel, dim3(R), dim3(kFinNT), 0, s, d.ctx_len, d.P,
+                     d.T_stride, K, w, topk);
+  return hipGetLastError();
+}
+
+}  // namespace hs

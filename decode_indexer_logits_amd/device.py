@@ -1,0 +1,176 @@
+"""Device-side plumbing for one decode step: torch tensors for every input,
+state and output buffer of the C ABI, the pinned host pool, and the four calls
+of a step on one stream.  No arithmetic of the method happens here.
+
+Layouts (HBM unless noted; B requests, P positions, L layers, T = T_stride):
+  indexer   q_idx [B,P,H,D] bf16 | w [B,P,H] f32 | idx_pool [N,64,D] e4m3
+            idx_scale [N] f32 | idx_bt [B,T/64] i32 | bias [B,T] f32
+  latent    pool [L, N_rows, 576] e4m3 | row_scale [L, N_rows] f32
+  residency bt [B,T/64] | hot_blocks [B,C/64] | tok2slot [B,T] | slot2tok [B,C]
+            stamp [B,C] | step [1] | err [1]            (all i32)
+  host      host_rows [L, B*T, 576] e4m3, host_scale [L, B*T] f32 (pinned,
+            read by the GPU in place) | host_bt [B,T/64] i64
+  step      scores [B,P,T] f32 | topk [B,P,K] | row_ids [B,P,K] | faults [B,P*K,2]
+            counts [B,4] (i32) | q [L,B,P,16,576] bf16 | out [L,B,P,16,512] f32
+            lse [L,B,P,16] f32
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import _lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(a, device, dtype_tag=None):
+    torch = _torch()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceStep:
+    """All device buffers of a workload, ready to run decode steps."""
+
+    def __init__(self, wl, device: str = "cuda:0", host_pool: bool = True):
+        torch = _torch()
+        _lib.load()
+        self.wl = wl
+        self.device = torch.device(device)
+        d = self.device
+        B, P, K, L, Ts = wl.B, wl.P, wl.K, wl.L, wl.T_stride
+        self.ctx_len = _dev(wl.ctx_len.astype(np.int32), d)
+        self.batch = _lib.make_batch(B, P, Ts, self.ctx_len)
+        # indexer cache
+        self.w = _dev(wl.w, d)
+        self.idx_pool = _dev(wl.idx_pool, d)
+        self.idx_scale = None if wl.idx_scale is None else _dev(wl.idx_scale, d)
+        self.idx_bt = _dev(wl.idx_bt.astype(np.int32), d)
+        self.bias = None if wl.bias is None else _dev(wl.bias, d)
+        qdt = torch.float32 if wl.q_dtype == "f32" else torch.int16
+        self.q_idx = torch.empty((B, P, wl.H_idx, wl.D_idx), dtype=qdt, device=d)
+        self.q = torch.empty((L, B, P, wl.Hq, 576), dtype=qdt, device=d)
+        # step buffers
+        self.scores = torch.empty((B, P, Ts), dtype=torch.float32, device=d)
+        self.topk = torch.empty((B, P, K), dtype=torch.int32, device=d)
+        self.row_ids = torch.empty((B, P, K), dtype=torch.int32, device=d)
+        self.faults = torch.zeros((B, P * K, 2), dtype=torch.int32, device=d)
+        self.counts = torch.zeros((B, 4), dtype=torch.int32, device=d)
+        self.out = torch.empty((L, B, P, wl.Hq, 512), dtype=torch.float32, device=d)
+        self.lse = torch.empty((L, B, P, wl.Hq), dtype=torch.float32, device=d)
+        self.ws_topk = torch.empty(max(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, P, Ts, K), 16),
+                                   dtype=torch.uint8, device=d)
+        mla_ws = _lib.workspace_bytes(_lib.HS_OP_MLA, B, P, Ts, K, wl.Hq)
+        self.ws_mla = torch.empty(max(mla_ws, 16), dtype=torch.uint8, device=d) if mla_ws else None
+        # latent pool and residency tables
+        from workloads.gen import build_pool
+        pool, rsc = build_pool(wl)
+        self.pool = _dev(pool, d)
+        self.row_scale = None if rsc is None else _dev(rsc, d)
+        del pool
+        self.n_rows = self.pool.shape[1]
+        self.bt = _dev(wl.bt.astype(np.int32), d)
+        C = wl.C
+        self.hot_blocks = _dev(wl.hot_blocks.astype(np.int32), d) if C else None
+        self.tok2slot = _dev(wl.tok2slot, d) if C else None
+        self.slot2tok = _dev(wl.slot2tok, d) if C else None
+        self.stamp = _dev(wl.stamp, d) if C else None
+        self.step_t = torch.tensor([wl.step], dtype=torch.int32, device=d)
+        self.err = torch.zeros(1, dtype=torch.int32, device=d)
+        self.host_rows = self.host_scale = self.host_bt = None
+        host_rows_dev = host_scale_dev = None
+        if wl.has_host and host_pool:
+            hr = wl.host_rows
+            self.host_rows = torch.empty(hr.shape, dtype=torch.uint8 if hr.dtype == np.uint8
+                                         else torch.float32, pin_memory=True)
+            self.host_rows.numpy()[...] = hr
+            host_rows_dev = _lib.host_device_ptr(self.host_rows)
+            if wl.host_scale is not None:
+                hs = wl.host_scale
+                self.host_scale = torch.empty(hs.shape, dtype=torch.float32, pin_memory=True)
+                self.host_scale.numpy()[...] = hs
+                host_scale_dev = _lib.host_device_ptr(self.host_scale)
+            self.host_bt = _dev(wl.host_bt, d)
+        kv_t = _lib.DTYPES[wl.kv_dtype]
+        self.res = _lib.Residency(
+            C, L, kv_t, 0, self.n_rows, B * Ts,
+            self.bt.data_ptr(), _p(self.hot_blocks), _p(self.tok2slot), _p(self.slot2tok),
+            _p(self.stamp), self.step_t.data_ptr(), self.err.data_ptr(), self.pool.data_ptr(),
+            _p(self.row_scale), host_rows_dev, host_scale_dev, _p(self.host_bt))
+        self.set_queries(1)
+
+    # ---------------------------------------------------------------- inputs
+    def set_queries(self, s: int = 1):
+        q_idx, q = self.wl.step_inputs(s)
+        self.q_idx.copy_(_dev(q_idx, self.device))
+        self.q.copy_(_dev(q, self.device))
+
+    # ---------------------------------------------------------------- stages
+    def run_indexer(self, stream=None):
+        wl = self.wl
+        _lib.indexer_scores(self.batch, wl.H_idx, wl.D_idx, wl.q_dtype, self.q_idx, self.w,
+                            wl.k_dtype, self.idx_pool, self.idx_scale, self.idx_bt, self.bias,
+                            self.scores, stream)
+
+    def run_topk(self, stream=None):
+        _lib.topk(self.batch, self.wl.K, self.scores, self.topk, self.ws_topk, stream)
+
+    def run_resolve(self, stream=None):
+        _lib.resolve_rows(self.batch, self.wl.K, self.topk, self.res, self.row_ids, self.faults,
+                          self.counts, stream)
+
+    def run_attention(self, layer: int, stream=None):
+        wl = self.wl
+        _lib.sparse_mla_decode(self.batch, wl.K, wl.Hq, wl.q_dtype, self.q[layer], wl.kv_dtype,
+                               self.pool[layer],
+                               None if self.row_scale is None else self.row_scale[layer],
+                               self.row_ids, wl.sm_scale, self.out[layer], self.lse[layer],
+                               self.ws_mla, stream)
+
+    def run(self, stream=None):
+        """One whole decode step: indexer, top-K, resolve (+ fault copies), L x attention."""
+        self.run_indexer(stream)
+        self.run_topk(stream)
+        self.run_resolve(stream)
+        for l in range(self.wl.L):
+            self.run_attention(l, stream)
+
+    # ---------------------------------------------------------------- state
+    def snapshot(self) -> dict:
+        """Copies of the mutable state (tables, step, pool rows and scales)."""
+        snap = {"step": self.step_t.clone(), "err": self.err.clone(), "pool": self.pool.clone()}
+        if self.row_scale is not None:
+            snap["row_scale"] = self.row_scale.clone()
+        if self.wl.C:
+            snap.update(tok2slot=self.tok2slot.clone(), slot2tok=self.slot2tok.clone(),
+                        stamp=self.stamp.clone())
+        return snap
+
+    def restore(self, snap: dict):
+        self.step_t.copy_(snap["step"])
+        self.err.copy_(snap["err"])
+        self.pool.copy_(snap["pool"])
+        if "row_scale" in snap:
+            self.row_scale.copy_(snap["row_scale"])
+        if self.wl.C:
+            self.tok2slot.copy_(snap["tok2slot"])
+            self.slot2tok.copy_(snap["slot2tok"])
+            self.stamp.copy_(snap["stamp"])
+
+    def state_numpy(self) -> dict:
+        """Host copies of the residency tables (for checks)."""
+        r = {"step": int(self.step_t.item()), "err": int(self.err.item())}
+        if self.wl.C:
+            r.update(tok2slot=self.tok2slot.cpu().numpy(), slot2tok=self.slot2tok.cpu().numpy(),
+                     stamp=self.stamp.cpu().numpy())
+        return r
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()

@@ -1,0 +1,233 @@
+/*
+ * hs.h -- C ABI of one decode step of indexer-driven sparse MLA attention with
+ * hybrid GPU/host KV residency, for AMD Instinct MI355X (gfx950).
+ *
+ * The step (page "Un contexte d'un million sur huit H200", sections "Ce qui se
+ * passe" and "Les trois états de résidence"):
+ *
+ *   hs_indexer_scores    the indexer scores every cached token of every request
+ *   hs_topk              the K best tokens of each query position are selected
+ *   hs_resolve_rows      the fused resolve maps each selected token to a pool row:
+ *                        resident page in place / hot slot with an LRU refresh /
+ *                        single-row fault copied from pinned host memory
+ *   hs_sparse_mla_decode sparse MLA attention over the selected latent rows
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise; host
+ *     pools are pinned host memory passed by their device-accessible address
+ *     (see hs_host_device_ptr).  The caller owns every buffer, including the
+ *     workspace; the library allocates nothing and keeps no state between calls
+ *     except the thread-local error message.
+ *   - Every call only enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *     default stream).  No call synchronizes, reads device memory on the host,
+ *     allocates, or issues a memset, so a whole step can be captured in a HIP
+ *     graph: nothing on the decode path waits for a CPU decision, as the page
+ *     above requires of the fused resolve.
+ *   - Arguments are validated on the host only (null pointers, shapes, types,
+ *     alignment, capacity).  A failed check returns a nonzero hs_status, enqueues
+ *     nothing and sets the message returned by hs_last_error().  Device contents
+ *     (block tables, lengths, token ids) are trusted; the resolve step reports
+ *     inconsistent residency tables through its device error word.
+ *   - Layouts are dense row-major; the block (page) size is 64 tokens.
+ */
+#ifndef HS_H
+#define HS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HS_ABI_VERSION 1
+#define HS_BLOCK 64        /* tokens per page of every paged cache          */
+#define HS_D_LATENT 576    /* latent row: 512 compressed + 64 rotary values  */
+#define HS_D_VALUE 512     /* value part of a latent row                     */
+
+typedef int32_t hs_status;
+enum {
+  HS_OK = 0,
+  HS_ERR_NULL = 1,       /* a required pointer is NULL                      */
+  HS_ERR_SHAPE = 2,      /* a size is out of the supported range            */
+  HS_ERR_DTYPE = 3,      /* unsupported element-type combination            */
+  HS_ERR_CAPACITY = 4,   /* hot capacity below P*K                          */
+  HS_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required      */
+  HS_ERR_ALIGN = 6,      /* a pointer is not 16-byte aligned                */
+  HS_ERR_HIP = 7         /* the HIP runtime rejected a launch               */
+};
+
+typedef enum {
+  HS_F32 = 0,    /* IEEE binary32                                          */
+  HS_BF16 = 1,   /* bfloat16                                               */
+  HS_E4M3 = 2    /* OCP FP8 E4M3FN code (bias 7, no infinity, max 448)     */
+} hs_dtype;
+
+/* Error bits the resolve step ORs into hs_residency.err (device). */
+#define HS_DEVERR_VICTIMS 1   /* more faults than replaceable hot slots      */
+#define HS_DEVERR_NO_HOST 2   /* a selected token is neither resident, hot,
+                                 nor present in the host pool                */
+
+/* Batch geometry shared by all calls.
+ * B requests with P query positions each.  Request b has T_b = ctx_len[b]
+ * cached tokens (0 <= T_b <= T_stride); query position p (0 <= p < P) sees the
+ * tokens 0 .. T_b - P + p (the P newest tokens are the P positions of a
+ * multi-token-prediction step; P = 4 for three speculative tokens, page "Un
+ * contexte d'un million sur huit H200", section "Les chiffres").
+ * T_stride is the row stride of every per-token array and a multiple of 64;
+ * every block table has max_blocks = T_stride / 64 columns. */
+typedef struct hs_batch {
+  int32_t B;               /* 1 .. 65535                                     */
+  int32_t P;               /* 1 .. 4                                         */
+  int32_t T_stride;        /* multiple of 64, 64 .. 2^24                     */
+  int32_t max_blocks;      /* T_stride / 64                                  */
+  const int32_t* ctx_len;  /* device [B] int32                               */
+} hs_batch;
+
+/* Indexer scores (page "Un contexte d'un million sur huit H200", section
+ * "Ce qui se passe": an indexer selects the tokens sparse MLA attends to; its
+ * cache stays resident and is much smaller than the latent cache).  The pages
+ * give no formula; the one computed is
+ *
+ *   scores[b,p,t] = sum_h w[b,p,h] * max(0, sum_d q[b,p,h,d] * k[b,t,d]) + bias[b,t]
+ *
+ * for 0 <= t <= T_b - P + p, with one key per token shared by all heads.
+ *   q_idx     [B, P, H_idx, D_idx]   q_t = HS_BF16 (with k_t = HS_E4M3) or
+ *                                    HS_F32 (with k_t = HS_F32)
+ *   w         [B, P, H_idx] fp32, non-negative values need not hold
+ *   idx_pool  [N_blocks, 64, D_idx]  key of token t of request b is row t % 64
+ *                                    of block idx_bt[b, t / 64]
+ *   idx_scale [N_blocks] fp32 per-block dequantization scale, > 0, or NULL (= 1);
+ *             must be NULL for HS_F32 keys
+ *   idx_bt    [B, max_blocks] int32; entries for pages past T_b are never read
+ *   bias      [B, T_stride] fp32 or NULL
+ *   scores    [B, P, T_stride] fp32 output; entries past a position's visible
+ *             limit are left unspecified (hs_topk never reads them)
+ * Supported: D_idx in {64, 128}; H_idx a multiple of 16 up to 64 on the
+ * HS_BF16/HS_E4M3 path (matrix cores, fp32 accumulation), 1 .. 64 on HS_F32.
+ * Keys, queries and scores need 16-byte alignment. */
+hs_status hs_indexer_scores(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
+                            hs_dtype q_t, const void* q_idx, const float* w,
+                            hs_dtype k_t, const void* idx_pool, const float* idx_scale,
+                            const int32_t* idx_bt, const float* bias, float* scores,
+                            void* stream);
+
+/* Top-K per query position (page "Un contexte d'un million sur huit H200",
+ * section "Ce qui se passe"; K = 2048 on "vLLM sert GLM-5.3 en contexte 1M sur
+ * 16 H200", section "Comment s'y prendre").  For each (b, p): the K largest
+ * scores among the visible tokens, ties going to the lower token index; written
+ * in ascending token order.  A position that sees n <= K tokens selects all n,
+ * followed by -1.  Scores must not be NaN; -0.0 equals +0.0.
+ *   scores [B, P, T_stride] fp32, topk [B, P, K] int32 output.
+ * 1 <= K <= 8192.  Workspace: hs_workspace_bytes(HS_OP_TOPK, ...). */
+hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t* topk,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Residency state of a batch: one shared paged pool of latent rows on the GPU,
+ * per-request hot buffers made of ordinary pool blocks (page "Un contexte d'un
+ * million sur huit H200", section "Les trois états de résidence", last
+ * paragraph) and a pinned host pool.  The tables are read and updated in place
+ * by hs_resolve_rows. */
+typedef struct hs_residency {
+  int32_t C;                  /* hot rows per request: 0, or a multiple of 64
+                                 with C >= P*K (the pages' default is 2K, and
+                                 (num_speculative_tokens + 2) K with MTP,
+                                 section "Ce qu'il faut en retenir")         */
+  int32_t L;                  /* latent layers sharing this state, 1 .. 16   */
+  hs_dtype kv_t;              /* HS_E4M3 (row_scale/host_scale required) or
+                                 HS_F32 (scales must be NULL)                */
+  int32_t pad_;
+  int64_t pool_layer_rows;    /* rows from one layer to the next in pool and
+                                 row_scale (>= rows used by the block ids)   */
+  int64_t host_layer_rows;    /* same for host_rows / host_scale             */
+  const int32_t* bt;          /* [B, max_blocks] pool block of a resident
+                                 page, -1 = page not resident               */
+  const int32_t* hot_blocks;  /* [B, C/64] pool blocks of the hot buffer;
+                                 slot v is row hot_blocks[b, v/64]*64 + v%64 */
+  int32_t* tok2slot;          /* [B, T_stride] hot slot of a token, -1 = none */
+  int32_t* slot2tok;          /* [B, C] token in a slot, -1 = empty          */
+  int32_t* stamp;             /* [B, C] last step that used the slot, 0 = never */
+  int32_t* step;              /* [1] step counter, incremented per call      */
+  int32_t* err;               /* [1] device error bits (HS_DEVERR_*), OR-ed  */
+  void* pool;                 /* [L, pool_layer_rows, 576] rows             */
+  float* row_scale;           /* [L, pool_layer_rows] per-row fp32 scale     */
+  const void* host_rows;      /* pinned host [L, host_layer_rows, 576], given
+                                 by its device-accessible address; may be
+                                 NULL when no page is host-only              */
+  const float* host_scale;    /* pinned host [L, host_layer_rows]            */
+  const int64_t* host_bt;     /* [B, max_blocks] host row of token 64*j of
+                                 page j, -1 = page has no host copy          */
+} hs_residency;
+
+/* Fused resolve (page "Un contexte d'un million sur huit H200", section "Les
+ * trois états de résidence": resident tokens are read in place, hot tokens
+ * refresh their LRU entry, a fault copies one row from pinned host memory, and
+ * no CPU decision sits on the path).  The pages give no LRU policy; the one
+ * implemented, bit-exact with the oracle:
+ *   s = step + 1 for the call.  Per request, U = the sorted distinct tokens of
+ *   topk[b]; each t in U (page j = t/64) is RESIDENT if bt[b,j] >= 0, a HIT if
+ *   tok2slot[b,t] >= 0 (its stamp becomes s), else a FAULT (ascending order).
+ *   Victims are the slots with stamp < s ordered by (stamp, slot); the i-th
+ *   fault takes the i-th victim, evicting its previous token, and the 576-value
+ *   row host_rows[l, host_bt[b,j] + t%64] and its scale are copied to the
+ *   slot's pool row in every layer l.  step becomes s.
+ * Outputs:
+ *   row_ids [B, P, K] int32: pool row of topk[b,p,k], -1 for -1 entries
+ *   faults  [B, P*K, 2] int32: (token, slot) of each served fault, ascending
+ *           tokens; entries past counts[b][2] are unspecified
+ *   counts  [B, 4] int32: resident, hits, faults served, evictions (over U)
+ * Faults beyond the replaceable slots and tokens with no copy anywhere get row
+ * -1 and set HS_DEVERR_* bits; with C >= P*K and a host copy of every
+ * non-resident page neither can happen.  P*K <= 8192.  No workspace is needed
+ * (ws may be NULL, ws_bytes 0). */
+hs_status hs_resolve_rows(const hs_batch* batch, int32_t K, const int32_t* topk,
+                          const hs_residency* res, int32_t* row_ids, int32_t* faults,
+                          int32_t* counts, void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse MLA decode attention in the absorbed (MQA) form that the
+ * sparse_mla_force_mqa option keeps on the sparse kernel (page "vLLM sert
+ * GLM-5.3 en contexte 1M sur 16 H200", section "Comment s'y prendre"): all Hq
+ * heads attend over the same selected latent rows x (576 values), which are
+ * the keys; the values are their first 512 values:
+ *   z_j = sm_scale * row_scale[r_j] * (q[b,p,h,:] . code(r_j))
+ *   out[b,p,h,:] = sum_j softmax(z)_j * row_scale[r_j] * code(r_j)[0:512]
+ *   lse[b,p,h]   = ln sum_j exp(z_j)
+ * over the rows r_j = row_ids[b,p,j] >= 0, j ascending; -1 entries are skipped.
+ * With no valid row the output is 0 and lse is -inf.  The reduction order
+ * depends only on the order of row_ids, never on the row addresses.
+ *   q       [B, P, Hq, 576]   HS_BF16 with kv_t = HS_E4M3, or HS_F32 with HS_F32
+ *   pool    [rows, 576] one layer's rows; row_scale [rows] fp32 (E4M3 only,
+ *           NULL for F32)
+ *   out     [B, P, Hq, 512] fp32; lse [B, P, Hq] fp32 or NULL
+ * Hq = 16 (one head shard).  1 <= K <= 8192.
+ * Workspace: hs_workspace_bytes(HS_OP_MLA, ...). */
+hs_status hs_sparse_mla_decode(const hs_batch* batch, int32_t K, int32_t Hq, hs_dtype q_t,
+                               const void* q, hs_dtype kv_t, const void* pool,
+                               const float* row_scale, const int32_t* row_ids,
+                               float sm_scale, float* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream);
+
+#define HS_OP_INDEXER 0
+#define HS_OP_TOPK 1
+#define HS_OP_RESOLVE 2
+#define HS_OP_MLA 3
+
+/* Device workspace in bytes needed by `op` for these sizes (0 if none). */
+size_t hs_workspace_bytes(int32_t op, int32_t B, int32_t P, int32_t T_stride, int32_t K,
+                          int32_t Hq);
+
+/* Device-accessible address of pinned host memory allocated with
+ * hipHostMalloc (or torch pin_memory); HS_ERR_HIP if it is not pinned. */
+hs_status hs_host_device_ptr(const void* pinned_host, const void** dev_ptr);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* hs_last_error(void);
+
+/* HS_ABI_VERSION of the loaded library. */
+int32_t hs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS_H */

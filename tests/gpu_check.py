@@ -1,0 +1,159 @@
+"""Stage-isolated comparison of one GPU decode step against the oracle.
+
+Each GPU stage is checked against the oracle stage fed with the inputs that
+GPU stage consumed: GPU scores vs oracle scores (floating point); GPU top-K vs
+the oracle's top-K of the GPU scores (exact) and of the oracle scores (swaps
+only among near-ties); GPU resolve vs the oracle resolve of the GPU top-K
+(bit-exact tables, rows, faults, counts and copied bytes); GPU attention vs the
+oracle attention over the GPU top-K (max relative error per output vector).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import attention as o_attn, indexer as o_idx, resolve as o_res, topk as o_topk
+
+SCORE_RTOL = 2e-5       # |gpu - oracle| / max|S| of the row (fp32 accumulation)
+TOPK_TIE_REL = 1e-3     # swaps allowed only within 1e-3 relative of the K-th score
+
+
+def oracle_state(wl):
+    return o_res.ResidencyState(wl.bt.copy(), wl.hot_blocks.copy(), wl.tok2slot.copy(),
+                                wl.slot2tok.copy(), wl.stamp.copy(), wl.host_bt.copy(), int(wl.step))
+
+
+def check_scores(wl, q_idx, scores, rows=None, sample=None, rng=None):
+    """Compare GPU scores with the oracle: every visible token of the listed
+    (b, p) rows, or a random sample of tokens per row when ``sample`` is set."""
+    B, P = wl.B, wl.P
+    rows = rows if rows is not None else [(b, p) for b in range(B) for p in range(P)]
+    worst = 0.0
+    if sample is None:
+        S = o_idx.indexer_scores(q_idx, wl.q_dtype, wl.w, wl.idx_pool, wl.k_dtype, wl.idx_scale,
+                                 wl.idx_bt, wl.ctx_len, wl.bias, T_stride=wl.T_stride)
+    for b, p in rows:
+        n = max(o_idx.visible_limit(int(wl.ctx_len[b]), P, p) + 1, 0)
+        if n == 0:
+            continue
+        if sample is None:
+            ref = S[b, p, :n]
+            got = scores[b, p, :n].astype(np.float64)
+        else:
+            toks = np.unique(np.concatenate([rng.integers(0, n, sample), [0, n - 1]]))
+            ref = o_idx.indexer_scores_at(q_idx, wl.q_dtype, wl.w, wl.idx_pool, wl.k_dtype,
+                                          wl.idx_scale, wl.idx_bt, b, p, toks, wl.bias)
+            got = scores[b, p, toks].astype(np.float64)
+        scale = max(np.max(np.abs(ref)), 1e-30)
+        err = float(np.max(np.abs(got - ref)) / scale)
+        worst = max(worst, err)
+        assert err <= SCORE_RTOL, (b, p, err)
+    return worst, (S if sample is None else None)
+
+
+def check_topk_exact(wl, scores, topk):
+    """GPU top-K equals the oracle top-K of the very same (GPU) scores."""
+    ref = o_topk.topk(scores.astype(np.float64), wl.ctx_len, wl.K)
+    bad = np.argwhere(np.any(ref != topk, axis=2))
+    assert len(bad) == 0, f"top-K differs for (b,p) {bad[:5].tolist()}"
+
+
+def check_topk_vs_oracle_scores(wl, S_oracle, topk):
+    """Against the oracle's own scores: equal sizes, and every token in the
+    symmetric difference scores within 1e-3 relative of the K-th score."""
+    n_swaps = 0
+    for b in range(wl.B):
+        for p in range(wl.P):
+            n = max(o_idx.visible_limit(int(wl.ctx_len[b]), wl.P, p) + 1, 0)
+            G = topk[b, p][topk[b, p] >= 0]
+            O = o_topk.topk_row(S_oracle[b, p], n, wl.K)
+            O = O[O >= 0]
+            assert len(G) == len(O) == min(n, wl.K)
+            diff = np.setxor1d(G, O)
+            if len(diff) == 0:
+                continue
+            sk = o_topk.kth_score(S_oracle[b, p], n, wl.K)
+            assert np.all(np.abs(S_oracle[b, p, diff] - sk) <= TOPK_TIE_REL * abs(sk)), (b, p)
+            n_swaps += len(diff)
+    return n_swaps
+
+
+def check_resolve(wl, ostate, topk, got: dict):
+    """Bit-exact: rows, counts, fault lists, tables, step and error bits."""
+    new, rr = o_res.resolve(topk, ostate)
+    assert np.array_equal(got["row_ids"], rr.row_ids), "row ids"
+    assert np.array_equal(got["counts"], rr.counts), (got["counts"][:4], rr.counts[:4])
+    for b in range(wl.B):
+        n = rr.counts[b, 2]
+        assert np.array_equal(got["faults"][b, :n], rr.faults[b]), f"faults of request {b}"
+    assert got["step"] == new.step and got["err"] == rr.err
+    if wl.C:
+        for name in ("tok2slot", "slot2tok", "stamp"):
+            assert np.array_equal(got[name], getattr(new, name)), name
+    return new, rr
+
+
+def check_copies(wl, rr, pool, row_scale, max_per_request=None):
+    """Every faulted row's bytes (and scale) in every layer equal the host row."""
+    for b in range(wl.B):
+        cl = rr.copies[b]
+        if max_per_request is not None:
+            cl = cl[:max_per_request]
+        for hr, pr in cl:
+            bb, t = divmod(int(hr), wl.T_stride)
+            assert bb == b
+            for l in range(wl.L):
+                assert np.array_equal(pool[l, pr], wl.lat[l, b, t]), (b, t, l)
+                if row_scale is not None:
+                    assert row_scale[l, pr] == wl.lat_scale[l, b, t // 64]
+
+
+def check_attention(wl, q_layers, topk, out, lse, tol, pairs=None):
+    """Max relative error per output vector against the oracle over the same selection."""
+    worst = 0.0
+    for l in range(wl.L):
+        ref_o, ref_l = o_attn.sparse_mla(q_layers[l], wl.q_dtype, wl.lat[l],
+                                         None if wl.lat_scale is None else wl.lat_scale[l],
+                                         wl.kv_dtype, topk, wl.sm_scale, pairs=pairs)
+        todo = pairs if pairs is not None else [(b, p) for b in range(wl.B) for p in range(wl.P)]
+        for b, p in todo:
+            e = o_attn.max_rel_err(out[l, b, p], ref_o[b, p])
+            worst = max(worst, e)
+            assert e <= tol, (l, b, p, e)
+            fin = np.isfinite(ref_l[b, p])
+            assert np.array_equal(fin, np.isfinite(lse[l, b, p]))
+            if fin.any():
+                assert np.max(np.abs(lse[l, b, p][fin] - ref_l[b, p][fin])) <= max(tol, 1e-5) * 10
+    return worst
+
+
+def gpu_outputs(ds) -> dict:
+    import torch
+    torch.cuda.synchronize()
+    g = {"scores": ds.scores.cpu().numpy(), "topk": ds.topk.cpu().numpy(),
+         "row_ids": ds.row_ids.cpu().numpy(), "counts": ds.counts.cpu().numpy(),
+         "faults": ds.faults.cpu().numpy(), "out": ds.out.cpu().numpy(),
+         "lse": ds.lse.cpu().numpy()}
+    g.update(ds.state_numpy())
+    return g
+
+
+def full_check(ds, wl, ostate, s=1, attn_tol=2e-2, check_oracle_topk=True, pairs=None,
+               score_sample=None, rng=None, copies=True, copy_limit=None):
+    """Run the GPU step s (inputs already set) and check every stage."""
+    q_idx, q = wl.step_inputs(s)
+    g = gpu_outputs(ds)
+    rows = None
+    worst_s, S = check_scores(wl, q_idx, g["scores"], sample=score_sample,
+                              rng=rng or np.random.default_rng(0))
+    check_topk_exact(wl, g["scores"], g["topk"])
+    swaps = 0
+    if check_oracle_topk and S is not None:
+        swaps = check_topk_vs_oracle_scores(wl, S, g["topk"])
+    new, rr = check_resolve(wl, ostate, g["topk"], g)
+    if copies and wl.C:
+        pool = ds.pool.cpu().numpy()
+        rsc = None if ds.row_scale is None else ds.row_scale.cpu().numpy()
+        check_copies(wl, rr, pool, rsc, copy_limit)
+    worst_a = check_attention(wl, q, g["topk"], g["out"], g["lse"], attn_tol, pairs)
+    return new, rr, {"score_err": worst_s, "attn_err": worst_a, "topk_swaps": swaps,
+                     "counts": g["counts"]}

@@ -1,0 +1,91 @@
+"""The C-ABI library: loads, exports every declared symbol, validates on the
+host, and its struct layouts match the binding (CPU only, no compute calls)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from decode_indexer_logits_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hs.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True,
+                         text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+    assert _lib.abi_version() == 1
+
+
+def test_struct_layout_matches_header(tmp_path):
+    c = tmp_path / "probe.c"
+    c.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "hs.h"\n'
+                 "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(hs_batch),"
+                 " offsetof(hs_batch, ctx_len), sizeof(hs_residency),"
+                 " offsetof(hs_residency, pool_layer_rows), offsetof(hs_residency, bt),"
+                 " offsetof(hs_residency, host_bt)); return 0;}\n")
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)], check=True)
+    vals = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()))
+    assert vals == [ctypes.sizeof(_lib.Batch), _lib.Batch.ctx_len.offset,
+                    ctypes.sizeof(_lib.Residency), _lib.Residency.pool_layer_rows.offset,
+                    _lib.Residency.bt.offset, _lib.Residency.host_bt.offset]
+
+
+def test_host_validation_rejects_bad_arguments_without_launching():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(16)            # never dereferenced: validation fails first
+    b = _lib.Batch(2, 1, 1024, 16, 16)
+    assert lib.hs_topk(None, 8, fake, fake, fake, 1 << 30, None) == 1
+    assert lib.hs_topk(ctypes.byref(b), 0, fake, fake, fake, 1 << 30, None) == 2
+    assert lib.hs_topk(ctypes.byref(b), 9000, fake, fake, fake, 1 << 30, None) == 2
+    assert lib.hs_topk(ctypes.byref(b), 8, fake, fake, fake, 10, None) == 5
+    assert "workspace" in _lib.last_error()
+    bad = _lib.Batch(2, 5, 1024, 16, 16)
+    assert lib.hs_topk(ctypes.byref(bad), 8, fake, fake, fake, 1 << 30, None) == 2
+    bad = _lib.Batch(2, 1, 1000, 15, 16)
+    assert lib.hs_topk(ctypes.byref(bad), 8, fake, fake, fake, 1 << 30, None) == 2
+    # indexer dtype and shape checks
+    assert lib.hs_indexer_scores(ctypes.byref(b), 64, 96, 1, fake, fake, 2, fake, None, fake,
+                                 None, fake, None) == 2
+    assert lib.hs_indexer_scores(ctypes.byref(b), 64, 128, 1, fake, fake, 0, fake, None, fake,
+                                 None, fake, None) == 3
+    assert lib.hs_indexer_scores(ctypes.byref(b), 24, 128, 1, fake, fake, 2, fake, None, fake,
+                                 None, fake, None) == 2
+    assert lib.hs_indexer_scores(ctypes.byref(b), 64, 128, 1, ctypes.c_void_p(17), fake, 2, fake,
+                                 None, fake, None, fake, None) == 6
+    # resolve: capacity rule C >= P*K
+    res = _lib.Residency(128, 1, 2, 0, 0, 0, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16)
+    assert lib.hs_resolve_rows(ctypes.byref(b), 256, fake, ctypes.byref(res), fake, fake, fake,
+                               None, 0, None) == 4
+    assert "C=128" in _lib.last_error()
+    res.C = 100
+    assert lib.hs_resolve_rows(ctypes.byref(b), 64, fake, ctypes.byref(res), fake, fake, fake,
+                               None, 0, None) == 2
+    # attention: one shard of 16 heads; workspace
+    assert lib.hs_sparse_mla_decode(ctypes.byref(b), 2048, 32, 1, fake, 2, fake, fake, fake,
+                                    0.1, fake, None, None, 0, None) == 2
+    assert lib.hs_sparse_mla_decode(ctypes.byref(b), 2048, 16, 1, fake, 2, fake, fake, fake,
+                                    0.1, fake, None, None, 0, None) == 5
+
+
+def test_workspace_sizes():
+    assert _lib.workspace_bytes(_lib.HS_OP_TOPK, 32, 1, 131072, 2048) >= 32 * 131072 * 8
+    assert _lib.workspace_bytes(_lib.HS_OP_RESOLVE, 32, 1, 131072, 2048) == 0
+    # 32 positions x 2048 rows split over many workgroups -> partials needed
+    assert _lib.workspace_bytes(_lib.HS_OP_MLA, 32, 1, 131072, 2048) > 0

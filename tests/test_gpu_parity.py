@@ -1,0 +1,202 @@
+"""GPU parity of the HIP decode step against the oracle, through the C ABI.
+
+Sizes here finish in seconds on the oracle and still span many tiles, ragged
+contexts and the degenerate cases; the full-size workloads are in
+test_gpu_fullsize.py.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+from workloads import gen
+from workloads.calibrate_mixed import calibrate
+import gpu_check as gc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_indexer_logits_amd import _lib
+    _lib.load()
+
+
+def _run(wl, s=1, **kw):
+    from decode_indexer_logits_amd.device import DeviceStep
+    ds = DeviceStep(wl)
+    if s != 1:
+        ds.set_queries(s)
+    ds.run()
+    return ds
+
+
+@pytest.mark.parametrize("K", [256, 4096, 8192])
+def test_tiny_fp32(K):
+    _say(f"tiny_fp32 K={K}")
+    wl = gen.tiny_fp32(K=K)
+    ds = _run(wl)
+    _, _, info = gc.full_check(ds, wl, gc.oracle_state(wl), attn_tol=1e-5)
+    _say(info)
+    if K >= 4096:
+        # K >= context: sparse attention over all rows = dense attention
+        from oracle import attention as oa
+        g = gc.gpu_outputs(ds)
+        do, dl = oa.dense_mla(wl.q[0], "f32", wl.lat[0], None, "f32", wl.ctx_len, wl.sm_scale)
+        assert oa.max_rel_err(g["out"][0], do) <= 1e-5
+        assert np.max(np.abs(g["lse"][0] - dl)) <= 1e-5
+
+
+def test_tiny_fp32_ragged_and_short():
+    # a context that is not a multiple of 64 and shorter than K
+    for T, K in ((4000, 256), (100, 256), (1, 8)):
+        _say(f"tiny_fp32 T={T} K={K}")
+        wl = gen.tiny_fp32(K=K, T=T)
+        ds = _run(wl)
+        gc.full_check(ds, wl, gc.oracle_state(wl), attn_tol=1e-5)
+
+
+def test_resident_fp8():
+    _say("resident_fp8 full size")
+    wl = gen.resident_fp8()
+    ds = _run(wl)
+    _, _, info = gc.full_check(ds, wl, gc.oracle_state(wl), attn_tol=2e-2)
+    _say(info)
+
+
+def test_resident_fp8_ragged_batch():
+    _say("resident_fp8 ragged small")
+    wl = gen.resident_fp8(B=5, T_lo=1, T_hi=3000, K=512)
+    ds = _run(wl)
+    _, _, info = gc.full_check(ds, wl, gc.oracle_state(wl), attn_tol=2e-2)
+    _say(info, wl.ctx_len)
+
+
+def _mixed_small(B=4, T=16384, K=512, tail=1024, seed=1003):
+    beta, hot, frac = calibrate(seed=seed, B=B, T=T, K=K, tail=tail)
+    return gen.mixed_128k(seed=seed, B=B, T=T, K=K, tail=tail, beta=beta, hot_tokens=hot)
+
+
+def test_mixed_small_faults_hits_evictions():
+    _say("mixed small")
+    wl = _mixed_small()
+    ds = _run(wl)
+    new, rr, info = gc.full_check(ds, wl, gc.oracle_state(wl), attn_tol=2e-2)
+    _say(info)
+    c = info["counts"]
+    assert np.all(c[:, 1] >= wl.K // 2 - 16)      # about half of the top-K hit
+    assert np.all(c[:, 2] > 0) and np.all(c[:, 3] == c[:, 2])   # full buffers: every fault evicts
+
+
+def test_mtp3_small_multi_step():
+    _say("mtp3 small, 3 steps")
+    wl = gen.mtp3_agentic(B=3, K=128, steps=3, first_turn=6000, per_turn=300, turns=5, out_max=50)
+    from decode_indexer_logits_amd.device import DeviceStep
+    ds = DeviceStep(wl)
+    ost = gc.oracle_state(wl)
+    for s in range(1, wl.steps + 1):
+        ds.set_queries(s)
+        ds.run()
+        ost, rr, info = gc.full_check(ds, wl, ost, s=s, attn_tol=2e-2)
+        _say(s, info["counts"].tolist())
+
+
+def test_norescache_small_hit_rate_warms_up():
+    _say("no-residency small, 4 steps")
+    wl = gen.norescache_1m(B=2, T=32768, K=256, L=2, steps=4)
+    from decode_indexer_logits_amd.device import DeviceStep
+    ds = DeviceStep(wl)
+    ost = gc.oracle_state(wl)
+    rates = []
+    for s in range(1, wl.steps + 1):
+        ds.set_queries(s)
+        ds.run()
+        ost, rr, info = gc.full_check(ds, wl, ost, s=s, attn_tol=2e-2)
+        c = info["counts"]
+        if s == 1:
+            assert np.all(c[:, 1] == 0) and np.all(c[:, 2] == wl.K) and np.all(c[:, 3] == 0)
+        rates.append(float(c[:, 1].sum() / max(c[:, 1].sum() + c[:, 2].sum(), 1)))
+    _say("hit rates", rates)
+    assert rates[0] == 0.0 and rates[-1] > 0.5
+
+
+def _relayout(wl, mode, seed=5):
+    """The same logical data with every page resident ("full") or none ("none")."""
+    B, nb = wl.B, wl.T_stride // 64
+    rng = np.random.default_rng(seed)
+    nblk = [-(-int(t) // 64) for t in wl.ctx_len]
+    hot_b = wl.C // 64
+    if mode == "full":
+        n_res = sum(nblk)
+    else:
+        n_res = 0
+    perm = rng.permutation(n_res + B * hot_b).astype(np.int32)
+    bt = np.full((B, nb), -1, np.int32)
+    off = 0
+    if mode == "full":
+        for b in range(B):
+            bt[b, :nblk[b]] = perm[off:off + nblk[b]]
+            off += nblk[b]
+    hot = perm[off:].reshape(B, hot_b)
+    return dataclasses.replace(wl, n_pool_blocks=n_res + B * hot_b, bt=bt, hot_blocks=hot,
+                               tok2slot=np.full_like(wl.tok2slot, -1),
+                               slot2tok=np.full_like(wl.slot2tok, -1),
+                               stamp=np.zeros_like(wl.stamp), step=0)
+
+
+def test_residency_invariance_bit_identical():
+    _say("residency invariance")
+    wl = _mixed_small(B=3, T=8192, K=256, tail=512)
+    outs = {}
+    for mode in ("mixed", "full", "none"):
+        w = wl if mode == "mixed" else _relayout(wl, mode)
+        ds = _run(w)
+        g = gc.gpu_outputs(ds)
+        gc.check_resolve(w, gc.oracle_state(w), g["topk"], g)
+        outs[mode] = (g["topk"], g["out"], g["lse"], g["counts"])
+        _say(mode, g["counts"].tolist())
+    for mode in ("full", "none"):
+        assert np.array_equal(outs[mode][0], outs["mixed"][0])
+        assert np.array_equal(outs[mode][1], outs["mixed"][1]), mode
+        assert np.array_equal(outs[mode][2], outs["mixed"][2]), mode
+    assert np.all(outs["full"][3][:, 0] == wl.K) and np.all(outs["none"][3][:, 0] == 0)
+
+
+def test_graph_capture_replays_match_eager():
+    _say("graph capture")
+    wl = _mixed_small(B=2, T=8192, K=256, tail=512)
+    from decode_indexer_logits_amd.device import DeviceStep
+    ds = DeviceStep(wl)
+    snap = ds.snapshot()
+    ds.run()
+    ref = gc.gpu_outputs(ds)
+    ds.restore(snap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            ds.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ds.restore(snap)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = gc.gpu_outputs(ds)
+        for k in ("topk", "row_ids", "counts", "out", "lse", "tok2slot", "slot2tok", "stamp"):
+            assert np.array_equal(got[k], ref[k]), (rep, k)
+        assert got["step"] == ref["step"]
+        _ = torch.ones(1024, device="cuda").sum().item()   # unrelated eager work between replays
