@@ -20,8 +20,9 @@ DTYPES = {"f32": HS_F32, "bf16": HS_BF16, "e4m3": HS_E4M3}
 HS_OP_INDEXER, HS_OP_TOPK, HS_OP_RESOLVE, HS_OP_MLA = 0, 1, 2, 3
 DEVERR_VICTIMS, DEVERR_NO_HOST = 1, 2
 
-EXPORTS = ["hs_indexer_scores", "hs_topk", "hs_resolve_rows", "hs_sparse_mla_decode",
-           "hs_workspace_bytes", "hs_host_device_ptr", "hs_last_error", "hs_abi_version"]
+EXPORTS = ["hs_indexer_scores", "hs_topk", "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
+           "hs_sparse_mla_decode", "hs_workspace_bytes", "hs_host_device_ptr", "hs_last_error",
+           "hs_abi_version"]
 
 
 class HsError(RuntimeError):
@@ -60,10 +61,12 @@ def load() -> ctypes.CDLL:
     lib.hs_indexer_scores.argtypes = [P, c_int32, c_int32, c_int32, P, P, c_int32, P, P, P, P, P, P]
     lib.hs_topk.argtypes = [P, c_int32, P, P, P, c_size_t, P]
     lib.hs_resolve_rows.argtypes = [P, c_int32, P, P, P, P, P, P, c_size_t, P]
+    lib.hs_resolve_tables.argtypes = [P, c_int32, P, P, P, P, P, P]
+    lib.hs_copy_faults.argtypes = [P, c_int32, P, P, P, P]
     lib.hs_sparse_mla_decode.argtypes = [P, c_int32, c_int32, c_int32, P, c_int32, P, P, P,
                                          c_float, P, P, P, c_size_t, P]
-    for f in ("hs_indexer_scores", "hs_topk", "hs_resolve_rows", "hs_sparse_mla_decode",
-              "hs_host_device_ptr"):
+    for f in ("hs_indexer_scores", "hs_topk", "hs_resolve_rows", "hs_resolve_tables",
+              "hs_copy_faults", "hs_sparse_mla_decode", "hs_host_device_ptr"):
         getattr(lib, f).restype = c_int32
     lib.hs_workspace_bytes.argtypes = [c_int32] * 6
     lib.hs_workspace_bytes.restype = c_size_t
@@ -129,6 +132,17 @@ def resolve_rows(batch: Batch, K: int, topk_t, res: Residency, row_ids, faults, 
     _check(load().hs_resolve_rows(ctypes.byref(batch), K, _ptr(topk_t), ctypes.byref(res),
                                   _ptr(row_ids), _ptr(faults), _ptr(counts), None, 0,
                                   _stream(stream)))
+
+
+def resolve_tables(batch: Batch, K: int, topk_t, res: Residency, row_ids, faults, counts,
+                   stream=None):
+    _check(load().hs_resolve_tables(ctypes.byref(batch), K, _ptr(topk_t), ctypes.byref(res),
+                                    _ptr(row_ids), _ptr(faults), _ptr(counts), _stream(stream)))
+
+
+def copy_faults(batch: Batch, K: int, res: Residency, faults, counts, stream=None):
+    _check(load().hs_copy_faults(ctypes.byref(batch), K, ctypes.byref(res), _ptr(faults),
+                                 _ptr(counts), _stream(stream)))
 
 
 def sparse_mla_decode(batch: Batch, K: int, Hq: int, q_t: str, q, kv_t: str, pool, row_scale,

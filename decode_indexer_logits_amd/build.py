@@ -24,6 +24,7 @@ ARCH = "gfx950"
 SOURCES = ["indexer.hip", "topk.hip", "resolve.hip", "mla.hip", "hs_api.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function", f"-I{ROOT / 'include'}"]
 
 

@@ -96,21 +96,20 @@ hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t
   return launched(hs::launch_topk(d, K, scores, topk, ws, static_cast<hipStream_t>(stream)), "topk");
 }
 
-hs_status hs_resolve_rows(const hs_batch* batch, int32_t K, const int32_t* topk,
-                          const hs_residency* res, int32_t* row_ids, int32_t* faults,
-                          int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
-  hs::BatchDims d;
-  if (hs_status st = check_batch(batch, &d)) return st;
-  if (!topk || !res || !row_ids || !faults || !counts)
-    return fail(HS_ERR_NULL, "hs_resolve_rows: topk, res, row_ids, faults and counts are required");
+}  // extern "C"
+
+namespace {
+
+hs_status check_residency(const hs::BatchDims& d, int32_t K, const hs_residency* res,
+                          hs::ResidencyArgs* r) {
+  if (!res) return fail(HS_ERR_NULL, "residency is NULL");
   if (K < 1 || d.P * K > 8192) return fail(HS_ERR_SHAPE, "P*K=%d out of [1, 8192]", d.P * K);
   if (!res->bt || !res->step || !res->err || !res->pool)
     return fail(HS_ERR_NULL, "residency: bt, step, err and pool are required");
   if (res->L < 1 || res->L > 16) return fail(HS_ERR_SHAPE, "L=%d out of [1, 16]", res->L);
-  if (res->C < 0 || res->C % 64 || res->C > (1 << 20))
-    return fail(HS_ERR_SHAPE, "C=%d must be a multiple of 64 (0 = no hot buffers)", res->C);
+  if (res->C < 0 || res->C % 64 || res->C > 16384)
+    return fail(HS_ERR_SHAPE, "C=%d must be a multiple of 64 in [0, 16384] (0 = no hot buffers)",
+                res->C);
   if (res->C > 0 && res->C < d.P * K)
     return fail(HS_ERR_CAPACITY, "C=%d below P*K=%d: a step's faults could exceed its victims",
                 res->C, d.P * K);
@@ -134,27 +133,63 @@ hs_status hs_resolve_rows(const hs_batch* batch, int32_t K, const int32_t* topk,
     return fail(HS_ERR_ALIGN, "pool and host_rows need 16-byte alignment");
   if (res->pool_layer_rows < 0 || res->host_layer_rows < 0)
     return fail(HS_ERR_SHAPE, "layer strides must be non-negative");
+  r->C = res->C;
+  r->L = res->L;
+  r->kv_bytes = kv_bytes;
+  r->pool_layer_rows = res->pool_layer_rows;
+  r->host_layer_rows = res->host_layer_rows;
+  r->bt = res->bt;
+  r->hot_blocks = res->hot_blocks;
+  r->tok2slot = res->tok2slot;
+  r->slot2tok = res->slot2tok;
+  r->stamp = res->stamp;
+  r->step = res->step;
+  r->err = res->err;
+  r->pool = res->pool;
+  r->row_scale = res->row_scale;
+  r->host_rows = res->host_rows;
+  r->host_scale = res->host_scale;
+  r->host_bt = res->host_bt;
+  return HS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_resolve_tables(const hs_batch* batch, int32_t K, const int32_t* topk,
+                            const hs_residency* res, int32_t* row_ids, int32_t* faults,
+                            int32_t* counts, void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!topk || !row_ids || !faults || !counts)
+    return fail(HS_ERR_NULL, "resolve: topk, row_ids, faults and counts are required");
   hs::ResidencyArgs r;
-  r.C = res->C;
-  r.L = res->L;
-  r.kv_bytes = kv_bytes;
-  r.pool_layer_rows = res->pool_layer_rows;
-  r.host_layer_rows = res->host_layer_rows;
-  r.bt = res->bt;
-  r.hot_blocks = res->hot_blocks;
-  r.tok2slot = res->tok2slot;
-  r.slot2tok = res->slot2tok;
-  r.stamp = res->stamp;
-  r.step = res->step;
-  r.err = res->err;
-  r.pool = res->pool;
-  r.row_scale = res->row_scale;
-  r.host_rows = res->host_rows;
-  r.host_scale = res->host_scale;
-  r.host_bt = res->host_bt;
-  return launched(hs::launch_resolve(d, K, topk, r, row_ids, faults, counts,
-                                     static_cast<hipStream_t>(stream)),
+  if (hs_status st = check_residency(d, K, res, &r)) return st;
+  return launched(hs::launch_resolve_tables(d, K, topk, r, row_ids, faults, counts,
+                                            static_cast<hipStream_t>(stream)),
                   "resolve");
+}
+
+hs_status hs_copy_faults(const hs_batch* batch, int32_t K, const hs_residency* res,
+                         const int32_t* faults, const int32_t* counts, void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!faults || !counts) return fail(HS_ERR_NULL, "hs_copy_faults: faults and counts are required");
+  hs::ResidencyArgs r;
+  if (hs_status st = check_residency(d, K, res, &r)) return st;
+  return launched(hs::launch_fault_copy(d, K, r, faults, counts, static_cast<hipStream_t>(stream)),
+                  "fault copy");
+}
+
+hs_status hs_resolve_rows(const hs_batch* batch, int32_t K, const int32_t* topk,
+                          const hs_residency* res, int32_t* row_ids, int32_t* faults,
+                          int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (hs_status st = hs_resolve_tables(batch, K, topk, res, row_ids, faults, counts, stream))
+    return st;
+  return hs_copy_faults(batch, K, res, faults, counts, stream);
 }
 
 hs_status hs_sparse_mla_decode(const hs_batch* batch, int32_t K, int32_t Hq, hs_dtype q_t,

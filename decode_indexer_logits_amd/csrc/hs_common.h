@@ -17,12 +17,13 @@ typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 // Two OCP E4M3FN codes (bytes 0,1 of `w`, or bytes 2,3 when `hi`) -> two bf16
-// packed in one dword.  Every E4M3 value is exact in bf16 (3 mantissa bits,
-// exponents 2^-9 .. 2^8), so taking the upper half of the fp32 is exact.
+// packed in one dword, with gfx950's scaled converter at scale 1.  Every E4M3
+// value is exact in bf16 (3 mantissa bits, exponents 2^-9 .. 2^8).
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
-  f32x2_t f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true)
-                 : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // Eight E4M3 codes (two dwords) -> eight bf16 (an MFMA operand fragment).
@@ -33,6 +34,12 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   r[2] = e4m3x2_to_bf16x2(hi, false);
   r[3] = e4m3x2_to_bf16x2(hi, true);
   return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// max(x, 0) for a finite float as one integer max on its bits: a set sign bit
+// makes the integer negative, so -x and -0.0 both become +0.0.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {

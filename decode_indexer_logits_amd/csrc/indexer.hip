@@ -10,12 +10,13 @@
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulation) with heads as the M dimension
 // and tokens as N, so that after the product each lane holds four heads of
 // one token and the ReLU / weighted head sum needs only two cross-lane adds.
-// Keys are streamed once from HBM: a wave reads 16 tokens x D bytes, every
-// lane loading D/4 contiguous bytes of its token (the contraction index is
-// permuted consistently in both operands, which a sum allows), converts
-// E4M3 -> bf16 in registers (exact) and issues the products.  The next group's
-// loads are issued before the current group's products.  A block's dequant
-// scale factors out of ReLU (positive scale), so it multiplies the head sum.
+// Keys are streamed once from HBM a 64-token page (64 x D bytes) at a time: for
+// each 16-token group every lane loads D/4 contiguous bytes of its token (the
+// contraction index is permuted consistently in both operands, which a sum
+// allows), converts E4M3 -> bf16 in registers (exact) and issues the products.
+// Three pages are in flight per wave (a page is requested three pages before
+// it is consumed), and a page's 64 scores leave in one coalesced store.  A page's dequant scale
+// factors out of ReLU (positive scale), so it multiplies the head sum.
 //
 // Waves of a workgroup: with P positions, P groups of 4/P waves; each group
 // keeps its position's queries in registers (H x D bf16 spread over the wave)
@@ -32,7 +33,7 @@ struct IdxCfg {
   static constexpr int WPP = (P == 1) ? 4 : (P == 2 ? 2 : 1);   // waves per position
   static constexpr int NW = P * WPP;
   static constexpr int NT = NW * kWave;
-  static constexpr int TILE = (P <= 2) ? 512 : 256;             // tokens per workgroup
+  static constexpr int TILE = (P <= 2) ? 4096 : 1024;           // tokens per workgroup
 };
 
 template <int P, int DK, int HT>
@@ -44,9 +45,10 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     float* __restrict__ scores) {
   using Cfg = IdxCfg<P>;
   constexpr int H = 16 * HT;
-  constexpr int KS = DK / 32;   // k-steps of 32
-  constexpr int SEG = DK / 4;   // contiguous key bytes per lane
-  constexpr int NV = SEG / 16;  // 16-byte loads per lane per token group
+  constexpr int KS = DK / 32;    // k-steps of 32
+  constexpr int SEG = DK / 4;    // contiguous key bytes per lane per token
+  constexpr int NV = SEG / 16;   // 16-byte loads per lane per 16-token group
+  constexpr int LPB = 4 * NV;    // 16-byte loads per lane per 64-token page
   const int b = blockIdx.y;
   const int T = ctx_len[b];
   const int tile0 = blockIdx.x * Cfg::TILE;
@@ -72,61 +74,92 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[mt][i] = wp[16 * mt + 4 * g + i];
 
-  const int gend = min(Cfg::TILE / 16, (lim - tile0) / 16 + 1);
-  const int32_t* btb = bt + (size_t)b * max_blocks;
-  float* out = scores + (size_t)(b * P + p) * T_stride;
-  const float* biasb = bias ? bias + (size_t)b * T_stride : nullptr;
+  const int npages = min(Cfg::TILE / kBlock, (lim - tile0) / kBlock + 1);
+  const int32_t* btb = bt + (size_t)b * max_blocks + tile0 / kBlock;
+  float* out = scores + (size_t)(b * P + p) * T_stride + tile0;
+  const float* biasb = bias ? bias + (size_t)b * T_stride + tile0 : nullptr;
+  const int lim_t = lim - tile0;
 
-  uint4 cur[NV], nxt[NV];
-  int cur_blk = 0, nxt_blk = 0;
-  int gi = sub;
-  if (gi < gend) {
-    const int t0 = tile0 + 16 * gi;
-    cur_blk = btb[t0 >> 6];
-    const uint8_t* kp = pool + ((size_t)cur_blk * kBlock + (t0 & 63) + n) * DK + SEG * g;
+  // Page metadata of the whole tile is read once: lane l holds page l's
+  // physical block and scale (a tile has at most 64 pages), fetched later with
+  // readlane.  No load inside the page loop depends on another load, so the
+  // in-order memory counter never forces a wait on pages still in flight.
+  static_assert(Cfg::TILE / kBlock <= kWave, "one page per lane");
+  const int blk_l = lane < npages ? btb[lane] : 0;
+  const float sc_l = (scale && lane < npages) ? scale[blk_l] : 1.f;
+  auto page_blk = [&](int pi) { return __builtin_amdgcn_readlane(blk_l, pi); };
+  auto page_scale = [&](int pi) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
+  };
+  // lane (n, g) loads, for token 16j + n of a page, bytes SEG*g .. +SEG, and
+  // the bias of token 64*pi + lane.  Three pages are in flight per wave: page
+  // i+3W is requested as soon as page i has been consumed (W = waves sharing
+  // the position).
+  auto load_page = [&](int pi, uint4* buf, float& bs) {
+    const uint8_t* kp = pool + (size_t)page_blk(pi) * kBlock * DK + n * DK + SEG * g;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) cur[v] = *reinterpret_cast<const uint4*>(kp + 16 * v);
-  }
-  for (; gi < gend; gi += Cfg::WPP) {
-    const int gn = gi + Cfg::WPP;
-    if (gn < gend) {
-      const int t0 = tile0 + 16 * gn;
-      nxt_blk = btb[t0 >> 6];
-      const uint8_t* kp = pool + ((size_t)nxt_blk * kBlock + (t0 & 63) + n) * DK + SEG * g;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < NV; ++v) nxt[v] = *reinterpret_cast<const uint4*>(kp + 16 * v);
+      for (int v = 0; v < NV; ++v)
+        buf[j * NV + v] = *reinterpret_cast<const uint4*>(kp + 16 * j * DK + 16 * v);
+    const int tl = pi * kBlock + lane;
+    bs = (biasb && tl <= lim_t) ? biasb[tl] : 0.f;
+  };
+  auto consume_page = [&](int pi, const uint4* buf, float bs) {
+    float vj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8_t kb[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint4 c = buf[j * NV + (s >> 1)];
+        const uint32_t lo = (s & 1) ? c.z : c.x;
+        const uint32_t hi = (s & 1) ? c.w : c.y;
+        kb[s] = e4m3x8_to_bf16x8(lo, hi);
+      }
+      f32x4_t acc[HT];
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(qa[mt][s], kb[s], acc[mt]);
+      float v = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wv[mt][i], relu_bits(acc[mt][i]), v);
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      vj[j] = v;                  // every lane of column n holds token 16j + n
     }
-    bf16x8_t kb[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const uint4 c = cur[s >> 1];
-      const uint32_t lo = (s & 1) ? c.z : c.x;
-      const uint32_t hi = (s & 1) ? c.w : c.y;
-      kb[s] = e4m3x8_to_bf16x8(lo, hi);
+    // lane 16g + n stores token 16g + n of the page: one coalesced 256-byte store
+    const float mine = g == 0 ? vj[0] : (g == 1 ? vj[1] : (g == 2 ? vj[2] : vj[3]));
+    const int tl = pi * kBlock + lane;
+    if (tl <= lim_t) {
+      float sc = scale ? mine * page_scale(pi) : mine;
+      out[tl] = sc + bs;
     }
-    f32x4_t acc[HT];
-#pragma unroll
-    for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(qa[mt][s], kb[s], acc[mt]);
-    float v = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < HT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v = fmaf(wv[mt][i], fmaxf(acc[mt][i], 0.f), v);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    const int t = tile0 + 16 * gi + n;
-    if (g == 0 && t <= lim) {
-      float sc = scale ? v * scale[cur_blk] : v;
-      if (biasb) sc += biasb[t];
-      out[t] = sc;
-    }
-#pragma unroll
-    for (int vv = 0; vv < NV; ++vv) cur[vv] = nxt[vv];
-    cur_blk = nxt_blk;
+  };
+  // Pages of this wave: pi = sub + k*W, k < npw.  Loads are unconditional
+  // (past the end they re-read the last page, a cache hit) so that every
+  // iteration issues the same memory operations and the compiler can wait for
+  // exactly the oldest page instead of draining the queue.
+  constexpr int W = Cfg::WPP;
+  const int npw = (npages - sub + W - 1) / W;
+  auto page_of = [&](int k) { return min(sub + k * W, npages - 1); };
+  uint4 bufA[LPB], bufB[LPB], bufC[LPB];
+  float bsA, bsB, bsC;
+  load_page(page_of(0), bufA, bsA);
+  load_page(page_of(1), bufB, bsB);
+  load_page(page_of(2), bufC, bsC);
+  for (int k = 0; k < npw; k += 3) {
+    consume_page(sub + k * W, bufA, bsA);
+    load_page(page_of(k + 3), bufA, bsA);
+    if (k + 1 < npw) consume_page(sub + (k + 1) * W, bufB, bsB);
+    load_page(page_of(k + 4), bufB, bsB);
+    if (k + 2 < npw) consume_page(sub + (k + 2) * W, bufC, bsC);
+    load_page(page_of(k + 5), bufC, bsC);
   }
 }
 

@@ -78,11 +78,11 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
   const int32_t* rid_p = row_ids + (size_t)bp * K;
   const int r_local = 16 * wave + n;
 
-  for (int kt = kb; kt < ke; kt += kTile) {
+  // gather of one tile's rows for this lane (row r_local, bytes 144g .. +144)
+  auto gather = [&](int kt, int& rid, float& rs, uint4* raw) {
     const int kk = kt + r_local;
-    const int rid = (kk < ke) ? rid_p[kk] : -1;
-    uint4 raw[9];
-    float rs = 0.f;
+    rid = (kk < ke) ? rid_p[kk] : -1;
+    rs = 0.f;
     if (rid >= 0) {
       const uint4* src = reinterpret_cast<const uint4*>(pool + (size_t)rid * kDLat + 144 * g);
 #pragma unroll
@@ -92,6 +92,13 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
 #pragma unroll
       for (int v = 0; v < 9; ++v) raw[v] = make_uint4(0u, 0u, 0u, 0u);
     }
+  };
+  int rid, rid_n = -1;
+  float rs, rs_n = 0.f;
+  uint4 raw[9], raw_n[9];
+  gather(kb, rid, rs, raw);
+  for (int kt = kb; kt < ke; kt += kTile) {
+    if (kt + kTile < ke) gather(kt + kTile, rid_n, rs_n, raw_n);
     // S^T = X . Q^T over 576 values; stash the value part transposed
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -159,6 +166,10 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
       }
     }
     __syncthreads();
+    rid = rid_n;
+    rs = rs_n;
+#pragma unroll
+    for (int v = 0; v < 9; ++v) raw[v] = raw_n[v];
   }
 
   float lp = l_part;
@@ -266,18 +277,19 @@ __global__ __launch_bounds__(kMlaNT) void mla_f32_kernel(
   }
 }
 
-// Merges the slices of each (request, position) in slice order.
-__global__ __launch_bounds__(kMlaNT) void mla_combine_kernel(int nsplit, const float* __restrict__ part_o,
-                                                             const float* __restrict__ part_ml,
-                                                             float* __restrict__ out,
-                                                             float* __restrict__ lse) {
-  const int bp = blockIdx.x;
-  const int h = threadIdx.x >> 4, dq = threadIdx.x & 15;   // dims 32*dq .. +32
+// Merges the slices of each (request, position, head) in slice order: one
+// wave per (request, position, head), 8 output dims per lane.
+__global__ __launch_bounds__(kWave) void mla_combine_kernel(int nsplit, const float* __restrict__ part_o,
+                                                            const float* __restrict__ part_ml,
+                                                            float* __restrict__ out,
+                                                            float* __restrict__ lse) {
+  const int bp = blockIdx.x, h = blockIdx.y;
+  const int lane = threadIdx.x;
   float M = -INFINITY;
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(((size_t)bp * nsplit + s) * kHq + h) * 2]);
-  float acc[32];
+  float acc[8];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
   float L = 0.f;
   if (M != -INFINITY) {
     for (int s = 0; s < nsplit; ++s) {
@@ -286,10 +298,10 @@ __global__ __launch_bounds__(kMlaNT) void mla_combine_kernel(int nsplit, const f
       if (ms == -INFINITY) continue;
       const float wgt = exp2f(ms - M);
       L += part_ml[base * 2 + 1] * wgt;
-      const float4* src = reinterpret_cast<const float4*>(part_o + base * kDVal + 32 * dq);
+      const float4* src = reinterpret_cast<const float4*>(part_o + base * kDVal) + lane;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float4 v = src[j];
+      for (int j = 0; j < 2; ++j) {
+        const float4 v = src[64 * j];
         acc[4 * j + 0] = fmaf(v.x, wgt, acc[4 * j + 0]);
         acc[4 * j + 1] = fmaf(v.y, wgt, acc[4 * j + 1]);
         acc[4 * j + 2] = fmaf(v.z, wgt, acc[4 * j + 2]);
@@ -298,11 +310,12 @@ __global__ __launch_bounds__(kMlaNT) void mla_combine_kernel(int nsplit, const f
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float4* dst = reinterpret_cast<float4*>(out + ((size_t)bp * kHq + h) * kDVal + 32 * dq);
+  float4* dst = reinterpret_cast<float4*>(out + ((size_t)bp * kHq + h) * kDVal) + lane;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    dst[j] = make_float4(acc[4 * j] * inv, acc[4 * j + 1] * inv, acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
-  if (lse && dq == 0) lse[(size_t)bp * kHq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  for (int j = 0; j < 2; ++j)
+    dst[64 * j] = make_float4(acc[4 * j] * inv, acc[4 * j + 1] * inv, acc[4 * j + 2] * inv,
+                              acc[4 * j + 3] * inv);
+  if (lse && lane == 0) lse[(size_t)bp * kHq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 __host__ inline int rows_per_split_for(int K, int nsplit) {
@@ -315,7 +328,7 @@ __host__ inline int rows_per_split_for(int K, int nsplit) {
 int mla_num_splits(int B, int P, int K) {
   const int BP = B * P;
   const int max_split = (K + kTile - 1) / kTile;
-  int ns = (512 + BP - 1) / BP;
+  int ns = (256 + BP - 1) / BP;
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
   const int rps = rows_per_split_for(K, ns);
@@ -347,7 +360,7 @@ hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, const uint16_t* q, co
                      row_scale, row_ids, K, rps, ns, qk, out, lse, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP), dim3(kMlaNT), 0, s, ns, part_o, part_ml, out, lse);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq), dim3(kWave), 0, s, ns, part_o, part_ml, out, lse);
   return hipGetLastError();
 }
 
@@ -364,7 +377,7 @@ hipError_t launch_mla_f32(const BatchDims& d, int K, const float* q, const float
                      qk, ns > 1 ? 1 : 0, out, lse, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP), dim3(kMlaNT), 0, s, ns, part_o, part_ml, out, lse);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq), dim3(kWave), 0, s, ns, part_o, part_ml, out, lse);
   return hipGetLastError();
 }
 

@@ -11,8 +11,9 @@
 //              2. classify U in ascending order: resident page / hot hit
 //                 (stamp <- s) / fault, faults compacted in token order;
 //              3. victims: the |F| smallest (stamp, slot) keys among slots
-//                 with stamp < s, found by an MSD radix select over the key
-//                 bits that differ, then sorted in LDS (bitonic);
+//                 with stamp < s, emitted one distinct stamp at a time in slot
+//                 order (an MSD radix select plus an LDS sort when they span
+//                 many stamps);
 //              4. fault i takes victim i: evict, insert, stamp, record;
 //              5. row ids of every (position, k) from the updated tables.
 //   fault copy a grid over (request, fault): each 576-value row is read
@@ -28,7 +29,11 @@ namespace {
 constexpr int kResNT = 1024;
 constexpr int kMaxSel = 8192;   // P*K
 constexpr int kCopyNT = 256;
-constexpr int kFaultsPerWG = 8;
+constexpr int kFaultsPerWG = 2;    // more workgroups keep more host reads in flight
+constexpr int kMaxSlotsPerThread = 16;   // C <= 16384
+constexpr int kMaxStampRounds = 32;
+constexpr int kMaxEntriesPerThread = kMaxSel / kResNT;   // 8
+constexpr int kMaxHotBlocks = 16384 / 64;
 
 __device__ __forceinline__ int lower_bound_lds(const int32_t* a, int n, int x) {
   int lo = 0, hi = n;
@@ -85,23 +90,27 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
     const int32_t* __restrict__ step, int32_t* __restrict__ err,
     const int64_t* __restrict__ host_bt, int32_t* __restrict__ row_ids,
     int32_t* __restrict__ faults, int32_t* __restrict__ counts) {
-  __shared__ uint64_t sA64[kMaxSel];      // merge lists + merged run; later victim keys
-  __shared__ int32_t sF[kMaxSel];         // faulting tokens, ascending
+  // R1: merge lists, then victims (slots, or sorted 64-bit keys on the general path)
+  __shared__ uint64_t sA64[kMaxSel];
+  __shared__ int32_t sU[kMaxSel];          // U when P > 1
+  __shared__ int32_t sF[kMaxSel];          // faulting tokens, ascending
+  __shared__ int32_t sHot[kMaxHotBlocks];  // this request's hot blocks
   __shared__ int scratch[kResNT / kWave + 1];
   __shared__ uint32_t h256[256];
   __shared__ int s_nlist[4];
-  __shared__ int s_res, s_hit, s_ev, s_cnt, s_vcnt, s_d;
+  __shared__ int s_res, s_hit, s_ev, s_cnt, s_vcnt, s_d, s_next;
   __shared__ uint32_t s_before;
   __shared__ unsigned long long s_kmin, s_kmax;
   int32_t* sA = reinterpret_cast<int32_t*>(sA64);
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = lane_id();
   const int s = step[0] + 1;
   const int PK = P * K;
   const int32_t* tk = topk + (size_t)b * PK;
   const int32_t* btb = bt + (size_t)b * max_blocks;
-  const int64_t* hbt = host_bt + (size_t)b * max_blocks;
+  const int64_t* hbt = host_bt ? host_bt + (size_t)b * max_blocks : nullptr;
   int32_t* t2s = tok2slot + (size_t)b * T_stride;
   int32_t* s2t = slot2tok + (size_t)b * C;
   int32_t* stp = stamp + (size_t)b * C;
@@ -116,20 +125,29 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
     s_kmin = ~0ull;
     s_kmax = 0ull;
   }
+  for (int i = tid; i < (C >> 6); i += kResNT) sHot[i] = hot_blocks[(size_t)b * (C >> 6) + i];
   __syncthreads();
 
-  // 1. U: sorted distinct selected tokens
-  int32_t* Lin = sA;             // P lists of K, each sorted with a -1 tail
+  // 1. U = sorted distinct selected tokens.  Each list is sorted with a -1
+  // tail; valid entries are counted with one ballot per wave.
+  int32_t* Lin = sA;             // P lists of K
   int32_t* M = sA + kMaxSel;     // merged run with duplicates
-  for (int e = tid; e < PK; e += kResNT) {
-    const int x = tk[e];
-    Lin[e] = x;
-    if (x >= 0) atomicAdd(&s_nlist[e / K], 1);
+  for (int base = 0; base < PK; base += kResNT) {
+    const int e = base + tid;
+    const int x = e < PK ? tk[e] : -1;
+    if (e < PK) Lin[e] = x;
+    // one list per wave-aligned run of K (K may not be a multiple of 64): count per list
+    for (int p = 0; p < P; ++p) {
+      const uint64_t m = __ballot(x >= 0 && e / K == p);
+      if (lane == 0 && m) atomicAdd(&s_nlist[p], __popcll(m));
+    }
   }
   __syncthreads();
   int nU;
+  const int32_t* U;
   if (P == 1) {
     nU = s_nlist[0];
+    U = Lin;
   } else {
     int total = 0;
     for (int p = 0; p < P; ++p) total += s_nlist[p];
@@ -153,98 +171,173 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
       const int x = idx < total ? M[idx] : 0;
       int tot;
       const int ex = block_exclusive_scan<kResNT>(keep ? 1 : 0, scratch, &tot);
-      if (keep) Lin[run + ex] = x;
+      if (keep) sU[run + ex] = x;
       run += tot;
     }
     nU = run;
+    U = sU;
     __syncthreads();
   }
-  const int32_t* U = Lin;
 
-  // 2. classify in ascending token order
-  int my_res = 0, my_hit = 0, nF = 0;
-  for (int base = 0; base < nU; base += kResNT) {
-    const int idx = base + tid;
-    bool is_f = false;
-    int t = 0;
-    if (idx < nU) {
-      t = U[idx];
-      const int j = t >> 6;
-      if (btb[j] >= 0) {
-        ++my_res;
-      } else {
-        const int v = C > 0 ? t2s[t] : -1;
-        if (v >= 0) {
-          ++my_hit;
-          stp[v] = s;
-        } else if (host_bt == nullptr || hbt[j] < 0) {
-          atomicOr(err, 2);
-        } else {
-          is_f = true;
-        }
-      }
+  // 2. classify.  Thread t owns the contiguous run U[t*E, t*E + E); all of its
+  // table reads are issued together.  Rows: >= 0 known, -1 none, <= -2 the
+  // (-2 - i)-th fault, resolved once victims are known.
+  const int E = (nU + kResNT - 1) / kResNT;   // <= kMaxEntriesPerThread
+  const int u0 = tid * E;
+  int tok[kMaxEntriesPerThread], row[kMaxEntriesPerThread];
+  int rb[kMaxEntriesPerThread];
+  int64_t hrow[kMaxEntriesPerThread];
+#pragma unroll
+  for (int e = 0; e < kMaxEntriesPerThread; ++e) {
+    const bool ok = e < E && u0 + e < nU;
+    tok[e] = ok ? U[u0 + e] : -1;
+    rb[e] = ok ? btb[tok[e] >> 6] : 0;
+    hrow[e] = (ok && hbt) ? hbt[tok[e] >> 6] : -1;
+  }
+  int vs[kMaxEntriesPerThread];
+#pragma unroll
+  for (int e = 0; e < kMaxEntriesPerThread; ++e)
+    vs[e] = (tok[e] >= 0 && rb[e] < 0 && C > 0) ? t2s[tok[e]] : -1;
+  int my_res = 0, my_hit = 0, my_f = 0;
+#pragma unroll
+  for (int e = 0; e < kMaxEntriesPerThread; ++e) {
+    row[e] = -1;
+    const int t = tok[e];
+    if (t < 0) continue;
+    if (rb[e] >= 0) {
+      ++my_res;
+      row[e] = rb[e] * kBlock + (t & 63);
+    } else if (vs[e] >= 0) {
+      ++my_hit;
+      stp[vs[e]] = s;
+      row[e] = sHot[vs[e] >> 6] * kBlock + (vs[e] & 63);
+    } else if (hrow[e] < 0) {
+      atomicOr(err, 2);
+    } else {
+      row[e] = -2;          // fault; index assigned below
+      ++my_f;
     }
-    int tot;
-    const int ex = block_exclusive_scan<kResNT>(is_f ? 1 : 0, scratch, &tot);
-    if (is_f) sF[nF + ex] = t;
-    nF += tot;
+  }
+  int nF;
+  {
+    int pos = block_exclusive_scan<kResNT>(my_f, scratch, &nF);
+#pragma unroll
+    for (int e = 0; e < kMaxEntriesPerThread; ++e)
+      if (row[e] == -2) {
+        sF[pos] = tok[e];
+        row[e] = -2 - pos;
+        ++pos;
+      }
   }
   if (my_res) atomicAdd(&s_res, my_res);
   if (my_hit) atomicAdd(&s_hit, my_hit);
   __threadfence();
   __syncthreads();
 
-  // 3. victims
+  // 3. victims: the n_serve smallest (stamp, slot) keys among slots with
+  // stamp < s, in that order.  Fast path: slots are split into contiguous
+  // runs per thread with their stamps in registers; one distinct stamp value
+  // at a time (oldest first), its slots are emitted in slot order by one block
+  // prefix sum.  LRU victims usually span a few distinct stamps; beyond
+  // kMaxStampRounds the general path (radix select + sort) takes over.
   int n_serve = 0;
+  bool keys64 = false;            // victims as sorted 64-bit keys (general path)
+  int32_t* V32 = sA;              // victim slots, fast path (R1: the merge lists are dead)
   if (nF > 0 && C > 0) {
-    int my_c = 0;
-    unsigned long long kmin = ~0ull, kmax = 0ull;
-    for (int v = tid; v < C; v += kResNT) {
-      const int st = stp[v];
-      if (st < s) {
-        const unsigned long long key = ((unsigned long long)(uint32_t)st << 32) | (uint32_t)v;
+    const int S = (C + kResNT - 1) / kResNT;
+    int st_reg[kMaxSlotsPerThread];
+    int my_c = 0, my_min = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < kMaxSlotsPerThread; ++j) {
+      const int v = tid * S + j;
+      st_reg[j] = (j < S && v < C) ? stp[v] : 0x7FFFFFFF;
+      if (st_reg[j] < s) {
         ++my_c;
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
+        my_min = min(my_min, st_reg[j]);
       }
     }
+    if (tid == 0) s_next = 0x7FFFFFFF;
+    __syncthreads();
     if (my_c) {
       atomicAdd(&s_cnt, my_c);
-      atomicMin(&s_kmin, kmin);
-      atomicMax(&s_kmax, kmax);
+      atomicMin(&s_next, my_min);
     }
     __syncthreads();
     const int n_cand = s_cnt;
     n_serve = min(nF, n_cand);
-    unsigned long long thr = s_kmax;
-    if (n_serve > 0 && n_serve < n_cand) {
-      // MSD radix select of the n_serve-th smallest key, from the highest
-      // byte in which candidate keys differ
-      const unsigned long long diff = s_kmin ^ s_kmax;
-      const int top_byte = (63 - __builtin_clzll(diff)) >> 3;
-      unsigned long long prefix = (top_byte == 7) ? 0ull : (s_kmin >> (8 * (top_byte + 1)));
-      uint32_t need = (uint32_t)n_serve;
-      for (int pos = top_byte; pos >= 0; --pos) {
-        if (tid < 256) h256[tid] = 0;
-        __syncthreads();
-        for (int v = tid; v < C; v += kResNT) {
-          const int st = stp[v];
-          if (st >= s) continue;
-          const unsigned long long key = ((unsigned long long)(uint32_t)st << 32) | (uint32_t)v;
-          if (pos == 7 || (key >> (8 * (pos + 1))) == prefix)
-            atomicAdd(&h256[(key >> (8 * pos)) & 0xFFu], 1u);
-        }
-        __syncthreads();
-        find_bin256_lo(h256, need, &s_d, &s_before);
-        prefix = (prefix << 8) | (unsigned long long)s_d;
-        need -= s_before;
-        __syncthreads();
+    int sigma = s_next;
+    int got = 0;
+    bool fast = true;
+    for (int round = 0; got < n_serve; ++round) {
+      if (round == kMaxStampRounds) {
+        fast = false;
+        break;
       }
-      thr = prefix;
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxSlotsPerThread; ++j) cnt += (st_reg[j] == sigma);
+      int tot;
+      int pos = got + block_exclusive_scan<kResNT>(cnt, scratch, &tot);
+#pragma unroll
+      for (int j = 0; j < kMaxSlotsPerThread; ++j)
+        if (st_reg[j] == sigma) {
+          if (pos < n_serve) V32[pos] = tid * S + j;
+          ++pos;
+        }
+      got += tot;
+      if (got >= n_serve) break;
+      int my_next = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < kMaxSlotsPerThread; ++j)
+        if (st_reg[j] > sigma && st_reg[j] < s) my_next = min(my_next, st_reg[j]);
+      if (tid == 0) s_next = 0x7FFFFFFF;
+      __syncthreads();
+      if (my_next != 0x7FFFFFFF) atomicMin(&s_next, my_next);
+      __syncthreads();
+      sigma = s_next;
     }
-    // gather the victims (exactly n_serve keys <= thr) and sort them
-    uint64_t* V = sA64;
-    if (n_serve > 0) {
+    if (!fast) {
+      keys64 = true;
+      unsigned long long kmin = ~0ull, kmax = 0ull;
+      for (int v = tid; v < C; v += kResNT) {
+        const int st = stp[v];
+        if (st < s) {
+          const unsigned long long key = ((unsigned long long)(uint32_t)st << 32) | (uint32_t)v;
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+        }
+      }
+      atomicMin(&s_kmin, kmin);
+      atomicMax(&s_kmax, kmax);
+      __syncthreads();
+      unsigned long long thr = s_kmax;
+      if (n_serve < n_cand) {
+        // MSD radix select of the n_serve-th smallest key, from the highest
+        // byte in which candidate keys differ
+        const unsigned long long diff = s_kmin ^ s_kmax;
+        const int top_byte = (63 - __builtin_clzll(diff)) >> 3;
+        unsigned long long prefix = (top_byte == 7) ? 0ull : (s_kmin >> (8 * (top_byte + 1)));
+        uint32_t need = (uint32_t)n_serve;
+        for (int pos = top_byte; pos >= 0; --pos) {
+          if (tid < 256) h256[tid] = 0;
+          __syncthreads();
+          for (int v = tid; v < C; v += kResNT) {
+            const int st = stp[v];
+            if (st >= s) continue;
+            const unsigned long long key = ((unsigned long long)(uint32_t)st << 32) | (uint32_t)v;
+            if (pos == 7 || (key >> (8 * (pos + 1))) == prefix)
+              atomicAdd(&h256[(key >> (8 * pos)) & 0xFFu], 1u);
+          }
+          __syncthreads();
+          find_bin256_lo(h256, need, &s_d, &s_before);
+          prefix = (prefix << 8) | (unsigned long long)s_d;
+          need -= s_before;
+          __syncthreads();
+        }
+        thr = prefix;
+      }
+      // gather the victims (exactly n_serve keys <= thr) and sort them
+      uint64_t* V = sA64;
       for (int v = tid; v < C; v += kResNT) {
         const int st = stp[v];
         if (st >= s) continue;
@@ -274,48 +367,61 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
           __syncthreads();
         }
       }
-      // 4. fault i -> victim i
-      int my_ev = 0;
-      int32_t* fb = faults + (size_t)b * PK * 2;
-      for (int i = tid; i < n_serve; i += kResNT) {
-        const int v = (int)(uint32_t)V[i];
-        const int t = sF[i];
-        const int old = s2t[v];
-        if (old >= 0) {
-          t2s[old] = -1;
-          ++my_ev;
-        }
-        s2t[v] = t;
-        t2s[t] = v;
-        stp[v] = s;
-        fb[2 * i] = t;
-        fb[2 * i + 1] = v;
-      }
-      if (my_ev) atomicAdd(&s_ev, my_ev);
     }
+    __syncthreads();
+    // 4. fault i -> victim i
+    int my_ev = 0;
+    int32_t* fb = faults + (size_t)b * PK * 2;
+    for (int i = tid; i < n_serve; i += kResNT) {
+      const int v = keys64 ? (int)(uint32_t)sA64[i] : V32[i];
+      const int t = sF[i];
+      const int old = s2t[v];
+      if (old >= 0) {
+        t2s[old] = -1;
+        ++my_ev;
+      }
+      s2t[v] = t;
+      t2s[t] = v;
+      stp[v] = s;
+      fb[2 * i] = t;
+      fb[2 * i + 1] = v;
+    }
+    if (my_ev) atomicAdd(&s_ev, my_ev);
   }
   if (tid == 0 && n_serve < nF) atomicOr(err, 1);
-  __threadfence();
-  __syncthreads();
-
-  // 5. row ids
-  const int32_t* hb = hot_blocks + (size_t)b * (C >> 6);
-  int32_t* rid = row_ids + (size_t)b * PK;
-  for (int e = tid; e < PK; e += kResNT) {
-    const int t = tk[e];
-    int r = -1;
-    if (t >= 0) {
-      const int j = t >> 6;
-      const int rb = btb[j];
-      if (rb >= 0) {
-        r = rb * kBlock + (t & 63);
-      } else if (C > 0) {
-        const int v = t2s[t];
-        if (v >= 0) r = hb[v >> 6] * kBlock + (v & 63);
+  // fault rows from their victims (faults past n_serve keep row -1)
+#pragma unroll
+  for (int e = 0; e < kMaxEntriesPerThread; ++e)
+    if (row[e] <= -2) {
+      const int i = -2 - row[e];
+      if (i < n_serve) {
+        const int v = keys64 ? (int)(uint32_t)sA64[i] : V32[i];
+        row[e] = sHot[v >> 6] * kBlock + (v & 63);
+      } else {
+        row[e] = -1;
       }
     }
-    rid[e] = r;
+
+  // 5. row ids of every (position, k)
+  int32_t* rid = row_ids + (size_t)b * PK;
+  if (P == 1) {
+#pragma unroll
+    for (int e = 0; e < kMaxEntriesPerThread; ++e)
+      if (e < E && u0 + e < nU) rid[u0 + e] = row[e];
+    for (int k = nU + tid; k < K; k += kResNT) rid[k] = -1;
+  } else {
+    __syncthreads();                       // every read of the victims is done
+    int32_t* rowU = sA;
+#pragma unroll
+    for (int e = 0; e < kMaxEntriesPerThread; ++e)
+      if (e < E && u0 + e < nU) rowU[u0 + e] = row[e];
+    __syncthreads();
+    for (int e = tid; e < PK; e += kResNT) {
+      const int t = tk[e];
+      rid[e] = t < 0 ? -1 : rowU[lower_bound_lds(sU, nU, t)];
+    }
   }
+  __syncthreads();                         // every eviction is counted
   if (tid == 0) {
     counts[b * 4 + 0] = s_res;
     counts[b * 4 + 1] = s_hit;
@@ -366,14 +472,18 @@ __global__ __launch_bounds__(kCopyNT) void fault_copy_kernel(
 
 }  // namespace
 
-hipError_t launch_resolve(const BatchDims& d, int K, const int32_t* topk, const ResidencyArgs& r,
-                          int32_t* row_ids, int32_t* faults, int32_t* counts, hipStream_t s) {
-  const int PK = d.P * K;
+hipError_t launch_resolve_tables(const BatchDims& d, int K, const int32_t* topk,
+                                 const ResidencyArgs& r, int32_t* row_ids, int32_t* faults,
+                                 int32_t* counts, hipStream_t s) {
   hipLaunchKernelGGL(resolve_kernel, dim3(d.B), dim3(kResNT), 0, s, d.T_stride, d.max_blocks, d.P,
                      K, topk, r.C, r.bt, r.hot_blocks, r.tok2slot, r.slot2tok, r.stamp, r.step,
                      r.err, r.host_bt, row_ids, faults, counts);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_fault_copy(const BatchDims& d, int K, const ResidencyArgs& r,
+                             const int32_t* faults, const int32_t* counts, hipStream_t s) {
+  const int PK = d.P * K;
   const int row_bytes = kDLat * r.kv_bytes;
   dim3 grid((PK + kFaultsPerWG - 1) / kFaultsPerWG, d.B);
   hipLaunchKernelGGL(fault_copy_kernel, grid, dim3(kCopyNT), 0, s, PK, r.C, r.L, row_bytes,

@@ -15,7 +15,8 @@
 //   4. finalize  one workgroup per row finishes the radix select on the
 //                candidates (11 + 10 more bits), resolves ties at the
 //                threshold toward the lower token (radix select on the token
-//                index), collects the K tokens and sorts them ascending in LDS.
+//                index), collects the K tokens and writes them in ascending
+//                order through an LDS bitmap per 64K-token segment.
 // The selection is exact: the same tokens as a full sort by (score desc,
 // token asc), written in ascending token order, -1 padded for short rows.
 #include "hs_common.h"
@@ -29,6 +30,8 @@ constexpr int kChunk = 8192;   // tokens per workgroup in passes 2 and 3
 constexpr int kScanNT = 256;
 constexpr int kFinNT = 1024;
 constexpr int kMaxK = 8192;
+constexpr int kSegTok = 1 << 16;          // tokens per bitmap segment in finalize
+constexpr int kSegWords = kSegTok / 32;
 
 struct TopkWs {
   uint32_t* hist;   // [R][2048]
@@ -104,16 +107,26 @@ __global__ __launch_bounds__(kScanNT) void topk_hist_kernel(const int32_t* __res
                                                             int P, int T_stride, int K,
                                                             const float* __restrict__ scores,
                                                             TopkWs ws) {
+  constexpr int kPer = kChunk / kScanNT;
   __shared__ uint32_t h[kBins1];
   const int r = blockIdx.y;
   const int n = row_visible(ctx_len, P, r);
   const int base = blockIdx.x * kChunk;
   if (n <= K || base >= n) return;
   for (int i = threadIdx.x; i < kBins1; i += kScanNT) h[i] = 0;
-  __syncthreads();
   const float* row = scores + (size_t)r * T_stride;
   const int end = min(base + kChunk, n);
-  for (int t = base + threadIdx.x; t < end; t += kScanNT) atomicAdd(&h[score_key(row[t]) >> 21], 1u);
+  uint32_t bins[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int t = base + i * kScanNT + threadIdx.x;
+    bins[i] = t < end ? (score_key(row[t]) >> 21) : 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  // all loads were issued above; only the LDS adds remain
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (bins[i] != 0xFFFFFFFFu) atomicAdd(&h[bins[i]], 1u);
   __syncthreads();
   for (int i = threadIdx.x; i < kBins1; i += kScanNT)
     if (h[i]) atomicAdd(&ws.hist[(size_t)r * kBins1 + i], h[i]);
@@ -123,14 +136,24 @@ __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __r
                                                               int P, int T_stride, int K,
                                                               const float* __restrict__ scores,
                                                               TopkWs ws) {
+  constexpr int kPer = kChunk / kScanNT;   // keys per thread, kept in registers
   __shared__ uint32_t h[kBins1];
   __shared__ int scratch[kScanNT / kWave + 1];
   __shared__ int s_b1;
   __shared__ uint32_t s_above;
+  __shared__ uint32_t s_base_sel, s_base_cand;
   const int r = blockIdx.y;
   const int n = row_visible(ctx_len, P, r);
   const int base = blockIdx.x * kChunk;
   if (n <= K || base >= n) return;
+  const float* row = scores + (size_t)r * T_stride;
+  const int end = min(base + kChunk, n);
+  uint32_t key[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int t = base + i * kScanNT + threadIdx.x;
+    key[i] = t < end ? score_key(row[t]) : 0u;
+  }
   for (int i = threadIdx.x; i < kBins1; i += kScanNT) h[i] = ws.hist[(size_t)r * kBins1 + i];
   __syncthreads();
   find_bin<kScanNT>(h, kBins1, (uint32_t)K, true, scratch, &s_b1, &s_above);
@@ -139,30 +162,37 @@ __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __r
     ws.cnt[r * 4 + 2] = b1;
     ws.cnt[r * 4 + 3] = s_above;
   }
-  const float* row = scores + (size_t)r * T_stride;
-  const int end = min(base + kChunk, n);
-  const int lane = lane_id();
-  for (int t0 = base; t0 < end; t0 += kScanNT) {
-    const int t = t0 + threadIdx.x;
-    const bool valid = t < end;
-    const uint32_t key = valid ? score_key(row[t]) : 0u;
-    const uint32_t bin = key >> 21;
-    const bool is_sel = valid && bin > b1;
-    const bool is_cand = valid && bin == b1;
-    const uint64_t ms = __ballot(is_sel);
-    const uint64_t mc = __ballot(is_cand);
-    uint32_t bs = 0, bc = 0;
-    if (lane == 0) {
-      if (ms) bs = atomicAdd(&ws.cnt[r * 4 + 0], (uint32_t)__popcll(ms));
-      if (mc) bc = atomicAdd(&ws.cnt[r * 4 + 1], (uint32_t)__popcll(mc));
-    }
-    bs = __shfl(bs, 0);
-    bc = __shfl(bc, 0);
-    if (is_sel) ws.sel[(size_t)r * K + bs + lanes_below(ms)] = t;
-    if (is_cand) {
-      const size_t o = (size_t)r * T_stride + bc + lanes_below(mc);
-      ws.ckey[o] = key;
-      ws.ctok[o] = t;
+  // count this thread's selections (low 16 bits) and candidates (high 16 bits)
+  int packed = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int t = base + i * kScanNT + threadIdx.x;
+    const uint32_t bin = key[i] >> 21;
+    if (t < end) packed += (bin > b1) ? 1 : ((bin == b1) ? 0x10000 : 0);
+  }
+  int total;
+  const int ex = block_exclusive_scan<kScanNT>(packed, scratch, &total);
+  if (threadIdx.x == 0) {
+    s_base_sel = (total & 0xFFFF) ? atomicAdd(&ws.cnt[r * 4 + 0], (uint32_t)(total & 0xFFFF)) : 0u;
+    s_base_cand = (total >> 16) ? atomicAdd(&ws.cnt[r * 4 + 1], (uint32_t)(total >> 16)) : 0u;
+  }
+  __syncthreads();
+  uint32_t ps = s_base_sel + (uint32_t)(ex & 0xFFFF);
+  uint32_t pc = s_base_cand + (uint32_t)(ex >> 16);
+  int32_t* sel = ws.sel + (size_t)r * K;
+  uint32_t* ck = ws.ckey + (size_t)r * T_stride;
+  int32_t* ct = ws.ctok + (size_t)r * T_stride;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int t = base + i * kScanNT + threadIdx.x;
+    if (t >= end) continue;
+    const uint32_t bin = key[i] >> 21;
+    if (bin > b1) {
+      sel[ps++] = t;
+    } else if (bin == b1) {
+      ck[pc] = key[i];
+      ct[pc] = t;
+      ++pc;
     }
   }
 }
@@ -172,6 +202,7 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
                                                                TopkWs ws, int32_t* __restrict__ topk) {
   __shared__ uint32_t h[kBins1];
   __shared__ int32_t outl[kMaxK];
+  __shared__ uint32_t bm[kSegWords];
   __shared__ int scratch[kFinNT / kWave + 1];
   __shared__ int s_d;
   __shared__ uint32_t s_before;
@@ -246,28 +277,41 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
       if (at < kMaxK) outl[at] = t;
     }
   }
-  int np = 1;
-  while (np < K) np <<= 1;
   __syncthreads();
-  for (int i = K + tid; i < np; i += kFinNT) outl[i] = 0x7FFFFFFF;
-  __syncthreads();
-  // bitonic sort, ascending
-  for (int size = 2; size <= np; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < np / 2; i += kFinNT) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool asc = (lo & size) == 0;
-        const int a = outl[lo], c = outl[hi];
-        if ((a > c) == asc) {
-          outl[lo] = c;
-          outl[hi] = a;
-        }
-      }
-      __syncthreads();
+  // emit the K selected tokens in ascending order: an LDS bitmap per 2^16-token
+  // segment, then a popcount prefix sum over its words
+  int written = 0;
+  const int nseg = (n + kSegTok - 1) / kSegTok;
+  for (int sg = 0; sg < nseg; ++sg) {
+    for (int i = tid; i < kSegWords; i += kFinNT) bm[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < K; i += kFinNT) {
+      const int t = outl[i];
+      if (t / kSegTok == sg) atomicOr(&bm[(t % kSegTok) >> 5], 1u << (t & 31));
     }
+    __syncthreads();
+    constexpr int kWpt = kSegWords / kFinNT;   // words per thread
+    uint32_t wd[kWpt];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kWpt; ++j) {
+      wd[j] = bm[tid * kWpt + j];
+      cnt += __popc(wd[j]);
+    }
+    int tot;
+    int pos = written + block_exclusive_scan<kFinNT>(cnt, scratch, &tot);
+#pragma unroll
+    for (int j = 0; j < kWpt; ++j) {
+      uint32_t x = wd[j];
+      const int t0 = sg * kSegTok + (tid * kWpt + j) * 32;
+      while (x) {
+        const int bit = __ffs(x) - 1;
+        out[pos++] = t0 + bit;
+        x &= x - 1;
+      }
+    }
+    written += tot;
   }
-  for (int k = tid; k < K; k += kFinNT) out[k] = outl[k];
 }
 
 }  // namespace

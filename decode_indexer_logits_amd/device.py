@@ -8,8 +8,8 @@ Layouts (HBM unless noted; B requests, P positions, L layers, T = T_stride):
   latent    pool [L, N_rows, 576] e4m3 | row_scale [L, N_rows] f32
   residency bt [B,T/64] | hot_blocks [B,C/64] | tok2slot [B,T] | slot2tok [B,C]
             stamp [B,C] | step [1] | err [1]            (all i32)
-  host      host_rows [L, B*T, 576] e4m3, host_scale [L, B*T] f32 (pinned,
-            read by the GPU in place) | host_bt [B,T/64] i64
+  host      host_rows [L, B*T, 576] e4m3 (pinned host memory, read by the GPU
+            in place) | host_scale [L, B*T] f32 (HBM) | host_bt [B,T/64] i64
   step      scores [B,P,T] f32 | topk [B,P,K] | row_ids [B,P,K] | faults [B,P*K,2]
             counts [B,4] (i32) | q [L,B,P,16,576] bf16 | out [L,B,P,16,512] f32
             lse [L,B,P,16] f32
@@ -81,7 +81,11 @@ class DeviceStep:
         self.tok2slot = _dev(wl.tok2slot, d) if C else None
         self.slot2tok = _dev(wl.slot2tok, d) if C else None
         self.stamp = _dev(wl.stamp, d) if C else None
-        self.step_t = torch.tensor([wl.step], dtype=torch.int32, device=d)
+        # one step counter per request chunk of the pipelined step (all equal);
+        # the single-stream step uses the first one
+        self.max_chunks = 16
+        self.steps_dev = torch.full((self.max_chunks,), wl.step, dtype=torch.int32, device=d)
+        self.step_t = self.steps_dev[:1]
         self.err = torch.zeros(1, dtype=torch.int32, device=d)
         self.host_rows = self.host_scale = self.host_bt = None
         host_rows_dev = host_scale_dev = None
@@ -92,10 +96,10 @@ class DeviceStep:
             self.host_rows.numpy()[...] = hr
             host_rows_dev = _lib.host_device_ptr(self.host_rows)
             if wl.host_scale is not None:
-                hs = wl.host_scale
-                self.host_scale = torch.empty(hs.shape, dtype=torch.float32, pin_memory=True)
-                self.host_scale.numpy()[...] = hs
-                host_scale_dev = _lib.host_device_ptr(self.host_scale)
+                # the per-row scales of the host pool are a small table: kept in
+                # HBM so a fault reads only its row over the host link
+                self.host_scale = _dev(wl.host_scale, d)
+                host_scale_dev = self.host_scale.data_ptr()
             self.host_bt = _dev(wl.host_bt, d)
         kv_t = _lib.DTYPES[wl.kv_dtype]
         self.res = _lib.Residency(
@@ -103,6 +107,9 @@ class DeviceStep:
             self.bt.data_ptr(), _p(self.hot_blocks), _p(self.tok2slot), _p(self.slot2tok),
             _p(self.stamp), self.step_t.data_ptr(), self.err.data_ptr(), self.pool.data_ptr(),
             _p(self.row_scale), host_rows_dev, host_scale_dev, _p(self.host_bt))
+        self._host_rows_dev, self._host_scale_dev = host_rows_dev, host_scale_dev
+        self._chunks = {}
+        self._streams = None
         self.set_queries(1)
 
     # ---------------------------------------------------------------- inputs
@@ -141,10 +148,94 @@ class DeviceStep:
         for l in range(self.wl.L):
             self.run_attention(l, stream)
 
+    # ---------------------------------------------------------------- pipelined step
+    def _chunk(self, c: int, nchunks: int):
+        """Views, batch and residency structs of request chunk c of nchunks."""
+        key = (c, nchunks)
+        if key in self._chunks:
+            return self._chunks[key]
+        wl = self.wl
+        bounds = np.linspace(0, wl.B, nchunks + 1).round().astype(int)
+        b0, b1 = int(bounds[c]), int(bounds[c + 1])
+        e = self.ctx_len.element_size()
+        batch = _lib.Batch(b1 - b0, wl.P, wl.T_stride, wl.T_stride // 64,
+                           self.ctx_len.data_ptr() + e * b0)
+        sl = slice(b0, b1)
+        ch = {"b0": b0, "b1": b1, "batch": batch, "sl": sl}
+        C = wl.C
+
+        def off(t, rows):
+            return None if t is None else t[rows].data_ptr()
+        ch["res"] = _lib.Residency(
+            C, wl.L, _lib.DTYPES[wl.kv_dtype], 0, self.n_rows, wl.B * wl.T_stride,
+            off(self.bt, sl), off(self.hot_blocks, sl), off(self.tok2slot, sl),
+            off(self.slot2tok, sl), off(self.stamp, sl), self.steps_dev[c:c + 1].data_ptr(),
+            self.err.data_ptr(), self.pool.data_ptr(), _p(self.row_scale), self._host_rows_dev,
+            self._host_scale_dev, off(self.host_bt, sl))
+        self._chunks[key] = ch
+        return ch
+
+    def _ensure_pipeline(self, nchunks: int):
+        torch = _torch()
+        if self._streams is None:
+            self._streams = (torch.cuda.Stream(device=self.device), torch.cuda.Stream(device=self.device))
+        wl = self.wl
+        need = 16
+        for c in range(nchunks):
+            ch = self._chunk(c, nchunks)
+            need = max(need, _lib.workspace_bytes(_lib.HS_OP_MLA, ch["b1"] - ch["b0"], wl.P,
+                                                  wl.T_stride, wl.K, wl.Hq))
+        if self.ws_mla is None or self.ws_mla.numel() < need:
+            self.ws_mla = torch.empty(need, dtype=torch.uint8, device=self.device)
+
+    def run_pipelined(self, nchunks: int = 4):
+        """One decode step with the batch split into request chunks on two streams:
+        a compute stream runs indexer -> top-K -> resolve tables chunk after chunk,
+        and a copy stream runs each chunk's host-link fault copies and attention
+        as soon as its tables are resolved, so the copies overlap the following
+        chunks' HBM-bound work.  Same results as run() (per-chunk step counters
+        all advance together)."""
+        torch = _torch()
+        if nchunks > self.max_chunks or nchunks > self.wl.B:
+            raise ValueError(f"nchunks={nchunks} out of range")
+        self._ensure_pipeline(nchunks)
+        wl = self.wl
+        cs, xs = self._streams
+        main = torch.cuda.current_stream(self.device)
+        cs.wait_stream(main)
+        xs.wait_stream(main)
+        if nchunks > 1:
+            with torch.cuda.stream(cs):   # every chunk starts from the same step number
+                self.steps_dev[1:nchunks].copy_(self.steps_dev[0].expand(nchunks - 1))
+        for c in range(nchunks):
+            ch = self._chunk(c, nchunks)
+            sl, batch, res = ch["sl"], ch["batch"], ch["res"]
+            with torch.cuda.stream(cs):
+                _lib.indexer_scores(batch, wl.H_idx, wl.D_idx, wl.q_dtype, self.q_idx[sl],
+                                    self.w[sl], wl.k_dtype, self.idx_pool, self.idx_scale,
+                                    self.idx_bt[sl], None if self.bias is None else self.bias[sl],
+                                    self.scores[sl])
+                _lib.topk(batch, wl.K, self.scores[sl], self.topk[sl], self.ws_topk)
+                _lib.resolve_tables(batch, wl.K, self.topk[sl], res, self.row_ids[sl],
+                                    self.faults[sl], self.counts[sl])
+                ev = torch.cuda.Event()
+                ev.record(cs)
+            xs.wait_event(ev)
+            with torch.cuda.stream(xs):
+                _lib.copy_faults(batch, wl.K, res, self.faults[sl], self.counts[sl])
+                for l in range(wl.L):
+                    _lib.sparse_mla_decode(batch, wl.K, wl.Hq, wl.q_dtype, self.q[l][sl],
+                                           wl.kv_dtype, self.pool[l],
+                                           None if self.row_scale is None else self.row_scale[l],
+                                           self.row_ids[sl], wl.sm_scale, self.out[l][sl],
+                                           self.lse[l][sl], self.ws_mla)
+        main.wait_stream(cs)
+        main.wait_stream(xs)
+
     # ---------------------------------------------------------------- state
     def snapshot(self) -> dict:
         """Copies of the mutable state (tables, step, pool rows and scales)."""
-        snap = {"step": self.step_t.clone(), "err": self.err.clone(), "pool": self.pool.clone()}
+        snap = {"step": self.steps_dev.clone(), "err": self.err.clone(), "pool": self.pool.clone()}
         if self.row_scale is not None:
             snap["row_scale"] = self.row_scale.clone()
         if self.wl.C:
@@ -153,7 +244,7 @@ class DeviceStep:
         return snap
 
     def restore(self, snap: dict):
-        self.step_t.copy_(snap["step"])
+        self.steps_dev.copy_(snap["step"])
         self.err.copy_(snap["err"])
         self.pool.copy_(snap["pool"])
         if "row_scale" in snap:

@@ -129,7 +129,7 @@ hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t
  * paragraph) and a pinned host pool.  The tables are read and updated in place
  * by hs_resolve_rows. */
 typedef struct hs_residency {
-  int32_t C;                  /* hot rows per request: 0, or a multiple of 64
+  int32_t C;                  /* hot rows per request: 0, or a multiple of 64 up to 16384,
                                  with C >= P*K (the pages' default is 2K, and
                                  (num_speculative_tokens + 2) K with MTP,
                                  section "Ce qu'il faut en retenir")         */
@@ -154,7 +154,11 @@ typedef struct hs_residency {
   const void* host_rows;      /* pinned host [L, host_layer_rows, 576], given
                                  by its device-accessible address; may be
                                  NULL when no page is host-only              */
-  const float* host_scale;    /* pinned host [L, host_layer_rows]            */
+  const float* host_scale;    /* [L, host_layer_rows] scale of each host row;
+                                 any device-accessible memory.  Device memory
+                                 is preferable: the table is small, and reading
+                                 it from the host costs one link transaction
+                                 per fault                                  */
   const int64_t* host_bt;     /* [B, max_blocks] host row of token 64*j of
                                  page j, -1 = page has no host copy          */
 } hs_residency;
@@ -183,6 +187,25 @@ typedef struct hs_residency {
 hs_status hs_resolve_rows(const hs_batch* batch, int32_t K, const int32_t* topk,
                           const hs_residency* res, int32_t* row_ids, int32_t* faults,
                           int32_t* counts, void* ws, size_t ws_bytes, void* stream);
+
+/* The two halves of hs_resolve_rows, for callers that overlap the host-link
+ * copies with other work (the copies are bound by the host link, the rest of
+ * the step by HBM):
+ *   hs_resolve_tables  everything but the copies: tables, row ids, fault list
+ *                      and counts (the same outputs as hs_resolve_rows);
+ *   hs_copy_faults     copies the rows listed in faults/counts (as written by
+ *                      the preceding hs_resolve_tables on the same batch and
+ *                      state) from the host pool into their slots in every
+ *                      layer, with their scales, and advances res->step.
+ * Enqueued on one stream in this order they are hs_resolve_rows.  The copy may
+ * run on another stream behind an event recorded after hs_resolve_tables;
+ * then nothing may read the faulted slots before it completes, and the next
+ * hs_resolve_tables on the same state (and step counter) must wait for it. */
+hs_status hs_resolve_tables(const hs_batch* batch, int32_t K, const int32_t* topk,
+                            const hs_residency* res, int32_t* row_ids, int32_t* faults,
+                            int32_t* counts, void* stream);
+hs_status hs_copy_faults(const hs_batch* batch, int32_t K, const hs_residency* res,
+                         const int32_t* faults, const int32_t* counts, void* stream);
 
 /* Sparse MLA decode attention in the absorbed (MQA) form that the
  * sparse_mla_force_mqa option keeps on the sparse kernel (page "vLLM sert

@@ -200,3 +200,101 @@ def test_graph_capture_replays_match_eager():
             assert np.array_equal(got[k], ref[k]), (rep, k)
         assert got["step"] == ref["step"]
         _ = torch.ones(1024, device="cuda").sum().item()   # unrelated eager work between replays
+
+
+def test_pipelined_step_matches_single_stream():
+    _say("pipelined vs single stream")
+    wl = _mixed_small(B=5, T=8192, K=256, tail=512)
+    from decode_indexer_logits_amd.device import DeviceStep
+    ds = DeviceStep(wl)
+    snap = ds.snapshot()
+    ds.run()
+    ref = gc.gpu_outputs(ds)
+    gc.check_resolve(wl, gc.oracle_state(wl), ref["topk"], ref)
+    keys = ("scores", "topk", "row_ids", "counts", "out", "lse", "tok2slot", "slot2tok", "stamp")
+    for nchunks in (2, 3, 5):
+        ds.restore(snap)
+        ds.run_pipelined(nchunks)
+        got = gc.gpu_outputs(ds)
+        for k in keys:
+            if k == "scores":
+                for b in range(wl.B):
+                    n = int(wl.ctx_len[b])
+                    assert np.array_equal(got[k][b, :, :n], ref[k][b, :, :n])
+            else:
+                assert np.array_equal(got[k], ref[k]), (nchunks, k)
+        assert got["step"] == ref["step"]
+        assert np.array_equal(ds.pool.cpu().numpy(), ds.pool.cpu().numpy())
+    # captured as one graph, replayed
+    ds.restore(snap)
+    ds.run_pipelined(3)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    ds.restore(snap)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            ds.run_pipelined(3)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ds.restore(snap)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = gc.gpu_outputs(ds)
+        for k in keys[1:]:
+            assert np.array_equal(got[k], ref[k]), ("graph", rep, k)
+
+
+@pytest.mark.parametrize("stamps", ["distinct", "range100", "two"])
+def test_resolve_victim_orders(stamps):
+    # victims spread over many distinct stamps (the general radix-select path),
+    # a moderate range, and only two stamps (the per-stamp fast path)
+    _say(f"victim order: {stamps}")
+    wl = _mixed_small(B=3, T=8192, K=256, tail=512)
+    rng = np.random.default_rng(11)
+    st = np.empty_like(wl.stamp)
+    for b in range(wl.B):
+        if stamps == "distinct":
+            st[b] = rng.permutation(wl.C) + 1
+        elif stamps == "range100":
+            st[b] = rng.integers(1, 101, wl.C)
+        else:
+            st[b] = rng.integers(1, 3, wl.C)
+    w2 = dataclasses.replace(wl, stamp=st.astype(np.int32), step=int(st.max()))
+    ds = _run(w2)
+    _, rr, info = gc.full_check(ds, w2, gc.oracle_state(w2), attn_tol=2e-2)
+    _say(info["counts"].tolist())
+    assert np.all(info["counts"][:, 3] > 0)
+
+
+def test_pipelined_chunks_of_eight_against_oracle():
+    # 32 requests in 4 chunks of 8, eager and as a graph: each replay checked
+    # bit-exactly against the oracle's resolve of the same selection
+    _say("pipelined B=32 in 4 chunks")
+    wl = _mixed_small(B=32, T=16384, K=512, tail=1024)
+    from decode_indexer_logits_amd.device import DeviceStep
+    ds = DeviceStep(wl)
+    snap = ds.snapshot()
+    ds.run_pipelined(4)
+    g1 = gc.gpu_outputs(ds)
+    gc.check_resolve(wl, gc.oracle_state(wl), g1["topk"], g1)
+    assert np.all(g1["counts"][:, 3] == g1["counts"][:, 2])   # full buffers: every fault evicts
+    ds.restore(snap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            ds.run_pipelined(4)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ds.restore(snap)
+        g.replay()
+        got = gc.gpu_outputs(ds)
+        gc.check_resolve(wl, gc.oracle_state(wl), got["topk"], got)
+        for k in ("topk", "row_ids", "counts", "out", "lse"):
+            assert np.array_equal(got[k], g1[k]), (rep, k)
