@@ -20,7 +20,7 @@ DTYPES = {"f32": HS_F32, "bf16": HS_BF16, "e4m3": HS_E4M3}
 HS_OP_INDEXER, HS_OP_TOPK, HS_OP_RESOLVE, HS_OP_MLA = 0, 1, 2, 3
 DEVERR_VICTIMS, DEVERR_NO_HOST = 1, 2
 
-EXPORTS = ["hs_indexer_scores", "hs_topk", "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
+EXPORTS = ["hs_indexer_scores", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
            "hs_sparse_mla_decode", "hs_workspace_bytes", "hs_host_device_ptr", "hs_last_error",
            "hs_abi_version"]
 
@@ -60,12 +60,14 @@ def load() -> ctypes.CDLL:
     P = c_void_p
     lib.hs_indexer_scores.argtypes = [P, c_int32, c_int32, c_int32, P, P, c_int32, P, P, P, P, P, P]
     lib.hs_topk.argtypes = [P, c_int32, P, P, P, c_size_t, P]
+    lib.hs_indexer_topk.argtypes = [P, c_int32, c_int32, c_int32, P, P, c_int32, P, P, P, P, P,
+                                    c_int32, P, P, c_size_t, P]
     lib.hs_resolve_rows.argtypes = [P, c_int32, P, P, P, P, P, P, c_size_t, P]
     lib.hs_resolve_tables.argtypes = [P, c_int32, P, P, P, P, P, P]
     lib.hs_copy_faults.argtypes = [P, c_int32, P, P, P, P]
     lib.hs_sparse_mla_decode.argtypes = [P, c_int32, c_int32, c_int32, P, c_int32, P, P, P,
                                          c_float, P, P, P, c_size_t, P]
-    for f in ("hs_indexer_scores", "hs_topk", "hs_resolve_rows", "hs_resolve_tables",
+    for f in ("hs_indexer_scores", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables",
               "hs_copy_faults", "hs_sparse_mla_decode", "hs_host_device_ptr"):
         getattr(lib, f).restype = c_int32
     lib.hs_workspace_bytes.argtypes = [c_int32] * 6
@@ -125,6 +127,15 @@ def indexer_scores(batch: Batch, H: int, D: int, q_t: str, q_idx, w, k_t: str, i
 def topk(batch: Batch, K: int, scores, out, ws, stream=None):
     _check(load().hs_topk(ctypes.byref(batch), K, _ptr(scores), _ptr(out), _ptr(ws),
                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def indexer_topk(batch: Batch, H: int, D: int, q_t: str, q_idx, w, k_t: str, idx_pool, idx_scale,
+                 idx_bt, bias, scores, K: int, out, ws, stream=None):
+    _check(load().hs_indexer_topk(ctypes.byref(batch), H, D, DTYPES[q_t], _ptr(q_idx), _ptr(w),
+                                  DTYPES[k_t], _ptr(idx_pool), _ptr(idx_scale), _ptr(idx_bt),
+                                  _ptr(bias), _ptr(scores), K, _ptr(out), _ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(),
+                                  _stream(stream)))
 
 
 def resolve_rows(batch: Batch, K: int, topk_t, res: Residency, row_ids, faults, counts,

@@ -52,47 +52,112 @@ hs_status launched(hipError_t e, const char* what) {
 
 extern "C" {
 
+}  // extern "C"
+
+namespace {
+
+enum class IdxPath { kBf16E4m3, kF32 };
+
+hs_status check_indexer(const hs::BatchDims& d, int32_t H_idx, int32_t D_idx, hs_dtype q_t,
+                        const void* q_idx, const float* w, hs_dtype k_t, const void* idx_pool,
+                        const float* idx_scale, const int32_t* idx_bt, float* scores,
+                        IdxPath* path) {
+  (void)d;
+  if (!q_idx || !w || !idx_pool || !idx_bt || !scores)
+    return fail(HS_ERR_NULL, "indexer: q_idx, w, idx_pool, idx_bt and scores are required");
+  if (D_idx != 64 && D_idx != 128) return fail(HS_ERR_SHAPE, "D_idx=%d must be 64 or 128", D_idx);
+  if (!aligned16(q_idx) || !aligned16(idx_pool) || !aligned16(scores))
+    return fail(HS_ERR_ALIGN, "indexer: q_idx, idx_pool and scores need 16-byte alignment");
+  if (q_t == HS_BF16 && k_t == HS_E4M3) {
+    if (H_idx < 16 || H_idx > 64 || H_idx % 16)
+      return fail(HS_ERR_SHAPE, "H_idx=%d must be 16, 32, 48 or 64 on the bf16/e4m3 path", H_idx);
+    *path = IdxPath::kBf16E4m3;
+    return HS_OK;
+  }
+  if (q_t == HS_F32 && k_t == HS_F32) {
+    if (H_idx < 1 || H_idx > 64) return fail(HS_ERR_SHAPE, "H_idx=%d out of [1, 64]", H_idx);
+    if (idx_scale) return fail(HS_ERR_DTYPE, "fp32 keys take no scale (idx_scale must be NULL)");
+    *path = IdxPath::kF32;
+    return HS_OK;
+  }
+  return fail(HS_ERR_DTYPE, "indexer supports (q, k) = (BF16, E4M3) or (F32, F32)");
+}
+
+hipError_t launch_indexer(const hs::BatchDims& d, IdxPath path, int32_t H_idx, int32_t D_idx,
+                          const void* q_idx, const float* w, const void* idx_pool,
+                          const float* idx_scale, const int32_t* idx_bt, const float* bias,
+                          float* scores, uint32_t* hist, hipStream_t s) {
+  if (path == IdxPath::kBf16E4m3)
+    return hs::launch_indexer_bf16_e4m3(d, H_idx, D_idx, static_cast<const uint16_t*>(q_idx), w,
+                                        static_cast<const uint8_t*>(idx_pool), idx_scale, idx_bt,
+                                        bias, scores, hist, s);
+  return hs::launch_indexer_f32(d, H_idx, D_idx, static_cast<const float*>(q_idx), w,
+                                static_cast<const float*>(idx_pool), idx_bt, bias, scores, s);
+}
+
+hs_status check_topk(const hs::BatchDims& d, int32_t K, int32_t* topk, void* ws, size_t ws_bytes) {
+  if (!topk) return fail(HS_ERR_NULL, "top-K: topk is required");
+  if (K < 1 || K > 8192) return fail(HS_ERR_SHAPE, "K=%d out of [1, 8192]", K);
+  const size_t need = hs::topk_workspace_bytes(d.B, d.P, d.T_stride, K);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "top-K needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace needs 16-byte alignment");
+  return HS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 hs_status hs_indexer_scores(const hs_batch* batch, int32_t H_idx, int32_t D_idx, hs_dtype q_t,
                             const void* q_idx, const float* w, hs_dtype k_t,
                             const void* idx_pool, const float* idx_scale, const int32_t* idx_bt,
                             const float* bias, float* scores, void* stream) {
   hs::BatchDims d;
   if (hs_status st = check_batch(batch, &d)) return st;
-  if (!q_idx || !w || !idx_pool || !idx_bt || !scores)
-    return fail(HS_ERR_NULL, "hs_indexer_scores: q_idx, w, idx_pool, idx_bt and scores are required");
-  if (D_idx != 64 && D_idx != 128) return fail(HS_ERR_SHAPE, "D_idx=%d must be 64 or 128", D_idx);
-  if (!aligned16(q_idx) || !aligned16(idx_pool) || !aligned16(scores))
-    return fail(HS_ERR_ALIGN, "hs_indexer_scores: q_idx, idx_pool and scores need 16-byte alignment");
+  IdxPath path;
+  if (hs_status st = check_indexer(d, H_idx, D_idx, q_t, q_idx, w, k_t, idx_pool, idx_scale,
+                                   idx_bt, scores, &path))
+    return st;
+  return launched(launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt,
+                                 bias, scores, nullptr, static_cast<hipStream_t>(stream)),
+                  "indexer");
+}
+
+hs_status hs_indexer_topk(const hs_batch* batch, int32_t H_idx, int32_t D_idx, hs_dtype q_t,
+                          const void* q_idx, const float* w, hs_dtype k_t, const void* idx_pool,
+                          const float* idx_scale, const int32_t* idx_bt, const float* bias,
+                          float* scores, int32_t K, int32_t* topk, void* ws, size_t ws_bytes,
+                          void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  IdxPath path;
+  if (hs_status st = check_indexer(d, H_idx, D_idx, q_t, q_idx, w, k_t, idx_pool, idx_scale,
+                                   idx_bt, scores, &path))
+    return st;
+  if (hs_status st = check_topk(d, K, topk, ws, ws_bytes)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (q_t == HS_BF16 && k_t == HS_E4M3) {
-    if (H_idx < 16 || H_idx > 64 || H_idx % 16)
-      return fail(HS_ERR_SHAPE, "H_idx=%d must be 16, 32, 48 or 64 on the bf16/e4m3 path", H_idx);
-    return launched(hs::launch_indexer_bf16_e4m3(d, H_idx, D_idx, static_cast<const uint16_t*>(q_idx),
-                                                 w, static_cast<const uint8_t*>(idx_pool), idx_scale,
-                                                 idx_bt, bias, scores, s),
-                    "indexer");
+  if (path == IdxPath::kF32) {
+    hipError_t e = launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt,
+                                  bias, scores, nullptr, s);
+    if (e != hipSuccess) return launched(e, "indexer");
+    return launched(hs::launch_topk(d, K, scores, topk, ws, s), "topk");
   }
-  if (q_t == HS_F32 && k_t == HS_F32) {
-    if (H_idx < 1 || H_idx > 64) return fail(HS_ERR_SHAPE, "H_idx=%d out of [1, 64]", H_idx);
-    if (idx_scale) return fail(HS_ERR_DTYPE, "fp32 keys take no scale (idx_scale must be NULL)");
-    return launched(hs::launch_indexer_f32(d, H_idx, D_idx, static_cast<const float*>(q_idx), w,
-                                           static_cast<const float*>(idx_pool), idx_bt, bias,
-                                           scores, s),
-                    "indexer");
-  }
-  return fail(HS_ERR_DTYPE, "indexer supports (q, k) = (BF16, E4M3) or (F32, F32)");
+  uint32_t* hist = nullptr;
+  hipError_t e = hs::launch_topk_zero(d, K, ws, &hist, s);
+  if (e == hipSuccess)
+    e = launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt, bias, scores,
+                       hist, s);
+  if (e == hipSuccess) e = hs::launch_topk_select(d, K, scores, topk, ws, s);
+  return launched(e, "indexer + top-K");
 }
 
 hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t* topk, void* ws,
                   size_t ws_bytes, void* stream) {
   hs::BatchDims d;
   if (hs_status st = check_batch(batch, &d)) return st;
-  if (!scores || !topk) return fail(HS_ERR_NULL, "hs_topk: scores and topk are required");
-  if (K < 1 || K > 8192) return fail(HS_ERR_SHAPE, "K=%d out of [1, 8192]", K);
-  const size_t need = hs::topk_workspace_bytes(d.B, d.P, d.T_stride, K);
-  if (!ws || ws_bytes < need)
-    return fail(HS_ERR_WORKSPACE, "hs_topk needs %zu workspace bytes, got %zu", need, ws_bytes);
-  if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace needs 16-byte alignment");
+  if (!scores) return fail(HS_ERR_NULL, "hs_topk: scores is required");
+  if (hs_status st = check_topk(d, K, topk, ws, ws_bytes)) return st;
   return launched(hs::launch_topk(d, K, scores, topk, ws, static_cast<hipStream_t>(stream)), "topk");
 }
 

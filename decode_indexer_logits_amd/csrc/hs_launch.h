@@ -13,11 +13,12 @@ struct BatchDims {
   const int32_t* ctx_len;
 };
 
-// Indexer: bf16 queries x E4M3 keys on the matrix cores.
+// Indexer: bf16 queries x E4M3 keys on the matrix cores.  With `hist`, the
+// 11-bit score-key histogram of every (request, position) is added to it.
 hipError_t launch_indexer_bf16_e4m3(const BatchDims& d, int H, int DK, const uint16_t* q,
                                    const float* w, const uint8_t* pool, const float* scale,
                                    const int32_t* bt, const float* bias, float* scores,
-                                   hipStream_t s);
+                                   uint32_t* hist, hipStream_t s);
 // Indexer: fp32 queries x fp32 keys on the vector ALUs.
 hipError_t launch_indexer_f32(const BatchDims& d, int H, int DK, const float* q, const float* w,
                               const float* pool, const int32_t* bt, const float* bias,
@@ -26,6 +27,11 @@ hipError_t launch_indexer_f32(const BatchDims& d, int H, int DK, const float* q,
 size_t topk_workspace_bytes(int B, int P, int T_stride, int K);
 hipError_t launch_topk(const BatchDims& d, int K, const float* scores, int32_t* topk, void* ws,
                        hipStream_t s);
+// The pieces of the fused indexer + top-K: zero the workspace counters (and
+// return the histogram the indexer fills), then select from that histogram.
+hipError_t launch_topk_zero(const BatchDims& d, int K, void* ws, uint32_t** hist, hipStream_t s);
+hipError_t launch_topk_select(const BatchDims& d, int K, const float* scores, int32_t* topk,
+                              void* ws, hipStream_t s);
 
 struct ResidencyArgs {
   int C, L, kv_bytes;               // kv_bytes: bytes per latent element (1 or 4)

@@ -36,13 +36,13 @@ struct IdxCfg {
   static constexpr int TILE = (P <= 2) ? 4096 : 1024;           // tokens per workgroup
 };
 
-template <int P, int DK, int HT>
+template <int P, int DK, int HT, bool HIST>
 __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     const int32_t* __restrict__ ctx_len, int T_stride, int max_blocks,
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint8_t* __restrict__ pool, const float* __restrict__ scale,
     const int32_t* __restrict__ bt, const float* __restrict__ bias,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, uint32_t* __restrict__ hist) {
   using Cfg = IdxCfg<P>;
   constexpr int H = 16 * HT;
   constexpr int KS = DK / 32;    // k-steps of 32
@@ -57,7 +57,15 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
   const int n = lane & 15, g = lane >> 4;
   const int p = wave / Cfg::WPP, sub = wave % Cfg::WPP;
   const int lim = T - P + p;
-  if (lim < tile0) return;
+  // Optional epilogue: the 2048-bin histogram of the top 11 bits of every
+  // stored score's order-preserving key, per (request, position), counted in
+  // LDS and added to `hist` (the first pass of the top-K radix select).
+  __shared__ uint32_t sh_hist[HIST ? P * 2048 : 1];
+  if (HIST) {
+    for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT) sh_hist[i] = 0;
+    __syncthreads();
+  }
+  if (lim >= tile0) {
 
   // query fragments: head 16*mt + n, dims SEG*g + 8*s .. +8
   bf16x8_t qa[HT][KS];
@@ -137,8 +145,9 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     const float mine = g == 0 ? vj[0] : (g == 1 ? vj[1] : (g == 2 ? vj[2] : vj[3]));
     const int tl = pi * kBlock + lane;
     if (tl <= lim_t) {
-      float sc = scale ? mine * page_scale(pi) : mine;
-      out[tl] = sc + bs;
+      const float val = (scale ? mine * page_scale(pi) : mine) + bs;
+      out[tl] = val;
+      if (HIST) atomicAdd(&sh_hist[p * 2048 + (score_key(val) >> 21)], 1u);
     }
   };
   // Pages of this wave: pi = sub + k*W, k < npw.  Loads are unconditional
@@ -160,6 +169,12 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     load_page(page_of(k + 4), bufB, bsB);
     if (k + 2 < npw) consume_page(sub + (k + 2) * W, bufC, bsC);
     load_page(page_of(k + 5), bufC, bsC);
+  }
+  }  // lim >= tile0
+  if (HIST) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT)
+      if (sh_hist[i]) atomicAdd(&hist[(size_t)(b * P + i / 2048) * 2048 + (i % 2048)], sh_hist[i]);
   }
 }
 
@@ -202,23 +217,29 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(
 template <int P, int DK, int HT>
 hipError_t launch_mfma(const BatchDims& d, const uint16_t* q, const float* w, const uint8_t* pool,
                        const float* scale, const int32_t* bt, const float* bias, float* scores,
-                       hipStream_t s) {
+                       uint32_t* hist, hipStream_t s) {
   using Cfg = IdxCfg<P>;
   dim3 grid((d.T_stride + Cfg::TILE - 1) / Cfg::TILE, d.B);
-  hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT>), grid, dim3(Cfg::NT), 0, s, d.ctx_len,
-                     d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias, scores);
+  if (hist)
+    hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT, true>), grid, dim3(Cfg::NT), 0, s,
+                       d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias, scores,
+                       hist);
+  else
+    hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT, false>), grid, dim3(Cfg::NT), 0, s,
+                       d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias, scores,
+                       hist);
   return hipGetLastError();
 }
 
 template <int P, int DK>
 hipError_t dispatch_ht(int HT, const BatchDims& d, const uint16_t* q, const float* w,
                        const uint8_t* pool, const float* scale, const int32_t* bt,
-                       const float* bias, float* scores, hipStream_t s) {
+                       const float* bias, float* scores, uint32_t* hist, hipStream_t s) {
   switch (HT) {
-    case 1: return launch_mfma<P, DK, 1>(d, q, w, pool, scale, bt, bias, scores, s);
-    case 2: return launch_mfma<P, DK, 2>(d, q, w, pool, scale, bt, bias, scores, s);
-    case 3: return launch_mfma<P, DK, 3>(d, q, w, pool, scale, bt, bias, scores, s);
-    case 4: return launch_mfma<P, DK, 4>(d, q, w, pool, scale, bt, bias, scores, s);
+    case 1: return launch_mfma<P, DK, 1>(d, q, w, pool, scale, bt, bias, scores, hist, s);
+    case 2: return launch_mfma<P, DK, 2>(d, q, w, pool, scale, bt, bias, scores, hist, s);
+    case 3: return launch_mfma<P, DK, 3>(d, q, w, pool, scale, bt, bias, scores, hist, s);
+    case 4: return launch_mfma<P, DK, 4>(d, q, w, pool, scale, bt, bias, scores, hist, s);
   }
   return hipErrorInvalidValue;
 }
@@ -226,9 +247,9 @@ hipError_t dispatch_ht(int HT, const BatchDims& d, const uint16_t* q, const floa
 template <int P>
 hipError_t dispatch_dk(int DK, int HT, const BatchDims& d, const uint16_t* q, const float* w,
                        const uint8_t* pool, const float* scale, const int32_t* bt,
-                       const float* bias, float* scores, hipStream_t s) {
-  if (DK == 64) return dispatch_ht<P, 64>(HT, d, q, w, pool, scale, bt, bias, scores, s);
-  if (DK == 128) return dispatch_ht<P, 128>(HT, d, q, w, pool, scale, bt, bias, scores, s);
+                       const float* bias, float* scores, uint32_t* hist, hipStream_t s) {
+  if (DK == 64) return dispatch_ht<P, 64>(HT, d, q, w, pool, scale, bt, bias, scores, hist, s);
+  if (DK == 128) return dispatch_ht<P, 128>(HT, d, q, w, pool, scale, bt, bias, scores, hist, s);
   return hipErrorInvalidValue;
 }
 
@@ -237,13 +258,13 @@ hipError_t dispatch_dk(int DK, int HT, const BatchDims& d, const uint16_t* q, co
 hipError_t launch_indexer_bf16_e4m3(const BatchDims& d, int H, int DK, const uint16_t* q,
                                    const float* w, const uint8_t* pool, const float* scale,
                                    const int32_t* bt, const float* bias, float* scores,
-                                   hipStream_t s) {
+                                   uint32_t* hist, hipStream_t s) {
   const int HT = H / 16;
   switch (d.P) {
-    case 1: return dispatch_dk<1>(DK, HT, d, q, w, pool, scale, bt, bias, scores, s);
-    case 2: return dispatch_dk<2>(DK, HT, d, q, w, pool, scale, bt, bias, scores, s);
-    case 3: return dispatch_dk<3>(DK, HT, d, q, w, pool, scale, bt, bias, scores, s);
-    case 4: return dispatch_dk<4>(DK, HT, d, q, w, pool, scale, bt, bias, scores, s);
+    case 1: return dispatch_dk<1>(DK, HT, d, q, w, pool, scale, bt, bias, scores, hist, s);
+    case 2: return dispatch_dk<2>(DK, HT, d, q, w, pool, scale, bt, bias, scores, hist, s);
+    case 3: return dispatch_dk<3>(DK, HT, d, q, w, pool, scale, bt, bias, scores, hist, s);
+    case 4: return dispatch_dk<4>(DK, HT, d, q, w, pool, scale, bt, bias, scores, hist, s);
   }
   return hipErrorInvalidValue;
 }

@@ -16,10 +16,11 @@
 //                 many stamps);
 //              4. fault i takes victim i: evict, insert, stamp, record;
 //              5. row ids of every (position, k) from the updated tables.
-//   fault copy a grid over (request, fault): each 576-value row is read
-//              straight from pinned host memory (zero-copy, 16-byte lanes)
-//              and written to its slot's pool row in every layer, with its
-//              scale; it also advances the step counter.
+//   fault copy a small persistent grid strides over every (request, fault,
+//              layer, 16-byte chunk): each 576-value row is read straight
+//              from pinned host memory (zero-copy) and written to its slot's
+//              pool row in every layer, with its scale; it also advances the
+//              step counter.
 #include "hs_common.h"
 #include "hs_launch.h"
 
@@ -29,7 +30,10 @@ namespace {
 constexpr int kResNT = 1024;
 constexpr int kMaxSel = 8192;   // P*K
 constexpr int kCopyNT = 256;
-constexpr int kFaultsPerWG = 2;    // more workgroups keep more host reads in flight
+constexpr int kCopyWGs = 256;
+constexpr int kCopyInFlight = 4;
+constexpr int kCopyBatch = 32;       // faults resolved per workgroup round
+constexpr int kCopyMaxL = 16;
 constexpr int kMaxSlotsPerThread = 16;   // C <= 16384
 constexpr int kMaxStampRounds = 32;
 constexpr int kMaxEntriesPerThread = kMaxSel / kResNT;   // 8
@@ -231,7 +235,9 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   }
   if (my_res) atomicAdd(&s_res, my_res);
   if (my_hit) atomicAdd(&s_hit, my_hit);
-  __threadfence();
+  // The stamps written above are read back below only by this workgroup, and
+  // no line of the table was read before: the barrier's workgroup-scope
+  // release/acquire is enough (a device-scope fence would write back L2).
   __syncthreads();
 
   // 3. victims: the n_serve smallest (stamp, slot) keys among slots with
@@ -430,42 +436,70 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   }
 }
 
+// Fault copies.  Zero-copy reads of pinned host memory are bound by the host
+// link, and its rate depends on the bytes in flight, not on the number of
+// waves: a persistent grid of kCopyWGs workgroups reaches the link rate while
+// leaving most CUs to kernels that run concurrently on other streams.  Each
+// request's faults are cut into batches of kCopyBatch; batches are dealt to
+// workgroups round-robin in request order.  A workgroup resolves a batch's
+// source and destination rows once into LDS, then streams its 16-byte chunks
+// with kCopyInFlight independent loads per thread.
 __global__ __launch_bounds__(kCopyNT) void fault_copy_kernel(
-    int PK, int C, int L, int row_bytes, int max_blocks, const int32_t* __restrict__ faults,
+    int B, int PK, int C, int L, int row_bytes, int max_blocks, const int32_t* __restrict__ faults,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ hot_blocks,
     const int64_t* __restrict__ host_bt, const uint8_t* __restrict__ host_rows,
     const float* __restrict__ host_scale, int64_t host_layer_rows, uint8_t* __restrict__ pool,
     float* __restrict__ row_scale, int64_t pool_layer_rows, int32_t* __restrict__ step) {
-  const int b = blockIdx.y;
-  if (blockIdx.x == 0 && b == 0 && threadIdx.x == 0) step[0] = step[0] + 1;
-  const int nf = counts[b * 4 + 2];
-  const int f0 = blockIdx.x * kFaultsPerWG;
-  if (f0 >= nf) return;
-  const int nloc = min(kFaultsPerWG, nf - f0);
+  __shared__ int64_t s_src[kCopyBatch * kCopyMaxL];
+  __shared__ int64_t s_dst[kCopyBatch * kCopyMaxL];
+  if (blockIdx.x == 0 && threadIdx.x == 0) step[0] = step[0] + 1;
   const int cpr = row_bytes / 16;           // 16-byte chunks per row
-  const int32_t* fb = faults + ((size_t)b * PK + f0) * 2;
-  const int32_t* hb = hot_blocks + (size_t)b * (C >> 6);
-  const int64_t* hbt = host_bt + (size_t)b * max_blocks;
-  const int per_fault = L * cpr;
-  for (int idx = threadIdx.x; idx < nloc * per_fault; idx += kCopyNT) {
-    const int fl = idx / per_fault;
-    const int rem = idx - fl * per_fault;
-    const int l = rem / cpr;
-    const int c = rem - l * cpr;
-    const int t = fb[2 * fl], v = fb[2 * fl + 1];
-    const int64_t hr = hbt[t >> 6] + (t & 63);
-    const int64_t pr = (int64_t)hb[v >> 6] * kBlock + (v & 63);
-    const uint4* src = reinterpret_cast<const uint4*>(host_rows + ((size_t)l * host_layer_rows + hr) * row_bytes) + c;
-    uint4* dst = reinterpret_cast<uint4*>(pool + ((size_t)l * pool_layer_rows + pr) * row_bytes) + c;
-    *dst = *src;
-  }
-  if (host_scale) {
-    for (int idx = threadIdx.x; idx < nloc * L; idx += kCopyNT) {
-      const int fl = idx / L, l = idx - fl * L;
-      const int t = fb[2 * fl], v = fb[2 * fl + 1];
-      const int64_t hr = hbt[t >> 6] + (t & 63);
-      const int64_t pr = (int64_t)hb[v >> 6] * kBlock + (v & 63);
-      row_scale[(size_t)l * pool_layer_rows + pr] = host_scale[(size_t)l * host_layer_rows + hr];
+  int gb = 0;                               // batches dealt so far
+  for (int b = 0; b < B; ++b) {
+    const int n = counts[b * 4 + 2];
+    const int nb = (n + kCopyBatch - 1) / kCopyBatch;
+    int j = (int)blockIdx.x - gb % (int)gridDim.x;
+    if (j < 0) j += gridDim.x;
+    gb += nb;
+    for (; j < nb; j += gridDim.x) {
+      const int f0 = j * kCopyBatch;
+      const int nloc = min(kCopyBatch, n - f0);
+      // one (fault, layer) per thread: source and destination byte offsets
+      for (int i = threadIdx.x; i < nloc * L; i += kCopyNT) {
+        const int fi = f0 + i / L, l = i % L;
+        const int32_t* fb = faults + ((size_t)b * PK + fi) * 2;
+        const int t = fb[0], sl = fb[1];
+        const int64_t hr = host_bt[(size_t)b * max_blocks + (t >> 6)] + (t & 63);
+        const int64_t pr =
+            (int64_t)hot_blocks[(size_t)b * (C >> 6) + (sl >> 6)] * kBlock + (sl & 63);
+        s_src[i] = ((int64_t)l * host_layer_rows + hr) * row_bytes;
+        s_dst[i] = ((int64_t)l * pool_layer_rows + pr) * row_bytes;
+        if (host_scale)
+          row_scale[(size_t)l * pool_layer_rows + pr] = host_scale[(size_t)l * host_layer_rows + hr];
+      }
+      __syncthreads();
+      const int nchunk = nloc * L * cpr;
+      for (int c0 = 0; c0 < nchunk; c0 += kCopyNT * kCopyInFlight) {
+        uint4 v0, v1, v2, v3;
+        int64_t d0 = -1, d1 = -1, d2 = -1, d3 = -1;
+        auto load = [&](int u, uint4& v, int64_t& d) {
+          const int idx = c0 + u * kCopyNT + (int)threadIdx.x;
+          if (idx < nchunk) {
+            const int row = idx / cpr, c = idx - row * cpr;
+            v = *reinterpret_cast<const uint4*>(host_rows + s_src[row] + (int64_t)c * 16);
+            d = s_dst[row] + (int64_t)c * 16;
+          }
+        };
+        load(0, v0, d0);
+        load(1, v1, d1);
+        load(2, v2, d2);
+        load(3, v3, d3);
+        if (d0 >= 0) *reinterpret_cast<uint4*>(pool + d0) = v0;
+        if (d1 >= 0) *reinterpret_cast<uint4*>(pool + d1) = v1;
+        if (d2 >= 0) *reinterpret_cast<uint4*>(pool + d2) = v2;
+        if (d3 >= 0) *reinterpret_cast<uint4*>(pool + d3) = v3;
+      }
+      __syncthreads();
     }
   }
 }
@@ -485,9 +519,8 @@ hipError_t launch_fault_copy(const BatchDims& d, int K, const ResidencyArgs& r,
                              const int32_t* faults, const int32_t* counts, hipStream_t s) {
   const int PK = d.P * K;
   const int row_bytes = kDLat * r.kv_bytes;
-  dim3 grid((PK + kFaultsPerWG - 1) / kFaultsPerWG, d.B);
-  hipLaunchKernelGGL(fault_copy_kernel, grid, dim3(kCopyNT), 0, s, PK, r.C, r.L, row_bytes,
-                     d.max_blocks, faults, counts, r.hot_blocks, r.host_bt,
+  hipLaunchKernelGGL(fault_copy_kernel, dim3(kCopyWGs), dim3(kCopyNT), 0, s, d.B, PK, r.C, r.L,
+                     row_bytes, d.max_blocks, faults, counts, r.hot_blocks, r.host_bt,
                      static_cast<const uint8_t*>(r.host_rows), r.host_scale, r.host_layer_rows,
                      static_cast<uint8_t*>(r.pool), r.row_scale, r.pool_layer_rows, r.step);
   return hipGetLastError();

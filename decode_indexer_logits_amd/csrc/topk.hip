@@ -6,17 +6,21 @@
 // Scores map to order-preserving uint32 keys.  A row (one request position,
 // up to 2^24 tokens) is spread over many workgroups so that a handful of very
 // long rows still fills the chip:
-//   1. zero      per-row histogram and counters
-//   2. histogram of the top 11 key bits, per 8192-token chunk: LDS counts,
-//                then one global atomic per non-empty bin
-//   3. filter    every chunk re-derives the bin b1 holding the K-th largest
-//                key; keys above b1 are selected outright, keys in b1 become
-//                candidates (wave ballots aggregate the global appends)
-//   4. finalize  one workgroup per row finishes the radix select on the
-//                candidates (11 + 10 more bits), resolves ties at the
-//                threshold toward the lower token (radix select on the token
-//                index), collects the K tokens and writes them in ascending
-//                order through an LDS bitmap per 64K-token segment.
+//   1. zero       per-row histogram and counters
+//   2. histogram  of the top 11 key bits, per 8192-token chunk: LDS counts,
+//                 then one global atomic per non-empty bin (the fused path of
+//                 hs_indexer_topk builds it in the indexer's epilogue instead)
+//   3. filter     every chunk re-derives the bin b1 holding the K-th largest
+//                 key; keys above b1 are selected outright, keys in b1 become
+//                 candidates (one global append per workgroup)
+//   4. finalize   one workgroup per row goes on with the radix select over
+//                 the candidates (11 + 10 more bits), sends ties at the
+//                 threshold to the lower token (radix select on the token
+//                 index), and writes the K tokens in ascending order through
+//                 an LDS bitmap per 64K-token segment.
+// Passes 3 and 4 stay separate kernels: handing a row from many workgroups to
+// one inside a kernel needs a device-scope release per workgroup, which on a
+// multi-die GPU writes back L2 and costs far more than a kernel boundary.
 // The selection is exact: the same tokens as a full sort by (score desc,
 // token asc), written in ascending token order, -1 padded for short rows.
 #include "hs_common.h"
@@ -28,14 +32,16 @@ namespace {
 constexpr int kBins1 = 2048;   // top 11 key bits
 constexpr int kChunk = 8192;   // tokens per workgroup in passes 2 and 3
 constexpr int kScanNT = 256;
-constexpr int kFinNT = 1024;
 constexpr int kMaxK = 8192;
+constexpr int kCnt = 8;                   // counters per row
+constexpr int kFinNT = 1024;
 constexpr int kSegTok = 1 << 16;          // tokens per bitmap segment in finalize
 constexpr int kSegWords = kSegTok / 32;
 
 struct TopkWs {
   uint32_t* hist;   // [R][2048]
-  uint32_t* cnt;    // [R][4]: selected-above count, candidate count, b1, count above b1
+  uint32_t* cnt;    // [R][8]: selected-above count, candidate count, b1, count above b1,
+                    //         finished-chunk ticket
   int32_t* sel;     // [R][K]
   uint32_t* ckey;   // [R][T_stride]
   int32_t* ctok;    // [R][T_stride]
@@ -49,7 +55,7 @@ __host__ __device__ inline TopkWs topk_ws(void* base, int R, int T_stride, int K
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)R * kBins1 * 4);
   w.cnt = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)R * 4 * 4);
+  p += align256((size_t)R * kCnt * 4);
   w.sel = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)R * K * 4);
   w.ckey = reinterpret_cast<uint32_t*>(p);
@@ -100,7 +106,7 @@ __device__ void find_bin(const uint32_t* h, int nbins, uint32_t k, bool from_top
 __global__ __launch_bounds__(kScanNT) void topk_zero_kernel(TopkWs ws) {
   const int r = blockIdx.x;
   for (int i = threadIdx.x; i < kBins1; i += kScanNT) ws.hist[(size_t)r * kBins1 + i] = 0;
-  if (threadIdx.x < 4) ws.cnt[r * 4 + threadIdx.x] = 0;
+  if (threadIdx.x < kCnt) ws.cnt[r * kCnt + threadIdx.x] = 0;
 }
 
 __global__ __launch_bounds__(kScanNT) void topk_hist_kernel(const int32_t* __restrict__ ctx_len,
@@ -132,6 +138,111 @@ __global__ __launch_bounds__(kScanNT) void topk_hist_kernel(const int32_t* __res
     if (h[i]) atomicAdd(&ws.hist[(size_t)r * kBins1 + i], h[i]);
 }
 
+// Finishes row r (n > K visible tokens) from the outright selections and the
+// candidates written by every chunk of the row.
+template <int NT>
+__device__ void finalize_row(int r, int n, int T_stride, int K, const TopkWs& ws,
+                             int32_t* __restrict__ out, uint32_t* h, int32_t* outl, uint32_t* bm,
+                             int* scratch, int* s_d, uint32_t* s_before, int* s_pos) {
+  const int tid = threadIdx.x;
+  const uint32_t b1 = ws.cnt[r * kCnt + 2];
+  const uint32_t above = ws.cnt[r * kCnt + 3];
+  const int nc = (int)ws.cnt[r * kCnt + 1];
+  const uint32_t* ck = ws.ckey + (size_t)r * T_stride;
+  const int32_t* ct = ws.ctok + (size_t)r * T_stride;
+  uint32_t kk = (uint32_t)K - above;   // candidates still needed, >= 1
+  // key bits 20..10
+  for (int i = tid; i < kBins1; i += NT) h[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < nc; i += NT) atomicAdd(&h[(ck[i] >> 10) & 0x7FFu], 1u);
+  __syncthreads();
+  find_bin<NT>(h, kBins1, kk, true, scratch, s_d, s_before);
+  const uint32_t dA = (uint32_t)*s_d;
+  kk -= *s_before;
+  // key bits 9..0
+  for (int i = tid; i < 1024; i += NT) h[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < nc; i += NT) {
+    const uint32_t key = ck[i];
+    if (((key >> 10) & 0x7FFu) == dA) atomicAdd(&h[key & 0x3FFu], 1u);
+  }
+  __syncthreads();
+  find_bin<NT>(h, 1024, kk, true, scratch, s_d, s_before);
+  const uint32_t dB = (uint32_t)*s_d;
+  kk -= *s_before;                       // ties at the threshold to take
+  const uint32_t n_eq = h[dB];
+  const uint32_t tau = (b1 << 21) | (dA << 10) | dB;
+  __syncthreads();
+  // ties: keep the kk lowest tokens among keys == tau
+  int t_cut = 0x7FFFFFFF;
+  if (n_eq > kk) {
+    uint32_t prefix = 0, need = kk;
+    for (int sh = 16; sh >= 0; sh -= 8) {
+      for (int i = tid; i < 256; i += NT) h[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < nc; i += NT) {
+        if (ck[i] != tau) continue;
+        const uint32_t t = (uint32_t)ct[i];
+        if (sh == 16 || (t >> (sh + 8)) == prefix) atomicAdd(&h[(t >> sh) & 0xFFu], 1u);
+      }
+      __syncthreads();
+      find_bin<NT>(h, 256, need, false, scratch, s_d, s_before);
+      prefix = (prefix << 8) | (uint32_t)*s_d;
+      need -= *s_before;
+      __syncthreads();
+    }
+    t_cut = (int)prefix;
+  }
+  // collect: the tokens selected outright, then the chosen candidates
+  const int32_t* sel = ws.sel + (size_t)r * K;
+  for (int i = tid; i < (int)above; i += NT) outl[i] = sel[i];
+  if (tid == 0) *s_pos = (int)above;
+  __syncthreads();
+  for (int i = tid; i < nc; i += NT) {
+    const uint32_t key = ck[i];
+    const int t = ct[i];
+    if (key > tau || (key == tau && t <= t_cut)) {
+      const int at = atomicAdd(s_pos, 1);
+      if (at < kMaxK) outl[at] = t;
+    }
+  }
+  __syncthreads();
+  // emit the K selected tokens in ascending order: an LDS bitmap per 2^16-token
+  // segment, then a popcount prefix sum over its words
+  constexpr int kWpt = kSegWords / NT;   // words per thread
+  int written = 0;
+  const int nseg = (n + kSegTok - 1) / kSegTok;
+  for (int sg = 0; sg < nseg; ++sg) {
+    for (int i = tid; i < kSegWords; i += NT) bm[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < K; i += NT) {
+      const int t = outl[i];
+      if (t / kSegTok == sg) atomicOr(&bm[(t % kSegTok) >> 5], 1u << (t & 31));
+    }
+    __syncthreads();
+    uint32_t wd[kWpt];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kWpt; ++j) {
+      wd[j] = bm[tid * kWpt + j];
+      cnt += __popc(wd[j]);
+    }
+    int tot;
+    int pos = written + block_exclusive_scan<NT>(cnt, scratch, &tot);
+#pragma unroll
+    for (int j = 0; j < kWpt; ++j) {
+      uint32_t x = wd[j];
+      const int t0 = sg * kSegTok + (tid * kWpt + j) * 32;
+      while (x) {
+        const int bit = __ffs(x) - 1;
+        out[pos++] = t0 + bit;
+        x &= x - 1;
+      }
+    }
+    written += tot;
+  }
+}
+
 __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __restrict__ ctx_len,
                                                               int P, int T_stride, int K,
                                                               const float* __restrict__ scores,
@@ -159,8 +270,8 @@ __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __r
   find_bin<kScanNT>(h, kBins1, (uint32_t)K, true, scratch, &s_b1, &s_above);
   const uint32_t b1 = (uint32_t)s_b1;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    ws.cnt[r * 4 + 2] = b1;
-    ws.cnt[r * 4 + 3] = s_above;
+    ws.cnt[r * kCnt + 2] = b1;
+    ws.cnt[r * kCnt + 3] = s_above;
   }
   // count this thread's selections (low 16 bits) and candidates (high 16 bits)
   int packed = 0;
@@ -173,8 +284,8 @@ __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __r
   int total;
   const int ex = block_exclusive_scan<kScanNT>(packed, scratch, &total);
   if (threadIdx.x == 0) {
-    s_base_sel = (total & 0xFFFF) ? atomicAdd(&ws.cnt[r * 4 + 0], (uint32_t)(total & 0xFFFF)) : 0u;
-    s_base_cand = (total >> 16) ? atomicAdd(&ws.cnt[r * 4 + 1], (uint32_t)(total >> 16)) : 0u;
+    s_base_sel = (total & 0xFFFF) ? atomicAdd(&ws.cnt[r * kCnt + 0], (uint32_t)(total & 0xFFFF)) : 0u;
+    s_base_cand = (total >> 16) ? atomicAdd(&ws.cnt[r * kCnt + 1], (uint32_t)(total >> 16)) : 0u;
   }
   __syncthreads();
   uint32_t ps = s_base_sel + (uint32_t)(ex & 0xFFFF);
@@ -204,121 +315,23 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   __shared__ int32_t outl[kMaxK];
   __shared__ uint32_t bm[kSegWords];
   __shared__ int scratch[kFinNT / kWave + 1];
-  __shared__ int s_d;
+  __shared__ int s_d, s_pos;
   __shared__ uint32_t s_before;
-  __shared__ int s_pos;
   const int r = blockIdx.x;
-  const int tid = threadIdx.x;
   const int n = row_visible(ctx_len, P, r);
   int32_t* out = topk + (size_t)r * K;
   if (n <= K) {
-    for (int k = tid; k < K; k += kFinNT) out[k] = k < n ? k : -1;
+    for (int k = threadIdx.x; k < K; k += kFinNT) out[k] = k < n ? k : -1;
     return;
   }
-  const uint32_t b1 = ws.cnt[r * 4 + 2];
-  const uint32_t above = ws.cnt[r * 4 + 3];
-  const int nc = (int)ws.cnt[r * 4 + 1];
-  const uint32_t* ck = ws.ckey + (size_t)r * T_stride;
-  const int32_t* ct = ws.ctok + (size_t)r * T_stride;
-  uint32_t kk = (uint32_t)K - above;   // candidates still needed, >= 1
-
-  // key bits 20..10
-  for (int i = tid; i < kBins1; i += kFinNT) h[i] = 0;
-  __syncthreads();
-  for (int i = tid; i < nc; i += kFinNT) atomicAdd(&h[(ck[i] >> 10) & 0x7FFu], 1u);
-  __syncthreads();
-  find_bin<kFinNT>(h, kBins1, kk, true, scratch, &s_d, &s_before);
-  const uint32_t dA = (uint32_t)s_d;
-  kk -= s_before;
-  // key bits 9..0
-  for (int i = tid; i < 1024; i += kFinNT) h[i] = 0;
-  __syncthreads();
-  for (int i = tid; i < nc; i += kFinNT) {
-    const uint32_t key = ck[i];
-    if (((key >> 10) & 0x7FFu) == dA) atomicAdd(&h[key & 0x3FFu], 1u);
-  }
-  __syncthreads();
-  find_bin<kFinNT>(h, 1024, kk, true, scratch, &s_d, &s_before);
-  const uint32_t dB = (uint32_t)s_d;
-  kk -= s_before;                        // ties at the threshold to take
-  const uint32_t n_eq = h[dB];
-  const uint32_t tau = (b1 << 21) | (dA << 10) | dB;
-  __syncthreads();
-  // ties: keep the kk lowest tokens among keys == tau
-  int t_cut = 0x7FFFFFFF;
-  if (n_eq > kk) {
-    uint32_t prefix = 0, need = kk;
-    for (int sh = 16; sh >= 0; sh -= 8) {
-      for (int i = tid; i < 256; i += kFinNT) h[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < nc; i += kFinNT) {
-        if (ck[i] != tau) continue;
-        const uint32_t t = (uint32_t)ct[i];
-        if (sh == 16 || (t >> (sh + 8)) == prefix) atomicAdd(&h[(t >> sh) & 0xFFu], 1u);
-      }
-      __syncthreads();
-      find_bin<kFinNT>(h, 256, need, false, scratch, &s_d, &s_before);
-      prefix = (prefix << 8) | (uint32_t)s_d;
-      need -= s_before;
-      __syncthreads();
-    }
-    t_cut = (int)prefix;
-  }
-  // collect: the tokens selected outright, then the chosen candidates
-  const int32_t* sel = ws.sel + (size_t)r * K;
-  for (int i = tid; i < (int)above; i += kFinNT) outl[i] = sel[i];
-  if (tid == 0) s_pos = (int)above;
-  __syncthreads();
-  for (int i = tid; i < nc; i += kFinNT) {
-    const uint32_t key = ck[i];
-    const int t = ct[i];
-    if (key > tau || (key == tau && t <= t_cut)) {
-      const int at = atomicAdd(&s_pos, 1);
-      if (at < kMaxK) outl[at] = t;
-    }
-  }
-  __syncthreads();
-  // emit the K selected tokens in ascending order: an LDS bitmap per 2^16-token
-  // segment, then a popcount prefix sum over its words
-  int written = 0;
-  const int nseg = (n + kSegTok - 1) / kSegTok;
-  for (int sg = 0; sg < nseg; ++sg) {
-    for (int i = tid; i < kSegWords; i += kFinNT) bm[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < K; i += kFinNT) {
-      const int t = outl[i];
-      if (t / kSegTok == sg) atomicOr(&bm[(t % kSegTok) >> 5], 1u << (t & 31));
-    }
-    __syncthreads();
-    constexpr int kWpt = kSegWords / kFinNT;   // words per thread
-    uint32_t wd[kWpt];
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < kWpt; ++j) {
-      wd[j] = bm[tid * kWpt + j];
-      cnt += __popc(wd[j]);
-    }
-    int tot;
-    int pos = written + block_exclusive_scan<kFinNT>(cnt, scratch, &tot);
-#pragma unroll
-    for (int j = 0; j < kWpt; ++j) {
-      uint32_t x = wd[j];
-      const int t0 = sg * kSegTok + (tid * kWpt + j) * 32;
-      while (x) {
-        const int bit = __ffs(x) - 1;
-        out[pos++] = t0 + bit;
-        x &= x - 1;
-      }
-    }
-    written += tot;
-  }
+  finalize_row<kFinNT>(r, n, T_stride, K, ws, out, h, outl, bm, scratch, &s_d, &s_before, &s_pos);
 }
 
 }  // namespace
 
 size_t topk_workspace_bytes(int B, int P, int T_stride, int K) {
   const size_t R = (size_t)B * P;
-  return align256(R * kBins1 * 4) + align256(R * 16) + align256(R * K * 4) +
+  return align256(R * kBins1 * 4) + align256(R * kCnt * 4) + align256(R * K * 4) +
          align256(R * T_stride * 4) + align256(R * T_stride * 4);
 }
 
@@ -330,6 +343,22 @@ hipError_t launch_topk(const BatchDims& d, int K, const float* scores, int32_t* 
   hipLaunchKernelGGL(topk_zero_kernel, dim3(R), dim3(kScanNT), 0, s, w);
   hipLaunchKernelGGL(topk_hist_kernel, dim3(nchunk, R), dim3(kScanNT), 0, s, d.ctx_len, d.P,
                      d.T_stride, K, scores, w);
+  return launch_topk_select(d, K, scores, topk, ws, s);
+}
+
+hipError_t launch_topk_zero(const BatchDims& d, int K, void* ws, uint32_t** hist, hipStream_t s) {
+  const int R = d.B * d.P;
+  TopkWs w = topk_ws(ws, R, d.T_stride, K);
+  *hist = w.hist;
+  hipLaunchKernelGGL(topk_zero_kernel, dim3(R), dim3(kScanNT), 0, s, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_select(const BatchDims& d, int K, const float* scores, int32_t* topk,
+                              void* ws, hipStream_t s) {
+  const int R = d.B * d.P;
+  TopkWs w = topk_ws(ws, R, d.T_stride, K);
+  const int nchunk = (d.T_stride + kChunk - 1) / kChunk;
   hipLaunchKernelGGL(topk_filter_kernel, dim3(nchunk, R), dim3(kScanNT), 0, s, d.ctx_len, d.P,
                      d.T_stride, K, scores, w);
   hipLaunchKernelGGL(topk_finalize_kernel, dim3(R), dim3(kFinNT), 0, s, d.ctx_len, d.P,

@@ -128,6 +128,13 @@ class DeviceStep:
     def run_topk(self, stream=None):
         _lib.topk(self.batch, self.wl.K, self.scores, self.topk, self.ws_topk, stream)
 
+    def run_indexer_topk(self, stream=None):
+        """Indexer and top-K in one call (histogram pass fused into the indexer)."""
+        wl = self.wl
+        _lib.indexer_topk(self.batch, wl.H_idx, wl.D_idx, wl.q_dtype, self.q_idx, self.w,
+                          wl.k_dtype, self.idx_pool, self.idx_scale, self.idx_bt, self.bias,
+                          self.scores, wl.K, self.topk, self.ws_topk, stream)
+
     def run_resolve(self, stream=None):
         _lib.resolve_rows(self.batch, self.wl.K, self.topk, self.res, self.row_ids, self.faults,
                           self.counts, stream)
@@ -141,9 +148,8 @@ class DeviceStep:
                                self.ws_mla, stream)
 
     def run(self, stream=None):
-        """One whole decode step: indexer, top-K, resolve (+ fault copies), L x attention."""
-        self.run_indexer(stream)
-        self.run_topk(stream)
+        """One whole decode step: indexer + top-K, resolve (+ fault copies), L x attention."""
+        self.run_indexer_topk(stream)
         self.run_resolve(stream)
         for l in range(self.wl.L):
             self.run_attention(l, stream)
@@ -211,11 +217,10 @@ class DeviceStep:
             ch = self._chunk(c, nchunks)
             sl, batch, res = ch["sl"], ch["batch"], ch["res"]
             with torch.cuda.stream(cs):
-                _lib.indexer_scores(batch, wl.H_idx, wl.D_idx, wl.q_dtype, self.q_idx[sl],
-                                    self.w[sl], wl.k_dtype, self.idx_pool, self.idx_scale,
-                                    self.idx_bt[sl], None if self.bias is None else self.bias[sl],
-                                    self.scores[sl])
-                _lib.topk(batch, wl.K, self.scores[sl], self.topk[sl], self.ws_topk)
+                _lib.indexer_topk(batch, wl.H_idx, wl.D_idx, wl.q_dtype, self.q_idx[sl],
+                                  self.w[sl], wl.k_dtype, self.idx_pool, self.idx_scale,
+                                  self.idx_bt[sl], None if self.bias is None else self.bias[sl],
+                                  self.scores[sl], wl.K, self.topk[sl], self.ws_topk)
                 _lib.resolve_tables(batch, wl.K, self.topk[sl], res, self.row_ids[sl],
                                     self.faults[sl], self.counts[sl])
                 ev = torch.cuda.Event()

@@ -123,6 +123,17 @@ hs_status hs_indexer_scores(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
 hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t* topk,
                   void* ws, size_t ws_bytes, void* stream);
 
+/* hs_indexer_scores followed by hs_topk, with the first pass of the top-K
+ * radix select (the per-row histogram of the top 11 score-key bits) built in
+ * the indexer's epilogue instead of a separate pass over the scores.  Same
+ * arguments, outputs and workspace (hs_workspace_bytes(HS_OP_TOPK, ...)) as
+ * the two calls; scores are still written. */
+hs_status hs_indexer_topk(const hs_batch* batch, int32_t H_idx, int32_t D_idx, hs_dtype q_t,
+                          const void* q_idx, const float* w, hs_dtype k_t, const void* idx_pool,
+                          const float* idx_scale, const int32_t* idx_bt, const float* bias,
+                          float* scores, int32_t K, int32_t* topk, void* ws, size_t ws_bytes,
+                          void* stream);
+
 /* Residency state of a batch: one shared paged pool of latent rows on the GPU,
  * per-request hot buffers made of ordinary pool blocks (page "Un contexte d'un
  * million sur huit H200", section "Les trois états de résidence", last

@@ -298,3 +298,30 @@ def test_pipelined_chunks_of_eight_against_oracle():
         gc.check_resolve(wl, gc.oracle_state(wl), got["topk"], got)
         for k in ("topk", "row_ids", "counts", "out", "lse"):
             assert np.array_equal(got[k], g1[k]), (rep, k)
+
+
+@pytest.mark.parametrize("name", ["resident_fp8", "mtp3", "tiny"])
+def test_fused_indexer_topk_matches_separate_calls(name):
+    _say(f"fused indexer+top-K vs separate: {name}")
+    if name == "resident_fp8":
+        wl = gen.resident_fp8(B=4)
+    elif name == "mtp3":
+        wl = gen.mtp3_agentic(B=3, K=128, steps=1, first_turn=6000, per_turn=300, turns=5, out_max=50)
+    else:
+        wl = gen.tiny_fp32(K=256)
+    from decode_indexer_logits_amd.device import DeviceStep
+    ds = DeviceStep(wl)
+    ds.run_indexer()
+    ds.run_topk()
+    torch.cuda.synchronize()
+    s1, t1 = ds.scores.clone(), ds.topk.clone()
+    ds.scores.fill_(float("nan"))
+    ds.topk.fill_(-7)
+    ds.run_indexer_topk()
+    torch.cuda.synchronize()
+    for b in range(wl.B):
+        for p in range(wl.P):
+            n = max(int(wl.ctx_len[b]) - wl.P + p + 1, 0)
+            assert torch.equal(ds.scores[b, p, :n], s1[b, p, :n])
+    assert torch.equal(ds.topk, t1)
+    gc.check_topk_exact(wl, ds.scores.cpu().numpy(), ds.topk.cpu().numpy())
