@@ -99,6 +99,7 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   __shared__ int32_t sU[kMaxSel];          // U when P > 1
   __shared__ int32_t sF[kMaxSel];          // faulting tokens, ascending
   __shared__ int32_t sHot[kMaxHotBlocks];  // this request's hot blocks
+  __shared__ uint32_t sHitMask[kMaxHotBlocks * 2];   // slots hit at this step (C bits)
   __shared__ int scratch[kResNT / kWave + 1];
   __shared__ uint32_t h256[256];
   __shared__ int s_nlist[4];
@@ -130,6 +131,17 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
     s_kmax = 0ull;
   }
   for (int i = tid; i < (C >> 6); i += kResNT) sHot[i] = hot_blocks[(size_t)b * (C >> 6) + i];
+  for (int i = tid; i < (C >> 5); i += kResNT) sHitMask[i] = 0u;
+  // stamps of this thread's contiguous run of slots, for the victim choice;
+  // loaded now, before the hits of this step are known (they are masked in
+  // from sHitMask later instead of read back)
+  const int S = (C + kResNT - 1) / kResNT;
+  int st_reg[kMaxSlotsPerThread];
+#pragma unroll
+  for (int j = 0; j < kMaxSlotsPerThread; ++j) {
+    const int v = tid * S + j;
+    st_reg[j] = (j < S && v < C) ? stp[v] : 0x7FFFFFFF;
+  }
   __syncthreads();
 
   // 1. U = sorted distinct selected tokens.  Each list is sorted with a -1
@@ -191,17 +203,17 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   int tok[kMaxEntriesPerThread], row[kMaxEntriesPerThread];
   int rb[kMaxEntriesPerThread];
   int64_t hrow[kMaxEntriesPerThread];
+  // the hot-slot lookup is issued with the page lookups (every token has an
+  // entry), so the classification waits for one round of loads, not two
+  int vs[kMaxEntriesPerThread];
 #pragma unroll
   for (int e = 0; e < kMaxEntriesPerThread; ++e) {
     const bool ok = e < E && u0 + e < nU;
     tok[e] = ok ? U[u0 + e] : -1;
     rb[e] = ok ? btb[tok[e] >> 6] : 0;
     hrow[e] = (ok && hbt) ? hbt[tok[e] >> 6] : -1;
+    vs[e] = (ok && C > 0) ? t2s[tok[e]] : -1;
   }
-  int vs[kMaxEntriesPerThread];
-#pragma unroll
-  for (int e = 0; e < kMaxEntriesPerThread; ++e)
-    vs[e] = (tok[e] >= 0 && rb[e] < 0 && C > 0) ? t2s[tok[e]] : -1;
   int my_res = 0, my_hit = 0, my_f = 0;
 #pragma unroll
   for (int e = 0; e < kMaxEntriesPerThread; ++e) {
@@ -214,6 +226,7 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
     } else if (vs[e] >= 0) {
       ++my_hit;
       stp[vs[e]] = s;
+      atomicOr(&sHitMask[vs[e] >> 5], 1u << (vs[e] & 31));
       row[e] = sHot[vs[e] >> 6] * kBlock + (vs[e] & 63);
     } else if (hrow[e] < 0) {
       atomicOr(err, 2);
@@ -250,13 +263,11 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   bool keys64 = false;            // victims as sorted 64-bit keys (general path)
   int32_t* V32 = sA;              // victim slots, fast path (R1: the merge lists are dead)
   if (nF > 0 && C > 0) {
-    const int S = (C + kResNT - 1) / kResNT;
-    int st_reg[kMaxSlotsPerThread];
     int my_c = 0, my_min = 0x7FFFFFFF;
 #pragma unroll
     for (int j = 0; j < kMaxSlotsPerThread; ++j) {
       const int v = tid * S + j;
-      st_reg[j] = (j < S && v < C) ? stp[v] : 0x7FFFFFFF;
+      if (j < S && v < C && (sHitMask[v >> 5] >> (v & 31)) & 1u) st_reg[j] = s;
       if (st_reg[j] < s) {
         ++my_c;
         my_min = min(my_min, st_reg[j]);
@@ -443,8 +454,9 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
 // request's faults are cut into batches of kCopyBatch; batches are dealt to
 // workgroups round-robin in request order.  A workgroup resolves a batch's
 // source and destination rows once into LDS, then streams its 16-byte chunks
-// with kCopyInFlight independent loads per thread.
-__global__ __launch_bounds__(kCopyNT) void fault_copy_kernel(
+// with U independent loads per thread.
+template <int NT, int U>
+__global__ __launch_bounds__(NT) void fault_copy_kernel(
     int B, int PK, int C, int L, int row_bytes, int max_blocks, const int32_t* __restrict__ faults,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ hot_blocks,
     const int64_t* __restrict__ host_bt, const uint8_t* __restrict__ host_rows,
@@ -465,7 +477,7 @@ __global__ __launch_bounds__(kCopyNT) void fault_copy_kernel(
       const int f0 = j * kCopyBatch;
       const int nloc = min(kCopyBatch, n - f0);
       // one (fault, layer) per thread: source and destination byte offsets
-      for (int i = threadIdx.x; i < nloc * L; i += kCopyNT) {
+      for (int i = threadIdx.x; i < nloc * L; i += NT) {
         const int fi = f0 + i / L, l = i % L;
         const int32_t* fb = faults + ((size_t)b * PK + fi) * 2;
         const int t = fb[0], sl = fb[1];
@@ -479,25 +491,22 @@ __global__ __launch_bounds__(kCopyNT) void fault_copy_kernel(
       }
       __syncthreads();
       const int nchunk = nloc * L * cpr;
-      for (int c0 = 0; c0 < nchunk; c0 += kCopyNT * kCopyInFlight) {
-        uint4 v0, v1, v2, v3;
-        int64_t d0 = -1, d1 = -1, d2 = -1, d3 = -1;
-        auto load = [&](int u, uint4& v, int64_t& d) {
-          const int idx = c0 + u * kCopyNT + (int)threadIdx.x;
+      for (int c0 = 0; c0 < nchunk; c0 += NT * U) {
+        uint4 v[U];
+        int64_t d[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int idx = c0 + u * NT + (int)threadIdx.x;
+          d[u] = -1;
           if (idx < nchunk) {
             const int row = idx / cpr, c = idx - row * cpr;
-            v = *reinterpret_cast<const uint4*>(host_rows + s_src[row] + (int64_t)c * 16);
-            d = s_dst[row] + (int64_t)c * 16;
+            v[u] = *reinterpret_cast<const uint4*>(host_rows + s_src[row] + (int64_t)c * 16);
+            d[u] = s_dst[row] + (int64_t)c * 16;
           }
-        };
-        load(0, v0, d0);
-        load(1, v1, d1);
-        load(2, v2, d2);
-        load(3, v3, d3);
-        if (d0 >= 0) *reinterpret_cast<uint4*>(pool + d0) = v0;
-        if (d1 >= 0) *reinterpret_cast<uint4*>(pool + d1) = v1;
-        if (d2 >= 0) *reinterpret_cast<uint4*>(pool + d2) = v2;
-        if (d3 >= 0) *reinterpret_cast<uint4*>(pool + d3) = v3;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (d[u] >= 0) *reinterpret_cast<uint4*>(pool + d[u]) = v[u];
       }
       __syncthreads();
     }
@@ -519,7 +528,7 @@ hipError_t launch_fault_copy(const BatchDims& d, int K, const ResidencyArgs& r,
                              const int32_t* faults, const int32_t* counts, hipStream_t s) {
   const int PK = d.P * K;
   const int row_bytes = kDLat * r.kv_bytes;
-  hipLaunchKernelGGL(fault_copy_kernel, dim3(kCopyWGs), dim3(kCopyNT), 0, s, d.B, PK, r.C, r.L,
+  hipLaunchKernelGGL((fault_copy_kernel<kCopyNT, kCopyInFlight>), dim3(kCopyWGs), dim3(kCopyNT), 0, s, d.B, PK, r.C, r.L,
                      row_bytes, d.max_blocks, faults, counts, r.hot_blocks, r.host_bt,
                      static_cast<const uint8_t*>(r.host_rows), r.host_scale, r.host_layer_rows,
                      static_cast<uint8_t*>(r.pool), r.row_scale, r.pool_layer_rows, r.step);

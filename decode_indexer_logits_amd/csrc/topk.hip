@@ -21,6 +21,11 @@
 // Passes 3 and 4 stay separate kernels: handing a row from many workgroups to
 // one inside a kernel needs a device-scope release per workgroup, which on a
 // multi-die GPU writes back L2 and costs far more than a kernel boundary.
+// Rows of at most 2^18 tokens skip that hand-off: one 1024-thread workgroup per
+// row streams the row once (keys above the threshold bin go straight into an
+// LDS bitmap, keys in it into an LDS candidate list), finishes the radix select
+// and emits from the bitmap -- one kernel after the histogram instead of two,
+// and no candidate round trip through HBM.
 // The selection is exact: the same tokens as a full sort by (score desc,
 // token asc), written in ascending token order, -1 padded for short rows.
 #include "hs_common.h"
@@ -37,6 +42,11 @@ constexpr int kCnt = 8;                   // counters per row
 constexpr int kFinNT = 1024;
 constexpr int kSegTok = 1 << 16;          // tokens per bitmap segment in finalize
 constexpr int kSegWords = kSegTok / 32;
+constexpr int kSelNT = 1024;
+constexpr int kSelMaxN = 1 << 18;         // longest row of the one-workgroup select
+constexpr int kSelWords = kSelMaxN / 32;
+constexpr int kSelCand = 12288;           // candidates held in LDS (else in the workspace)
+constexpr int kSelU = 8;                  // 16-byte score loads per thread per round
 
 struct TopkWs {
   uint32_t* hist;   // [R][2048]
@@ -138,19 +148,15 @@ __global__ __launch_bounds__(kScanNT) void topk_hist_kernel(const int32_t* __res
     if (h[i]) atomicAdd(&ws.hist[(size_t)r * kBins1 + i], h[i]);
 }
 
-// Finishes row r (n > K visible tokens) from the outright selections and the
-// candidates written by every chunk of the row.
+// Exact threshold among the candidates ck/ct[0, nc) (every key has top bits
+// b1): tau = the kk-th largest key (bits 20..10, then 9..0), and t_cut = the
+// largest token kept among keys equal to tau (ties go to lower tokens;
+// INT_MAX when all of them are kept).  Returned in every thread.
 template <int NT>
-__device__ void finalize_row(int r, int n, int T_stride, int K, const TopkWs& ws,
-                             int32_t* __restrict__ out, uint32_t* h, int32_t* outl, uint32_t* bm,
-                             int* scratch, int* s_d, uint32_t* s_before, int* s_pos) {
+__device__ void candidates_threshold(const uint32_t* ck, const int32_t* ct, int nc, uint32_t b1,
+                                     uint32_t kk, uint32_t* h, int* scratch, int* s_d,
+                                     uint32_t* s_before, uint32_t* tau_out, int* t_cut_out) {
   const int tid = threadIdx.x;
-  const uint32_t b1 = ws.cnt[r * kCnt + 2];
-  const uint32_t above = ws.cnt[r * kCnt + 3];
-  const int nc = (int)ws.cnt[r * kCnt + 1];
-  const uint32_t* ck = ws.ckey + (size_t)r * T_stride;
-  const int32_t* ct = ws.ctok + (size_t)r * T_stride;
-  uint32_t kk = (uint32_t)K - above;   // candidates still needed, >= 1
   // key bits 20..10
   for (int i = tid; i < kBins1; i += NT) h[i] = 0;
   __syncthreads();
@@ -193,6 +199,55 @@ __device__ void finalize_row(int r, int n, int T_stride, int K, const TopkWs& ws
     }
     t_cut = (int)prefix;
   }
+  *tau_out = tau;
+  *t_cut_out = t_cut;
+}
+
+// Writes the set bits of bm[0, nwords) as ascending tokens t_base + bit to
+// out[written ...]; returns the number written.  Every thread must call it.
+template <int NT, int WPT>
+__device__ int emit_bitmap(const uint32_t* bm, int nwords, int t_base, int written,
+                           int32_t* __restrict__ out, int* scratch) {
+  const int tid = threadIdx.x;
+  uint32_t wd[WPT];
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int w = tid * WPT + j;
+    wd[j] = w < nwords ? bm[w] : 0u;
+    cnt += __popc(wd[j]);
+  }
+  int tot;
+  int pos = written + block_exclusive_scan<NT>(cnt, scratch, &tot);
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    uint32_t x = wd[j];
+    const int t0 = t_base + (tid * WPT + j) * 32;
+    while (x) {
+      const int bit = __ffs(x) - 1;
+      out[pos++] = t0 + bit;
+      x &= x - 1;
+    }
+  }
+  return tot;
+}
+
+// Finishes row r (n > K visible tokens) from the outright selections and the
+// candidates written by every chunk of the row.
+template <int NT>
+__device__ void finalize_row(int r, int n, int T_stride, int K, const TopkWs& ws,
+                             int32_t* __restrict__ out, uint32_t* h, int32_t* outl, uint32_t* bm,
+                             int* scratch, int* s_d, uint32_t* s_before, int* s_pos) {
+  const int tid = threadIdx.x;
+  const uint32_t b1 = ws.cnt[r * kCnt + 2];
+  const uint32_t above = ws.cnt[r * kCnt + 3];
+  const int nc = (int)ws.cnt[r * kCnt + 1];
+  const uint32_t* ck = ws.ckey + (size_t)r * T_stride;
+  const int32_t* ct = ws.ctok + (size_t)r * T_stride;
+  uint32_t tau;
+  int t_cut;
+  candidates_threshold<NT>(ck, ct, nc, b1, (uint32_t)K - above, h, scratch, s_d, s_before, &tau,
+                           &t_cut);
   // collect: the tokens selected outright, then the chosen candidates
   const int32_t* sel = ws.sel + (size_t)r * K;
   for (int i = tid; i < (int)above; i += NT) outl[i] = sel[i];
@@ -209,7 +264,6 @@ __device__ void finalize_row(int r, int n, int T_stride, int K, const TopkWs& ws
   __syncthreads();
   // emit the K selected tokens in ascending order: an LDS bitmap per 2^16-token
   // segment, then a popcount prefix sum over its words
-  constexpr int kWpt = kSegWords / NT;   // words per thread
   int written = 0;
   const int nseg = (n + kSegTok - 1) / kSegTok;
   for (int sg = 0; sg < nseg; ++sg) {
@@ -220,26 +274,7 @@ __device__ void finalize_row(int r, int n, int T_stride, int K, const TopkWs& ws
       if (t / kSegTok == sg) atomicOr(&bm[(t % kSegTok) >> 5], 1u << (t & 31));
     }
     __syncthreads();
-    uint32_t wd[kWpt];
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < kWpt; ++j) {
-      wd[j] = bm[tid * kWpt + j];
-      cnt += __popc(wd[j]);
-    }
-    int tot;
-    int pos = written + block_exclusive_scan<NT>(cnt, scratch, &tot);
-#pragma unroll
-    for (int j = 0; j < kWpt; ++j) {
-      uint32_t x = wd[j];
-      const int t0 = sg * kSegTok + (tid * kWpt + j) * 32;
-      while (x) {
-        const int bit = __ffs(x) - 1;
-        out[pos++] = t0 + bit;
-        x &= x - 1;
-      }
-    }
-    written += tot;
+    written += emit_bitmap<NT, kSegWords / NT>(bm, kSegWords, sg * kSegTok, written, out, scratch);
   }
 }
 
@@ -327,6 +362,101 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   finalize_row<kFinNT>(r, n, T_stride, K, ws, out, h, outl, bm, scratch, &s_d, &s_before, &s_pos);
 }
 
+// Filter and finalize of one row (n <= 2^18 visible tokens) in one workgroup,
+// from the row's complete 11-bit histogram.
+__global__ __launch_bounds__(kSelNT) void topk_select_row_kernel(
+    const int32_t* __restrict__ ctx_len, int P, int T_stride, int K,
+    const float* __restrict__ scores, TopkWs ws, int32_t* __restrict__ topk) {
+  __shared__ uint32_t h[kBins1];
+  __shared__ uint32_t bm[kSelWords];
+  __shared__ uint32_t s_ck[kSelCand];
+  __shared__ int32_t s_ct[kSelCand];
+  __shared__ int scratch[kSelNT / kWave + 1];
+  __shared__ int s_d, s_nc;
+  __shared__ uint32_t s_before;
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x;
+  const int n = row_visible(ctx_len, P, r);
+  int32_t* out = topk + (size_t)r * K;
+  if (n <= K) {
+    for (int k = tid; k < K; k += kSelNT) out[k] = k < n ? k : -1;
+    return;
+  }
+  const float* row = scores + (size_t)r * T_stride;
+  // the first round's 16-byte loads go out before the histogram scan; every
+  // round then issues the next round's loads before working on its own
+  constexpr int kStep = kSelNT * 4 * kSelU;            // tokens per round
+  float4 v[kSelU];
+#pragma unroll
+  for (int u = 0; u < kSelU; ++u) {
+    const int t = (u * kSelNT + tid) * 4;
+    if (t < n) v[u] = *reinterpret_cast<const float4*>(row + t);
+  }
+  for (int i = tid; i < kBins1; i += kSelNT) h[i] = ws.hist[(size_t)r * kBins1 + i];
+  const int nwords = (n + 31) >> 5;
+  for (int i = tid; i < nwords; i += kSelNT) bm[i] = 0u;
+  if (tid == 0) s_nc = 0;
+  __syncthreads();
+  find_bin<kSelNT>(h, kBins1, (uint32_t)K, true, scratch, &s_d, &s_before);
+  const uint32_t b1 = (uint32_t)s_d;
+  const uint32_t above = s_before;
+  // the histogram gives the candidate count up front: LDS when they fit
+  const bool in_lds = h[b1] <= (uint32_t)kSelCand;
+  const int cap = in_lds ? kSelCand : T_stride;
+  uint32_t* ck = in_lds ? s_ck : ws.ckey + (size_t)r * T_stride;
+  int32_t* ct = in_lds ? s_ct : ws.ctok + (size_t)r * T_stride;
+  const int lane = lane_id();
+  for (int base = 0; base < n; base += kStep) {
+    float4 nx[kSelU];
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) {
+      const int t = base + kStep + (u * kSelNT + tid) * 4;
+      if (t < n) nx[u] = *reinterpret_cast<const float4*>(row + t);
+    }
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) {
+      const int t0 = base + (u * kSelNT + tid) * 4;
+      const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + e;
+        const uint32_t key = score_key(f[e]);
+        const uint32_t bin = key >> 21;
+        const bool ok = t < n;
+        if (ok && bin > b1) atomicOr(&bm[t >> 5], 1u << (t & 31));
+        const bool cand = ok && bin == b1;
+        const uint64_t m = __ballot(cand);
+        if (m) {
+          const int leader = __ffsll((long long)m) - 1;
+          int basepos = 0;
+          if (lane == leader) basepos = atomicAdd(&s_nc, __popcll(m));
+          basepos = __shfl(basepos, leader);
+          const int at = basepos + lanes_below(m);
+          if (cand && at < cap) {
+            ck[at] = key;
+            ct[at] = t;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) v[u] = nx[u];
+  }
+  __syncthreads();
+  const int nc = min(s_nc, cap);
+  uint32_t tau;
+  int t_cut;
+  candidates_threshold<kSelNT>(ck, ct, nc, b1, (uint32_t)K - above, h, scratch, &s_d, &s_before,
+                               &tau, &t_cut);
+  for (int i = tid; i < nc; i += kSelNT) {
+    const uint32_t key = ck[i];
+    const int t = ct[i];
+    if (key > tau || (key == tau && t <= t_cut)) atomicOr(&bm[t >> 5], 1u << (t & 31));
+  }
+  __syncthreads();
+  emit_bitmap<kSelNT, kSelWords / kSelNT>(bm, nwords, 0, 0, out, scratch);
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int B, int P, int T_stride, int K) {
@@ -358,6 +488,11 @@ hipError_t launch_topk_select(const BatchDims& d, int K, const float* scores, in
                               void* ws, hipStream_t s) {
   const int R = d.B * d.P;
   TopkWs w = topk_ws(ws, R, d.T_stride, K);
+  if (d.T_stride <= kSelMaxN) {
+    hipLaunchKernelGGL(topk_select_row_kernel, dim3(R), dim3(kSelNT), 0, s, d.ctx_len, d.P,
+                       d.T_stride, K, scores, w, topk);
+    return hipGetLastError();
+  }
   const int nchunk = (d.T_stride + kChunk - 1) / kChunk;
   hipLaunchKernelGGL(topk_filter_kernel, dim3(nchunk, R), dim3(kScanNT), 0, s, d.ctx_len, d.P,
                      d.T_stride, K, scores, w);

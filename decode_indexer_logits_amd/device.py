@@ -139,6 +139,13 @@ class DeviceStep:
         _lib.resolve_rows(self.batch, self.wl.K, self.topk, self.res, self.row_ids, self.faults,
                           self.counts, stream)
 
+    def run_resolve_tables(self, stream=None):
+        _lib.resolve_tables(self.batch, self.wl.K, self.topk, self.res, self.row_ids, self.faults,
+                            self.counts, stream)
+
+    def run_copy_faults(self, stream=None):
+        _lib.copy_faults(self.batch, self.wl.K, self.res, self.faults, self.counts, stream)
+
     def run_attention(self, layer: int, stream=None):
         wl = self.wl
         _lib.sparse_mla_decode(self.batch, wl.K, wl.Hq, wl.q_dtype, self.q[layer], wl.kv_dtype,

@@ -77,6 +77,29 @@ def check_topk_vs_oracle_scores(wl, S_oracle, topk):
     return n_swaps
 
 
+def check_topk_vs_oracle_scores_rows(wl, q_idx, topk, requests):
+    """check_topk_vs_oracle_scores for the listed requests only, with the
+    oracle's scores computed for those requests alone (full-size workloads)."""
+    n_swaps = 0
+    for b in requests:
+        sl = [b]
+        S = o_idx.indexer_scores(q_idx[sl], wl.q_dtype, wl.w[sl], wl.idx_pool, wl.k_dtype,
+                                 wl.idx_scale, wl.idx_bt[sl], wl.ctx_len[sl],
+                                 None if wl.bias is None else wl.bias[sl], T_stride=wl.T_stride)
+        for p in range(wl.P):
+            n = max(o_idx.visible_limit(int(wl.ctx_len[b]), wl.P, p) + 1, 0)
+            G = topk[b, p][topk[b, p] >= 0]
+            O = o_topk.topk_row(S[0, p], n, wl.K)
+            O = O[O >= 0]
+            assert len(G) == len(O) == min(n, wl.K)
+            diff = np.setxor1d(G, O)
+            if len(diff):
+                sk = o_topk.kth_score(S[0, p], n, wl.K)
+                assert np.all(np.abs(S[0, p, diff] - sk) <= TOPK_TIE_REL * abs(sk)), (b, p)
+                n_swaps += len(diff)
+    return n_swaps
+
+
 def check_resolve(wl, ostate, topk, got: dict):
     """Bit-exact: rows, counts, fault lists, tables, step and error bits."""
     new, rr = o_res.resolve(topk, ostate)

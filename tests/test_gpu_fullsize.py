@@ -1,0 +1,154 @@
+"""GPU parity at the workloads' full sizes, through the C ABI.
+
+Mixed residency at 128K (B=32, T=131072, K=2048) runs as one captured HIP
+graph, the launch configuration the benchmark times; the MTP3 mix (B=64, P=4,
+4 steps) and the 1M-token no-residency start (B=4, T=2^20, L=4, 16 steps) run
+eagerly, step after step from their initial state.
+
+What is checked at these sizes:
+  scores     a random sample of tokens per (request, position), plus the first
+             and last visible token, recomputed one by one by the oracle;
+  top-K      bit-exact against the oracle's top-K of the GPU scores for every
+             row, and against the oracle's own scores (near-tie swaps only)
+             for the first and last request at 128K, the first request at
+             the first step of the multi-step runs;
+  resolve    every table, row id, fault list, count, step and error word
+             bit-exact for every request; the bytes and scale of every
+             faulted row in every layer;
+  attention  every output vector against the oracle over the same selection.
+"""
+import gc as _gc
+import sys
+
+import numpy as np
+import pytest
+
+from workloads import gen
+import gpu_check as gc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_indexer_logits_amd import _lib
+    _lib.load()
+    yield
+    _gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _check_step(ds, wl, ost, s, rng, score_sample, oracle_topk_requests, attn_tol=2e-2):
+    q_idx, q = wl.step_inputs(s)
+    g = gc.gpu_outputs(ds)
+    worst_s, _ = gc.check_scores(wl, q_idx, g["scores"], sample=score_sample, rng=rng)
+    gc.check_topk_exact(wl, g["scores"], g["topk"])
+    swaps = gc.check_topk_vs_oracle_scores_rows(wl, q_idx, g["topk"], oracle_topk_requests)
+    new, rr = gc.check_resolve(wl, ost, g["topk"], g)
+    if wl.C:
+        pool = ds.pool.cpu().numpy()
+        rsc = None if ds.row_scale is None else ds.row_scale.cpu().numpy()
+        gc.check_copies(wl, rr, pool, rsc)
+        del pool
+    worst_a = gc.check_attention(wl, q, g["topk"], g["out"], g["lse"], attn_tol)
+    return new, rr, {"score_err": worst_s, "attn_err": worst_a, "topk_swaps": swaps,
+                     "counts_mean": g["counts"].mean(axis=0).round(1).tolist(),
+                     "err": g["err"]}
+
+
+@pytest.mark.timeout(600)
+def test_mixed_128k_full_size_graph():
+    _say("mixed_128k full size (B=32, T=131072, K=2048), captured graph")
+    from decode_indexer_logits_amd.device import DeviceStep
+    wl = gen.mixed_128k()
+    ds = DeviceStep(wl)
+    snap = ds.snapshot()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ds.run()                          # warm every kernel before capture
+    torch.cuda.synchronize()
+    ds.restore(snap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            ds.run()
+    torch.cuda.synchronize()
+    ds.restore(snap)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    _say("replayed; checking against the oracle")
+    rng = np.random.default_rng(11)
+    _, _, info = _check_step(ds, wl, gc.oracle_state(wl), 1, rng, score_sample=2048,
+                             oracle_topk_requests=[0, wl.B - 1])
+    _say(info)
+    c = ds.counts.cpu().numpy()
+    assert info["err"] == 0
+    assert np.all(c[:, 1] >= 900)                     # pre-seeded: about half of the top-K hits
+    assert np.all(c[:, 2] > 0) and np.all(c[:, 3] == c[:, 2])
+    assert np.all(c[:, 0] + c[:, 1] + c[:, 2] == wl.K)
+    del ds, g
+    _gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_mtp3_agentic_full_size_four_steps():
+    _say("mtp3_agentic full size (B=64, P=4, K=2048, C=10240), 4 steps")
+    from decode_indexer_logits_amd.device import DeviceStep
+    wl = gen.mtp3_agentic()
+    ds = DeviceStep(wl)
+    ost = gc.oracle_state(wl)
+    rng = np.random.default_rng(12)
+    for s in range(1, wl.steps + 1):
+        ds.set_queries(s)
+        ds.run()
+        ost, rr, info = _check_step(ds, wl, ost, s, rng, score_sample=512,
+                                    oracle_topk_requests=[0] if s == 1 else [])
+        _say(f"step {s}", info)
+        assert info["err"] == 0
+        if s == 1:
+            assert info["counts_mean"][1] == 0.0        # hot buffers start empty
+    del ds
+    _gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_norescache_1m_full_size_sixteen_steps():
+    _say("norescache_1m full size (B=4, T=2^20, L=4, K=2048), 16 steps")
+    from decode_indexer_logits_amd.device import DeviceStep
+    wl = gen.norescache_1m()
+    _say("generated")
+    ds = DeviceStep(wl)
+    ost = gc.oracle_state(wl)
+    rng = np.random.default_rng(13)
+    rates = []
+    for s in range(1, wl.steps + 1):
+        ds.set_queries(s)
+        ds.run()
+        ost, rr, info = _check_step(ds, wl, ost, s, rng, score_sample=2048,
+                                    oracle_topk_requests=[0] if s == 1 else [])
+        c = rr.counts
+        rate = float(c[:, 1].sum() / max(c[:, 1].sum() + c[:, 2].sum(), 1))
+        rates.append(round(rate, 4))
+        _say(f"step {s} hit rate {rate:.4f}", info)
+        assert info["err"] == 0
+        if s == 1:
+            assert np.all(c[:, 1] == 0) and np.all(c[:, 2] == wl.K) and np.all(c[:, 3] == 0)
+    _say("hit rates", rates)
+    assert rates[0] == 0.0 and min(rates[1:]) > 0.0
+    del ds
+    _gc.collect()
+    torch.cuda.empty_cache()

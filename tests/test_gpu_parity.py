@@ -210,6 +210,7 @@ def test_pipelined_step_matches_single_stream():
     snap = ds.snapshot()
     ds.run()
     ref = gc.gpu_outputs(ds)
+    ref_pool = ds.pool.cpu().numpy()
     gc.check_resolve(wl, gc.oracle_state(wl), ref["topk"], ref)
     keys = ("scores", "topk", "row_ids", "counts", "out", "lse", "tok2slot", "slot2tok", "stamp")
     for nchunks in (2, 3, 5):
@@ -224,7 +225,7 @@ def test_pipelined_step_matches_single_stream():
             else:
                 assert np.array_equal(got[k], ref[k]), (nchunks, k)
         assert got["step"] == ref["step"]
-        assert np.array_equal(ds.pool.cpu().numpy(), ds.pool.cpu().numpy())
+        assert np.array_equal(ds.pool.cpu().numpy(), ref_pool), nchunks
     # captured as one graph, replayed
     ds.restore(snap)
     ds.run_pipelined(3)
@@ -325,3 +326,49 @@ def test_fused_indexer_topk_matches_separate_calls(name):
             assert torch.equal(ds.scores[b, p, :n], s1[b, p, :n])
     assert torch.equal(ds.topk, t1)
     gc.check_topk_exact(wl, ds.scores.cpu().numpy(), ds.topk.cpu().numpy())
+
+
+def _planted_scores(case, rng, B, P, T_stride):
+    shape = (B, P, T_stride)
+    if case == "quarter_steps":          # few distinct values: heavy ties at the threshold
+        return (np.round(rng.standard_normal(shape) * 4) / 4).astype(np.float32)
+    if case == "signed_zeros":           # most scores are +0 or -0, which are equal
+        s = np.where(rng.random(shape) < 0.5, np.float32(0.0), np.float32(-0.0))
+        pos = rng.random(shape) < 0.01
+        s[pos] = rng.random(int(pos.sum())).astype(np.float32)
+        neg = rng.random(shape) < 0.2
+        s[neg] = -rng.random(int(neg.sum())).astype(np.float32)
+        return s.astype(np.float32)
+    if case == "all_equal":              # every visible token ties
+        return np.ones(shape, dtype=np.float32)
+    if case == "distinct":
+        return rng.standard_normal(shape).astype(np.float32)
+    raise ValueError(case)
+
+
+@pytest.mark.parametrize("case", ["quarter_steps", "signed_zeros", "all_equal", "distinct"])
+@pytest.mark.parametrize("T_stride", [65536, (1 << 18) + 64])
+def test_topk_planted_ties_against_oracle(case, T_stride):
+    """hs_topk alone on planted score rows, bit-exact against the oracle's
+    (score desc, token asc) selection: rows up to 2^18 tokens take the
+    one-workgroup select, longer rows the multi-workgroup filter; the
+    all-equal case has more candidates than the LDS list holds."""
+    _say(f"topk planted {case} T_stride={T_stride}")
+    from decode_indexer_logits_amd import _lib
+    from oracle import topk as o_topk
+    seed = ["quarter_steps", "signed_zeros", "all_equal", "distinct"].index(case)
+    rng = np.random.default_rng(100 + 2 * seed + (T_stride > 65536))
+    B, P, K = 3, 2, 2048
+    ctx = np.array([T_stride, T_stride // 2 + 37, 2500], dtype=np.int32)
+    S = _planted_scores(case, rng, B, P, T_stride)
+    d_ctx = torch.from_numpy(ctx).cuda()
+    d_s = torch.from_numpy(S).cuda()
+    out = torch.empty((B, P, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, P, T_stride, K), dtype=torch.uint8,
+                     device="cuda")
+    batch = _lib.make_batch(B, P, T_stride, d_ctx)
+    _lib.topk(batch, K, d_s, out, ws)
+    got = out.cpu().numpy()
+    ref = o_topk.topk(S.astype(np.float64), ctx, K)
+    bad = np.argwhere(np.any(ref != got, axis=2))
+    assert len(bad) == 0, f"rows {bad[:4].tolist()}"
