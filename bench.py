@@ -32,6 +32,28 @@ HBM_PEAK_GBS = 8000.0
 HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 KV_ROW = 576
 
+# HBM bytes per launch of hs_indexer_scores on the 128K mixed workload, from two
+# rocprofv3 --pmc runs (FETCH_SIZE x 2 + WRITE_SIZE x 1, factors calibrated with a
+# 512 MiB read and a 512 MiB fill in the same runs; profiles/indexer_mixed_128k_pmc.txt).
+# Reported only while the kernel's sources are the ones the counters were taken on.
+INDEXER_TRAFFIC = {"workload": "mixed_128k", "bytes": 579.95e6,
+                   "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
+                               "decode_indexer_logits_amd/csrc/hs_common.h"),
+                   "sha256": "096c9be35c6aa0da9b4c461080d3c5c0a2aafa9ec4941fc79daa7f12dae9e556"}
+
+
+def _indexer_traffic(workload: str):
+    """Counter-measured HBM bytes per indexer launch, or None if the sources changed
+    since the counters were taken or the workload differs."""
+    import hashlib
+    if workload != INDEXER_TRAFFIC["workload"]:
+        return None
+    h = hashlib.sha256()
+    for f in INDEXER_TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return INDEXER_TRAFFIC["bytes"] if h.hexdigest() == INDEXER_TRAFFIC["sha256"] else None
+
 
 def _algorithmic_bytes(wl, counts):
     """Bytes the method itself must move per step, by stage."""
@@ -240,6 +262,7 @@ def main():
     hbm_phase_s = (stage_ms["indexer_topk"] + stage_ms["resolve_tables"]
                    + stage_ms["attention"]) / 1e3
     link_gbs = alg["host_link"] / (stage_ms["fault_copy"] / 1e3) / 1e9
+    traffic = _indexer_traffic(wl.name)
     p10, p90 = ms_sorted[len(ms) // 10], ms_sorted[min(len(ms) - 1, (len(ms) * 9) // 10)]
     result = {
         "metric": "sparse-MLA decode steps/s + achieved HBM GB/s, 128K ctx, K=2048, 1 GPU",
@@ -264,7 +287,8 @@ def main():
                    "graph": not a.no_graph, "pipeline_chunks": a.chunks},
         "roofline": {"bound": "hbm", "kernel": "indexer_bf16_e4m3",
                      "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE)",
                      "algorithmic_bytes": idx_bytes, "avg_ms": round(stage_ms["indexer"], 4)},
         "step_bandwidth": {
             "whole_step_GBs": round(hbm_phase_bytes / step_s / 1e9, 1),

@@ -157,6 +157,7 @@ hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t
   hs::BatchDims d;
   if (hs_status st = check_batch(batch, &d)) return st;
   if (!scores) return fail(HS_ERR_NULL, "hs_topk: scores is required");
+  if (!aligned16(scores)) return fail(HS_ERR_ALIGN, "hs_topk: scores need 16-byte alignment");
   if (hs_status st = check_topk(d, K, topk, ws, ws_bytes)) return st;
   return launched(hs::launch_topk(d, K, scores, topk, ws, static_cast<hipStream_t>(stream)), "topk");
 }

@@ -4,28 +4,27 @@
 // "Comment s'y prendre").
 //
 // Scores map to order-preserving uint32 keys.  A row (one request position,
-// up to 2^24 tokens) is spread over many workgroups so that a handful of very
-// long rows still fills the chip:
+// up to 2^24 tokens) is spread over many workgroups so that both few long rows
+// and many short ones fill the chip:
 //   1. zero       per-row histogram and counters
 //   2. histogram  of the top 11 key bits, per 8192-token chunk: LDS counts,
 //                 then one global atomic per non-empty bin (the fused path of
 //                 hs_indexer_topk builds it in the indexer's epilogue instead)
-//   3. filter     every chunk re-derives the bin b1 holding the K-th largest
-//                 key; keys above b1 are selected outright, keys in b1 become
-//                 candidates (one global append per workgroup)
-//   4. finalize   one workgroup per row goes on with the radix select over
-//                 the candidates (11 + 10 more bits), sends ties at the
-//                 threshold to the lower token (radix select on the token
-//                 index), and writes the K tokens in ascending order through
-//                 an LDS bitmap per 64K-token segment.
+//   3. filter     one wave of every 4096-token workgroup finds the bin b1
+//                 holding the K-th largest key from the row's histogram; keys
+//                 above b1 are selected outright, keys in b1 become candidates;
+//                 the workgroup reserves its output ranges with one pair of
+//                 global atomics
+//   4. finalize   one workgroup per row stages the candidates in LDS, goes on
+//                 with the radix select over them (key bits 20..10, then 9..0),
+//                 sends ties at the threshold to the lower token (radix select
+//                 on the token index), and writes the K tokens in ascending
+//                 order through an LDS bitmap per 64K-token segment.
 // Passes 3 and 4 stay separate kernels: handing a row from many workgroups to
 // one inside a kernel needs a device-scope release per workgroup, which on a
 // multi-die GPU writes back L2 and costs far more than a kernel boundary.
-// Rows of at most 2^18 tokens skip that hand-off: one 1024-thread workgroup per
-// row streams the row once (keys above the threshold bin go straight into an
-// LDS bitmap, keys in it into an LDS candidate list), finishes the radix select
-// and emits from the bitmap -- one kernel after the histogram instead of two,
-// and no candidate round trip through HBM.
+// A row is not finished by one workgroup from the start either: at 2^17 tokens
+// per row the per-token work alone keeps one CU busy for tens of microseconds.
 // The selection is exact: the same tokens as a full sort by (score desc,
 // token asc), written in ascending token order, -1 padded for short rows.
 #include "hs_common.h"
@@ -35,23 +34,20 @@ namespace hs {
 namespace {
 
 constexpr int kBins1 = 2048;   // top 11 key bits
-constexpr int kChunk = 8192;   // tokens per workgroup in passes 2 and 3
+constexpr int kChunk = 8192;   // tokens per workgroup of the histogram pass
+constexpr int kFChunk = 4096;  // tokens per workgroup of the filter pass
 constexpr int kScanNT = 256;
+constexpr int kFPer = kFChunk / kScanNT / 4;   // 16-byte loads per filter thread
 constexpr int kMaxK = 8192;
 constexpr int kCnt = 8;                   // counters per row
 constexpr int kFinNT = 1024;
 constexpr int kSegTok = 1 << 16;          // tokens per bitmap segment in finalize
 constexpr int kSegWords = kSegTok / 32;
-constexpr int kSelNT = 1024;
-constexpr int kSelMaxN = 1 << 18;         // longest row of the one-workgroup select
-constexpr int kSelWords = kSelMaxN / 32;
-constexpr int kSelCand = 12288;           // candidates held in LDS (else in the workspace)
-constexpr int kSelU = 8;                  // 16-byte score loads per thread per round
+constexpr int kFinCand = 12288;           // candidates staged in LDS by finalize
 
 struct TopkWs {
   uint32_t* hist;   // [R][2048]
-  uint32_t* cnt;    // [R][8]: selected-above count, candidate count, b1, count above b1,
-                    //         finished-chunk ticket
+  uint32_t* cnt;    // [R][8]: selected-above count, candidate count, b1, count above b1
   int32_t* sel;     // [R][K]
   uint32_t* ckey;   // [R][T_stride]
   int32_t* ctok;    // [R][T_stride]
@@ -111,6 +107,48 @@ __device__ void find_bin(const uint32_t* h, int nbins, uint32_t k, bool from_top
     }
   }
   __syncthreads();
+}
+
+// The same search from the top over a row's 2048-bin histogram in global
+// memory, by one wave: lane l reads bins 32l .. 32l+31 (eight 16-byte loads),
+// a suffix sum over the lanes places each lane's range, and the lane holding
+// the k-th largest key walks its bins.  Only the finding lane writes.
+__device__ void wave_find_bin_top(const uint32_t* __restrict__ hrow, uint32_t k, int* d_out,
+                                  uint32_t* before_out) {
+  const int lane = lane_id();
+  uint4 q[8];
+  const uint4* src = reinterpret_cast<const uint4*>(hrow) + lane * 8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) q[j] = src[j];
+  uint32_t c[32];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    c[4 * j] = q[j].x;
+    c[4 * j + 1] = q[j].y;
+    c[4 * j + 2] = q[j].z;
+    c[4 * j + 3] = q[j].w;
+  }
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) local += c[j];
+  // sum over the lanes above this one (higher bins come first)
+  uint32_t incl = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t y = __shfl_down(incl, o);
+    if (lane + o < kWave) incl += y;
+  }
+  uint32_t before = incl - local;
+  if (before < k && before + local >= k) {
+#pragma unroll
+    for (int j = 31; j >= 0; --j) {
+      if (before < k && before + c[j] >= k) {
+        *d_out = lane * 32 + j;
+        *before_out = before;
+      }
+      before += c[j];
+    }
+  }
 }
 
 __global__ __launch_bounds__(kScanNT) void topk_zero_kernel(TopkWs ws) {
@@ -232,32 +270,146 @@ __device__ int emit_bitmap(const uint32_t* bm, int nwords, int t_base, int writt
   return tot;
 }
 
-// Finishes row r (n > K visible tokens) from the outright selections and the
-// candidates written by every chunk of the row.
-template <int NT>
-__device__ void finalize_row(int r, int n, int T_stride, int K, const TopkWs& ws,
-                             int32_t* __restrict__ out, uint32_t* h, int32_t* outl, uint32_t* bm,
-                             int* scratch, int* s_d, uint32_t* s_before, int* s_pos) {
+__global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __restrict__ ctx_len,
+                                                              int P, int T_stride, int K,
+                                                              const float* __restrict__ scores,
+                                                              TopkWs ws) {
+  __shared__ int s_b1;
+  __shared__ uint32_t s_above;
+  __shared__ int s_wsum[kScanNT / kWave];
+  __shared__ uint32_t s_base_sel, s_base_cand;
+  const int r = blockIdx.y;
+  const int n = row_visible(ctx_len, P, r);
+  const int base = blockIdx.x * kFChunk;
+  if (n <= K || base >= n) return;
   const int tid = threadIdx.x;
+  const int lane = lane_id(), wid = tid / kWave;
+  const float* row = scores + (size_t)r * T_stride;
+  // 16 consecutive-in-lane-order tokens per thread, as four 16-byte loads
+  // (rows are 256-byte aligned and padded to a multiple of 64 tokens)
+  float4 v[kFPer];
+#pragma unroll
+  for (int u = 0; u < kFPer; ++u) {
+    const int t = base + (u * kScanNT + tid) * 4;
+    if (t < n) v[u] = *reinterpret_cast<const float4*>(row + t);
+  }
+  if (wid == 0) wave_find_bin_top(ws.hist + (size_t)r * kBins1, (uint32_t)K, &s_b1, &s_above);
+  __syncthreads();
+  const uint32_t b1 = (uint32_t)s_b1;
+  if (blockIdx.x == 0 && tid == 0) {
+    ws.cnt[r * kCnt + 2] = b1;
+    ws.cnt[r * kCnt + 3] = s_above;
+  }
+  uint32_t key[kFPer * 4];
+  int packed = 0;            // selections (low 16 bits), candidates (high 16 bits)
+#pragma unroll
+  for (int u = 0; u < kFPer; ++u) {
+    const int t0 = base + (u * kScanNT + tid) * 4;
+    const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t k = t0 + e < n ? score_key(f[e]) : 0u;   // key 0: never kept
+      key[u * 4 + e] = k;
+      const uint32_t bin = k >> 21;
+      packed += (t0 + e < n) ? ((bin > b1) ? 1 : ((bin == b1) ? 0x10000 : 0)) : 0;
+    }
+  }
+  // block exclusive prefix of the packed counts: wave scan, then wave sums
+  int incl = packed;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) s_wsum[wid] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int total = 0;
+    for (int w = 0; w < kScanNT / kWave; ++w) {
+      const int x = s_wsum[w];
+      s_wsum[w] = total;
+      total += x;
+    }
+    s_base_sel = (total & 0xFFFF) ? atomicAdd(&ws.cnt[r * kCnt + 0], (uint32_t)(total & 0xFFFF)) : 0u;
+    s_base_cand = (total >> 16) ? atomicAdd(&ws.cnt[r * kCnt + 1], (uint32_t)(total >> 16)) : 0u;
+  }
+  __syncthreads();
+  if (!packed) return;
+  const int ex = s_wsum[wid] + incl - packed;
+  uint32_t ps = s_base_sel + (uint32_t)(ex & 0xFFFF);
+  uint32_t pc = s_base_cand + (uint32_t)(ex >> 16);
+  int32_t* sel = ws.sel + (size_t)r * K;
+  uint32_t* ck = ws.ckey + (size_t)r * T_stride;
+  int32_t* ct = ws.ctok + (size_t)r * T_stride;
+#pragma unroll
+  for (int u = 0; u < kFPer; ++u) {
+    const int t0 = base + (u * kScanNT + tid) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = t0 + e;
+      if (t >= n) continue;
+      const uint32_t k = key[u * 4 + e];
+      const uint32_t bin = k >> 21;
+      if (bin > b1) {
+        sel[ps++] = t;
+      } else if (bin == b1) {
+        ck[pc] = k;
+        ct[pc] = t;
+        ++pc;
+      }
+    }
+  }
+}
+
+// Finishes row r (n > K visible tokens) from the outright selections and the
+// candidates written by every filter workgroup of the row.
+__global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __restrict__ ctx_len,
+                                                               int P, int T_stride, int K,
+                                                               TopkWs ws, int32_t* __restrict__ topk) {
+  __shared__ uint32_t h[kBins1];
+  __shared__ int32_t outl[kMaxK];
+  __shared__ uint32_t bm[kSegWords];
+  __shared__ uint32_t s_ck[kFinCand];
+  __shared__ int32_t s_ct[kFinCand];
+  __shared__ int scratch[kFinNT / kWave + 1];
+  __shared__ int s_d, s_pos;
+  __shared__ uint32_t s_before;
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x;
+  const int n = row_visible(ctx_len, P, r);
+  int32_t* out = topk + (size_t)r * K;
+  if (n <= K) {
+    for (int k = tid; k < K; k += kFinNT) out[k] = k < n ? k : -1;
+    return;
+  }
   const uint32_t b1 = ws.cnt[r * kCnt + 2];
   const uint32_t above = ws.cnt[r * kCnt + 3];
   const int nc = (int)ws.cnt[r * kCnt + 1];
-  const uint32_t* ck = ws.ckey + (size_t)r * T_stride;
-  const int32_t* ct = ws.ctok + (size_t)r * T_stride;
+  const uint32_t* gk = ws.ckey + (size_t)r * T_stride;
+  const int32_t* gt = ws.ctok + (size_t)r * T_stride;
+  // the outright selections and (when they fit) the candidates go to LDS
+  // with one pass of independent loads
+  const int32_t* sel = ws.sel + (size_t)r * K;
+  for (int i = tid; i < (int)above; i += kFinNT) outl[i] = sel[i];
+  const bool in_lds = nc <= kFinCand;
+  if (in_lds)
+    for (int i = tid; i < nc; i += kFinNT) {
+      s_ck[i] = gk[i];
+      s_ct[i] = gt[i];
+    }
+  if (tid == 0) s_pos = (int)above;
+  __syncthreads();
+  const uint32_t* ck = in_lds ? s_ck : gk;
+  const int32_t* ct = in_lds ? s_ct : gt;
   uint32_t tau;
   int t_cut;
-  candidates_threshold<NT>(ck, ct, nc, b1, (uint32_t)K - above, h, scratch, s_d, s_before, &tau,
-                           &t_cut);
-  // collect: the tokens selected outright, then the chosen candidates
-  const int32_t* sel = ws.sel + (size_t)r * K;
-  for (int i = tid; i < (int)above; i += NT) outl[i] = sel[i];
-  if (tid == 0) *s_pos = (int)above;
-  __syncthreads();
-  for (int i = tid; i < nc; i += NT) {
+  candidates_threshold<kFinNT>(ck, ct, nc, b1, (uint32_t)K - above, h, scratch, &s_d, &s_before,
+                               &tau, &t_cut);
+  for (int i = tid; i < nc; i += kFinNT) {
     const uint32_t key = ck[i];
     const int t = ct[i];
     if (key > tau || (key == tau && t <= t_cut)) {
-      const int at = atomicAdd(s_pos, 1);
+      const int at = atomicAdd(&s_pos, 1);
       if (at < kMaxK) outl[at] = t;
     }
   }
@@ -267,194 +419,16 @@ __device__ void finalize_row(int r, int n, int T_stride, int K, const TopkWs& ws
   int written = 0;
   const int nseg = (n + kSegTok - 1) / kSegTok;
   for (int sg = 0; sg < nseg; ++sg) {
-    for (int i = tid; i < kSegWords; i += NT) bm[i] = 0u;
+    for (int i = tid; i < kSegWords; i += kFinNT) bm[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < K; i += NT) {
+    for (int i = tid; i < K; i += kFinNT) {
       const int t = outl[i];
       if (t / kSegTok == sg) atomicOr(&bm[(t % kSegTok) >> 5], 1u << (t & 31));
     }
     __syncthreads();
-    written += emit_bitmap<NT, kSegWords / NT>(bm, kSegWords, sg * kSegTok, written, out, scratch);
+    written += emit_bitmap<kFinNT, kSegWords / kFinNT>(bm, kSegWords, sg * kSegTok, written, out,
+                                                       scratch);
   }
-}
-
-__global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __restrict__ ctx_len,
-                                                              int P, int T_stride, int K,
-                                                              const float* __restrict__ scores,
-                                                              TopkWs ws) {
-  constexpr int kPer = kChunk / kScanNT;   // keys per thread, kept in registers
-  __shared__ uint32_t h[kBins1];
-  __shared__ int scratch[kScanNT / kWave + 1];
-  __shared__ int s_b1;
-  __shared__ uint32_t s_above;
-  __shared__ uint32_t s_base_sel, s_base_cand;
-  const int r = blockIdx.y;
-  const int n = row_visible(ctx_len, P, r);
-  const int base = blockIdx.x * kChunk;
-  if (n <= K || base >= n) return;
-  const float* row = scores + (size_t)r * T_stride;
-  const int end = min(base + kChunk, n);
-  uint32_t key[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int t = base + i * kScanNT + threadIdx.x;
-    key[i] = t < end ? score_key(row[t]) : 0u;
-  }
-  for (int i = threadIdx.x; i < kBins1; i += kScanNT) h[i] = ws.hist[(size_t)r * kBins1 + i];
-  __syncthreads();
-  find_bin<kScanNT>(h, kBins1, (uint32_t)K, true, scratch, &s_b1, &s_above);
-  const uint32_t b1 = (uint32_t)s_b1;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    ws.cnt[r * kCnt + 2] = b1;
-    ws.cnt[r * kCnt + 3] = s_above;
-  }
-  // count this thread's selections (low 16 bits) and candidates (high 16 bits)
-  int packed = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int t = base + i * kScanNT + threadIdx.x;
-    const uint32_t bin = key[i] >> 21;
-    if (t < end) packed += (bin > b1) ? 1 : ((bin == b1) ? 0x10000 : 0);
-  }
-  int total;
-  const int ex = block_exclusive_scan<kScanNT>(packed, scratch, &total);
-  if (threadIdx.x == 0) {
-    s_base_sel = (total & 0xFFFF) ? atomicAdd(&ws.cnt[r * kCnt + 0], (uint32_t)(total & 0xFFFF)) : 0u;
-    s_base_cand = (total >> 16) ? atomicAdd(&ws.cnt[r * kCnt + 1], (uint32_t)(total >> 16)) : 0u;
-  }
-  __syncthreads();
-  uint32_t ps = s_base_sel + (uint32_t)(ex & 0xFFFF);
-  uint32_t pc = s_base_cand + (uint32_t)(ex >> 16);
-  int32_t* sel = ws.sel + (size_t)r * K;
-  uint32_t* ck = ws.ckey + (size_t)r * T_stride;
-  int32_t* ct = ws.ctok + (size_t)r * T_stride;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int t = base + i * kScanNT + threadIdx.x;
-    if (t >= end) continue;
-    const uint32_t bin = key[i] >> 21;
-    if (bin > b1) {
-      sel[ps++] = t;
-    } else if (bin == b1) {
-      ck[pc] = key[i];
-      ct[pc] = t;
-      ++pc;
-    }
-  }
-}
-
-__global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __restrict__ ctx_len,
-                                                               int P, int T_stride, int K,
-                                                               TopkWs ws, int32_t* __restrict__ topk) {
-  __shared__ uint32_t h[kBins1];
-  __shared__ int32_t outl[kMaxK];
-  __shared__ uint32_t bm[kSegWords];
-  __shared__ int scratch[kFinNT / kWave + 1];
-  __shared__ int s_d, s_pos;
-  __shared__ uint32_t s_before;
-  const int r = blockIdx.x;
-  const int n = row_visible(ctx_len, P, r);
-  int32_t* out = topk + (size_t)r * K;
-  if (n <= K) {
-    for (int k = threadIdx.x; k < K; k += kFinNT) out[k] = k < n ? k : -1;
-    return;
-  }
-  finalize_row<kFinNT>(r, n, T_stride, K, ws, out, h, outl, bm, scratch, &s_d, &s_before, &s_pos);
-}
-
-// Filter and finalize of one row (n <= 2^18 visible tokens) in one workgroup,
-// from the row's complete 11-bit histogram.
-__global__ __launch_bounds__(kSelNT) void topk_select_row_kernel(
-    const int32_t* __restrict__ ctx_len, int P, int T_stride, int K,
-    const float* __restrict__ scores, TopkWs ws, int32_t* __restrict__ topk) {
-  __shared__ uint32_t h[kBins1];
-  __shared__ uint32_t bm[kSelWords];
-  __shared__ uint32_t s_ck[kSelCand];
-  __shared__ int32_t s_ct[kSelCand];
-  __shared__ int scratch[kSelNT / kWave + 1];
-  __shared__ int s_d, s_nc;
-  __shared__ uint32_t s_before;
-  const int tid = threadIdx.x;
-  const int r = blockIdx.x;
-  const int n = row_visible(ctx_len, P, r);
-  int32_t* out = topk + (size_t)r * K;
-  if (n <= K) {
-    for (int k = tid; k < K; k += kSelNT) out[k] = k < n ? k : -1;
-    return;
-  }
-  const float* row = scores + (size_t)r * T_stride;
-  // the first round's 16-byte loads go out before the histogram scan; every
-  // round then issues the next round's loads before working on its own
-  constexpr int kStep = kSelNT * 4 * kSelU;            // tokens per round
-  float4 v[kSelU];
-#pragma unroll
-  for (int u = 0; u < kSelU; ++u) {
-    const int t = (u * kSelNT + tid) * 4;
-    if (t < n) v[u] = *reinterpret_cast<const float4*>(row + t);
-  }
-  for (int i = tid; i < kBins1; i += kSelNT) h[i] = ws.hist[(size_t)r * kBins1 + i];
-  const int nwords = (n + 31) >> 5;
-  for (int i = tid; i < nwords; i += kSelNT) bm[i] = 0u;
-  if (tid == 0) s_nc = 0;
-  __syncthreads();
-  find_bin<kSelNT>(h, kBins1, (uint32_t)K, true, scratch, &s_d, &s_before);
-  const uint32_t b1 = (uint32_t)s_d;
-  const uint32_t above = s_before;
-  // the histogram gives the candidate count up front: LDS when they fit
-  const bool in_lds = h[b1] <= (uint32_t)kSelCand;
-  const int cap = in_lds ? kSelCand : T_stride;
-  uint32_t* ck = in_lds ? s_ck : ws.ckey + (size_t)r * T_stride;
-  int32_t* ct = in_lds ? s_ct : ws.ctok + (size_t)r * T_stride;
-  const int lane = lane_id();
-  for (int base = 0; base < n; base += kStep) {
-    float4 nx[kSelU];
-#pragma unroll
-    for (int u = 0; u < kSelU; ++u) {
-      const int t = base + kStep + (u * kSelNT + tid) * 4;
-      if (t < n) nx[u] = *reinterpret_cast<const float4*>(row + t);
-    }
-#pragma unroll
-    for (int u = 0; u < kSelU; ++u) {
-      const int t0 = base + (u * kSelNT + tid) * 4;
-      const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = t0 + e;
-        const uint32_t key = score_key(f[e]);
-        const uint32_t bin = key >> 21;
-        const bool ok = t < n;
-        if (ok && bin > b1) atomicOr(&bm[t >> 5], 1u << (t & 31));
-        const bool cand = ok && bin == b1;
-        const uint64_t m = __ballot(cand);
-        if (m) {
-          const int leader = __ffsll((long long)m) - 1;
-          int basepos = 0;
-          if (lane == leader) basepos = atomicAdd(&s_nc, __popcll(m));
-          basepos = __shfl(basepos, leader);
-          const int at = basepos + lanes_below(m);
-          if (cand && at < cap) {
-            ck[at] = key;
-            ct[at] = t;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kSelU; ++u) v[u] = nx[u];
-  }
-  __syncthreads();
-  const int nc = min(s_nc, cap);
-  uint32_t tau;
-  int t_cut;
-  candidates_threshold<kSelNT>(ck, ct, nc, b1, (uint32_t)K - above, h, scratch, &s_d, &s_before,
-                               &tau, &t_cut);
-  for (int i = tid; i < nc; i += kSelNT) {
-    const uint32_t key = ck[i];
-    const int t = ct[i];
-    if (key > tau || (key == tau && t <= t_cut)) atomicOr(&bm[t >> 5], 1u << (t & 31));
-  }
-  __syncthreads();
-  emit_bitmap<kSelNT, kSelWords / kSelNT>(bm, nwords, 0, 0, out, scratch);
 }
 
 }  // namespace
@@ -488,12 +462,7 @@ hipError_t launch_topk_select(const BatchDims& d, int K, const float* scores, in
                               void* ws, hipStream_t s) {
   const int R = d.B * d.P;
   TopkWs w = topk_ws(ws, R, d.T_stride, K);
-  if (d.T_stride <= kSelMaxN) {
-    hipLaunchKernelGGL(topk_select_row_kernel, dim3(R), dim3(kSelNT), 0, s, d.ctx_len, d.P,
-                       d.T_stride, K, scores, w, topk);
-    return hipGetLastError();
-  }
-  const int nchunk = (d.T_stride + kChunk - 1) / kChunk;
+  const int nchunk = (d.T_stride + kFChunk - 1) / kFChunk;
   hipLaunchKernelGGL(topk_filter_kernel, dim3(nchunk, R), dim3(kScanNT), 0, s, d.ctx_len, d.P,
                      d.T_stride, K, scores, w);
   hipLaunchKernelGGL(topk_finalize_kernel, dim3(R), dim3(kFinNT), 0, s, d.ctx_len, d.P,

@@ -118,8 +118,9 @@ hs_status hs_indexer_scores(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
  * scores among the visible tokens, ties going to the lower token index; written
  * in ascending token order.  A position that sees n <= K tokens selects all n,
  * followed by -1.  Scores must not be NaN; -0.0 equals +0.0.
- *   scores [B, P, T_stride] fp32, topk [B, P, K] int32 output.
- * 1 <= K <= 8192.  Workspace: hs_workspace_bytes(HS_OP_TOPK, ...). */
+ *   scores [B, P, T_stride] fp32 (16-byte aligned), topk [B, P, K] int32 output.
+ * 1 <= K <= 8192.  Workspace: hs_workspace_bytes(HS_OP_TOPK, ...), 16-byte
+ * aligned; its contents on entry do not matter. */
 hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t* topk,
                   void* ws, size_t ws_bytes, void* stream);
 

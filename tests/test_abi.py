@@ -56,6 +56,8 @@ def test_host_validation_rejects_bad_arguments_without_launching():
     assert lib.hs_topk(ctypes.byref(b), 9000, fake, fake, fake, 1 << 30, None) == 2
     assert lib.hs_topk(ctypes.byref(b), 8, fake, fake, fake, 10, None) == 5
     assert "workspace" in _lib.last_error()
+    assert lib.hs_topk(ctypes.byref(b), 8, ctypes.c_void_p(20), fake, fake, 1 << 30, None) == 6
+    assert "scores" in _lib.last_error()
     bad = _lib.Batch(2, 5, 1024, 16, 16)
     assert lib.hs_topk(ctypes.byref(bad), 8, fake, fake, fake, 1 << 30, None) == 2
     bad = _lib.Batch(2, 1, 1000, 15, 16)

@@ -350,9 +350,9 @@ def _planted_scores(case, rng, B, P, T_stride):
 @pytest.mark.parametrize("T_stride", [65536, (1 << 18) + 64])
 def test_topk_planted_ties_against_oracle(case, T_stride):
     """hs_topk alone on planted score rows, bit-exact against the oracle's
-    (score desc, token asc) selection: rows up to 2^18 tokens take the
-    one-workgroup select, longer rows the multi-workgroup filter; the
-    all-equal case has more candidates than the LDS list holds."""
+    (score desc, token asc) selection, for rows of 64K and 2^18 + 64 tokens
+    (four 64K-token bitmap segments); the all-equal and signed-zero cases have
+    more candidates than the finalize pass stages in LDS."""
     _say(f"topk planted {case} T_stride={T_stride}")
     from decode_indexer_logits_amd import _lib
     from oracle import topk as o_topk
