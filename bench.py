@@ -121,6 +121,7 @@ def cpu_baseline(wl, n_req: int):
     except Exception:
         cores = len(os.sched_getaffinity(0))
     q_idx, q = wl.step_inputs(1)
+    n_req = min(n_req, wl.B)
     sel_b = list(range(n_req))
     t0 = time.perf_counter()
     S = oi.indexer_scores(q_idx[sel_b], wl.q_dtype, wl.w[sel_b], wl.idx_pool, wl.k_dtype,
@@ -154,6 +155,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--chunks", type=int, default=1,
                     help="request chunks of the pipelined step (1 = one stream, no overlap)")
+    ap.add_argument("--copy-wgs", type=int, default=32,
+                    help="workgroups of the fault copy in the pipelined step")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path does not "
@@ -191,7 +194,7 @@ def main():
         if nchunks == 1:
             ds.run()
         else:
-            ds.run_pipelined(nchunks)
+            ds.run_pipelined(nchunks, a.copy_wgs)
 
     def capture(nchunks):
         g = torch.cuda.CUDAGraph()
@@ -284,7 +287,8 @@ def main():
                    "query_heads": wl.Hq, "indexer_heads": wl.H_idx, "indexer_dim": wl.D_idx,
                    "layers": wl.L, "positions": wl.P, "hot_rows": wl.C,
                    "resident_tail_tokens": 4096 if wl.name == "mixed_128k" else None,
-                   "graph": not a.no_graph, "pipeline_chunks": a.chunks},
+                   "graph": not a.no_graph, "pipeline_chunks": a.chunks,
+                   "pipeline_copy_workgroups": a.copy_wgs if a.chunks > 1 else None},
         "roofline": {"bound": "hbm", "kernel": "indexer_bf16_e4m3",
                      "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -64,7 +64,7 @@ def load() -> ctypes.CDLL:
                                     c_int32, P, P, c_size_t, P]
     lib.hs_resolve_rows.argtypes = [P, c_int32, P, P, P, P, P, P, c_size_t, P]
     lib.hs_resolve_tables.argtypes = [P, c_int32, P, P, P, P, P, P]
-    lib.hs_copy_faults.argtypes = [P, c_int32, P, P, P, P]
+    lib.hs_copy_faults.argtypes = [P, c_int32, P, P, P, c_int32, P]
     lib.hs_sparse_mla_decode.argtypes = [P, c_int32, c_int32, c_int32, P, c_int32, P, P, P,
                                          c_float, P, P, P, c_size_t, P]
     for f in ("hs_indexer_scores", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables",
@@ -151,9 +151,10 @@ def resolve_tables(batch: Batch, K: int, topk_t, res: Residency, row_ids, faults
                                     _ptr(row_ids), _ptr(faults), _ptr(counts), _stream(stream)))
 
 
-def copy_faults(batch: Batch, K: int, res: Residency, faults, counts, stream=None):
+def copy_faults(batch: Batch, K: int, res: Residency, faults, counts, workgroups: int = 0,
+                stream=None):
     _check(load().hs_copy_faults(ctypes.byref(batch), K, ctypes.byref(res), _ptr(faults),
-                                 _ptr(counts), _stream(stream)))
+                                 _ptr(counts), workgroups, _stream(stream)))
 
 
 def sparse_mla_decode(batch: Batch, K: int, Hq: int, q_t: str, q, kv_t: str, pool, row_scale,

@@ -238,13 +238,17 @@ hs_status hs_resolve_tables(const hs_batch* batch, int32_t K, const int32_t* top
 }
 
 hs_status hs_copy_faults(const hs_batch* batch, int32_t K, const hs_residency* res,
-                         const int32_t* faults, const int32_t* counts, void* stream) {
+                         const int32_t* faults, const int32_t* counts, int32_t workgroups,
+                         void* stream) {
   hs::BatchDims d;
   if (hs_status st = check_batch(batch, &d)) return st;
   if (!faults || !counts) return fail(HS_ERR_NULL, "hs_copy_faults: faults and counts are required");
+  if (workgroups < 0 || workgroups > 1024)
+    return fail(HS_ERR_SHAPE, "hs_copy_faults: workgroups=%d out of [0, 1024]", workgroups);
   hs::ResidencyArgs r;
   if (hs_status st = check_residency(d, K, res, &r)) return st;
-  return launched(hs::launch_fault_copy(d, K, r, faults, counts, static_cast<hipStream_t>(stream)),
+  return launched(hs::launch_fault_copy(d, K, r, faults, counts, workgroups,
+                                        static_cast<hipStream_t>(stream)),
                   "fault copy");
 }
 
@@ -255,7 +259,7 @@ hs_status hs_resolve_rows(const hs_batch* batch, int32_t K, const int32_t* topk,
   (void)ws_bytes;
   if (hs_status st = hs_resolve_tables(batch, K, topk, res, row_ids, faults, counts, stream))
     return st;
-  return hs_copy_faults(batch, K, res, faults, counts, stream);
+  return hs_copy_faults(batch, K, res, faults, counts, 0, stream);
 }
 
 hs_status hs_sparse_mla_decode(const hs_batch* batch, int32_t K, int32_t Hq, hs_dtype q_t,

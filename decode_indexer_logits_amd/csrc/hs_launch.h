@@ -52,8 +52,10 @@ struct ResidencyArgs {
 hipError_t launch_resolve_tables(const BatchDims& d, int K, const int32_t* topk,
                                  const ResidencyArgs& r, int32_t* row_ids, int32_t* faults,
                                  int32_t* counts, hipStream_t s);
+// workgroups = 0: the default grid (every CU)
 hipError_t launch_fault_copy(const BatchDims& d, int K, const ResidencyArgs& r,
-                             const int32_t* faults, const int32_t* counts, hipStream_t s);
+                             const int32_t* faults, const int32_t* counts, int workgroups,
+                             hipStream_t s);
 
 int mla_num_splits(int B, int P, int K);
 size_t mla_workspace_bytes(int B, int P, int K, int Hq);

@@ -11,9 +11,11 @@
 // and tokens as N, so that after the product each lane holds four heads of
 // one token and the ReLU / weighted head sum needs only two cross-lane adds.
 // Keys are streamed once from HBM a 64-token page (64 x D bytes) at a time: for
-// each 16-token group every lane loads D/4 contiguous bytes of its token (the
-// contraction index is permuted consistently in both operands, which a sum
-// allows), converts E4M3 -> bf16 in registers (exact) and issues the products.
+// each 16-token group every lane loads 16 bytes of its token from each 64-byte
+// half of the key row, so that a wave's load covers whole 64-byte halves of 16
+// rows (the contraction index is permuted consistently in both operands, which
+// a sum allows), converts E4M3 -> bf16 in registers (exact) and issues the
+// products.
 // Three pages are in flight per wave (a page is requested three pages before
 // it is consumed), and a page's 64 scores leave in one coalesced store.  A page's dequant scale
 // factors out of ReLU (positive scale), so it multiplies the head sum.
@@ -33,7 +35,7 @@ struct IdxCfg {
   static constexpr int WPP = (P == 1) ? 4 : (P == 2 ? 2 : 1);   // waves per position
   static constexpr int NW = P * WPP;
   static constexpr int NT = NW * kWave;
-  static constexpr int TILE = (P <= 2) ? 4096 : 1024;           // tokens per workgroup
+  static constexpr int TILE = 4096;                              // tokens per workgroup
 };
 
 template <int P, int DK, int HT, bool HIST>
@@ -46,8 +48,7 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
   using Cfg = IdxCfg<P>;
   constexpr int H = 16 * HT;
   constexpr int KS = DK / 32;    // k-steps of 32
-  constexpr int SEG = DK / 4;    // contiguous key bytes per lane per token
-  constexpr int NV = SEG / 16;   // 16-byte loads per lane per 16-token group
+  constexpr int NV = DK / 64;    // 16-byte loads per lane per 16-token group
   constexpr int LPB = 4 * NV;    // 16-byte loads per lane per 64-token page
   const int b = blockIdx.y;
   const int T = ctx_len[b];
@@ -67,14 +68,20 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
   }
   if (lim >= tile0) {
 
-  // query fragments: head 16*mt + n, dims SEG*g + 8*s .. +8
+  // Contraction order: lane group g owns key bytes 16g .. 16g+15 of each
+  // 64-byte half of a token's key, so that one 16-byte load per lane covers
+  // whole 64-byte halves of 16 key rows (half the memory requests of a
+  // 16-byte-strided layout).  k-step s takes dims dim0(s) .. +8 of head n in A
+  // and of token n in B.
+  auto dim0 = [&](int s) { return 16 * g + 64 * (s >> 1) + 8 * (s & 1); };
+  // query fragments: head 16*mt + n, dims dim0(s) .. +8
   bf16x8_t qa[HT][KS];
   const uint16_t* qp = q + (size_t)(b * P + p) * H * DK;
 #pragma unroll
   for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qa[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + (16 * mt + n) * DK + SEG * g + 8 * s));
+      qa[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + (16 * mt + n) * DK + dim0(s)));
   float wv[HT][4];
   const float* wp = w + (size_t)(b * P + p) * H;
 #pragma unroll
@@ -99,17 +106,17 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
   auto page_scale = [&](int pi) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
   };
-  // lane (n, g) loads, for token 16j + n of a page, bytes SEG*g .. +SEG, and
+  // lane (n, g) loads, for token 16j + n of a page, bytes 16g + 64v .. +16, and
   // the bias of token 64*pi + lane.  Three pages are in flight per wave: page
   // i+3W is requested as soon as page i has been consumed (W = waves sharing
   // the position).
   auto load_page = [&](int pi, uint4* buf, float& bs) {
-    const uint8_t* kp = pool + (size_t)page_blk(pi) * kBlock * DK + n * DK + SEG * g;
+    const uint8_t* kp = pool + (size_t)page_blk(pi) * kBlock * DK + n * DK + 16 * g;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < NV; ++v)
-        buf[j * NV + v] = *reinterpret_cast<const uint4*>(kp + 16 * j * DK + 16 * v);
+        buf[j * NV + v] = *reinterpret_cast<const uint4*>(kp + 16 * j * DK + 64 * v);
     const int tl = pi * kBlock + lane;
     bs = (biasb && tl <= lim_t) ? biasb[tl] : 0.f;
   };

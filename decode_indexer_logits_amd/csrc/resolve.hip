@@ -525,10 +525,12 @@ hipError_t launch_resolve_tables(const BatchDims& d, int K, const int32_t* topk,
 }
 
 hipError_t launch_fault_copy(const BatchDims& d, int K, const ResidencyArgs& r,
-                             const int32_t* faults, const int32_t* counts, hipStream_t s) {
+                             const int32_t* faults, const int32_t* counts, int workgroups,
+                             hipStream_t s) {
   const int PK = d.P * K;
   const int row_bytes = kDLat * r.kv_bytes;
-  hipLaunchKernelGGL((fault_copy_kernel<kCopyNT, kCopyInFlight>), dim3(kCopyWGs), dim3(kCopyNT), 0, s, d.B, PK, r.C, r.L,
+  const int grid = workgroups > 0 ? workgroups : kCopyWGs;
+  hipLaunchKernelGGL((fault_copy_kernel<kCopyNT, kCopyInFlight>), dim3(grid), dim3(kCopyNT), 0, s, d.B, PK, r.C, r.L,
                      row_bytes, d.max_blocks, faults, counts, r.hot_blocks, r.host_bt,
                      static_cast<const uint8_t*>(r.host_rows), r.host_scale, r.host_layer_rows,
                      static_cast<uint8_t*>(r.pool), r.row_scale, r.pool_layer_rows, r.step);

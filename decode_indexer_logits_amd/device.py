@@ -143,8 +143,9 @@ class DeviceStep:
         _lib.resolve_tables(self.batch, self.wl.K, self.topk, self.res, self.row_ids, self.faults,
                             self.counts, stream)
 
-    def run_copy_faults(self, stream=None):
-        _lib.copy_faults(self.batch, self.wl.K, self.res, self.faults, self.counts, stream)
+    def run_copy_faults(self, workgroups: int = 0, stream=None):
+        _lib.copy_faults(self.batch, self.wl.K, self.res, self.faults, self.counts, workgroups,
+                         stream=stream)
 
     def run_attention(self, layer: int, stream=None):
         wl = self.wl
@@ -201,13 +202,14 @@ class DeviceStep:
         if self.ws_mla is None or self.ws_mla.numel() < need:
             self.ws_mla = torch.empty(need, dtype=torch.uint8, device=self.device)
 
-    def run_pipelined(self, nchunks: int = 4):
+    def run_pipelined(self, nchunks: int = 4, copy_workgroups: int = 32):
         """One decode step with the batch split into request chunks on two streams:
         a compute stream runs indexer -> top-K -> resolve tables chunk after chunk,
         and a copy stream runs each chunk's host-link fault copies and attention
         as soon as its tables are resolved, so the copies overlap the following
-        chunks' HBM-bound work.  Same results as run() (per-chunk step counters
-        all advance together)."""
+        chunks' HBM-bound work.  The copies use `copy_workgroups` workgroups so
+        that most compute units stay with the HBM-bound kernels.  Same results
+        as run() (per-chunk step counters all advance together)."""
         torch = _torch()
         if nchunks > self.max_chunks or nchunks > self.wl.B:
             raise ValueError(f"nchunks={nchunks} out of range")
@@ -234,7 +236,8 @@ class DeviceStep:
                 ev.record(cs)
             xs.wait_event(ev)
             with torch.cuda.stream(xs):
-                _lib.copy_faults(batch, wl.K, res, self.faults[sl], self.counts[sl])
+                _lib.copy_faults(batch, wl.K, res, self.faults[sl], self.counts[sl],
+                                 copy_workgroups)
                 for l in range(wl.L):
                     _lib.sparse_mla_decode(batch, wl.K, wl.Hq, wl.q_dtype, self.q[l][sl],
                                            wl.kv_dtype, self.pool[l],

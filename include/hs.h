@@ -212,12 +212,17 @@ hs_status hs_resolve_rows(const hs_batch* batch, int32_t K, const int32_t* topk,
  * Enqueued on one stream in this order they are hs_resolve_rows.  The copy may
  * run on another stream behind an event recorded after hs_resolve_tables;
  * then nothing may read the faulted slots before it completes, and the next
- * hs_resolve_tables on the same state (and step counter) must wait for it. */
+ * hs_resolve_tables on the same state (and step counter) must wait for it.
+ * `workgroups` bounds the copy's grid: 0 lets it use the whole GPU (fastest
+ * alone); a small grid (e.g. 32) leaves most compute units to HBM-bound work
+ * running concurrently on another stream, at nearly the same link rate.
+ * 0 <= workgroups <= 1024. */
 hs_status hs_resolve_tables(const hs_batch* batch, int32_t K, const int32_t* topk,
                             const hs_residency* res, int32_t* row_ids, int32_t* faults,
                             int32_t* counts, void* stream);
 hs_status hs_copy_faults(const hs_batch* batch, int32_t K, const hs_residency* res,
-                         const int32_t* faults, const int32_t* counts, void* stream);
+                         const int32_t* faults, const int32_t* counts, int32_t workgroups,
+                         void* stream);
 
 /* Sparse MLA decode attention in the absorbed (MQA) form that the
  * sparse_mla_force_mqa option keeps on the sparse kernel (page "vLLM sert
