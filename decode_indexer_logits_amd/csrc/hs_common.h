@@ -73,6 +73,29 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Sum over the four 16-lane rows of a wave, in every lane of column lane % 16:
+// (row0 + row1) + (row2 + row3), the same additions as a butterfly over lane
+// distances 16 then 32, done with gfx950's row-swap permutes instead of LDS
+// permutes.
+__device__ __forceinline__ float sum_rows16(float v) {
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t y = __float_as_uint(s);
+  const auto c = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Maximum over the four 16-lane rows (same pattern as sum_rows16).
+__device__ __forceinline__ float max_rows16(float v) {
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const float s = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t y = __float_as_uint(s);
+  const auto c = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int from) {
   for (int o = from; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

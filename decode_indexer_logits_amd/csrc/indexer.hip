@@ -144,8 +144,7 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
       for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) v = fmaf(wv[mt][i], relu_bits(acc[mt][i]), v);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
+      v = sum_rows16(v);
       vj[j] = v;                  // every lane of column n holds token 16j + n
     }
     // lane 16g + n stores token 16g + n of the page: one coalesced 256-byte store
@@ -182,6 +181,161 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     __syncthreads();
     for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT)
       if (sh_hist[i]) atomicAdd(&hist[(size_t)(b * P + i / 2048) * 2048 + (i % 2048)], sh_hist[i]);
+  }
+}
+
+// Several query positions (P = 2..4, speculative tokens): every position reads
+// the same keys, so a workgroup loads and converts each key page once and
+// shares it through LDS.  Wave w converts 16-token group w of the page
+// (E4M3 -> bf16 MFMA B fragments, 16 KB per page) into one of two LDS page
+// buffers while the page before is multiplied; the waves of position p
+// (WPP = 4/P of them, groups split between them) read the fragments back and
+// run the products against their position's queries.  One barrier per page.
+// Raw key loads run three pages ahead in registers (8 bytes per token-row per
+// lane, a quarter page per wave).  The histogram epilogue packs two 16-bit
+// bins per LDS word (a position sees at most 4096 tokens of a tile).
+template <int P, int DK, int HT, bool HIST>
+__global__ __launch_bounds__(256) void indexer_mp_kernel(
+    const int32_t* __restrict__ ctx_len, int T_stride, int max_blocks,
+    const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const uint8_t* __restrict__ pool, const float* __restrict__ scale,
+    const int32_t* __restrict__ bt, const float* __restrict__ bias,
+    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+  static_assert(P >= 2 && P <= 4, "multi-position kernel");
+  constexpr int TILE = 4096;
+  constexpr int WPP = (P == 2) ? 2 : 1;      // waves per position (P = 3: wave 3 only converts)
+  constexpr int H = 16 * HT;
+  constexpr int KS = DK / 32;
+  constexpr int NV = DK / 64;
+  constexpr int FR = 4 * KS;                 // B fragments per page (4 groups x KS k-steps)
+  __shared__ bf16x8_t sk[2][FR][kWave];      // two converted pages
+  __shared__ uint32_t sh_hist[HIST ? P * 1024 : 1];
+  const int b = blockIdx.y;
+  const int T = ctx_len[b];
+  const int tile0 = blockIdx.x * TILE;
+  if (tile0 >= T) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int p = wave / WPP, sub = wave % WPP;
+  const bool active = p < P;
+  const int lim = T - P + (active ? p : P - 1);
+  const int lim_any = T - 1;                 // last token any position sees
+  if (HIST)
+    for (int i = threadIdx.x; i < P * 1024; i += 256) sh_hist[i] = 0;
+  const int npages = min(TILE / kBlock, (lim_any - tile0) / kBlock + 1);
+  const int32_t* btb = bt + (size_t)b * max_blocks + tile0 / kBlock;
+  const int blk_l = lane < npages ? btb[lane] : 0;
+  const float sc_l = (scale && lane < npages) ? scale[blk_l] : 1.f;
+  auto page_blk = [&](int pi) { return __builtin_amdgcn_readlane(blk_l, pi); };
+  auto page_scale = [&](int pi) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
+  };
+  // query fragments of this wave's position (same contraction order as the
+  // one-position kernel)
+  auto dim0 = [&](int s) { return 16 * g + 64 * (s >> 1) + 8 * (s & 1); };
+  bf16x8_t qa[HT][KS];
+  float wv[HT][4];
+  const int pq = active ? p : 0;
+  const uint16_t* qp = q + (size_t)(b * P + pq) * H * DK;
+#pragma unroll
+  for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qa[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + (16 * mt + n) * DK + dim0(s)));
+  const float* wp = w + (size_t)(b * P + pq) * H;
+#pragma unroll
+  for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[mt][i] = wp[16 * mt + 4 * g + i];
+  float* out = scores + (size_t)(b * P + pq) * T_stride + tile0;
+  const float* biasb = bias ? bias + (size_t)b * T_stride + tile0 : nullptr;
+  const int lim_t = lim - tile0;
+  // raw keys of group `wave` of page pi: token 16*wave + n, bytes 16g + 64v
+  auto load_raw = [&](int pi, uint4* r) {
+    const uint8_t* kp = pool + (size_t)page_blk(min(pi, npages - 1)) * kBlock * DK +
+                        (16 * wave + n) * DK + 16 * g;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) r[v] = *reinterpret_cast<const uint4*>(kp + 64 * v);
+  };
+  auto convert = [&](const uint4* r, int buf) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 c = r[s >> 1];
+      const uint32_t lo = (s & 1) ? c.z : c.x;
+      const uint32_t hi = (s & 1) ? c.w : c.y;
+      sk[buf][wave * KS + s][lane] = e4m3x8_to_bf16x8(lo, hi);
+    }
+  };
+  auto compute = [&](int pi, int buf) {
+    if (!active) return;
+    const int tl = pi * kBlock + lane;
+    const float bs = (biasb && tl <= lim_t) ? biasb[tl] : 0.f;
+    float vj[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j % WPP != sub) continue;
+      bf16x8_t kb[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kb[s] = sk[buf][j * KS + s][lane];
+      f32x4_t acc[HT];
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // keep issuing this wave's products back to back once they start
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(qa[mt][s], kb[s], acc[mt]);
+      __builtin_amdgcn_s_setprio(0);
+      float v = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wv[mt][i], relu_bits(acc[mt][i]), v);
+      v = sum_rows16(v);
+      vj[j] = v;
+    }
+    // lane 16g + n stores token 16g + n when group g is one of this wave's
+    const float mine = g == 0 ? vj[0] : (g == 1 ? vj[1] : (g == 2 ? vj[2] : vj[3]));
+    if (g % WPP == sub && tl <= lim_t) {
+      const float val = (scale ? mine * page_scale(pi) : mine) + bs;
+      out[tl] = val;
+      if (HIST) {
+        const uint32_t bin = score_key(val) >> 21;
+        atomicAdd(&sh_hist[p * 1024 + (bin >> 1)], 1u << (16 * (bin & 1)));
+      }
+    }
+  };
+  // software pipeline: raw loads three pages ahead, conversion one page ahead
+  uint4 rA[NV], rB[NV], rC[NV];
+  load_raw(0, rA);
+  load_raw(1, rB);
+  load_raw(2, rC);
+  convert(rA, 0);
+  load_raw(3, rA);
+  __syncthreads();
+  for (int k = 0; k < npages; k += 3) {
+    // page k+1 from rB, k+2 from rC, k+3 from rA
+    if (k + 1 < npages) { convert(rB, (k + 1) & 1); load_raw(k + 4, rB); }
+    compute(k, k & 1);
+    __syncthreads();
+    if (k + 1 >= npages) break;
+    if (k + 2 < npages) { convert(rC, (k + 2) & 1); load_raw(k + 5, rC); }
+    compute(k + 1, (k + 1) & 1);
+    __syncthreads();
+    if (k + 2 >= npages) break;
+    if (k + 3 < npages) { convert(rA, (k + 3) & 1); load_raw(k + 6, rA); }
+    compute(k + 2, (k + 2) & 1);
+    __syncthreads();
+  }
+  if (HIST) {
+    for (int i = threadIdx.x; i < P * 1024; i += 256) {
+      const uint32_t x = sh_hist[i];
+      const int pos = i / 1024, bin = 2 * (i % 1024);
+      uint32_t* hrow = hist + (size_t)(b * P + pos) * 2048;
+      if (x & 0xFFFFu) atomicAdd(&hrow[bin], x & 0xFFFFu);
+      if (x >> 16) atomicAdd(&hrow[bin + 1], x >> 16);
+    }
   }
 }
 
@@ -227,6 +381,17 @@ hipError_t launch_mfma(const BatchDims& d, const uint16_t* q, const float* w, co
                        uint32_t* hist, hipStream_t s) {
   using Cfg = IdxCfg<P>;
   dim3 grid((d.T_stride + Cfg::TILE - 1) / Cfg::TILE, d.B);
+  if (P > 1) {
+    if (hist)
+      hipLaunchKernelGGL((indexer_mp_kernel<(P > 1 ? P : 2), DK, HT, true>), grid, dim3(256), 0, s,
+                         d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias, scores,
+                         hist);
+    else
+      hipLaunchKernelGGL((indexer_mp_kernel<(P > 1 ? P : 2), DK, HT, false>), grid, dim3(256), 0,
+                         s, d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias,
+                         scores, hist);
+    return hipGetLastError();
+  }
   if (hist)
     hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT, true>), grid, dim3(Cfg::NT), 0, s,
                        d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias, scores,

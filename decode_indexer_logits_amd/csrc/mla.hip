@@ -133,8 +133,7 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
       z[i] = (r_i >= 0) ? acc[i] * qk_scale_log2 * sc[i] : -INFINITY;
     }
     float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_rows16(mx);
     if (g == 0) red[wave][n] = mx;
     __syncthreads();
     const float mt = fmaxf(fmaxf(red[0][n], red[1][n]), fmaxf(red[2][n], red[3][n]));
@@ -173,8 +172,7 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
   }
 
   float lp = l_part;
-  lp += __shfl_xor(lp, 16);
-  lp += __shfl_xor(lp, 32);
+  lp = sum_rows16(lp);
   if (g == 0) red[wave][n] = lp;
   __syncthreads();
   const float l_tot = (red[0][n] + red[1][n]) + (red[2][n] + red[3][n]);

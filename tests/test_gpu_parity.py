@@ -111,6 +111,24 @@ def test_mtp3_small_multi_step():
         _say(s, info["counts"].tolist())
 
 
+@pytest.mark.parametrize("P", [2, 3])
+def test_speculative_positions_two_and_three(P):
+    """P = 2 and 3 query positions (the shared-key indexer splits a page's
+    groups between two waves per position at P = 2 and leaves one converting
+    wave idle at P = 3); two steps, every stage against the oracle."""
+    _say(f"mtp P={P} small, 2 steps")
+    wl = gen.mtp3_agentic(B=3, K=128, steps=2, first_turn=9000, per_turn=300, turns=5,
+                          out_max=50, P=P)
+    from decode_indexer_logits_amd.device import DeviceStep
+    ds = DeviceStep(wl)
+    ost = gc.oracle_state(wl)
+    for s in range(1, wl.steps + 1):
+        ds.set_queries(s)
+        ds.run()
+        ost, rr, info = gc.full_check(ds, wl, ost, s=s, attn_tol=2e-2)
+        _say(s, info["counts"].tolist())
+
+
 def test_norescache_small_hit_rate_warms_up():
     _say("no-residency small, 4 steps")
     wl = gen.norescache_1m(B=2, T=32768, K=256, L=2, steps=4)

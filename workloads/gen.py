@@ -536,7 +536,8 @@ def conversation_lengths(ss, B: int, first_turn: int = 74160, per_turn: int = 97
 
 def mtp3_agentic(seed: int = 1004, B: int = 64, K: int = 2048, steps: int = 4,
                  rho: float = 0.95, pool_frac: float = 0.40, first_turn: int = 74160,
-                 per_turn: int = 973, turns: int = 13, out_max: int = 220) -> Workload:
+                 per_turn: int = 973, turns: int = 13, out_max: int = 220,
+                 P: int = 4) -> Workload:
     """MTP3 agentic mix: 3 speculative tokens, so P = 4 query positions and hot
     buffers of (3 + 2) x K = 10240 rows per request.  Context lengths follow
     13-turn conversations (first turn 74,160 tokens, then +753 input and +220
@@ -544,9 +545,10 @@ def mtp3_agentic(seed: int = 1004, B: int = 64, K: int = 2048, steps: int = 4,
     output position j ~ U{1..220}.  The GPU pool holds 40 % of all rows: the hot
     blocks plus an equal resident tail per request; the rest is host-only.
     Four steps with the indexer queries drifting as AR(1) (rho = 0.95) and fresh
-    attention queries per step; hot buffers start empty."""
+    attention queries per step; hot buffers start empty.  ``P`` other than 4
+    (P - 1 speculative tokens, hot buffers (P + 1) x K) serves smaller tests."""
     ch = _children(seed)
-    P, Hq, H, D, L = 4, 16, 64, 128, 1
+    Hq, H, D, L = 16, 64, 128, 1
     C = (P + 1) * K
     ctx = conversation_lengths(ch[0], B, first_turn, per_turn, turns, out_max)
     Ts = _round_up(int(ctx.max()), BLOCK)
