@@ -96,6 +96,30 @@ __device__ __forceinline__ float max_rows16(float v) {
   return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
+// Reductions over the whole wave (every lane receives the result): quad
+// butterflies and the half-row / row mirrors as DPP moves, then the two row
+// swaps.  All 64 lanes must be active.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_allreduce_u32(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op((uint32_t)a[0], (uint32_t)a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op((uint32_t)c[0], (uint32_t)c[1]);
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  return (int)wave_allreduce_u32((uint32_t)v, [](uint32_t x, uint32_t y) { return x + y; });
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+  return (int)wave_allreduce_u32(
+      (uint32_t)v, [](uint32_t x, uint32_t y) { return (uint32_t)min((int)x, (int)y); });
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int from) {
   for (int o = from; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

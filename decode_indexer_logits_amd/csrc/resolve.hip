@@ -103,7 +103,8 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   __shared__ int scratch[kResNT / kWave + 1];
   __shared__ uint32_t h256[256];
   __shared__ int s_nlist[4];
-  __shared__ int s_res, s_hit, s_ev, s_cnt, s_vcnt, s_d, s_next;
+  __shared__ int s_res, s_hit, s_ev, s_vcnt, s_d;
+  __shared__ int s_wa[2][kResNT / kWave], s_wb[2][kResNT / kWave];   // per-wave partials
   __shared__ uint32_t s_before;
   __shared__ unsigned long long s_kmin, s_kmax;
   int32_t* sA = reinterpret_cast<int32_t*>(sA64);
@@ -125,7 +126,6 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
     s_res = 0;
     s_hit = 0;
     s_ev = 0;
-    s_cnt = 0;
     s_vcnt = 0;
     s_kmin = ~0ull;
     s_kmax = 0ull;
@@ -246,8 +246,14 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
         ++pos;
       }
   }
-  if (my_res) atomicAdd(&s_res, my_res);
-  if (my_hit) atomicAdd(&s_hit, my_hit);
+  // per-wave totals, one LDS atomic per wave (same-address atomics from every
+  // thread serialize)
+  my_res = wave_sum_i32(my_res);
+  my_hit = wave_sum_i32(my_hit);
+  if (lane == 0) {
+    if (my_res) atomicAdd(&s_res, my_res);
+    if (my_hit) atomicAdd(&s_hit, my_hit);
+  }
   // The stamps written above are read back below only by this workgroup, and
   // no line of the table was read before: the barrier's workgroup-scope
   // release/acquire is enough (a device-scope fence would write back L2).
@@ -263,6 +269,7 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   bool keys64 = false;            // victims as sorted 64-bit keys (general path)
   int32_t* V32 = sA;              // victim slots, fast path (R1: the merge lists are dead)
   if (nF > 0 && C > 0) {
+    const int wid = tid / kWave;
     int my_c = 0, my_min = 0x7FFFFFFF;
 #pragma unroll
     for (int j = 0; j < kMaxSlotsPerThread; ++j) {
@@ -273,28 +280,58 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
         my_min = min(my_min, st_reg[j]);
       }
     }
-    if (tid == 0) s_next = 0x7FFFFFFF;
-    __syncthreads();
-    if (my_c) {
-      atomicAdd(&s_cnt, my_c);
-      atomicMin(&s_next, my_min);
+    // candidate count and oldest stamp: wave reductions, one barrier
+    my_c = wave_sum_i32(my_c);
+    my_min = wave_min_i32(my_min);
+    if (lane == 0) {
+      s_wa[0][wid] = my_c;
+      s_wb[0][wid] = my_min;
     }
     __syncthreads();
-    const int n_cand = s_cnt;
+    int n_cand = 0, sigma = 0x7FFFFFFF;
+#pragma unroll
+    for (int w = 0; w < kResNT / kWave; ++w) {
+      n_cand += s_wa[0][w];
+      sigma = min(sigma, s_wb[0][w]);
+    }
     n_serve = min(nF, n_cand);
-    int sigma = s_next;
     int got = 0;
     bool fast = true;
+    // one distinct stamp per round, slots in slot order: a slot's rank within
+    // the round is the number of equal stamps in earlier slots, counted with
+    // one ballot per slot of a thread's run (slot = tid*S + j) plus the
+    // earlier waves' totals; one barrier per round (partials double-buffered)
     for (int round = 0; got < n_serve; ++round) {
       if (round == kMaxStampRounds) {
         fast = false;
         break;
       }
-      int cnt = 0;
+      const int buf = (round + 1) & 1;
+      int below = 0, wtot = 0, my_next = 0x7FFFFFFF;
+      uint64_t m[kMaxSlotsPerThread];
 #pragma unroll
-      for (int j = 0; j < kMaxSlotsPerThread; ++j) cnt += (st_reg[j] == sigma);
-      int tot;
-      int pos = got + block_exclusive_scan<kResNT>(cnt, scratch, &tot);
+      for (int j = 0; j < kMaxSlotsPerThread; ++j) {
+        m[j] = __ballot(st_reg[j] == sigma);
+        below += lanes_below(m[j]);
+        wtot += __popcll(m[j]);
+        if (st_reg[j] > sigma && st_reg[j] < s) my_next = min(my_next, st_reg[j]);
+      }
+      my_next = wave_min_i32(my_next);
+      if (lane == 0) {
+        s_wa[buf][wid] = wtot;
+        s_wb[buf][wid] = my_next;
+      }
+      __syncthreads();
+      int off = 0, tot = 0, nxt = 0x7FFFFFFF;
+#pragma unroll
+      for (int w = 0; w < kResNT / kWave; ++w) {
+        const int x = s_wa[buf][w];
+        off += w < wid ? x : 0;
+        tot += x;
+        nxt = min(nxt, s_wb[buf][w]);
+      }
+      // equal stamps in this thread's earlier slots
+      int pos = got + off + below;
 #pragma unroll
       for (int j = 0; j < kMaxSlotsPerThread; ++j)
         if (st_reg[j] == sigma) {
@@ -302,16 +339,7 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
           ++pos;
         }
       got += tot;
-      if (got >= n_serve) break;
-      int my_next = 0x7FFFFFFF;
-#pragma unroll
-      for (int j = 0; j < kMaxSlotsPerThread; ++j)
-        if (st_reg[j] > sigma && st_reg[j] < s) my_next = min(my_next, st_reg[j]);
-      if (tid == 0) s_next = 0x7FFFFFFF;
-      __syncthreads();
-      if (my_next != 0x7FFFFFFF) atomicMin(&s_next, my_next);
-      __syncthreads();
-      sigma = s_next;
+      sigma = nxt;
     }
     if (!fast) {
       keys64 = true;
@@ -403,7 +431,8 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
       fb[2 * i] = t;
       fb[2 * i + 1] = v;
     }
-    if (my_ev) atomicAdd(&s_ev, my_ev);
+    my_ev = wave_sum_i32(my_ev);
+    if (lane == 0 && my_ev) atomicAdd(&s_ev, my_ev);
   }
   if (tid == 0 && n_serve < nF) atomicOr(err, 1);
   // fault rows from their victims (faults past n_serve keep row -1)
