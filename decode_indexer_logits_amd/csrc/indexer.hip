@@ -16,9 +16,11 @@
 // rows (the contraction index is permuted consistently in both operands, which
 // a sum allows), converts E4M3 -> bf16 in registers (exact) and issues the
 // products.
-// Three pages are in flight per wave (a page is requested three pages before
-// it is consumed), and a page's 64 scores leave in one coalesced store.  A page's dequant scale
-// factors out of ReLU (positive scale), so it multiplies the head sum.
+// Two pages are in flight per wave (a page is requested two pages before it
+// is consumed; head weights sit in LDS so that the queries and the ring fit
+// in registers), and a page's 64 scores leave in one coalesced store.  A
+// page's dequant scale factors out of ReLU (positive scale), so it multiplies
+// the head sum.
 //
 // Waves of a workgroup: with P positions, P groups of 4/P waves; each group
 // keeps its position's queries in registers (H x D bf16 spread over the wave)
@@ -82,12 +84,13 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       qa[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + (16 * mt + n) * DK + dim0(s)));
-  float wv[HT][4];
+  // head weights stay in LDS (read as float4 per 16-token group) to keep
+  // registers for the key ring
+  __shared__ float4 sw4[P][H / 4];
   const float* wp = w + (size_t)(b * P + p) * H;
-#pragma unroll
-  for (int mt = 0; mt < HT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wv[mt][i] = wp[16 * mt + 4 * g + i];
+  if (sub == 0)
+    for (int i = lane; i < H / 4; i += kWave) sw4[p][i] = reinterpret_cast<const float4*>(wp)[i];
+  __syncthreads();
 
   const int npages = min(Cfg::TILE / kBlock, (lim - tile0) / kBlock + 1);
   const int32_t* btb = bt + (size_t)b * max_blocks + tile0 / kBlock;
@@ -107,8 +110,8 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
   };
   // lane (n, g) loads, for token 16j + n of a page, bytes 16g + 64v .. +16, and
-  // the bias of token 64*pi + lane.  Three pages are in flight per wave: page
-  // i+3W is requested as soon as page i has been consumed (W = waves sharing
+  // the bias of token 64*pi + lane.  Two pages are in flight per wave: page
+  // i+2W is requested as soon as page i has been consumed (W = waves sharing
   // the position).
   auto load_page = [&](int pi, uint4* buf, float& bs) {
     const uint8_t* kp = pool + (size_t)page_blk(pi) * kBlock * DK + n * DK + 16 * g;
@@ -124,26 +127,28 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     float vj[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bf16x8_t kb[KS];
+      f32x4_t acc[HT];
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // each k-step's key fragment is converted right before its products
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const uint4 c = buf[j * NV + (s >> 1)];
         const uint32_t lo = (s & 1) ? c.z : c.x;
         const uint32_t hi = (s & 1) ? c.w : c.y;
-        kb[s] = e4m3x8_to_bf16x8(lo, hi);
+        const bf16x8_t kb = e4m3x8_to_bf16x8(lo, hi);
+#pragma unroll
+        for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(qa[mt][s], kb, acc[mt]);
       }
-      f32x4_t acc[HT];
-#pragma unroll
-      for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(qa[mt][s], kb[s], acc[mt]);
       float v = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < HT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v = fmaf(wv[mt][i], relu_bits(acc[mt][i]), v);
+      for (int mt = 0; mt < HT; ++mt) {
+        const float4 wq = sw4[p][4 * mt + g];
+        v = fmaf(wq.x, relu_bits(acc[mt][0]), v);
+        v = fmaf(wq.y, relu_bits(acc[mt][1]), v);
+        v = fmaf(wq.z, relu_bits(acc[mt][2]), v);
+        v = fmaf(wq.w, relu_bits(acc[mt][3]), v);
+      }
       v = sum_rows16(v);
       vj[j] = v;                  // every lane of column n holds token 16j + n
     }
@@ -163,18 +168,15 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
   constexpr int W = Cfg::WPP;
   const int npw = (npages - sub + W - 1) / W;
   auto page_of = [&](int k) { return min(sub + k * W, npages - 1); };
-  uint4 bufA[LPB], bufB[LPB], bufC[LPB];
-  float bsA, bsB, bsC;
+  uint4 bufA[LPB], bufB[LPB];
+  float bsA, bsB;
   load_page(page_of(0), bufA, bsA);
   load_page(page_of(1), bufB, bsB);
-  load_page(page_of(2), bufC, bsC);
-  for (int k = 0; k < npw; k += 3) {
+  for (int k = 0; k < npw; k += 2) {
     consume_page(sub + k * W, bufA, bsA);
-    load_page(page_of(k + 3), bufA, bsA);
+    load_page(page_of(k + 2), bufA, bsA);
     if (k + 1 < npw) consume_page(sub + (k + 1) * W, bufB, bsB);
-    load_page(page_of(k + 4), bufB, bsB);
-    if (k + 2 < npw) consume_page(sub + (k + 2) * W, bufC, bsC);
-    load_page(page_of(k + 5), bufC, bsC);
+    load_page(page_of(k + 3), bufB, bsB);
   }
   }  // lim >= tile0
   if (HIST) {

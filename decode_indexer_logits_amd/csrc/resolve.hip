@@ -526,12 +526,15 @@ __global__ __launch_bounds__(NT) void fault_copy_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int idx = c0 + u * NT + (int)threadIdx.x;
-          d[u] = -1;
+          uint4 x = make_uint4(0u, 0u, 0u, 0u);
+          int64_t dd = -1;
           if (idx < nchunk) {
             const int row = idx / cpr, c = idx - row * cpr;
-            v[u] = *reinterpret_cast<const uint4*>(host_rows + s_src[row] + (int64_t)c * 16);
-            d[u] = s_dst[row] + (int64_t)c * 16;
+            x = *reinterpret_cast<const uint4*>(host_rows + s_src[row] + (int64_t)c * 16);
+            dd = s_dst[row] + (int64_t)c * 16;
           }
+          v[u] = x;
+          d[u] = dd;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)

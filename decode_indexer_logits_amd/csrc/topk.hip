@@ -19,7 +19,8 @@
 //                 with the radix select over them (key bits 20..10, then 9..0),
 //                 sends ties at the threshold to the lower token (radix select
 //                 on the token index), and writes the K tokens in ascending
-//                 order through an LDS bitmap per 64K-token segment.
+//                 order through an LDS bitmap (one for rows up to 786432
+//                 tokens, else one per 64K-token segment).
 // Passes 3 and 4 stay separate kernels: handing a row from many workgroups to
 // one inside a kernel needs a device-scope release per workgroup, which on a
 // multi-die GPU writes back L2 and costs far more than a kernel boundary.
@@ -369,8 +370,9 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   __shared__ uint32_t h[kBins1];
   __shared__ int32_t outl[kMaxK];
   __shared__ uint32_t bm[kSegWords];
-  __shared__ uint32_t s_ck[kFinCand];
-  __shared__ int32_t s_ct[kFinCand];
+  __shared__ uint32_t s_cand[2 * kFinCand];   // candidate keys, then tokens; later the bitmap
+  uint32_t* s_ck = s_cand;
+  int32_t* s_ct = reinterpret_cast<int32_t*>(s_cand + kFinCand);
   __shared__ int scratch[kFinNT / kWave + 1];
   __shared__ int s_d, s_pos;
   __shared__ uint32_t s_before;
@@ -405,17 +407,49 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   int t_cut;
   candidates_threshold<kFinNT>(ck, ct, nc, b1, (uint32_t)K - above, h, scratch, &s_d, &s_before,
                                &tau, &t_cut);
-  for (int i = tid; i < nc; i += kFinNT) {
-    const uint32_t key = ck[i];
-    const int t = ct[i];
-    if (key > tau || (key == tau && t <= t_cut)) {
-      const int at = atomicAdd(&s_pos, 1);
-      if (at < kMaxK) outl[at] = t;
+  // chosen candidates join the outright selections: one ballot and one LDS
+  // atomic per wave (same-address atomics from every thread serialize)
+  const int lane = lane_id();
+  const int nc_up = (nc + kFinNT - 1) / kFinNT * kFinNT;
+  for (int i = tid; i < nc_up; i += kFinNT) {
+    bool chosen = false;
+    int t = 0;
+    if (i < nc) {
+      const uint32_t key = ck[i];
+      t = ct[i];
+      chosen = key > tau || (key == tau && t <= t_cut);
+    }
+    const uint64_t m = __ballot(chosen);
+    if (m) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&s_pos, __popcll(m));
+      base = __shfl(base, 0);
+      const int at = base + lanes_below(m);
+      if (chosen && at < kMaxK) outl[at] = t;
     }
   }
   __syncthreads();
-  // emit the K selected tokens in ascending order: an LDS bitmap per 2^16-token
-  // segment, then a popcount prefix sum over its words
+  // emit the K selected tokens in ascending order through an LDS bitmap and a
+  // popcount prefix sum: rows up to 786432 tokens in one bitmap laid over the
+  // (now dead) candidate list, longer rows in 2^16-token segments
+  const int nwords = (n + 31) / 32;
+  if (nwords <= 2 * kFinCand) {
+    uint32_t* bmw = s_cand;
+    for (int i = tid; i < nwords; i += kFinNT) bmw[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < K; i += kFinNT) {
+      const int t = outl[i];
+      atomicOr(&bmw[t >> 5], 1u << (t & 31));
+    }
+    __syncthreads();
+    if (nwords <= 4 * kFinNT)
+      emit_bitmap<kFinNT, 4>(bmw, nwords, 0, 0, out, scratch);
+    else if (nwords <= 8 * kFinNT)
+      emit_bitmap<kFinNT, 8>(bmw, nwords, 0, 0, out, scratch);
+    else
+      emit_bitmap<kFinNT, 24>(bmw, nwords, 0, 0, out, scratch);
+    return;
+  }
   int written = 0;
   const int nseg = (n + kSegTok - 1) / kSegTok;
   for (int sg = 0; sg < nseg; ++sg) {
