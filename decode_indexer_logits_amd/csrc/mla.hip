@@ -10,15 +10,16 @@
 //   QK   wave w takes rows 16w..16w+15 of the tile: S^T[rows x 16 heads] on
 //        the matrix cores (18 steps of v_mfma_f32_16x16x32_bf16 over the 576
 //        values).  Each lane reads 144 contiguous bytes of its row straight
-//        from HBM (the gather by row id), converts E4M3 -> bf16 in registers
-//        and also stores the 512 value entries transposed into LDS.
+//        from HBM (the gather by row id; row ids are read one tile ahead),
+//        converts E4M3 -> bf16 in registers and also stores its 512 value
+//        entries row-major into LDS (16-byte writes).
 //   softmax  online, per head; the tile maximum is combined across the four
 //        waves through LDS; the row's scale is folded into the logit and
 //        into the probability that multiplies its value codes.
 //   PV   wave w owns output dims 128w..128w+127: O^T[dims x heads] +=
-//        V^T[dims x 64 rows] . P^T[64 rows x heads], operands read from LDS
-//        (V^T chunks XOR-swizzled to keep both the transposing writes and
-//        the 16-byte reads free of bank conflicts).
+//        V^T[dims x 64 rows] . P^T[64 rows x heads], operands read from LDS;
+//        the V^T fragments come out of the row-major tile through gfx950's
+//        transposing LDS read (ds_read_b64_tr_b16), so no transposed stores.
 // A workgroup covers rows [split*R, split*R + R) in ascending k.  With one
 // slice it writes out/lse directly; otherwise the combine kernel merges the
 // slices' (O, max, sum) in slice order, so the reduction order depends only on
@@ -30,16 +31,27 @@ namespace hs {
 namespace {
 
 constexpr int kMlaNT = 256;
+constexpr int kMlaTargetWGs = 256;   // splits of the selected rows fill about this many workgroups
 constexpr int kTile = 64;
-constexpr int kVtStride = 72;   // bf16 per dim row: 64 rows + 8 pad (144 bytes)
 constexpr int kPtStride = 72;
 constexpr int kHq = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ int vt_index(int dim, int row) {
-  const int chunk = (row >> 3) ^ ((dim >> 3) & 7);
-  return dim * kVtStride + chunk * 8 + (row & 7);
+constexpr int kVrStride = 520;  // bf16 per row of the value tile: 512 + 8 pad (1040 bytes)
+
+typedef short lds_v4i16 __attribute__((ext_vector_type(4)));
+
+// Four consecutive value rows r0..r0+3 of one dim, for the MFMA A operand
+// (V^T: dims as M, rows as K), read from the row-major value tile with
+// gfx950's transposing LDS read: within each 16-lane group, source lane c
+// names 4 dims of row r0 + c/4 (dims d0 + 4*(c%4)), and lane i receives dim
+// d0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ lds_v4i16 vr_read_tr(const uint16_t* Vr, int r0, int d0, int c) {
+  const uint16_t* src = Vr + (r0 + (c >> 2)) * kVrStride + d0 + 4 * (c & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) lds_v4i16*)(
+          (__attribute__((address_space(3))) uint16_t*)(src)));
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -54,7 +66,7 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
     const float* __restrict__ row_scale, const int32_t* __restrict__ row_ids, int K,
     int rows_per_split, int nsplit, float qk_scale_log2, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kDVal * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vr[kTile * kVrStride];   // value tile, row-major
   __shared__ __attribute__((aligned(16))) uint16_t Pt[kHq * kPtStride];
   __shared__ float red[4][kHq];
 
@@ -78,10 +90,13 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
   const int32_t* rid_p = row_ids + (size_t)bp * K;
   const int r_local = 16 * wave + n;
 
-  // gather of one tile's rows for this lane (row r_local, bytes 144g .. +144)
-  auto gather = [&](int kt, int& rid, float& rs, uint4* raw) {
+  // row ids run one tile ahead of the row loads, so a tile's rows wait for one
+  // round of loads, not two; this lane gathers row r_local, bytes 144g .. +144
+  auto load_rid = [&](int kt) {
     const int kk = kt + r_local;
-    rid = (kk < ke) ? rid_p[kk] : -1;
+    return (kk < ke) ? rid_p[kk] : -1;
+  };
+  auto gather = [&](int rid, float& rs, uint4* raw) {
     rs = 0.f;
     if (rid >= 0) {
       const uint4* src = reinterpret_cast<const uint4*>(pool + (size_t)rid * kDLat + 144 * g);
@@ -93,13 +108,17 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
       for (int v = 0; v < 9; ++v) raw[v] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  int rid, rid_n = -1;
+  int rid = load_rid(kb), rid_n = load_rid(kb + kTile);
   float rs, rs_n = 0.f;
   uint4 raw[9], raw_n[9];
-  gather(kb, rid, rs, raw);
+  gather(rid, rs, raw);
   for (int kt = kb; kt < ke; kt += kTile) {
-    if (kt + kTile < ke) gather(kt + kTile, rid_n, rs_n, raw_n);
-    // S^T = X . Q^T over 576 values; stash the value part transposed
+    int rid_nn = -1;
+    if (kt + kTile < ke) {
+      gather(rid_n, rs_n, raw_n);
+      rid_nn = load_rid(kt + 2 * kTile);
+    }
+    // S^T = X . Q^T over 576 values; stash the value part (row-major) in LDS
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 18; ++s) {
@@ -113,14 +132,9 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
       xb[3] = e4m3x2_to_bf16x2(hi, true);
       acc = mfma16x16x32(as_bf16x8(xb), qf[s], acc);
       const int dim0 = 144 * g + 8 * s;
-      if (dim0 < kDVal) {
-        uint16_t* dst = Vt + vt_index(dim0, r_local);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dst[(2 * i) * kVtStride] = (uint16_t)(xb[i] & 0xFFFFu);
-          dst[(2 * i + 1) * kVtStride] = (uint16_t)(xb[i] >> 16);
-        }
-      }
+      if (dim0 < kDVal)
+        *reinterpret_cast<uint4*>(Vr + r_local * kVrStride + dim0) =
+            make_uint4(xb[0], xb[1], xb[2], xb[3]);
     }
     // logits of this lane's rows 4g+i (head n), log2 domain
     float z[4];
@@ -159,14 +173,21 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
       const bf16x8_t pb = as_bf16x8(*reinterpret_cast<const uint4*>(Pt + n * kPtStride + 32 * c + 8 * g));
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const int dim = 128 * wave + 16 * dt + n;
-        const bf16x8_t va = as_bf16x8(*reinterpret_cast<const uint4*>(Vt + vt_index(dim, 32 * c + 8 * g)));
-        o[dt] = mfma16x16x32(va, pb, o[dt]);
+        const int d0 = 128 * wave + 16 * dt;
+        const lds_v4i16 lo = vr_read_tr(Vr, 32 * c + 8 * g, d0, n);
+        const lds_v4i16 hi = vr_read_tr(Vr, 32 * c + 8 * g + 4, d0, n);
+        u32x4_t w;
+        w[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+        w[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+        w[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+        w[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+        o[dt] = mfma16x16x32(as_bf16x8(w), pb, o[dt]);
       }
     }
     __syncthreads();
     rid = rid_n;
     rs = rs_n;
+    rid_n = rid_nn;
 #pragma unroll
     for (int v = 0; v < 9; ++v) raw[v] = raw_n[v];
   }
@@ -276,35 +297,62 @@ __global__ __launch_bounds__(kMlaNT) void mla_f32_kernel(
 }
 
 // Merges the slices of each (request, position, head) in slice order: one
-// wave per (request, position, head), 8 output dims per lane.
+// wave per (request, position, head), 8 output dims per lane.  The slices'
+// maxima and sums are read by one lane each and combined with wave
+// reductions; the partial outputs are then read four slices at a time, so
+// their loads overlap.
 __global__ __launch_bounds__(kWave) void mla_combine_kernel(int nsplit, const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
                                                             float* __restrict__ out,
                                                             float* __restrict__ lse) {
   const int bp = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x;
+  auto ml_index = [&](int sidx) { return (((size_t)bp * nsplit + sidx) * kHq + h) * 2; };
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(((size_t)bp * nsplit + s) * kHq + h) * 2]);
+  for (int s0 = 0; s0 < nsplit; s0 += kWave) {
+    const int sidx = s0 + lane;
+    const float ms = sidx < nsplit ? part_ml[ml_index(sidx)] : -INFINITY;
+    M = fmaxf(M, ms);
+  }
+  M = max_rows16(M);
+  M = fmaxf(M, __shfl_xor(M, 1));
+  M = fmaxf(M, __shfl_xor(M, 2));
+  M = fmaxf(M, __shfl_xor(M, 4));
+  M = fmaxf(M, __shfl_xor(M, 8));
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
   float L = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const size_t base = ((size_t)bp * nsplit + s) * kHq + h;
-      const float ms = part_ml[base * 2];
-      if (ms == -INFINITY) continue;
-      const float wgt = exp2f(ms - M);
-      L += part_ml[base * 2 + 1] * wgt;
-      const float4* src = reinterpret_cast<const float4*>(part_o + base * kDVal) + lane;
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+      float wgt[4];
+      float4 v[4][2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float4 v = src[64 * j];
-        acc[4 * j + 0] = fmaf(v.x, wgt, acc[4 * j + 0]);
-        acc[4 * j + 1] = fmaf(v.y, wgt, acc[4 * j + 1]);
-        acc[4 * j + 2] = fmaf(v.z, wgt, acc[4 * j + 2]);
-        acc[4 * j + 3] = fmaf(v.w, wgt, acc[4 * j + 3]);
+      for (int u = 0; u < 4; ++u) {
+        const int sidx = s0 + u;
+        wgt[u] = 0.f;
+        v[u][0] = v[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (sidx < nsplit) {
+          const size_t base = ((size_t)bp * nsplit + sidx) * kHq + h;
+          const float ms = part_ml[base * 2];
+          if (ms != -INFINITY) {
+            wgt[u] = exp2f(ms - M);
+            L += part_ml[base * 2 + 1] * wgt[u];
+            const float4* src = reinterpret_cast<const float4*>(part_o + base * kDVal) + lane;
+            v[u][0] = src[0];
+            v[u][1] = src[64];
+          }
+        }
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[4 * j + 0] = fmaf(v[u][j].x, wgt[u], acc[4 * j + 0]);
+          acc[4 * j + 1] = fmaf(v[u][j].y, wgt[u], acc[4 * j + 1]);
+          acc[4 * j + 2] = fmaf(v[u][j].z, wgt[u], acc[4 * j + 2]);
+          acc[4 * j + 3] = fmaf(v[u][j].w, wgt[u], acc[4 * j + 3]);
+        }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -326,7 +374,7 @@ __host__ inline int rows_per_split_for(int K, int nsplit) {
 int mla_num_splits(int B, int P, int K) {
   const int BP = B * P;
   const int max_split = (K + kTile - 1) / kTile;
-  int ns = (256 + BP - 1) / BP;
+  int ns = (kMlaTargetWGs + BP - 1) / BP;
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
   const int rps = rows_per_split_for(K, ns);
