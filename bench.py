@@ -36,10 +36,10 @@ KV_ROW = 576
 # rocprofv3 --pmc runs (FETCH_SIZE x 2 + WRITE_SIZE x 1, factors calibrated with a
 # 512 MiB read and a 512 MiB fill in the same runs; profiles/indexer_mixed_128k_pmc.txt).
 # Reported only while the kernel's sources are the ones the counters were taken on.
-INDEXER_TRAFFIC = {"workload": "mixed_128k", "bytes": 579.95e6,
+INDEXER_TRAFFIC = {"workload": "mixed_128k", "bytes": 579.70e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
-                   "sha256": "096c9be35c6aa0da9b4c461080d3c5c0a2aafa9ec4941fc79daa7f12dae9e556"}
+                   "sha256": "22053c09bb56af732acc54b80c093a87502e4b6164f72644b5d6cdeca94fc244"}
 
 
 def _indexer_traffic(workload: str):
