@@ -98,6 +98,27 @@ def test_mixed_small_faults_hits_evictions():
     assert np.all(c[:, 2] > 0) and np.all(c[:, 3] == c[:, 2])   # full buffers: every fault evicts
 
 
+def test_maximum_sizes_k8192_hot16384():
+    """The largest supported selection and hot buffer: K = 8192 (P*K = 8192
+    entries per request in resolve) with C = 2K = 16384 hot rows (16 slots per
+    resolve thread), rows of 40960 tokens."""
+    _say("mixed K=8192 C=16384")
+    wl = _mixed_small(B=2, T=40960, K=8192, tail=1024)
+    assert wl.C == 16384 and wl.K == 8192
+    ds = _run(wl)
+    new, rr, info = gc.full_check(ds, wl, gc.oracle_state(wl), attn_tol=2e-2)
+    _say(info)
+    assert np.all(info["counts"][:, 2] > 0)
+
+
+def test_single_row_selection_k1():
+    """K = 1: the best token alone; attention over one row returns that row."""
+    _say("tiny_fp32 K=1")
+    wl = gen.tiny_fp32(K=1)
+    ds = _run(wl)
+    gc.full_check(ds, wl, gc.oracle_state(wl), attn_tol=1e-5)
+
+
 def test_mtp3_small_multi_step():
     _say("mtp3 small, 3 steps")
     wl = gen.mtp3_agentic(B=3, K=128, steps=3, first_turn=6000, per_turn=300, turns=5, out_max=50)
