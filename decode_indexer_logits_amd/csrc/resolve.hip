@@ -16,11 +16,11 @@
 //                 many stamps);
 //              4. fault i takes victim i: evict, insert, stamp, record;
 //              5. row ids of every (position, k) from the updated tables.
-//   fault copy a small persistent grid strides over every (request, fault,
-//              layer, 16-byte chunk): each 576-value row is read straight
-//              from pinned host memory (zero-copy) and written to its slot's
-//              pool row in every layer, with its scale; it also advances the
-//              step counter.
+//   fault copy a persistent grid takes the faults in small batches, a few
+//              requests at a time: each 576-value row is read straight from
+//              pinned host memory (zero-copy) and written to its slot's pool
+//              row in every layer, with its scale; it also advances the step
+//              counter.
 #include "hs_common.h"
 #include "hs_launch.h"
 
@@ -32,7 +32,7 @@ constexpr int kMaxSel = 8192;   // P*K
 constexpr int kCopyNT = 256;
 constexpr int kCopyWGs = 256;
 constexpr int kCopyInFlight = 4;
-constexpr int kCopyBatch = 32;       // faults resolved per workgroup round
+constexpr int kCopyBatch = 8;        // faults per workgroup batch
 constexpr int kCopyMaxL = 16;
 constexpr int kMaxSlotsPerThread = 16;   // C <= 16384
 constexpr int kMaxStampRounds = 32;
@@ -477,71 +477,102 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
 }
 
 // Fault copies.  Zero-copy reads of pinned host memory are bound by the host
-// link, and its rate depends on the bytes in flight, not on the number of
-// waves: a persistent grid of kCopyWGs workgroups reaches the link rate while
-// leaving most CUs to kernels that run concurrently on other streams.  Each
-// request's faults are cut into batches of kCopyBatch; batches are dealt to
-// workgroups round-robin in request order.  A workgroup resolves a batch's
-// source and destination rows once into LDS, then streams its 16-byte chunks
-// with U independent loads per thread.
-template <int NT, int U>
+// link and, for rows scattered over gigabytes of 4-KiB host pages, by the
+// GPU's address translation: random rows inside a 75 MB window stream at the
+// link rate, the same rows spread over 2.4 GB lose about 12 %.  So the grid
+// keeps few requests in flight: each request's faults are cut into small
+// batches (BATCH faults) dealt to the persistent workgroups round-robin in
+// request order, so that the batches in flight at any time come from about
+// grid x BATCH / faults-per-request requests.  A workgroup pipelines its
+// batches: while the host reads of one batch are in flight, the source and
+// destination rows of its next batch are looked up into the other LDS buffer.
+template <int BATCH>
+struct CopyCursor {
+  int b, j, gbb;   // request, batch within it, batches of earlier requests
+
+  // Advances to this workgroup's next batch; false when there is none.
+  __device__ bool next(int B, const int32_t* __restrict__ counts, int grid, int me) {
+    j += grid;
+    while (b < B) {
+      const int nb = (counts[b * 4 + 2] + BATCH - 1) / BATCH;
+      if (j < nb) return true;
+      gbb += nb;
+      ++b;
+      j = me - gbb % grid;
+      if (j < 0) j += grid;
+    }
+    return false;
+  }
+};
+
+template <int NT, int U, int BATCH>
 __global__ __launch_bounds__(NT) void fault_copy_kernel(
     int B, int PK, int C, int L, int row_bytes, int max_blocks, const int32_t* __restrict__ faults,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ hot_blocks,
     const int64_t* __restrict__ host_bt, const uint8_t* __restrict__ host_rows,
     const float* __restrict__ host_scale, int64_t host_layer_rows, uint8_t* __restrict__ pool,
     float* __restrict__ row_scale, int64_t pool_layer_rows, int32_t* __restrict__ step) {
-  __shared__ int64_t s_src[kCopyBatch * kCopyMaxL];
-  __shared__ int64_t s_dst[kCopyBatch * kCopyMaxL];
+  __shared__ int64_t s_src[2][BATCH * kCopyMaxL];
+  __shared__ int64_t s_dst[2][BATCH * kCopyMaxL];
+  __shared__ int s_n[2];
   if (blockIdx.x == 0 && threadIdx.x == 0) step[0] = step[0] + 1;
   const int cpr = row_bytes / 16;           // 16-byte chunks per row
-  int gb = 0;                               // batches dealt so far
-  for (int b = 0; b < B; ++b) {
-    const int n = counts[b * 4 + 2];
-    const int nb = (n + kCopyBatch - 1) / kCopyBatch;
-    int j = (int)blockIdx.x - gb % (int)gridDim.x;
-    if (j < 0) j += gridDim.x;
-    gb += nb;
-    for (; j < nb; j += gridDim.x) {
-      const int f0 = j * kCopyBatch;
-      const int nloc = min(kCopyBatch, n - f0);
-      // one (fault, layer) per thread: source and destination byte offsets
-      for (int i = threadIdx.x; i < nloc * L; i += NT) {
-        const int fi = f0 + i / L, l = i % L;
-        const int32_t* fb = faults + ((size_t)b * PK + fi) * 2;
-        const int t = fb[0], sl = fb[1];
-        const int64_t hr = host_bt[(size_t)b * max_blocks + (t >> 6)] + (t & 63);
-        const int64_t pr =
-            (int64_t)hot_blocks[(size_t)b * (C >> 6) + (sl >> 6)] * kBlock + (sl & 63);
-        s_src[i] = ((int64_t)l * host_layer_rows + hr) * row_bytes;
-        s_dst[i] = ((int64_t)l * pool_layer_rows + pr) * row_bytes;
-        if (host_scale)
-          row_scale[(size_t)l * pool_layer_rows + pr] = host_scale[(size_t)l * host_layer_rows + hr];
-      }
-      __syncthreads();
-      const int nchunk = nloc * L * cpr;
-      for (int c0 = 0; c0 < nchunk; c0 += NT * U) {
-        uint4 v[U];
-        int64_t d[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int idx = c0 + u * NT + (int)threadIdx.x;
-          uint4 x = make_uint4(0u, 0u, 0u, 0u);
-          int64_t dd = -1;
-          if (idx < nchunk) {
-            const int row = idx / cpr, c = idx - row * cpr;
-            x = *reinterpret_cast<const uint4*>(host_rows + s_src[row] + (int64_t)c * 16);
-            dd = s_dst[row] + (int64_t)c * 16;
-          }
-          v[u] = x;
-          d[u] = dd;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (d[u] >= 0) *reinterpret_cast<uint4*>(pool + d[u]) = v[u];
-      }
-      __syncthreads();
+  const int grid = gridDim.x, me = blockIdx.x;
+  // source and destination byte offsets of one batch, one (fault, layer) per thread
+  auto lookup = [&](const CopyCursor<BATCH>& cu, int buf) {
+    const int n = counts[cu.b * 4 + 2];
+    const int f0 = cu.j * BATCH;
+    const int nloc = min(BATCH, n - f0);
+    if (threadIdx.x == 0) s_n[buf] = nloc;
+    for (int i = threadIdx.x; i < nloc * L; i += NT) {
+      const int fi = f0 + i / L, l = i % L;
+      const int32_t* fb = faults + ((size_t)cu.b * PK + fi) * 2;
+      const int t = fb[0], sl = fb[1];
+      const int64_t hr = host_bt[(size_t)cu.b * max_blocks + (t >> 6)] + (t & 63);
+      const int64_t pr =
+          (int64_t)hot_blocks[(size_t)cu.b * (C >> 6) + (sl >> 6)] * kBlock + (sl & 63);
+      s_src[buf][i] = ((int64_t)l * host_layer_rows + hr) * row_bytes;
+      s_dst[buf][i] = ((int64_t)l * pool_layer_rows + pr) * row_bytes;
+      if (host_scale)
+        row_scale[(size_t)l * pool_layer_rows + pr] = host_scale[(size_t)l * host_layer_rows + hr];
     }
+  };
+  CopyCursor<BATCH> cur{0, me - grid, 0};
+  bool have = cur.next(B, counts, grid, me);
+  if (have) lookup(cur, 0);
+  __syncthreads();
+  int buf = 0;
+  while (have) {
+    CopyCursor<BATCH> nxt = cur;
+    const bool have_next = nxt.next(B, counts, grid, me);
+    const int nchunk = s_n[buf] * L * cpr;
+    for (int c0 = 0; c0 < nchunk; c0 += NT * U) {
+      uint4 v[U];
+      int64_t d[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = c0 + u * NT + (int)threadIdx.x;
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        int64_t dd = -1;
+        if (idx < nchunk) {
+          const int row = idx / cpr, c = idx - row * cpr;
+          x = *reinterpret_cast<const uint4*>(host_rows + s_src[buf][row] + (int64_t)c * 16);
+          dd = s_dst[buf][row] + (int64_t)c * 16;
+        }
+        v[u] = x;
+        d[u] = dd;
+      }
+      // the next batch's lookups go out while these host reads are in flight
+      if (c0 == 0 && have_next) lookup(nxt, buf ^ 1);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (d[u] >= 0) *reinterpret_cast<uint4*>(pool + d[u]) = v[u];
+    }
+    if (nchunk == 0 && have_next) lookup(nxt, buf ^ 1);
+    __syncthreads();
+    cur = nxt;
+    have = have_next;
+    buf ^= 1;
   }
 }
 
@@ -562,7 +593,7 @@ hipError_t launch_fault_copy(const BatchDims& d, int K, const ResidencyArgs& r,
   const int PK = d.P * K;
   const int row_bytes = kDLat * r.kv_bytes;
   const int grid = workgroups > 0 ? workgroups : kCopyWGs;
-  hipLaunchKernelGGL((fault_copy_kernel<kCopyNT, kCopyInFlight>), dim3(grid), dim3(kCopyNT), 0, s, d.B, PK, r.C, r.L,
+  hipLaunchKernelGGL((fault_copy_kernel<kCopyNT, kCopyInFlight, kCopyBatch>), dim3(grid), dim3(kCopyNT), 0, s, d.B, PK, r.C, r.L,
                      row_bytes, d.max_blocks, faults, counts, r.hot_blocks, r.host_bt,
                      static_cast<const uint8_t*>(r.host_rows), r.host_scale, r.host_layer_rows,
                      static_cast<uint8_t*>(r.pool), r.row_scale, r.pool_layer_rows, r.step);
