@@ -56,7 +56,8 @@ def _indexer_traffic(workload: str):
 
 
 def _algorithmic_bytes(wl, counts):
-    """Bytes the method itself must move per step, by stage."""
+    """Bytes the method itself must move per step, by stage: what each kernel has to read
+    or write at least once, whatever its tiling."""
     B, P, K, L = wl.B, wl.P, wl.K, wl.L
     tok = int(wl.ctx_len.sum())
     nblk = sum(-(-int(t) // 64) for t in wl.ctx_len)

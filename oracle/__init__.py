@@ -20,8 +20,9 @@ The method is described on four web pages (cited by title and section):
   on its own and that hot buffers share the one block pool.
 
 The pages fix the mechanism but not the formulas.  Where they are silent the
-oracle takes one stated reading (listed in the design doc together with the pin
-that fixes each function):
+oracle takes one stated reading, written in the docstring of the function
+that applies it; the tests under ``tests/test_oracle_*.py`` pin each function
+to something other than itself:
 
 * ``numerics``  -- OCP FP8 E4M3FN decode table, bf16 decode.
 * ``indexer``   -- S[b,p,t] = sum_h w[b,p,h] * ReLU(q[b,p,h,:] . k[b,t,:]) + bias.
