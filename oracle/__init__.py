@@ -26,6 +26,8 @@ to something other than itself:
 
 * ``numerics``  -- OCP FP8 E4M3FN decode table, bf16 decode.
 * ``indexer``   -- S[b,p,t] = sum_h w[b,p,h] * ReLU(q[b,p,h,:] . k[b,t,:]) + bias.
+* ``quant``     -- optional E4M3 queries for the indexer: per-head absmax scale
+  to 448, binary32 rounding to the nearest code, scale folded into w.
 * ``topk``      -- K largest scores, ties to the lower token, ascending output.
 * ``resolve``   -- the residency state machine (resident / hot hit with LRU
   refresh / single-row fault from host).
