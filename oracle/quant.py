@@ -9,14 +9,16 @@ queries are also E4M3, so that the q.k contraction runs with both operands in
 FP8.  The rule, per (request, position, head) vector q[0..D-1] of bf16 values:
 
     amax  = max_d |q[d]|                                      (exact)
-    if amax == 0:  codes = 0, s = 0
+    if amax < 2^-64:  codes = 0, s = 0                        (zero or negligible head)
     else:          inv   = fl32(448 / amax)                   (binary32 division)
                    x[d]  = fl32(q[d] * inv)                   (binary32 product)
                    codes = nearest E4M3FN value to x[d], ties to the even code
                    s     = fl32(amax / 448)
     w_scaled[h] = fl32(w[h] * s)
 
-fl32 is IEEE binary32 round-to-nearest-even.  Every step that decides a code
+fl32 is IEEE binary32 round-to-nearest-even.  The 2^-64 floor keeps 448/amax
+finite (bf16 reaches down to 2^-133); a head that small adds at most
+128 * 2^-64 * |k| * |w| to a score.  Every step that decides a code
 is a binary32 operation, so a binary32 implementation reproduces the codes
 exactly.  Because s >= 0, the scale leaves the ReLU:
 w * ReLU((s * q8) . k) = (w * s) * ReLU(q8 . k).  The quantized indexer is
@@ -73,7 +75,7 @@ def quantize_queries(q_bits, w):
     q = decode_bf16(q_bits).astype(np.float32)          # exact: bf16 is a binary32 prefix
     w = np.asarray(w, dtype=np.float32)
     amax = np.abs(q).max(axis=-1)                        # [..., H]
-    nz = amax > 0
+    nz = amax >= np.float32(2.0 ** -64)
     safe = np.where(nz, amax, np.float32(1.0))
     inv = (np.float32(E4M3_MAX) / safe).astype(np.float32)
     x = (q * inv[..., None]).astype(np.float32)
