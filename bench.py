@@ -36,17 +36,17 @@ KV_ROW = 576
 # rocprofv3 --pmc runs (FETCH_SIZE x 2 + WRITE_SIZE x 1, factors calibrated with a
 # 512 MiB read and a 512 MiB fill in the same runs; profiles/indexer_mixed_128k_pmc.txt).
 # Reported only while the kernel's sources are the ones the counters were taken on.
-INDEXER_TRAFFIC = {"workload": "mixed_128k", "bytes": 579.70e6,
+INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 579.70e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
                    "sha256": "22053c09bb56af732acc54b80c093a87502e4b6164f72644b5d6cdeca94fc244"}
 
 
-def _indexer_traffic(workload: str):
+def _indexer_traffic(workload: str, indexer_q: str):
     """Counter-measured HBM bytes per indexer launch, or None if the sources changed
-    since the counters were taken or the workload differs."""
+    since the counters were taken or the workload or query type differs."""
     import hashlib
-    if workload != INDEXER_TRAFFIC["workload"]:
+    if workload != INDEXER_TRAFFIC["workload"] or indexer_q != INDEXER_TRAFFIC["indexer_q"]:
         return None
     h = hashlib.sha256()
     for f in INDEXER_TRAFFIC["sources"]:
@@ -112,10 +112,10 @@ def _time_launches(fn, n, torch, restore=None, flush=None):
     return sum(ms) / len(ms), ms
 
 
-def cpu_baseline(wl, n_req: int):
+def cpu_baseline(wl, n_req: int, indexer_q: str = "bf16"):
     """Time the oracle's full decode step on a sample of the batch (host cores)."""
     import numpy as np
-    from oracle import indexer as oi, topk as ot, resolve as orr, attention as oa
+    from oracle import indexer as oi, topk as ot, resolve as orr, attention as oa, quant as oq
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -125,7 +125,11 @@ def cpu_baseline(wl, n_req: int):
     n_req = min(n_req, wl.B)
     sel_b = list(range(n_req))
     t0 = time.perf_counter()
-    S = oi.indexer_scores(q_idx[sel_b], wl.q_dtype, wl.w[sel_b], wl.idx_pool, wl.k_dtype,
+    qi, qt, w = q_idx[sel_b], wl.q_dtype, wl.w[sel_b]
+    if indexer_q == "e4m3":
+        qi, w, _ = oq.quantize_queries(qi, w)
+        qt = "e4m3"
+    S = oi.indexer_scores(qi, qt, w, wl.idx_pool, wl.k_dtype,
                           wl.idx_scale, wl.idx_bt[sel_b], wl.ctx_len[sel_b],
                           None if wl.bias is None else wl.bias[sel_b], T_stride=wl.T_stride)
     tk = ot.topk(S, wl.ctx_len[sel_b], wl.K)
@@ -158,6 +162,9 @@ def main():
                     help="request chunks of the pipelined step (1 = one stream, no overlap)")
     ap.add_argument("--copy-wgs", type=int, default=32,
                     help="workgroups of the fault copy in the pipelined step")
+    ap.add_argument("--indexer-q", choices=("bf16", "e4m3"), default="bf16",
+                    help="indexer query type: the bf16 queries, or E4M3 codes quantized per "
+                         "head every step (fp8 x fp8 matrix cores)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path does not "
@@ -175,7 +182,8 @@ def main():
     t0 = time.time()
     wl = gen.by_name(a.workload)
     log(f"[bench] workload {wl.name} generated in {time.time() - t0:.1f}s")
-    ds = DeviceStep(wl)
+    ds = DeviceStep(wl, indexer_q=a.indexer_q if a.indexer_q == "e4m3" else None)
+    e4m3 = ds.indexer_q == "e4m3"
     snap = ds.snapshot()
     # MALL flush by reading 512 MB: a read leaves clean lines, so the timed step
     # does not pay for write-backs of flush data (a 512 MB fill would)
@@ -242,7 +250,12 @@ def main():
     log(f"[bench] single-stream step {single_ms:.4f} ms")
     # ---- per-stage kernel timings (eager launches, same stream)
     stage_ms = {}
-    stage_ms["indexer"], _ = _time_launches(ds.run_indexer, a.kernel_reps, torch, None, flush)
+    if e4m3:
+        stage_ms["quantize"], _ = _time_launches(ds.run_quantize, a.kernel_reps, torch, None,
+                                                 flush)
+    # the indexer kernel alone (E4M3 codes of the last quantization reused)
+    stage_ms["indexer"], _ = _time_launches(lambda: ds.run_indexer(quantize=False),
+                                            a.kernel_reps, torch, None, flush)
     stage_ms["topk"], _ = _time_launches(ds.run_topk, a.kernel_reps, torch, None, flush)
     stage_ms["indexer_topk"], _ = _time_launches(ds.run_indexer_topk, a.kernel_reps, torch, None,
                                                  flush)
@@ -266,7 +279,7 @@ def main():
     hbm_phase_s = (stage_ms["indexer_topk"] + stage_ms["resolve_tables"]
                    + stage_ms["attention"]) / 1e3
     link_gbs = alg["host_link"] / (stage_ms["fault_copy"] / 1e3) / 1e9
-    traffic = _indexer_traffic(wl.name)
+    traffic = _indexer_traffic(wl.name, ds.indexer_q)
     p10, p90 = ms_sorted[len(ms) // 10], ms_sorted[min(len(ms) - 1, (len(ms) * 9) // 10)]
     result = {
         "metric": "sparse-MLA decode steps/s + achieved HBM GB/s, 128K ctx, K=2048, 1 GPU",
@@ -281,16 +294,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "dtype_note": "bf16 queries x e4m3 latent/keys on bf16 matrix cores, fp32 accumulation",
+        "dtype": "e4m3/bf16" if e4m3 else "bf16",
+        "dtype_note": ("indexer: e4m3 queries (quantized per head each step) x e4m3 keys on "
+                       "fp8 matrix cores; attention: bf16 queries x e4m3 latent on bf16 matrix "
+                       "cores; fp32 accumulation" if e4m3 else
+                       "bf16 queries x e4m3 latent/keys on bf16 matrix cores, fp32 accumulation"),
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "ctx": int(wl.ctx_len.max()), "top_k": wl.K,
                    "query_heads": wl.Hq, "indexer_heads": wl.H_idx, "indexer_dim": wl.D_idx,
                    "layers": wl.L, "positions": wl.P, "hot_rows": wl.C,
                    "resident_tail_tokens": 4096 if wl.name == "mixed_128k" else None,
+                   "indexer_queries": ds.indexer_q,
                    "graph": not a.no_graph, "pipeline_chunks": a.chunks,
                    "pipeline_copy_workgroups": a.copy_wgs if a.chunks > 1 else None},
-        "roofline": {"bound": "hbm", "kernel": "indexer_bf16_e4m3",
+        "roofline": {"bound": "hbm",
+                     "kernel": "indexer_e4m3_kernel" if e4m3 else "indexer_bf16_e4m3_kernel",
                      "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE)",
@@ -318,7 +336,7 @@ def main():
     }
     if not a.no_cpu_baseline:
         log("[bench] timing the oracle on host cores")
-        cb = cpu_baseline(wl, a.cpu_requests)
+        cb = cpu_baseline(wl, a.cpu_requests, ds.indexer_q)
         cb["value"] = round(cb["value"], 5)
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)

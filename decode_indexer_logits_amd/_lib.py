@@ -20,7 +20,7 @@ DTYPES = {"f32": HS_F32, "bf16": HS_BF16, "e4m3": HS_E4M3}
 HS_OP_INDEXER, HS_OP_TOPK, HS_OP_RESOLVE, HS_OP_MLA = 0, 1, 2, 3
 DEVERR_VICTIMS, DEVERR_NO_HOST = 1, 2
 
-EXPORTS = ["hs_indexer_scores", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
+EXPORTS = ["hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
            "hs_sparse_mla_decode", "hs_workspace_bytes", "hs_host_device_ptr", "hs_last_error",
            "hs_abi_version"]
 
@@ -59,6 +59,7 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(str(LIB_PATH))
     P = c_void_p
     lib.hs_indexer_scores.argtypes = [P, c_int32, c_int32, c_int32, P, P, c_int32, P, P, P, P, P, P]
+    lib.hs_quantize_queries.argtypes = [P, c_int32, c_int32, P, P, P, P, P]
     lib.hs_topk.argtypes = [P, c_int32, P, P, P, c_size_t, P]
     lib.hs_indexer_topk.argtypes = [P, c_int32, c_int32, c_int32, P, P, c_int32, P, P, P, P, P,
                                     c_int32, P, P, c_size_t, P]
@@ -67,7 +68,7 @@ def load() -> ctypes.CDLL:
     lib.hs_copy_faults.argtypes = [P, c_int32, P, P, P, c_int32, P]
     lib.hs_sparse_mla_decode.argtypes = [P, c_int32, c_int32, c_int32, P, c_int32, P, P, P,
                                          c_float, P, P, P, c_size_t, P]
-    for f in ("hs_indexer_scores", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables",
+    for f in ("hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables",
               "hs_copy_faults", "hs_sparse_mla_decode", "hs_host_device_ptr"):
         getattr(lib, f).restype = c_int32
     lib.hs_workspace_bytes.argtypes = [c_int32] * 6
@@ -122,6 +123,11 @@ def indexer_scores(batch: Batch, H: int, D: int, q_t: str, q_idx, w, k_t: str, i
     _check(load().hs_indexer_scores(ctypes.byref(batch), H, D, DTYPES[q_t], _ptr(q_idx), _ptr(w),
                                     DTYPES[k_t], _ptr(idx_pool), _ptr(idx_scale), _ptr(idx_bt),
                                     _ptr(bias), _ptr(scores), _stream(stream)))
+
+
+def quantize_queries(batch: Batch, H: int, D: int, q_idx, w, q8, w_scaled, stream=None):
+    _check(load().hs_quantize_queries(ctypes.byref(batch), H, D, _ptr(q_idx), _ptr(w), _ptr(q8),
+                                      _ptr(w_scaled), _stream(stream)))
 
 
 def topk(batch: Batch, K: int, scores, out, ws, stream=None):

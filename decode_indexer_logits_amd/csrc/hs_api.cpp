@@ -50,13 +50,9 @@ hs_status launched(hipError_t e, const char* what) {
 
 }  // namespace
 
-extern "C" {
-
-}  // extern "C"
-
 namespace {
 
-enum class IdxPath { kBf16E4m3, kF32 };
+enum class IdxPath { kBf16E4m3, kE4m3E4m3, kF32 };
 
 hs_status check_indexer(const hs::BatchDims& d, int32_t H_idx, int32_t D_idx, hs_dtype q_t,
                         const void* q_idx, const float* w, hs_dtype k_t, const void* idx_pool,
@@ -68,10 +64,19 @@ hs_status check_indexer(const hs::BatchDims& d, int32_t H_idx, int32_t D_idx, hs
   if (D_idx != 64 && D_idx != 128) return fail(HS_ERR_SHAPE, "D_idx=%d must be 64 or 128", D_idx);
   if (!aligned16(q_idx) || !aligned16(idx_pool) || !aligned16(scores))
     return fail(HS_ERR_ALIGN, "indexer: q_idx, idx_pool and scores need 16-byte alignment");
+  if (q_t != HS_F32 && !aligned16(w))
+    return fail(HS_ERR_ALIGN, "indexer: w needs 16-byte alignment on the matrix-core paths");
   if (q_t == HS_BF16 && k_t == HS_E4M3) {
     if (H_idx < 16 || H_idx > 64 || H_idx % 16)
       return fail(HS_ERR_SHAPE, "H_idx=%d must be 16, 32, 48 or 64 on the bf16/e4m3 path", H_idx);
     *path = IdxPath::kBf16E4m3;
+    return HS_OK;
+  }
+  if (q_t == HS_E4M3 && k_t == HS_E4M3) {
+    if (D_idx != 128) return fail(HS_ERR_SHAPE, "D_idx=%d must be 128 on the e4m3/e4m3 path", D_idx);
+    if (H_idx < 16 || H_idx > 64 || H_idx % 16)
+      return fail(HS_ERR_SHAPE, "H_idx=%d must be 16, 32, 48 or 64 on the e4m3/e4m3 path", H_idx);
+    *path = IdxPath::kE4m3E4m3;
     return HS_OK;
   }
   if (q_t == HS_F32 && k_t == HS_F32) {
@@ -80,7 +85,7 @@ hs_status check_indexer(const hs::BatchDims& d, int32_t H_idx, int32_t D_idx, hs
     *path = IdxPath::kF32;
     return HS_OK;
   }
-  return fail(HS_ERR_DTYPE, "indexer supports (q, k) = (BF16, E4M3) or (F32, F32)");
+  return fail(HS_ERR_DTYPE, "indexer supports (q, k) = (BF16, E4M3), (E4M3, E4M3) or (F32, F32)");
 }
 
 hipError_t launch_indexer(const hs::BatchDims& d, IdxPath path, int32_t H_idx, int32_t D_idx,
@@ -91,6 +96,10 @@ hipError_t launch_indexer(const hs::BatchDims& d, IdxPath path, int32_t H_idx, i
     return hs::launch_indexer_bf16_e4m3(d, H_idx, D_idx, static_cast<const uint16_t*>(q_idx), w,
                                         static_cast<const uint8_t*>(idx_pool), idx_scale, idx_bt,
                                         bias, scores, hist, s);
+  if (path == IdxPath::kE4m3E4m3)
+    return hs::launch_indexer_e4m3(d, H_idx, static_cast<const uint8_t*>(q_idx), w,
+                                   static_cast<const uint8_t*>(idx_pool), idx_scale, idx_bt,
+                                   bias, scores, hist, s);
   return hs::launch_indexer_f32(d, H_idx, D_idx, static_cast<const float*>(q_idx), w,
                                 static_cast<const float*>(idx_pool), idx_bt, bias, scores, s);
 }
@@ -122,6 +131,23 @@ hs_status hs_indexer_scores(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
   return launched(launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt,
                                  bias, scores, nullptr, static_cast<hipStream_t>(stream)),
                   "indexer");
+}
+
+hs_status hs_quantize_queries(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
+                              const void* q_idx, const float* w, uint8_t* q8, float* w_scaled,
+                              void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!q_idx || !w || !q8 || !w_scaled)
+    return fail(HS_ERR_NULL, "quantize: q_idx, w, q8 and w_scaled are required");
+  if (D_idx != 64 && D_idx != 128) return fail(HS_ERR_SHAPE, "D_idx=%d must be 64 or 128", D_idx);
+  if (H_idx < 1 || H_idx > 64) return fail(HS_ERR_SHAPE, "H_idx=%d out of [1, 64]", H_idx);
+  if ((reinterpret_cast<uintptr_t>(q_idx) & 3u) || (reinterpret_cast<uintptr_t>(q8) & 1u))
+    return fail(HS_ERR_ALIGN, "quantize: q_idx needs 4-byte and q8 2-byte alignment");
+  const int rows = d.B * d.P * H_idx;
+  return launched(hs::launch_quantize_queries(rows, D_idx, static_cast<const uint16_t*>(q_idx), w,
+                                              q8, w_scaled, static_cast<hipStream_t>(stream)),
+                  "quantize queries");
 }
 
 hs_status hs_indexer_topk(const hs_batch* batch, int32_t H_idx, int32_t D_idx, hs_dtype q_t,

@@ -57,6 +57,23 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+
+// 16x16x128 E4M3 x E4M3 matrix-core product with fp32 accumulation (the
+// f8f6f4 instruction with both operand formats E4M3 and no block scales):
+//   D[16x16] = A[16x128] * B[128x16] + C.
+// Lane l holds A[l%16][32*(l/16) .. +32] and B[32*(l/16) .. +32][l%16], byte
+// i of its eight dwords being contraction index 32*(l/16) + i; D as for the
+// 16x16x32 product.  Every product of two E4M3 values is exact in fp32.
+__device__ __forceinline__ f32x4_t mfma16x16x128_e4m3(i32x8_t a, i32x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x8_t as_i32x8(uint4 lo, uint4 hi) {
+  return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key);
 // -0.0 is folded onto +0.0 so that equal scores get equal keys.
 __device__ __forceinline__ uint32_t score_key(float s) {

@@ -19,6 +19,13 @@ hipError_t launch_indexer_bf16_e4m3(const BatchDims& d, int H, int DK, const uin
                                    const float* w, const uint8_t* pool, const float* scale,
                                    const int32_t* bt, const float* bias, float* scores,
                                    uint32_t* hist, hipStream_t s);
+// Indexer: E4M3 queries x E4M3 keys (D = 128) on the fp8 matrix cores.
+hipError_t launch_indexer_e4m3(const BatchDims& d, int H, const uint8_t* q8, const float* w,
+                               const uint8_t* pool, const float* scale, const int32_t* bt,
+                               const float* bias, float* scores, uint32_t* hist, hipStream_t s);
+// Per-head E4M3 quantization of `rows` bf16 query vectors of DK (64 or 128).
+hipError_t launch_quantize_queries(int rows, int DK, const uint16_t* q, const float* w,
+                                   uint8_t* q8, float* w_scaled, hipStream_t s);
 // Indexer: fp32 queries x fp32 keys on the vector ALUs.
 hipError_t launch_indexer_f32(const BatchDims& d, int H, int DK, const float* q, const float* w,
                               const float* pool, const int32_t* bt, const float* bias,

@@ -211,6 +211,7 @@ __global__ __launch_bounds__(256) void indexer_mp_kernel(
   constexpr int NV = DK / 64;
   constexpr int FR = 4 * KS;                 // B fragments per page (4 groups x KS k-steps)
   __shared__ bf16x8_t sk[2][FR][kWave];      // two converted pages
+  __shared__ float sbias[2][4][kWave];       // the two pages' token biases, per wave
   __shared__ uint32_t sh_hist[HIST ? P * 1024 : 1];
   const int b = blockIdx.y;
   const int T = ctx_len[b];
@@ -252,26 +253,39 @@ __global__ __launch_bounds__(256) void indexer_mp_kernel(
   float* out = scores + (size_t)(b * P + pq) * T_stride + tile0;
   const float* biasb = bias ? bias + (size_t)b * T_stride + tile0 : nullptr;
   const int lim_t = lim - tile0;
-  // raw keys of group `wave` of page pi: token 16*wave + n, bytes 16g + 64v
-  auto load_raw = [&](int pi, uint4* r) {
+  // Raw keys of group `wave` of page pi (token 16*wave + n, bytes 16g + 64v)
+  // and the bias of token 64*pi + lane, loaded together and without per-lane
+  // conditions: pages past the tile's end re-read the last page and the bias
+  // index is clamped to the request's last token (without a bias the load
+  // reads ctx_len[0] and the value is dropped), so that every wait in the
+  // loop is for the oldest page only.
+  const int lim_any_t = lim_any - tile0;
+  struct Raw { uint4 r[NV]; float bias; };
+  auto load_raw = [&](int pi) {
+    Raw x;
     const uint8_t* kp = pool + (size_t)page_blk(min(pi, npages - 1)) * kBlock * DK +
                         (16 * wave + n) * DK + 16 * g;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) r[v] = *reinterpret_cast<const uint4*>(kp + 64 * v);
+    for (int v = 0; v < NV; ++v) x.r[v] = *reinterpret_cast<const uint4*>(kp + 64 * v);
+    const float* bp = biasb ? biasb + min(pi * kBlock + lane, lim_any_t)
+                            : reinterpret_cast<const float*>(ctx_len);
+    x.bias = *bp;
+    return x;
   };
-  auto convert = [&](const uint4* r, int buf) {
+  auto convert = [&](const Raw& x, int buf) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const uint4 c = r[s >> 1];
+      const uint4 c = x.r[s >> 1];
       const uint32_t lo = (s & 1) ? c.z : c.x;
       const uint32_t hi = (s & 1) ? c.w : c.y;
       sk[buf][wave * KS + s][lane] = e4m3x8_to_bf16x8(lo, hi);
     }
+    sbias[buf][wave][lane] = x.bias;
   };
   auto compute = [&](int pi, int buf) {
     if (!active) return;
     const int tl = pi * kBlock + lane;
-    const float bs = (biasb && tl <= lim_t) ? biasb[tl] : 0.f;
+    const float bs = biasb ? sbias[buf][wave][lane] : 0.f;
     float vj[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -308,26 +322,27 @@ __global__ __launch_bounds__(256) void indexer_mp_kernel(
       }
     }
   };
-  // software pipeline: raw loads three pages ahead, conversion one page ahead
-  uint4 rA[NV], rB[NV], rC[NV];
-  load_raw(0, rA);
-  load_raw(1, rB);
-  load_raw(2, rC);
+  // Software pipeline: raw loads three pages ahead, conversion one page
+  // ahead.  Conversions and loads are unconditional (a page past the end is
+  // converted into the idle buffer and never read), so the loop has no
+  // per-page branch around memory operations.
+  Raw rA = load_raw(0), rB = load_raw(1), rC = load_raw(2);
   convert(rA, 0);
-  load_raw(3, rA);
+  rA = load_raw(3);
   __syncthreads();
   for (int k = 0; k < npages; k += 3) {
     // page k+1 from rB, k+2 from rC, k+3 from rA
-    if (k + 1 < npages) { convert(rB, (k + 1) & 1); load_raw(k + 4, rB); }
+    convert(rB, (k + 1) & 1);
+    rB = load_raw(k + 4);
     compute(k, k & 1);
     __syncthreads();
-    if (k + 1 >= npages) break;
-    if (k + 2 < npages) { convert(rC, (k + 2) & 1); load_raw(k + 5, rC); }
-    compute(k + 1, (k + 1) & 1);
+    convert(rC, (k + 2) & 1);
+    rC = load_raw(k + 5);
+    if (k + 1 < npages) compute(k + 1, (k + 1) & 1);
     __syncthreads();
-    if (k + 2 >= npages) break;
-    if (k + 3 < npages) { convert(rA, (k + 3) & 1); load_raw(k + 6, rA); }
-    compute(k + 2, (k + 2) & 1);
+    convert(rA, (k + 3) & 1);
+    rA = load_raw(k + 6);
+    if (k + 2 < npages) compute(k + 2, (k + 2) & 1);
     __syncthreads();
   }
   if (HIST) {
@@ -339,6 +354,306 @@ __global__ __launch_bounds__(256) void indexer_mp_kernel(
       if (x >> 16) atomicAdd(&hrow[bin + 1], x >> 16);
     }
   }
+}
+
+// E4M3 queries x E4M3 keys (D = 128; queries quantized per head by
+// quantize_queries_kernel, the per-head scale already folded into w).  One
+// 16x16x128 fp8 product covers 16 heads x 16 tokens over the whole key, and
+// the key bytes are the B operand as loaded: no conversion at all.  Lane
+// (n, g) holds contraction bytes 16g .. 16g+15 and 64+16g .. 64+16g+15 of
+// head n's query and of token n's key (the same permutation of the
+// contraction index in both operands), so each of its two 16-byte key loads
+// covers whole 64-byte halves of 16 key rows.
+// One position (P = 1): four waves split the tile's pages, each keeping the
+// queries in registers (HT x 8 dwords) with two pages in flight.  Several
+// positions use indexer_e4m3_mp_kernel below.
+template <int P, int HT, bool HIST>
+__global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
+    const int32_t* __restrict__ ctx_len, int T_stride, int max_blocks,
+    const uint8_t* __restrict__ q8, const float* __restrict__ w,
+    const uint8_t* __restrict__ pool, const float* __restrict__ scale,
+    const int32_t* __restrict__ bt, const float* __restrict__ bias,
+    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+  using Cfg = IdxCfg<P>;
+  constexpr int DK = 128;
+  constexpr int H = 16 * HT;
+  const int b = blockIdx.y;
+  const int T = ctx_len[b];
+  const int tile0 = blockIdx.x * Cfg::TILE;
+  if (tile0 >= T) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int p = wave / Cfg::WPP, sub = wave % Cfg::WPP;
+  const int lim = T - P + p;
+  __shared__ uint32_t sh_hist[HIST ? P * 2048 : 1];
+  __shared__ float4 sw4[P][H / 4];
+  if (HIST)
+    for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT) sh_hist[i] = 0;
+  const float* wp = w + (size_t)(b * P + p) * H;
+  if (sub == 0)
+    for (int i = lane; i < H / 4; i += kWave) sw4[p][i] = reinterpret_cast<const float4*>(wp)[i];
+  __syncthreads();
+
+  if (lim >= tile0) {
+  i32x8_t qa[HT];
+  const uint8_t* qp = q8 + (size_t)(b * P + p) * H * DK + 16 * g;
+#pragma unroll
+  for (int mt = 0; mt < HT; ++mt) {
+    const uint8_t* r = qp + (16 * mt + n) * DK;
+    qa[mt] = as_i32x8(*reinterpret_cast<const uint4*>(r), *reinterpret_cast<const uint4*>(r + 64));
+  }
+  const int npages = min(Cfg::TILE / kBlock, (lim - tile0) / kBlock + 1);
+  const int32_t* btb = bt + (size_t)b * max_blocks + tile0 / kBlock;
+  float* out = scores + (size_t)(b * P + p) * T_stride + tile0;
+  const float* biasb = bias ? bias + (size_t)b * T_stride + tile0 : nullptr;
+  const int lim_t = lim - tile0;
+  static_assert(Cfg::TILE / kBlock <= kWave, "one page per lane");
+  const int blk_l = lane < npages ? btb[lane] : 0;
+  const float sc_l = (scale && lane < npages) ? scale[blk_l] : 1.f;
+  auto page_blk = [&](int pi) { return __builtin_amdgcn_readlane(blk_l, pi); };
+  auto page_scale = [&](int pi) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
+  };
+  // token 16j + n of the page: bytes 16g .. +16 and 64 + 16g .. +16
+  auto load_page = [&](int pi, uint4* buf, float& bs) {
+    const uint8_t* kp = pool + (size_t)page_blk(pi) * kBlock * DK + n * DK + 16 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      buf[2 * j] = *reinterpret_cast<const uint4*>(kp + 16 * j * DK);
+      buf[2 * j + 1] = *reinterpret_cast<const uint4*>(kp + 16 * j * DK + 64);
+    }
+    const int tl = pi * kBlock + lane;
+    bs = (biasb && tl <= lim_t) ? biasb[tl] : 0.f;
+  };
+  auto consume_page = [&](int pi, const uint4* buf, float bs) {
+    f32x4_t acc[4][HT];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const i32x8_t kb = as_i32x8(buf[2 * j], buf[2 * j + 1]);
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt)
+        acc[j][mt] = mfma16x16x128_e4m3(qa[mt], kb, f32x4_t{0.f, 0.f, 0.f, 0.f});
+    }
+    float vj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt) {
+        const float4 wq = sw4[p][4 * mt + g];
+        v = fmaf(wq.x, relu_bits(acc[j][mt][0]), v);
+        v = fmaf(wq.y, relu_bits(acc[j][mt][1]), v);
+        v = fmaf(wq.z, relu_bits(acc[j][mt][2]), v);
+        v = fmaf(wq.w, relu_bits(acc[j][mt][3]), v);
+      }
+      vj[j] = sum_rows16(v);      // every lane of column n holds token 16j + n
+    }
+    const float mine = g == 0 ? vj[0] : (g == 1 ? vj[1] : (g == 2 ? vj[2] : vj[3]));
+    const int tl = pi * kBlock + lane;
+    if (tl <= lim_t) {
+      const float val = (scale ? mine * page_scale(pi) : mine) + bs;
+      out[tl] = val;
+      if (HIST) atomicAdd(&sh_hist[p * 2048 + (score_key(val) >> 21)], 1u);
+    }
+  };
+  constexpr int W = Cfg::WPP;
+  const int npw = (npages - sub + W - 1) / W;
+  auto page_of = [&](int k) { return min(sub + k * W, npages - 1); };
+  uint4 bufA[8], bufB[8];
+  float bsA, bsB;
+  load_page(page_of(0), bufA, bsA);
+  load_page(page_of(1), bufB, bsB);
+  for (int k = 0; k < npw; k += 2) {
+    consume_page(sub + k * W, bufA, bsA);
+    load_page(page_of(k + 2), bufA, bsA);
+    if (k + 1 < npw) consume_page(sub + (k + 1) * W, bufB, bsB);
+    load_page(page_of(k + 3), bufB, bsB);
+  }
+  }  // lim >= tile0
+  if (HIST) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT)
+      if (sh_hist[i]) atomicAdd(&hist[(size_t)(b * P + i / 2048) * 2048 + (i % 2048)], sh_hist[i]);
+  }
+}
+
+// E4M3 x E4M3 with several query positions (P = 2..4): every position reads
+// the same keys, so the workgroup loads each page once and shares the raw
+// bytes through LDS.  Wave w loads 16-token group w of a page (each lane the
+// 32 bytes that are its B operand) into one of two LDS page buffers while
+// the page before is multiplied; the waves of position p (4/P of them at
+// P = 2, one otherwise; at P = 3 wave 3 only loads) read every group back
+// and run their products.  One barrier per page; raw loads run three pages
+// ahead in registers.  The histogram epilogue packs two 16-bit bins per LDS
+// word (a position sees at most 4096 tokens of a tile).
+template <int P, int HT, bool HIST>
+__global__ __launch_bounds__(256) void indexer_e4m3_mp_kernel(
+    const int32_t* __restrict__ ctx_len, int T_stride, int max_blocks,
+    const uint8_t* __restrict__ q8, const float* __restrict__ w,
+    const uint8_t* __restrict__ pool, const float* __restrict__ scale,
+    const int32_t* __restrict__ bt, const float* __restrict__ bias,
+    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+  static_assert(P >= 2 && P <= 4, "multi-position kernel");
+  constexpr int TILE = 4096;
+  constexpr int DK = 128;
+  constexpr int WPP = (P == 2) ? 2 : 1;
+  constexpr int H = 16 * HT;
+  __shared__ uint4 sk[2][4][2][kWave];       // two pages: [group][half][lane]
+  __shared__ float sbias[2][4][kWave];       // the two pages' token biases, per wave
+  __shared__ uint32_t sh_hist[HIST ? P * 1024 : 1];
+  const int b = blockIdx.y;
+  const int T = ctx_len[b];
+  const int tile0 = blockIdx.x * TILE;
+  if (tile0 >= T) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int p = wave / WPP, sub = wave % WPP;
+  const bool active = p < P;
+  const int lim = T - P + (active ? p : P - 1);
+  const int lim_any = T - 1;
+  if (HIST)
+    for (int i = threadIdx.x; i < P * 1024; i += 256) sh_hist[i] = 0;
+  const int npages = min(TILE / kBlock, (lim_any - tile0) / kBlock + 1);
+  const int32_t* btb = bt + (size_t)b * max_blocks + tile0 / kBlock;
+  const int blk_l = lane < npages ? btb[lane] : 0;
+  const float sc_l = (scale && lane < npages) ? scale[blk_l] : 1.f;
+  auto page_blk = [&](int pi) { return __builtin_amdgcn_readlane(blk_l, pi); };
+  auto page_scale = [&](int pi) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
+  };
+  const int pq = active ? p : 0;
+  i32x8_t qa[HT];
+  float wv[HT][4];
+  {
+    const uint8_t* qp = q8 + (size_t)(b * P + pq) * H * DK + 16 * g;
+    const float* wp = w + (size_t)(b * P + pq) * H;
+#pragma unroll
+    for (int mt = 0; mt < HT; ++mt) {
+      const uint8_t* r = qp + (16 * mt + n) * DK;
+      qa[mt] = as_i32x8(*reinterpret_cast<const uint4*>(r), *reinterpret_cast<const uint4*>(r + 64));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[mt][i] = wp[16 * mt + 4 * g + i];
+    }
+  }
+  float* out = scores + (size_t)(b * P + pq) * T_stride + tile0;
+  const float* biasb = bias ? bias + (size_t)b * T_stride + tile0 : nullptr;
+  const int lim_t = lim - tile0;
+  // token 16*wave + n of page pi: key bytes 16g .. +16 and 64 + 16g .. +16,
+  // with the bias of token 64*pi + lane; no per-lane condition on any load
+  // (clamped page and bias index; without a bias the load reads ctx_len[0]
+  // and the value is dropped), so every wait in the loop is for the oldest
+  // page only.
+  const int lim_any_t = lim_any - tile0;
+  struct Raw { uint4 lo, hi; float bias; };
+  auto load_raw = [&](int pi) {
+    const uint8_t* kp = pool + (size_t)page_blk(min(pi, npages - 1)) * kBlock * DK +
+                        (16 * wave + n) * DK + 16 * g;
+    const float* bp = biasb ? biasb + min(pi * kBlock + lane, lim_any_t)
+                            : reinterpret_cast<const float*>(ctx_len);
+    return Raw{*reinterpret_cast<const uint4*>(kp), *reinterpret_cast<const uint4*>(kp + 64), *bp};
+  };
+  auto stash = [&](const Raw& r, int buf) {
+    sk[buf][wave][0][lane] = r.lo;
+    sk[buf][wave][1][lane] = r.hi;
+    sbias[buf][wave][lane] = r.bias;
+  };
+  auto compute = [&](int pi, int buf) {
+    if (!active) return;
+    const int tl = pi * kBlock + lane;
+    const float bs = biasb ? sbias[buf][wave][lane] : 0.f;
+    float vj[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j % WPP != sub) continue;
+      const i32x8_t kb = as_i32x8(sk[buf][j][0][lane], sk[buf][j][1][lane]);
+      f32x4_t acc[HT];
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt)
+        acc[mt] = mfma16x16x128_e4m3(qa[mt], kb, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      float v = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wv[mt][i], relu_bits(acc[mt][i]), v);
+      vj[j] = sum_rows16(v);
+    }
+    const float mine = g == 0 ? vj[0] : (g == 1 ? vj[1] : (g == 2 ? vj[2] : vj[3]));
+    if (g % WPP == sub && tl <= lim_t) {
+      const float val = (scale ? mine * page_scale(pi) : mine) + bs;
+      out[tl] = val;
+      if (HIST) {
+        const uint32_t bin = score_key(val) >> 21;
+        atomicAdd(&sh_hist[p * 1024 + (bin >> 1)], 1u << (16 * (bin & 1)));
+      }
+    }
+  };
+  // loads and stashes are unconditional (a page past the end lands in the
+  // idle buffer and is never read)
+  Raw rA = load_raw(0), rB = load_raw(1), rC = load_raw(2);
+  stash(rA, 0);
+  rA = load_raw(3);
+  __syncthreads();
+  for (int k = 0; k < npages; k += 3) {
+    stash(rB, (k + 1) & 1);
+    rB = load_raw(k + 4);
+    compute(k, k & 1);
+    __syncthreads();
+    stash(rC, (k + 2) & 1);
+    rC = load_raw(k + 5);
+    if (k + 1 < npages) compute(k + 1, (k + 1) & 1);
+    __syncthreads();
+    stash(rA, (k + 3) & 1);
+    rA = load_raw(k + 6);
+    if (k + 2 < npages) compute(k + 2, (k + 2) & 1);
+    __syncthreads();
+  }
+  if (HIST) {
+    for (int i = threadIdx.x; i < P * 1024; i += 256) {
+      const uint32_t x = sh_hist[i];
+      const int pos = i / 1024, bin = 2 * (i % 1024);
+      uint32_t* hrow = hist + (size_t)(b * P + pos) * 2048;
+      if (x & 0xFFFFu) atomicAdd(&hrow[bin], x & 0xFFFFu);
+      if (x >> 16) atomicAdd(&hrow[bin + 1], x >> 16);
+    }
+  }
+}
+
+// Per-head E4M3 quantization of bf16 indexer queries, one wave per
+// (request, position, head) row of DK values: amax by an integer max over the
+// magnitudes' bits, then binary32 inv = 448 / amax, x = q * inv, and the
+// hardware's round-to-nearest-even conversion to E4M3; rows with
+// amax < 2^-64 become zero.  w_scaled = w * (amax / 448).
+template <int DK>
+__global__ __launch_bounds__(256) void quantize_queries_kernel(
+    int rows, const uint16_t* __restrict__ q, const float* __restrict__ w,
+    uint8_t* __restrict__ q8, float* __restrict__ w_scaled) {
+  constexpr int PER = DK / kWave;   // 1 or 2 values per lane
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  float x[PER];
+  if (PER == 2) {
+    const uint32_t u = reinterpret_cast<const uint32_t*>(q + (size_t)row * DK)[lane];
+    x[0] = __uint_as_float(u << 16);
+    x[PER - 1] = __uint_as_float(u & 0xFFFF0000u);
+  } else {
+    x[0] = __uint_as_float((uint32_t)q[(size_t)row * DK + lane] << 16);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  m = wave_allreduce_u32(m, [](uint32_t a, uint32_t c) { return max(a, c); });
+  const float amax = __uint_as_float(m);
+  const bool live = amax >= 0x1p-64f;
+  const float inv = live ? 448.f / amax : 0.f;
+  if (PER == 2) {
+    const uint32_t c = live ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[PER - 1] * inv, 0, false) & 0xFFFFu : 0u;
+    reinterpret_cast<uint16_t*>(q8 + (size_t)row * DK)[lane] = (uint16_t)c;
+  } else {
+    const uint32_t c = live ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, 0.f, 0, false) & 0xFFu : 0u;
+    q8[(size_t)row * DK + lane] = (uint8_t)c;
+  }
+  if (lane == 0) w_scaled[row] = w[row] * (live ? amax / 448.f : 0.f);
 }
 
 // fp32 path (vector ALUs): one thread per (position, token).
@@ -441,6 +756,77 @@ hipError_t launch_indexer_bf16_e4m3(const BatchDims& d, int H, int DK, const uin
     case 4: return dispatch_dk<4>(DK, HT, d, q, w, pool, scale, bt, bias, scores, hist, s);
   }
   return hipErrorInvalidValue;
+}
+
+namespace {
+
+template <int P, int HT>
+hipError_t launch_e4m3_ht(const BatchDims& d, const uint8_t* q8, const float* w,
+                          const uint8_t* pool, const float* scale, const int32_t* bt,
+                          const float* bias, float* scores, uint32_t* hist, hipStream_t s) {
+  using Cfg = IdxCfg<P>;
+  dim3 grid((d.T_stride + Cfg::TILE - 1) / Cfg::TILE, d.B);
+  if (P > 1) {
+    constexpr int PM = P > 1 ? P : 2;
+    if (hist)
+      hipLaunchKernelGGL((indexer_e4m3_mp_kernel<PM, HT, true>), grid, dim3(256), 0, s,
+                         d.ctx_len, d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias,
+                         scores, hist);
+    else
+      hipLaunchKernelGGL((indexer_e4m3_mp_kernel<PM, HT, false>), grid, dim3(256), 0, s,
+                         d.ctx_len, d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias,
+                         scores, hist);
+    return hipGetLastError();
+  }
+  if (hist)
+    hipLaunchKernelGGL((indexer_e4m3_kernel<P, HT, true>), grid, dim3(Cfg::NT), 0, s, d.ctx_len,
+                       d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias, scores, hist);
+  else
+    hipLaunchKernelGGL((indexer_e4m3_kernel<P, HT, false>), grid, dim3(Cfg::NT), 0, s, d.ctx_len,
+                       d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias, scores, hist);
+  return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_e4m3_p(int HT, const BatchDims& d, const uint8_t* q8, const float* w,
+                         const uint8_t* pool, const float* scale, const int32_t* bt,
+                         const float* bias, float* scores, uint32_t* hist, hipStream_t s) {
+  switch (HT) {
+    case 1: return launch_e4m3_ht<P, 1>(d, q8, w, pool, scale, bt, bias, scores, hist, s);
+    case 2: return launch_e4m3_ht<P, 2>(d, q8, w, pool, scale, bt, bias, scores, hist, s);
+    case 3: return launch_e4m3_ht<P, 3>(d, q8, w, pool, scale, bt, bias, scores, hist, s);
+    case 4: return launch_e4m3_ht<P, 4>(d, q8, w, pool, scale, bt, bias, scores, hist, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_indexer_e4m3(const BatchDims& d, int H, const uint8_t* q8, const float* w,
+                               const uint8_t* pool, const float* scale, const int32_t* bt,
+                               const float* bias, float* scores, uint32_t* hist, hipStream_t s) {
+  const int HT = H / 16;
+  switch (d.P) {
+    case 1: return launch_e4m3_p<1>(HT, d, q8, w, pool, scale, bt, bias, scores, hist, s);
+    case 2: return launch_e4m3_p<2>(HT, d, q8, w, pool, scale, bt, bias, scores, hist, s);
+    case 3: return launch_e4m3_p<3>(HT, d, q8, w, pool, scale, bt, bias, scores, hist, s);
+    case 4: return launch_e4m3_p<4>(HT, d, q8, w, pool, scale, bt, bias, scores, hist, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize_queries(int rows, int DK, const uint16_t* q, const float* w,
+                                   uint8_t* q8, float* w_scaled, hipStream_t s) {
+  const dim3 grid((rows + 3) / 4);
+  if (DK == 64)
+    hipLaunchKernelGGL(quantize_queries_kernel<64>, grid, dim3(256), 0, s, rows, q, w, q8,
+                       w_scaled);
+  else if (DK == 128)
+    hipLaunchKernelGGL(quantize_queries_kernel<128>, grid, dim3(256), 0, s, rows, q, w, q8,
+                       w_scaled);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_indexer_f32(const BatchDims& d, int H, int DK, const float* q, const float* w,

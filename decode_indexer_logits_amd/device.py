@@ -38,7 +38,11 @@ def _dev(a, device, dtype_tag=None):
 class DeviceStep:
     """All device buffers of a workload, ready to run decode steps."""
 
-    def __init__(self, wl, device: str = "cuda:0", host_pool: bool = True):
+    def __init__(self, wl, device: str = "cuda:0", host_pool: bool = True,
+                 indexer_q: str | None = None):
+        """indexer_q: the indexer's query type, "bf16" (the workload's own
+        queries) or "e4m3" (quantized per head every step by
+        hs_quantize_queries before the indexer)."""
         torch = _torch()
         _lib.load()
         self.wl = wl
@@ -56,6 +60,15 @@ class DeviceStep:
         qdt = torch.float32 if wl.q_dtype == "f32" else torch.int16
         self.q_idx = torch.empty((B, P, wl.H_idx, wl.D_idx), dtype=qdt, device=d)
         self.q = torch.empty((L, B, P, wl.Hq, 576), dtype=qdt, device=d)
+        self.indexer_q = indexer_q or wl.q_dtype
+        self.q8 = self.w_scaled = None
+        if self.indexer_q == "e4m3":
+            if wl.q_dtype != "bf16" or wl.k_dtype != "e4m3":
+                raise ValueError("E4M3 indexer queries need bf16 queries and E4M3 keys")
+            self.q8 = torch.empty((B, P, wl.H_idx, wl.D_idx), dtype=torch.uint8, device=d)
+            self.w_scaled = torch.empty((B, P, wl.H_idx), dtype=torch.float32, device=d)
+        elif self.indexer_q != wl.q_dtype:
+            raise ValueError(f"indexer_q={indexer_q!r} not available for this workload")
         # step buffers
         self.scores = torch.empty((B, P, Ts), dtype=torch.float32, device=d)
         self.topk = torch.empty((B, P, K), dtype=torch.int32, device=d)
@@ -119,9 +132,25 @@ class DeviceStep:
         self.q.copy_(_dev(q, self.device))
 
     # ---------------------------------------------------------------- stages
-    def run_indexer(self, stream=None):
+    def run_quantize(self, stream=None):
         wl = self.wl
-        _lib.indexer_scores(self.batch, wl.H_idx, wl.D_idx, wl.q_dtype, self.q_idx, self.w,
+        _lib.quantize_queries(self.batch, wl.H_idx, wl.D_idx, self.q_idx, self.w, self.q8,
+                              self.w_scaled, stream)
+
+    def _indexer_inputs(self, stream, quantize=True):
+        """(query type, queries, head weights) the indexer reads; quantizes first
+        when the indexer runs on E4M3 queries (unless `quantize` is False: the
+        codes of the last quantization are reused)."""
+        if self.indexer_q == "e4m3":
+            if quantize:
+                self.run_quantize(stream)
+            return "e4m3", self.q8, self.w_scaled
+        return self.wl.q_dtype, self.q_idx, self.w
+
+    def run_indexer(self, stream=None, quantize=True):
+        wl = self.wl
+        qt, qi, w = self._indexer_inputs(stream, quantize)
+        _lib.indexer_scores(self.batch, wl.H_idx, wl.D_idx, qt, qi, w,
                             wl.k_dtype, self.idx_pool, self.idx_scale, self.idx_bt, self.bias,
                             self.scores, stream)
 
@@ -131,7 +160,8 @@ class DeviceStep:
     def run_indexer_topk(self, stream=None):
         """Indexer and top-K in one call (histogram pass fused into the indexer)."""
         wl = self.wl
-        _lib.indexer_topk(self.batch, wl.H_idx, wl.D_idx, wl.q_dtype, self.q_idx, self.w,
+        qt, qi, w = self._indexer_inputs(stream)
+        _lib.indexer_topk(self.batch, wl.H_idx, wl.D_idx, qt, qi, w,
                           wl.k_dtype, self.idx_pool, self.idx_scale, self.idx_bt, self.bias,
                           self.scores, wl.K, self.topk, self.ws_topk, stream)
 
@@ -222,12 +252,14 @@ class DeviceStep:
         if nchunks > 1:
             with torch.cuda.stream(cs):   # every chunk starts from the same step number
                 self.steps_dev[1:nchunks].copy_(self.steps_dev[0].expand(nchunks - 1))
+        with torch.cuda.stream(cs):
+            qt, qi, qw = self._indexer_inputs(None)
         for c in range(nchunks):
             ch = self._chunk(c, nchunks)
             sl, batch, res = ch["sl"], ch["batch"], ch["res"]
             with torch.cuda.stream(cs):
-                _lib.indexer_topk(batch, wl.H_idx, wl.D_idx, wl.q_dtype, self.q_idx[sl],
-                                  self.w[sl], wl.k_dtype, self.idx_pool, self.idx_scale,
+                _lib.indexer_topk(batch, wl.H_idx, wl.D_idx, qt, qi[sl],
+                                  qw[sl], wl.k_dtype, self.idx_pool, self.idx_scale,
                                   self.idx_bt[sl], None if self.bias is None else self.bias[sl],
                                   self.scores[sl], wl.K, self.topk[sl], self.ws_topk)
                 _lib.resolve_tables(batch, wl.K, self.topk[sl], res, self.row_ids[sl],

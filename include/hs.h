@@ -92,7 +92,9 @@ typedef struct hs_batch {
  *   scores[b,p,t] = sum_h w[b,p,h] * max(0, sum_d q[b,p,h,d] * k[b,t,d]) + bias[b,t]
  *
  * for 0 <= t <= T_b - P + p, with one key per token shared by all heads.
- *   q_idx     [B, P, H_idx, D_idx]   q_t = HS_BF16 (with k_t = HS_E4M3) or
+ *   q_idx     [B, P, H_idx, D_idx]   q_t = HS_BF16 (with k_t = HS_E4M3),
+ *                                    HS_E4M3 (with k_t = HS_E4M3; D_idx = 128;
+ *                                    codes from hs_quantize_queries) or
  *                                    HS_F32 (with k_t = HS_F32)
  *   w         [B, P, H_idx] fp32, non-negative values need not hold
  *   idx_pool  [N_blocks, 64, D_idx]  key of token t of request b is row t % 64
@@ -104,13 +106,36 @@ typedef struct hs_batch {
  *   scores    [B, P, T_stride] fp32 output; entries past a position's visible
  *             limit are left unspecified (hs_topk never reads them)
  * Supported: D_idx in {64, 128}; H_idx a multiple of 16 up to 64 on the
- * HS_BF16/HS_E4M3 path (matrix cores, fp32 accumulation), 1 .. 64 on HS_F32.
- * Keys, queries and scores need 16-byte alignment. */
+ * HS_BF16/HS_E4M3 path (bf16 matrix cores, fp32 accumulation) and on the
+ * HS_E4M3/HS_E4M3 path (fp8 matrix cores, exact products, fp32 accumulation;
+ * D_idx = 128 only), 1 .. 64 on HS_F32.
+ * Keys, queries and scores need 16-byte alignment, and so does w on the
+ * matrix-core paths. */
 hs_status hs_indexer_scores(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
                             hs_dtype q_t, const void* q_idx, const float* w,
                             hs_dtype k_t, const void* idx_pool, const float* idx_scale,
                             const int32_t* idx_bt, const float* bias, float* scores,
                             void* stream);
+
+/* Per-head E4M3 quantization of bf16 indexer queries, for the HS_E4M3 query
+ * path of hs_indexer_scores / hs_indexer_topk.  The pages keep the KV cache in
+ * FP8 (page "Un contexte d'un million sur huit H200", section "Les chiffres")
+ * and leave the indexer's query precision open; this is an optional variant
+ * that puts both operands of the q.k contraction in FP8.  For every row
+ * r = (b, p, h) of D_idx values:
+ *   amax = max_d |q[r, d]|;  if amax < 2^-64 the row's codes and s are 0,
+ *   else inv = 448 / amax, q8[r, d] = E4M3(q[r, d] * inv) (binary32 division
+ *   and product, round to nearest, ties to even), s = amax / 448;
+ *   w_scaled[r] = w[r] * s   (binary32).
+ * Because s >= 0 it leaves the ReLU, so scores computed from (q8, w_scaled)
+ * approximate those of (q, w) with the queries rounded to 4 significant bits.
+ *   q_idx    [B, P, H_idx, D_idx] bf16, finite; w [B, P, H_idx] fp32
+ *   q8       [B, P, H_idx, D_idx] E4M3 codes (output; may not alias q_idx)
+ *   w_scaled [B, P, H_idx] fp32 (output; may alias w)
+ * D_idx in {64, 128}; 1 <= H_idx <= 64. */
+hs_status hs_quantize_queries(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
+                              const void* q_idx, const float* w, uint8_t* q8, float* w_scaled,
+                              void* stream);
 
 /* Top-K per query position (page "Un contexte d'un million sur huit H200",
  * section "Ce qui se passe"; K = 2048 on "vLLM sert GLM-5.3 en contexte 1M sur

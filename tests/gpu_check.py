@@ -11,7 +11,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from oracle import attention as o_attn, indexer as o_idx, resolve as o_res, topk as o_topk
+from oracle import attention as o_attn, indexer as o_idx, quant as o_quant, resolve as o_res, \
+    topk as o_topk
 
 SCORE_RTOL = 2e-5       # |gpu - oracle| / max|S| of the row (fp32 accumulation)
 TOPK_TIE_REL = 1e-3     # swaps allowed only within 1e-3 relative of the K-th score
@@ -22,14 +23,39 @@ def oracle_state(wl):
                                 wl.slot2tok.copy(), wl.stamp.copy(), wl.host_bt.copy(), int(wl.step))
 
 
-def check_scores(wl, q_idx, scores, rows=None, sample=None, rng=None):
+def indexer_queries(wl, q_idx, indexer_q=None):
+    """(queries, their type tag, head weights) as the indexer consumes them:
+    the workload's own, or with indexer_q == "e4m3" the oracle's per-head E4M3
+    quantization of them (codes and scaled weights)."""
+    if indexer_q in (None, wl.q_dtype):
+        return q_idx, wl.q_dtype, wl.w
+    assert indexer_q == "e4m3"
+    codes, w_scaled, _ = o_quant.quantize_queries(q_idx, wl.w)
+    return codes, "e4m3", w_scaled
+
+
+def check_quantized(q_idx, w, q8, w_scaled):
+    """GPU query quantization against the oracle's: codes bit-exact (a zero
+    may carry either sign) and scaled weights bit-exact."""
+    codes, ws, _ = o_quant.quantize_queries(q_idx, w)
+    strip = lambda c: np.where(c == 0x80, np.uint8(0), c)
+    bad = np.argwhere(strip(codes) != strip(q8))
+    assert len(bad) == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
+    bits = lambda x: np.where(x == 0, np.uint32(0), np.ascontiguousarray(x, np.float32).view(np.uint32))
+    assert np.array_equal(bits(ws), bits(w_scaled)), "w_scaled"
+
+
+def check_scores(wl, q_idx, scores, rows=None, sample=None, rng=None, q_dtype=None, w=None):
     """Compare GPU scores with the oracle: every visible token of the listed
-    (b, p) rows, or a random sample of tokens per row when ``sample`` is set."""
+    (b, p) rows, or a random sample of tokens per row when ``sample`` is set.
+    q_dtype / w override the workload's query type and head weights."""
     B, P = wl.B, wl.P
+    q_dtype = q_dtype or wl.q_dtype
+    w = wl.w if w is None else w
     rows = rows if rows is not None else [(b, p) for b in range(B) for p in range(P)]
     worst = 0.0
     if sample is None:
-        S = o_idx.indexer_scores(q_idx, wl.q_dtype, wl.w, wl.idx_pool, wl.k_dtype, wl.idx_scale,
+        S = o_idx.indexer_scores(q_idx, q_dtype, w, wl.idx_pool, wl.k_dtype, wl.idx_scale,
                                  wl.idx_bt, wl.ctx_len, wl.bias, T_stride=wl.T_stride)
     for b, p in rows:
         n = max(o_idx.visible_limit(int(wl.ctx_len[b]), P, p) + 1, 0)
@@ -40,7 +66,7 @@ def check_scores(wl, q_idx, scores, rows=None, sample=None, rng=None):
             got = scores[b, p, :n].astype(np.float64)
         else:
             toks = np.unique(np.concatenate([rng.integers(0, n, sample), [0, n - 1]]))
-            ref = o_idx.indexer_scores_at(q_idx, wl.q_dtype, wl.w, wl.idx_pool, wl.k_dtype,
+            ref = o_idx.indexer_scores_at(q_idx, q_dtype, w, wl.idx_pool, wl.k_dtype,
                                           wl.idx_scale, wl.idx_bt, b, p, toks, wl.bias)
             got = scores[b, p, toks].astype(np.float64)
         scale = max(np.max(np.abs(ref)), 1e-30)
@@ -77,13 +103,15 @@ def check_topk_vs_oracle_scores(wl, S_oracle, topk):
     return n_swaps
 
 
-def check_topk_vs_oracle_scores_rows(wl, q_idx, topk, requests):
+def check_topk_vs_oracle_scores_rows(wl, q_idx, topk, requests, q_dtype=None, w=None):
     """check_topk_vs_oracle_scores for the listed requests only, with the
     oracle's scores computed for those requests alone (full-size workloads)."""
     n_swaps = 0
+    q_dtype = q_dtype or wl.q_dtype
+    w = wl.w if w is None else w
     for b in requests:
         sl = [b]
-        S = o_idx.indexer_scores(q_idx[sl], wl.q_dtype, wl.w[sl], wl.idx_pool, wl.k_dtype,
+        S = o_idx.indexer_scores(q_idx[sl], q_dtype, w[sl], wl.idx_pool, wl.k_dtype,
                                  wl.idx_scale, wl.idx_bt[sl], wl.ctx_len[sl],
                                  None if wl.bias is None else wl.bias[sl], T_stride=wl.T_stride)
         for p in range(wl.P):
@@ -162,12 +190,17 @@ def gpu_outputs(ds) -> dict:
 
 def full_check(ds, wl, ostate, s=1, attn_tol=2e-2, check_oracle_topk=True, pairs=None,
                score_sample=None, rng=None, copies=True, copy_limit=None):
-    """Run the GPU step s (inputs already set) and check every stage."""
+    """Check every stage of GPU step s (already run on the device step `ds`).
+    When ds quantizes the indexer's queries, the quantization is checked first
+    and the scores are compared with the oracle's indexer on its own codes."""
     q_idx, q = wl.step_inputs(s)
     g = gpu_outputs(ds)
-    rows = None
-    worst_s, S = check_scores(wl, q_idx, g["scores"], sample=score_sample,
-                              rng=rng or np.random.default_rng(0))
+    indexer_q = getattr(ds, "indexer_q", None)
+    if indexer_q == "e4m3":
+        check_quantized(q_idx, wl.w, ds.q8.cpu().numpy(), ds.w_scaled.cpu().numpy())
+    qi, qdt, w = indexer_queries(wl, q_idx, indexer_q)
+    worst_s, S = check_scores(wl, qi, g["scores"], sample=score_sample,
+                              rng=rng or np.random.default_rng(0), q_dtype=qdt, w=w)
     check_topk_exact(wl, g["scores"], g["topk"])
     swaps = 0
     if check_oracle_topk and S is not None:

@@ -71,6 +71,19 @@ def test_host_validation_rejects_bad_arguments_without_launching():
                                  None, fake, None) == 2
     assert lib.hs_indexer_scores(ctypes.byref(b), 64, 128, 1, ctypes.c_void_p(17), fake, 2, fake,
                                  None, fake, None, fake, None) == 6
+    # E4M3 queries: E4M3 keys and D = 128 only
+    assert lib.hs_indexer_scores(ctypes.byref(b), 64, 64, 2, fake, fake, 2, fake, None, fake,
+                                 None, fake, None) == 2
+    assert lib.hs_indexer_scores(ctypes.byref(b), 64, 128, 2, fake, fake, 1, fake, None, fake,
+                                 None, fake, None) == 3
+    assert lib.hs_indexer_scores(ctypes.byref(b), 40, 128, 2, fake, fake, 2, fake, None, fake,
+                                 None, fake, None) == 2
+    # query quantization
+    assert lib.hs_quantize_queries(ctypes.byref(b), 64, 128, fake, fake, None, fake, None) == 1
+    assert lib.hs_quantize_queries(ctypes.byref(b), 64, 96, fake, fake, fake, fake, None) == 2
+    assert lib.hs_quantize_queries(ctypes.byref(b), 65, 128, fake, fake, fake, fake, None) == 2
+    assert lib.hs_quantize_queries(ctypes.byref(b), 64, 128, ctypes.c_void_p(18), fake, fake,
+                                   fake, None) == 6
     # resolve: capacity rule C >= P*K
     res = _lib.Residency(128, 1, 2, 0, 0, 0, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16)
     assert lib.hs_resolve_rows(ctypes.byref(b), 256, fake, ctypes.byref(res), fake, fake, fake,
