@@ -64,6 +64,10 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
   // stored score's order-preserving key, per (request, position), counted in
   // LDS and added to `hist` (the first pass of the top-K radix select).
   __shared__ uint32_t sh_hist[HIST ? P * 2048 : 1];
+  // The tile's scores are gathered in LDS and leave in one contiguous burst
+  // at the end: 256-byte score stores interleaved with the key stream cost
+  // far more HBM time than their bytes.
+  __shared__ __attribute__((aligned(16))) float s_out[Cfg::TILE];
   if (HIST) {
     for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT) sh_hist[i] = 0;
     __syncthreads();
@@ -94,7 +98,6 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
 
   const int npages = min(Cfg::TILE / kBlock, (lim - tile0) / kBlock + 1);
   const int32_t* btb = bt + (size_t)b * max_blocks + tile0 / kBlock;
-  float* out = scores + (size_t)(b * P + p) * T_stride + tile0;
   const float* biasb = bias ? bias + (size_t)b * T_stride + tile0 : nullptr;
   const int lim_t = lim - tile0;
 
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     const int tl = pi * kBlock + lane;
     if (tl <= lim_t) {
       const float val = (scale ? mine * page_scale(pi) : mine) + bs;
-      out[tl] = val;
+      s_out[tl] = val;
       if (HIST) atomicAdd(&sh_hist[p * 2048 + (score_key(val) >> 21)], 1u);
     }
   };
@@ -179,8 +182,15 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     load_page(page_of(k + 3), bufB, bsB);
   }
   }  // lim >= tile0
+  __syncthreads();
+  if (lim >= tile0) {
+    // whole pages: entries past the visible limit are unspecified
+    const int nt = min(Cfg::TILE, ((lim - tile0) / kBlock + 1) * kBlock);
+    float* o = scores + (size_t)(b * P + p) * T_stride + tile0;
+    for (int i = 4 * threadIdx.x; i < nt; i += 4 * Cfg::NT)
+      *reinterpret_cast<float4*>(o + i) = *reinterpret_cast<const float4*>(s_out + i);
+  }
   if (HIST) {
-    __syncthreads();
     for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT)
       if (sh_hist[i]) atomicAdd(&hist[(size_t)(b * P + i / 2048) * 2048 + (i % 2048)], sh_hist[i]);
   }
@@ -386,6 +396,10 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
   const int p = wave / Cfg::WPP, sub = wave % Cfg::WPP;
   const int lim = T - P + p;
   __shared__ uint32_t sh_hist[HIST ? P * 2048 : 1];
+  // The tile's scores are gathered in LDS and leave in one contiguous burst
+  // at the end: 256-byte score stores interleaved with the key stream cost
+  // far more HBM time than their bytes.
+  __shared__ __attribute__((aligned(16))) float s_out[Cfg::TILE];
   __shared__ float4 sw4[P][H / 4];
   if (HIST)
     for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT) sh_hist[i] = 0;
@@ -404,7 +418,6 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
   }
   const int npages = min(Cfg::TILE / kBlock, (lim - tile0) / kBlock + 1);
   const int32_t* btb = bt + (size_t)b * max_blocks + tile0 / kBlock;
-  float* out = scores + (size_t)(b * P + p) * T_stride + tile0;
   const float* biasb = bias ? bias + (size_t)b * T_stride + tile0 : nullptr;
   const int lim_t = lim - tile0;
   static_assert(Cfg::TILE / kBlock <= kWave, "one page per lane");
@@ -452,7 +465,7 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
     const int tl = pi * kBlock + lane;
     if (tl <= lim_t) {
       const float val = (scale ? mine * page_scale(pi) : mine) + bs;
-      out[tl] = val;
+      s_out[tl] = val;
       if (HIST) atomicAdd(&sh_hist[p * 2048 + (score_key(val) >> 21)], 1u);
     }
   };
@@ -470,8 +483,15 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
     load_page(page_of(k + 3), bufB, bsB);
   }
   }  // lim >= tile0
+  __syncthreads();
+  if (lim >= tile0) {
+    // whole pages: entries past the visible limit are unspecified
+    const int nt = min(Cfg::TILE, ((lim - tile0) / kBlock + 1) * kBlock);
+    float* o = scores + (size_t)(b * P + p) * T_stride + tile0;
+    for (int i = 4 * threadIdx.x; i < nt; i += 4 * Cfg::NT)
+      *reinterpret_cast<float4*>(o + i) = *reinterpret_cast<const float4*>(s_out + i);
+  }
   if (HIST) {
-    __syncthreads();
     for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT)
       if (sh_hist[i]) atomicAdd(&hist[(size_t)(b * P + i / 2048) * 2048 + (i % 2048)], sh_hist[i]);
   }
