@@ -40,7 +40,7 @@ struct IdxCfg {
   static constexpr int TILE = 4096;                              // tokens per workgroup
 };
 
-template <int P, int DK, int HT, bool HIST>
+template <int P, int DK, int HT, bool HIST, int TILE>
 __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     const int32_t* __restrict__ ctx_len, int T_stride, int max_blocks,
     const uint16_t* __restrict__ q, const float* __restrict__ w,
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
   constexpr int LPB = 4 * NV;    // 16-byte loads per lane per 64-token page
   const int b = blockIdx.y;
   const int T = ctx_len[b];
-  const int tile0 = blockIdx.x * Cfg::TILE;
+  const int tile0 = blockIdx.x * TILE;
   if (tile0 >= T) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
   // The tile's scores are gathered in LDS and leave in one contiguous burst
   // at the end: 256-byte score stores interleaved with the key stream cost
   // far more HBM time than their bytes.
-  __shared__ __attribute__((aligned(16))) float s_out[Cfg::TILE];
+  __shared__ __attribute__((aligned(16))) float s_out[TILE];
   if (HIST) {
     for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT) sh_hist[i] = 0;
     __syncthreads();
@@ -96,21 +96,30 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     for (int i = lane; i < H / 4; i += kWave) sw4[p][i] = reinterpret_cast<const float4*>(wp)[i];
   __syncthreads();
 
-  const int npages = min(Cfg::TILE / kBlock, (lim - tile0) / kBlock + 1);
+  const int npages = min(TILE / kBlock, (lim - tile0) / kBlock + 1);
   const int32_t* btb = bt + (size_t)b * max_blocks + tile0 / kBlock;
   const float* biasb = bias ? bias + (size_t)b * T_stride + tile0 : nullptr;
   const int lim_t = lim - tile0;
 
-  // Page metadata of the whole tile is read once: lane l holds page l's
-  // physical block and scale (a tile has at most 64 pages), fetched later with
-  // readlane.  No load inside the page loop depends on another load, so the
-  // in-order memory counter never forces a wait on pages still in flight.
-  static_assert(Cfg::TILE / kBlock <= kWave, "one page per lane");
+  // Page metadata of the whole tile is read once: lane l holds the physical
+  // block and scale of pages l and 64 + l (a tile has at most 128 pages),
+  // fetched later with readlane.  No load inside the page loop depends on
+  // another load, so the in-order memory counter never forces a wait on pages
+  // still in flight.
+  static_assert(TILE == 4096 || TILE == 8192, "tile of 64 or 128 pages");
+  constexpr bool kTwo = TILE > 4096;
   const int blk_l = lane < npages ? btb[lane] : 0;
   const float sc_l = (scale && lane < npages) ? scale[blk_l] : 1.f;
-  auto page_blk = [&](int pi) { return __builtin_amdgcn_readlane(blk_l, pi); };
+  const int blk_h = (kTwo && kWave + lane < npages) ? btb[kWave + lane] : 0;
+  const float sc_h = (kTwo && scale && kWave + lane < npages) ? scale[blk_h] : 1.f;
+  auto page_blk = [&](int pi) {
+    return (kTwo && pi >= kWave) ? __builtin_amdgcn_readlane(blk_h, pi - kWave)
+                                 : __builtin_amdgcn_readlane(blk_l, pi);
+  };
   auto page_scale = [&](int pi) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
+    return __int_as_float((kTwo && pi >= kWave)
+                              ? __builtin_amdgcn_readlane(__float_as_int(sc_h), pi - kWave)
+                              : __builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
   };
   // lane (n, g) loads, for token 16j + n of a page, bytes 16g + 64v .. +16, and
   // the bias of token 64*pi + lane.  Two pages are in flight per wave: page
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
   __syncthreads();
   if (lim >= tile0) {
     // whole pages: entries past the visible limit are unspecified
-    const int nt = min(Cfg::TILE, ((lim - tile0) / kBlock + 1) * kBlock);
+    const int nt = min(TILE, ((lim - tile0) / kBlock + 1) * kBlock);
     float* o = scores + (size_t)(b * P + p) * T_stride + tile0;
     for (int i = 4 * threadIdx.x; i < nt; i += 4 * Cfg::NT)
       *reinterpret_cast<float4*>(o + i) = *reinterpret_cast<const float4*>(s_out + i);
@@ -729,14 +738,28 @@ hipError_t launch_mfma(const BatchDims& d, const uint16_t* q, const float* w, co
                          scores, hist);
     return hipGetLastError();
   }
+  // 128-page tiles when they still give every CU two workgroups (one round of
+  // workgroups instead of two: fewer start-ups with no keys in flight)
+  if ((size_t)d.B * ((d.T_stride + 8191) / 8192) >= 512) {
+    const dim3 g2((d.T_stride + 8191) / 8192, d.B);
+    if (hist)
+      hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT, true, 8192>), g2, dim3(Cfg::NT), 0,
+                         s, d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias,
+                         scores, hist);
+    else
+      hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT, false, 8192>), g2, dim3(Cfg::NT), 0,
+                         s, d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias,
+                         scores, hist);
+    return hipGetLastError();
+  }
   if (hist)
-    hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT, true>), grid, dim3(Cfg::NT), 0, s,
-                       d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias, scores,
-                       hist);
+    hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT, true, 4096>), grid, dim3(Cfg::NT), 0,
+                       s, d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias,
+                       scores, hist);
   else
-    hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT, false>), grid, dim3(Cfg::NT), 0, s,
-                       d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias, scores,
-                       hist);
+    hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT, false, 4096>), grid, dim3(Cfg::NT), 0,
+                       s, d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias,
+                       scores, hist);
   return hipGetLastError();
 }
 

@@ -411,3 +411,50 @@ def test_topk_planted_ties_against_oracle(case, T_stride):
     ref = o_topk.topk(S.astype(np.float64), ctx, K)
     bad = np.argwhere(np.any(ref != got, axis=2))
     assert len(bad) == 0, f"rows {bad[:4].tolist()}"
+
+
+def test_indexer_many_requests_long_tiles():
+    """256 requests over a 16K-token stride: enough tiles for the one-position
+    indexer's 128-page tiles.  Ragged contexts (empty, one token, on and off
+    the 4096/8192 boundaries); fused and separate indexer calls give the same
+    scores bit for bit; sampled scores against the oracle; top-K exact."""
+    from decode_indexer_logits_amd import _lib
+    from oracle import indexer as o_idx, topk as o_topk
+    rng = np.random.default_rng(21)
+    B, Ts, K = 256, 16384, 512
+    ctx = rng.integers(1, 12001, B).astype(np.int32)
+    ctx[:8] = [0, 1, 64, 4096, 8191, 8192, 8193, 16384]
+    _say(f"indexer many requests B={B} T_stride={Ts}")
+    x = gen.indexer_inputs(2100, ctx, Ts)
+    dev = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).cuda()
+           for k, v in x.items() if isinstance(v, np.ndarray)}
+    batch = _lib.make_batch(B, 1, Ts, dev["ctx_len"])
+    s1 = torch.empty((B, 1, Ts), dtype=torch.float32, device="cuda")
+    s2 = torch.empty_like(s1)
+    topk = torch.empty((B, 1, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, 1, Ts, K), dtype=torch.uint8,
+                     device="cuda")
+    args = (x["H"], x["D"], "bf16", dev["q_idx"], dev["w"], "e4m3", dev["idx_pool"],
+            dev["idx_scale"], dev["idx_bt"], dev["bias"])
+    _lib.indexer_scores(batch, *args, s1)
+    _lib.indexer_topk(batch, *args, s2, K, topk, ws)
+    torch.cuda.synchronize()
+    g1, g2, gt = s1.cpu().numpy(), s2.cpu().numpy(), topk.cpu().numpy()
+    worst = 0.0
+    for b in range(B):
+        n = int(ctx[b])
+        assert np.array_equal(g1[b, 0, :n].view(np.uint32), g2[b, 0, :n].view(np.uint32)), b
+        if n == 0:
+            continue
+        toks = np.unique(np.concatenate([rng.integers(0, n, 24), [0, n - 1],
+                                         [t for t in (4095, 4096, 8191, 8192) if t < n]])
+                         .astype(np.int64))
+        ref = o_idx.indexer_scores_at(x["q_idx"], "bf16", x["w"], x["idx_pool"], "e4m3",
+                                      x["idx_scale"], x["idx_bt"], b, 0, toks, x["bias"])
+        err = float(np.max(np.abs(g2[b, 0, toks] - ref)) / max(np.max(np.abs(ref)), 1e-30))
+        worst = max(worst, err)
+        assert err <= gc.SCORE_RTOL, (b, err)
+    ref_t = o_topk.topk(g2.astype(np.float64), ctx, K)
+    bad = np.argwhere(np.any(ref_t != gt, axis=2))
+    assert len(bad) == 0, f"top-K rows {bad[:4].tolist()}"
+    _say(f"worst sampled score error {worst:.2e}")
