@@ -36,10 +36,10 @@ KV_ROW = 576
 # rocprofv3 --pmc runs (FETCH_SIZE x 2 + WRITE_SIZE x 1, factors calibrated with a
 # 512 MiB read and a 512 MiB fill in the same runs; profiles/indexer_mixed_128k_pmc.txt).
 # Reported only while the kernel's sources are the ones the counters were taken on.
-INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 579.70e6,
+INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.17e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
-                   "sha256": "22053c09bb56af732acc54b80c093a87502e4b6164f72644b5d6cdeca94fc244"}
+                   "sha256": "5429f0b5122de042993b4e84336e133decea8b82bdce379aee78fb782f19915d"}
 
 
 def _indexer_traffic(workload: str, indexer_q: str):
