@@ -29,6 +29,8 @@ to something other than itself:
 * ``quant``     -- optional E4M3 queries for the indexer: per-head absmax scale
   to 448, binary32 rounding to the nearest code, scale folded into w.
 * ``topk``      -- K largest scores, ties to the lower token, ascending output.
+* ``cache_ops`` -- KV append, pre-copy of completed pages to the host pool,
+  demotion of resident pages (the steps on either side of a decode step).
 * ``resolve``   -- the residency state machine (resident / hot hit with LRU
   refresh / single-row fault from host).
 * ``attention`` -- absorbed-MQA softmax attention over the selected latent rows,
