@@ -17,12 +17,13 @@ LIB_PATH = Path(__file__).resolve().parent / "libhisparse.so"
 
 HS_F32, HS_BF16, HS_E4M3 = 0, 1, 2
 DTYPES = {"f32": HS_F32, "bf16": HS_BF16, "e4m3": HS_E4M3}
-HS_OP_INDEXER, HS_OP_TOPK, HS_OP_RESOLVE, HS_OP_MLA = 0, 1, 2, 3
+HS_OP_INDEXER, HS_OP_TOPK, HS_OP_RESOLVE, HS_OP_MLA, HS_OP_CACHE = 0, 1, 2, 3, 4
 DEVERR_VICTIMS, DEVERR_NO_HOST = 1, 2
+DEVERR_APPEND_RANGE, DEVERR_APPEND_NO_BLOCK, DEVERR_DEMOTE_FULL = 4, 8, 16
 
 EXPORTS = ["hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
-           "hs_sparse_mla_decode", "hs_workspace_bytes", "hs_host_device_ptr", "hs_last_error",
-           "hs_abi_version"]
+           "hs_sparse_mla_decode", "hs_append_tokens", "hs_precopy_pages", "hs_demote_pages",
+           "hs_workspace_bytes", "hs_host_device_ptr", "hs_last_error", "hs_abi_version"]
 
 
 class HsError(RuntimeError):
@@ -43,6 +44,16 @@ class Residency(ctypes.Structure):
                 ("slot2tok", c_void_p), ("stamp", c_void_p), ("step", c_void_p),
                 ("err", c_void_p), ("pool", c_void_p), ("row_scale", c_void_p),
                 ("host_rows", c_void_p), ("host_scale", c_void_p), ("host_bt", c_void_p)]
+
+
+class FreeList(ctypes.Structure):
+    _fields_ = [("blocks", c_void_p), ("count", c_void_p), ("capacity", c_int32),
+                ("pad_", c_int32)]
+
+
+class IndexCache(ctypes.Structure):
+    _fields_ = [("k_t", c_int32), ("D_idx", c_int32), ("pool", c_void_p), ("scale", c_void_p),
+                ("bt", c_void_p)]
 
 
 _lib = None
@@ -68,6 +79,11 @@ def load() -> ctypes.CDLL:
     lib.hs_copy_faults.argtypes = [P, c_int32, P, P, P, c_int32, P]
     lib.hs_sparse_mla_decode.argtypes = [P, c_int32, c_int32, c_int32, P, c_int32, P, P, P,
                                          c_float, P, P, P, c_size_t, P]
+    lib.hs_append_tokens.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, c_size_t, P]
+    lib.hs_precopy_pages.argtypes = [P, P, c_int32, P]
+    lib.hs_demote_pages.argtypes = [P, P, P, c_int32, P, P, c_size_t, P]
+    for f in ("hs_append_tokens", "hs_precopy_pages", "hs_demote_pages"):
+        getattr(lib, f).restype = c_int32
     for f in ("hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables",
               "hs_copy_faults", "hs_sparse_mla_decode", "hs_host_device_ptr"):
         getattr(lib, f).restype = c_int32
@@ -170,3 +186,27 @@ def sparse_mla_decode(batch: Batch, K: int, Hq: int, q_t: str, q, kv_t: str, poo
                                        float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
                                        0 if ws is None else ws.numel() * ws.element_size(),
                                        _stream(stream)))
+
+
+def append_tokens(batch: Batch, ctx_len, n_new, res: Residency, new_rows, new_row_scale,
+                  idx: IndexCache, new_keys, new_key_scale, latent_free: FreeList,
+                  idx_free: FreeList, ws, stream=None):
+    _check(load().hs_append_tokens(ctypes.byref(batch), _ptr(ctx_len), _ptr(n_new),
+                                   ctypes.byref(res), _ptr(new_rows), _ptr(new_row_scale),
+                                   ctypes.byref(idx), _ptr(new_keys), _ptr(new_key_scale),
+                                   ctypes.byref(latent_free), ctypes.byref(idx_free), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(),
+                                   _stream(stream)))
+
+
+def precopy_pages(batch: Batch, res: Residency, max_pages: int, stream=None):
+    _check(load().hs_precopy_pages(ctypes.byref(batch), ctypes.byref(res), max_pages,
+                                   _stream(stream)))
+
+
+def demote_pages(batch: Batch, res: Residency, n_demote, tail_pages: int, latent_free: FreeList,
+                 ws, stream=None):
+    _check(load().hs_demote_pages(ctypes.byref(batch), ctypes.byref(res), _ptr(n_demote),
+                                  tail_pages, ctypes.byref(latent_free), _ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(),
+                                  _stream(stream)))

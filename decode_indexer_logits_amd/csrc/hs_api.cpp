@@ -325,12 +325,126 @@ hs_status hs_sparse_mla_decode(const hs_batch* batch, int32_t K, int32_t Hq, hs_
 
 size_t hs_workspace_bytes(int32_t op, int32_t B, int32_t P, int32_t T_stride, int32_t K,
                           int32_t Hq) {
+  if (op == HS_OP_CACHE) return B < 1 ? 0 : hs::cache_workspace_bytes(B);
   if (B < 1 || P < 1 || K < 1) return 0;
   switch (op) {
     case HS_OP_TOPK: return hs::topk_workspace_bytes(B, P, T_stride, K);
     case HS_OP_MLA: return hs::mla_workspace_bytes(B, P, K, Hq);
     default: return 0;
   }
+}
+
+static_assert(HS_DEVERR_APPEND_RANGE == hs::kDevErrAppendRange &&
+                  HS_DEVERR_APPEND_NO_BLOCK == hs::kDevErrAppendNoBlock &&
+                  HS_DEVERR_DEMOTE_FULL == hs::kDevErrDemoteFull,
+              "device error bits");
+
+}  // extern "C"
+
+namespace {
+
+hs_status check_free_list(const hs_free_list* f, const char* what, hs::FreeListArgs* out) {
+  if (!f || !f->blocks || !f->count) return fail(HS_ERR_NULL, "%s free list is incomplete", what);
+  if (f->capacity < 1) return fail(HS_ERR_SHAPE, "%s free list capacity=%d", what, f->capacity);
+  out->blocks = f->blocks;
+  out->count = f->count;
+  out->capacity = f->capacity;
+  return HS_OK;
+}
+
+hs_status check_cache_ws(const hs::BatchDims& d, void* ws, size_t ws_bytes) {
+  const size_t need = hs::cache_workspace_bytes(d.B);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "cache operations need %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace needs 16-byte alignment");
+  return HS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_append_tokens(const hs_batch* batch, int32_t* ctx_len, const int32_t* n_new,
+                           const hs_residency* res, const void* new_rows,
+                           const float* new_row_scale, const hs_index_cache* idx,
+                           const void* new_keys, const float* new_key_scale,
+                           const hs_free_list* latent_free, const hs_free_list* idx_free,
+                           void* ws, size_t ws_bytes, void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!ctx_len || ctx_len != batch->ctx_len)
+    return fail(HS_ERR_SHAPE, "hs_append_tokens: ctx_len must be batch->ctx_len");
+  if (!n_new || !new_rows || !idx || !new_keys)
+    return fail(HS_ERR_NULL, "hs_append_tokens: n_new, new_rows, idx and new_keys are required");
+  hs::ResidencyArgs r;
+  if (hs_status st = check_residency(d, 1, res, &r)) return st;
+  if (res->kv_t == HS_E4M3 && !new_row_scale)
+    return fail(HS_ERR_NULL, "E4M3 rows need new_row_scale");
+  if (res->kv_t == HS_F32 && new_row_scale)
+    return fail(HS_ERR_DTYPE, "F32 rows take no new_row_scale");
+  if (!idx->pool || !idx->bt) return fail(HS_ERR_NULL, "indexer cache: pool and bt are required");
+  if (idx->D_idx != 64 && idx->D_idx != 128)
+    return fail(HS_ERR_SHAPE, "D_idx=%d must be 64 or 128", idx->D_idx);
+  int key_bytes;
+  if (idx->k_t == HS_E4M3) {
+    key_bytes = idx->D_idx;
+    if (!idx->scale || !new_key_scale)
+      return fail(HS_ERR_NULL, "E4M3 keys need the block scales and new_key_scale");
+  } else if (idx->k_t == HS_F32) {
+    key_bytes = 4 * idx->D_idx;
+    if (idx->scale || new_key_scale) return fail(HS_ERR_DTYPE, "F32 keys take no scales");
+  } else {
+    return fail(HS_ERR_DTYPE, "indexer keys must be E4M3 or F32");
+  }
+  if (!aligned16(new_rows) || !aligned16(new_keys) || !aligned16(idx->pool))
+    return fail(HS_ERR_ALIGN, "new_rows, new_keys and the indexer pool need 16-byte alignment");
+  hs::FreeListArgs lf, fi;
+  if (hs_status st = check_free_list(latent_free, "latent", &lf)) return st;
+  if (hs_status st = check_free_list(idx_free, "indexer", &fi)) return st;
+  if (hs_status st = check_cache_ws(d, ws, ws_bytes)) return st;
+  return launched(hs::launch_append_tokens(d, ctx_len, n_new, r, new_rows, new_row_scale,
+                                           key_bytes, idx->pool, idx->scale, idx->bt, new_keys,
+                                           new_key_scale, lf, fi, ws,
+                                           static_cast<hipStream_t>(stream)),
+                  "append");
+}
+
+hs_status hs_precopy_pages(const hs_batch* batch, const hs_residency* res, int32_t max_pages,
+                           void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  hs::ResidencyArgs r;
+  if (hs_status st = check_residency(d, 1, res, &r)) return st;
+  if (!res->host_rows || !res->host_bt || (res->kv_t == HS_E4M3 && !res->host_scale))
+    return fail(HS_ERR_NULL, "pre-copy needs host_rows, host_bt (and host_scale for E4M3)");
+  if (max_pages < 1 || max_pages > hs::precopy_max_pages())
+    return fail(HS_ERR_SHAPE, "max_pages=%d out of [1, %d]", max_pages, hs::precopy_max_pages());
+  if (res->host_layer_rows < (int64_t)d.B * d.T_stride)
+    return fail(HS_ERR_SHAPE, "the host pool needs B*T_stride=%lld rows per layer",
+                (long long)d.B * d.T_stride);
+  return launched(hs::launch_precopy_pages(d, r, max_pages, static_cast<hipStream_t>(stream)),
+                  "pre-copy");
+}
+
+hs_status hs_demote_pages(const hs_batch* batch, const hs_residency* res,
+                          const int32_t* n_demote, int32_t tail_pages,
+                          const hs_free_list* latent_free, void* ws, size_t ws_bytes,
+                          void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!n_demote) return fail(HS_ERR_NULL, "hs_demote_pages: n_demote is required");
+  hs::ResidencyArgs r;
+  if (hs_status st = check_residency(d, 1, res, &r)) return st;
+  if (!res->host_bt) return fail(HS_ERR_NULL, "demotion needs host_bt");
+  if (tail_pages < 1 || tail_pages > d.max_blocks)
+    return fail(HS_ERR_SHAPE, "tail_pages=%d out of [1, %d]", tail_pages, d.max_blocks);
+  hs::FreeListArgs lf;
+  if (hs_status st = check_free_list(latent_free, "latent", &lf)) return st;
+  if (hs_status st = check_cache_ws(d, ws, ws_bytes)) return st;
+  return launched(hs::launch_demote_pages(d, r, n_demote, tail_pages, lf, ws,
+                                          static_cast<hipStream_t>(stream)),
+                  "demotion");
 }
 
 hs_status hs_host_device_ptr(const void* pinned_host, const void** dev_ptr) {

@@ -64,6 +64,28 @@ hipError_t launch_fault_copy(const BatchDims& d, int K, const ResidencyArgs& r,
                              const int32_t* faults, const int32_t* counts, int workgroups,
                              hipStream_t s);
 
+// Device error bits of the cache operations (the HS_DEVERR_* values of hs.h).
+constexpr int kDevErrAppendRange = 4;
+constexpr int kDevErrAppendNoBlock = 8;
+constexpr int kDevErrDemoteFull = 16;
+struct FreeListArgs {
+  int32_t* blocks;
+  int32_t* count;
+  int capacity;
+};
+size_t cache_workspace_bytes(int B);
+int precopy_max_pages();
+hipError_t launch_append_tokens(const BatchDims& d, int32_t* ctx_len, const int32_t* n_new,
+                                const ResidencyArgs& r, const void* new_rows,
+                                const float* new_row_scale, int key_bytes, void* idx_pool,
+                                float* idx_scale, int32_t* idx_bt, const void* new_keys,
+                                const float* new_key_scale, const FreeListArgs& lat,
+                                const FreeListArgs& idx, void* ws, hipStream_t s);
+hipError_t launch_precopy_pages(const BatchDims& d, const ResidencyArgs& r, int max_pages,
+                                hipStream_t s);
+hipError_t launch_demote_pages(const BatchDims& d, const ResidencyArgs& r,
+                               const int32_t* n_demote, int tail_pages,
+                               const FreeListArgs& lat, void* ws, hipStream_t s);
 int mla_num_splits(int B, int P, int K);
 size_t mla_workspace_bytes(int B, int P, int K, int Hq);
 hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, const uint16_t* q, const uint8_t* pool,

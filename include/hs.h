@@ -65,6 +65,15 @@ typedef enum {
 
 /* Error bits the resolve step ORs into hs_residency.err (device). */
 #define HS_DEVERR_VICTIMS 1   /* more faults than replaceable hot slots      */
+#define HS_DEVERR_APPEND_RANGE 4    /* hs_append_tokens: a request would pass
+                                       T_stride or take more than P tokens, or
+                                       the page receiving its first new token is
+                                       not resident; nothing was appended      */
+#define HS_DEVERR_APPEND_NO_BLOCK 8 /* hs_append_tokens: a free list holds fewer
+                                       blocks than the pages to open; nothing
+                                       was appended                            */
+#define HS_DEVERR_DEMOTE_FULL 16    /* hs_demote_pages: the free list cannot take
+                                       the blocks; nothing was demoted         */
 #define HS_DEVERR_NO_HOST 2   /* a selected token is neither resident, hot,
                                  nor present in the host pool                */
 
@@ -276,10 +285,84 @@ hs_status hs_sparse_mla_decode(const hs_batch* batch, int32_t K, int32_t Hq, hs_
 #define HS_OP_TOPK 1
 #define HS_OP_RESOLVE 2
 #define HS_OP_MLA 3
+#define HS_OP_CACHE 4
 
 /* Device workspace in bytes needed by `op` for these sizes (0 if none). */
 size_t hs_workspace_bytes(int32_t op, int32_t B, int32_t P, int32_t T_stride, int32_t K,
                           int32_t Hq);
+
+/* ---- Around the decode step: KV append, pre-copy, demotion ----
+ * Page "Un contexte d'un million sur huit H200", section "Les trois états de
+ * résidence": with full residency completed prefix pages are copied to the
+ * host ahead of time, so that their block can be given up later without a
+ * copy; with mixed residency the tail stays on the GPU and older pages live
+ * only on the host; the indexer's cache stays resident (section "Ce qui se
+ * passe").  Every decision is taken on the device and is deterministic, so
+ * the calls are graph-capturable and reproducible.
+ *
+ * A free list is a stack of pool blocks in device memory: blocks[0 .. *count-1]
+ * are free, the top is blocks[*count - 1]. */
+typedef struct hs_free_list {
+  int32_t* blocks;     /* device [capacity]                                 */
+  int32_t* count;      /* device [1]                                        */
+  int32_t capacity;
+  int32_t pad_;
+} hs_free_list;
+
+/* The indexer's paged key cache (as passed to hs_indexer_scores). */
+typedef struct hs_index_cache {
+  hs_dtype k_t;        /* HS_E4M3 (scale per block) or HS_F32 (no scale)    */
+  int32_t D_idx;       /* 64 or 128                                         */
+  void* pool;          /* [N_idx_blocks, 64, D_idx]                         */
+  float* scale;        /* [N_idx_blocks] or NULL                            */
+  int32_t* bt;         /* [B, max_blocks]                                   */
+} hs_index_cache;
+
+/* Append n_new[b] (0 .. P) tokens to request b after its last token: the
+ * latent row of every layer with its scale, and the indexer key.  A token at
+ * a page start (t % 64 == 0) opens a page: a latent block and an indexer block
+ * are popped from the two free lists (request order, then token order) and
+ * the indexer block's scale is set to that token's new_key_scale.  Then
+ * ctx_len[b] += n_new[b].  All-or-nothing: on a range or capacity problem the
+ * call appends nothing and sets HS_DEVERR_APPEND_* in res->err.
+ *   ctx_len       the batch's ctx_len (batch->ctx_len), updated in place
+ *   n_new         device [B] int32
+ *   res           latent pool, row_scale, bt (updated), err, L, kv_t
+ *   new_rows      device [B, P, L, 576] in kv_t; new_row_scale [B, P, L] fp32
+ *                 (E4M3) or NULL (F32)
+ *   idx           indexer cache (pool, scale and bt updated)
+ *   new_keys      device [B, P, D_idx] in idx->k_t; new_key_scale [B, P] fp32
+ *                 (E4M3) or NULL (F32)
+ *   ws            hs_workspace_bytes(HS_OP_CACHE, B, ...) bytes, 16-byte aligned
+ * Pointers to row data need 16-byte alignment. */
+hs_status hs_append_tokens(const hs_batch* batch, int32_t* ctx_len, const int32_t* n_new,
+                           const hs_residency* res, const void* new_rows,
+                           const float* new_row_scale, const hs_index_cache* idx,
+                           const void* new_keys, const float* new_key_scale,
+                           const hs_free_list* latent_free, const hs_free_list* idx_free,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Pre-copy: for every request, its lowest completed pages (all 64 tokens below
+ * T_b) that are resident and have no host copy, at most max_pages (1 .. 1024)
+ * per request, are copied (rows and scales of every layer) to their host slot,
+ * host row b*T_stride + 64p, and host_bt records it.  Writes res->host_rows
+ * (pinned host memory, zero-copy), res->host_scale and res->host_bt, which must
+ * all be given; the host pool holds B*T_stride rows per layer
+ * (res->host_layer_rows >= B*T_stride).  Bound by the host link (writes). */
+hs_status hs_precopy_pages(const hs_batch* batch, const hs_residency* res, int32_t max_pages,
+                           void* stream);
+
+/* Demotion under pressure: request b gives up the blocks of its lowest
+ * n_demote[b] pages that are resident, have a host copy and lie outside its
+ * last tail_pages pages (tail_pages >= 1: the tail, counted from the page of
+ * its last token, is never demoted).  bt becomes -1 for them and their blocks
+ * are pushed on latent_free (request order, then page order).  All-or-nothing
+ * if the free list would pass its capacity (HS_DEVERR_DEMOTE_FULL).
+ *   n_demote  device [B] int32;  ws as for hs_append_tokens. */
+hs_status hs_demote_pages(const hs_batch* batch, const hs_residency* res,
+                          const int32_t* n_demote, int32_t tail_pages,
+                          const hs_free_list* latent_free, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* Device-accessible address of pinned host memory allocated with
  * hipHostMalloc (or torch pin_memory); HS_ERR_HIP if it is not pinned. */

@@ -22,8 +22,10 @@ Readings taken (the pages give the states, not the bookkeeping):
   that token (keys arrive quantized against their block's scale).  The free
   lists are stacks: blocks[0 .. count-1], the top is blocks[count-1]; pops go
   in request order, then token order.  The call is all-or-nothing: if any
-  request would pass T_stride, or the pages to open exceed a free list, no
-  token is appended and an error bit is set.
+  request would pass T_stride or take more than P tokens, if the page that
+  receives a request's first new token is not resident (when that token does
+  not open it), or if the pages to open exceed a free list, no token is
+  appended and an error bit is set.
 * Pre-copy.  A completed page (every one of its 64 tokens below T_b) that is
   resident (bt >= 0) and has no host copy (host_bt < 0) is copied, rows and
   row scales of every layer, to its host slot: host row b * T_stride + 64 * p
@@ -85,13 +87,17 @@ def append_tokens(st: CacheState, n_new, new_rows, new_row_scale, new_keys, new_
     new_key_scale [B, P] or None (only read for tokens that open a page).
     """
     B = len(st.ctx_len)
+    P = np.asarray(new_keys).shape[1]
     n_new = np.asarray(n_new)
     err = 0
     need = 0
     for b in range(B):
         T, n = int(st.ctx_len[b]), int(n_new[b])
-        if T + n > st.T_stride:
+        partial = n > 0 and T % BLOCK != 0
+        if (n < 0 or n > P or T + n > st.T_stride or
+                (partial and (st.bt[b, T // BLOCK] < 0 or st.idx_bt[b, T // BLOCK] < 0))):
             err |= ERR_APPEND_RANGE
+            continue
         need += _pages_opened(T, n)
     if need > len(st.free) or need > len(st.idx_free):
         err |= ERR_APPEND_NO_BLOCK

@@ -38,13 +38,19 @@ def test_struct_layout_matches_header(tmp_path):
                  "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(hs_batch),"
                  " offsetof(hs_batch, ctx_len), sizeof(hs_residency),"
                  " offsetof(hs_residency, pool_layer_rows), offsetof(hs_residency, bt),"
-                 " offsetof(hs_residency, host_bt)); return 0;}\n")
+                 " offsetof(hs_residency, host_bt));"
+                 " printf(\"%zu %zu %zu %zu %zu\\n\", sizeof(hs_free_list), offsetof(hs_free_list, capacity),"
+                 " sizeof(hs_index_cache), offsetof(hs_index_cache, pool), offsetof(hs_index_cache, bt));"
+                 " return 0;}\n")
     exe = tmp_path / "probe"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)], check=True)
     vals = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()))
     assert vals == [ctypes.sizeof(_lib.Batch), _lib.Batch.ctx_len.offset,
                     ctypes.sizeof(_lib.Residency), _lib.Residency.pool_layer_rows.offset,
-                    _lib.Residency.bt.offset, _lib.Residency.host_bt.offset]
+                    _lib.Residency.bt.offset, _lib.Residency.host_bt.offset,
+                    ctypes.sizeof(_lib.FreeList), _lib.FreeList.capacity.offset,
+                    ctypes.sizeof(_lib.IndexCache), _lib.IndexCache.pool.offset,
+                    _lib.IndexCache.bt.offset]
 
 
 def test_host_validation_rejects_bad_arguments_without_launching():
@@ -97,6 +103,38 @@ def test_host_validation_rejects_bad_arguments_without_launching():
                                     0.1, fake, None, None, 0, None) == 2
     assert lib.hs_sparse_mla_decode(ctypes.byref(b), 2048, 16, 1, fake, 2, fake, fake, fake,
                                     0.1, fake, None, None, 0, None) == 5
+
+
+def test_cache_operations_validate_on_the_host():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(16)
+    ctx = ctypes.c_void_p(32)
+    b = _lib.Batch(2, 1, 1024, 16, 32)
+    res = _lib.Residency(0, 1, 2, 0, 1 << 20, 2048, 16, None, None, None, None, 16, 16, 16, 16,
+                         16, 16, 16)
+    idx = _lib.IndexCache(2, 128, 16, 16, 16)
+    fl = _lib.FreeList(16, 16, 8, 0)
+    ws_n = _lib.workspace_bytes(_lib.HS_OP_CACHE, 2, 1, 1024, 1)
+    assert ws_n >= (2 + 4) * 4
+    args = lambda c, w=ws_n: (ctypes.byref(b), c, fake, ctypes.byref(res), fake, fake,
+                              ctypes.byref(idx), fake, fake, ctypes.byref(fl), ctypes.byref(fl),
+                              fake, w, None)
+    assert lib.hs_append_tokens(*args(fake)) == 2                 # ctx_len is not the batch's
+    assert lib.hs_append_tokens(*args(ctx, 4)) == 5               # workspace too small
+    bad = _lib.FreeList(16, None, 8, 0)
+    assert lib.hs_append_tokens(ctypes.byref(b), ctx, fake, ctypes.byref(res), fake, fake,
+                                ctypes.byref(idx), fake, fake, ctypes.byref(bad),
+                                ctypes.byref(fl), fake, ws_n, None) == 1
+    idx64 = _lib.IndexCache(2, 96, 16, 16, 16)
+    assert lib.hs_append_tokens(ctypes.byref(b), ctx, fake, ctypes.byref(res), fake, fake,
+                                ctypes.byref(idx64), fake, fake, ctypes.byref(fl),
+                                ctypes.byref(fl), fake, ws_n, None) == 2
+    assert lib.hs_precopy_pages(ctypes.byref(b), ctypes.byref(res), 0, None) == 2
+    assert lib.hs_precopy_pages(ctypes.byref(b), ctypes.byref(res), 2000, None) == 2
+    assert lib.hs_demote_pages(ctypes.byref(b), ctypes.byref(res), fake, 0, ctypes.byref(fl),
+                               fake, ws_n, None) == 2            # the tail must stay
+    assert lib.hs_demote_pages(ctypes.byref(b), ctypes.byref(res), None, 1, ctypes.byref(fl),
+                               fake, ws_n, None) == 1
 
 
 def test_workspace_sizes():
