@@ -148,6 +148,97 @@ def cpu_baseline(wl, n_req: int, indexer_q: str = "bf16"):
             "seconds": dt}
 
 
+def cache_ops_bench(torch, reps: int = 5) -> dict:
+    """KV append, pre-copy and demotion on a full-residency batch: 32 requests of
+    65536 tokens (1024 pages each) plus 3 tokens of room, E4M3 rows of one layer,
+    a pinned host pool with one slot per page.  Per rep (state restored untimed):
+    pre-copy of 64 pages per request (2048 pages, 75.5 MB over the host link),
+    demotion of 64 pages per request, append of one token per request (half of
+    them opening a page).  HIP events on the launch stream."""
+    import numpy as np
+    from decode_indexer_logits_amd import _lib
+    _lib.load()
+    B, T0, Ts, L, D, Dk = 32, 65536, 65536 + 64, 1, 576, 128
+    MB = Ts // 64
+    pages = T0 // 64
+    g = torch.Generator(device="cuda").manual_seed(7)
+    nb = B * pages + 2 * B
+    pool = torch.randint(0, 256, (L, nb * 64, D), dtype=torch.uint8, device="cuda", generator=g)
+    row_scale = torch.rand((L, nb * 64), device="cuda", generator=g)
+    perm = torch.randperm(B * pages, device="cuda", generator=g).to(torch.int32)
+    bt0 = torch.full((B, MB), -1, dtype=torch.int32, device="cuda")
+    bt0[:, :pages] = perm.view(B, pages)
+    # every other request ends on a page boundary, so its next token opens a page
+    ctx0 = torch.tensor([T0 if b % 2 == 0 else T0 - 1 for b in range(B)], dtype=torch.int32,
+                        device="cuda")
+    idx_pool = torch.randint(0, 256, (nb, 64, Dk), dtype=torch.uint8, device="cuda", generator=g)
+    idx_scale = torch.rand(nb, device="cuda", generator=g)
+    ibt0 = bt0.clone()
+    free0 = torch.arange(B * pages, nb, dtype=torch.int32, device="cuda")
+    cap = nb
+    free = torch.zeros(cap, dtype=torch.int32, device="cuda")
+    ifree = torch.zeros(cap, dtype=torch.int32, device="cuda")
+    free_n = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ifree_n = torch.zeros(1, dtype=torch.int32, device="cuda")
+    host_rows = torch.empty((L, B * Ts, D), dtype=torch.uint8, pin_memory=True)
+    host_scale = torch.zeros((L, B * Ts), device="cuda")
+    hbt = torch.full((B, MB), -1, dtype=torch.int64, device="cuda")
+    bt, ibt, ctx = bt0.clone(), ibt0.clone(), ctx0.clone()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    step = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(_lib.workspace_bytes(_lib.HS_OP_CACHE, B, 1, Ts, 1), dtype=torch.uint8,
+                     device="cuda")
+    batch = _lib.make_batch(B, 1, Ts, ctx)
+    res = _lib.Residency(0, L, _lib.HS_E4M3, 0, nb * 64, B * Ts, bt.data_ptr(), None, None,
+                         None, None, step.data_ptr(), err.data_ptr(), pool.data_ptr(),
+                         row_scale.data_ptr(), _lib.host_device_ptr(host_rows),
+                         host_scale.data_ptr(), hbt.data_ptr())
+    idx = _lib.IndexCache(_lib.HS_E4M3, Dk, idx_pool.data_ptr(), idx_scale.data_ptr(),
+                          ibt.data_ptr())
+    lf = _lib.FreeList(free.data_ptr(), free_n.data_ptr(), cap, 0)
+    fi = _lib.FreeList(ifree.data_ptr(), ifree_n.data_ptr(), cap, 0)
+    n_new = torch.ones(B, dtype=torch.int32, device="cuda")
+    n_dem = torch.full((B,), 64, dtype=torch.int32, device="cuda")
+    rows = torch.randint(0, 256, (B, 1, L, D), dtype=torch.uint8, device="cuda", generator=g)
+    rsc = torch.rand((B, 1, L), device="cuda", generator=g)
+    keys = torch.randint(0, 256, (B, 1, Dk), dtype=torch.uint8, device="cuda", generator=g)
+    ksc = torch.rand((B, 1), device="cuda", generator=g)
+
+    def restore():
+        bt.copy_(bt0), ibt.copy_(ibt0), ctx.copy_(ctx0), hbt.fill_(-1), err.zero_()
+        nf = free0.numel()
+        free[:nf].copy_(free0), ifree[:nf].copy_(free0)
+        free_n.fill_(nf), ifree_n.fill_(nf)
+
+    st = torch.cuda.current_stream()
+    t = {"precopy": [], "demote": [], "append": []}
+    for r in range(reps + 1):
+        restore()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(st)
+        _lib.precopy_pages(batch, res, 64)
+        ev[1].record(st)
+        _lib.demote_pages(batch, res, n_dem, 1, lf, ws)
+        ev[2].record(st)
+        _lib.append_tokens(batch, ctx, n_new, res, rows, rsc, idx, keys, ksc, lf, fi, ws)
+        ev[3].record(st)
+        torch.cuda.synchronize()
+        if r:
+            t["precopy"].append(ev[0].elapsed_time(ev[1]))
+            t["demote"].append(ev[1].elapsed_time(ev[2]))
+            t["append"].append(ev[2].elapsed_time(ev[3]))
+    assert int(err.item()) == 0 and int(hbt[:, :64].min().item()) >= 0
+    assert int(bt[:, :64].max().item()) == -1 and int(free_n.item()) == free0.numel() + 64 * B - B // 2
+    med = {k: sorted(v)[len(v) // 2] for k, v in t.items()}
+    pc_bytes = B * 64 * 64 * L * (D + 4)
+    return {"workload": "full residency, 32 x 65536 tokens, 1 layer of E4M3 rows",
+            "precopy_ms": round(med["precopy"], 4), "precopy_pages": B * 64,
+            "precopy_GBs": round(pc_bytes / (med["precopy"] / 1e3) / 1e9, 2),
+            "demote_ms": round(med["demote"], 4), "demote_pages": B * 64,
+            "append_ms": round(med["append"], 4), "append_tokens": B,
+            "host_link_peak_GBs": HOST_LINK_PEAK_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +253,8 @@ def main():
                     help="request chunks of the pipelined step (1 = one stream, no overlap)")
     ap.add_argument("--copy-wgs", type=int, default=32,
                     help="workgroups of the fault copy in the pipelined step")
+    ap.add_argument("--cache-ops", action="store_true",
+                    help="also time KV append, pre-copy and demotion (a separate batch)")
     ap.add_argument("--indexer-q", choices=("bf16", "e4m3"), default="bf16",
                     help="indexer query type: the bf16 queries, or E4M3 codes quantized per "
                          "head every step (fp8 x fp8 matrix cores)")
@@ -334,9 +427,15 @@ def main():
         "single_stream_ms_per_step": round(single_ms, 4),
         "wall_s_timed_loop_incl_restore_flush": round(wall, 4),
     }
+    indexer_q = ds.indexer_q
+    if a.cache_ops:
+        del ds, snap, flush_buf
+        torch.cuda.empty_cache()
+        result["cache_ops"] = cache_ops_bench(torch)
+        log(f"[bench] cache ops {json.dumps(result['cache_ops'])}")
     if not a.no_cpu_baseline:
         log("[bench] timing the oracle on host cores")
-        cb = cpu_baseline(wl, a.cpu_requests, ds.indexer_q)
+        cb = cpu_baseline(wl, a.cpu_requests, indexer_q)
         cb["value"] = round(cb["value"], 5)
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
