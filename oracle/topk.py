@@ -56,3 +56,30 @@ def kth_score(scores_row: np.ndarray, n_visible: int, K: int) -> float:
         return -np.inf
     s = np.asarray(scores_row[:n], dtype=np.float64)
     return float(np.partition(s, n - K)[n - K])
+
+
+def topk_sharded_row(scores_row: np.ndarray, n_visible: int, K: int, shard_len: int) -> np.ndarray:
+    """The selection computed the way a token-sharded cache would: the visible
+    tokens are cut into contiguous shards of shard_len tokens, each shard keeps
+    its own top-K (the rule of topk_row), and the K best of the union of those
+    candidates are kept (same order and tie rule), in ascending token order.
+
+    Page "Un contexte d'un million sur huit H200", section "Les chiffres" (DCP:
+    the KV cache is split across GPUs by tokens).  Every token of the global
+    top-K is in its shard's top-K, so this equals topk_row; the function is the
+    definition the sharded GPU path follows, and the tests pin the equality.
+    """
+    n = max(int(n_visible), 0)
+    cand = []
+    for s0 in range(0, n, shard_len):
+        m = min(shard_len, n - s0)
+        sel = topk_row(np.asarray(scores_row)[s0:s0 + m], m, K)
+        cand.extend(int(t) + s0 for t in sel if t >= 0)
+    cand = np.array(sorted(cand), dtype=np.int64)
+    out = np.full(K, -1, dtype=np.int32)
+    if len(cand) == 0:
+        return out
+    sub = topk_row(np.asarray(scores_row)[cand], len(cand), K)
+    sub = sub[sub >= 0]
+    out[:len(sub)] = cand[sub]
+    return out

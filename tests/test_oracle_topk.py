@@ -52,3 +52,34 @@ def test_kth_score():
     s = np.array([3.0, 1.0, 2.0, 5.0])
     assert topk.kth_score(s, 4, 2) == 3.0
     assert topk.kth_score(s, 4, 4) == -np.inf
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sharded_selection_equals_the_global_one(seed):
+    # Every token of the global top-K is among its shard's top-K, so the merge
+    # of the shards' selections is the global selection, ties included.
+    from oracle import topk as ot
+    rng = np.random.default_rng(900 + seed)
+    for _ in range(20):
+        shard = int(rng.choice([64, 128, 256]))
+        n = int(rng.integers(0, 6 * shard))
+        K = int(rng.integers(1, 3 * shard))
+        # coarse scores: many exact ties across shards
+        row = np.round(rng.standard_normal(6 * shard) * 3) / 2
+        row[rng.random(row.shape) < 0.1] = -0.0
+        got = ot.topk_sharded_row(row, n, K, shard)
+        assert np.array_equal(got, ot.topk_row(row, n, K)), (n, K, shard)
+
+
+def test_sharded_selection_brute_force_small():
+    # exhaustive over every score pattern of 6 tokens with values in {0, 1, 2}
+    import itertools
+    from oracle import topk as ot
+    for vals in itertools.product([0.0, 1.0, 2.0], repeat=6):
+        row = np.array(vals)
+        for K in (1, 2, 3, 5):
+            for shard in (1, 2, 4):
+                order = sorted(range(6), key=lambda t: (-row[t], t))[:K]
+                want = np.full(K, -1)
+                want[:min(K, 6)] = sorted(order)
+                assert np.array_equal(ot.topk_sharded_row(row, 6, K, shard), want)
