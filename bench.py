@@ -253,6 +253,8 @@ def main():
                     help="request chunks of the pipelined step (1 = one stream, no overlap)")
     ap.add_argument("--copy-wgs", type=int, default=32,
                     help="workgroups of the fault copy in the pipelined step")
+    ap.add_argument("--topk-shards", type=int, default=0,
+                    help="also time the token-sharded top-K with this many shards (P = 1)")
     ap.add_argument("--cache-ops", action="store_true",
                     help="also time KV append, pre-copy and demotion (a separate batch)")
     ap.add_argument("--indexer-q", choices=("bf16", "e4m3"), default="bf16",
@@ -352,6 +354,17 @@ def main():
     stage_ms["topk"], _ = _time_launches(ds.run_topk, a.kernel_reps, torch, None, flush)
     stage_ms["indexer_topk"], _ = _time_launches(ds.run_indexer_topk, a.kernel_reps, torch, None,
                                                  flush)
+    if a.topk_shards and wl.P == 1:
+        from decode_indexer_logits_amd import _lib
+        S = a.topk_shards
+        sh_out = torch.empty_like(ds.topk)
+        sh_ws = torch.empty(_lib.topk_sharded_workspace_bytes(wl.B, wl.T_stride, wl.K, S),
+                            dtype=torch.uint8, device="cuda")
+        run_sh = lambda: _lib.topk_sharded(ds.batch, wl.K, S, ds.scores, sh_out, sh_ws)
+        stage_ms[f"topk_sharded_{S}"], _ = _time_launches(run_sh, a.kernel_reps, torch, None, flush)
+        ds.run_topk()
+        torch.cuda.synchronize()
+        assert torch.equal(sh_out, ds.topk), "sharded top-K differs from hs_topk"
     stage_ms["resolve_tables"], _ = _time_launches(ds.run_resolve_tables, a.kernel_reps, torch,
                                                    restore, flush)
 

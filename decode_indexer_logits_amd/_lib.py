@@ -22,7 +22,8 @@ DEVERR_VICTIMS, DEVERR_NO_HOST = 1, 2
 DEVERR_APPEND_RANGE, DEVERR_APPEND_NO_BLOCK, DEVERR_DEMOTE_FULL = 4, 8, 16
 
 EXPORTS = ["hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
-           "hs_sparse_mla_decode", "hs_append_tokens", "hs_precopy_pages", "hs_demote_pages",
+           "hs_sparse_mla_decode", "hs_topk_sharded", "hs_topk_sharded_workspace_bytes",
+           "hs_append_tokens", "hs_precopy_pages", "hs_demote_pages",
            "hs_workspace_bytes", "hs_host_device_ptr", "hs_last_error", "hs_abi_version"]
 
 
@@ -79,6 +80,10 @@ def load() -> ctypes.CDLL:
     lib.hs_copy_faults.argtypes = [P, c_int32, P, P, P, c_int32, P]
     lib.hs_sparse_mla_decode.argtypes = [P, c_int32, c_int32, c_int32, P, c_int32, P, P, P,
                                          c_float, P, P, P, c_size_t, P]
+    lib.hs_topk_sharded.argtypes = [P, c_int32, c_int32, P, P, P, c_size_t, P]
+    lib.hs_topk_sharded.restype = c_int32
+    lib.hs_topk_sharded_workspace_bytes.argtypes = [c_int32] * 4
+    lib.hs_topk_sharded_workspace_bytes.restype = c_size_t
     lib.hs_append_tokens.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, c_size_t, P]
     lib.hs_precopy_pages.argtypes = [P, P, c_int32, P]
     lib.hs_demote_pages.argtypes = [P, P, P, c_int32, P, P, c_size_t, P]
@@ -208,5 +213,15 @@ def demote_pages(batch: Batch, res: Residency, n_demote, tail_pages: int, latent
                  ws, stream=None):
     _check(load().hs_demote_pages(ctypes.byref(batch), ctypes.byref(res), _ptr(n_demote),
                                   tail_pages, ctypes.byref(latent_free), _ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(),
+                                  _stream(stream)))
+
+
+def topk_sharded_workspace_bytes(B: int, T_stride: int, K: int, S: int) -> int:
+    return load().hs_topk_sharded_workspace_bytes(B, T_stride, K, S)
+
+
+def topk_sharded(batch: Batch, K: int, S: int, scores, out, ws, stream=None):
+    _check(load().hs_topk_sharded(ctypes.byref(batch), K, S, _ptr(scores), _ptr(out), _ptr(ws),
                                   0 if ws is None else ws.numel() * ws.element_size(),
                                   _stream(stream)))

@@ -21,7 +21,7 @@ OUT = PKG / "libhisparse.so"
 BUILD = ROOT / "_build"
 ARCH = "gfx950"
 
-SOURCES = ["indexer.hip", "topk.hip", "resolve.hip", "mla.hip", "cache_ops.hip", "hs_api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "resolve.hip", "mla.hip", "cache_ops.hip", "shard_topk.hip", "hs_api.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-mllvm", "-amdgpu-mfma-vgpr-form",

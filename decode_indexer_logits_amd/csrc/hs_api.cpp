@@ -178,6 +178,30 @@ hs_status hs_indexer_topk(const hs_batch* batch, int32_t H_idx, int32_t D_idx, h
   return launched(e, "indexer + top-K");
 }
 
+size_t hs_topk_sharded_workspace_bytes(int32_t B, int32_t T_stride, int32_t K, int32_t S) {
+  if (B < 1 || K < 1 || S < 1 || S > 64 || T_stride < 64 * S || T_stride % (64 * S)) return 0;
+  return hs::topk_sharded_workspace_bytes(B, T_stride, K, S);
+}
+
+hs_status hs_topk_sharded(const hs_batch* batch, int32_t K, int32_t S, const float* scores,
+                          int32_t* topk, void* ws, size_t ws_bytes, void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!scores || !topk) return fail(HS_ERR_NULL, "hs_topk_sharded: scores and topk are required");
+  if (d.P != 1) return fail(HS_ERR_SHAPE, "hs_topk_sharded: one query position (P=%d)", d.P);
+  if (K < 1 || K > 8192) return fail(HS_ERR_SHAPE, "K=%d out of [1, 8192]", K);
+  if (S < 1 || S > 64 || d.T_stride % (64 * S))
+    return fail(HS_ERR_SHAPE, "S=%d must be in [1, 64] and T_stride=%d a multiple of 64*S", S,
+                d.T_stride);
+  if (!aligned16(scores)) return fail(HS_ERR_ALIGN, "hs_topk_sharded: scores need 16-byte alignment");
+  const size_t need = hs::topk_sharded_workspace_bytes(d.B, d.T_stride, K, S);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "sharded top-K needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace needs 16-byte alignment");
+  return launched(hs::launch_topk_sharded(d, K, S, scores, topk, ws, static_cast<hipStream_t>(stream)),
+                  "sharded top-K");
+}
+
 hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t* topk, void* ws,
                   size_t ws_bytes, void* stream) {
   hs::BatchDims d;

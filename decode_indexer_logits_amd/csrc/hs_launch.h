@@ -34,6 +34,9 @@ hipError_t launch_indexer_f32(const BatchDims& d, int H, int DK, const float* q,
 size_t topk_workspace_bytes(int B, int P, int T_stride, int K);
 hipError_t launch_topk(const BatchDims& d, int K, const float* scores, int32_t* topk, void* ws,
                        hipStream_t s);
+size_t topk_sharded_workspace_bytes(int B, int T_stride, int K, int S);
+hipError_t launch_topk_sharded(const BatchDims& d, int K, int S, const float* scores,
+                               int32_t* topk, void* ws, hipStream_t s);
 // The pieces of the fused indexer + top-K: zero the workspace counters (and
 // return the histogram the indexer fills), then select from that histogram.
 hipError_t launch_topk_zero(const BatchDims& d, int K, void* ws, uint32_t** hist, hipStream_t s);

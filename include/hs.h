@@ -158,6 +158,21 @@ hs_status hs_quantize_queries(const hs_batch* batch, int32_t H_idx, int32_t D_id
 hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t* topk,
                   void* ws, size_t ws_bytes, void* stream);
 
+/* Token-sharded top-K: the selection as a cache split across GPUs by tokens
+ * makes it (page "Un contexte d'un million sur huit H200", section "Les
+ * chiffres": DCP splits the KV cache by tokens), emulated on one GPU.  Each
+ * request's tokens are cut into S contiguous shards of T_stride/S tokens; each
+ * shard keeps its own top-K, and the K best of the union of those candidates
+ * are kept, with the same order and tie rule.  The result equals hs_topk's
+ * (every token of the global top-K is in its shard's top-K); a few long rows
+ * become S times as many short ones for the radix select.
+ * One query position (batch->P == 1); 1 <= S <= 64 and T_stride a multiple of
+ * 64*S; 1 <= K <= 8192; scores 16-byte aligned.  Workspace:
+ * hs_topk_sharded_workspace_bytes(B, T_stride, K, S), 16-byte aligned. */
+hs_status hs_topk_sharded(const hs_batch* batch, int32_t K, int32_t S, const float* scores,
+                          int32_t* topk, void* ws, size_t ws_bytes, void* stream);
+size_t hs_topk_sharded_workspace_bytes(int32_t B, int32_t T_stride, int32_t K, int32_t S);
+
 /* hs_indexer_scores followed by hs_topk, with the first pass of the top-K
  * radix select (the per-row histogram of the top 11 score-key bits) built in
  * the indexer's epilogue instead of a separate pass over the scores.  Same
