@@ -82,6 +82,21 @@ def test_resident_fp8_ragged_batch():
     _say(info, wl.ctx_len)
 
 
+def test_empty_single_and_page_edge_requests():
+    """A request with no tokens (every output -1, attention output 0 and lse
+    -inf), one token, and contexts at and around page edges, shorter and
+    longer than K, through the whole step."""
+    _say("edge contexts [0, 1, 63, 64, 65, 130, 2000]")
+    wl = gen.resident_fp8(K=128, ctx_len=[0, 1, 63, 64, 65, 130, 2000])
+    ds = _run(wl)
+    _, _, info = gc.full_check(ds, wl, gc.oracle_state(wl), attn_tol=2e-2)
+    g = gc.gpu_outputs(ds)
+    assert np.all(g["topk"][0] == -1) and np.all(g["out"][:, 0] == 0)
+    assert np.all(np.isneginf(g["lse"][:, 0]))
+    assert np.array_equal(g["topk"][1, 0, :2], [0, -1])
+    _say(info)
+
+
 def _mixed_small(B=4, T=16384, K=512, tail=1024, seed=1003):
     beta, hot, frac = calibrate(seed=seed, B=B, T=T, K=K, tail=tail)
     return gen.mixed_128k(seed=seed, B=B, T=T, K=K, tail=tail, beta=beta, hot_tokens=hot)

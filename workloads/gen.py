@@ -403,16 +403,20 @@ def tiny_fp32(K: int = 256, seed: int = 1001, T: int = 4096) -> Workload:
 
 
 def resident_fp8(seed: int = 1002, B: int = 8, T_lo: int = 16384, T_hi: int = 32768,
-                 K: int = 2048) -> Workload:
+                 K: int = 2048, ctx_len=None) -> Workload:
     """B=8, T ~ U{16K..32K}, K=2048, 16 bf16 heads (one shard of 128), fp8
     latent and indexer keys with per-block scales, indexer 64 heads x 128, an
     attention-sink bias of +2 sigma on the first 64 and last 256 tokens, whole
-    cache resident in shuffled blocks."""
+    cache resident in shuffled blocks.  ctx_len, when given, fixes the context
+    lengths (and B) instead of drawing them."""
     ch = _children(seed)
     P, Hq, H, D, L = 1, 16, 64, 128, 1
     g0 = np.random.Generator(np.random.PCG64(ch[0]))
     ctx = g0.integers(T_lo, T_hi + 1, size=B).astype(np.int32)
-    Ts = _round_up(int(ctx.max()), BLOCK)
+    if ctx_len is not None:
+        ctx = np.asarray(ctx_len, dtype=np.int32)
+        B = len(ctx)
+    Ts = max(_round_up(int(ctx.max()), BLOCK), BLOCK)
     idx_pool, idx_scale, idx_bt = _indexer_cache(ch, B, ctx, Ts, D, fp8=True)
     q_idx = _queries(ch[4], (B, P, H, D), "bf16")
     w = uniform_f32(ch[5], (B, P, H))
