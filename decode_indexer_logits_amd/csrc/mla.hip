@@ -296,72 +296,75 @@ __global__ __launch_bounds__(kMlaNT) void mla_f32_kernel(
   }
 }
 
-// Merges the slices of each (request, position, head) in slice order: one
-// wave per (request, position, head), 8 output dims per lane.  The slices'
-// maxima and sums are read by one lane each and combined with wave
-// reductions; the partial outputs are then read four slices at a time, so
-// their loads overlap.
+// Merges the slices of each (request, position, head) in slice order: two
+// waves per (request, position, head), each for 256 of the 512 output dims
+// (one float4 per lane).  Every slice's maximum and sum are read at once, a
+// lane per slice, and combined with wave reductions; each slice's weight is
+// then broadcast from its lane while the partial outputs stream in eight
+// slices at a time with no load waiting on another.
+constexpr int kCombineMaxSplit = 128;   // K <= 8192 rows in tiles of 64
 __global__ __launch_bounds__(kWave) void mla_combine_kernel(int nsplit, const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
                                                             float* __restrict__ out,
                                                             float* __restrict__ lse) {
-  const int bp = blockIdx.x, h = blockIdx.y;
+  const int bp = blockIdx.x, h = blockIdx.y, half = blockIdx.z;
   const int lane = threadIdx.x;
   auto ml_index = [&](int sidx) { return (((size_t)bp * nsplit + sidx) * kHq + h) * 2; };
+  // every split's (m, l) at once: lane s holds splits s and 64 + s
+  float ms[kCombineMaxSplit / kWave], ls[kCombineMaxSplit / kWave];
   float M = -INFINITY;
-  for (int s0 = 0; s0 < nsplit; s0 += kWave) {
-    const int sidx = s0 + lane;
-    const float ms = sidx < nsplit ? part_ml[ml_index(sidx)] : -INFINITY;
-    M = fmaxf(M, ms);
+#pragma unroll
+  for (int k = 0; k < kCombineMaxSplit / kWave; ++k) {
+    const int sidx = kWave * k + lane;
+    ms[k] = sidx < nsplit ? part_ml[ml_index(sidx)] : -INFINITY;
+    ls[k] = sidx < nsplit ? part_ml[ml_index(sidx) + 1] : 0.f;
+    M = fmaxf(M, ms[k]);
   }
   M = max_rows16(M);
   M = fmaxf(M, __shfl_xor(M, 1));
   M = fmaxf(M, __shfl_xor(M, 2));
   M = fmaxf(M, __shfl_xor(M, 4));
   M = fmaxf(M, __shfl_xor(M, 8));
-  float acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  float wl[kCombineMaxSplit / kWave];
   float L = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < nsplit; s0 += 4) {
-      float wgt[4];
-      float4 v[4][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int sidx = s0 + u;
-        wgt[u] = 0.f;
-        v[u][0] = v[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (sidx < nsplit) {
-          const size_t base = ((size_t)bp * nsplit + sidx) * kHq + h;
-          const float ms = part_ml[base * 2];
-          if (ms != -INFINITY) {
-            wgt[u] = exp2f(ms - M);
-            L += part_ml[base * 2 + 1] * wgt[u];
-            const float4* src = reinterpret_cast<const float4*>(part_o + base * kDVal) + lane;
-            v[u][0] = src[0];
-            v[u][1] = src[64];
-          }
-        }
-      }
+  for (int k = 0; k < kCombineMaxSplit / kWave; ++k) {
+    wl[k] = (M != -INFINITY && ms[k] != -INFINITY) ? exp2f(ms[k] - M) : 0.f;
+    L = fmaf(ls[k], wl[k], L);
+  }
+  L = sum_rows16(L);
+  L += __shfl_xor(L, 1);
+  L += __shfl_xor(L, 2);
+  L += __shfl_xor(L, 4);
+  L += __shfl_xor(L, 8);
+  // values: this wave's 256 of the 512 dims, one float4 per lane per split, in
+  // split order; a split's partial output is finite (zero when it saw no row),
+  // so every load is unconditional and weight 0 drops it
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4* src = reinterpret_cast<const float4*>(
+                          part_o + (((size_t)bp * nsplit) * kHq + h) * kDVal + 256 * half) + lane;
+  const size_t split_stride = (size_t)kHq * kDVal / 4;      // float4s from one split to the next
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float4 v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u)
+      v[u] = (s0 + u < nsplit) ? src[(size_t)(s0 + u) * split_stride] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[4 * j + 0] = fmaf(v[u][j].x, wgt[u], acc[4 * j + 0]);
-          acc[4 * j + 1] = fmaf(v[u][j].y, wgt[u], acc[4 * j + 1]);
-          acc[4 * j + 2] = fmaf(v[u][j].z, wgt[u], acc[4 * j + 2]);
-          acc[4 * j + 3] = fmaf(v[u][j].w, wgt[u], acc[4 * j + 3]);
-        }
+    for (int u = 0; u < 8; ++u) {
+      const int sidx = s0 + u;
+      const float wsel = sidx < kWave ? wl[0] : wl[1];
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsel), sidx & (kWave - 1)));
+      acc.x = fmaf(v[u].x, w, acc.x);
+      acc.y = fmaf(v[u].y, w, acc.y);
+      acc.z = fmaf(v[u].z, w, acc.z);
+      acc.w = fmaf(v[u].w, w, acc.w);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float4* dst = reinterpret_cast<float4*>(out + ((size_t)bp * kHq + h) * kDVal) + lane;
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    dst[64 * j] = make_float4(acc[4 * j] * inv, acc[4 * j + 1] * inv, acc[4 * j + 2] * inv,
-                              acc[4 * j + 3] * inv);
-  if (lse && lane == 0) lse[(size_t)bp * kHq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  reinterpret_cast<float4*>(out + ((size_t)bp * kHq + h) * kDVal + 256 * half)[lane] =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (lse && half == 0 && lane == 0)
+    lse[(size_t)bp * kHq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 __host__ inline int rows_per_split_for(int K, int nsplit) {
@@ -374,6 +377,7 @@ __host__ inline int rows_per_split_for(int K, int nsplit) {
 int mla_num_splits(int B, int P, int K) {
   const int BP = B * P;
   const int max_split = (K + kTile - 1) / kTile;
+  static_assert(8192 / kTile <= kCombineMaxSplit, "one lane per slice in the combine");
   int ns = (kMlaTargetWGs + BP - 1) / BP;
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
@@ -406,7 +410,7 @@ hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, const uint16_t* q, co
                      row_scale, row_ids, K, rps, ns, qk, out, lse, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq), dim3(kWave), 0, s, ns, part_o, part_ml, out, lse);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq, 2), dim3(kWave), 0, s, ns, part_o, part_ml, out, lse);
   return hipGetLastError();
 }
 
@@ -423,7 +427,7 @@ hipError_t launch_mla_f32(const BatchDims& d, int K, const float* q, const float
                      qk, ns > 1 ? 1 : 0, out, lse, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq), dim3(kWave), 0, s, ns, part_o, part_ml, out, lse);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq, 2), dim3(kWave), 0, s, ns, part_o, part_ml, out, lse);
   return hipGetLastError();
 }
 
