@@ -239,6 +239,95 @@ def cache_ops_bench(torch, reps: int = 5) -> dict:
             "host_link_peak_GBs": HOST_LINK_PEAK_GBS}
 
 
+def ceilings(torch, ds, wl, reps: int = 10) -> dict:
+    """Measured ceilings on this machine, as context for the fractions of the published peaks
+    (probe kernels of libhsprobe.so, HIP events, MALL flushed before each launch):
+    - the indexer's key pages read in the indexer's own page order with no products and
+      no score writes (the same grid and two pages in flight per wave);
+    - a plain stream of the same number of bytes over the key pool;
+    - a 256 MiB DMA copy from pinned host memory to HBM (the host link)."""
+    import ctypes
+    from pathlib import Path
+    import numpy as np
+    lib = ctypes.CDLL(str(Path(ROOT) / "decode_indexer_logits_amd" / "libhsprobe.so"))
+    vp = ctypes.c_void_p
+    lib.hsp_read_stream.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, vp]
+    lib.hsp_read_pages.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+    flush_buf = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    sink0 = torch.empty((), dtype=torch.float32, device="cuda")
+    flush = lambda: torch.sum(flush_buf, dim=0, out=sink0)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    st = vp(torch.cuda.current_stream().cuda_stream)
+    out = {}
+    key_bytes = int(wl.ctx_len.astype(np.int64).sum()) * wl.D_idx
+    if wl.D_idx == 128 and wl.k_dtype == "e4m3":
+        def pages():
+            r = lib.hsp_read_pages(vp(ds.ctx_len.data_ptr()), wl.B, wl.T_stride,
+                                   wl.T_stride // 64, vp(ds.idx_pool.data_ptr()),
+                                   vp(ds.idx_bt.data_ptr()), vp(sink.data_ptr()), st)
+            assert r == 0, f"hsp_read_pages: hip error {r}"
+        pages_ms, _ = _time_launches(pages, reps, torch, None, flush)
+        out["key_pages_in_indexer_order_GBs"] = round(key_bytes / (pages_ms / 1e3) / 1e9, 1)
+        out["key_pages_us"] = round(pages_ms * 1e3, 1)
+    n = (ds.idx_pool.numel() * ds.idx_pool.element_size()) // 16 * 16
+    n = min(n, key_bytes)
+
+    def stream():
+        r = lib.hsp_read_stream(vp(ds.idx_pool.data_ptr()), n, 512, vp(sink.data_ptr()), st)
+        assert r == 0, f"hsp_read_stream: hip error {r}"
+    stream_ms, _ = _time_launches(stream, reps, torch, None, flush)
+    out["plain_read_stream_GBs"] = round(n / (stream_ms / 1e3) / 1e9, 1)
+    out["plain_read_stream_bytes"] = int(n)
+    src = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    dma_ms, _ = _time_launches(lambda: dst.copy_(src, non_blocking=True), reps, torch)
+    out["host_dma_GBs"] = round((256 << 20) / (dma_ms / 1e3) / 1e9, 2)
+    del src, dst, flush_buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def sequence_bench(ds, wl, torch, step_fn, flush, snap0, repeats: int) -> dict:
+    """The workload's step sequence in order (steps 1..n with that step's queries), from
+    the initial residency state, `repeats` times.  Per step: the median step time (HIP
+    events around the captured step; query upload and MALL flush before the start event)
+    and, per request, the resident / hit / fault counts and the hit rate over the
+    host-only tokens selected: hits / (hits + faults).  snap0: the initial state."""
+    st = torch.cuda.current_stream()
+    ms = [[] for _ in range(wl.steps)]
+    counts = [None] * wl.steps
+    for rep in range(repeats):
+        ds.restore(snap0)
+        for s in range(1, wl.steps + 1):
+            ds.set_queries(s)
+            flush()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            step_fn()
+            b.record(st)
+            torch.cuda.synchronize()
+            ms[s - 1].append(a.elapsed_time(b))
+            c = ds.counts.cpu().numpy().sum(axis=0)
+            if counts[s - 1] is None:
+                counts[s - 1] = c
+            elif not (counts[s - 1] == c).all():
+                raise RuntimeError(f"step {s} counts differ between repeats")
+    ds.restore(snap0)
+    ds.set_queries(1)
+    torch.cuda.synchronize()
+    med = [sorted(m)[len(m) // 2] for m in ms]
+    hit_rate = [float(c[1]) / max(int(c[1]) + int(c[2]), 1) for c in counts]
+    return {"steps": wl.steps, "repeats": repeats,
+            "ms_per_step": [round(x, 4) for x in med],
+            "hit_rate": [round(x, 4) for x in hit_rate],
+            "per_request": {k: [round(float(c[i]) / wl.B, 1) for c in counts]
+                            for i, k in enumerate(["resident", "hit", "fault", "evicted"])},
+            "sequence_steps_per_s": round(wl.steps / (sum(med) / 1e3), 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +346,8 @@ def main():
                     help="also time the token-sharded top-K with this many shards (P = 1)")
     ap.add_argument("--cache-ops", action="store_true",
                     help="also time KV append, pre-copy and demotion (a separate batch)")
+    ap.add_argument("--seq-repeats", type=int, default=3,
+                    help="repeats of the step sequence of multi-step workloads (0: skip)")
     ap.add_argument("--indexer-q", choices=("bf16", "e4m3"), default="bf16",
                     help="indexer query type: the bf16 queries, or E4M3 codes quantized per "
                          "head every step (fp8 x fp8 matrix cores)")
@@ -376,6 +467,15 @@ def main():
     stage_ms["attention"], _ = _time_launches(lambda: [ds.run_attention(l) for l in range(wl.L)],
                                               a.kernel_reps, torch, None, flush)
     log(f"[bench] stage ms {json.dumps({k: round(v, 4) for k, v in stage_ms.items()})}")
+    ceil = ceilings(torch, ds, wl)
+    if "key_pages_us" in ceil:
+        ceil["indexer_time_over_key_pages_time"] = round(stage_ms["indexer"] * 1e3 /
+                                                         ceil["key_pages_us"], 3)
+    log(f"[bench] ceilings {json.dumps(ceil)}")
+    seq = None
+    if wl.steps > 1 and a.seq_repeats > 0:
+        seq = sequence_bench(ds, wl, torch, step_fn, flush, snap, a.seq_repeats)
+        log(f"[bench] sequence {json.dumps(seq)}")
     alg = _algorithmic_bytes(wl, counts)
     idx_bytes = sum(alg["indexer"].values())
     hbm_phase_bytes = (idx_bytes + sum(alg["topk"].values()) + sum(alg["resolve"].values())
@@ -433,11 +533,14 @@ def main():
         "host_link": {"bound": "pcie", "kernel": "fault_copy", "achieved": round(link_gbs, 2),
                       "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
                       "frac": round(link_gbs / HOST_LINK_PEAK_GBS, 4),
-                      "bytes": alg["host_link"], "avg_ms": round(stage_ms["fault_copy"], 4)},
+                      "bytes": alg["host_link"], "avg_ms": round(stage_ms["fault_copy"], 4),
+                      "frac_of_measured_dma": round(link_gbs / ceil["host_dma_GBs"], 4)},
+        "ceilings": ceil,
         "residency_counts_per_request": dict(zip(["resident", "hit", "fault", "evicted"],
                                                  counts.mean(axis=0).round(2).tolist())),
         "device_error_bits": err,
         "single_stream_ms_per_step": round(single_ms, 4),
+        "sequence": seq,
         "wall_s_timed_loop_incl_restore_flush": round(wall, 4),
     }
     indexer_q = ds.indexer_q

@@ -1,4 +1,5 @@
-"""Builds the HIP library ``libhisparse.so`` in-tree for gfx950.
+"""Builds the HIP library ``libhisparse.so`` in-tree for gfx950, and the
+bandwidth-probe library ``libhsprobe.so`` that only the benchmark loads.
 
 Run ``python -m decode_indexer_logits_amd.build``.  Every source is compiled
 with hipcc for gfx950 only (packed-fp32 instruction selection disabled), in
@@ -18,6 +19,7 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 OUT = PKG / "libhisparse.so"
+PROBE_OUT = PKG / "libhsprobe.so"
 BUILD = ROOT / "_build"
 ARCH = "gfx950"
 
@@ -60,7 +62,19 @@ def build(verbose: bool = False) -> Path:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, OUT)
+    build_probe()
     return OUT
+
+
+def build_probe() -> Path:
+    """Compiles csrc/probe.hip (benchmark bandwidth probes) into libhsprobe.so."""
+    tmp = PROBE_OUT.with_suffix(".so.tmp")
+    cmd = [hipcc(), *FLAGS, "-shared", str(CSRC / "probe.hip"), "-o", str(tmp)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on probe.hip:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE_OUT)
+    return PROBE_OUT
 
 
 if __name__ == "__main__":

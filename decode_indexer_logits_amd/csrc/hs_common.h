@@ -142,34 +142,43 @@ __device__ __forceinline__ float wave_max_xor(float v, int from) {
   return v;
 }
 
-// Exclusive prefix sum over a block of NT threads; `scratch` holds NT/64 + 1
-// ints.  Returns the thread's exclusive prefix; *total receives the block sum.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
+// 1, 2, 4 and 8 lanes inside each 16-lane row (lanes without a source add
+// zero), then lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into
+// rows 2 and 3.  All 64 lanes must be active.
+__device__ __forceinline__ int wave_inclusive_scan_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return x;
+}
+
+// Exclusive prefix sum over a block of NT threads (at most 16 waves); every
+// thread must call it.  `scratch` holds NT/64 + 1 ints.  Returns the thread's
+// exclusive prefix; *total receives the block sum.  Each wave scans its lanes
+// with DPP, the wave sums meet in LDS, and every wave scans the (at most 16)
+// wave sums in its first row: two barriers, no serial loop.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  constexpr int NW = NT / kWave;
+  static_assert(NT % kWave == 0 && NW >= 1 && NW <= 16, "one to sixteen whole waves");
   const int lane = lane_id();
-  const int wid = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int x = wave_inclusive_scan_i32(v);
   if (lane == kWave - 1) scratch[wid] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < NT / kWave; ++i) {
-      int t = scratch[i];
-      scratch[i] = run;
-      run += t;
-    }
-    scratch[NT / kWave] = run;
-  }
-  __syncthreads();
-  int r = scratch[wid] + x - v;
-  *total = scratch[NT / kWave];
-  __syncthreads();
-  return r;
+  int ws = lane < NW ? scratch[lane] : 0;
+  ws += __builtin_amdgcn_update_dpp(0, ws, 0x111, 0xF, 0xF, false);
+  ws += __builtin_amdgcn_update_dpp(0, ws, 0x112, 0xF, 0xF, false);
+  ws += __builtin_amdgcn_update_dpp(0, ws, 0x114, 0xF, 0xF, false);
+  ws += __builtin_amdgcn_update_dpp(0, ws, 0x118, 0xF, 0xF, false);
+  const int before = wid ? __builtin_amdgcn_readlane(ws, wid - 1) : 0;
+  *total = __builtin_amdgcn_readlane(ws, NW - 1);
+  __syncthreads();   // the next call may rewrite scratch
+  return before + x - v;
 }
 
 }  // namespace hs

@@ -10,7 +10,8 @@
 //   2. histogram  of the top 11 key bits, per 8192-token chunk: LDS counts,
 //                 then one global atomic per non-empty bin (the fused path of
 //                 hs_indexer_topk builds it in the indexer's epilogue instead)
-//   3. filter     one wave of every 4096-token workgroup finds the bin b1
+//   3. filter     one wave of every 4096-token workgroup (16384 on rows over
+//                 2^18 tokens) finds the bin b1
 //                 holding the K-th largest key from the row's histogram; keys
 //                 above b1 are selected outright, keys in b1 become candidates;
 //                 the workgroup reserves its output ranges with one pair of
@@ -19,8 +20,8 @@
 //                 with the radix select over them (key bits 20..10, then 9..0),
 //                 sends ties at the threshold to the lower token (radix select
 //                 on the token index), and writes the K tokens in ascending
-//                 order through an LDS bitmap (one for rows up to 786432
-//                 tokens, else one per 64K-token segment).
+//                 order: an LDS bitmap per 786432 tokens, each selected token
+//                 placed by the popcounts before it.
 // Passes 3 and 4 stay separate kernels: handing a row from many workgroups to
 // one inside a kernel needs a device-scope release per workgroup, which on a
 // multi-die GPU writes back L2 and costs far more than a kernel boundary.
@@ -36,14 +37,12 @@ namespace {
 
 constexpr int kBins1 = 2048;   // top 11 key bits
 constexpr int kChunk = 8192;   // tokens per workgroup of the histogram pass
-constexpr int kFChunk = 4096;  // tokens per workgroup of the filter pass
+constexpr int kFChunk = 4096;  // tokens per workgroup of the filter pass (rows up to 2^18)
+constexpr int kFChunkLong = 16384;   // the same for longer rows
 constexpr int kScanNT = 256;
-constexpr int kFPer = kFChunk / kScanNT / 4;   // 16-byte loads per filter thread
 constexpr int kMaxK = 8192;
 constexpr int kCnt = 8;                   // counters per row
 constexpr int kFinNT = 1024;
-constexpr int kSegTok = 1 << 16;          // tokens per bitmap segment in finalize
-constexpr int kSegWords = kSegTok / 32;
 constexpr int kFinCand = 12288;           // candidates staged in LDS by finalize
 
 struct TopkWs {
@@ -242,35 +241,10 @@ __device__ void candidates_threshold(const uint32_t* ck, const int32_t* ct, int 
   *t_cut_out = t_cut;
 }
 
-// Writes the set bits of bm[0, nwords) as ascending tokens t_base + bit to
-// out[written ...]; returns the number written.  Every thread must call it.
-template <int NT, int WPT>
-__device__ int emit_bitmap(const uint32_t* bm, int nwords, int t_base, int written,
-                           int32_t* __restrict__ out, int* scratch) {
-  const int tid = threadIdx.x;
-  uint32_t wd[WPT];
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < WPT; ++j) {
-    const int w = tid * WPT + j;
-    wd[j] = w < nwords ? bm[w] : 0u;
-    cnt += __popc(wd[j]);
-  }
-  int tot;
-  int pos = written + block_exclusive_scan<NT>(cnt, scratch, &tot);
-#pragma unroll
-  for (int j = 0; j < WPT; ++j) {
-    uint32_t x = wd[j];
-    const int t0 = t_base + (tid * WPT + j) * 32;
-    while (x) {
-      const int bit = __ffs(x) - 1;
-      out[pos++] = t0 + bit;
-      x &= x - 1;
-    }
-  }
-  return tot;
-}
-
+// FCH tokens per workgroup: 4096, or 16384 on rows longer than 2^18 tokens so
+// that at most 64 workgroups per row share the row's two output counters
+// (same-address atomics from every die serialize).
+template <int FCH>
 __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __restrict__ ctx_len,
                                                               int P, int T_stride, int K,
                                                               const float* __restrict__ scores,
@@ -281,7 +255,8 @@ __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __r
   __shared__ uint32_t s_base_sel, s_base_cand;
   const int r = blockIdx.y;
   const int n = row_visible(ctx_len, P, r);
-  const int base = blockIdx.x * kFChunk;
+  constexpr int kFPer = FCH / kScanNT / 4;   // 16-byte loads per thread
+  const int base = blockIdx.x * FCH;
   if (n <= K || base >= n) return;
   const int tid = threadIdx.x;
   const int lane = lane_id(), wid = tid / kWave;
@@ -369,7 +344,6 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
                                                                TopkWs ws, int32_t* __restrict__ topk) {
   __shared__ uint32_t h[kBins1];
   __shared__ int32_t outl[kMaxK];
-  __shared__ uint32_t bm[kSegWords];
   __shared__ uint32_t s_cand[2 * kFinCand];   // candidate keys, then tokens; later the bitmap
   uint32_t* s_ck = s_cand;
   int32_t* s_ct = reinterpret_cast<int32_t*>(s_cand + kFinCand);
@@ -429,39 +403,47 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
     }
   }
   __syncthreads();
-  // emit the K selected tokens in ascending order through an LDS bitmap and a
-  // popcount prefix sum: rows up to 786432 tokens in one bitmap laid over the
-  // (now dead) candidate list, longer rows in 2^16-token segments
-  const int nwords = (n + 31) / 32;
-  if (nwords <= 2 * kFinCand) {
-    uint32_t* bmw = s_cand;
+  // emit the K selected tokens in ascending order: an LDS bitmap laid over the
+  // (now dead) candidate list, one pass per 786432 tokens of the row.  Thread j
+  // owns a run of wpt bitmap words; a block scan of the runs' popcounts goes to
+  // LDS, and each selected token finds its own output index as its run's
+  // prefix plus the popcounts of the words before it in the run, so the work
+  // per thread stays even however the selection clusters.
+  constexpr int kBmWords = 2 * kFinCand;
+  constexpr int kBmTok = kBmWords * 32;
+  static_assert(kBmWords % kFinNT == 0 && kFinNT <= kBins1, "runs fit the prefix array");
+  uint32_t* bmw = s_cand;
+  uint32_t* run_pre = h;                    // the radix histogram is dead by now
+  int written = 0;
+  for (int seg0 = 0; seg0 < n; seg0 += kBmTok) {
+    const int nwords = (min(kBmTok, n - seg0) + 31) / 32;
+    const int wpt = (nwords + kFinNT - 1) / kFinNT;
     for (int i = tid; i < nwords; i += kFinNT) bmw[i] = 0u;
     __syncthreads();
     for (int i = tid; i < K; i += kFinNT) {
-      const int t = outl[i];
-      atomicOr(&bmw[t >> 5], 1u << (t & 31));
+      const int t = outl[i] - seg0;
+      if (t >= 0 && t < kBmTok) atomicOr(&bmw[t >> 5], 1u << (t & 31));
     }
     __syncthreads();
-    if (nwords <= 4 * kFinNT)
-      emit_bitmap<kFinNT, 4>(bmw, nwords, 0, 0, out, scratch);
-    else if (nwords <= 8 * kFinNT)
-      emit_bitmap<kFinNT, 8>(bmw, nwords, 0, 0, out, scratch);
-    else
-      emit_bitmap<kFinNT, 24>(bmw, nwords, 0, 0, out, scratch);
-    return;
-  }
-  int written = 0;
-  const int nseg = (n + kSegTok - 1) / kSegTok;
-  for (int sg = 0; sg < nseg; ++sg) {
-    for (int i = tid; i < kSegWords; i += kFinNT) bm[i] = 0u;
+    int c = 0;
+    for (int j = 0; j < wpt; ++j) {
+      const int w = tid * wpt + j;
+      if (w < nwords) c += __popc(bmw[w]);
+    }
+    int tot;
+    run_pre[tid] = (uint32_t)block_exclusive_scan<kFinNT>(c, scratch, &tot);
     __syncthreads();
     for (int i = tid; i < K; i += kFinNT) {
-      const int t = outl[i];
-      if (t / kSegTok == sg) atomicOr(&bm[(t % kSegTok) >> 5], 1u << (t & 31));
+      const int t = outl[i] - seg0;
+      if (t < 0 || t >= kBmTok) continue;
+      const int w = t >> 5;
+      const int r0 = (w / wpt) * wpt;
+      int rank = (int)run_pre[w / wpt] + __popc(bmw[w] & ((1u << (t & 31)) - 1u));
+      for (int w2 = r0; w2 < w; ++w2) rank += __popc(bmw[w2]);
+      out[written + rank] = outl[i];
     }
-    __syncthreads();
-    written += emit_bitmap<kFinNT, kSegWords / kFinNT>(bm, kSegWords, sg * kSegTok, written, out,
-                                                       scratch);
+    written += tot;
+    __syncthreads();   // the next pass rewrites the bitmap and the run prefixes
   }
 }
 
@@ -496,9 +478,15 @@ hipError_t launch_topk_select(const BatchDims& d, int K, const float* scores, in
                               void* ws, hipStream_t s) {
   const int R = d.B * d.P;
   TopkWs w = topk_ws(ws, R, d.T_stride, K);
-  const int nchunk = (d.T_stride + kFChunk - 1) / kFChunk;
-  hipLaunchKernelGGL(topk_filter_kernel, dim3(nchunk, R), dim3(kScanNT), 0, s, d.ctx_len, d.P,
-                     d.T_stride, K, scores, w);
+  if (d.T_stride > 64 * kFChunk) {
+    const int nchunk = (d.T_stride + kFChunkLong - 1) / kFChunkLong;
+    hipLaunchKernelGGL(topk_filter_kernel<kFChunkLong>, dim3(nchunk, R), dim3(kScanNT), 0, s,
+                       d.ctx_len, d.P, d.T_stride, K, scores, w);
+  } else {
+    const int nchunk = (d.T_stride + kFChunk - 1) / kFChunk;
+    hipLaunchKernelGGL(topk_filter_kernel<kFChunk>, dim3(nchunk, R), dim3(kScanNT), 0, s,
+                       d.ctx_len, d.P, d.T_stride, K, scores, w);
+  }
   hipLaunchKernelGGL(topk_finalize_kernel, dim3(R), dim3(kFinNT), 0, s, d.ctx_len, d.P,
                      d.T_stride, K, w, topk);
   return hipGetLastError();
