@@ -87,6 +87,12 @@ __device__ void find_bin256_lo(const uint32_t* h, uint32_t k, int* d_out, uint32
   __syncthreads();
 }
 
+// MAXS: stamp registers per thread (slots of a thread's run, C <= MAXS * 1024);
+// MAXE: distinct selected tokens per thread (P * K <= MAXE * 1024).  The launch
+// takes the smallest instance that fits: every per-thread loop is unrolled to
+// these bounds, and a latency-bound kernel that runs once per workgroup pays
+// for its code size in instruction fetches.
+template <int MAXS, int MAXE>
 __global__ __launch_bounds__(kResNT) void resolve_kernel(
     int T_stride, int max_blocks, int P, int K, const int32_t* __restrict__ topk, int C,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ hot_blocks,
@@ -136,9 +142,9 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   // loaded now, before the hits of this step are known (they are masked in
   // from sHitMask later instead of read back)
   const int S = (C + kResNT - 1) / kResNT;
-  int st_reg[kMaxSlotsPerThread];
+  int st_reg[MAXS];
 #pragma unroll
-  for (int j = 0; j < kMaxSlotsPerThread; ++j) {
+  for (int j = 0; j < MAXS; ++j) {
     const int v = tid * S + j;
     st_reg[j] = (j < S && v < C) ? stp[v] : 0x7FFFFFFF;
   }
@@ -198,16 +204,16 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   // 2. classify.  Thread t owns the contiguous run U[t*E, t*E + E); all of its
   // table reads are issued together.  Rows: >= 0 known, -1 none, <= -2 the
   // (-2 - i)-th fault, resolved once victims are known.
-  const int E = (nU + kResNT - 1) / kResNT;   // <= kMaxEntriesPerThread
+  const int E = (nU + kResNT - 1) / kResNT;   // <= MAXE
   const int u0 = tid * E;
-  int tok[kMaxEntriesPerThread], row[kMaxEntriesPerThread];
-  int rb[kMaxEntriesPerThread];
-  int64_t hrow[kMaxEntriesPerThread];
+  int tok[MAXE], row[MAXE];
+  int rb[MAXE];
+  int64_t hrow[MAXE];
   // the hot-slot lookup is issued with the page lookups (every token has an
   // entry), so the classification waits for one round of loads, not two
-  int vs[kMaxEntriesPerThread];
+  int vs[MAXE];
 #pragma unroll
-  for (int e = 0; e < kMaxEntriesPerThread; ++e) {
+  for (int e = 0; e < MAXE; ++e) {
     const bool ok = e < E && u0 + e < nU;
     tok[e] = ok ? U[u0 + e] : -1;
     rb[e] = ok ? btb[tok[e] >> 6] : 0;
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   }
   int my_res = 0, my_hit = 0, my_f = 0;
 #pragma unroll
-  for (int e = 0; e < kMaxEntriesPerThread; ++e) {
+  for (int e = 0; e < MAXE; ++e) {
     row[e] = -1;
     const int t = tok[e];
     if (t < 0) continue;
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   {
     int pos = block_exclusive_scan<kResNT>(my_f, scratch, &nF);
 #pragma unroll
-    for (int e = 0; e < kMaxEntriesPerThread; ++e)
+    for (int e = 0; e < MAXE; ++e)
       if (row[e] == -2) {
         sF[pos] = tok[e];
         row[e] = -2 - pos;
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
     const int wid = tid / kWave;
     int my_c = 0, my_min = 0x7FFFFFFF;
 #pragma unroll
-    for (int j = 0; j < kMaxSlotsPerThread; ++j) {
+    for (int j = 0; j < MAXS; ++j) {
       const int v = tid * S + j;
       if (j < S && v < C && (sHitMask[v >> 5] >> (v & 31)) & 1u) st_reg[j] = s;
       if (st_reg[j] < s) {
@@ -308,9 +314,9 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
       }
       const int buf = (round + 1) & 1;
       int below = 0, wtot = 0, my_next = 0x7FFFFFFF;
-      uint64_t m[kMaxSlotsPerThread];
+      uint64_t m[MAXS];
 #pragma unroll
-      for (int j = 0; j < kMaxSlotsPerThread; ++j) {
+      for (int j = 0; j < MAXS; ++j) {
         m[j] = __ballot(st_reg[j] == sigma);
         below += lanes_below(m[j]);
         wtot += __popcll(m[j]);
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
       // equal stamps in this thread's earlier slots
       int pos = got + off + below;
 #pragma unroll
-      for (int j = 0; j < kMaxSlotsPerThread; ++j)
+      for (int j = 0; j < MAXS; ++j)
         if (st_reg[j] == sigma) {
           if (pos < n_serve) V32[pos] = tid * S + j;
           ++pos;
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   if (tid == 0 && n_serve < nF) atomicOr(err, 1);
   // fault rows from their victims (faults past n_serve keep row -1)
 #pragma unroll
-  for (int e = 0; e < kMaxEntriesPerThread; ++e)
+  for (int e = 0; e < MAXE; ++e)
     if (row[e] <= -2) {
       const int i = -2 - row[e];
       if (i < n_serve) {
@@ -452,14 +458,14 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   int32_t* rid = row_ids + (size_t)b * PK;
   if (P == 1) {
 #pragma unroll
-    for (int e = 0; e < kMaxEntriesPerThread; ++e)
+    for (int e = 0; e < MAXE; ++e)
       if (e < E && u0 + e < nU) rid[u0 + e] = row[e];
     for (int k = nU + tid; k < K; k += kResNT) rid[k] = -1;
   } else {
     __syncthreads();                       // every read of the victims is done
     int32_t* rowU = sA;
 #pragma unroll
-    for (int e = 0; e < kMaxEntriesPerThread; ++e)
+    for (int e = 0; e < MAXE; ++e)
       if (e < E && u0 + e < nU) rowU[u0 + e] = row[e];
     __syncthreads();
     for (int e = tid; e < PK; e += kResNT) {
@@ -581,9 +587,18 @@ __global__ __launch_bounds__(NT) void fault_copy_kernel(
 hipError_t launch_resolve_tables(const BatchDims& d, int K, const int32_t* topk,
                                  const ResidencyArgs& r, int32_t* row_ids, int32_t* faults,
                                  int32_t* counts, hipStream_t s) {
-  hipLaunchKernelGGL(resolve_kernel, dim3(d.B), dim3(kResNT), 0, s, d.T_stride, d.max_blocks, d.P,
-                     K, topk, r.C, r.bt, r.hot_blocks, r.tok2slot, r.slot2tok, r.stamp, r.step,
-                     r.err, r.host_bt, row_ids, faults, counts);
+#define HS_RESOLVE(S_, E_)                                                                    \
+  hipLaunchKernelGGL((resolve_kernel<S_, E_>), dim3(d.B), dim3(kResNT), 0, s, d.T_stride,      \
+                     d.max_blocks, d.P, K, topk, r.C, r.bt, r.hot_blocks, r.tok2slot, r.slot2tok, \
+                     r.stamp, r.step, r.err, r.host_bt, row_ids, faults, counts)
+  const int slots = (r.C + kResNT - 1) / kResNT, entries = (d.P * K + kResNT - 1) / kResNT;
+  static_assert(kMaxSlotsPerThread == 16 && kMaxEntriesPerThread == 8, "instances below");
+  if (slots <= 4 && entries <= 2) HS_RESOLVE(4, 2);
+  else if (slots <= 4 && entries <= 4) HS_RESOLVE(4, 4);
+  else if (slots <= 8 && entries <= 4) HS_RESOLVE(8, 4);
+  else if (slots <= 8 && entries <= 8) HS_RESOLVE(8, 8);
+  else HS_RESOLVE(16, 8);
+#undef HS_RESOLVE
   return hipGetLastError();
 }
 
