@@ -109,6 +109,7 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   __shared__ int scratch[kResNT / kWave + 1];
   __shared__ uint32_t h256[256];
   __shared__ int s_nlist[4];
+  __shared__ int s_wl[kResNT / kWave][4];   // valid entries per (wave, list)
   __shared__ int s_res, s_hit, s_ev, s_vcnt, s_d;
   __shared__ int s_wa[2][kResNT / kWave], s_wb[2][kResNT / kWave];   // per-wave partials
   __shared__ uint32_t s_before;
@@ -127,7 +128,6 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   int32_t* s2t = slot2tok + (size_t)b * C;
   int32_t* stp = stamp + (size_t)b * C;
 
-  if (tid < 4) s_nlist[tid] = 0;
   if (tid == 0) {
     s_res = 0;
     s_hit = 0;
@@ -148,21 +148,32 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
     const int v = tid * S + j;
     st_reg[j] = (j < S && v < C) ? stp[v] : 0x7FFFFFFF;
   }
-  __syncthreads();
-
   // 1. U = sorted distinct selected tokens.  Each list is sorted with a -1
-  // tail; valid entries are counted with one ballot per wave.
+  // tail; valid entries are counted with one ballot per wave and list.  The
+  // lists are read in the same round of loads as the hot blocks and stamps.
   int32_t* Lin = sA;             // P lists of K
   int32_t* M = sA + kMaxSel;     // merged run with duplicates
-  for (int base = 0; base < PK; base += kResNT) {
-    const int e = base + tid;
-    const int x = e < PK ? tk[e] : -1;
-    if (e < PK) Lin[e] = x;
-    // one list per wave-aligned run of K (K may not be a multiple of 64): count per list
-    for (int p = 0; p < P; ++p) {
-      const uint64_t m = __ballot(x >= 0 && e / K == p);
-      if (lane == 0 && m) atomicAdd(&s_nlist[p], __popcll(m));
+  {
+    const int wid = tid / kWave;
+    int nl[4] = {0, 0, 0, 0};
+    for (int base = 0; base < PK; base += kResNT) {
+      const int e = base + tid;
+      const int x = e < PK ? tk[e] : -1;
+      if (e < PK) Lin[e] = x;
+      // one list per run of K entries (K may not be a multiple of 64)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        if (p < P) nl[p] += __popcll(__ballot(x >= 0 && e / K == p));
     }
+    if (lane == 0)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) s_wl[wid][p] = nl[p];
+  }
+  __syncthreads();
+  if (tid < P) {
+    int c = 0;
+    for (int w = 0; w < kResNT / kWave; ++w) c += s_wl[w][tid];
+    s_nlist[tid] = c;
   }
   __syncthreads();
   int nU;
