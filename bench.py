@@ -39,7 +39,7 @@ KV_ROW = 576
 INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.17e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
-                   "sha256": "5429f0b5122de042993b4e84336e133decea8b82bdce379aee78fb782f19915d"}
+                   "sha256": "73d0ee542a6caf8ba7de33321a05ceb75e5ba736f00f4eb8540228af5de3e28a"}
 
 
 def _indexer_traffic(workload: str, indexer_q: str):
@@ -241,7 +241,8 @@ def cache_ops_bench(torch, reps: int = 5) -> dict:
 
 def ceilings(torch, ds, wl, reps: int = 10) -> dict:
     """Measured ceilings on this machine, as context for the fractions of the published peaks
-    (probe kernels of libhsprobe.so, HIP events, MALL flushed before each launch):
+    (probe kernels of libhsprobe.so, median of HIP-event timings after one untimed launch,
+    MALL flushed before each launch):
     - the indexer's key pages read in the indexer's own page order with no products and
       no score writes (the same grid and two pages in flight per wave);
     - a plain stream of the same number of bytes over the key pool;
@@ -266,7 +267,10 @@ def ceilings(torch, ds, wl, reps: int = 10) -> dict:
                                    wl.T_stride // 64, vp(ds.idx_pool.data_ptr()),
                                    vp(ds.idx_bt.data_ptr()), vp(sink.data_ptr()), st)
             assert r == 0, f"hsp_read_pages: hip error {r}"
-        pages_ms, _ = _time_launches(pages, reps, torch, None, flush)
+        pages()                       # the first launch loads the code object
+        torch.cuda.synchronize()
+        _, ms = _time_launches(pages, reps, torch, None, flush)
+        pages_ms = sorted(ms)[len(ms) // 2]
         out["key_pages_in_indexer_order_GBs"] = round(key_bytes / (pages_ms / 1e3) / 1e9, 1)
         out["key_pages_us"] = round(pages_ms * 1e3, 1)
     n = (ds.idx_pool.numel() * ds.idx_pool.element_size()) // 16 * 16
@@ -275,14 +279,18 @@ def ceilings(torch, ds, wl, reps: int = 10) -> dict:
     def stream():
         r = lib.hsp_read_stream(vp(ds.idx_pool.data_ptr()), n, 512, vp(sink.data_ptr()), st)
         assert r == 0, f"hsp_read_stream: hip error {r}"
-    stream_ms, _ = _time_launches(stream, reps, torch, None, flush)
+    stream()
+    torch.cuda.synchronize()
+    _, ms = _time_launches(stream, reps, torch, None, flush)
+    stream_ms = sorted(ms)[len(ms) // 2]
     out["plain_read_stream_GBs"] = round(n / (stream_ms / 1e3) / 1e9, 1)
     out["plain_read_stream_bytes"] = int(n)
     src = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     dst.copy_(src, non_blocking=True)
     torch.cuda.synchronize()
-    dma_ms, _ = _time_launches(lambda: dst.copy_(src, non_blocking=True), reps, torch)
+    _, ms = _time_launches(lambda: dst.copy_(src, non_blocking=True), reps, torch)
+    dma_ms = sorted(ms)[len(ms) // 2]
     out["host_dma_GBs"] = round((256 << 20) / (dma_ms / 1e3) / 1e9, 2)
     del src, dst, flush_buf
     torch.cuda.empty_cache()

@@ -32,6 +32,18 @@ def test_library_exports_every_declared_function():
     assert _lib.abi_version() == 1
 
 
+def test_probe_library_is_separate_and_loads():
+    """The benchmark's bandwidth probes live in their own library; the decode-step
+    library exports none of them."""
+    probe = _lib.LIB_PATH.parent / "libhsprobe.so"
+    lib = ctypes.CDLL(str(probe))
+    for n in ("hsp_read_stream", "hsp_read_pages"):
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True,
+                         text=True).stdout
+    assert "hsp_" not in out
+
+
 def test_struct_layout_matches_header(tmp_path):
     c = tmp_path / "probe.c"
     c.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "hs.h"\n'
