@@ -354,6 +354,9 @@ def main():
                     help="also time the token-sharded top-K with this many shards (P = 1)")
     ap.add_argument("--cache-ops", action="store_true",
                     help="also time KV append, pre-copy and demotion (a separate batch)")
+    ap.add_argument("--host-layout", choices=("interleaved", "layer_major"), default="interleaved",
+                    help="host pool layout: the L rows of a token together, or one plane per "
+                         "layer (the same for one layer)")
     ap.add_argument("--seq-repeats", type=int, default=3,
                     help="repeats of the step sequence of multi-step workloads (0: skip)")
     ap.add_argument("--indexer-q", choices=("bf16", "e4m3"), default="bf16",
@@ -376,7 +379,8 @@ def main():
     t0 = time.time()
     wl = gen.by_name(a.workload)
     log(f"[bench] workload {wl.name} generated in {time.time() - t0:.1f}s")
-    ds = DeviceStep(wl, indexer_q=a.indexer_q if a.indexer_q == "e4m3" else None)
+    ds = DeviceStep(wl, indexer_q=a.indexer_q if a.indexer_q == "e4m3" else None,
+                    host_layout=a.host_layout)
     e4m3 = ds.indexer_q == "e4m3"
     snap = ds.snapshot()
     # MALL flush by reading 512 MB: a read leaves clean lines, so the timed step
@@ -518,7 +522,7 @@ def main():
                    "query_heads": wl.Hq, "indexer_heads": wl.H_idx, "indexer_dim": wl.D_idx,
                    "layers": wl.L, "positions": wl.P, "hot_rows": wl.C,
                    "resident_tail_tokens": 4096 if wl.name == "mixed_128k" else None,
-                   "indexer_queries": ds.indexer_q,
+                   "indexer_queries": ds.indexer_q, "host_layout": ds.host_layout,
                    "graph": not a.no_graph, "pipeline_chunks": a.chunks,
                    "pipeline_copy_workgroups": a.copy_wgs if a.chunks > 1 else None},
         "roofline": {"bound": "hbm",

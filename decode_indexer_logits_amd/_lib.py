@@ -39,7 +39,7 @@ class Batch(ctypes.Structure):
 
 
 class Residency(ctypes.Structure):
-    _fields_ = [("C", c_int32), ("L", c_int32), ("kv_t", c_int32), ("pad_", c_int32),
+    _fields_ = [("C", c_int32), ("L", c_int32), ("kv_t", c_int32), ("host_row_pitch", c_int32),
                 ("pool_layer_rows", c_int64), ("host_layer_rows", c_int64),
                 ("bt", c_void_p), ("hot_blocks", c_void_p), ("tok2slot", c_void_p),
                 ("slot2tok", c_void_p), ("stamp", c_void_p), ("step", c_void_p),

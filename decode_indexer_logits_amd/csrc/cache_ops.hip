@@ -144,7 +144,8 @@ __global__ __launch_bounds__(kCopyNT) void append_copy_kernel(
 // 64p), every layer with its scales, and recorded in host_bt.
 __global__ __launch_bounds__(kCopyNT) void precopy_kernel(
     int T_stride, int max_blocks, int L, int row_bytes, int64_t pool_layer_rows,
-    int64_t host_layer_rows, int max_pages, const int32_t* __restrict__ ctx_len,
+    int64_t host_layer_rows, int64_t host_pitch, int max_pages,
+    const int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ bt, int64_t* __restrict__ host_bt,
     const uint8_t* __restrict__ pool, const float* __restrict__ row_scale,
     uint8_t* __restrict__ host_rows, float* __restrict__ host_scale) {
@@ -170,16 +171,19 @@ __global__ __launch_bounds__(kCopyNT) void precopy_kernel(
     const int k = x / per_page, y = x % per_page;
     const int l = y / (kBlock * rv), z = y % (kBlock * rv);
     const int p = s_pages[k];
+    const int r = z / rv, c = z % rv;
     const int64_t src = (int64_t)btb[p] * kBlock;
-    const int64_t dst = (int64_t)b * T_stride + (int64_t)p * kBlock;
-    reinterpret_cast<uint4*>(host_rows + ((size_t)l * host_layer_rows + dst) * row_bytes)[z] =
+    const int64_t h = (int64_t)b * T_stride + (int64_t)p * kBlock + r;
+    reinterpret_cast<uint4*>(host_rows + ((int64_t)l * host_layer_rows + h * host_pitch) *
+                                             row_bytes)[c] =
         reinterpret_cast<const uint4*>(pool + ((size_t)l * pool_layer_rows + src) * row_bytes)[z];
   }
   if (row_scale)
     for (int x = threadIdx.x; x < found * L * kBlock; x += kCopyNT) {
       const int k = x / (L * kBlock), l = (x / kBlock) % L, r = x % kBlock;
       const int p = s_pages[k];
-      host_scale[(size_t)l * host_layer_rows + (int64_t)b * T_stride + (int64_t)p * kBlock + r] =
+      host_scale[(int64_t)l * host_layer_rows +
+                 ((int64_t)b * T_stride + (int64_t)p * kBlock + r) * host_pitch] =
           row_scale[(size_t)l * pool_layer_rows + (int64_t)btb[p] * kBlock + r];
     }
   // readers of host_bt run in later launches, after these copies complete
@@ -298,7 +302,7 @@ hipError_t launch_append_tokens(const BatchDims& d, int32_t* ctx_len, const int3
 hipError_t launch_precopy_pages(const BatchDims& d, const ResidencyArgs& r, int max_pages,
                                 hipStream_t s) {
   hipLaunchKernelGGL(precopy_kernel, dim3(d.B), dim3(kCopyNT), 0, s, d.T_stride, d.max_blocks,
-                     r.L, kDLat * r.kv_bytes, r.pool_layer_rows, r.host_layer_rows,
+                     r.L, kDLat * r.kv_bytes, r.pool_layer_rows, r.host_layer_rows, r.host_row_pitch,
                      min(max_pages, kPreMax), d.ctx_len, r.bt,
                      const_cast<int64_t*>(r.host_bt), static_cast<const uint8_t*>(r.pool),
                      r.row_scale,

@@ -249,11 +249,14 @@ hs_status check_residency(const hs::BatchDims& d, int32_t K, const hs_residency*
     return fail(HS_ERR_ALIGN, "pool and host_rows need 16-byte alignment");
   if (res->pool_layer_rows < 0 || res->host_layer_rows < 0)
     return fail(HS_ERR_SHAPE, "layer strides must be non-negative");
+  if (res->host_row_pitch < 0)
+    return fail(HS_ERR_SHAPE, "host_row_pitch=%d must be non-negative", res->host_row_pitch);
   r->C = res->C;
   r->L = res->L;
   r->kv_bytes = kv_bytes;
   r->pool_layer_rows = res->pool_layer_rows;
   r->host_layer_rows = res->host_layer_rows;
+  r->host_row_pitch = res->host_row_pitch > 1 ? res->host_row_pitch : 1;
   r->bt = res->bt;
   r->hot_blocks = res->hot_blocks;
   r->tok2slot = res->tok2slot;
@@ -444,9 +447,17 @@ hs_status hs_precopy_pages(const hs_batch* batch, const hs_residency* res, int32
     return fail(HS_ERR_NULL, "pre-copy needs host_rows, host_bt (and host_scale for E4M3)");
   if (max_pages < 1 || max_pages > hs::precopy_max_pages())
     return fail(HS_ERR_SHAPE, "max_pages=%d out of [1, %d]", max_pages, hs::precopy_max_pages());
-  if (res->host_layer_rows < (int64_t)d.B * d.T_stride)
-    return fail(HS_ERR_SHAPE, "the host pool needs B*T_stride=%lld rows per layer",
-                (long long)d.B * d.T_stride);
+  // host slot of page j of request b: tokens b*T_stride + 64j ..; the layers'
+  // rows must not overlap: planes of B*T_stride tokens, or the L rows of a
+  // token inside its pitch
+  const int64_t n_tok = (int64_t)d.B * d.T_stride;
+  if (res->L > 1 && r.host_layer_rows < n_tok * r.host_row_pitch &&
+      (r.host_layer_rows < 1 || r.host_row_pitch < (int64_t)res->L * r.host_layer_rows))
+    return fail(HS_ERR_SHAPE,
+                "host pool of B*T_stride=%lld tokens: layers overlap (host_layer_rows=%lld, "
+                "host_row_pitch=%lld; need host_layer_rows >= B*T_stride*pitch or pitch >= "
+                "L*host_layer_rows)",
+                (long long)n_tok, (long long)r.host_layer_rows, (long long)r.host_row_pitch);
   return launched(hs::launch_precopy_pages(d, r, max_pages, static_cast<hipStream_t>(stream)),
                   "pre-copy");
 }

@@ -46,6 +46,7 @@ hipError_t launch_topk_select(const BatchDims& d, int K, const float* scores, in
 struct ResidencyArgs {
   int C, L, kv_bytes;               // kv_bytes: bytes per latent element (1 or 4)
   int64_t pool_layer_rows, host_layer_rows;
+  int64_t host_row_pitch;           // rows from one host token to the next (>= 1)
   const int32_t* bt;
   const int32_t* hot_blocks;
   int32_t* tok2slot;

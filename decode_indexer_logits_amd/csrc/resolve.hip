@@ -527,8 +527,9 @@ __global__ __launch_bounds__(NT) void fault_copy_kernel(
     int B, int PK, int C, int L, int row_bytes, int max_blocks, const int32_t* __restrict__ faults,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ hot_blocks,
     const int64_t* __restrict__ host_bt, const uint8_t* __restrict__ host_rows,
-    const float* __restrict__ host_scale, int64_t host_layer_rows, uint8_t* __restrict__ pool,
-    float* __restrict__ row_scale, int64_t pool_layer_rows, int32_t* __restrict__ step) {
+    const float* __restrict__ host_scale, int64_t host_layer_rows, int64_t host_pitch,
+    uint8_t* __restrict__ pool, float* __restrict__ row_scale, int64_t pool_layer_rows,
+    int32_t* __restrict__ step) {
   __shared__ int64_t s_src[2][BATCH * kCopyMaxL];
   __shared__ int64_t s_dst[2][BATCH * kCopyMaxL];
   __shared__ int s_n[2];
@@ -548,10 +549,10 @@ __global__ __launch_bounds__(NT) void fault_copy_kernel(
       const int64_t hr = host_bt[(size_t)cu.b * max_blocks + (t >> 6)] + (t & 63);
       const int64_t pr =
           (int64_t)hot_blocks[(size_t)cu.b * (C >> 6) + (sl >> 6)] * kBlock + (sl & 63);
-      s_src[buf][i] = ((int64_t)l * host_layer_rows + hr) * row_bytes;
+      const int64_t hrow = (int64_t)l * host_layer_rows + hr * host_pitch;
+      s_src[buf][i] = hrow * row_bytes;
       s_dst[buf][i] = ((int64_t)l * pool_layer_rows + pr) * row_bytes;
-      if (host_scale)
-        row_scale[(size_t)l * pool_layer_rows + pr] = host_scale[(size_t)l * host_layer_rows + hr];
+      if (host_scale) row_scale[(size_t)l * pool_layer_rows + pr] = host_scale[hrow];
     }
   };
   CopyCursor<BATCH> cur{0, me - grid, 0};
@@ -622,6 +623,7 @@ hipError_t launch_fault_copy(const BatchDims& d, int K, const ResidencyArgs& r,
   hipLaunchKernelGGL((fault_copy_kernel<kCopyNT, kCopyInFlight, kCopyBatch>), dim3(grid), dim3(kCopyNT), 0, s, d.B, PK, r.C, r.L,
                      row_bytes, d.max_blocks, faults, counts, r.hot_blocks, r.host_bt,
                      static_cast<const uint8_t*>(r.host_rows), r.host_scale, r.host_layer_rows,
+                     r.host_row_pitch,
                      static_cast<uint8_t*>(r.pool), r.row_scale, r.pool_layer_rows, r.step);
   return hipGetLastError();
 }

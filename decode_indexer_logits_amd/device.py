@@ -39,10 +39,14 @@ class DeviceStep:
     """All device buffers of a workload, ready to run decode steps."""
 
     def __init__(self, wl, device: str = "cuda:0", host_pool: bool = True,
-                 indexer_q: str | None = None):
+                 indexer_q: str | None = None, host_layout: str = "interleaved"):
         """indexer_q: the indexer's query type, "bf16" (the workload's own
         queries) or "e4m3" (quantized per head every step by
-        hs_quantize_queries before the indexer)."""
+        hs_quantize_queries before the indexer).
+        host_layout: "interleaved" keeps the L rows of a host token together
+        ([tokens, L, 576], host_row_pitch = L: one contiguous read per fault),
+        "layer_major" keeps one plane per layer ([L, tokens, 576]); the same
+        for one layer."""
         torch = _torch()
         _lib.load()
         self.wl = wl
@@ -102,21 +106,29 @@ class DeviceStep:
         self.err = torch.zeros(1, dtype=torch.int32, device=d)
         self.host_rows = self.host_scale = self.host_bt = None
         host_rows_dev = host_scale_dev = None
+        if host_layout not in ("interleaved", "layer_major"):
+            raise ValueError(f"host_layout={host_layout!r}")
+        self.host_layout = host_layout
+        inter = host_layout == "interleaved"
+        # host row of (layer l, host token h) = l * host_layer_rows + h * host_row_pitch
+        self.host_layer_rows, self.host_row_pitch = (1, L) if inter else (B * Ts, 1)
         if wl.has_host and host_pool:
-            hr = wl.host_rows
-            self.host_rows = torch.empty(hr.shape, dtype=torch.uint8 if hr.dtype == np.uint8
+            hr = wl.host_rows                                     # [L, B*Ts, 576]
+            shape = (hr.shape[1], L, hr.shape[2]) if inter else hr.shape
+            self.host_rows = torch.empty(shape, dtype=torch.uint8 if hr.dtype == np.uint8
                                          else torch.float32, pin_memory=True)
-            self.host_rows.numpy()[...] = hr
+            self.host_rows.numpy()[...] = hr.transpose(1, 0, 2) if inter else hr
             host_rows_dev = _lib.host_device_ptr(self.host_rows)
             if wl.host_scale is not None:
                 # the per-row scales of the host pool are a small table: kept in
                 # HBM so a fault reads only its row over the host link
-                self.host_scale = _dev(wl.host_scale, d)
+                hs_ = wl.host_scale                               # [L, B*Ts]
+                self.host_scale = _dev(np.ascontiguousarray(hs_.T) if inter else hs_, d)
                 host_scale_dev = self.host_scale.data_ptr()
             self.host_bt = _dev(wl.host_bt, d)
         kv_t = _lib.DTYPES[wl.kv_dtype]
         self.res = _lib.Residency(
-            C, L, kv_t, 0, self.n_rows, B * Ts,
+            C, L, kv_t, self.host_row_pitch, self.n_rows, self.host_layer_rows,
             self.bt.data_ptr(), _p(self.hot_blocks), _p(self.tok2slot), _p(self.slot2tok),
             _p(self.stamp), self.step_t.data_ptr(), self.err.data_ptr(), self.pool.data_ptr(),
             _p(self.row_scale), host_rows_dev, host_scale_dev, _p(self.host_bt))
@@ -211,7 +223,8 @@ class DeviceStep:
         def off(t, rows):
             return None if t is None else t[rows].data_ptr()
         ch["res"] = _lib.Residency(
-            C, wl.L, _lib.DTYPES[wl.kv_dtype], 0, self.n_rows, wl.B * wl.T_stride,
+            C, wl.L, _lib.DTYPES[wl.kv_dtype], self.host_row_pitch, self.n_rows,
+            self.host_layer_rows,
             off(self.bt, sl), off(self.hot_blocks, sl), off(self.tok2slot, sl),
             off(self.slot2tok, sl), off(self.stamp, sl), self.steps_dev[c:c + 1].data_ptr(),
             self.err.data_ptr(), self.pool.data_ptr(), _p(self.row_scale), self._host_rows_dev,

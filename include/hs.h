@@ -197,7 +197,12 @@ typedef struct hs_residency {
   int32_t L;                  /* latent layers sharing this state, 1 .. 16   */
   hs_dtype kv_t;              /* HS_E4M3 (row_scale/host_scale required) or
                                  HS_F32 (scales must be NULL)                */
-  int32_t pad_;
+  int32_t host_row_pitch;     /* rows from one host token to the next in
+                                 host_rows / host_scale: 0 or 1 = consecutive
+                                 (layer-major [L, host_layer_rows, 576]); L
+                                 with host_layer_rows = 1 interleaves the
+                                 layers ([tokens, L, 576]), so the L rows of
+                                 one fault are one contiguous read           */
   int64_t pool_layer_rows;    /* rows from one layer to the next in pool and
                                  row_scale (>= rows used by the block ids)   */
   int64_t host_layer_rows;    /* same for host_rows / host_scale             */
@@ -212,16 +217,20 @@ typedef struct hs_residency {
   int32_t* err;               /* [1] device error bits (HS_DEVERR_*), OR-ed  */
   void* pool;                 /* [L, pool_layer_rows, 576] rows             */
   float* row_scale;           /* [L, pool_layer_rows] per-row fp32 scale     */
-  const void* host_rows;      /* pinned host [L, host_layer_rows, 576], given
-                                 by its device-accessible address; may be
-                                 NULL when no page is host-only              */
-  const float* host_scale;    /* [L, host_layer_rows] scale of each host row;
+  const void* host_rows;      /* pinned host rows of 576 values, given by its
+                                 device-accessible address: token h of layer
+                                 l is row l*host_layer_rows + h*pitch (pitch =
+                                 max(host_row_pitch, 1)); may be NULL when no
+                                 page is host-only                           */
+  const float* host_scale;    /* scale of each host row, same indexing;
                                  any device-accessible memory.  Device memory
                                  is preferable: the table is small, and reading
                                  it from the host costs one link transaction
                                  per fault                                  */
-  const int64_t* host_bt;     /* [B, max_blocks] host row of token 64*j of
-                                 page j, -1 = page has no host copy          */
+  const int64_t* host_bt;     /* [B, max_blocks] host token index h of token
+                                 64*j of page j (its row in layer l is
+                                 l*host_layer_rows + h*pitch), -1 = page has
+                                 no host copy                                */
 } hs_residency;
 
 /* Fused resolve (page "Un contexte d'un million sur huit H200", section "Les
@@ -233,9 +242,9 @@ typedef struct hs_residency {
  *   topk[b]; each t in U (page j = t/64) is RESIDENT if bt[b,j] >= 0, a HIT if
  *   tok2slot[b,t] >= 0 (its stamp becomes s), else a FAULT (ascending order).
  *   Victims are the slots with stamp < s ordered by (stamp, slot); the i-th
- *   fault takes the i-th victim, evicting its previous token, and the 576-value
- *   row host_rows[l, host_bt[b,j] + t%64] and its scale are copied to the
- *   slot's pool row in every layer l.  step becomes s.
+ *   fault takes the i-th victim, evicting its previous token, and host row
+ *   l*host_layer_rows + (host_bt[b,j] + t%64)*pitch (576 values) and its scale
+ *   are copied to the slot's pool row in every layer l.  step becomes s.
  * Outputs:
  *   row_ids [B, P, K] int32: pool row of topk[b,p,k], -1 for -1 entries
  *   faults  [B, P*K, 2] int32: (token, slot) of each served fault, ascending

@@ -143,6 +143,15 @@ def test_cache_operations_validate_on_the_host():
                                 ctypes.byref(fl), fake, ws_n, None) == 2
     assert lib.hs_precopy_pages(ctypes.byref(b), ctypes.byref(res), 0, None) == 2
     assert lib.hs_precopy_pages(ctypes.byref(b), ctypes.byref(res), 2000, None) == 2
+    # two layers of a 2 x 1024-token host pool: planes of 2048 rows, or the two rows of a
+    # token side by side (pitch 2, layer stride 1) are accepted; overlapping layouts are not
+    def two_layers(pitch, layer_rows):
+        return _lib.Residency(0, 2, 2, pitch, 1 << 20, layer_rows, 16, None, None, None, None, 16,
+                              16, 16, 16, 16, 16, 16)
+    bad_layouts = [(0, 2047), (1, 1000), (2, 2), (3, 2), (-1, 2048)]
+    for pitch, lr in bad_layouts:
+        r2 = two_layers(pitch, lr)
+        assert lib.hs_precopy_pages(ctypes.byref(b), ctypes.byref(r2), 4, None) == 2, (pitch, lr)
     assert lib.hs_demote_pages(ctypes.byref(b), ctypes.byref(res), fake, 0, ctypes.byref(fl),
                                fake, ws_n, None) == 2            # the tail must stay
     assert lib.hs_demote_pages(ctypes.byref(b), ctypes.byref(res), None, 1, ctypes.byref(fl),

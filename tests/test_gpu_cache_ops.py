@@ -35,7 +35,9 @@ def _gpu():
 class _Dev:
     """Device copy of a CacheState, with the C ABI structs that point into it."""
 
-    def __init__(self, st: co.CacheState, P: int):
+    def __init__(self, st: co.CacheState, P: int, interleaved: bool = False):
+        """interleaved: the host pool keeps the L rows of a token together
+        ([tokens, L, 576], host_row_pitch = L) instead of one plane per layer."""
         from decode_indexer_logits_amd import _lib
         self.lib = _lib
         cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -45,8 +47,11 @@ class _Dev:
         self.bt, self.idx_bt, self.host_bt = cu(st.bt), cu(st.idx_bt), cu(st.host_bt)
         self.pool, self.row_scale = cu(st.pool), cu(st.row_scale)
         self.idx_pool, self.idx_scale = cu(st.idx_pool), cu(st.idx_scale)
-        self.host_rows = torch.from_numpy(st.host_rows.copy()).pin_memory()
-        self.host_scale = cu(st.host_scale)
+        self.inter = interleaved
+        hr, hs = (st.host_rows.transpose(1, 0, 2), st.host_scale.T) if interleaved else \
+            (st.host_rows, st.host_scale)
+        self.host_rows = torch.from_numpy(np.ascontiguousarray(hr)).pin_memory()
+        self.host_scale = cu(hs)
         cap = st.free_capacity
         self.free = torch.zeros(cap, dtype=torch.int32, device="cuda")
         self.free[:len(st.free)] = torch.tensor(st.free, dtype=torch.int32)
@@ -60,7 +65,8 @@ class _Dev:
                               dtype=torch.uint8, device="cuda")
         self.batch = _lib.make_batch(B, P, self.T_stride, self.ctx)
         L, n_rows = st.pool.shape[:2]
-        self.res = _lib.Residency(0, L, _lib.HS_E4M3, 0, n_rows, B * self.T_stride,
+        pitch, layer_rows = (L, 1) if interleaved else (0, B * self.T_stride)
+        self.res = _lib.Residency(0, L, _lib.HS_E4M3, pitch, n_rows, layer_rows,
                                   self.bt.data_ptr(), None, None, None, None,
                                   self.step.data_ptr(), self.err.data_ptr(), self.pool.data_ptr(),
                                   self.row_scale.data_ptr(), _lib.host_device_ptr(self.host_rows),
@@ -94,8 +100,12 @@ class _Dev:
         eq(self.row_scale.view(torch.int32), st.row_scale.view(np.int32), "row_scale")
         eq(self.idx_pool, st.idx_pool, "idx_pool")
         eq(self.idx_scale.view(torch.int32), st.idx_scale.view(np.int32), "idx_scale")
-        np.testing.assert_array_equal(self.host_rows.numpy(), st.host_rows, err_msg=what)
-        eq(self.host_scale.view(torch.int32), st.host_scale.view(np.int32), "host_scale")
+        hr = self.host_rows.numpy()
+        np.testing.assert_array_equal(hr.transpose(1, 0, 2) if self.inter else hr, st.host_rows,
+                                      err_msg=what)
+        hs = self.host_scale.view(torch.int32).cpu().numpy()
+        np.testing.assert_array_equal(hs.T if self.inter else hs, st.host_scale.view(np.int32),
+                                      err_msg=f"{what}: host_scale")
 
 
 def _initial(rng, B=5, T_stride=1024, L=2, D=576, Dk=128, spare=10, spare_idx=12):
@@ -121,13 +131,14 @@ def _initial(rng, B=5, T_stride=1024, L=2, D=576, Dk=128, spare=10, spare_idx=12
         free=order, idx_free=iorder, free_capacity=nb)
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_cache_operations_against_oracle(seed):
+@pytest.mark.parametrize("seed,layout", [(0, "layer_major"), (1, "layer_major"),
+                                         (2, "interleaved")])
+def test_cache_operations_against_oracle(seed, layout):
     from decode_indexer_logits_amd import _lib
     rng = np.random.default_rng(500 + seed)
     P = 4
     st = _initial(rng)
-    dev = _Dev(st, P)
+    dev = _Dev(st, P, interleaved=layout == "interleaved")
     dev.compare(st, "initial")
     B = len(st.ctx_len)
     L, _, D = st.pool.shape

@@ -165,11 +165,14 @@ def test_speculative_positions_two_and_three(P):
         _say(s, info["counts"].tolist())
 
 
-def test_norescache_small_hit_rate_warms_up():
-    _say("no-residency small, 4 steps")
+@pytest.mark.parametrize("layout", ["interleaved", "layer_major"])
+def test_norescache_small_hit_rate_warms_up(layout):
+    """Four steps from an empty hot buffer with two layers, the host pool laid
+    out with the layers of a token together or one plane per layer."""
+    _say(f"no-residency small, 4 steps, host pool {layout}")
     wl = gen.norescache_1m(B=2, T=32768, K=256, L=2, steps=4)
     from decode_indexer_logits_amd.device import DeviceStep
-    ds = DeviceStep(wl)
+    ds = DeviceStep(wl, host_layout=layout)
     ost = gc.oracle_state(wl)
     rates = []
     for s in range(1, wl.steps + 1):
