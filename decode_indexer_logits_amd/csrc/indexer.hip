@@ -106,7 +106,7 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
   // fetched later with readlane.  No load inside the page loop depends on
   // another load, so the in-order memory counter never forces a wait on pages
   // still in flight.
-  static_assert(TILE == 4096 || TILE == 8192, "tile of 64 or 128 pages");
+  static_assert(TILE == 512 || TILE == 4096 || TILE == 8192, "tile of 8, 64 or 128 pages");
   constexpr bool kTwo = TILE > 4096;
   const int blk_l = lane < npages ? btb[lane] : 0;
   const float sc_l = (scale && lane < npages) ? scale[blk_l] : 1.f;
@@ -739,7 +739,21 @@ hipError_t launch_mfma(const BatchDims& d, const uint16_t* q, const float* w, co
     return hipGetLastError();
   }
   // 128-page tiles when they still give every CU two workgroups (one round of
-  // workgroups instead of two: fewer start-ups with no keys in flight)
+  // workgroups instead of two: fewer start-ups with no keys in flight); 8-page
+  // tiles when 64-page ones would leave most of the chip idle (few short
+  // requests: 8 requests of 32K tokens make 64 workgroups of 4096 tokens)
+  if ((size_t)d.B * ((d.T_stride + 4095) / 4096) < 256) {
+    const dim3 g8((d.T_stride + 511) / 512, d.B);
+    if (hist)
+      hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT, true, 512>), g8, dim3(Cfg::NT), 0,
+                         s, d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias,
+                         scores, hist);
+    else
+      hipLaunchKernelGGL((indexer_bf16_e4m3_kernel<P, DK, HT, false, 512>), g8, dim3(Cfg::NT), 0,
+                         s, d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias,
+                         scores, hist);
+    return hipGetLastError();
+  }
   if ((size_t)d.B * ((d.T_stride + 8191) / 8192) >= 512) {
     const dim3 g2((d.T_stride + 8191) / 8192, d.B);
     if (hist)

@@ -11,7 +11,8 @@
 //                 then one global atomic per non-empty bin (the fused path of
 //                 hs_indexer_topk builds it in the indexer's epilogue instead)
 //   3. filter     one wave of every 4096-token workgroup (16384 on rows over
-//                 2^18 tokens) finds the bin b1
+//                 2^18 tokens, 1024 when few rows would leave the chip idle)
+//                 finds the bin b1
 //                 holding the K-th largest key from the row's histogram; keys
 //                 above b1 are selected outright, keys in b1 become candidates;
 //                 the workgroup reserves its output ranges with one pair of
@@ -39,6 +40,7 @@ constexpr int kBins1 = 2048;   // top 11 key bits
 constexpr int kChunk = 8192;   // tokens per workgroup of the histogram pass
 constexpr int kFChunk = 4096;  // tokens per workgroup of the filter pass (rows up to 2^18)
 constexpr int kFChunkLong = 16384;   // the same for longer rows
+constexpr int kFChunkShort = 1024;   // the same when few rows would leave the chip idle
 constexpr int kScanNT = 256;
 constexpr int kMaxK = 8192;
 constexpr int kCnt = 8;                   // counters per row
@@ -481,6 +483,10 @@ hipError_t launch_topk_select(const BatchDims& d, int K, const float* scores, in
   if (d.T_stride > 64 * kFChunk) {
     const int nchunk = (d.T_stride + kFChunkLong - 1) / kFChunkLong;
     hipLaunchKernelGGL(topk_filter_kernel<kFChunkLong>, dim3(nchunk, R), dim3(kScanNT), 0, s,
+                       d.ctx_len, d.P, d.T_stride, K, scores, w);
+  } else if ((size_t)R * ((d.T_stride + kFChunk - 1) / kFChunk) < 256) {
+    const int nchunk = (d.T_stride + kFChunkShort - 1) / kFChunkShort;
+    hipLaunchKernelGGL(topk_filter_kernel<kFChunkShort>, dim3(nchunk, R), dim3(kScanNT), 0, s,
                        d.ctx_len, d.P, d.T_stride, K, scores, w);
   } else {
     const int nchunk = (d.T_stride + kFChunk - 1) / kFChunk;

@@ -431,17 +431,22 @@ def test_topk_planted_ties_against_oracle(case, T_stride):
     assert len(bad) == 0, f"rows {bad[:4].tolist()}"
 
 
-def test_indexer_many_requests_long_tiles():
-    """256 requests over a 16K-token stride: enough tiles for the one-position
-    indexer's 128-page tiles.  Ragged contexts (empty, one token, on and off
-    the 4096/8192 boundaries); fused and separate indexer calls give the same
-    scores bit for bit; sampled scores against the oracle; top-K exact."""
+@pytest.mark.parametrize("B", [256, 64, 12])
+def test_indexer_many_requests_long_tiles(B):
+    """Requests over a 16K-token stride, as many as select each tile size of the
+    one-position indexer: 256 requests take 128-page tiles, 64 take 64-page
+    tiles, 12 take 8-page tiles (and 1024-token top-K filter chunks).  Ragged
+    contexts (empty, one token, on and off the 512/4096/8192 boundaries); fused
+    and separate indexer calls give the same scores bit for bit; sampled scores
+    against the oracle; top-K exact."""
     from decode_indexer_logits_amd import _lib
     from oracle import indexer as o_idx, topk as o_topk
-    rng = np.random.default_rng(21)
-    B, Ts, K = 256, 16384, 512
+    rng = np.random.default_rng(21 + B)
+    Ts, K = 16384, 512
     ctx = rng.integers(1, 12001, B).astype(np.int32)
     ctx[:8] = [0, 1, 64, 4096, 8191, 8192, 8193, 16384]
+    if B > 11:
+        ctx[8:12] = [511, 512, 513, 4097]
     _say(f"indexer many requests B={B} T_stride={Ts}")
     x = gen.indexer_inputs(2100, ctx, Ts)
     dev = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).cuda()
@@ -465,7 +470,7 @@ def test_indexer_many_requests_long_tiles():
         if n == 0:
             continue
         toks = np.unique(np.concatenate([rng.integers(0, n, 24), [0, n - 1],
-                                         [t for t in (4095, 4096, 8191, 8192) if t < n]])
+                                         [t for t in (511, 512, 4095, 4096, 8191, 8192) if t < n]])
                          .astype(np.int64))
         ref = o_idx.indexer_scores_at(x["q_idx"], "bf16", x["w"], x["idx_pool"], "e4m3",
                                       x["idx_scale"], x["idx_bt"], b, 0, toks, x["bias"])
