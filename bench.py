@@ -297,12 +297,14 @@ def ceilings(torch, ds, wl, reps: int = 10) -> dict:
     return out
 
 
-def sequence_bench(ds, wl, torch, step_fn, flush, snap0, repeats: int) -> dict:
+def sequence_bench(ds, wl, torch, step_fn, flush, snap0, repeats: int, append: bool = False) -> dict:
     """The workload's step sequence in order (steps 1..n with that step's queries), from
     the initial residency state, `repeats` times.  Per step: the median step time (HIP
     events around the captured step; query upload and MALL flush before the start event)
     and, per request, the resident / hit / fault counts and the hit rate over the
-    host-only tokens selected: hits / (hits + faults).  snap0: the initial state."""
+    host-only tokens selected: hits / (hits + faults).  snap0: the initial state.  With
+    append, every step but the last is followed (untimed) by a KV append of one token per
+    request, so each step sees a context one token longer."""
     st = torch.cuda.current_stream()
     ms = [[] for _ in range(wl.steps)]
     counts = [None] * wl.steps
@@ -319,6 +321,11 @@ def sequence_bench(ds, wl, torch, step_fn, flush, snap0, repeats: int) -> dict:
             torch.cuda.synchronize()
             ms[s - 1].append(a.elapsed_time(b))
             c = ds.counts.cpu().numpy().sum(axis=0)
+            if append and s < wl.steps:
+                ds.append(s)
+                torch.cuda.synchronize()
+                if int(ds.err.item()):
+                    raise RuntimeError(f"append after step {s}: device error {int(ds.err.item())}")
             if counts[s - 1] is None:
                 counts[s - 1] = c
             elif not (counts[s - 1] == c).all():
@@ -328,7 +335,8 @@ def sequence_bench(ds, wl, torch, step_fn, flush, snap0, repeats: int) -> dict:
     torch.cuda.synchronize()
     med = [sorted(m)[len(m) // 2] for m in ms]
     hit_rate = [float(c[1]) / max(int(c[1]) + int(c[2]), 1) for c in counts]
-    return {"steps": wl.steps, "repeats": repeats,
+    return {"steps": wl.steps, "repeats": repeats, "append": append,
+            "ctx_first_last": [int(wl.ctx_len.max()), int(wl.ctx_len.max()) + (wl.steps - 1 if append else 0)],
             "ms_per_step": [round(x, 4) for x in med],
             "hit_rate": [round(x, 4) for x in hit_rate],
             "per_request": {k: [round(float(c[i]) / wl.B, 1) for c in counts]
@@ -357,6 +365,10 @@ def main():
     ap.add_argument("--host-layout", choices=("interleaved", "layer_major"), default="interleaved",
                     help="host pool layout: the L rows of a token together, or one plane per "
                          "layer (the same for one layer)")
+    ap.add_argument("--append", action="store_true",
+                    help="decode loop: after every step of the sequence but the last, append "
+                         "one token per request (hs_append_tokens), so the context grows "
+                         "(workloads that support it: norescache_1m)")
     ap.add_argument("--seq-repeats", type=int, default=3,
                     help="repeats of the step sequence of multi-step workloads (0: skip)")
     ap.add_argument("--indexer-q", choices=("bf16", "e4m3"), default="bf16",
@@ -377,7 +389,7 @@ def main():
         print(*x, file=sys.stderr, flush=True)
 
     t0 = time.time()
-    wl = gen.by_name(a.workload)
+    wl = gen.by_name(a.workload, **({"append": True} if a.append else {}))
     log(f"[bench] workload {wl.name} generated in {time.time() - t0:.1f}s")
     ds = DeviceStep(wl, indexer_q=a.indexer_q if a.indexer_q == "e4m3" else None,
                     host_layout=a.host_layout)
@@ -486,7 +498,7 @@ def main():
     log(f"[bench] ceilings {json.dumps(ceil)}")
     seq = None
     if wl.steps > 1 and a.seq_repeats > 0:
-        seq = sequence_bench(ds, wl, torch, step_fn, flush, snap, a.seq_repeats)
+        seq = sequence_bench(ds, wl, torch, step_fn, flush, snap, a.seq_repeats, a.append)
         log(f"[bench] sequence {json.dumps(seq)}")
     alg = _algorithmic_bytes(wl, counts)
     idx_bytes = sum(alg["indexer"].values())
@@ -523,6 +535,7 @@ def main():
                    "layers": wl.L, "positions": wl.P, "hot_rows": wl.C,
                    "resident_tail_tokens": 4096 if wl.name == "mixed_128k" else None,
                    "indexer_queries": ds.indexer_q, "host_layout": ds.host_layout,
+                   "append_loop": a.append,
                    "graph": not a.no_graph, "pipeline_chunks": a.chunks,
                    "pipeline_copy_workgroups": a.copy_wgs if a.chunks > 1 else None},
         "roofline": {"bound": "hbm",

@@ -133,6 +133,22 @@ class DeviceStep:
             _p(self.stamp), self.step_t.data_ptr(), self.err.data_ptr(), self.pool.data_ptr(),
             _p(self.row_scale), host_rows_dev, host_scale_dev, _p(self.host_bt))
         self._host_rows_dev, self._host_scale_dev = host_rows_dev, host_scale_dev
+        # decode loop with KV append: the two free lists (stacks) and the caches'
+        # descriptors the append call writes through
+        self.free = self.idx_free = None
+        if getattr(wl, "appends", False):
+            def stack(ids):
+                t = torch.zeros(len(ids), dtype=torch.int32, device=d)
+                t.copy_(torch.from_numpy(np.asarray(ids, np.int32)))
+                n = torch.tensor([len(ids)], dtype=torch.int32, device=d)
+                return t, n
+            self.free, self.free_n = stack(wl.free_blocks)
+            self.idx_free, self.idx_free_n = stack(wl.idx_free_blocks)
+            self.idx_cache = _lib.IndexCache(_lib.DTYPES[wl.k_dtype], wl.D_idx,
+                                             self.idx_pool.data_ptr(), _p(self.idx_scale),
+                                             self.idx_bt.data_ptr())
+            self.ws_cache = torch.empty(_lib.workspace_bytes(_lib.HS_OP_CACHE, B, P, Ts, 1),
+                                        dtype=torch.uint8, device=d)
         self._chunks = {}
         self._streams = None
         self.set_queries(1)
@@ -203,6 +219,23 @@ class DeviceStep:
         self.run_resolve(stream)
         for l in range(self.wl.L):
             self.run_attention(l, stream)
+
+    def append(self, s: int, stream=None):
+        """KV append after step s of a decode-loop workload: one token per request
+        (its latent rows in every layer and its indexer key) through
+        hs_append_tokens; the context grows by one on the device."""
+        torch = _torch()
+        n_new, rows, rsc, keys, ksc = self.wl.append_inputs(s)
+        dev = lambda a: None if a is None else torch.from_numpy(a).to(self.device)
+        self._app_in = [dev(a) for a in (n_new, rows, rsc, keys, ksc)]   # kept until run
+        n_d, rows_d, rsc_d, keys_d, ksc_d = self._app_in
+        _lib.append_tokens(self.batch, self.ctx_len, n_d, self.res, rows_d, rsc_d, self.idx_cache,
+                           keys_d, ksc_d,
+                           _lib.FreeList(self.free.data_ptr(), self.free_n.data_ptr(),
+                                         self.free.numel(), 0),
+                           _lib.FreeList(self.idx_free.data_ptr(), self.idx_free_n.data_ptr(),
+                                         self.idx_free.numel(), 0),
+                           self.ws_cache, stream)
 
     # ---------------------------------------------------------------- pipelined step
     def _chunk(self, c: int, nchunks: int):
@@ -301,6 +334,11 @@ class DeviceStep:
         if self.wl.C:
             snap.update(tok2slot=self.tok2slot.clone(), slot2tok=self.slot2tok.clone(),
                         stamp=self.stamp.clone())
+        if self.free is not None:
+            # what the appends change (the rows they write are rewritten identically)
+            snap.update(ctx_len=self.ctx_len.clone(), bt=self.bt.clone(),
+                        idx_bt=self.idx_bt.clone(), idx_scale=self.idx_scale.clone(),
+                        free_n=self.free_n.clone(), idx_free_n=self.idx_free_n.clone())
         return snap
 
     def restore(self, snap: dict):
@@ -313,6 +351,9 @@ class DeviceStep:
             self.tok2slot.copy_(snap["tok2slot"])
             self.slot2tok.copy_(snap["slot2tok"])
             self.stamp.copy_(snap["stamp"])
+        if "ctx_len" in snap:
+            for k in ("ctx_len", "bt", "idx_bt", "idx_scale", "free_n", "idx_free_n"):
+                getattr(self, k).copy_(snap[k])
 
     def state_numpy(self) -> dict:
         """Host copies of the residency tables (for checks)."""

@@ -213,3 +213,72 @@ def full_check(ds, wl, ostate, s=1, attn_tol=2e-2, check_oracle_topk=True, pairs
     worst_a = check_attention(wl, q, g["topk"], g["out"], g["lse"], attn_tol, pairs)
     return new, rr, {"score_err": worst_s, "attn_err": worst_a, "topk_swaps": swaps,
                      "counts": g["counts"]}
+
+
+# ------------------------------------------------------------------ decode loop with append
+
+def cache_mirror(wl):
+    """The oracle's own copy of the tables a KV append changes (oracle/cache_ops
+    state): block tables, indexer cache, free lists, and a zero latent pool of the
+    workload's size (only the appended rows are ever compared)."""
+    from oracle import cache_ops as o_co
+    L, n_rows = wl.L, wl.n_pool_blocks * 64
+    dt = np.float32 if wl.kv_dtype == "f32" else np.uint8
+    return o_co.CacheState(
+        ctx_len=wl.ctx_len.copy(), bt=wl.bt.copy(), idx_bt=wl.idx_bt.copy(),
+        host_bt=wl.host_bt.copy(), pool=np.zeros((L, n_rows, 576), dt),
+        row_scale=None if wl.lat_scale is None else np.zeros((L, n_rows), np.float32),
+        idx_pool=wl.idx_pool.copy(), idx_scale=None if wl.idx_scale is None else wl.idx_scale.copy(),
+        host_rows=np.zeros((L, 1, 576), dt), host_scale=None,
+        free=[int(x) for x in wl.free_blocks], idx_free=[int(x) for x in wl.idx_free_blocks],
+        free_capacity=len(wl.free_blocks))
+
+
+def append_and_check(ds, wl, ostate, cs, s):
+    """The KV append after step s, on the device (ds.append) and in the oracle (on
+    the mirror cs); the device's tables, free lists, indexer cache and appended
+    latent rows must equal the oracle's.  Then the logical workload and the
+    oracle residency state follow the append, for the next step's checks."""
+    import torch
+    from oracle import cache_ops as o_co
+    n_new, rows, rsc, keys, ksc = wl.append_inputs(s)
+    t_new = cs.ctx_len.astype(np.int64).copy()
+    assert o_co.append_tokens(cs, n_new, rows, rsc, keys, ksc) == 0
+    ds.append(s)
+    torch.cuda.synchronize()
+
+    def eq(d, h, what):
+        np.testing.assert_array_equal(d.cpu().numpy(), h, err_msg=f"after step {s}: {what}")
+    eq(ds.ctx_len, cs.ctx_len, "ctx_len")
+    eq(ds.bt, cs.bt, "bt")
+    eq(ds.idx_bt, cs.idx_bt, "idx_bt")
+    for b in range(wl.B):                  # the indexer blocks of the pages appended to
+        for t in range(int(t_new[b]), int(cs.ctx_len[b])):
+            blk = int(cs.idx_bt[b, t // 64])
+            eq(ds.idx_pool[blk], cs.idx_pool[blk], f"indexer block {blk}")
+    if cs.idx_scale is not None:
+        eq(ds.idx_scale.view(torch.int32), cs.idx_scale.view(np.int32), "indexer scales")
+    assert int(ds.free_n.item()) == len(cs.free), "latent free list"
+    assert int(ds.idx_free_n.item()) == len(cs.idx_free), "indexer free list"
+    assert ds.free[:len(cs.free)].cpu().numpy().tolist() == cs.free
+    assert ds.idx_free[:len(cs.idx_free)].cpu().numpy().tolist() == cs.idx_free
+    assert int(ds.err.item()) == 0
+    for b in range(wl.B):
+        for i, t in enumerate(range(int(t_new[b]), int(cs.ctx_len[b]))):
+            row = int(cs.bt[b, t // 64]) * 64 + t % 64
+            eq(ds.pool[:, row], cs.pool[:, row], f"latent row of token {t}, request {b}")
+            if cs.row_scale is not None:
+                eq(ds.row_scale[:, row].view(torch.int32), cs.row_scale[:, row].view(np.int32),
+                   f"row scale of token {t}, request {b}")
+            assert np.array_equal(cs.pool[:, row], rows[b, i])
+    wl.ctx_len[:] = cs.ctx_len
+    wl.bt[:] = cs.bt
+    wl.idx_bt[:] = cs.idx_bt
+    ostate.bt[:] = cs.bt
+    for b in range(wl.B):
+        for t in range(int(t_new[b]), int(cs.ctx_len[b])):
+            blk = int(cs.idx_bt[b, t // 64])
+            wl.idx_pool[blk] = cs.idx_pool[blk]
+            if cs.idx_scale is not None:
+                wl.idx_scale[blk] = cs.idx_scale[blk]
+    return ostate

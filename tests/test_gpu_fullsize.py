@@ -126,13 +126,18 @@ def test_mtp3_agentic_full_size_four_steps():
 
 
 @pytest.mark.timeout(900)
-def test_norescache_1m_full_size_sixteen_steps():
-    _say("norescache_1m full size (B=4, T=2^20, L=4, K=2048), 16 steps")
+@pytest.mark.parametrize("append", [False, True])
+def test_norescache_1m_full_size_sixteen_steps(append):
+    """Sixteen steps at full size; with append, every step but the last is
+    followed by a KV append of one token per request (the context grows from
+    2^20 to 2^20 + 15), checked against the oracle's append."""
+    _say(f"norescache_1m full size (B=4, T=2^20, L=4, K=2048), 16 steps, append={append}")
     from decode_indexer_logits_amd.device import DeviceStep
-    wl = gen.norescache_1m()
+    wl = gen.norescache_1m(append=append)
     _say("generated")
     ds = DeviceStep(wl)
     ost = gc.oracle_state(wl)
+    cs = gc.cache_mirror(wl) if append else None
     rng = np.random.default_rng(13)
     rates = []
     for s in range(1, wl.steps + 1):
@@ -147,6 +152,8 @@ def test_norescache_1m_full_size_sixteen_steps():
         assert info["err"] == 0
         if s == 1:
             assert np.all(c[:, 1] == 0) and np.all(c[:, 2] == wl.K) and np.all(c[:, 3] == 0)
+        if append and s < wl.steps:
+            ost = gc.append_and_check(ds, wl, ost, cs, s)
     _say("hit rates", rates)
     assert rates[0] == 0.0 and min(rates[1:]) > 0.0
     del ds

@@ -95,3 +95,27 @@ def test_sink_bias_sigma_closed_form_matches_scores():
         assert abs(emp / wl.info["sigma"][b] - 1) < 0.03
         assert wl.bias[b, 0] == np.float32(2 * wl.info["sigma"][b])
         assert wl.bias[b, T - 1] == wl.bias[b, 0] and wl.bias[b, 64] == 0 and wl.bias[b, T - 257] == 0
+
+
+def test_append_loop_inputs():
+    """The decode-loop variant: room for the appended tokens, spare blocks past the
+    initial pools on two stacks, appended rows and scales taken from the latent's
+    own rows past the context, one key scale per new page."""
+    wl = gen.norescache_1m(B=2, T=8192, K=64, L=2, steps=70, append=True)
+    base = gen.norescache_1m(B=2, T=8192, K=64, L=2, steps=70)
+    assert not base.appends and base.T_stride == 8192
+    assert wl.appends and wl.T_stride == 8192 + 128 and wl.ctx_len.tolist() == [8192, 8192]
+    n_idx0 = wl.idx_pool.shape[0] - 4
+    assert sorted(wl.free_blocks.tolist()) == list(range(wl.n_pool_blocks - 4, wl.n_pool_blocks))
+    assert sorted(wl.idx_free_blocks.tolist()) == list(range(n_idx0, n_idx0 + 4))
+    assert not wl.idx_pool[n_idx0:].any() and not wl.idx_scale[n_idx0:].any()
+    for s in (1, 2, 64, 65, 69):
+        n_new, rows, rsc, keys, ksc = wl.append_inputs(s)
+        t = 8192 + s - 1
+        assert n_new.tolist() == [1, 1]
+        for b in range(2):
+            assert np.array_equal(rows[b, 0], wl.lat[:, b, t])
+            assert np.array_equal(rsc[b, 0], wl.lat_scale[:, b, t // 64])
+            assert np.array_equal(keys[b, 0], wl.app_keys[b, s - 1])
+            assert ksc[b, 0] == wl.app_key_scale[b, (s - 1) // 64 * 64]
+        assert rows.any() and keys.any()

@@ -184,6 +184,15 @@ class Workload:
     steps: int = 1                 # length of the step sequence
     _step_q: list = field(default_factory=list, repr=False)   # per step (q_idx, q)
     info: dict = field(default_factory=dict)
+    # decode loop with KV append (None when the context stays fixed over the steps):
+    # after step s < steps every request appends token ctx0[b] + s - 1, whose latent
+    # rows (every layer) and page scale are already in `lat` / `lat_scale` past the
+    # context, and whose key is app_keys[b, s - 1] (page scale app_key_scale[b, s - 1]).
+    ctx0: np.ndarray | None = None            # [B] int32 context before the first append
+    free_blocks: np.ndarray | None = None     # latent free list, bottom .. top (int32)
+    idx_free_blocks: np.ndarray | None = None # indexer free list, bottom .. top (int32)
+    app_keys: np.ndarray | None = None        # [B, steps - 1, D_idx] key codes
+    app_key_scale: np.ndarray | None = None   # [B, steps - 1] scale of the key's page
 
     @property
     def max_blocks(self) -> int:
@@ -211,6 +220,28 @@ class Workload:
         if self.lat_scale is None:
             return None
         return np.repeat(self.lat_scale, BLOCK, axis=2).reshape(self.L, self.B * self.T_stride)
+
+    @property
+    def appends(self) -> bool:
+        return self.ctx0 is not None
+
+    def append_inputs(self, s: int):
+        """Inputs of the KV append that follows step s (1 <= s < steps): one token per
+        request.  Returns (n_new [B] int32, rows [B,1,L,576], row_scale [B,1,L] or
+        None, keys [B,1,D_idx], key_scale [B,1] or None)."""
+        assert self.appends and 1 <= s < self.steps
+        i = s - 1
+        t = self.ctx0.astype(np.int64) + i
+        b = np.arange(self.B)
+        rows = self.lat[:, b, t].transpose(1, 0, 2)[:, None]          # [B,1,L,576]
+        rsc = None
+        if self.lat_scale is not None:
+            rsc = self.lat_scale[:, b, t // BLOCK].T[:, None].astype(np.float32)
+        keys = self.app_keys[:, i][:, None]
+        ksc = None if self.app_key_scale is None else self.app_key_scale[:, i][:, None]
+        return (np.ones(self.B, np.int32), np.ascontiguousarray(rows),
+                None if rsc is None else np.ascontiguousarray(rsc), np.ascontiguousarray(keys),
+                None if ksc is None else np.ascontiguousarray(ksc))
 
     def step_inputs(self, s: int = 1):
         """(q_idx, q) of step s (1-based): q_idx [B,P,H,D], q [L,B,P,Hq,576]."""
@@ -584,23 +615,52 @@ def mtp3_agentic(seed: int = 1004, B: int = 64, K: int = 2048, steps: int = 4,
 
 
 def norescache_1m(seed: int = 1005, B: int = 4, T: int = 1 << 20, K: int = 2048, L: int = 4,
-                  steps: int = 16, rho: float = 0.95) -> Workload:
+                  steps: int = 16, rho: float = 0.95, append: bool = False) -> Workload:
     """1M-token no-residency start: B=4, T=2^20, K=2048, 16 heads, fp8 latent,
     four sparse-MLA layers sharing one indexer layer.  The indexer cache is
     resident; the whole latent is host-only and the hot buffers (2K rows per
     request, shared by the four layers) start empty, so rows fault in as the
     indexer asks for them.  Sixteen steps with AR(1) drifting indexer queries
-    (rho = 0.95) and fresh attention queries per layer per step."""
+    (rho = 0.95) and fresh attention queries per layer per step.
+
+    append: a decode loop -- after every step but the last each request appends
+    one token (latent rows of every layer and an indexer key), so the context
+    grows by one per step.  T must be a multiple of 64: the first appended token
+    opens a new page, whose latent and indexer blocks come from two free lists of
+    spare blocks (a seeded order).  The appended rows are the latent's own draws
+    past the context (quantized per page like every page); keys come from one
+    more page of N(0,1) keys per request, quantized per page."""
     ch = _children(seed)
     P, Hq, H, D = 1, 16, 64, 128
     C = 2 * K
     ctx = np.full(B, T, dtype=np.int32)
-    Ts = _round_up(T, BLOCK)
+    n_app = steps - 1 if append else 0
+    if append and T % BLOCK:
+        raise ValueError("the append loop needs a page-aligned context")
+    Ts = _round_up(T + n_app, BLOCK)
     idx_pool, idx_scale, idx_bt = _indexer_cache(ch, B, ctx, Ts, D, fp8=True)
     w = uniform_f32(ch[5], (B, P, H))
     n_pool, _, hot = _place_blocks(ch, B, [[] for _ in range(B)], C // BLOCK)
     bt = np.full((B, Ts // BLOCK), -1, dtype=np.int32)
-    lat, lat_scale = _latent(ch, L, B, ctx, Ts, fp8=True)
+    lat, lat_scale = _latent(ch, L, B, ctx + n_app, Ts, fp8=True)
+    extra = {}
+    if append:
+        # spare blocks for the pages the appends open, on two stacks in a seeded order
+        npg = -(-n_app // BLOCK)
+        ss = np.random.SeedSequence(seed, spawn_key=(10,)).spawn(3)
+        g = np.random.Generator(np.random.PCG64(ss[0]))
+        free = (n_pool + g.permutation(B * npg)).astype(np.int32)
+        n_idx = idx_pool.shape[0]
+        idx_free = (n_idx + g.permutation(B * npg)).astype(np.int32)
+        n_pool += B * npg
+        idx_pool = np.concatenate([idx_pool, np.zeros((B * npg, BLOCK, D), idx_pool.dtype)])
+        idx_scale = np.concatenate([idx_scale, np.zeros(B * npg, np.float32)])
+        kc, ks = _fp8_rows(ss[1], B * npg, D)                # [B*npg, 64, D], [B*npg]
+        i = np.arange(n_app)
+        kc = kc.reshape(B, npg * BLOCK, D)[:, :n_app]
+        ks = ks.reshape(B, npg)[:, i // BLOCK]
+        extra = dict(ctx0=ctx.copy(), free_blocks=free, idx_free_blocks=idx_free,
+                     app_keys=np.ascontiguousarray(kc), app_key_scale=np.ascontiguousarray(ks))
     g4 = np.random.Generator(np.random.PCG64(ch[4]))
     q0 = g4.standard_normal((B, P, H, D))
     qs = _ar1_steps(ch, q0, steps, rho)
@@ -610,7 +670,8 @@ def norescache_1m(seed: int = 1005, B: int = 4, T: int = 1 << 20, K: int = 2048,
     t2s, s2t, st = _empty_hot(B, C, Ts)
     return Workload("norescache_1m", seed, B, P, K, L, Hq, H, D, Ts, ctx, C, "bf16", "e4m3",
                     "e4m3", 1.0 / math.sqrt(D_LATENT), w, idx_pool, idx_scale, idx_bt, None,
-                    lat, lat_scale, n_pool, bt, hot, t2s, s2t, st, 0, True, steps, step_q)
+                    lat, lat_scale, n_pool, bt, hot, t2s, s2t, st, 0, True, steps, step_q,
+                    **extra)
 
 
 def indexer_inputs(seed: int, ctx_len, T_stride: int, H: int = 64, D: int = 128,
