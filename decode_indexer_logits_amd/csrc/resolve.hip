@@ -153,17 +153,26 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   // lists are read in the same round of loads as the hot blocks and stamps.
   int32_t* Lin = sA;             // P lists of K
   int32_t* M = sA + kMaxSel;     // merged run with duplicates
+  // entry i*1024 + tid of the P lists, kept in registers to the end (row ids)
+  int xs[MAXE];
   {
     const int wid = tid / kWave;
     int nl[4] = {0, 0, 0, 0};
-    for (int base = 0; base < PK; base += kResNT) {
-      const int e = base + tid;
-      const int x = e < PK ? tk[e] : -1;
-      if (e < PK) Lin[e] = x;
+    // unrolled to the instance's bound (P*K <= MAXE*1024) so that every load is
+    // issued before the first one is used
+#pragma unroll
+    for (int i = 0; i < MAXE; ++i) {
+      const int e = i * kResNT + tid;
+      xs[i] = e < PK ? tk[e] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < MAXE; ++i) {
+      const int e = i * kResNT + tid;
+      if (e < PK) Lin[e] = xs[i];
       // one list per run of K entries (K may not be a multiple of 64)
 #pragma unroll
       for (int p = 0; p < 4; ++p)
-        if (p < P) nl[p] += __popcll(__ballot(x >= 0 && e / K == p));
+        if (p < P) nl[p] += __popcll(__ballot(xs[i] >= 0 && e / K == p));
     }
     if (lane == 0)
 #pragma unroll
@@ -178,9 +187,51 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   __syncthreads();
   int nU;
   const int32_t* U;
+  // with several positions: index in U of each of this thread's entries, when
+  // the bitmap path below computes it
+  int urank[MAXE];
+  bool have_rank = false;
   if (P == 1) {
     nU = s_nlist[0];
     U = Lin;
+  } else if (T_stride <= kMaxSel * 32) {
+    // a bitmap of the selected tokens over the merge region: duplicates across
+    // the positions collapse, and a token's index in U is the number of set
+    // bits below it (thread j owns a run of words; a block scan of the runs'
+    // popcounts, then the popcounts before the token inside its run)
+    uint32_t* bm = reinterpret_cast<uint32_t*>(M);
+    int32_t* run_pre = sF;                 // the fault list is written later
+    const int nwords = T_stride / 32;
+    const int wpt = (nwords + kResNT - 1) / kResNT;
+    for (int w = tid; w < nwords; w += kResNT) bm[w] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MAXE; ++i)
+      if (xs[i] >= 0) atomicOr(&bm[xs[i] >> 5], 1u << (xs[i] & 31));
+    __syncthreads();
+    int c = 0;
+    for (int j = 0; j < wpt; ++j) {
+      const int w = tid * wpt + j;
+      if (w < nwords) c += __popc(bm[w]);
+    }
+    int tot;
+    run_pre[tid] = block_exclusive_scan<kResNT>(c, scratch, &tot);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MAXE; ++i) {
+      urank[i] = -1;
+      const int x = xs[i];
+      if (x < 0) continue;
+      const int w = x >> 5, run = w / wpt;
+      int r = run_pre[run] + __popc(bm[w] & ((1u << (x & 31)) - 1u));
+      for (int w2 = run * wpt; w2 < w; ++w2) r += __popc(bm[w2]);
+      urank[i] = r;
+      sU[r] = x;                            // equal tokens write the same entry
+    }
+    nU = tot;
+    U = sU;
+    have_rank = true;
+    __syncthreads();
   } else {
     int total = 0;
     for (int p = 0; p < P; ++p) total += s_nlist[p];
@@ -479,9 +530,17 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
     for (int e = 0; e < MAXE; ++e)
       if (e < E && u0 + e < nU) rowU[u0 + e] = row[e];
     __syncthreads();
-    for (int e = tid; e < PK; e += kResNT) {
-      const int t = tk[e];
-      rid[e] = t < 0 ? -1 : rowU[lower_bound_lds(sU, nU, t)];
+    if (have_rank) {
+#pragma unroll
+      for (int i = 0; i < MAXE; ++i) {
+        const int e = i * kResNT + tid;
+        if (e < PK) rid[e] = xs[i] < 0 ? -1 : rowU[urank[i]];
+      }
+    } else {
+      for (int e = tid; e < PK; e += kResNT) {
+        const int t = tk[e];
+        rid[e] = t < 0 ? -1 : rowU[lower_bound_lds(sU, nU, t)];
+      }
     }
   }
   __syncthreads();                         // every eviction is counted

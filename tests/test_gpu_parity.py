@@ -481,3 +481,21 @@ def test_indexer_many_requests_long_tiles(B):
     bad = np.argwhere(np.any(ref_t != gt, axis=2))
     assert len(bad) == 0, f"top-K rows {bad[:4].tolist()}"
     _say(f"worst sampled score error {worst:.2e}")
+
+
+def test_resolve_merge_path_long_stride():
+    """Several positions on a token stride past 262144 take the resolve kernel's
+    list merge (binary searches and a dedup scan) instead of its token bitmap;
+    two steps with two positions, checked stage by stage against the oracle."""
+    from decode_indexer_logits_amd.device import DeviceStep
+    wl = gen.mtp3_agentic(B=2, K=64, steps=2, first_turn=262200, per_turn=100, turns=2,
+                          out_max=20, P=2)
+    assert wl.T_stride > 262144 and wl.P == 2
+    _say(f"resolve merge path: T_stride={wl.T_stride}, P=2")
+    ds = DeviceStep(wl)
+    ost = gc.oracle_state(wl)
+    for s in range(1, wl.steps + 1):
+        ds.set_queries(s)
+        ds.run()
+        ost, rr, info = gc.full_check(ds, wl, ost, s=s, attn_tol=2e-2)
+        _say(s, info["counts"].tolist())
