@@ -34,6 +34,7 @@ constexpr int kCopyWGs = 256;
 constexpr int kCopyInFlight = 4;
 constexpr int kCopyBatch = 8;        // faults per workgroup batch
 constexpr int kCopyMaxL = 16;
+constexpr int kCopyCntLds = 4096;    // requests whose fault counts the copy stages in LDS
 constexpr int kMaxSlotsPerThread = 16;   // C <= 16384
 constexpr int kMaxStampRounds = 32;
 constexpr int kMaxEntriesPerThread = kMaxSel / kResNT;   // 8
@@ -567,10 +568,12 @@ struct CopyCursor {
   int b, j, gbb;   // request, batch within it, batches of earlier requests
 
   // Advances to this workgroup's next batch; false when there is none.
-  __device__ bool next(int B, const int32_t* __restrict__ counts, int grid, int me) {
+  // nfault(b): the fault count of request b.
+  template <typename F>
+  __device__ bool next(int B, F nfault, int grid, int me) {
     j += grid;
     while (b < B) {
-      const int nb = (counts[b * 4 + 2] + BATCH - 1) / BATCH;
+      const int nb = (nfault(b) + BATCH - 1) / BATCH;
       if (j < nb) return true;
       gbb += nb;
       ++b;
@@ -592,12 +595,21 @@ __global__ __launch_bounds__(NT) void fault_copy_kernel(
   __shared__ int64_t s_src[2][BATCH * kCopyMaxL];
   __shared__ int64_t s_dst[2][BATCH * kCopyMaxL];
   __shared__ int s_n[2];
+  // every request's fault count, read once into LDS (up to kCopyCntLds requests):
+  // a workgroup walks the requests to find its batches, and a walk of dependent
+  // global loads would cost a memory round trip per request
+  __shared__ int s_cnt[kCopyCntLds];
   if (blockIdx.x == 0 && threadIdx.x == 0) step[0] = step[0] + 1;
+  const bool cnt_lds = B <= kCopyCntLds;
+  if (cnt_lds)
+    for (int i = threadIdx.x; i < B; i += NT) s_cnt[i] = counts[i * 4 + 2];
+  __syncthreads();
+  auto nfault = [&](int r) { return cnt_lds ? s_cnt[r] : counts[r * 4 + 2]; };
   const int cpr = row_bytes / 16;           // 16-byte chunks per row
   const int grid = gridDim.x, me = blockIdx.x;
   // source and destination byte offsets of one batch, one (fault, layer) per thread
   auto lookup = [&](const CopyCursor<BATCH>& cu, int buf) {
-    const int n = counts[cu.b * 4 + 2];
+    const int n = nfault(cu.b);
     const int f0 = cu.j * BATCH;
     const int nloc = min(BATCH, n - f0);
     if (threadIdx.x == 0) s_n[buf] = nloc;
@@ -615,13 +627,13 @@ __global__ __launch_bounds__(NT) void fault_copy_kernel(
     }
   };
   CopyCursor<BATCH> cur{0, me - grid, 0};
-  bool have = cur.next(B, counts, grid, me);
+  bool have = cur.next(B, nfault, grid, me);
   if (have) lookup(cur, 0);
   __syncthreads();
   int buf = 0;
   while (have) {
     CopyCursor<BATCH> nxt = cur;
-    const bool have_next = nxt.next(B, counts, grid, me);
+    const bool have_next = nxt.next(B, nfault, grid, me);
     const int nchunk = s_n[buf] * L * cpr;
     for (int c0 = 0; c0 < nchunk; c0 += NT * U) {
       uint4 v[U];
