@@ -488,8 +488,9 @@ def main():
         ds.run_resolve_tables()
     stage_ms["fault_copy"], _ = _time_launches(ds.run_copy_faults, a.kernel_reps, torch,
                                                restore_resolved, flush)
-    stage_ms["attention"], _ = _time_launches(lambda: [ds.run_attention(l) for l in range(wl.L)],
-                                              a.kernel_reps, torch, None, flush)
+    stage_ms["attention"], _ = _time_launches(
+        (lambda: ds.run_attention_layers()) if wl.L > 1 else (lambda: ds.run_attention(0)),
+        a.kernel_reps, torch, None, flush)
     log(f"[bench] stage ms {json.dumps({k: round(v, 4) for k, v in stage_ms.items()})}")
     ceil = ceilings(torch, ds, wl)
     if "key_pages_us" in ceil:

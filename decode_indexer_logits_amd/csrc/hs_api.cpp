@@ -315,39 +315,75 @@ hs_status hs_resolve_rows(const hs_batch* batch, int32_t K, const int32_t* topk,
   return hs_copy_faults(batch, K, res, faults, counts, 0, stream);
 }
 
-hs_status hs_sparse_mla_decode(const hs_batch* batch, int32_t K, int32_t Hq, hs_dtype q_t,
-                               const void* q, hs_dtype kv_t, const void* pool,
-                               const float* row_scale, const int32_t* row_ids, float sm_scale,
-                               float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+hs_status sparse_mla(const char* name, const hs_batch* batch, int32_t K, int32_t Hq, int32_t L,
+                     hs_dtype q_t, const void* q, hs_dtype kv_t, const void* pool,
+                     int64_t pool_layer_rows, const float* row_scale, const int32_t* row_ids,
+                     float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                     void* stream) {
   hs::BatchDims d;
   if (hs_status st = check_batch(batch, &d)) return st;
   if (!q || !pool || !row_ids || !out)
-    return fail(HS_ERR_NULL, "hs_sparse_mla_decode: q, pool, row_ids and out are required");
+    return fail(HS_ERR_NULL, "%s: q, pool, row_ids and out are required", name);
   if (K < 1 || K > 8192) return fail(HS_ERR_SHAPE, "K=%d out of [1, 8192]", K);
   if (Hq != 16) return fail(HS_ERR_SHAPE, "Hq=%d: one shard of 16 heads per call", Hq);
+  if (L < 1 || L > 16) return fail(HS_ERR_SHAPE, "L=%d out of [1, 16]", L);
+  if (L > 1 && pool_layer_rows < 1)
+    return fail(HS_ERR_SHAPE, "pool_layer_rows=%lld must be positive for L > 1",
+                (long long)pool_layer_rows);
   if (!aligned16(q) || !aligned16(pool) || !aligned16(out))
     return fail(HS_ERR_ALIGN, "q, pool and out need 16-byte alignment");
-  const size_t need = hs::mla_workspace_bytes(d.B, d.P, K, Hq);
+  const size_t need = hs::mla_workspace_bytes(d.B, d.P, K, Hq, L);
   if (need && (!ws || ws_bytes < need))
-    return fail(HS_ERR_WORKSPACE, "hs_sparse_mla_decode needs %zu workspace bytes, got %zu", need,
-                ws_bytes);
+    return fail(HS_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", name, need, ws_bytes);
   if (need && !aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace needs 16-byte alignment");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (q_t == HS_BF16 && kv_t == HS_E4M3) {
     if (!row_scale) return fail(HS_ERR_NULL, "E4M3 rows need row_scale");
-    return launched(hs::launch_mla_bf16_e4m3(d, K, static_cast<const uint16_t*>(q),
+    return launched(hs::launch_mla_bf16_e4m3(d, K, L, pool_layer_rows,
+                                             static_cast<const uint16_t*>(q),
                                              static_cast<const uint8_t*>(pool), row_scale, row_ids,
                                              sm_scale, out, lse, ws, s),
-                    "sparse_mla");
+                    name);
   }
   if (q_t == HS_F32 && kv_t == HS_F32) {
     if (row_scale) return fail(HS_ERR_DTYPE, "F32 rows take no row_scale");
-    return launched(hs::launch_mla_f32(d, K, static_cast<const float*>(q),
+    return launched(hs::launch_mla_f32(d, K, L, pool_layer_rows, static_cast<const float*>(q),
                                        static_cast<const float*>(pool), row_ids, sm_scale, out,
                                        lse, ws, s),
-                    "sparse_mla");
+                    name);
   }
   return fail(HS_ERR_DTYPE, "sparse MLA supports (q, kv) = (BF16, E4M3) or (F32, F32)");
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_sparse_mla_decode(const hs_batch* batch, int32_t K, int32_t Hq, hs_dtype q_t,
+                               const void* q, hs_dtype kv_t, const void* pool,
+                               const float* row_scale, const int32_t* row_ids, float sm_scale,
+                               float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return sparse_mla("hs_sparse_mla_decode", batch, K, Hq, 1, q_t, q, kv_t, pool, 0, row_scale,
+                    row_ids, sm_scale, out, lse, ws, ws_bytes, stream);
+}
+
+hs_status hs_sparse_mla_decode_layers(const hs_batch* batch, int32_t K, int32_t Hq, int32_t L,
+                                      hs_dtype q_t, const void* q, hs_dtype kv_t,
+                                      const void* pool, int64_t pool_layer_rows,
+                                      const float* row_scale, const int32_t* row_ids,
+                                      float sm_scale, float* out, float* lse, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  return sparse_mla("hs_sparse_mla_decode_layers", batch, K, Hq, L, q_t, q, kv_t, pool,
+                    pool_layer_rows, row_scale, row_ids, sm_scale, out, lse, ws, ws_bytes, stream);
+}
+
+size_t hs_mla_layers_workspace_bytes(int32_t B, int32_t P, int32_t K, int32_t Hq, int32_t L) {
+  if (B < 1 || P < 1 || K < 1 || L < 1) return 0;
+  return hs::mla_workspace_bytes(B, P, K, Hq, L);
 }
 
 size_t hs_workspace_bytes(int32_t op, int32_t B, int32_t P, int32_t T_stride, int32_t K,
@@ -356,7 +392,7 @@ size_t hs_workspace_bytes(int32_t op, int32_t B, int32_t P, int32_t T_stride, in
   if (B < 1 || P < 1 || K < 1) return 0;
   switch (op) {
     case HS_OP_TOPK: return hs::topk_workspace_bytes(B, P, T_stride, K);
-    case HS_OP_MLA: return hs::mla_workspace_bytes(B, P, K, Hq);
+    case HS_OP_MLA: return hs::mla_workspace_bytes(B, P, K, Hq, 1);
     default: return 0;
   }
 }

@@ -90,13 +90,16 @@ hipError_t launch_precopy_pages(const BatchDims& d, const ResidencyArgs& r, int 
 hipError_t launch_demote_pages(const BatchDims& d, const ResidencyArgs& r,
                                const int32_t* n_demote, int tail_pages,
                                const FreeListArgs& lat, void* ws, hipStream_t s);
-int mla_num_splits(int B, int P, int K);
-size_t mla_workspace_bytes(int B, int P, int K, int Hq);
-hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, const uint16_t* q, const uint8_t* pool,
-                                const float* row_scale, const int32_t* row_ids, float sm_scale,
-                                float* out, float* lse, void* ws, hipStream_t s);
-hipError_t launch_mla_f32(const BatchDims& d, int K, const float* q, const float* pool,
-                          const int32_t* row_ids, float sm_scale, float* out, float* lse,
-                          void* ws, hipStream_t s);
+// Sparse MLA over L layers that share the row ids: queries [L, B, P, 16, 576],
+// layer l's pool rows at l * pool_layer_rows, outputs [L, B, P, 16, 512].
+int mla_num_splits(int B, int P, int K, int L);
+size_t mla_workspace_bytes(int B, int P, int K, int Hq, int L);
+hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, int L, int64_t pool_layer_rows,
+                                const uint16_t* q, const uint8_t* pool, const float* row_scale,
+                                const int32_t* row_ids, float sm_scale, float* out, float* lse,
+                                void* ws, hipStream_t s);
+hipError_t launch_mla_f32(const BatchDims& d, int K, int L, int64_t pool_layer_rows,
+                          const float* q, const float* pool, const int32_t* row_ids,
+                          float sm_scale, float* out, float* lse, void* ws, hipStream_t s);
 
 }  // namespace hs

@@ -9,10 +9,13 @@
 // contiguous slice of its K selected rows, in 64-row tiles:
 //   QK   wave w takes rows 16w..16w+15 of the tile: S^T[rows x 16 heads] on
 //        the matrix cores (18 steps of v_mfma_f32_16x16x32_bf16 over the 576
-//        values).  Each lane reads 144 contiguous bytes of its row straight
-//        from HBM (the gather by row id; row ids are read one tile ahead),
-//        converts E4M3 -> bf16 in registers and also stores its 512 value
-//        entries row-major into LDS (16-byte writes).
+//        values).  Lane (n, g) reads bytes 16g .. 16g+15 of every 64-byte
+//        chunk of its row straight from HBM (the gather by row id; row ids
+//        are read one tile ahead), so one wave load covers whole 64-byte
+//        chunks of 16 rows; the contraction index is permuted the same way in
+//        the query fragments, which a sum allows.  It converts E4M3 -> bf16 in
+//        registers and also stores its value entries row-major into LDS at
+//        their own dims (16-byte writes).
 //   softmax  online, per head; the tile maximum is combined across the four
 //        waves through LDS; the row's scale is folded into the logit and
 //        into the probability that multiplies its value codes.
@@ -65,23 +68,40 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ pool,
     const float* __restrict__ row_scale, const int32_t* __restrict__ row_ids, int K,
     int rows_per_split, int nsplit, float qk_scale_log2, float* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int64_t pool_layer_rows) {
   __shared__ __attribute__((aligned(16))) uint16_t Vr[kTile * kVrStride];   // value tile, row-major
   __shared__ __attribute__((aligned(16))) uint16_t Pt[kHq * kPtStride];
   __shared__ float red[4][kHq];
 
   const int bp = blockIdx.y, split = blockIdx.x;
+  // layer blockIdx.z of a multi-layer call: its queries, pool rows, scales,
+  // outputs and partials sit one layer stride further (same row ids)
+  {
+    const size_t layer = blockIdx.z, BPn = gridDim.y;
+    q += layer * BPn * kHq * kDLat;
+    pool += layer * (size_t)pool_layer_rows * kDLat;
+    if (row_scale) row_scale += layer * (size_t)pool_layer_rows;
+    out += layer * BPn * kHq * kDVal;
+    if (lse) lse += layer * BPn * kHq;
+    if (SPLIT) {
+      part_o += layer * BPn * nsplit * kHq * kDVal;
+      part_ml += layer * BPn * nsplit * kHq * 2;
+    }
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
   const int kb = split * rows_per_split;
   const int ke = min(K, kb + rows_per_split);
 
-  // Q^T fragments: head n, dims 144g + 8s .. +8
+  // contraction step s takes dims dim0(s) .. +8 of head n (Q) and of row n (X)
+  auto dim0 = [&](int s) { return 64 * (s >> 1) + 16 * g + 8 * (s & 1); };
   bf16x8_t qf[18];
   {
-    const uint16_t* qp = q + ((size_t)bp * kHq + n) * kDLat + 144 * g;
+    const uint16_t* qp = q + ((size_t)bp * kHq + n) * kDLat;
 #pragma unroll
-    for (int s = 0; s < 18; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 8 * s));
+    for (int s = 0; s < 18; ++s)
+      qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + dim0(s)));
   }
   f32x4_t o[8];
 #pragma unroll
@@ -91,7 +111,7 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
   const int r_local = 16 * wave + n;
 
   // row ids run one tile ahead of the row loads, so a tile's rows wait for one
-  // round of loads, not two; this lane gathers row r_local, bytes 144g .. +144
+  // round of loads, not two; this lane gathers row r_local, bytes 64v + 16g .. +16
   auto load_rid = [&](int kt) {
     const int kk = kt + r_local;
     return (kk < ke) ? rid_p[kk] : -1;
@@ -99,9 +119,9 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
   auto gather = [&](int rid, float& rs, uint4* raw) {
     rs = 0.f;
     if (rid >= 0) {
-      const uint4* src = reinterpret_cast<const uint4*>(pool + (size_t)rid * kDLat + 144 * g);
+      const uint8_t* src = pool + (size_t)rid * kDLat + 16 * g;
 #pragma unroll
-      for (int v = 0; v < 9; ++v) raw[v] = src[v];
+      for (int v = 0; v < 9; ++v) raw[v] = *reinterpret_cast<const uint4*>(src + 64 * v);
       rs = row_scale ? row_scale[rid] : 1.f;
     } else {
 #pragma unroll
@@ -131,9 +151,8 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
       xb[2] = e4m3x2_to_bf16x2(hi, false);
       xb[3] = e4m3x2_to_bf16x2(hi, true);
       acc = mfma16x16x32(as_bf16x8(xb), qf[s], acc);
-      const int dim0 = 144 * g + 8 * s;
-      if (dim0 < kDVal)
-        *reinterpret_cast<uint4*>(Vr + r_local * kVrStride + dim0) =
+      if (dim0(s) < kDVal)
+        *reinterpret_cast<uint4*>(Vr + r_local * kVrStride + dim0(s)) =
             make_uint4(xb[0], xb[1], xb[2], xb[3]);
     }
     // logits of this lane's rows 4g+i (head n), log2 domain
@@ -307,7 +326,15 @@ __global__ __launch_bounds__(kWave) void mla_combine_kernel(int nsplit, const fl
                                                             const float* __restrict__ part_ml,
                                                             float* __restrict__ out,
                                                             float* __restrict__ lse) {
-  const int bp = blockIdx.x, h = blockIdx.y, half = blockIdx.z;
+  // grid (B*P, heads, 2 * layers): a wave per (request-position, head, half of the dims, layer)
+  const int bp = blockIdx.x, h = blockIdx.y, half = blockIdx.z & 1;
+  {
+    const size_t layer = blockIdx.z >> 1, BPn = gridDim.x;   // z = 2 * layer + half
+    part_o += layer * BPn * nsplit * kHq * kDVal;
+    part_ml += layer * BPn * nsplit * kHq * 2;
+    out += layer * BPn * kHq * kDVal;
+    if (lse) lse += layer * BPn * kHq;
+  }
   const int lane = threadIdx.x;
   auto ml_index = [&](int sidx) { return (((size_t)bp * nsplit + sidx) * kHq + h) * 2; };
   // every split's (m, l) at once: lane s holds splits s and 64 + s
@@ -374,61 +401,79 @@ __host__ inline int rows_per_split_for(int K, int nsplit) {
 
 }  // namespace
 
-int mla_num_splits(int B, int P, int K) {
-  const int BP = B * P;
+// Splits of the K rows so that one launch of L layers fills about
+// kMlaTargetWGs workgroups.
+int mla_num_splits(int B, int P, int K, int L) {
+  const int BPL = B * P * L;
   const int max_split = (K + kTile - 1) / kTile;
   static_assert(8192 / kTile <= kCombineMaxSplit, "one lane per slice in the combine");
-  int ns = (kMlaTargetWGs + BP - 1) / BP;
+  int ns = (kMlaTargetWGs + BPL - 1) / BPL;
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
   const int rps = rows_per_split_for(K, ns);
   return (K + rps - 1) / rps;
 }
 
-size_t mla_workspace_bytes(int B, int P, int K, int Hq) {
-  const int ns = mla_num_splits(B, P, K);
+size_t mla_workspace_bytes(int B, int P, int K, int Hq, int L) {
+  const int ns = mla_num_splits(B, P, K, L);
   if (ns <= 1) return 0;
-  const size_t parts = (size_t)B * P * ns * Hq;
+  const size_t parts = (size_t)L * B * P * ns * Hq;
   return parts * kDVal * 4 + parts * 2 * 4;
 }
 
-hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, const uint16_t* q, const uint8_t* pool,
-                                const float* row_scale, const int32_t* row_ids, float sm_scale,
-                                float* out, float* lse, void* ws, hipStream_t s) {
+hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, int L, int64_t pool_layer_rows,
+                                const uint16_t* q, const uint8_t* pool, const float* row_scale,
+                                const int32_t* row_ids, float sm_scale, float* out, float* lse,
+                                void* ws, hipStream_t s) {
   const int BP = d.B * d.P;
-  const int ns = mla_num_splits(d.B, d.P, K);
+  const int ns = mla_num_splits(d.B, d.P, K, L);
   const int rps = rows_per_split_for(K, ns);
   const float qk = sm_scale * kLog2e;
   if (ns == 1) {
-    hipLaunchKernelGGL((mla_bf16_e4m3_kernel<false>), dim3(1, BP), dim3(kMlaNT), 0, s, q, pool,
-                       row_scale, row_ids, K, rps, 1, qk, out, lse, nullptr, nullptr);
+    hipLaunchKernelGGL((mla_bf16_e4m3_kernel<false>), dim3(1, BP, L), dim3(kMlaNT), 0, s, q, pool,
+                       row_scale, row_ids, K, rps, 1, qk, out, lse, nullptr, nullptr,
+                       pool_layer_rows);
     return hipGetLastError();
   }
   float* part_o = static_cast<float*>(ws);
-  float* part_ml = part_o + (size_t)BP * ns * kHq * kDVal;
-  hipLaunchKernelGGL((mla_bf16_e4m3_kernel<true>), dim3(ns, BP), dim3(kMlaNT), 0, s, q, pool,
-                     row_scale, row_ids, K, rps, ns, qk, out, lse, part_o, part_ml);
+  float* part_ml = part_o + (size_t)L * BP * ns * kHq * kDVal;
+  hipLaunchKernelGGL((mla_bf16_e4m3_kernel<true>), dim3(ns, BP, L), dim3(kMlaNT), 0, s, q, pool,
+                     row_scale, row_ids, K, rps, ns, qk, out, lse, part_o, part_ml,
+                     pool_layer_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq, 2), dim3(kWave), 0, s, ns, part_o, part_ml, out, lse);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq, 2 * L), dim3(kWave), 0, s, ns, part_o,
+                     part_ml, out, lse);
   return hipGetLastError();
 }
 
-hipError_t launch_mla_f32(const BatchDims& d, int K, const float* q, const float* pool,
-                          const int32_t* row_ids, float sm_scale, float* out, float* lse,
-                          void* ws, hipStream_t s) {
+hipError_t launch_mla_f32(const BatchDims& d, int K, int L, int64_t pool_layer_rows,
+                          const float* q, const float* pool, const int32_t* row_ids,
+                          float sm_scale, float* out, float* lse, void* ws, hipStream_t s) {
   const int BP = d.B * d.P;
-  const int ns = mla_num_splits(d.B, d.P, K);
+  const int ns = mla_num_splits(d.B, d.P, K, L);
   const int rps = rows_per_split_for(K, ns);
   const float qk = sm_scale * kLog2e;
+  // one launch per layer; the layers reuse the first layer's partials (same stream)
   float* part_o = static_cast<float*>(ws);
   float* part_ml = ns > 1 ? part_o + (size_t)BP * ns * kHq * kDVal : nullptr;
-  hipLaunchKernelGGL(mla_f32_kernel, dim3(ns, BP), dim3(kMlaNT), 0, s, q, pool, row_ids, K, rps, ns,
-                     qk, ns > 1 ? 1 : 0, out, lse, part_o, part_ml);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ns == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq, 2), dim3(kWave), 0, s, ns, part_o, part_ml, out, lse);
-  return hipGetLastError();
+  for (int l = 0; l < L; ++l) {
+    const float* ql = q + (size_t)l * BP * kHq * kDLat;
+    const float* pl = pool + (size_t)l * pool_layer_rows * kDLat;
+    float* ol = out + (size_t)l * BP * kHq * kDVal;
+    float* ll = lse ? lse + (size_t)l * BP * kHq : nullptr;
+    hipLaunchKernelGGL(mla_f32_kernel, dim3(ns, BP), dim3(kMlaNT), 0, s, ql, pl, row_ids, K, rps,
+                       ns, qk, ns > 1 ? 1 : 0, ol, ll, part_o, part_ml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ns > 1) {
+      hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq, 2), dim3(kWave), 0, s, ns, part_o,
+                         part_ml, ol, ll);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace hs

@@ -84,6 +84,8 @@ class DeviceStep:
         self.ws_topk = torch.empty(max(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, P, Ts, K), 16),
                                    dtype=torch.uint8, device=d)
         mla_ws = _lib.workspace_bytes(_lib.HS_OP_MLA, B, P, Ts, K, wl.Hq)
+        if L > 1:
+            mla_ws = max(mla_ws, _lib.mla_layers_workspace_bytes(B, P, K, wl.Hq, L))
         self.ws_mla = torch.empty(max(mla_ws, 16), dtype=torch.uint8, device=d) if mla_ws else None
         # latent pool and residency tables
         from workloads.gen import build_pool
@@ -213,12 +215,23 @@ class DeviceStep:
                                self.row_ids, wl.sm_scale, self.out[layer], self.lse[layer],
                                self.ws_mla, stream)
 
+    def run_attention_layers(self, stream=None):
+        """Attention of all L layers over the shared row ids in one call."""
+        wl = self.wl
+        _lib.sparse_mla_decode_layers(self.batch, wl.K, wl.Hq, wl.L, wl.q_dtype, self.q,
+                                      wl.kv_dtype, self.pool, self.n_rows, self.row_scale,
+                                      self.row_ids, wl.sm_scale, self.out, self.lse, self.ws_mla,
+                                      stream)
+
     def run(self, stream=None):
-        """One whole decode step: indexer + top-K, resolve (+ fault copies), L x attention."""
+        """One whole decode step: indexer + top-K, resolve (+ fault copies), attention of
+        the L layers (one call for several layers)."""
         self.run_indexer_topk(stream)
         self.run_resolve(stream)
-        for l in range(self.wl.L):
-            self.run_attention(l, stream)
+        if self.wl.L > 1:
+            self.run_attention_layers(stream)
+        else:
+            self.run_attention(0, stream)
 
     def append(self, s: int, stream=None):
         """KV append after step s of a decode-loop workload: one token per request

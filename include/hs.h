@@ -11,6 +11,7 @@
  *                        resident page in place / hot slot with an LRU refresh /
  *                        single-row fault copied from pinned host memory
  *   hs_sparse_mla_decode sparse MLA attention over the selected latent rows
+ *                        (hs_sparse_mla_decode_layers: several layers, one launch)
  *
  * Conventions shared by every entry point:
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise; host
@@ -304,6 +305,28 @@ hs_status hs_sparse_mla_decode(const hs_batch* batch, int32_t K, int32_t Hq, hs_
                                const float* row_scale, const int32_t* row_ids,
                                float sm_scale, float* out, float* lse, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* The same attention for L layers that share one selection (the IndexShare
+ * reuse on page "Un contexte d'un million sur huit H200", section "Ce qui se
+ * passe": one indexer pass and one top-K set feed several attention layers), in
+ * one launch: the grid spans the layers, so layers that are each too small to
+ * fill the GPU run side by side, and one combine merges every layer's slices.
+ *   q         [L, B, P, Hq, 576]    layer l's queries
+ *   pool      [L, pool_layer_rows, 576], row_scale [L, pool_layer_rows]: layer
+ *             l's row r is at l * pool_layer_rows + r (row_ids index every layer)
+ *   out       [L, B, P, Hq, 512], lse [L, B, P, Hq] (NULL = not written)
+ *   ws        hs_mla_layers_workspace_bytes(B, P, K, Hq, L) bytes, 16-byte
+ *             aligned (0 = none needed)
+ * L = 1 computes the same as hs_sparse_mla_decode.  For L > 1 the K rows are cut
+ * into fewer slices per layer, so the fp32 summation order (and the last bits)
+ * can differ from L calls of hs_sparse_mla_decode; it depends only on row_ids. */
+hs_status hs_sparse_mla_decode_layers(const hs_batch* batch, int32_t K, int32_t Hq, int32_t L,
+                                      hs_dtype q_t, const void* q, hs_dtype kv_t,
+                                      const void* pool, int64_t pool_layer_rows,
+                                      const float* row_scale, const int32_t* row_ids,
+                                      float sm_scale, float* out, float* lse, void* ws,
+                                      size_t ws_bytes, void* stream);
+size_t hs_mla_layers_workspace_bytes(int32_t B, int32_t P, int32_t K, int32_t Hq, int32_t L);
 
 #define HS_OP_INDEXER 0
 #define HS_OP_TOPK 1

@@ -158,6 +158,23 @@ def test_cache_operations_validate_on_the_host():
                                fake, ws_n, None) == 1
 
 
+def test_attention_layers_validates_on_the_host():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(16)
+    b = _lib.Batch(2, 1, 1024, 16, 32)
+    call = lambda K, Hq, L, plr, ws_n: lib.hs_sparse_mla_decode_layers(
+        ctypes.byref(b), K, Hq, L, _lib.HS_BF16, fake, _lib.HS_E4M3, fake, plr, fake, fake,
+        ctypes.c_float(0.05), fake, None, fake, ws_n, None)
+    assert call(2048, 16, 0, 4096, 1 << 30) == 2            # L out of range
+    assert call(2048, 16, 17, 4096, 1 << 30) == 2
+    assert call(2048, 16, 4, 0, 1 << 30) == 2               # no layer stride for L > 1
+    assert call(2048, 8, 4, 4096, 1 << 30) == 2             # one shard of 16 heads
+    need = _lib.mla_layers_workspace_bytes(2, 1, 2048, 16, 4)
+    assert need > 0 and call(2048, 16, 4, 4096, need - 1) == 5
+    assert _lib.mla_layers_workspace_bytes(2, 1, 2048, 16, 1) == \
+        _lib.workspace_bytes(_lib.HS_OP_MLA, 2, 1, 1024, 2048, 16)
+
+
 def test_workspace_sizes():
     assert _lib.workspace_bytes(_lib.HS_OP_TOPK, 32, 1, 131072, 2048) >= 32 * 131072 * 8
     assert _lib.workspace_bytes(_lib.HS_OP_RESOLVE, 32, 1, 131072, 2048) == 0

@@ -499,3 +499,51 @@ def test_resolve_merge_path_long_stride():
         ds.run()
         ost, rr, info = gc.full_check(ds, wl, ost, s=s, attn_tol=2e-2)
         _say(s, info["counts"].tolist())
+
+
+@pytest.mark.parametrize("kv", ["e4m3", "f32"])
+def test_attention_layers_call_matches_per_layer_calls(kv):
+    """hs_sparse_mla_decode_layers over L layers against L calls of
+    hs_sparse_mla_decode: identical for L = 1, equal to fp32 summation order for
+    L = 3 (fewer slices per layer); both paths (bf16 x E4M3 and fp32)."""
+    from decode_indexer_logits_amd import _lib
+    rng = np.random.default_rng(71)
+    B, P, K, Hq, L, n_rows = 3, 1, 1000, 16, 3, 4096
+    ctx = torch.tensor([K, K, K], dtype=torch.int32, device="cuda")
+    batch = _lib.make_batch(B, P, 1024, ctx)
+    rid = np.stack([rng.choice(n_rows, K, replace=False) for _ in range(B)]).astype(np.int32)
+    rid[1, 700:] = -1                                   # a short selection
+    row_ids = torch.from_numpy(rid.reshape(B, P, K)).cuda()
+    if kv == "e4m3":
+        q = torch.from_numpy(gen.bf16_bits(rng.standard_normal((L, B, P, Hq, 576))).view(np.int16)).cuda()
+        pool = torch.randint(0, 256, (L, n_rows, 576), dtype=torch.uint8, device="cuda")
+        pool[(pool & 0x7F) == 0x7F] = 0                 # no NaN codes
+        rs = torch.rand((L, n_rows), device="cuda") * 0.02
+        qt = "bf16"
+    else:
+        q = torch.randn((L, B, P, Hq, 576), device="cuda")
+        pool = torch.randn((L, n_rows, 576), device="cuda")
+        rs = None
+        qt = "f32"
+    ws = torch.empty(max(_lib.mla_layers_workspace_bytes(B, P, K, Hq, L),
+                         _lib.workspace_bytes(_lib.HS_OP_MLA, B, P, 1024, K, Hq), 16),
+                     dtype=torch.uint8, device="cuda")
+    out1 = torch.empty((L, B, P, Hq, 512), device="cuda")
+    lse1 = torch.empty((L, B, P, Hq), device="cuda")
+    for l in range(L):
+        _lib.sparse_mla_decode(batch, K, Hq, qt, q[l], kv, pool[l], None if rs is None else rs[l],
+                               row_ids, 1.0 / 24.0, out1[l], lse1[l], ws)
+    outL = torch.empty_like(out1)
+    lseL = torch.empty_like(lse1)
+    _lib.sparse_mla_decode_layers(batch, K, Hq, L, qt, q, kv, pool, n_rows, rs, row_ids, 1.0 / 24.0,
+                                  outL, lseL, ws)
+    one = torch.empty_like(out1[0])
+    one_lse = torch.empty_like(lse1[0])
+    _lib.sparse_mla_decode_layers(batch, K, Hq, 1, qt, q[0], kv, pool[0], n_rows,
+                                  None if rs is None else rs[0], row_ids, 1.0 / 24.0, one, one_lse,
+                                  ws)
+    torch.cuda.synchronize()
+    assert torch.equal(one, out1[0]) and torch.equal(one_lse, lse1[0])
+    err = ((outL - out1).abs().amax(dim=-1) / out1.abs().amax(dim=-1).clamp_min(1e-30)).max().item()
+    assert err <= 1e-5, err
+    assert torch.allclose(lseL, lse1, rtol=1e-6, atol=1e-6)
