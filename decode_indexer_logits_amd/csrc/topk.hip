@@ -10,7 +10,7 @@
 //   2. histogram  of the top 11 key bits, per 8192-token chunk: LDS counts,
 //                 then one global atomic per non-empty bin (the fused path of
 //                 hs_indexer_topk builds it in the indexer's epilogue instead)
-//   3. filter     one wave of every 4096-token workgroup (16384 on rows over
+//   3. filter     one wave of every 4096-token workgroup (8192 on rows over
 //                 2^18 tokens, 1024 when few rows would leave the chip idle)
 //                 finds the bin b1
 //                 holding the K-th largest key from the row's histogram; keys
@@ -39,7 +39,7 @@ namespace {
 constexpr int kBins1 = 2048;   // top 11 key bits
 constexpr int kChunk = 8192;   // tokens per workgroup of the histogram pass
 constexpr int kFChunk = 4096;  // tokens per workgroup of the filter pass (rows up to 2^18)
-constexpr int kFChunkLong = 16384;   // the same for longer rows
+constexpr int kFChunkLong = 8192;    // the same for longer rows
 constexpr int kFChunkShort = 1024;   // the same when few rows would leave the chip idle
 constexpr int kScanNT = 256;
 constexpr int kMaxK = 8192;
@@ -243,8 +243,8 @@ __device__ void candidates_threshold(const uint32_t* ck, const int32_t* ct, int 
   *t_cut_out = t_cut;
 }
 
-// FCH tokens per workgroup: 4096, or 16384 on rows longer than 2^18 tokens so
-// that at most 64 workgroups per row share the row's two output counters
+// FCH tokens per workgroup: 4096, or 8192 on rows longer than 2^18 tokens so
+// that at most 128 workgroups per row share the row's two output counters
 // (same-address atomics from every die serialize).
 template <int FCH>
 __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __restrict__ ctx_len,
