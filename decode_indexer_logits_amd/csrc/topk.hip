@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   uint32_t* s_ck = s_cand;
   int32_t* s_ct = reinterpret_cast<int32_t*>(s_cand + kFinCand);
   __shared__ int scratch[kFinNT / kWave + 1];
-  __shared__ int s_d, s_pos;
+  __shared__ int s_d, s_pos, s_stage;
   __shared__ uint32_t s_before;
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
@@ -375,26 +375,15 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
       s_ck[i] = gk[i];
       s_ct[i] = gt[i];
     }
-  if (tid == 0) s_pos = (int)above;
+  if (tid == 0) {
+    s_pos = (int)above;
+    s_stage = 0;                  // staging cursor of the two-pass path below
+  }
   __syncthreads();
-  const uint32_t* ck = in_lds ? s_ck : gk;
-  const int32_t* ct = in_lds ? s_ct : gt;
-  uint32_t tau;
-  int t_cut;
-  candidates_threshold<kFinNT>(ck, ct, nc, b1, (uint32_t)K - above, h, scratch, &s_d, &s_before,
-                               &tau, &t_cut);
+  const int lane = lane_id();
   // chosen candidates join the outright selections: one ballot and one LDS
   // atomic per wave (same-address atomics from every thread serialize)
-  const int lane = lane_id();
-  const int nc_up = (nc + kFinNT - 1) / kFinNT * kFinNT;
-  for (int i = tid; i < nc_up; i += kFinNT) {
-    bool chosen = false;
-    int t = 0;
-    if (i < nc) {
-      const uint32_t key = ck[i];
-      t = ct[i];
-      chosen = key > tau || (key == tau && t <= t_cut);
-    }
+  auto push = [&](bool chosen, int t) {
     const uint64_t m = __ballot(chosen);
     if (m) {
       int base = 0;
@@ -403,6 +392,70 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
       const int at = base + lanes_below(m);
       if (chosen && at < kMaxK) outl[at] = t;
     }
+  };
+  const uint32_t* ck = in_lds ? s_ck : gk;
+  const int32_t* ct = in_lds ? s_ct : gt;
+  int nsel = nc;                  // candidates the threshold search runs over
+  uint32_t kk = (uint32_t)K - above;
+  if (!in_lds) {
+    // Too many candidates for LDS: one pass over global memory bins them by
+    // key bits 20..10 and finds the sub-bin dA holding the kk-th largest key;
+    // a second pass selects the candidates above dA outright and stages those
+    // in dA in LDS (their number is the bin's count), and the search goes on
+    // over the staged set.  A sub-bin too large for LDS keeps every pass in
+    // global memory.
+    for (int i = tid; i < kBins1; i += kFinNT) h[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < nc; i += kFinNT) atomicAdd(&h[(gk[i] >> 10) & 0x7FFu], 1u);
+    __syncthreads();
+    find_bin<kFinNT>(h, kBins1, kk, true, scratch, &s_d, &s_before);
+    const uint32_t dA = (uint32_t)s_d;
+    const int n2 = (int)h[dA];
+    if (n2 <= kFinCand) {
+      kk -= s_before;
+      const int nc_up = (nc + kFinNT - 1) / kFinNT * kFinNT;
+      for (int i = tid; i < nc_up; i += kFinNT) {
+        uint32_t key = 0;
+        int t = 0;
+        if (i < nc) {
+          key = gk[i];
+          t = gt[i];
+        }
+        const uint32_t sub = (key >> 10) & 0x7FFu;
+        push(i < nc && sub > dA, t);
+        const bool stage = i < nc && sub == dA;
+        const uint64_t m = __ballot(stage);
+        if (m) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&s_stage, __popcll(m));
+          base = __shfl(base, 0);
+          if (stage) {
+            const int at = base + lanes_below(m);
+            s_ck[at] = key;
+            s_ct[at] = t;
+          }
+        }
+      }
+      __syncthreads();
+      ck = s_ck;
+      ct = s_ct;
+      nsel = n2;
+    }
+    __syncthreads();
+  }
+  uint32_t tau;
+  int t_cut;
+  candidates_threshold<kFinNT>(ck, ct, nsel, b1, kk, h, scratch, &s_d, &s_before, &tau, &t_cut);
+  const int ns_up = (nsel + kFinNT - 1) / kFinNT * kFinNT;
+  for (int i = tid; i < ns_up; i += kFinNT) {
+    bool chosen = false;
+    int t = 0;
+    if (i < nsel) {
+      const uint32_t key = ck[i];
+      t = ct[i];
+      chosen = key > tau || (key == tau && t <= t_cut);
+    }
+    push(chosen, t);
   }
   __syncthreads();
   // emit the K selected tokens in ascending order: an LDS bitmap laid over the
