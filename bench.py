@@ -240,7 +240,7 @@ def cache_ops_bench(torch, reps: int = 5) -> dict:
 
 
 def ceilings(torch, ds, wl, reps: int = 10) -> dict:
-    """Measured ceilings on this machine, as context for the fractions of the published peaks
+    """Measured ceilings of the machine it runs on, as context for the fractions of the published peaks
     (probe kernels of libhsprobe.so, median of HIP-event timings after one untimed launch,
     MALL flushed before each launch):
     - the indexer's key pages read in the indexer's own page order with no products and
