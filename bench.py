@@ -246,7 +246,9 @@ def ceilings(torch, ds, wl, reps: int = 10) -> dict:
     - the indexer's key pages read in the indexer's own page order with no products and
       no score writes (the same grid and two pages in flight per wave);
     - a plain stream of the same number of bytes over the key pool;
-    - a 256 MiB DMA copy from pinned host memory to HBM (the host link)."""
+    - a 256 MiB DMA copy from pinned host memory to HBM (the host link);
+    - zero-copy reads of 32768 seeded random 576-byte rows of the workload's own pinned
+      host pool into HBM (the fault copy's access pattern, without the method)."""
     import ctypes
     from pathlib import Path
     import numpy as np
@@ -254,6 +256,7 @@ def ceilings(torch, ds, wl, reps: int = 10) -> dict:
     vp = ctypes.c_void_p
     lib.hsp_read_stream.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, vp]
     lib.hsp_read_pages.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+    lib.hsp_host_gather.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp]
     flush_buf = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     sink0 = torch.empty((), dtype=torch.float32, device="cuda")
     flush = lambda: torch.sum(flush_buf, dim=0, out=sink0)
@@ -292,6 +295,25 @@ def ceilings(torch, ds, wl, reps: int = 10) -> dict:
     _, ms = _time_launches(lambda: dst.copy_(src, non_blocking=True), reps, torch)
     dma_ms = sorted(ms)[len(ms) // 2]
     out["host_dma_GBs"] = round((256 << 20) / (dma_ms / 1e3) / 1e9, 2)
+    if ds.host_rows is not None:
+        nrows_host = ds.host_rows.numel() * ds.host_rows.element_size() // 576
+        n_g = min(32768, nrows_host)
+        g = np.random.default_rng(12345)
+        offs = torch.from_numpy(g.choice(nrows_host, n_g, replace=False).astype(np.int64) * 576).cuda()
+        gdst = torch.empty(n_g * 576, dtype=torch.uint8, device="cuda")
+        hdev = ds._host_rows_dev
+
+        def gather():
+            r = lib.hsp_host_gather(vp(hdev), vp(offs.data_ptr()), n_g, 576, vp(gdst.data_ptr()), st)
+            assert r == 0, f"hsp_host_gather: hip error {r}"
+        gather()
+        torch.cuda.synchronize()
+        _, ms = _time_launches(gather, reps, torch)
+        g_ms = sorted(ms)[len(ms) // 2]
+        out["host_random_rows_GBs"] = round(n_g * 576 / (g_ms / 1e3) / 1e9, 2)
+        out["host_random_rows_note"] = (f"{n_g} random 576-byte rows of the {nrows_host * 576 / 1e9:.2f} GB "
+                                        "pinned host pool, zero-copy into HBM")
+        del gdst, offs
     del src, dst, flush_buf
     torch.cuda.empty_cache()
     return out

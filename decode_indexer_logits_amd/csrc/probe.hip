@@ -4,13 +4,15 @@
 //
 //   hsp_read_stream  reads n 16-byte words once, a grid-stride loop with four
 //                    independent loads per thread (the plain HBM read rate)
+//   hsp_host_gather  copies scattered rows from pinned host memory to HBM
+//                    (zero-copy reads, the access pattern of the fault copy)
 //   hsp_read_pages   reads the indexer's key pages in the indexer's own order
 //                    (one workgroup of four waves per 8192-token tile, pages
 //                    through the block table, two pages in flight per wave), with
 //                    no products and no score writes
 //
-// Both fold what they read into one word that is stored only when it equals an
-// impossible value, so the loads are not removed.
+// The two read probes fold what they read into one word that is stored only
+// when it equals an impossible value, so the loads are not removed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -82,9 +84,37 @@ __global__ __launch_bounds__(256) void read_pages_kernel(const int32_t* __restri
   if (acc == 0x9E3779B9u) sink[blockIdx.y * gridDim.x + blockIdx.x] = acc;
 }
 
+// Zero-copy gather of n rows of row_bytes (a multiple of 16) from device-mapped
+// pinned host memory into device memory: rows[i] is the byte offset of row i.
+// Eight rows per workgroup of 256 threads, 16-byte words.
+__global__ __launch_bounds__(256) void host_gather_kernel(const uint8_t* __restrict__ host,
+                                                          const int64_t* __restrict__ rows, int n,
+                                                          int row_bytes, uint8_t* __restrict__ dst) {
+  const int r0 = blockIdx.x * 8;
+  const int words = row_bytes / 16;
+  for (int w = threadIdx.x; w < 8 * words; w += 256) {
+    const int i = r0 + w / words, c = w % words;
+    if (i >= n) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(host + rows[i] + 16 * c);
+    *reinterpret_cast<uint4*>(dst + (int64_t)i * row_bytes + 16 * c) = v;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Copies n rows of row_bytes from the device-mapped pinned host address `host`
+// (offsets rows[0..n), 16-byte aligned) to dst (n * row_bytes bytes).
+int hsp_host_gather(const void* host, const int64_t* rows, int n, int row_bytes, void* dst,
+                    hipStream_t stream) {
+  if (!host || !rows || !dst || n < 1 || row_bytes < 16 || row_bytes % 16)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(host_gather_kernel, dim3((n + 7) / 8), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(host), rows, n, row_bytes,
+                     static_cast<uint8_t*>(dst));
+  return (int)hipGetLastError();
+}
 
 // Reads `bytes` (a multiple of 16, 16-byte aligned) from device memory `src`
 // with `workgroups` workgroups of 256 threads; `sink` holds `workgroups` words

@@ -37,7 +37,7 @@ def test_probe_library_is_separate_and_loads():
     library exports none of them."""
     probe = _lib.LIB_PATH.parent / "libhsprobe.so"
     lib = ctypes.CDLL(str(probe))
-    for n in ("hsp_read_stream", "hsp_read_pages"):
+    for n in ("hsp_read_stream", "hsp_read_pages", "hsp_host_gather"):
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True,
                          text=True).stdout
