@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kMlaNT = 256;
 constexpr int kMlaTargetWGs = 256;   // splits of the selected rows fill about this many workgroups
+constexpr int kMlaMaxSplitRows = 1024;   // and no slice walks more than 16 tiles
 constexpr int kTile = 64;
 constexpr int kPtStride = 72;
 constexpr int kHq = 16;
@@ -402,12 +403,15 @@ __host__ inline int rows_per_split_for(int K, int nsplit) {
 }  // namespace
 
 // Splits of the K rows so that one launch of L layers fills about
-// kMlaTargetWGs workgroups.
+// kMlaTargetWGs workgroups, with at most kMlaMaxSplitRows rows per slice (a
+// slice's tiles run one after another: at 256 request-positions one slice
+// each would walk 32 tiles).
 int mla_num_splits(int B, int P, int K, int L) {
   const int BPL = B * P * L;
   const int max_split = (K + kTile - 1) / kTile;
   static_assert(8192 / kTile <= kCombineMaxSplit, "one lane per slice in the combine");
   int ns = (kMlaTargetWGs + BPL - 1) / BPL;
+  ns = max(ns, (K + kMlaMaxSplitRows - 1) / kMlaMaxSplitRows);
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
   const int rps = rows_per_split_for(K, ns);
