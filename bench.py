@@ -36,10 +36,10 @@ KV_ROW = 576
 # rocprofv3 --pmc runs (FETCH_SIZE x 2 + WRITE_SIZE x 1, factors calibrated with a
 # 512 MiB read and a 512 MiB fill in the same runs; profiles/indexer_mixed_128k_pmc.txt).
 # Reported only while the kernel's sources are the ones the counters were taken on.
-INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.17e6,
+INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.04e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
-                   "sha256": "73d0ee542a6caf8ba7de33321a05ceb75e5ba736f00f4eb8540228af5de3e28a"}
+                   "sha256": "4637495306c4878956527295468e9452d87aa15c85adf6fb860c3f408f624249"}
 
 
 def _indexer_traffic(workload: str, indexer_q: str):
