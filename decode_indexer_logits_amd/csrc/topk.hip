@@ -370,10 +370,27 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   const int32_t* sel = ws.sel + (size_t)r * K;
   for (int i = tid; i < (int)above; i += kFinNT) outl[i] = sel[i];
   const bool in_lds = nc <= kFinCand;
+  // loops over global candidates issue kLd independent loads per thread before
+  // using any of them (the candidates' order does not matter to the result)
+  constexpr int kLd = 8;
   if (in_lds)
-    for (int i = tid; i < nc; i += kFinNT) {
-      s_ck[i] = gk[i];
-      s_ct[i] = gt[i];
+    for (int i0 = tid; i0 < nc; i0 += kLd * kFinNT) {
+      uint32_t kx[kLd];
+      int32_t tx[kLd];
+#pragma unroll
+      for (int u = 0; u < kLd; ++u) {
+        const int i = min(i0 + u * kFinNT, nc - 1);
+        kx[u] = gk[i];
+        tx[u] = gt[i];
+      }
+#pragma unroll
+      for (int u = 0; u < kLd; ++u) {
+        const int i = i0 + u * kFinNT;
+        if (i < nc) {
+          s_ck[i] = kx[u];
+          s_ct[i] = tx[u];
+        }
+      }
     }
   if (tid == 0) {
     s_pos = (int)above;
@@ -406,33 +423,49 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
     // global memory.
     for (int i = tid; i < kBins1; i += kFinNT) h[i] = 0;
     __syncthreads();
-    for (int i = tid; i < nc; i += kFinNT) atomicAdd(&h[(gk[i] >> 10) & 0x7FFu], 1u);
+    for (int i0 = tid; i0 < nc; i0 += kLd * kFinNT) {
+      uint32_t kx[kLd];
+#pragma unroll
+      for (int u = 0; u < kLd; ++u) kx[u] = gk[min(i0 + u * kFinNT, nc - 1)];
+#pragma unroll
+      for (int u = 0; u < kLd; ++u)
+        if (i0 + u * kFinNT < nc) atomicAdd(&h[(kx[u] >> 10) & 0x7FFu], 1u);
+    }
     __syncthreads();
     find_bin<kFinNT>(h, kBins1, kk, true, scratch, &s_d, &s_before);
     const uint32_t dA = (uint32_t)s_d;
     const int n2 = (int)h[dA];
     if (n2 <= kFinCand) {
       kk -= s_before;
-      const int nc_up = (nc + kFinNT - 1) / kFinNT * kFinNT;
-      for (int i = tid; i < nc_up; i += kFinNT) {
-        uint32_t key = 0;
-        int t = 0;
-        if (i < nc) {
-          key = gk[i];
-          t = gt[i];
+      // every thread runs the same number of batches (the ballots need whole waves)
+      const int nc_up = (nc + kLd * kFinNT - 1) / (kLd * kFinNT) * (kLd * kFinNT);
+      for (int i0 = tid; i0 < nc_up; i0 += kLd * kFinNT) {
+        uint32_t kx[kLd];
+        int32_t tx[kLd];
+#pragma unroll
+        for (int u = 0; u < kLd; ++u) {
+          const int i = min(i0 + u * kFinNT, nc - 1);
+          kx[u] = gk[i];
+          tx[u] = gt[i];
         }
-        const uint32_t sub = (key >> 10) & 0x7FFu;
-        push(i < nc && sub > dA, t);
-        const bool stage = i < nc && sub == dA;
-        const uint64_t m = __ballot(stage);
-        if (m) {
-          int base = 0;
-          if (lane == 0) base = atomicAdd(&s_stage, __popcll(m));
-          base = __shfl(base, 0);
-          if (stage) {
-            const int at = base + lanes_below(m);
-            s_ck[at] = key;
-            s_ct[at] = t;
+#pragma unroll
+        for (int u = 0; u < kLd; ++u) {
+          const bool valid = i0 + u * kFinNT < nc;
+          const uint32_t key = kx[u];
+          const int t = tx[u];
+          const uint32_t sub = (key >> 10) & 0x7FFu;
+          push(valid && sub > dA, t);
+          const bool stage = valid && sub == dA;
+          const uint64_t m = __ballot(stage);
+          if (m) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&s_stage, __popcll(m));
+            base = __shfl(base, 0);
+            if (stage) {
+              const int at = base + lanes_below(m);
+              s_ck[at] = key;
+              s_ct[at] = t;
+            }
           }
         }
       }
