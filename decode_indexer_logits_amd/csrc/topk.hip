@@ -368,11 +368,19 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   // the outright selections and (when they fit) the candidates go to LDS
   // with one pass of independent loads
   const int32_t* sel = ws.sel + (size_t)r * K;
-  for (int i = tid; i < (int)above; i += kFinNT) outl[i] = sel[i];
-  const bool in_lds = nc <= kFinCand;
-  // loops over global candidates issue kLd independent loads per thread before
+  // loops over global memory issue kLd independent loads per thread before
   // using any of them (the candidates' order does not matter to the result)
   constexpr int kLd = 8;
+  static_assert(kLd * kFinNT >= kMaxK, "one round of loads covers the outright selections");
+  {
+    int32_t sx[kLd];
+#pragma unroll
+    for (int u = 0; u < kLd; ++u) sx[u] = sel[min(tid + u * kFinNT, max((int)above - 1, 0))];
+#pragma unroll
+    for (int u = 0; u < kLd; ++u)
+      if (tid + u * kFinNT < (int)above) outl[tid + u * kFinNT] = sx[u];
+  }
+  const bool in_lds = nc <= kFinCand;
   if (in_lds)
     for (int i0 = tid; i0 < nc; i0 += kLd * kFinNT) {
       uint32_t kx[kLd];
