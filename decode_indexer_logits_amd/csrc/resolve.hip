@@ -483,15 +483,30 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
       }
     }
     __syncthreads();
-    // 4. fault i -> victim i
+    // 4. fault i -> victim i.  Victims are distinct slots and an evicted token
+    // is hot, so never one of the faults: every old slot owner is read first
+    // (one round of loads, n_serve <= P*K <= MAXE * kResNT), then written.
     int my_ev = 0;
     int32_t* fb = faults + (size_t)b * PK * 2;
-    for (int i = tid; i < n_serve; i += kResNT) {
-      const int v = keys64 ? (int)(uint32_t)sA64[i] : V32[i];
-      const int t = sF[i];
-      const int old = s2t[v];
-      if (old >= 0) {
-        t2s[old] = -1;
+    int vv[MAXE], tt[MAXE], oo[MAXE];
+#pragma unroll
+    for (int u = 0; u < MAXE; ++u) {
+      const int i = tid + u * kResNT;
+      vv[u] = -1;
+      tt[u] = 0;
+      if (i < n_serve) {
+        vv[u] = keys64 ? (int)(uint32_t)sA64[i] : V32[i];
+        tt[u] = sF[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < MAXE; ++u) oo[u] = vv[u] >= 0 ? s2t[vv[u]] : -1;
+#pragma unroll
+    for (int u = 0; u < MAXE; ++u) {
+      const int v = vv[u], t = tt[u], i = tid + u * kResNT;
+      if (v < 0) continue;
+      if (oo[u] >= 0) {
+        t2s[oo[u]] = -1;
         ++my_ev;
       }
       s2t[v] = t;
