@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
                                                                TopkWs ws, int32_t* __restrict__ topk) {
   __shared__ uint32_t h[kBins1];
   __shared__ int32_t outl[kMaxK];
-  __shared__ uint32_t s_cand[2 * kFinCand];   // candidate keys, then tokens; later the bitmap
+  __shared__ __attribute__((aligned(16))) uint32_t s_cand[2 * kFinCand];   // candidate keys, then tokens; later the bitmap
   uint32_t* s_ck = s_cand;
   int32_t* s_ct = reinterpret_cast<int32_t*>(s_cand + kFinCand);
   __shared__ int scratch[kFinNT / kWave + 1];
@@ -505,16 +505,22 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   // LDS, and each selected token finds its own output index as its run's
   // prefix plus the popcounts of the words before it in the run, so the work
   // per thread stays even however the selection clusters.
+  // Runs are whole 16-byte groups of words (wpt a multiple of 4), so a run's
+  // popcounts and a token's count of the set bits before it in its run come
+  // from independent 16-byte LDS reads; words past the pass's tokens are zero.
   constexpr int kBmWords = 2 * kFinCand;
   constexpr int kBmTok = kBmWords * 32;
-  static_assert(kBmWords % kFinNT == 0 && kFinNT <= kBins1, "runs fit the prefix array");
+  constexpr int kMaxQ = kBmWords / kFinNT / 4;   // 16-byte groups per run, at most
+  static_assert(kBmWords % (4 * kFinNT) == 0 && kFinNT <= kBins1, "runs fit the prefix array");
   uint32_t* bmw = s_cand;
+  const uint4* bmq = reinterpret_cast<const uint4*>(s_cand);
   uint32_t* run_pre = h;                    // the radix histogram is dead by now
+  auto popc4 = [](uint4 x) { return __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w); };
   int written = 0;
   for (int seg0 = 0; seg0 < n; seg0 += kBmTok) {
     const int nwords = (min(kBmTok, n - seg0) + 31) / 32;
-    const int wpt = (nwords + kFinNT - 1) / kFinNT;
-    for (int i = tid; i < nwords; i += kFinNT) bmw[i] = 0u;
+    const int qpt = (nwords + 4 * kFinNT - 1) / (4 * kFinNT);   // groups per run, <= kMaxQ
+    for (int i = tid; i < 4 * qpt * kFinNT; i += kFinNT) bmw[i] = 0u;
     __syncthreads();
     for (int i = tid; i < K; i += kFinNT) {
       const int t = outl[i] - seg0;
@@ -522,10 +528,9 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
     }
     __syncthreads();
     int c = 0;
-    for (int j = 0; j < wpt; ++j) {
-      const int w = tid * wpt + j;
-      if (w < nwords) c += __popc(bmw[w]);
-    }
+#pragma unroll
+    for (int q = 0; q < kMaxQ; ++q)
+      if (q < qpt) c += popc4(bmq[tid * qpt + q]);
     int tot;
     run_pre[tid] = (uint32_t)block_exclusive_scan<kFinNT>(c, scratch, &tot);
     __syncthreads();
@@ -533,9 +538,17 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
       const int t = outl[i] - seg0;
       if (t < 0 || t >= kBmTok) continue;
       const int w = t >> 5;
-      const int r0 = (w / wpt) * wpt;
-      int rank = (int)run_pre[w / wpt] + __popc(bmw[w] & ((1u << (t & 31)) - 1u));
-      for (int w2 = r0; w2 < w; ++w2) rank += __popc(bmw[w2]);
+      const int run = w / (4 * qpt);
+      const int dw = w - run * 4 * qpt;                 // words of the run before w
+      int rank = (int)run_pre[run] + __popc(bmw[w] & ((1u << (t & 31)) - 1u));
+#pragma unroll
+      for (int q = 0; q < kMaxQ; ++q) {
+        if (4 * q >= dw) continue;
+        const uint4 x = bmq[run * qpt + q];
+        const int k = dw - 4 * q;                      // words of this group before w
+        rank += __popc(x.x) + (k > 1 ? __popc(x.y) : 0) + (k > 2 ? __popc(x.z) : 0) +
+                (k > 3 ? __popc(x.w) : 0);
+      }
       out[written + rank] = outl[i];
     }
     written += tot;
