@@ -507,7 +507,8 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   // per thread stays even however the selection clusters.
   // Runs are whole 16-byte groups of words (wpt a multiple of 4), so a run's
   // popcounts and a token's count of the set bits before it in its run come
-  // from independent 16-byte LDS reads; words past the pass's tokens are zero.
+  // from independent 16-byte LDS reads; the last group's words past the pass's
+  // tokens are zero, and groups past it are never read.
   constexpr int kBmWords = 2 * kFinCand;
   constexpr int kBmTok = kBmWords * 32;
   constexpr int kMaxQ = kBmWords / kFinNT / 4;   // 16-byte groups per run, at most
@@ -520,7 +521,8 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   for (int seg0 = 0; seg0 < n; seg0 += kBmTok) {
     const int nwords = (min(kBmTok, n - seg0) + 31) / 32;
     const int qpt = (nwords + 4 * kFinNT - 1) / (4 * kFinNT);   // groups per run, <= kMaxQ
-    for (int i = tid; i < 4 * qpt * kFinNT; i += kFinNT) bmw[i] = 0u;
+    const int ngroups = (nwords + 3) / 4;
+    for (int i = tid; i < 4 * ngroups; i += kFinNT) bmw[i] = 0u;
     __syncthreads();
     for (int i = tid; i < K; i += kFinNT) {
       const int t = outl[i] - seg0;
@@ -530,7 +532,7 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
     int c = 0;
 #pragma unroll
     for (int q = 0; q < kMaxQ; ++q)
-      if (q < qpt) c += popc4(bmq[tid * qpt + q]);
+      if (q < qpt && tid * qpt + q < ngroups) c += popc4(bmq[tid * qpt + q]);
     int tot;
     run_pre[tid] = (uint32_t)block_exclusive_scan<kFinNT>(c, scratch, &tot);
     __syncthreads();
