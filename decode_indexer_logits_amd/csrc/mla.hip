@@ -97,6 +97,17 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
 
   // contraction step s takes dims dim0(s) .. +8 of head n (Q) and of row n (X)
   auto dim0 = [&](int s) { return 64 * (s >> 1) + 16 * g + 8 * (s & 1); };
+  const int32_t* rid_p = row_ids + (size_t)bp * K;
+  const int r_local = 16 * wave + n;
+  // row ids run one tile ahead of the row loads, so a tile's rows wait for one
+  // round of loads, not two; this lane gathers row r_local, bytes 64v + 16g .. +16
+  auto load_rid = [&](int kt) {
+    const int kk = kt + r_local;
+    return (kk < ke) ? rid_p[kk] : -1;
+  };
+  // the first row ids go out before the queries: loads complete in order, so
+  // the first gather then waits for its row ids only
+  int rid = load_rid(kb), rid_n = load_rid(kb + kTile);
   bf16x8_t qf[18];
   {
     const uint16_t* qp = q + ((size_t)bp * kHq + n) * kDLat;
@@ -108,15 +119,6 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
-  const int32_t* rid_p = row_ids + (size_t)bp * K;
-  const int r_local = 16 * wave + n;
-
-  // row ids run one tile ahead of the row loads, so a tile's rows wait for one
-  // round of loads, not two; this lane gathers row r_local, bytes 64v + 16g .. +16
-  auto load_rid = [&](int kt) {
-    const int kk = kt + r_local;
-    return (kk < ke) ? rid_p[kk] : -1;
-  };
   auto gather = [&](int rid, float& rs, uint4* raw) {
     rs = 0.f;
     if (rid >= 0) {
@@ -129,7 +131,6 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
       for (int v = 0; v < 9; ++v) raw[v] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  int rid = load_rid(kb), rid_n = load_rid(kb + kTile);
   float rs, rs_n = 0.f;
   uint4 raw[9], raw_n[9];
   gather(rid, rs, raw);
