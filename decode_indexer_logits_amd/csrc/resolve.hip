@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
       // one list per run of K entries (K may not be a multiple of 64)
 #pragma unroll
       for (int p = 0; p < 4; ++p)
-        if (p < P) nl[p] += __popcll(__ballot(xs[i] >= 0 && e / K == p));
+        if (p < P) nl[p] += __popcll(__ballot(xs[i] >= 0 && e >= p * K && e < p * K + K));
     }
     if (lane == 0)
 #pragma unroll
@@ -198,12 +198,13 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
   } else if (T_stride <= kMaxSel * 32) {
     // a bitmap of the selected tokens over the merge region: duplicates across
     // the positions collapse, and a token's index in U is the number of set
-    // bits below it (thread j owns a run of words; a block scan of the runs'
-    // popcounts, then the popcounts before the token inside its run)
+    // bits below it (thread j owns a run of 2^lw words; a block scan of the
+    // runs' popcounts, then the popcounts before the token inside its run)
     uint32_t* bm = reinterpret_cast<uint32_t*>(M);
     int32_t* run_pre = sF;                 // the fault list is written later
     const int nwords = T_stride / 32;
     const int wpt = (nwords + kResNT - 1) / kResNT;
+    const int lw = wpt <= 1 ? 0 : 32 - __clz(wpt - 1);   // runs of a power of two >= wpt words
     for (int w = tid; w < nwords; w += kResNT) bm[w] = 0u;
     __syncthreads();
 #pragma unroll
@@ -211,8 +212,8 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
       if (xs[i] >= 0) atomicOr(&bm[xs[i] >> 5], 1u << (xs[i] & 31));
     __syncthreads();
     int c = 0;
-    for (int j = 0; j < wpt; ++j) {
-      const int w = tid * wpt + j;
+    for (int j = 0; j < (1 << lw); ++j) {
+      const int w = (tid << lw) + j;
       if (w < nwords) c += __popc(bm[w]);
     }
     int tot;
@@ -223,9 +224,9 @@ __global__ __launch_bounds__(kResNT) void resolve_kernel(
       urank[i] = -1;
       const int x = xs[i];
       if (x < 0) continue;
-      const int w = x >> 5, run = w / wpt;
+      const int w = x >> 5, run = w >> lw;
       int r = run_pre[run] + __popc(bm[w] & ((1u << (x & 31)) - 1u));
-      for (int w2 = run * wpt; w2 < w; ++w2) r += __popc(bm[w2]);
+      for (int w2 = run << lw; w2 < w; ++w2) r += __popc(bm[w2]);
       urank[i] = r;
       sU[r] = x;                            // equal tokens write the same entry
     }
