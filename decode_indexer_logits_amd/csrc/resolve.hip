@@ -696,6 +696,7 @@ hipError_t launch_resolve_tables(const BatchDims& d, int K, const int32_t* topk,
   else if (slots <= 4 && entries <= 4) HS_RESOLVE(4, 4);
   else if (slots <= 8 && entries <= 4) HS_RESOLVE(8, 4);
   else if (slots <= 8 && entries <= 8) HS_RESOLVE(8, 8);
+  else if (slots <= 10 && entries <= 8) HS_RESOLVE(10, 8);   // (3+2)K hot rows at K = 2048
   else HS_RESOLVE(16, 8);
 #undef HS_RESOLVE
   return hipGetLastError();
