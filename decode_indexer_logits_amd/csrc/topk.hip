@@ -133,14 +133,10 @@ __device__ void wave_find_bin_top(const uint32_t* __restrict__ hrow, uint32_t k,
   uint32_t local = 0;
 #pragma unroll
   for (int j = 0; j < 32; ++j) local += c[j];
-  // sum over the lanes above this one (higher bins come first)
-  uint32_t incl = local;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_down(incl, o);
-    if (lane + o < kWave) incl += y;
-  }
-  uint32_t before = incl - local;
+  // sum over the lanes above this one (higher bins come first): the wave total
+  // less the inclusive prefix (DPP scan; the whole wave is active here)
+  const int pre = wave_inclusive_scan_i32((int)local);
+  uint32_t before = (uint32_t)(__builtin_amdgcn_readlane(pre, kWave - 1) - pre);
   if (before < k && before + local >= k) {
 #pragma unroll
     for (int j = 31; j >= 0; --j) {
@@ -292,13 +288,8 @@ __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __r
       packed += (t0 + e < n) ? ((bin > b1) ? 1 : ((bin == b1) ? 0x10000 : 0)) : 0;
     }
   }
-  // block exclusive prefix of the packed counts: wave scan, then wave sums
-  int incl = packed;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  // block exclusive prefix of the packed counts: DPP wave scan, then wave sums
+  const int incl = wave_inclusive_scan_i32(packed);
   if (lane == kWave - 1) s_wsum[wid] = incl;
   __syncthreads();
   if (tid == 0) {
