@@ -1,6 +1,6 @@
 // Token-sharded top-K on one GPU: the way a cache split across GPUs by tokens
-// selects (page "Un contexte d'un million sur huit H200", section "Les
-// chiffres": DCP splits the KV cache by tokens).  Each request's visible
+// selects (page "vLLM sert GLM-5.3 en contexte 1M sur 16 H200", section "Le
+// mécanisme": DCP splits the KV cache by tokens across GPUs).  Each request's visible
 // tokens are cut into S contiguous shards of T_stride/S tokens; every shard
 // keeps its own top-K (a row of its own for the radix select, so a few long
 // rows become many short ones), the candidates of all shards are gathered

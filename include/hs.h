@@ -160,8 +160,9 @@ hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t
                   void* ws, size_t ws_bytes, void* stream);
 
 /* Token-sharded top-K: the selection as a cache split across GPUs by tokens
- * makes it (page "Un contexte d'un million sur huit H200", section "Les
- * chiffres": DCP splits the KV cache by tokens), emulated on one GPU.  Each
+ * makes it (page "vLLM sert GLM-5.3 en contexte 1M sur 16 H200", section "Le
+ * mécanisme": DCP splits the KV cache by tokens across GPUs and gathers the
+ * fragments at every layer), emulated on one GPU.  Each
  * request's tokens are cut into S contiguous shards of T_stride/S tokens; each
  * shard keeps its own top-K, and the K best of the union of those candidates
  * are kept, with the same order and tie rule.  The result equals hs_topk's

@@ -48,7 +48,7 @@ import numpy as np
 
 BLOCK = 64
 
-ERR_APPEND_RANGE = 4      # a request would pass T_stride
+ERR_APPEND_RANGE = 4      # a request would pass T_stride or P, or its partial last page is not resident
 ERR_APPEND_NO_BLOCK = 8   # a free list has fewer blocks than the pages to open
 ERR_DEMOTE_FULL = 16      # the latent free list cannot take the demoted blocks
 

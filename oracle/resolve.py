@@ -150,17 +150,3 @@ def resolve(topk: np.ndarray, state: ResidencyState) -> tuple[ResidencyState, Re
     res.err = err
     return st, res
 
-
-def apply_copies(result: ResolveResult, host_rows, host_scale, pool, row_scale) -> None:
-    """Perform the fault copies of ``result`` on numpy arrays, for every layer.
-
-    host_rows [L, N_host, 576], host_scale [L, N_host] or None,
-    pool [L, N_rows, 576], row_scale [L, N_rows] or None (modified in place).
-    """
-    for clist in result.copies:
-        if len(clist) == 0:
-            continue
-        src, dst = clist[:, 0], clist[:, 1]
-        pool[:, dst] = host_rows[:, src]
-        if row_scale is not None:
-            row_scale[:, dst] = host_scale[:, src]

@@ -64,8 +64,8 @@ def topk_sharded_row(scores_row: np.ndarray, n_visible: int, K: int, shard_len: 
     its own top-K (the rule of topk_row), and the K best of the union of those
     candidates are kept (same order and tie rule), in ascending token order.
 
-    Page "Un contexte d'un million sur huit H200", section "Les chiffres" (DCP:
-    the KV cache is split across GPUs by tokens).  Every token of the global
+    Page "vLLM sert GLM-5.3 en contexte 1M sur 16 H200", section "Le
+    mécanisme" (DCP: the KV cache is split across GPUs by tokens).  Every token of the global
     top-K is in its shard's top-K, so this equals topk_row; the function is the
     definition the sharded GPU path follows, and the tests pin the equality.
     """

@@ -6,6 +6,7 @@ request's tokens must read (the rows appended, in order): whatever the
 operations do with blocks, the logical cache may not change, no block may be
 lost or held twice, host copies equal the pool, and the tail stays resident.
 """
+import copy
 import json
 import os
 
@@ -71,6 +72,32 @@ def test_hand_traced_append_precopy_demote():
     assert err == 0 and st.free == d["free"] and st.bt.tolist() == d["bt"]
 
 
+def test_hand_traced_append_rejections():
+    """Each append rejection rule on its own, with a control that differs from
+    the rejected case only in the condition the rule tests."""
+    g = json.load(open(os.path.join(GOLD, "append_reject_tiny.json")))
+    P = g["P"]
+    for case in g["cases"]:
+        ini = dict(g["base"], **case["override"])
+        st = _state(2, g["T_stride"], 1, 2, 2, 8, 8, ini["ctx_len"], ini["bt"], ini["idx_bt"],
+                    ini["free"], ini["idx_free"], ini["free_capacity"])
+        before = (st.pool.copy(), st.idx_pool.copy(), st.idx_bt.copy(), list(st.free),
+                  list(st.idx_free))
+        rows = np.full((2, P, 1, 2), 9, np.uint8)
+        keys = np.full((2, P, 2), 7, np.uint8)
+        err = co.append_tokens(st, case["n_new"], rows, np.ones((2, P, 1), np.float32), keys,
+                               np.ones((2, P), np.float32))
+        assert err == case["err"], case["name"]
+        assert st.bt.tolist() == case["bt"], case["name"]
+        assert st.ctx_len.tolist() == case["ctx_len"], case["name"]
+        if err:
+            assert np.array_equal(st.pool, before[0]) and np.array_equal(st.idx_pool, before[1])
+            assert np.array_equal(st.idx_bt, before[2])
+            assert st.free == before[3] and st.idx_free == before[4], case["name"]
+        else:
+            assert not np.array_equal(st.pool, before[0]), case["name"]
+
+
 def _random_run(seed, steps=80):
     rng = np.random.default_rng(seed)
     B, T_stride, L, D, Dk, P = 3, 1024, 2, 3, 2, 8
@@ -100,10 +127,16 @@ def _random_run(seed, steps=80):
         snap = (st.bt.copy(), st.ctx_len.copy(), list(st.free), list(st.idx_free), st.host_bt.copy())
         if op == 0:
             n_new = rng.integers(0, P + 1, B)
+            over = rng.random() < 0.15
+            if over:
+                # one request asks for more tokens than a step accepts
+                n_new[int(rng.integers(0, B))] = P + 1
             rows = rng.integers(0, 255, (B, P, L, D)).astype(np.uint8)
             keys = rng.integers(0, 255, (B, P, Dk)).astype(np.uint8)
             err = co.append_tokens(st, n_new, rows, np.ones((B, P, L), np.float32), keys,
                                    np.ones((B, P), np.float32))
+            if over:
+                assert err & co.ERR_APPEND_RANGE
             if err:
                 assert np.array_equal(st.bt, snap[0]) and np.array_equal(st.ctx_len, snap[1])
                 assert st.free == snap[2] and st.idx_free == snap[3]
@@ -112,6 +145,7 @@ def _random_run(seed, steps=80):
                     ref[b].extend(rows[b, i].copy() for i in range(int(n_new[b])))
         elif op == 1:
             co.precopy_pages(st, int(rng.integers(1, 4)))
+            _partial_page_rejection(st, rng, P, L, D, Dk)
         else:
             err, plan = co.demote_pages(st, rng.integers(0, 4, B), tail)
             if err:
@@ -141,6 +175,30 @@ def _random_run(seed, steps=80):
                     h, s = int(st.host_bt[b, p]), int(st.bt[b, p]) * 64
                     assert np.array_equal(st.host_rows[:, h:h + 64], st.pool[:, s:s + 64])
     return st
+
+
+def _partial_page_rejection(st, rng, P, L, D, Dk):
+    """On a copy of the state, take away the block of one request's partly
+    filled last page (latent or indexer side): an append that would write into
+    it must be refused and change nothing."""
+    cand = [b for b in range(len(st.ctx_len)) if int(st.ctx_len[b]) % 64 != 0]
+    if not cand:
+        return
+    b = cand[int(rng.integers(0, len(cand)))]
+    c = copy.deepcopy(st)
+    page = int(c.ctx_len[b]) // 64
+    (c.bt if rng.random() < 0.5 else c.idx_bt)[b, page] = -1
+    snap = copy.deepcopy(c)
+    n_new = np.zeros(len(c.ctx_len), np.int64)
+    n_new[b] = int(rng.integers(1, P + 1))
+    err = co.append_tokens(c, n_new, np.zeros((len(n_new), P, L, D), np.uint8),
+                           np.ones((len(n_new), P, L), np.float32),
+                           np.zeros((len(n_new), P, Dk), np.uint8),
+                           np.ones((len(n_new), P), np.float32))
+    assert err & co.ERR_APPEND_RANGE
+    assert np.array_equal(c.bt, snap.bt) and np.array_equal(c.idx_bt, snap.idx_bt)
+    assert np.array_equal(c.ctx_len, snap.ctx_len) and np.array_equal(c.pool, snap.pool)
+    assert c.free == snap.free and c.idx_free == snap.idx_free
 
 
 @pytest.mark.parametrize("seed", range(6))
