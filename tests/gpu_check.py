@@ -158,8 +158,19 @@ def check_copies(wl, rr, pool, row_scale, max_per_request=None):
                     assert row_scale[l, pr] == wl.lat_scale[l, b, t // 64]
 
 
+def lse_bound(tol, ref_lse):
+    """Allowed |lse_gpu - lse_ref|.  e^d - 1 is the relative error of the
+    softmax normaliser.  The logits are exact products of bf16 queries and
+    bf16-exact rows summed in fp32 on the GPU, so lse does not see the bf16
+    rounding of the probabilities that sets the 2e-2 output budget of the fp8
+    path: the bound is min(tol, 1e-3) relative to max(1, |lse|), i.e. 1e-5
+    relative in fp32 and 1e-3 relative on the fp8 path."""
+    return min(tol, 1e-3) * np.maximum(1.0, np.abs(ref_lse))
+
+
 def check_attention(wl, q_layers, topk, out, lse, tol, pairs=None):
-    """Max relative error per output vector against the oracle over the same selection."""
+    """Max relative error per output vector against the oracle over the same
+    selection, and the log-sum-exp within lse_bound."""
     worst = 0.0
     for l in range(wl.L):
         ref_o, ref_l = o_attn.sparse_mla(q_layers[l], wl.q_dtype, wl.lat[l],
@@ -173,7 +184,8 @@ def check_attention(wl, q_layers, topk, out, lse, tol, pairs=None):
             fin = np.isfinite(ref_l[b, p])
             assert np.array_equal(fin, np.isfinite(lse[l, b, p]))
             if fin.any():
-                assert np.max(np.abs(lse[l, b, p][fin] - ref_l[b, p][fin])) <= max(tol, 1e-5) * 10
+                d = np.abs(lse[l, b, p][fin].astype(np.float64) - ref_l[b, p][fin])
+                assert np.all(d <= lse_bound(tol, ref_l[b, p][fin])), (l, b, p, float(d.max()))
     return worst
 
 

@@ -270,10 +270,14 @@ def test_pipelined_step_matches_single_stream():
     ref_pool = ds.pool.cpu().numpy()
     gc.check_resolve(wl, gc.oracle_state(wl), ref["topk"], ref)
     keys = ("scores", "topk", "row_ids", "counts", "out", "lse", "tok2slot", "slot2tok", "stamp")
+    q = wl.step_inputs(1)[1]
+    gc.check_attention(wl, q, ref["topk"], ref["out"], ref["lse"], 2e-2)
     for nchunks in (2, 3, 5):
         ds.restore(snap)
         ds.run_pipelined(nchunks)
         got = gc.gpu_outputs(ds)
+        gc.check_resolve(wl, gc.oracle_state(wl), got["topk"], got)
+        gc.check_attention(wl, q, got["topk"], got["out"], got["lse"], 2e-2)
         for k in keys:
             if k == "scores":
                 for b in range(wl.B):
@@ -302,6 +306,7 @@ def test_pipelined_step_matches_single_stream():
         g.replay()
         torch.cuda.synchronize()
         got = gc.gpu_outputs(ds)
+        gc.check_attention(wl, q, got["topk"], got["out"], got["lse"], 2e-2)
         for k in keys[1:]:
             assert np.array_equal(got[k], ref[k]), ("graph", rep, k)
 
@@ -339,6 +344,8 @@ def test_pipelined_chunks_of_eight_against_oracle():
     ds.run_pipelined(4)
     g1 = gc.gpu_outputs(ds)
     gc.check_resolve(wl, gc.oracle_state(wl), g1["topk"], g1)
+    q = wl.step_inputs(1)[1]
+    gc.check_attention(wl, q, g1["topk"], g1["out"], g1["lse"], 2e-2)
     assert np.all(g1["counts"][:, 3] == g1["counts"][:, 2])   # full buffers: every fault evicts
     ds.restore(snap)
     torch.cuda.synchronize()
@@ -437,8 +444,9 @@ def test_indexer_many_requests_long_tiles(B):
     one-position indexer: 256 requests take 128-page tiles, 64 take 64-page
     tiles, 12 take 8-page tiles (and 1024-token top-K filter chunks).  Ragged
     contexts (empty, one token, on and off the 512/4096/8192 boundaries); fused
-    and separate indexer calls give the same scores bit for bit; sampled scores
-    against the oracle; top-K exact."""
+    and separate indexer calls give the same scores bit for bit; every visible
+    score against the oracle; top-K exact on the GPU scores and within the
+    near-tie rule on the oracle's."""
     from decode_indexer_logits_amd import _lib
     from oracle import indexer as o_idx, topk as o_topk
     rng = np.random.default_rng(21 + B)
@@ -463,24 +471,31 @@ def test_indexer_many_requests_long_tiles(B):
     _lib.indexer_topk(batch, *args, s2, K, topk, ws)
     torch.cuda.synchronize()
     g1, g2, gt = s1.cpu().numpy(), s2.cpu().numpy(), topk.cpu().numpy()
-    worst = 0.0
+    S = o_idx.indexer_scores(x["q_idx"], "bf16", x["w"], x["idx_pool"], "e4m3", x["idx_scale"],
+                             x["idx_bt"], ctx, x["bias"], T_stride=Ts)
+    worst, swaps = 0.0, 0
     for b in range(B):
         n = int(ctx[b])
         assert np.array_equal(g1[b, 0, :n].view(np.uint32), g2[b, 0, :n].view(np.uint32)), b
         if n == 0:
             continue
-        toks = np.unique(np.concatenate([rng.integers(0, n, 24), [0, n - 1],
-                                         [t for t in (511, 512, 4095, 4096, 8191, 8192) if t < n]])
-                         .astype(np.int64))
-        ref = o_idx.indexer_scores_at(x["q_idx"], "bf16", x["w"], x["idx_pool"], "e4m3",
-                                      x["idx_scale"], x["idx_bt"], b, 0, toks, x["bias"])
-        err = float(np.max(np.abs(g2[b, 0, toks] - ref)) / max(np.max(np.abs(ref)), 1e-30))
+        ref = S[b, 0, :n]
+        err = float(np.max(np.abs(g2[b, 0, :n] - ref)) / max(np.max(np.abs(ref)), 1e-30))
         worst = max(worst, err)
         assert err <= gc.SCORE_RTOL, (b, err)
+        G = gt[b, 0][gt[b, 0] >= 0]
+        O = o_topk.topk_row(S[b, 0], n, K)
+        O = O[O >= 0]
+        assert len(G) == len(O) == min(n, K)
+        diff = np.setxor1d(G, O)
+        if len(diff):
+            sk = o_topk.kth_score(S[b, 0], n, K)
+            assert np.all(np.abs(S[b, 0, diff] - sk) <= gc.TOPK_TIE_REL * abs(sk)), b
+            swaps += len(diff)
     ref_t = o_topk.topk(g2.astype(np.float64), ctx, K)
     bad = np.argwhere(np.any(ref_t != gt, axis=2))
     assert len(bad) == 0, f"top-K rows {bad[:4].tolist()}"
-    _say(f"worst sampled score error {worst:.2e}")
+    _say(f"worst score error {worst:.2e}, near-tie swaps {swaps}")
 
 
 def test_resolve_merge_path_long_stride():
@@ -503,9 +518,10 @@ def test_resolve_merge_path_long_stride():
 
 @pytest.mark.parametrize("kv", ["e4m3", "f32"])
 def test_attention_layers_call_matches_per_layer_calls(kv):
-    """hs_sparse_mla_decode_layers over L layers against L calls of
-    hs_sparse_mla_decode: identical for L = 1, equal to fp32 summation order for
-    L = 3 (fewer slices per layer); both paths (bf16 x E4M3 and fp32)."""
+    """hs_sparse_mla_decode_layers over L layers against the oracle's attention
+    over the same rows, and against L calls of hs_sparse_mla_decode: identical
+    for L = 1, equal to fp32 summation order for L = 3 (fewer slices per
+    layer); both paths (bf16 x E4M3 and fp32)."""
     from decode_indexer_logits_amd import _lib
     rng = np.random.default_rng(71)
     B, P, K, Hq, L, n_rows = 3, 1, 1000, 16, 3, 4096
@@ -547,3 +563,19 @@ def test_attention_layers_call_matches_per_layer_calls(kv):
     err = ((outL - out1).abs().amax(dim=-1) / out1.abs().amax(dim=-1).clamp_min(1e-30)).max().item()
     assert err <= 1e-5, err
     assert torch.allclose(lseL, lse1, rtol=1e-6, atol=1e-6)
+    # the oracle over the same rows, from the same codes and scales
+    from oracle import attention as o_attn, numerics as o_num
+    tol = 2e-2 if kv == "e4m3" else 1e-5
+    qn = q.cpu().numpy()
+    qn = qn.view(np.uint16) if kv == "e4m3" else qn
+    pn, rsn = pool.cpu().numpy(), None if rs is None else rs.cpu().numpy()
+    oL, lL = outL.cpu().numpy(), lseL.cpu().numpy()
+    for l in range(L):
+        for b in range(B):
+            sel = rid[b][rid[b] >= 0]
+            x = o_num.to_f64(pn[l][sel], kv)
+            if rsn is not None:
+                x = x * rsn[l][sel].astype(np.float64)[:, None]
+            ro, rl = o_attn.attend(o_num.to_f64(qn[l, b, 0], qt), x, 1.0 / 24.0)
+            assert o_attn.max_rel_err(oL[l, b, 0], ro) <= tol, (kv, l, b)
+            assert np.all(np.abs(lL[l, b, 0] - rl) <= gc.lse_bound(tol, rl)), (kv, l, b)
