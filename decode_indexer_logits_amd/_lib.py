@@ -21,7 +21,8 @@ HS_OP_INDEXER, HS_OP_TOPK, HS_OP_RESOLVE, HS_OP_MLA, HS_OP_CACHE = 0, 1, 2, 3, 4
 DEVERR_VICTIMS, DEVERR_NO_HOST = 1, 2
 DEVERR_APPEND_RANGE, DEVERR_APPEND_NO_BLOCK, DEVERR_DEMOTE_FULL = 4, 8, 16
 
-EXPORTS = ["hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
+EXPORTS = ["hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk",
+           "hs_indexer_topk_noalloc", "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
            "hs_sparse_mla_decode", "hs_sparse_mla_decode_layers", "hs_mla_layers_workspace_bytes",
            "hs_topk_sharded", "hs_topk_sharded_workspace_bytes",
            "hs_append_tokens", "hs_precopy_pages", "hs_demote_pages",
@@ -76,6 +77,8 @@ def load() -> ctypes.CDLL:
     lib.hs_topk.argtypes = [P, c_int32, P, P, P, c_size_t, P]
     lib.hs_indexer_topk.argtypes = [P, c_int32, c_int32, c_int32, P, P, c_int32, P, P, P, P, P,
                                     c_int32, P, P, c_size_t, P]
+    lib.hs_indexer_topk_noalloc.argtypes = [P, c_int32, c_int32, c_int32, P, P, c_int32, P, P, P,
+                                            P, P, c_int32, P, P]
     lib.hs_resolve_rows.argtypes = [P, c_int32, P, P, P, P, P, P, c_size_t, P]
     lib.hs_resolve_tables.argtypes = [P, c_int32, P, P, P, P, P, P]
     lib.hs_copy_faults.argtypes = [P, c_int32, P, P, P, c_int32, P]
@@ -95,7 +98,8 @@ def load() -> ctypes.CDLL:
     lib.hs_demote_pages.argtypes = [P, P, P, c_int32, P, P, c_size_t, P]
     for f in ("hs_append_tokens", "hs_precopy_pages", "hs_demote_pages"):
         getattr(lib, f).restype = c_int32
-    for f in ("hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk", "hs_resolve_rows", "hs_resolve_tables",
+    for f in ("hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk",
+              "hs_indexer_topk_noalloc", "hs_resolve_rows", "hs_resolve_tables",
               "hs_copy_faults", "hs_sparse_mla_decode", "hs_host_device_ptr"):
         getattr(lib, f).restype = c_int32
     lib.hs_workspace_bytes.argtypes = [c_int32] * 6
@@ -169,6 +173,14 @@ def indexer_topk(batch: Batch, H: int, D: int, q_t: str, q_idx, w, k_t: str, idx
                                   _ptr(bias), _ptr(scores), K, _ptr(out), _ptr(ws),
                                   0 if ws is None else ws.numel() * ws.element_size(),
                                   _stream(stream)))
+
+
+def indexer_topk_noalloc(batch: Batch, H: int, D: int, q_t: str, q_idx, w, k_t: str, idx_pool,
+                         idx_scale, idx_bt, bias, scores, K: int, out, stream=None):
+    _check(load().hs_indexer_topk_noalloc(ctypes.byref(batch), H, D, DTYPES[q_t], _ptr(q_idx),
+                                          _ptr(w), DTYPES[k_t], _ptr(idx_pool), _ptr(idx_scale),
+                                          _ptr(idx_bt), _ptr(bias), _ptr(scores), K, _ptr(out),
+                                          _stream(stream)))
 
 
 def resolve_rows(batch: Batch, K: int, topk_t, res: Residency, row_ids, faults, counts,

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/hs.h"
 #include "hs_launch.h"
@@ -114,6 +115,57 @@ hs_status check_topk(const hs::BatchDims& d, int32_t K, int32_t* topk, void* ws,
   return HS_OK;
 }
 
+// Indexer with the first top-K radix pass in its epilogue, then the selection.
+// The workspace's histogram and counters are cleared by a kernel first.
+hs_status launch_indexer_topk(const hs::BatchDims& d, IdxPath path, int32_t H_idx, int32_t D_idx,
+                              const void* q_idx, const float* w, const void* idx_pool,
+                              const float* idx_scale, const int32_t* idx_bt, const float* bias,
+                              float* scores, int32_t K, int32_t* topk, void* ws, hipStream_t s) {
+  if (path == IdxPath::kF32) {
+    hipError_t e = launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt,
+                                  bias, scores, nullptr, s);
+    if (e != hipSuccess) return launched(e, "indexer");
+    return launched(hs::launch_topk(d, K, scores, topk, ws, s), "topk");
+  }
+  uint32_t* hist = nullptr;
+  hipError_t e = hs::launch_topk_zero(d, K, ws, &hist, s);
+  if (e == hipSuccess)
+    e = launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt, bias, scores,
+                       hist, s);
+  if (e == hipSuccess) e = hs::launch_topk_select(d, K, scores, topk, ws, s);
+  return launched(e, "indexer + top-K");
+}
+
+// Scratch of hs_indexer_topk_noalloc, for callers that cannot allocate: one
+// copy per GPU, created with the code object and held until the process ends.
+// Host code never uses the array's name as an address: static_scratch() looks
+// up this device's copy once and every launch takes that pointer.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hs_status static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HS_ERR_HIP, "device %d is beyond the %d the scratch table tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(HS_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,20 +214,33 @@ hs_status hs_indexer_topk(const hs_batch* batch, int32_t H_idx, int32_t D_idx, h
                                    idx_bt, scores, &path))
     return st;
   if (hs_status st = check_topk(d, K, topk, ws, ws_bytes)) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (path == IdxPath::kF32) {
-    hipError_t e = launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt,
-                                  bias, scores, nullptr, s);
-    if (e != hipSuccess) return launched(e, "indexer");
-    return launched(hs::launch_topk(d, K, scores, topk, ws, s), "topk");
-  }
-  uint32_t* hist = nullptr;
-  hipError_t e = hs::launch_topk_zero(d, K, ws, &hist, s);
-  if (e == hipSuccess)
-    e = launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt, bias, scores,
-                       hist, s);
-  if (e == hipSuccess) e = hs::launch_topk_select(d, K, scores, topk, ws, s);
-  return launched(e, "indexer + top-K");
+  return launch_indexer_topk(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt, bias,
+                             scores, K, topk, ws, static_cast<hipStream_t>(stream));
+}
+
+hs_status hs_indexer_topk_noalloc(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
+                                  hs_dtype q_t, const void* q_idx, const float* w, hs_dtype k_t,
+                                  const void* idx_pool, const float* idx_scale,
+                                  const int32_t* idx_bt, const float* bias, float* scores,
+                                  int32_t K, int32_t* topk, void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  IdxPath path;
+  if (hs_status st = check_indexer(d, H_idx, D_idx, q_t, q_idx, w, k_t, idx_pool, idx_scale,
+                                   idx_bt, scores, &path))
+    return st;
+  if (!topk) return fail(HS_ERR_NULL, "top-K: topk is required");
+  if (K < 1 || K > 8192) return fail(HS_ERR_SHAPE, "K=%d out of [1, 8192]", K);
+  const size_t need = hs::topk_workspace_bytes(d.B, d.P, d.T_stride, K);
+  if (need > kStaticScratchBytes)
+    return fail(HS_ERR_WORKSPACE,
+                "hs_indexer_topk_noalloc: these sizes need %zu bytes of scratch; the library's "
+                "static scratch holds %zu (use hs_indexer_topk with a workspace)",
+                need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if (hs_status st = static_scratch(&ws)) return st;
+  return launch_indexer_topk(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt, bias,
+                             scores, K, topk, ws, static_cast<hipStream_t>(stream));
 }
 
 size_t hs_topk_sharded_workspace_bytes(int32_t B, int32_t T_stride, int32_t K, int32_t S) {

@@ -186,6 +186,25 @@ hs_status hs_indexer_topk(const hs_batch* batch, int32_t H_idx, int32_t D_idx, h
                           float* scores, int32_t K, int32_t* topk, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* hs_indexer_topk for callers that cannot allocate device memory: code under
+ * HIP graph capture that may not call hipMalloc, tight serving loops, and
+ * harnesses that forbid allocation.  Same arguments and results as
+ * hs_indexer_topk without ws/ws_bytes: the workspace is a static device
+ * array inside the library, 64 MiB per GPU, created when the library's code
+ * object is loaded on that GPU and held until the process ends.  The call
+ * allocates nothing; it clears the part of the array that must start at zero
+ * with a kernel on `stream`.  Sizes whose hs_workspace_bytes(HS_OP_TOPK, ...)
+ * exceed 64 MiB are rejected with HS_ERR_WORKSPACE (B*P*T_stride up to about
+ * 8.3 million tokens: the 128K batch of 32 and the 1M batch of 4 fit).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialized by the
+ * caller. */
+hs_status hs_indexer_topk_noalloc(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
+                                  hs_dtype q_t, const void* q_idx, const float* w, hs_dtype k_t,
+                                  const void* idx_pool, const float* idx_scale,
+                                  const int32_t* idx_bt, const float* bias, float* scores,
+                                  int32_t K, int32_t* topk, void* stream);
+
 /* Residency state of a batch: one shared paged pool of latent rows on the GPU,
  * per-request hot buffers made of ordinary pool blocks (page "Un contexte d'un
  * million sur huit H200", section "Les trois états de résidence", last

@@ -78,6 +78,11 @@ def test_host_validation_rejects_bad_arguments_without_launching():
     assert "scores" in _lib.last_error()
     bad = _lib.Batch(2, 5, 1024, 16, 16)
     assert lib.hs_topk(ctypes.byref(bad), 8, fake, fake, fake, 1 << 30, None) == 2
+    # the allocation-free variant refuses sizes beyond its static scratch
+    big = _lib.Batch(64, 1, 1 << 20, (1 << 20) // 64, 16)
+    assert lib.hs_indexer_topk_noalloc(ctypes.byref(big), 64, 128, 1, fake, fake, 2, fake, fake,
+                                       fake, None, fake, 2048, fake, None) == 5
+    assert "static scratch" in _lib.last_error()
     bad = _lib.Batch(2, 1, 1000, 15, 16)
     assert lib.hs_topk(ctypes.byref(bad), 8, fake, fake, fake, 1 << 30, None) == 2
     # indexer dtype and shape checks
