@@ -32,11 +32,12 @@ HBM_PEAK_GBS = 8000.0
 HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 KV_ROW = 576
 
-# HBM bytes per launch of hs_indexer_scores on the 128K mixed workload, from two
-# rocprofv3 --pmc runs (FETCH_SIZE x 2 + WRITE_SIZE x 1, factors calibrated with a
-# 512 MiB read and a 512 MiB fill in the same runs; profiles/indexer_mixed_128k_pmc.txt).
-# Reported only while the kernel's sources are the ones the counters were taken on.
-INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.04e6,
+# HBM bytes per launch of the in-step indexer instance (with the top-K histogram epilogue)
+# on the 128K mixed workload, from two rocprofv3 --pmc runs (FETCH_SIZE x 2 + WRITE_SIZE x 1,
+# factors calibrated with a 512 MiB read and a 512 MiB fill in the same runs;
+# profiles/hbm_counters_mixed_128k.txt).  Reported only while the kernel's sources are the
+# ones the counters were taken on.
+INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.11e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
                    "sha256": "4637495306c4878956527295468e9452d87aa15c85adf6fb860c3f408f624249"}
@@ -55,9 +56,13 @@ def _indexer_traffic(workload: str, indexer_q: str):
     return INDEXER_TRAFFIC["bytes"] if h.hexdigest() == INDEXER_TRAFFIC["sha256"] else None
 
 
-def _algorithmic_bytes(wl, counts):
+def _algorithmic_bytes(wl, counts, mla_ws_bytes: int = 0):
     """Bytes the method itself must move per step, by stage: what each kernel has to read
-    or write at least once, whatever its tiling."""
+    or write at least once, whatever its tiling: keys, scales, tables, bias, queries, the
+    selected rows, row ids, outputs and the residency tables.  The scores are an
+    intermediate between the indexer and the top-K: their write and read-back are
+    implementation traffic, reported apart with the attention's split partials and never
+    counted as useful bytes."""
     B, P, K, L = wl.B, wl.P, wl.K, wl.L
     tok = int(wl.ctx_len.sum())
     nblk = sum(-(-int(t) // 64) for t in wl.ctx_len)
@@ -67,7 +72,6 @@ def _algorithmic_bytes(wl, counts):
         "block_table": nblk * 4,
         "bias": (tok * 4) if wl.bias is not None else 0,
         "queries_weights": B * P * wl.H_idx * (wl.D_idx * 2 + 4),
-        "scores_out": P * tok * 4,
     }
     res_, hit, flt, ev = (int(x) for x in counts.sum(axis=0))
     u = res_ + hit + flt
@@ -84,16 +88,20 @@ def _algorithmic_bytes(wl, counts):
         "q": L * B * P * wl.Hq * KV_ROW * 2,
         "out": L * B * P * wl.Hq * (512 + 1) * 4,
     }
-    topk = {"scores_in": P * tok * 4, "topk_out": B * P * K * 4}
+    topk = {"topk_out": B * P * K * 4}
+    implementation = {"scores_written": P * tok * 4, "scores_read": P * tok * 4,
+                      "attention_partials_written_and_read": 2 * mla_ws_bytes}
     # fault copies: rows over the host link, written to the pool with their scales
     copy = {"host_rows": flt * L * KV_ROW, "pool_rows_written": flt * L * (KV_ROW + 4),
             "scales_and_tables": flt * (8 + L * 4 + 16)}
     return {"indexer": idx, "topk": topk, "resolve": resolve, "attention": attn,
-            "fault_copy": copy, "host_link": flt * L * KV_ROW}
+            "fault_copy": copy, "host_link": flt * L * KV_ROW, "implementation": implementation}
 
 
-def _time_launches(fn, n, torch, restore=None, flush=None):
-    """Average duration (ms) of fn() over n launches, HIP events on the current stream."""
+def _time_launches(fn, n, torch, restore=None, flush=None, after=None):
+    """Average duration (ms) of fn() over n launches, HIP events on the current stream
+    (the stream every call launches on); restore/flush run before the start event and
+    `after` after the end event, untimed."""
     st = torch.cuda.current_stream()
     ts = []
     for _ in range(n):
@@ -106,46 +114,90 @@ def _time_launches(fn, n, torch, restore=None, flush=None):
         a.record(st)
         fn()
         b.record(st)
+        if after:
+            after()
         ts.append((a, b))
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in ts]
     return sum(ms) / len(ms), ms
 
 
-def cpu_baseline(wl, n_req: int, indexer_q: str = "bf16"):
-    """Time the oracle's full decode step on a sample of the batch (host cores)."""
+def _request_slice(wl, n: int):
+    """The first n requests of a workload, as a workload of their own (array views)."""
+    import dataclasses
+    if n >= wl.B:
+        return wl
+    sl = slice(0, n)
+    q = [(qi[sl], qq[:, sl]) for qi, qq in wl._step_q]
+    return dataclasses.replace(
+        wl, B=n, ctx_len=wl.ctx_len[sl], w=wl.w[sl], idx_bt=wl.idx_bt[sl],
+        bias=None if wl.bias is None else wl.bias[sl], lat=wl.lat[:, sl],
+        lat_scale=None if wl.lat_scale is None else wl.lat_scale[:, sl], bt=wl.bt[sl],
+        hot_blocks=wl.hot_blocks[sl], tok2slot=wl.tok2slot[sl], slot2tok=wl.slot2tok[sl],
+        stamp=wl.stamp[sl], _step_q=q)
+
+
+def _machine() -> dict:
+    """CPU model, the cores this process may run on, and numpy's BLAS."""
     import numpy as np
-    from oracle import indexer as oi, topk as ot, resolve as orr, attention as oa, quant as oq
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{blas.get('name')} {blas.get('version')}"
     except Exception:
-        cores = len(os.sched_getaffinity(0))
-    q_idx, q = wl.step_inputs(1)
-    n_req = min(n_req, wl.B)
-    sel_b = list(range(n_req))
-    t0 = time.perf_counter()
-    qi, qt, w = q_idx[sel_b], wl.q_dtype, wl.w[sel_b]
-    if indexer_q == "e4m3":
-        qi, w, _ = oq.quantize_queries(qi, w)
-        qt = "e4m3"
-    S = oi.indexer_scores(qi, qt, w, wl.idx_pool, wl.k_dtype,
-                          wl.idx_scale, wl.idx_bt[sel_b], wl.ctx_len[sel_b],
-                          None if wl.bias is None else wl.bias[sel_b], T_stride=wl.T_stride)
-    tk = ot.topk(S, wl.ctx_len[sel_b], wl.K)
-    st = orr.ResidencyState(wl.bt[sel_b], wl.hot_blocks[sel_b], wl.tok2slot[sel_b],
-                            wl.slot2tok[sel_b], wl.stamp[sel_b], wl.host_bt[sel_b], wl.step)
-    _, rr = orr.resolve(tk, st)
-    for l in range(wl.L):
-        oa.sparse_mla(q[l][sel_b], wl.q_dtype, wl.lat[l][sel_b],
-                      None if wl.lat_scale is None else wl.lat_scale[l][sel_b], wl.kv_dtype,
-                      tk, wl.sm_scale)
-    dt = time.perf_counter() - t0
-    per_step = dt * wl.B / n_req
+        blas = "unknown"
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas}
+
+
+def cpu_baseline(wl, n_req: int, indexer_q: str = "bf16", runs: int = 3):
+    """The oracle's composed decode step (oracle.step.decode_step: indexer, top-K,
+    resolve, attention of every layer) on the first n_req requests, on the host cores,
+    with numpy's BLAS limited to the cores this process may use; the median of `runs`
+    runs, scaled to the batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import quant as oq, resolve as orr, step as ostep
+    mach = _machine()
+    cores = mach["affinity_cores"]
+    sub = _request_slice(wl, min(n_req, wl.B))
+    q_idx, q = sub.step_inputs(1)
+    times = []
+    with threadpool_limits(limits=cores, user_api="blas"):
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            w = sub
+            qi = q_idx
+            if indexer_q == "e4m3":
+                import dataclasses
+                qi, w_sc, _ = oq.quantize_queries(q_idx, sub.w)
+                w = dataclasses.replace(sub, w=w_sc, q_dtype="e4m3")
+            st = orr.ResidencyState(sub.bt, sub.hot_blocks, sub.tok2slot, sub.slot2tok, sub.stamp,
+                                    sub.host_bt, sub.step)
+            if indexer_q == "e4m3":
+                # the E4M3 codes feed the indexer; the attention keeps the bf16 queries
+                from oracle import indexer as oi
+                S = oi.indexer_scores(qi, "e4m3", w.w, sub.idx_pool, sub.k_dtype, sub.idx_scale,
+                                      sub.idx_bt, sub.ctx_len, sub.bias, T_stride=sub.T_stride)
+                ostep.decode_step(sub, st, q_idx, q, scores=S)
+            else:
+                ostep.decode_step(sub, st, qi, q)
+            times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
+    per_step = dt * wl.B / sub.B
     return {"value": 1.0 / per_step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"float64 numpy oracle, full step (indexer, top-K, resolve, attention) "
-                      f"for {n_req} of {wl.B} requests in {dt:.1f} s, scaled to the batch",
-            "seconds": dt}
+            "sample": f"float64 numpy oracle (oracle.step.decode_step: indexer, top-K, resolve, "
+                      f"attention) on {sub.B} of {wl.B} requests, median of {runs} runs "
+                      f"({', '.join(f'{x:.2f}' for x in times)} s), scaled to the batch",
+            "seconds": dt, "label": f"float64 numpy oracle on {cores} cores -- a reported "
+                                    "baseline, not the target", **mach}
 
 
 def cache_ops_bench(torch, reps: int = 5) -> dict:
@@ -485,9 +537,15 @@ def main():
     if e4m3:
         stage_ms["quantize"], _ = _time_launches(ds.run_quantize, a.kernel_reps, torch, None,
                                                  flush)
-    # the indexer kernel alone (E4M3 codes of the last quantization reused)
-    stage_ms["indexer"], _ = _time_launches(lambda: ds.run_indexer(quantize=False),
-                                            a.kernel_reps, torch, None, flush)
+    # the indexer as the step runs it: the first half of the fused indexer + top-K
+    # (histogram epilogue), its selection half run after the end event; E4M3 codes of
+    # the last quantization reused
+    stage_ms["indexer"], _ = _time_launches(lambda: ds.run_indexer_topk_scores(quantize=False),
+                                            a.kernel_reps, torch, None, flush,
+                                            after=ds.run_indexer_topk_select)
+    # hs_indexer_scores alone (no histogram epilogue)
+    stage_ms["indexer_standalone"], _ = _time_launches(lambda: ds.run_indexer(quantize=False),
+                                                       a.kernel_reps, torch, None, flush)
     stage_ms["topk"], _ = _time_launches(ds.run_topk, a.kernel_reps, torch, None, flush)
     stage_ms["indexer_topk"], _ = _time_launches(ds.run_indexer_topk, a.kernel_reps, torch, None,
                                                  flush)
@@ -513,6 +571,33 @@ def main():
     stage_ms["attention"], _ = _time_launches(
         (lambda: ds.run_attention_layers()) if wl.L > 1 else (lambda: ds.run_attention(0)),
         a.kernel_reps, torch, None, flush)
+    # the HBM phase as the step runs it: one captured graph of every kernel of the step
+    # but the fault copies (indexer + top-K, resolve tables, attention), timed per replay
+    # from the restored state with the MALL flushed
+    def phase_eager():
+        ds.run_indexer_topk()
+        ds.run_resolve_tables()
+        if wl.L > 1:
+            ds.run_attention_layers()
+        else:
+            ds.run_attention(0)
+    if a.no_graph:
+        phase_fn = phase_eager
+    else:
+        pg = torch.cuda.CUDAGraph()
+        ps = torch.cuda.Stream()
+        ps.wait_stream(torch.cuda.current_stream())
+        restore()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(ps):
+            with torch.cuda.graph(pg, stream=ps):
+                phase_eager()
+        torch.cuda.synchronize()
+        phase_fn = pg.replay
+    _, ph_ms = _time_launches(phase_fn, max(a.steps, 5), torch, restore, flush)
+    stage_ms["hbm_phase_graph"] = sorted(ph_ms)[len(ph_ms) // 2]
+    restore()
+    torch.cuda.synchronize()
     log(f"[bench] stage ms {json.dumps({k: round(v, 4) for k, v in stage_ms.items()})}")
     ceil = ceilings(torch, ds, wl)
     if "key_pages_us" in ceil:
@@ -523,14 +608,18 @@ def main():
     if wl.steps > 1 and a.seq_repeats > 0:
         seq = sequence_bench(ds, wl, torch, step_fn, flush, snap, a.seq_repeats, a.append)
         log(f"[bench] sequence {json.dumps(seq)}")
-    alg = _algorithmic_bytes(wl, counts)
+    mla_ws = 0 if ds.ws_mla is None else ds.ws_mla.numel()
+    alg = _algorithmic_bytes(wl, counts, mla_ws)
     idx_bytes = sum(alg["indexer"].values())
     hbm_phase_bytes = (idx_bytes + sum(alg["topk"].values()) + sum(alg["resolve"].values())
                        + sum(alg["attention"].values()))
+    impl_bytes = sum(alg["implementation"].values())
     step_s = med / 1e3
     idx_gbs = idx_bytes / (stage_ms["indexer"] / 1e3) / 1e9
-    hbm_phase_s = (stage_ms["indexer_topk"] + stage_ms["resolve_tables"]
-                   + stage_ms["attention"]) / 1e3
+    idx_sa_gbs = idx_bytes / (stage_ms["indexer_standalone"] / 1e3) / 1e9
+    hbm_phase_s = stage_ms["hbm_phase_graph"] / 1e3
+    hbm_phase_eager_s = (stage_ms["indexer_topk"] + stage_ms["resolve_tables"]
+                         + stage_ms["attention"]) / 1e3
     link_gbs = alg["host_link"] / (stage_ms["fault_copy"] / 1e3) / 1e9
     traffic = _indexer_traffic(wl.name, ds.indexer_q)
     p10, p90 = ms_sorted[len(ms) // 10], ms_sorted[min(len(ms) - 1, (len(ms) * 9) // 10)]
@@ -562,20 +651,36 @@ def main():
                    "graph": not a.no_graph, "pipeline_chunks": a.chunks,
                    "pipeline_copy_workgroups": a.copy_wgs if a.chunks > 1 else None},
         "roofline": {"bound": "hbm",
-                     "kernel": "indexer_e4m3_kernel" if e4m3 else "indexer_bf16_e4m3_kernel",
+                     "kernel": ("indexer_e4m3_kernel" if e4m3 else "indexer_bf16_e4m3_kernel")
+                               + " (in-step instance with the top-K histogram epilogue)",
                      "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE)",
-                     "algorithmic_bytes": idx_bytes, "avg_ms": round(stage_ms["indexer"], 4)},
+                     "algorithmic_bytes": idx_bytes,
+                     "algorithmic_note": "keys, key scales, block table, bias, queries and head "
+                                         "weights; the score writes are implementation traffic",
+                     "avg_ms": round(stage_ms["indexer"], 4),
+                     "standalone_avg_ms": round(stage_ms["indexer_standalone"], 4),
+                     "standalone_frac": round(idx_sa_gbs / HBM_PEAK_GBS, 4)},
         "step_bandwidth": {
             "whole_step_GBs": round(hbm_phase_bytes / step_s / 1e9, 1),
             "whole_step_frac": round(hbm_phase_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
             "hbm_phase_GBs": round(hbm_phase_bytes / hbm_phase_s / 1e9, 1),
             "hbm_phase_frac": round(hbm_phase_bytes / hbm_phase_s / 1e9 / HBM_PEAK_GBS, 4),
-            "hbm_phase_note": "algorithmic bytes of indexer+top-K+resolve tables+attention over "
-                              "the sum of their eager kernel times (fault copies excluded: "
-                              "they are bound by the host link)",
+            "hbm_phase_ms": round(stage_ms["hbm_phase_graph"], 4),
+            "hbm_phase_note": "the target's figure: algorithmic bytes of indexer, top-K, "
+                              "resolve tables and attention over the median time of one "
+                              "captured graph of exactly those kernels (the step without its "
+                              "host-link-bound fault copies), state restored and MALL flushed "
+                              "before each replay",
+            "hbm_phase_frac_eager_sum": round(hbm_phase_bytes / hbm_phase_eager_s / 1e9
+                                              / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": hbm_phase_bytes,
+            "algorithmic_bytes_by_stage": {k: sum(alg[k].values()) for k in
+                                           ("indexer", "topk", "resolve", "attention")},
+            "implementation_bytes": alg["implementation"],
+            "implementation_note": "score round trip and attention split partials: moved by "
+                                   "this implementation, not counted as useful bytes",
             "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         },
         "host_link": {"bound": "pcie", "kernel": "fault_copy", "achieved": round(link_gbs, 2),

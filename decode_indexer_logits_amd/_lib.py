@@ -22,7 +22,8 @@ DEVERR_VICTIMS, DEVERR_NO_HOST = 1, 2
 DEVERR_APPEND_RANGE, DEVERR_APPEND_NO_BLOCK, DEVERR_DEMOTE_FULL = 4, 8, 16
 
 EXPORTS = ["hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk",
-           "hs_indexer_topk_noalloc", "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
+           "hs_indexer_topk_noalloc", "hs_indexer_topk_scores", "hs_indexer_topk_select",
+           "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
            "hs_sparse_mla_decode", "hs_sparse_mla_decode_layers", "hs_mla_layers_workspace_bytes",
            "hs_topk_sharded", "hs_topk_sharded_workspace_bytes",
            "hs_append_tokens", "hs_precopy_pages", "hs_demote_pages",
@@ -79,6 +80,9 @@ def load() -> ctypes.CDLL:
                                     c_int32, P, P, c_size_t, P]
     lib.hs_indexer_topk_noalloc.argtypes = [P, c_int32, c_int32, c_int32, P, P, c_int32, P, P, P,
                                             P, P, c_int32, P, P]
+    lib.hs_indexer_topk_scores.argtypes = [P, c_int32, c_int32, c_int32, P, P, c_int32, P, P, P,
+                                           P, P, c_int32, P, c_size_t, P]
+    lib.hs_indexer_topk_select.argtypes = [P, c_int32, c_int32, P, P, P, c_size_t, P]
     lib.hs_resolve_rows.argtypes = [P, c_int32, P, P, P, P, P, P, c_size_t, P]
     lib.hs_resolve_tables.argtypes = [P, c_int32, P, P, P, P, P, P]
     lib.hs_copy_faults.argtypes = [P, c_int32, P, P, P, c_int32, P]
@@ -99,7 +103,8 @@ def load() -> ctypes.CDLL:
     for f in ("hs_append_tokens", "hs_precopy_pages", "hs_demote_pages"):
         getattr(lib, f).restype = c_int32
     for f in ("hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk",
-              "hs_indexer_topk_noalloc", "hs_resolve_rows", "hs_resolve_tables",
+              "hs_indexer_topk_noalloc", "hs_indexer_topk_scores", "hs_indexer_topk_select",
+           "hs_resolve_rows", "hs_resolve_tables",
               "hs_copy_faults", "hs_sparse_mla_decode", "hs_host_device_ptr"):
         getattr(lib, f).restype = c_int32
     lib.hs_workspace_bytes.argtypes = [c_int32] * 6
@@ -146,7 +151,10 @@ def host_device_ptr(pinned) -> int:
 
 
 def make_batch(B: int, P: int, T_stride: int, ctx_len) -> Batch:
-    return Batch(B, P, T_stride, T_stride // 64, _ptr(ctx_len))
+    """The batch struct; it keeps a reference to ctx_len, whose address it holds."""
+    b = Batch(B, P, T_stride, T_stride // 64, _ptr(ctx_len))
+    b._ctx_len_ref = ctx_len
+    return b
 
 
 def indexer_scores(batch: Batch, H: int, D: int, q_t: str, q_idx, w, k_t: str, idx_pool,
@@ -173,6 +181,22 @@ def indexer_topk(batch: Batch, H: int, D: int, q_t: str, q_idx, w, k_t: str, idx
                                   _ptr(bias), _ptr(scores), K, _ptr(out), _ptr(ws),
                                   0 if ws is None else ws.numel() * ws.element_size(),
                                   _stream(stream)))
+
+
+def indexer_topk_scores(batch: Batch, H: int, D: int, q_t: str, q_idx, w, k_t: str, idx_pool,
+                        idx_scale, idx_bt, bias, scores, K: int, ws, stream=None):
+    _check(load().hs_indexer_topk_scores(ctypes.byref(batch), H, D, DTYPES[q_t], _ptr(q_idx),
+                                         _ptr(w), DTYPES[k_t], _ptr(idx_pool), _ptr(idx_scale),
+                                         _ptr(idx_bt), _ptr(bias), _ptr(scores), K, _ptr(ws),
+                                         0 if ws is None else ws.numel() * ws.element_size(),
+                                         _stream(stream)))
+
+
+def indexer_topk_select(batch: Batch, q_t: str, K: int, scores, out, ws, stream=None):
+    _check(load().hs_indexer_topk_select(ctypes.byref(batch), DTYPES[q_t], K, _ptr(scores),
+                                         _ptr(out), _ptr(ws),
+                                         0 if ws is None else ws.numel() * ws.element_size(),
+                                         _stream(stream)))
 
 
 def indexer_topk_noalloc(batch: Batch, H: int, D: int, q_t: str, q_idx, w, k_t: str, idx_pool,

@@ -115,24 +115,46 @@ hs_status check_topk(const hs::BatchDims& d, int32_t K, int32_t* topk, void* ws,
   return HS_OK;
 }
 
-// Indexer with the first top-K radix pass in its epilogue, then the selection.
-// The workspace's histogram and counters are cleared by a kernel first.
+// First half of the fused indexer + top-K: the indexer, with the first top-K
+// radix pass (every row's histogram) added into the workspace in its
+// epilogue.  The histogram and counter area must be zero on entry (the second
+// half leaves it so); `clear` zeroes it first with a kernel, for a workspace
+// in an unknown state.  The fp32 indexer has no fused histogram.
+hipError_t launch_indexer_topk_scores(const hs::BatchDims& d, IdxPath path, int32_t H_idx,
+                                      int32_t D_idx, const void* q_idx, const float* w,
+                                      const void* idx_pool, const float* idx_scale,
+                                      const int32_t* idx_bt, const float* bias, float* scores,
+                                      int32_t K, void* ws, bool clear, hipStream_t s) {
+  if (path == IdxPath::kF32)
+    return launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt, bias,
+                          scores, nullptr, s);
+  uint32_t* hist = hs::topk_histograms(ws);
+  if (clear) {
+    hipError_t e = hs::launch_topk_zero(d, K, ws, &hist, s);
+    if (e != hipSuccess) return e;
+  }
+  return launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt, bias,
+                        scores, hist, s);
+}
+
+// Second half: the rest of the selection (after the fp32 indexer, the whole
+// of hs_topk, histogram pass included).  Leaves the histogram and counter
+// area zero.
+hipError_t launch_indexer_topk_select(const hs::BatchDims& d, bool fused_hist, const float* scores,
+                                      int32_t K, int32_t* topk, void* ws, hipStream_t s) {
+  if (!fused_hist) return hs::launch_topk(d, K, scores, topk, ws, s);
+  return hs::launch_topk_select(d, K, scores, topk, ws, s);
+}
+
 hs_status launch_indexer_topk(const hs::BatchDims& d, IdxPath path, int32_t H_idx, int32_t D_idx,
                               const void* q_idx, const float* w, const void* idx_pool,
                               const float* idx_scale, const int32_t* idx_bt, const float* bias,
-                              float* scores, int32_t K, int32_t* topk, void* ws, hipStream_t s) {
-  if (path == IdxPath::kF32) {
-    hipError_t e = launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt,
-                                  bias, scores, nullptr, s);
-    if (e != hipSuccess) return launched(e, "indexer");
-    return launched(hs::launch_topk(d, K, scores, topk, ws, s), "topk");
-  }
-  uint32_t* hist = nullptr;
-  hipError_t e = hs::launch_topk_zero(d, K, ws, &hist, s);
+                              float* scores, int32_t K, int32_t* topk, void* ws, bool clear,
+                              hipStream_t s) {
+  hipError_t e = launch_indexer_topk_scores(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale,
+                                            idx_bt, bias, scores, K, ws, clear, s);
   if (e == hipSuccess)
-    e = launch_indexer(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt, bias, scores,
-                       hist, s);
-  if (e == hipSuccess) e = hs::launch_topk_select(d, K, scores, topk, ws, s);
+    e = launch_indexer_topk_select(d, path != IdxPath::kF32, scores, K, topk, ws, s);
   return launched(e, "indexer + top-K");
 }
 
@@ -215,7 +237,42 @@ hs_status hs_indexer_topk(const hs_batch* batch, int32_t H_idx, int32_t D_idx, h
     return st;
   if (hs_status st = check_topk(d, K, topk, ws, ws_bytes)) return st;
   return launch_indexer_topk(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt, bias,
-                             scores, K, topk, ws, static_cast<hipStream_t>(stream));
+                             scores, K, topk, ws, false, static_cast<hipStream_t>(stream));
+}
+
+hs_status hs_indexer_topk_scores(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
+                                 hs_dtype q_t, const void* q_idx, const float* w, hs_dtype k_t,
+                                 const void* idx_pool, const float* idx_scale,
+                                 const int32_t* idx_bt, const float* bias, float* scores,
+                                 int32_t K, void* ws, size_t ws_bytes, void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  IdxPath path;
+  if (hs_status st = check_indexer(d, H_idx, D_idx, q_t, q_idx, w, k_t, idx_pool, idx_scale,
+                                   idx_bt, scores, &path))
+    return st;
+  int32_t unused_topk = 0;
+  if (hs_status st = check_topk(d, K, &unused_topk, ws, ws_bytes)) return st;
+  return launched(launch_indexer_topk_scores(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale,
+                                             idx_bt, bias, scores, K, ws, false,
+                                             static_cast<hipStream_t>(stream)),
+                  "indexer (fused top-K histogram)");
+}
+
+hs_status hs_indexer_topk_select(const hs_batch* batch, hs_dtype q_t, int32_t K,
+                                 const float* scores, int32_t* topk, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!scores) return fail(HS_ERR_NULL, "hs_indexer_topk_select: scores is required");
+  if (!aligned16(scores))
+    return fail(HS_ERR_ALIGN, "hs_indexer_topk_select: scores need 16-byte alignment");
+  if (q_t != HS_F32 && q_t != HS_BF16 && q_t != HS_E4M3)
+    return fail(HS_ERR_DTYPE, "hs_indexer_topk_select: q_t=%d is not a query type", (int)q_t);
+  if (hs_status st = check_topk(d, K, topk, ws, ws_bytes)) return st;
+  return launched(launch_indexer_topk_select(d, q_t != HS_F32, scores, K, topk, ws,
+                                             static_cast<hipStream_t>(stream)),
+                  "top-K selection");
 }
 
 hs_status hs_indexer_topk_noalloc(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
@@ -240,7 +297,7 @@ hs_status hs_indexer_topk_noalloc(const hs_batch* batch, int32_t H_idx, int32_t 
   void* ws = nullptr;
   if (hs_status st = static_scratch(&ws)) return st;
   return launch_indexer_topk(d, path, H_idx, D_idx, q_idx, w, idx_pool, idx_scale, idx_bt, bias,
-                             scores, K, topk, ws, static_cast<hipStream_t>(stream));
+                             scores, K, topk, ws, true, static_cast<hipStream_t>(stream));
 }
 
 size_t hs_topk_sharded_workspace_bytes(int32_t B, int32_t T_stride, int32_t K, int32_t S) {

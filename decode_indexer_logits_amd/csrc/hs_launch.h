@@ -37,8 +37,11 @@ hipError_t launch_topk(const BatchDims& d, int K, const float* scores, int32_t* 
 size_t topk_sharded_workspace_bytes(int B, int T_stride, int K, int S);
 hipError_t launch_topk_sharded(const BatchDims& d, int K, int S, const float* scores,
                                int32_t* topk, void* ws, hipStream_t s);
-// The pieces of the fused indexer + top-K: zero the workspace counters (and
-// return the histogram the indexer fills), then select from that histogram.
+// The pieces of the fused indexer + top-K: the histogram area the indexer
+// fills (at the start of the workspace), a kernel that zeroes it with the
+// counters (the selection leaves both zero, so only a workspace in an unknown
+// state needs it), and the selection from that histogram.
+uint32_t* topk_histograms(void* ws);
 hipError_t launch_topk_zero(const BatchDims& d, int K, void* ws, uint32_t** hist, hipStream_t s);
 hipError_t launch_topk_select(const BatchDims& d, int K, const float* scores, int32_t* topk,
                               void* ws, hipStream_t s);

@@ -6,7 +6,10 @@
 // Scores map to order-preserving uint32 keys.  A row (one request position,
 // up to 2^24 tokens) is spread over many workgroups so that both few long rows
 // and many short ones fill the chip:
-//   1. zero       per-row histogram and counters
+//   1. zero       per-row histogram and counters (hs_topk only: the finalize
+//                 pass below returns every word of the workspace the call
+//                 wrote to zero, so hs_indexer_topk, whose workspace is zeroed
+//                 once by its owner, needs no clearing launch)
 //   2. histogram  of the top 11 key bits, per 8192-token chunk: LDS counts,
 //                 then one global atomic per non-empty bin (the fused path of
 //                 hs_indexer_topk builds it in the indexer's epilogue instead)
@@ -267,7 +270,15 @@ __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __r
     const int t = base + (u * kScanNT + tid) * 4;
     if (t < n) v[u] = *reinterpret_cast<const float4*>(row + t);
   }
-  if (wid == 0) wave_find_bin_top(ws.hist + (size_t)r * kBins1, (uint32_t)K, &s_b1, &s_above);
+  if (wid == 0) {
+    // defined values if the histogram holds fewer than K keys (it cannot, unless
+    // the workspace was not zero on entry)
+    if (lane == 0) {
+      s_b1 = 0;
+      s_above = 0;
+    }
+    wave_find_bin_top(ws.hist + (size_t)r * kBins1, (uint32_t)K, &s_b1, &s_above);
+  }
   __syncthreads();
   const uint32_t b1 = (uint32_t)s_b1;
   if (blockIdx.x == 0 && tid == 0) {
@@ -319,11 +330,16 @@ __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __r
       if (t >= n) continue;
       const uint32_t k = key[u * 4 + e];
       const uint32_t bin = k >> 21;
+      // the bounds hold whenever the histogram is the row's (kept even if the
+      // workspace was not zero on entry, so that no write leaves the row)
       if (bin > b1) {
-        sel[ps++] = t;
+        if (ps < (uint32_t)K) sel[ps] = t;
+        ++ps;
       } else if (bin == b1) {
-        ck[pc] = k;
-        ct[pc] = t;
+        if (pc < (uint32_t)T_stride) {
+          ck[pc] = k;
+          ct[pc] = t;
+        }
         ++pc;
       }
     }
@@ -347,18 +363,36 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   const int r = blockIdx.x;
   const int n = row_visible(ctx_len, P, r);
   int32_t* out = topk + (size_t)r * K;
+  uint32_t* gk = ws.ckey + (size_t)r * T_stride;
+  int32_t* gt = ws.ctok + (size_t)r * T_stride;
+  int32_t* sel = ws.sel + (size_t)r * K;
+  // Everything the call wrote into the row's part of the workspace is dead once
+  // read, and is zeroed for the next call: the histogram and counters, the
+  // outright selections and the candidates (every filter workgroup of the row
+  // finished before this kernel began).  A workspace zeroed once therefore
+  // comes back zero from every call, whatever the batch geometry of the next.
+  auto clear_row = [&](int nc_written) {
+    for (int i = tid; i < kBins1 / 4; i += kFinNT)
+      reinterpret_cast<uint4*>(ws.hist + (size_t)r * kBins1)[i] = make_uint4(0, 0, 0, 0);
+    if (tid < kCnt) ws.cnt[r * kCnt + tid] = 0;
+    for (int i = tid; i < K; i += kFinNT) sel[i] = 0;
+    for (int i = tid; i < nc_written; i += kFinNT) {
+      gk[i] = 0u;
+      gt[i] = 0;
+    }
+  };
   if (n <= K) {
     for (int k = tid; k < K; k += kFinNT) out[k] = k < n ? k : -1;
+    clear_row(0);
     return;
   }
+  // counts are clamped to the row's buffers (they hold whenever the workspace
+  // was zero on entry; the clamps keep every access inside the row otherwise)
   const uint32_t b1 = ws.cnt[r * kCnt + 2];
-  const uint32_t above = ws.cnt[r * kCnt + 3];
-  const int nc = (int)ws.cnt[r * kCnt + 1];
-  const uint32_t* gk = ws.ckey + (size_t)r * T_stride;
-  const int32_t* gt = ws.ctok + (size_t)r * T_stride;
+  const uint32_t above = min(ws.cnt[r * kCnt + 3], (uint32_t)K);
+  const int nc = (int)min(ws.cnt[r * kCnt + 1], (uint32_t)T_stride);
   // the outright selections and (when they fit) the candidates go to LDS
   // with one pass of independent loads
-  const int32_t* sel = ws.sel + (size_t)r * K;
   // loops over global memory issue kLd independent loads per thread before
   // using any of them (the candidates' order does not matter to the result)
   constexpr int kLd = 8;
@@ -394,6 +428,8 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   if (tid == 0) {
     s_pos = (int)above;
     s_stage = 0;                  // staging cursor of the two-pass path below
+    s_d = 0;                      // bin searches leave these unchanged if they find
+    s_before = 0;                 // nothing (only with a workspace not zero on entry)
   }
   __syncthreads();
   const int lane = lane_id();
@@ -547,6 +583,7 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
     written += tot;
     __syncthreads();   // the next pass rewrites the bitmap and the run prefixes
   }
+  clear_row(nc);
 }
 
 }  // namespace
@@ -567,6 +604,8 @@ hipError_t launch_topk(const BatchDims& d, int K, const float* scores, int32_t* 
                      d.T_stride, K, scores, w);
   return launch_topk_select(d, K, scores, topk, ws, s);
 }
+
+uint32_t* topk_histograms(void* ws) { return static_cast<uint32_t*>(ws); }
 
 hipError_t launch_topk_zero(const BatchDims& d, int K, void* ws, uint32_t** hist, hipStream_t s) {
   const int R = d.B * d.P;

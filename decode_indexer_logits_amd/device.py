@@ -36,7 +36,12 @@ def _dev(a, device, dtype_tag=None):
 
 
 class DeviceStep:
-    """All device buffers of a workload, ready to run decode steps."""
+    """All device buffers of a workload, ready to run decode steps.
+
+    ``wl`` is any object with the workload attributes used below (sizes, dtype
+    tags, the indexer cache, residency tables, host pool and per-step queries as
+    numpy arrays) and a ``physical_pool()`` method giving the initial pool
+    contents; this module imports no workload generator."""
 
     def __init__(self, wl, device: str = "cuda:0", host_pool: bool = True,
                  indexer_q: str | None = None, host_layout: str = "interleaved"):
@@ -81,15 +86,17 @@ class DeviceStep:
         self.counts = torch.zeros((B, 4), dtype=torch.int32, device=d)
         self.out = torch.empty((L, B, P, wl.Hq, 512), dtype=torch.float32, device=d)
         self.lse = torch.empty((L, B, P, wl.Hq), dtype=torch.float32, device=d)
-        self.ws_topk = torch.empty(max(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, P, Ts, K), 16),
+        # zero-filled once: the fused indexer adds its histograms into it, and
+        # every selection returns what it wrote to zero
+        self.ws_topk = torch.zeros(max(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, P, Ts, K), 16),
                                    dtype=torch.uint8, device=d)
         mla_ws = _lib.workspace_bytes(_lib.HS_OP_MLA, B, P, Ts, K, wl.Hq)
         if L > 1:
             mla_ws = max(mla_ws, _lib.mla_layers_workspace_bytes(B, P, K, wl.Hq, L))
         self.ws_mla = torch.empty(max(mla_ws, 16), dtype=torch.uint8, device=d) if mla_ws else None
-        # latent pool and residency tables
-        from workloads.gen import build_pool
-        pool, rsc = build_pool(wl)
+        # latent pool and residency tables: the workload supplies the pool's
+        # initial contents (resident pages and occupied hot slots)
+        pool, rsc = wl.physical_pool()
         self.pool = _dev(pool, d)
         self.row_scale = None if rsc is None else _dev(rsc, d)
         del pool
@@ -194,6 +201,20 @@ class DeviceStep:
         _lib.indexer_topk(self.batch, wl.H_idx, wl.D_idx, qt, qi, w,
                           wl.k_dtype, self.idx_pool, self.idx_scale, self.idx_bt, self.bias,
                           self.scores, wl.K, self.topk, self.ws_topk, stream)
+
+    def run_indexer_topk_scores(self, stream=None, quantize=True):
+        """First half of run_indexer_topk: the indexer with the top-K histogram
+        in its epilogue (run_indexer_topk_select must follow)."""
+        wl = self.wl
+        qt, qi, w = self._indexer_inputs(stream, quantize)
+        _lib.indexer_topk_scores(self.batch, wl.H_idx, wl.D_idx, qt, qi, w, wl.k_dtype,
+                                 self.idx_pool, self.idx_scale, self.idx_bt, self.bias,
+                                 self.scores, wl.K, self.ws_topk, stream)
+
+    def run_indexer_topk_select(self, stream=None):
+        """Second half of run_indexer_topk: the selection."""
+        _lib.indexer_topk_select(self.batch, self.indexer_q, self.wl.K, self.scores, self.topk,
+                                 self.ws_topk, stream)
 
     def run_resolve(self, stream=None):
         _lib.resolve_rows(self.batch, self.wl.K, self.topk, self.res, self.row_ids, self.faults,

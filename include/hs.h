@@ -155,7 +155,8 @@ hs_status hs_quantize_queries(const hs_batch* batch, int32_t H_idx, int32_t D_id
  * followed by -1.  Scores must not be NaN; -0.0 equals +0.0.
  *   scores [B, P, T_stride] fp32 (16-byte aligned), topk [B, P, K] int32 output.
  * 1 <= K <= 8192.  Workspace: hs_workspace_bytes(HS_OP_TOPK, ...), 16-byte
- * aligned; its contents on entry do not matter. */
+ * aligned; its contents on entry do not matter (the call clears what it
+ * needs), and it is left zero-filled. */
 hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t* topk,
                   void* ws, size_t ws_bytes, void* stream);
 
@@ -178,13 +179,37 @@ size_t hs_topk_sharded_workspace_bytes(int32_t B, int32_t T_stride, int32_t K, i
 /* hs_indexer_scores followed by hs_topk, with the first pass of the top-K
  * radix select (the per-row histogram of the top 11 score-key bits) built in
  * the indexer's epilogue instead of a separate pass over the scores.  Same
- * arguments, outputs and workspace (hs_workspace_bytes(HS_OP_TOPK, ...)) as
- * the two calls; scores are still written. */
+ * arguments and outputs as the two calls; scores are still written.
+ * Workspace: hs_workspace_bytes(HS_OP_TOPK, ...) bytes, 16-byte aligned, and
+ * ZERO-FILLED before its first use: the histograms are added into it.  Every
+ * call (and every hs_topk call) returns every word it wrote to zero, so a
+ * workspace zeroed once can be reused as it is by any later call, whatever
+ * its batch geometry. */
 hs_status hs_indexer_topk(const hs_batch* batch, int32_t H_idx, int32_t D_idx, hs_dtype q_t,
                           const void* q_idx, const float* w, hs_dtype k_t, const void* idx_pool,
                           const float* idx_scale, const int32_t* idx_bt, const float* bias,
                           float* scores, int32_t K, int32_t* topk, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* The two halves of hs_indexer_topk, for callers that schedule or time them
+ * apart:
+ *   hs_indexer_topk_scores  the indexer: scores, and every row's histogram
+ *                           added into the (zeroed) workspace (none for
+ *                           HS_F32 queries);
+ *   hs_indexer_topk_select  the rest of the selection from those scores and
+ *                           histograms (for q_t = HS_F32 the whole of
+ *                           hs_topk); it returns the workspace to zero.
+ * Enqueued in this order on one stream, with the same batch, K, scores and
+ * workspace, they are hs_indexer_topk.  A scores half must be followed by its
+ * select half before the workspace is used again. */
+hs_status hs_indexer_topk_scores(const hs_batch* batch, int32_t H_idx, int32_t D_idx,
+                                 hs_dtype q_t, const void* q_idx, const float* w, hs_dtype k_t,
+                                 const void* idx_pool, const float* idx_scale,
+                                 const int32_t* idx_bt, const float* bias, float* scores,
+                                 int32_t K, void* ws, size_t ws_bytes, void* stream);
+hs_status hs_indexer_topk_select(const hs_batch* batch, hs_dtype q_t, int32_t K,
+                                 const float* scores, int32_t* topk, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* hs_indexer_topk for callers that cannot allocate device memory: code under
  * HIP graph capture that may not call hipMalloc, tight serving loops, and

@@ -392,6 +392,69 @@ def test_fused_indexer_topk_matches_separate_calls(name):
     gc.check_topk_exact(wl, ds.scores.cpu().numpy(), ds.topk.cpu().numpy())
 
 
+def test_fused_indexer_topk_workspace_reuse_and_halves():
+    """The selection returns every workspace word it wrote to zero, so fused
+    calls in a row on one workspace (zeroed once) stay exact whether B*P grows
+    or shrinks (the histogram area of a larger batch covers the selections and
+    candidates of a smaller one); the two halves (hs_indexer_topk_scores, then
+    hs_indexer_topk_select) give the fused call's scores and top-K bit for
+    bit; after hs_topk on a dirtied workspace the fused call is exact again."""
+    from decode_indexer_logits_amd import _lib
+    from oracle import topk as o_topk
+    Ts, K = 16384, 512
+    ws = torch.zeros(_lib.workspace_bytes(_lib.HS_OP_TOPK, 24, 1, Ts, K), dtype=torch.uint8,
+                     device="cuda")
+
+    def inputs(seed, B):
+        rng = np.random.default_rng(seed)
+        ctx = rng.integers(1, Ts + 1, B).astype(np.int32)
+        ctx[0] = Ts
+        x = gen.indexer_inputs(seed, ctx, Ts)
+        dev = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).cuda()
+               for k, v in x.items() if isinstance(v, np.ndarray)}
+        batch = _lib.make_batch(B, 1, Ts, dev["ctx_len"])
+        args = (x["H"], x["D"], "bf16", dev["q_idx"], dev["w"], "e4m3", dev["idx_pool"],
+                dev["idx_scale"], dev["idx_bt"], dev["bias"])
+        # dev is returned too: the batch holds the address of dev["ctx_len"]
+        return ctx, batch, args, dev
+
+    def fused(batch, args, B, w):
+        s = torch.empty((B, 1, Ts), device="cuda")
+        t = torch.full((B, 1, K), -7, dtype=torch.int32, device="cuda")
+        _lib.indexer_topk(batch, *args, s, K, t, w)
+        torch.cuda.synchronize()
+        return s.cpu().numpy(), t.cpu().numpy()
+
+    for seed, B in ((40, 7), (41, 24), (42, 24), (43, 7)):
+        _say(f"fused indexer + top-K on a reused workspace: B={B}")
+        ctx, batch, args, dev = inputs(seed, B)
+        sc, tk = fused(batch, args, B, ws)
+        assert np.array_equal(tk, o_topk.topk(sc.astype(np.float64), ctx, K)), (seed, B)
+        # the halves on the same (reused) workspace
+        s2 = torch.empty((B, 1, Ts), device="cuda")
+        t2 = torch.full((B, 1, K), -7, dtype=torch.int32, device="cuda")
+        _lib.indexer_topk_scores(batch, *args, s2, K, ws)
+        _lib.indexer_topk_select(batch, "bf16", K, s2, t2, ws)
+        torch.cuda.synchronize()
+        for b in range(B):
+            n = int(ctx[b])
+            assert np.array_equal(s2.cpu().numpy()[b, 0, :n].view(np.uint32),
+                                  sc[b, 0, :n].view(np.uint32)), b
+        assert np.array_equal(t2.cpu().numpy(), tk)
+    # a dirtied workspace: hs_topk clears what it needs and leaves it zero again
+    ws.fill_(0xA5)
+    ctx, batch, args, dev = inputs(44, 24)
+    s = torch.empty((24, 1, Ts), device="cuda")
+    t = torch.empty((24, 1, K), dtype=torch.int32, device="cuda")
+    _lib.indexer_scores(batch, *args, s)
+    _lib.topk(batch, K, s, t, ws)
+    torch.cuda.synchronize()
+    sc = s.cpu().numpy()
+    assert np.array_equal(t.cpu().numpy(), o_topk.topk(sc.astype(np.float64), ctx, K))
+    sc2, tk2 = fused(batch, args, 24, ws)
+    assert np.array_equal(tk2, o_topk.topk(sc2.astype(np.float64), ctx, K))
+
+
 def _planted_scores(case, rng, B, P, T_stride):
     shape = (B, P, T_stride)
     if case == "quarter_steps":          # few distinct values: heavy ties at the threshold
@@ -463,7 +526,7 @@ def test_indexer_many_requests_long_tiles(B):
     s1 = torch.empty((B, 1, Ts), dtype=torch.float32, device="cuda")
     s2 = torch.empty_like(s1)
     topk = torch.empty((B, 1, K), dtype=torch.int32, device="cuda")
-    ws = torch.empty(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, 1, Ts, K), dtype=torch.uint8,
+    ws = torch.zeros(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, 1, Ts, K), dtype=torch.uint8,
                      device="cuda")
     args = (x["H"], x["D"], "bf16", dev["q_idx"], dev["w"], "e4m3", dev["idx_pool"],
             dev["idx_scale"], dev["idx_bt"], dev["bias"])

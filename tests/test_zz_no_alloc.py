@@ -52,7 +52,7 @@ def _both(x, qt, kt, K):
             dev["idx_bt"], dev.get("bias"))
     s_ref = torch.full((B, 1, Ts), float("nan"), device="cuda")
     t_ref = torch.full((B, 1, K), -7, dtype=torch.int32, device="cuda")
-    ws = torch.empty(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, 1, Ts, K), dtype=torch.uint8,
+    ws = torch.zeros(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, 1, Ts, K), dtype=torch.uint8,
                      device="cuda")
     _lib.indexer_topk(batch, *args, s_ref, K, t_ref, ws)
     s = torch.full_like(s_ref, float("nan"))

@@ -247,6 +247,11 @@ class Workload:
         """(q_idx, q) of step s (1-based): q_idx [B,P,H,D], q [L,B,P,Hq,576]."""
         return self._step_q[s - 1]
 
+    def physical_pool(self):
+        """(pool [L, n_rows, 576], row_scale [L, n_rows] or None) of the initial
+        state: what the device pool holds before the first step."""
+        return build_pool(self)
+
     @property
     def q_idx(self):
         return self._step_q[0][0]
