@@ -26,8 +26,12 @@ ARCH = "gfx950"
 SOURCES = ["indexer.hip", "topk.hip", "resolve.hip", "mla.hip", "cache_ops.hip", "shard_topk.hip", "hs_api.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function", f"-I{ROOT / 'include'}"]
+# Matrix-core accumulators in ordinary VGPRs, except for the attention kernel,
+# whose 128 output accumulators per lane belong in the accumulation registers
+# (the VGPRs then hold the row gathers and the operands of many LDS reads).
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+NO_VGPR_FORM = {"mla.hip"}
 
 
 def hipcc() -> str:
@@ -39,7 +43,8 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> Path:
     obj = BUILD / (Path(src).stem + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", str(CSRC / src), "-o", str(obj)]
+    extra = [] if src in NO_VGPR_FORM else VGPR_FORM
+    cmd = [hipcc(), *FLAGS, *extra, "-c", str(CSRC / src), "-o", str(obj)]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -69,7 +74,7 @@ def build(verbose: bool = False) -> Path:
 def build_probe() -> Path:
     """Compiles csrc/probe.hip (benchmark bandwidth probes) into libhsprobe.so."""
     tmp = PROBE_OUT.with_suffix(".so.tmp")
-    cmd = [hipcc(), *FLAGS, "-shared", str(CSRC / "probe.hip"), "-o", str(tmp)]
+    cmd = [hipcc(), *FLAGS, *VGPR_FORM, "-shared", str(CSRC / "probe.hip"), "-o", str(tmp)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on probe.hip:\n{r.stdout}{r.stderr}")

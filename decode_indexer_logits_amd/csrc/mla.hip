@@ -36,6 +36,7 @@ namespace {
 constexpr int kMlaNT = 256;
 constexpr int kMlaTargetWGs = 256;   // splits of the selected rows fill about this many workgroups
 constexpr int kMlaMaxSplitRows = 1024;   // and no slice walks more than 16 tiles
+constexpr int kMlaRing = 4;              // tiles of row gathers in flight per workgroup
 constexpr int kTile = 64;
 constexpr int kPtStride = 72;
 constexpr int kHq = 16;
@@ -65,15 +66,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 }
 
 template <bool SPLIT>
-__global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
+__global__ __launch_bounds__(kMlaNT, 1) void mla_bf16_e4m3_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ pool,
     const float* __restrict__ row_scale, const int32_t* __restrict__ row_ids, int K,
     int rows_per_split, int nsplit, float qk_scale_log2, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
     int64_t pool_layer_rows) {
-  __shared__ __attribute__((aligned(16))) uint16_t Vr[kTile * kVrStride];   // value tile, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t Pt[kHq * kPtStride];
-  __shared__ float red[4][kHq];
+  // per wave: the value parts of its current two 16-row tiles (bf16, row-major);
+  // once every wave is done with its rows, the same memory holds the four
+  // waves' output partials for the in-workgroup merge
+  __shared__ __attribute__((aligned(16))) uint16_t stash[4][2][16 * kVrStride];
+  __shared__ int s_rid[4][kMlaMaxSplitRows / 4];   // each wave's row ids, -1 past its rows
+  __shared__ float s_m[4][kHq], s_l[4][kHq];
+  // the queries, loaded once per workgroup: rows of 72 16-byte words padded to
+  // 73, so that the 16 heads' fragment reads fall on distinct banks
+  constexpr int kQRow = kDLat * 2 / 16;
+  __shared__ uint4 s_q[kHq * (kQRow + 1)];
+  static_assert(sizeof(stash) >= 4 * kHq * kDVal * sizeof(float), "the merge reuses the stash");
 
   const int bp = blockIdx.y, split = blockIdx.x;
   // layer blockIdx.z of a multi-layer call: its queries, pool rows, scales,
@@ -90,113 +99,177 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
       part_ml += layer * BPn * nsplit * kHq * 2;
     }
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;
+  // the slice [kb, kb + nrows) of the selection; wave w takes its quarter
+  // [w0, w1), in 16-row tiles (rows_per_split is a multiple of 64)
   const int kb = split * rows_per_split;
-  const int ke = min(K, kb + rows_per_split);
+  const int nrows = max(min(K, kb + rows_per_split) - kb, 0);
+  const int per_wave = rows_per_split / 4;
+  const int w0 = min(wave * per_wave, nrows), w1 = min(w0 + per_wave, nrows);
+  const int ntiles = (w1 - w0 + 15) / 16;
 
   // contraction step s takes dims dim0(s) .. +8 of head n (Q) and of row n (X)
   auto dim0 = [&](int s) { return 64 * (s >> 1) + 16 * g + 8 * (s & 1); };
-  const int32_t* rid_p = row_ids + (size_t)bp * K;
-  const int r_local = 16 * wave + n;
-  // row ids run one tile ahead of the row loads, so a tile's rows wait for one
-  // round of loads, not two; this lane gathers row r_local, bytes 64v + 16g .. +16
-  auto load_rid = [&](int kt) {
-    const int kk = kt + r_local;
-    return (kk < ke) ? rid_p[kk] : -1;
-  };
-  // the first row ids go out before the queries: loads complete in order, so
-  // the first gather then waits for its row ids only
-  int rid = load_rid(kb), rid_n = load_rid(kb + kTile);
-  bf16x8_t qf[18];
+  // the row ids first (the gathers wait for them), then the queries, which
+  // stay in flight while the row ids go to this wave's own LDS row (the wave
+  // alone reads them back, in program order after these writes)
+  int* wrid = s_rid[wave];
+  int first = -1;
+  constexpr int kPer = kMlaMaxSplitRows / 4 / kWave;
+  int r[kPer];
+  constexpr int kQPer = (kHq * kQRow + kMlaNT - 1) / kMlaNT;
+  const uint4* qg = reinterpret_cast<const uint4*>(q + (size_t)bp * kHq * kDLat);
+  uint4 qv[kQPer];
   {
-    const uint16_t* qp = q + ((size_t)bp * kHq + n) * kDLat;
+    const int32_t* rp = row_ids + (size_t)bp * K + kb + w0;
 #pragma unroll
-    for (int s = 0; s < 18; ++s)
-      qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + dim0(s)));
+    for (int u = 0; u < kPer; ++u) {
+      const int i = lane + u * kWave;
+      r[u] = i < w1 - w0 ? rp[i] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int i = tid + kMlaNT * k;
+      qv[k] = i < kHq * kQRow ? qg[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      wrid[lane + u * kWave] = r[u];
+      if (first < 0 && r[u] >= 0) first = r[u];
+    }
   }
-  f32x4_t o[8];
+  // a valid row of this wave: the target of reads that fill rows with id -1
+  // and ring slots past the last tile (their probabilities are zero).  A wave
+  // with no valid row reads the workgroup's queries instead (any readable 16
+  // bytes) and skips the work.
+  const uint64_t have = __ballot(first >= 0);
+  const int fallback = have ? __shfl(first, __ffsll((long long)have) - 1) : 0;
+  const uint8_t* const no_row = reinterpret_cast<const uint8_t*>(qg);
+  // the scale of this wave's row `lane` (rows of tiles 0..3), one load per wave
+  const float sc_lane = have ? row_scale[r[0] >= 0 ? r[0] : fallback]
+                             : *reinterpret_cast<const float*>(no_row);
+  const bool few = ntiles <= kMlaRing;   // every tile in flight from the start
+
+  f32x4_t o[32];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 32; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
-  auto gather = [&](int rid, float& rs, uint4* raw) {
-    rs = 0.f;
-    if (rid >= 0) {
-      const uint8_t* src = pool + (size_t)rid * kDLat + 16 * g;
+
+  // Row gathers: a ring of kMlaRing tiles in registers, every gather issued
+  // unconditionally so that the compiler waits for the oldest tile only.
+  // Lane (n, g) gathers row n of the tile, bytes 64v + 16g .. +16 for v =
+  // 0..8 (a wave load covers whole 64-byte chunks of 16 rows).  A slot past
+  // the last tile reads one 16-byte line of the fallback row instead.  Beyond
+  // the first kMlaRing tiles a slot also loads its rows' scales.
+  uint4 raw[kMlaRing][9];
+  float rs[kMlaRing];
+  auto issue = [&](int t, uint4* rw, float& sc, bool with_scale) {
+    const bool live = have && t < ntiles;
+    const int rid = wrid[min(t, max(ntiles - 1, 0)) * 16 + n];
+    const int row = (live && rid >= 0) ? rid : fallback;
+    // the scale first: waiting for it never waits for the row loads behind it
+    if (with_scale) sc = row_scale[row];
+    const uint8_t* src = have ? pool + (size_t)row * kDLat + (live ? 16 * g : 0) : no_row;
+    const int step = live ? 64 : 0;
 #pragma unroll
-      for (int v = 0; v < 9; ++v) raw[v] = *reinterpret_cast<const uint4*>(src + 64 * v);
-      rs = row_scale ? row_scale[rid] : 1.f;
-    } else {
-#pragma unroll
-      for (int v = 0; v < 9; ++v) raw[v] = make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int v = 0; v < 9; ++v) rw[v] = *reinterpret_cast<const uint4*>(src + step * v);
   };
-  float rs, rs_n = 0.f;
-  uint4 raw[9], raw_n[9];
-  gather(rid, rs, raw);
-  for (int kt = kb; kt < ke; kt += kTile) {
-    int rid_nn = -1;
-    if (kt + kTile < ke) {
-      gather(rid_n, rs_n, raw_n);
-      rid_nn = load_rid(kt + 2 * kTile);
-    }
-    // S^T = X . Q^T over 576 values; stash the value part (row-major) in LDS
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 18; ++s) {
-      const uint4 c = raw[s >> 1];
-      const uint32_t lo = (s & 1) ? c.z : c.x;
-      const uint32_t hi = (s & 1) ? c.w : c.y;
-      u32x4_t xb;
-      xb[0] = e4m3x2_to_bf16x2(lo, false);
-      xb[1] = e4m3x2_to_bf16x2(lo, true);
-      xb[2] = e4m3x2_to_bf16x2(hi, false);
-      xb[3] = e4m3x2_to_bf16x2(hi, true);
-      acc = mfma16x16x32(as_bf16x8(xb), qf[s], acc);
-      if (dim0(s) < kDVal)
-        *reinterpret_cast<uint4*>(Vr + r_local * kVrStride + dim0(s)) =
-            make_uint4(xb[0], xb[1], xb[2], xb[3]);
-    }
-    // logits of this lane's rows 4g+i (head n), log2 domain
-    float z[4];
-    float sc[4];
+  for (int j = 0; j < kMlaRing; ++j) issue(j, raw[j], rs[j], false);
+  // the queries to LDS once they arrive (the gathers stay in flight), then
+  // every wave reads its fragments: head n, dims dim0(s) .. +8
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int src_lane = 4 * g + i;
-      const int r_i = __shfl(rid, src_lane);
-      sc[i] = __shfl(rs, src_lane);
-      z[i] = (r_i >= 0) ? acc[i] * qk_scale_log2 * sc[i] : -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mx = max_rows16(mx);
-    if (g == 0) red[wave][n] = mx;
-    __syncthreads();
-    const float mt = fmaxf(fmaxf(red[0][n], red[1][n]), fmaxf(red[2][n], red[3][n]));
-    const float m_new = fmaxf(m_run, mt);
-    float alpha = 1.f, p[4] = {0.f, 0.f, 0.f, 0.f};
-    if (m_new != -INFINITY) {
-      alpha = exp2f(m_run - m_new);
+  for (int k = 0; k < kQPer; ++k) {
+    const int i = tid + kMlaNT * k;
+    if (i < kHq * kQRow) s_q[(i / kQRow) * (kQRow + 1) + i % kQRow] = qv[k];
+  }
+  __syncthreads();
+  // query fragment of contraction step s, read from LDS where it is used
+  const uint4* qrow = s_q + n * (kQRow + 1);
+  auto qfrag = [&](int s) { return as_bf16x8(qrow[dim0(s) / 8]); };
+
+  if (have) {
+
+    uint16_t* stA = stash[wave][0];
+    uint16_t* stB = stash[wave][1];
+    // Tiles t and t + 1 (slots a, b): S^T = X . Q^T for both (two independent
+    // product chains), the value parts stashed in this wave's LDS, online
+    // softmax over the 32 rows, then O^T += V^T . P^T with K = 32 rows laid
+    // out as [rows 4g..4g+3 of tile t, rows 4g..4g+3 of tile t + 1] in lane
+    // group g: the probabilities are then already the B operand of this lane.
+    auto pair = [&](int t, const uint4* ra, float rsa, const uint4* rb, float rsb) {
+      // scales of the tiles' rows: lane 16t + r holds row r of tile t (< 4),
+      // a refilled slot's lane r holds its row r
+      const bool lane_sc = t < kMlaRing;
+      f32x4_t aA = f32x4_t{0.f, 0.f, 0.f, 0.f}, aB = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = exp2f(z[i] - m_new);
-    }
-    l_part = l_part * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    {
-      const uint32_t w0 = f32_to_bf16_rne(p[0] * sc[0]) | (f32_to_bf16_rne(p[1] * sc[1]) << 16);
-      const uint32_t w1 = f32_to_bf16_rne(p[2] * sc[2]) | (f32_to_bf16_rne(p[3] * sc[3]) << 16);
-      *reinterpret_cast<uint2*>(Pt + n * kPtStride + 16 * wave + 4 * g) = make_uint2(w0, w1);
-    }
+      for (int s = 0; s < 18; ++s) {
+        const uint4 ca = ra[s >> 1], cb = rb[s >> 1];
+        u32x4_t xa, xb;
+        const uint32_t la = (s & 1) ? ca.z : ca.x, ha = (s & 1) ? ca.w : ca.y;
+        const uint32_t lb = (s & 1) ? cb.z : cb.x, hb = (s & 1) ? cb.w : cb.y;
+        xa[0] = e4m3x2_to_bf16x2(la, false);
+        xa[1] = e4m3x2_to_bf16x2(la, true);
+        xa[2] = e4m3x2_to_bf16x2(ha, false);
+        xa[3] = e4m3x2_to_bf16x2(ha, true);
+        xb[0] = e4m3x2_to_bf16x2(lb, false);
+        xb[1] = e4m3x2_to_bf16x2(lb, true);
+        xb[2] = e4m3x2_to_bf16x2(hb, false);
+        xb[3] = e4m3x2_to_bf16x2(hb, true);
+        const bf16x8_t qs = qfrag(s);
+        aA = mfma16x16x32(as_bf16x8(xa), qs, aA);
+        aB = mfma16x16x32(as_bf16x8(xb), qs, aB);
+        if (dim0(s) < kDVal) {
+          *reinterpret_cast<uint4*>(stA + n * kVrStride + dim0(s)) = make_uint4(xa[0], xa[1], xa[2], xa[3]);
+          *reinterpret_cast<uint4*>(stB + n * kVrStride + dim0(s)) = make_uint4(xb[0], xb[1], xb[2], xb[3]);
+        }
+      }
+      // logits of rows 4g+i of both tiles (head n), log2 domain; a row id of -1
+      // (or a row past the wave's rows) gets -inf
+      float z[8], sc[8];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-    m_run = m_new;
-    __syncthreads();
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        sc[i] = lane_sc ? __shfl(sc_lane, 16 * t + r) : __shfl(rsa, r);
+        sc[4 + i] = lane_sc ? __shfl(sc_lane, 16 * (t + 1) + r) : __shfl(rsb, r);
+        const int ida = wrid[t * 16 + r];
+        const int idb_any = wrid[min(t + 1, ntiles - 1) * 16 + r];
+        const int idb = (t + 1 < ntiles) ? idb_any : -1;
+        z[i] = ida >= 0 ? aA[i] * qk_scale_log2 * sc[i] : -INFINITY;
+        z[4 + i] = idb >= 0 ? aB[i] * qk_scale_log2 * sc[4 + i] : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                       fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+      mx = max_rows16(mx);
+      const float m_new = fmaxf(m_run, mx);
+      float alpha = 1.f, p[8];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bf16x8_t pb = as_bf16x8(*reinterpret_cast<const uint4*>(Pt + n * kPtStride + 32 * c + 8 * g));
+      for (int i = 0; i < 8; ++i) p[i] = 0.f;
+      if (m_new != -INFINITY) {
+        alpha = exp2f(m_run - m_new);
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int d0 = 128 * wave + 16 * dt;
-        const lds_v4i16 lo = vr_read_tr(Vr, 32 * c + 8 * g, d0, n);
-        const lds_v4i16 hi = vr_read_tr(Vr, 32 * c + 8 * g + 4, d0, n);
+        for (int i = 0; i < 8; ++i) p[i] = exp2f(z[i] - m_new);
+      }
+      l_part = l_part * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+      m_run = m_new;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < 32; ++dt) o[dt] *= alpha;
+      }
+      // probabilities times the row scale (which multiplies the value codes)
+      u32x4_t pw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pw[i] = f32_to_bf16_rne(p[2 * i] * sc[2 * i]) | (f32_to_bf16_rne(p[2 * i + 1] * sc[2 * i + 1]) << 16);
+      const bf16x8_t pb = as_bf16x8(pw);
+      // the stash writes above come first in this wave's LDS order
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt) {
+        const lds_v4i16 lo = vr_read_tr(stA, 4 * g, 16 * dt, n);
+        const lds_v4i16 hi = vr_read_tr(stB, 4 * g, 16 * dt, n);
         u32x4_t w;
         w[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
         w[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
@@ -204,38 +277,87 @@ __global__ __launch_bounds__(kMlaNT, 2) void mla_bf16_e4m3_kernel(
         w[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
         o[dt] = mfma16x16x32(as_bf16x8(w), pb, o[dt]);
       }
+      __builtin_amdgcn_wave_barrier();
+    };
+
+    // tile t sits in slot t % kMlaRing.  A wave with at most kMlaRing tiles
+    // (every slice of up to 256 rows) has all of them in flight from the start
+    // and runs straight through; longer ones refill a processed pair's slots
+    // with the tiles kMlaRing further on.  The branches are uniform per wave
+    // and hold no global load.
+    static_assert(kMlaRing == 4, "two pairs of slots");
+    if (few) {
+      pair(0, raw[0], rs[0], raw[1], rs[1]);
+      if (ntiles > 2) pair(2, raw[2], rs[2], raw[3], rs[3]);
+    } else {
+      for (int t0 = 0; t0 < ntiles; t0 += 4) {
+        pair(t0, raw[0], rs[0], raw[1], rs[1]);
+        issue(t0 + 4, raw[0], rs[0], true);
+        issue(t0 + 5, raw[1], rs[1], true);
+        if (t0 + 2 < ntiles) pair(t0 + 2, raw[2], rs[2], raw[3], rs[3]);
+        issue(t0 + 6, raw[2], rs[2], true);
+        issue(t0 + 7, raw[3], rs[3], true);
+      }
     }
-    __syncthreads();
-    rid = rid_n;
-    rs = rs_n;
-    rid_n = rid_nn;
-#pragma unroll
-    for (int v = 0; v < 9; ++v) raw[v] = raw_n[v];
   }
 
-  float lp = l_part;
-  lp = sum_rows16(lp);
-  if (g == 0) red[wave][n] = lp;
+  // merge the four waves in wave order: per head, M = max of the waves'
+  // maxima, each wave weighted by 2^(m_w - M).  Each wave's accumulators go
+  // to LDS as they sit in its registers ([tile dt][lane] float4s, lane
+  // (n, g) holding head n, dims 16dt + 4g .. +3), so writes and reads are
+  // lane-contiguous 16-byte accesses.
+  const float l_w = sum_rows16(l_part);
+  __syncthreads();                               // every wave is done with its stash
+  float4* s_o = reinterpret_cast<float4*>(&stash[0][0][0]);   // [4 waves][32 tiles][64 lanes]
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt)
+    s_o[(wave * 32 + dt) * kWave + lane] = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  if (g == 0) {
+    s_m[wave][n] = m_run;
+    s_l[wave][n] = l_w;
+  }
   __syncthreads();
-  const float l_tot = (red[0][n] + red[1][n]) + (red[2][n] + red[3][n]);
-  if (!SPLIT) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* op = out + ((size_t)bp * kHq + n) * kDVal + 128 * wave + 4 * g;
+  // thread j merges slots j + 256k (k = 0..7) of the [32 tiles][64 lanes]
+  // grid: all of head h = j % 16
+  const int h = tid & 15;
+  float mw[4], M = -INFINITY;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(op + 16 * dt) =
-          make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-    if (lse && wave == 0 && g == 0)
-      lse[(size_t)bp * kHq + n] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  } else {
-    const size_t base = ((size_t)bp * nsplit + split) * kHq + n;
-    float* op = part_o + base * kDVal + 128 * wave + 4 * g;
+  for (int w = 0; w < 4; ++w) {
+    mw[w] = s_m[w][h];
+    M = fmaxf(M, mw[w]);
+  }
+  float e[4], L = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (wave == 0 && g == 0) {
-      part_ml[base * 2] = m_run;
-      part_ml[base * 2 + 1] = l_tot;
+  for (int w = 0; w < 4; ++w) {
+    e[w] = (M != -INFINITY && mw[w] != -INFINITY) ? exp2f(mw[w] - M) : 0.f;
+    L = fmaf(s_l[w][h], e[w], L);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float* dst = SPLIT ? part_o + (((size_t)bp * nsplit + split) * kHq + h) * kDVal
+                     : out + ((size_t)bp * kHq + h) * kDVal;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int slot = tid + 256 * k;                  // tile dt = slot / 64, lane = slot % 64
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 v = s_o[w * 32 * kWave + slot];
+      acc.x = fmaf(v.x, e[w], acc.x);
+      acc.y = fmaf(v.y, e[w], acc.y);
+      acc.z = fmaf(v.z, e[w], acc.z);
+      acc.w = fmaf(v.w, e[w], acc.w);
+    }
+    const int d = 16 * (slot >> 6) + 4 * ((slot & 63) >> 4);
+    if (!SPLIT) acc = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    *reinterpret_cast<float4*>(dst + d) = acc;
+  }
+  if (tid < kHq) {
+    if (!SPLIT) {
+      if (lse) lse[(size_t)bp * kHq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      const size_t base = ((size_t)bp * nsplit + split) * kHq + h;
+      part_ml[base * 2] = M;
+      part_ml[base * 2 + 1] = L;
     }
   }
 }
@@ -339,6 +461,16 @@ __global__ __launch_bounds__(kWave) void mla_combine_kernel(int nsplit, const fl
   }
   const int lane = threadIdx.x;
   auto ml_index = [&](int sidx) { return (((size_t)bp * nsplit + sidx) * kHq + h) * 2; };
+  // the first eight slices' partial outputs go out before the maxima and sums,
+  // so that up to eight slices cost one round trip: this wave's 256 of the 512
+  // dims, one float4 per lane per slice
+  const float4* src = reinterpret_cast<const float4*>(
+                          part_o + (((size_t)bp * nsplit) * kHq + h) * kDVal + 256 * half) + lane;
+  const size_t split_stride = (size_t)kHq * kDVal / 4;      // float4s from one split to the next
+  float4 v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    v[u] = (u < nsplit) ? src[(size_t)u * split_stride] : make_float4(0.f, 0.f, 0.f, 0.f);
   // every split's (m, l) at once: lane s holds splits s and 64 + s
   float ms[kCombineMaxSplit / kWave], ls[kCombineMaxSplit / kWave];
   float M = -INFINITY;
@@ -366,18 +498,15 @@ __global__ __launch_bounds__(kWave) void mla_combine_kernel(int nsplit, const fl
   L += __shfl_xor(L, 2);
   L += __shfl_xor(L, 4);
   L += __shfl_xor(L, 8);
-  // values: this wave's 256 of the 512 dims, one float4 per lane per split, in
-  // split order; a split's partial output is finite (zero when it saw no row),
-  // so every load is unconditional and weight 0 drops it
+  // values in split order; a split's partial output is finite (zero when it saw
+  // no row), and weight 0 drops it
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float4* src = reinterpret_cast<const float4*>(
-                          part_o + (((size_t)bp * nsplit) * kHq + h) * kDVal + 256 * half) + lane;
-  const size_t split_stride = (size_t)kHq * kDVal / 4;      // float4s from one split to the next
   for (int s0 = 0; s0 < nsplit; s0 += 8) {
-    float4 v[8];
+    if (s0 > 0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = (s0 + u < nsplit) ? src[(size_t)(s0 + u) * split_stride] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int u = 0; u < 8; ++u)
+        v[u] = (s0 + u < nsplit) ? src[(size_t)(s0 + u) * split_stride] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int sidx = s0 + u;
