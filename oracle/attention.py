@@ -85,6 +85,53 @@ def sparse_mla(q, q_dtype: str, lat, lat_scale, kv_dtype: str, topk, sm_scale: f
     return out, lse
 
 
+def sparse_mla_sharded(q, q_dtype: str, lat, lat_scale, kv_dtype: str, topk, sm_scale: float,
+                       shard_len: int):
+    """The same attention computed the way a cache split across GPUs by tokens
+    computes it (page "vLLM sert GLM-5.3 en contexte 1M sur 16 H200", section
+    "Le mécanisme": DCP splits the KV cache by tokens across GPUs and gathers
+    the fragments at every layer).  The tokens are cut into contiguous shards
+    of shard_len tokens; each shard attends over the selected tokens it holds
+    and hands over its normalised output and log-sum-exp; the fragments are
+    merged in shard order by their log-sum-exp weights:
+
+      LSE = ln sum_s exp(lse_s),   out = sum_s exp(lse_s - LSE) * out_s.
+
+    A shard holding no selected token contributes out_s = 0, lse_s = -inf
+    (weight 0).  Returns (out [B,P,Hq,512], lse [B,P,Hq], shard_out
+    [B,P,S,Hq,512], shard_lse [B,P,S,Hq]) in float64, S = ceil(T_stride /
+    shard_len) with T_stride = lat.shape[1].
+    """
+    qf = to_f64(q, q_dtype)
+    B, P, Hq, _ = qf.shape
+    S = -(-lat.shape[1] // shard_len)
+    shard_out = np.zeros((B, P, S, Hq, D_VALUE))
+    shard_lse = np.full((B, P, S, Hq), -np.inf)
+    out = np.zeros((B, P, Hq, D_VALUE))
+    lse = np.full((B, P, Hq), -np.inf)
+    for b in range(B):
+        for p in range(P):
+            sel = np.asarray(topk[b, p])
+            sel = sel[sel >= 0]
+            for s in range(S):
+                mine = sel[(sel >= s * shard_len) & (sel < (s + 1) * shard_len)]
+                if len(mine) == 0:
+                    continue
+                x = logical_rows(lat[b], None if lat_scale is None else lat_scale[b], kv_dtype,
+                                 mine)
+                shard_out[b, p, s], shard_lse[b, p, s] = attend(qf[b, p], x, sm_scale)
+            ls = shard_lse[b, p]                                      # [S, Hq]
+            M = ls.max(axis=0)                                        # [Hq]
+            ok = np.isfinite(M)
+            w = np.where(ok[None, :], np.exp(ls - np.where(ok, M, 0.0)[None, :]), 0.0)
+            tot = w.sum(axis=0)
+            out[b, p] = np.where(ok[:, None],
+                                 (w[:, :, None] * shard_out[b, p]).sum(axis=0)
+                                 / np.where(ok, tot, 1.0)[:, None], 0.0)
+            lse[b, p] = np.where(ok, M + np.log(np.where(ok, tot, 1.0)), -np.inf)
+    return out, lse, shard_out, shard_lse
+
+
 def dense_mla(q, q_dtype: str, lat, lat_scale, kv_dtype: str, ctx_len, sm_scale: float):
     """Dense attention over every visible token (the K >= context reference)."""
     qf = to_f64(q, q_dtype)

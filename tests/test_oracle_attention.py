@@ -98,3 +98,49 @@ def test_row_order_does_not_matter_and_max_rel_err():
     assert np.allclose(o1, o2, rtol=1e-13, atol=1e-13) and np.allclose(l1, l2, rtol=1e-13)
     a = np.array([[1.0, -2.0, 4.0]])
     assert abs(attention.max_rel_err(a + np.array([[0, 0.04, 0]]), a) - 0.01) < 1e-15
+
+
+def test_sharded_attention_merges_to_the_global_attention():
+    """Token-sharded attention: the log-sum-exp merge of the shard fragments is
+    the attention over the whole selection (an identity of the softmax), for
+    shard counts that leave empty shards, split the selection unevenly or put
+    everything in one shard; each fragment is the attention over the selected
+    tokens of its shard alone."""
+    rng = np.random.default_rng(7)
+    T = 1024
+    lat, lsc, q = _setup(rng, T=T, Hq=4, B=2, P=2)
+    K = 96
+    topk = np.full((2, 2, K), -1, np.int32)
+    topk[0, 0] = np.sort(rng.choice(T, K, replace=False))
+    topk[0, 1, :40] = np.sort(rng.choice(200, 40, replace=False))     # one region only
+    topk[1, 0, :K - 5] = np.sort(rng.choice(T, K - 5, replace=False)) # -1 padded
+    topk[1, 1, :1] = [777]                                            # a single row
+    ref_o, ref_l = attention.sparse_mla(q, "bf16", lat, lsc, "e4m3", topk, 1 / 24)
+    for shard_len in (1024, 512, 256, 64, 16):
+        o, l, so, sl = attention.sparse_mla_sharded(q, "bf16", lat, lsc, "e4m3", topk, 1 / 24,
+                                                    shard_len)
+        assert so.shape[2] == T // shard_len
+        assert np.max(np.abs(o - ref_o)) < 1e-12 and np.max(np.abs(l - ref_l)) < 1e-12
+        for b in range(2):
+            for p in range(2):
+                sel = topk[b, p][topk[b, p] >= 0]
+                for s in range(T // shard_len):
+                    mine = sel[(sel >= s * shard_len) & (sel < (s + 1) * shard_len)]
+                    if len(mine) == 0:
+                        assert np.all(so[b, p, s] == 0) and np.all(np.isneginf(sl[b, p, s]))
+                        continue
+                    x = attention.logical_rows(lat[b], lsc[b], "e4m3", mine)
+                    qv = gen.bf16_values(q[b, p]).astype(np.float64)
+                    z = (qv @ x.T) / 24
+                    # closed forms: one row gives that row; the lse of the
+                    # fragment is the log of the partition sum over its rows
+                    assert np.allclose(sl[b, p, s], np.log(np.exp(z).sum(axis=1)), rtol=1e-12)
+                    if len(mine) == 1:
+                        assert np.allclose(so[b, p, s], np.broadcast_to(x[0, :512], so[b, p, s].shape),
+                                           rtol=1e-12)
+                # the fragment weights exp(lse_s - LSE) sum to one
+                w = np.exp(sl[b, p] - l[b, p][None, :])
+                assert np.allclose(w.sum(axis=0), 1.0, rtol=1e-12)
+    # one shard: the fragment is the global attention
+    o, l, so, sl = attention.sparse_mla_sharded(q, "bf16", lat, lsc, "e4m3", topk, 1 / 24, T)
+    assert np.array_equal(so[:, :, 0], o) and np.array_equal(sl[:, :, 0], l)
