@@ -26,6 +26,7 @@ EXPORTS = ["hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_to
            "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
            "hs_sparse_mla_decode", "hs_sparse_mla_decode_layers", "hs_mla_layers_workspace_bytes",
            "hs_topk_sharded", "hs_topk_sharded_workspace_bytes",
+           "hs_sparse_mla_decode_sharded", "hs_mla_sharded_workspace_bytes",
            "hs_append_tokens", "hs_precopy_pages", "hs_demote_pages",
            "hs_workspace_bytes", "hs_host_device_ptr", "hs_last_error", "hs_abi_version"]
 
@@ -93,6 +94,11 @@ def load() -> ctypes.CDLL:
     lib.hs_sparse_mla_decode_layers.restype = c_int32
     lib.hs_mla_layers_workspace_bytes.argtypes = [c_int32] * 5
     lib.hs_mla_layers_workspace_bytes.restype = c_size_t
+    lib.hs_sparse_mla_decode_sharded.argtypes = [P, c_int32, c_int32, c_int32, c_int32, P, c_int32,
+                                                 P, P, P, P, c_float, P, P, P, P, P, c_size_t, P]
+    lib.hs_sparse_mla_decode_sharded.restype = c_int32
+    lib.hs_mla_sharded_workspace_bytes.argtypes = [c_int32] * 5
+    lib.hs_mla_sharded_workspace_bytes.restype = c_size_t
     lib.hs_topk_sharded.argtypes = [P, c_int32, c_int32, P, P, P, c_size_t, P]
     lib.hs_topk_sharded.restype = c_int32
     lib.hs_topk_sharded_workspace_bytes.argtypes = [c_int32] * 4
@@ -247,6 +253,20 @@ def sparse_mla_decode_layers(batch: Batch, K: int, Hq: int, L: int, q_t: str, q,
 
 def mla_layers_workspace_bytes(B: int, P: int, K: int, Hq: int, L: int) -> int:
     return load().hs_mla_layers_workspace_bytes(B, P, K, Hq, L)
+
+
+def sparse_mla_decode_sharded(batch: Batch, K: int, S: int, Hq: int, q_t: str, q, kv_t: str, pool,
+                              row_scale, topk, row_ids, sm_scale: float, shard_out, shard_lse,
+                              out, lse, ws, stream=None):
+    _check(load().hs_sparse_mla_decode_sharded(
+        ctypes.byref(batch), K, S, Hq, DTYPES[q_t], _ptr(q), DTYPES[kv_t], _ptr(pool),
+        _ptr(row_scale), _ptr(topk), _ptr(row_ids), float(sm_scale), _ptr(shard_out),
+        _ptr(shard_lse), _ptr(out), _ptr(lse), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mla_sharded_workspace_bytes(B: int, P: int, K: int, S: int, Hq: int) -> int:
+    return load().hs_mla_sharded_workspace_bytes(B, P, K, S, Hq)
 
 
 def append_tokens(batch: Batch, ctx_len, n_new, res: Residency, new_rows, new_row_scale,

@@ -451,7 +451,8 @@ hs_status sparse_mla(const char* name, const hs_batch* batch, int32_t K, int32_t
   if (!q || !pool || !row_ids || !out)
     return fail(HS_ERR_NULL, "%s: q, pool, row_ids and out are required", name);
   if (K < 1 || K > 8192) return fail(HS_ERR_SHAPE, "K=%d out of [1, 8192]", K);
-  if (Hq != 16) return fail(HS_ERR_SHAPE, "Hq=%d: one shard of 16 heads per call", Hq);
+  if (Hq < 16 || Hq > 128 || Hq % 16)
+    return fail(HS_ERR_SHAPE, "Hq=%d must be a multiple of 16 in [16, 128]", Hq);
   if (L < 1 || L > 16) return fail(HS_ERR_SHAPE, "L=%d out of [1, 16]", L);
   if (L > 1 && pool_layer_rows < 1)
     return fail(HS_ERR_SHAPE, "pool_layer_rows=%lld must be positive for L > 1",
@@ -465,7 +466,7 @@ hs_status sparse_mla(const char* name, const hs_batch* batch, int32_t K, int32_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (q_t == HS_BF16 && kv_t == HS_E4M3) {
     if (!row_scale) return fail(HS_ERR_NULL, "E4M3 rows need row_scale");
-    return launched(hs::launch_mla_bf16_e4m3(d, K, L, pool_layer_rows,
+    return launched(hs::launch_mla_bf16_e4m3(d, K, L, Hq, pool_layer_rows,
                                              static_cast<const uint16_t*>(q),
                                              static_cast<const uint8_t*>(pool), row_scale, row_ids,
                                              sm_scale, out, lse, ws, s),
@@ -473,7 +474,7 @@ hs_status sparse_mla(const char* name, const hs_batch* batch, int32_t K, int32_t
   }
   if (q_t == HS_F32 && kv_t == HS_F32) {
     if (row_scale) return fail(HS_ERR_DTYPE, "F32 rows take no row_scale");
-    return launched(hs::launch_mla_f32(d, K, L, pool_layer_rows, static_cast<const float*>(q),
+    return launched(hs::launch_mla_f32(d, K, L, Hq, pool_layer_rows, static_cast<const float*>(q),
                                        static_cast<const float*>(pool), row_ids, sm_scale, out,
                                        lse, ws, s),
                     name);
@@ -504,8 +505,54 @@ hs_status hs_sparse_mla_decode_layers(const hs_batch* batch, int32_t K, int32_t 
 }
 
 size_t hs_mla_layers_workspace_bytes(int32_t B, int32_t P, int32_t K, int32_t Hq, int32_t L) {
-  if (B < 1 || P < 1 || K < 1 || L < 1) return 0;
+  if (B < 1 || P < 1 || K < 1 || L < 1 || Hq < 16 || Hq % 16) return 0;
   return hs::mla_workspace_bytes(B, P, K, Hq, L);
+}
+
+size_t hs_mla_sharded_workspace_bytes(int32_t B, int32_t P, int32_t K, int32_t S, int32_t Hq) {
+  if (B < 1 || P < 1 || K < 1 || K > 8192 || S < 1 || S > 64 || Hq < 16 || Hq > 128 || Hq % 16)
+    return 0;
+  return hs::mla_sharded_workspace_bytes(B, P, K, S, Hq);
+}
+
+hs_status hs_sparse_mla_decode_sharded(const hs_batch* batch, int32_t K, int32_t S, int32_t Hq,
+                                       hs_dtype q_t, const void* q, hs_dtype kv_t,
+                                       const void* pool, const float* row_scale,
+                                       const int32_t* topk, const int32_t* row_ids,
+                                       float sm_scale, float* shard_out, float* shard_lse,
+                                       float* out, float* lse, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  const char* name = "hs_sparse_mla_decode_sharded";
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!q || !pool || !topk || !row_ids || !shard_out || !shard_lse || !out)
+    return fail(HS_ERR_NULL, "%s: q, pool, topk, row_ids, shard_out, shard_lse and out are required",
+                name);
+  if (K < 1 || K > 8192) return fail(HS_ERR_SHAPE, "K=%d out of [1, 8192]", K);
+  if (S < 1 || S > 64 || d.T_stride % S)
+    return fail(HS_ERR_SHAPE, "S=%d must be in [1, 64] and divide T_stride=%d", S, d.T_stride);
+  if (Hq < 16 || Hq > 128 || Hq % 16)
+    return fail(HS_ERR_SHAPE, "Hq=%d must be a multiple of 16 in [16, 128]", Hq);
+  if (!aligned16(q) || !aligned16(pool) || !aligned16(out) || !aligned16(shard_out))
+    return fail(HS_ERR_ALIGN, "q, pool, shard_out and out need 16-byte alignment");
+  const size_t need = hs::mla_sharded_workspace_bytes(d.B, d.P, K, S, Hq);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", name, need, ws_bytes);
+  if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace needs 16-byte alignment");
+  bool f32;
+  if (q_t == HS_BF16 && kv_t == HS_E4M3) {
+    if (!row_scale) return fail(HS_ERR_NULL, "E4M3 rows need row_scale");
+    f32 = false;
+  } else if (q_t == HS_F32 && kv_t == HS_F32) {
+    if (row_scale) return fail(HS_ERR_DTYPE, "F32 rows take no row_scale");
+    f32 = true;
+  } else {
+    return fail(HS_ERR_DTYPE, "sparse MLA supports (q, kv) = (BF16, E4M3) or (F32, F32)");
+  }
+  return launched(hs::launch_mla_sharded(d, K, S, Hq, f32, q, pool, row_scale, topk, row_ids,
+                                         sm_scale, shard_out, shard_lse, out, lse, ws,
+                                         static_cast<hipStream_t>(stream)),
+                  name);
 }
 
 size_t hs_workspace_bytes(int32_t op, int32_t B, int32_t P, int32_t T_stride, int32_t K,

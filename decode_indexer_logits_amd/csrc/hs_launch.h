@@ -93,16 +93,24 @@ hipError_t launch_precopy_pages(const BatchDims& d, const ResidencyArgs& r, int 
 hipError_t launch_demote_pages(const BatchDims& d, const ResidencyArgs& r,
                                const int32_t* n_demote, int tail_pages,
                                const FreeListArgs& lat, void* ws, hipStream_t s);
-// Sparse MLA over L layers that share the row ids: queries [L, B, P, 16, 576],
-// layer l's pool rows at l * pool_layer_rows, outputs [L, B, P, 16, 512].
-int mla_num_splits(int B, int P, int K, int L);
+// Sparse MLA over L layers that share the row ids: queries [L, B, P, Hq, 576],
+// layer l's pool rows at l * pool_layer_rows, outputs [L, B, P, Hq, 512];
+// Hq a multiple of 16 (G = Hq / 16 head groups).
+int mla_num_splits(int B, int P, int K, int L, int G);
 size_t mla_workspace_bytes(int B, int P, int K, int Hq, int L);
-hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, int L, int64_t pool_layer_rows,
+hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, int L, int Hq, int64_t pool_layer_rows,
                                 const uint16_t* q, const uint8_t* pool, const float* row_scale,
                                 const int32_t* row_ids, float sm_scale, float* out, float* lse,
                                 void* ws, hipStream_t s);
-hipError_t launch_mla_f32(const BatchDims& d, int K, int L, int64_t pool_layer_rows,
+hipError_t launch_mla_f32(const BatchDims& d, int K, int L, int Hq, int64_t pool_layer_rows,
                           const float* q, const float* pool, const int32_t* row_ids,
                           float sm_scale, float* out, float* lse, void* ws, hipStream_t s);
+// Token-sharded attention: S shards of T_stride / S tokens; per-shard outputs
+// [B, P, S, Hq, 512] and log-sum-exp [B, P, S, Hq], merged into out / lse.
+size_t mla_sharded_workspace_bytes(int B, int P, int K, int S, int Hq);
+hipError_t launch_mla_sharded(const BatchDims& d, int K, int S, int Hq, bool f32, const void* q,
+                              const void* pool, const float* row_scale, const int32_t* topk,
+                              const int32_t* row_ids, float sm_scale, float* shard_out,
+                              float* shard_lse, float* out, float* lse, void* ws, hipStream_t s);
 
 }  // namespace hs

@@ -37,6 +37,7 @@ constexpr int kMlaNT = 256;
 constexpr int kMlaTargetWGs = 256;   // splits of the selected rows fill about this many workgroups
 constexpr int kMlaMaxSplitRows = 1024;   // and no slice walks more than 16 tiles
 constexpr int kMlaRing = 4;              // tiles of row gathers in flight per workgroup
+constexpr int kMaxShards = 64;           // token shards of the sharded attention
 constexpr int kTile = 64;
 constexpr int kPtStride = 72;
 constexpr int kHq = 16;
@@ -71,7 +72,8 @@ __global__ __launch_bounds__(kMlaNT, 1) void mla_bf16_e4m3_kernel(
     const float* __restrict__ row_scale, const int32_t* __restrict__ row_ids, int K,
     int rows_per_split, int nsplit, float qk_scale_log2, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int64_t pool_layer_rows) {
+    int64_t pool_layer_rows, int hgroups, const int32_t* __restrict__ chunk_lo,
+    const int32_t* __restrict__ chunk_hi) {
   // per wave: the value parts of its current two 16-row tiles (bf16, row-major);
   // once every wave is done with its rows, the same memory holds the four
   // waves' output partials for the in-workgroup merge
@@ -84,7 +86,11 @@ __global__ __launch_bounds__(kMlaNT, 1) void mla_bf16_e4m3_kernel(
   __shared__ uint4 s_q[kHq * (kQRow + 1)];
   static_assert(sizeof(stash) >= 4 * kHq * kDVal * sizeof(float), "the merge reuses the stash");
 
+  // blockIdx.y = (request position) * hgroups + (group of 16 heads): the
+  // queries, outputs and partials of that head group; the row ids are the
+  // request position's, shared by its head groups
   const int bp = blockIdx.y, split = blockIdx.x;
+  const int rbp = bp / hgroups;
   // layer blockIdx.z of a multi-layer call: its queries, pool rows, scales,
   // outputs and partials sit one layer stride further (same row ids)
   {
@@ -102,10 +108,17 @@ __global__ __launch_bounds__(kMlaNT, 1) void mla_bf16_e4m3_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;
-  // the slice [kb, kb + nrows) of the selection; wave w takes its quarter
-  // [w0, w1), in 16-row tiles (rows_per_split is a multiple of 64)
-  const int kb = split * rows_per_split;
-  const int nrows = max(min(K, kb + rows_per_split) - kb, 0);
+  // the slice [kb, kb + nrows) of the selection: split * rows_per_split on,
+  // or the chunk of a chunk list (at most rows_per_split rows); wave w takes
+  // its quarter [w0, w1), in 16-row tiles (rows_per_split is a multiple of 64)
+  int kb, nrows;
+  if (chunk_lo) {
+    kb = min(max(chunk_lo[(size_t)rbp * nsplit + split], 0), K);
+    nrows = min(max(chunk_hi[(size_t)rbp * nsplit + split] - kb, 0), min(rows_per_split, K - kb));
+  } else {
+    kb = split * rows_per_split;
+    nrows = max(min(K, kb + rows_per_split) - kb, 0);
+  }
   const int per_wave = rows_per_split / 4;
   const int w0 = min(wave * per_wave, nrows), w1 = min(w0 + per_wave, nrows);
   const int ntiles = (w1 - w0 + 15) / 16;
@@ -123,7 +136,7 @@ __global__ __launch_bounds__(kMlaNT, 1) void mla_bf16_e4m3_kernel(
   const uint4* qg = reinterpret_cast<const uint4*>(q + (size_t)bp * kHq * kDLat);
   uint4 qv[kQPer];
   {
-    const int32_t* rp = row_ids + (size_t)bp * K + kb + w0;
+    const int32_t* rp = row_ids + (size_t)rbp * K + kb + w0;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = lane + u * kWave;
@@ -367,22 +380,30 @@ __global__ __launch_bounds__(kMlaNT) void mla_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ pool, const int32_t* __restrict__ row_ids,
     int K, int rows_per_split, int nsplit, float qk_scale_log2, int split_mode,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, int hgroups, const int32_t* __restrict__ chunk_lo,
+    const int32_t* __restrict__ chunk_hi) {
   __shared__ float Qs[kHq][kDLat];
   __shared__ float Xs[16][kDLat];
   __shared__ float Ps[kHq][16];
   __shared__ int Rs[16];
-  const int bp = blockIdx.y, split = blockIdx.x;
+  const int bp = blockIdx.y, split = blockIdx.x;   // as in the bf16 kernel
+  const int rbp = bp / hgroups;
   const int tid = threadIdx.x;
   const int h = tid >> 4, r = tid & 15;       // logits: (head, row); PV: (head, dim group)
-  const int kb = split * rows_per_split;
-  const int ke = min(K, kb + rows_per_split);
+  int kb, ke;
+  if (chunk_lo) {
+    kb = min(max(chunk_lo[(size_t)rbp * nsplit + split], 0), K);
+    ke = min(max(chunk_hi[(size_t)rbp * nsplit + split], kb), min(kb + rows_per_split, K));
+  } else {
+    kb = split * rows_per_split;
+    ke = min(K, kb + rows_per_split);
+  }
   for (int i = tid; i < kHq * kDLat; i += kMlaNT) Qs[i / kDLat][i % kDLat] = q[(size_t)bp * kHq * kDLat + i];
   float acc[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) acc[j] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const int32_t* rid_p = row_ids + (size_t)bp * K;
+  const int32_t* rid_p = row_ids + (size_t)rbp * K;
   for (int kt = kb; kt < ke; kt += 16) {
     __syncthreads();
     if (tid < 16) Rs[tid] = (kt + tid < ke) ? rid_p[kt + tid] : -1;
@@ -530,14 +551,164 @@ __host__ inline int rows_per_split_for(int K, int nsplit) {
   return (r + kTile - 1) / kTile * kTile;
 }
 
+// ---- token-sharded attention (several GPUs splitting the cache by tokens,
+// emulated on one): the selected rows each shard owns are a contiguous range
+// of the ascending top-K, attended in chunks of at most kShardChunk rows
+
+constexpr int kShardChunk = 256;   // rows per workgroup: each wave's 64 rows fit its ring
+
+// One workgroup per request position: the boundaries of its shards' ranges in
+// the top-K list (entry k is in shard topk[k] / shard_len; -1 entries end the
+// list), then the chunk list: the chunks of shard 0, then shard 1, ...,
+// chunk_first[s] the first chunk of shard s, empty chunks up to cmax.
+__global__ __launch_bounds__(256) void shard_chunks_kernel(const int32_t* __restrict__ topk, int K,
+                                                           int S, int shard_len, int cmax,
+                                                           int32_t* __restrict__ chunk_lo,
+                                                           int32_t* __restrict__ chunk_hi,
+                                                           int32_t* __restrict__ chunk_first) {
+  __shared__ int s_bounds[kMaxShards + 1];
+  __shared__ int s_total;
+  const int bp = blockIdx.x, tid = threadIdx.x;
+  const int32_t* t = topk + (size_t)bp * K;
+  for (int i = tid; i <= S; i += 256) s_bounds[i] = 0;
+  __syncthreads();
+  auto shard_of = [&](int k) {
+    const int tok = t[k];
+    return tok >= 0 ? min(tok / shard_len, S) : S;
+  };
+  // entry k starts shards prev+1 .. cur (each shard's start is written once
+  // when the list is ascending)
+  for (int k = tid; k <= K; k += 256) {
+    const int cur = k < K ? shard_of(k) : S;
+    const int prev = k > 0 ? shard_of(k - 1) : -1;
+    for (int sh = prev + 1; sh <= min(cur, S); ++sh) s_bounds[sh] = k;
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    int lo = 0, hi = 0, nch = 0;
+    if (tid < S) {
+      lo = min(max(s_bounds[tid], 0), K);
+      hi = max(min(max(s_bounds[tid + 1], 0), K), lo);
+      nch = (hi - lo + kShardChunk - 1) / kShardChunk;
+    }
+    // an ascending list needs at most K / kShardChunk + S chunks (cmax); the
+    // clamps keep any other list's chunks inside the arrays
+    const int incl = wave_inclusive_scan_i32(nch);
+    const int first = min(incl - nch, cmax);
+    const int last = min(incl, cmax);
+    if (tid < S) {
+      chunk_first[(size_t)bp * (S + 1) + tid] = first;
+      for (int j = 0; j < last - first; ++j) {
+        chunk_lo[(size_t)bp * cmax + first + j] = lo + j * kShardChunk;
+        chunk_hi[(size_t)bp * cmax + first + j] = min(hi, lo + (j + 1) * kShardChunk);
+      }
+    }
+    const int total = min(__builtin_amdgcn_readlane(incl, kWave - 1), cmax);
+    if (tid == 0) {
+      chunk_first[(size_t)bp * (S + 1) + S] = total;
+      s_total = total;
+    }
+  }
+  __syncthreads();
+  for (int c = s_total + tid; c < cmax; c += 256) {
+    chunk_lo[(size_t)bp * cmax + c] = 0;
+    chunk_hi[(size_t)bp * cmax + c] = 0;
+  }
+}
+
+// Per (request position, shard, head, half of the dims), one wave: the shard's
+// chunks merged in chunk order into the shard's normalised output and its
+// log-sum-exp (natural log), as one GPU of a token-sharded cache hands them
+// over; a shard with no selected row gives 0 and -inf.
+__global__ __launch_bounds__(kWave) void shard_merge_kernel(int S, int Hq, int cmax,
+                                                            const int32_t* __restrict__ chunk_first,
+                                                            const float* __restrict__ part_o,
+                                                            const float* __restrict__ part_ml,
+                                                            float* __restrict__ shard_out,
+                                                            float* __restrict__ shard_lse) {
+  const int bp = blockIdx.x / S, sh = blockIdx.x % S, h = blockIdx.y, half = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int pbp = bp * (Hq / kHq) + h / kHq, hl = h % kHq;
+  const int c0 = chunk_first[(size_t)bp * (S + 1) + sh];
+  // at most K / kShardChunk <= 32 chunks for an ascending list; a lane each
+  const int nc = min(chunk_first[(size_t)bp * (S + 1) + sh + 1] - c0, kWave);
+  auto ml = [&](int c) { return part_ml + (((size_t)pbp * cmax + c0 + c) * kHq + hl) * 2; };
+  const float m = lane < nc ? ml(lane)[0] : -INFINITY;
+  const float l = lane < nc ? ml(lane)[1] : 0.f;
+  float M = max_rows16(m);
+  M = fmaxf(M, __shfl_xor(M, 1));
+  M = fmaxf(M, __shfl_xor(M, 2));
+  M = fmaxf(M, __shfl_xor(M, 4));
+  M = fmaxf(M, __shfl_xor(M, 8));
+  const float w = (M != -INFINITY && m != -INFINITY) ? exp2f(m - M) : 0.f;
+  float L = sum_rows16(l * w);
+  L += __shfl_xor(L, 1);
+  L += __shfl_xor(L, 2);
+  L += __shfl_xor(L, 4);
+  L += __shfl_xor(L, 8);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = 0; c < nc; ++c) {
+    const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
+    const float4 v = reinterpret_cast<const float4*>(
+        part_o + (((size_t)pbp * cmax + c0 + c) * kHq + hl) * kDVal + 256 * half)[lane];
+    acc.x = fmaf(v.x, wc, acc.x);
+    acc.y = fmaf(v.y, wc, acc.y);
+    acc.z = fmaf(v.z, wc, acc.z);
+    acc.w = fmaf(v.w, wc, acc.w);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  reinterpret_cast<float4*>(shard_out + (((size_t)bp * S + sh) * Hq + h) * kDVal + 256 * half)[lane] =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (half == 0 && lane == 0)
+    shard_lse[((size_t)bp * S + sh) * Hq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+// Per (request position, head, half of the dims), one wave: the S shards'
+// outputs merged in shard order by their log-sum-exp weights,
+// out = sum_s e^(lse_s - LSE) out_s with LSE = ln sum_s e^(lse_s).
+__global__ __launch_bounds__(kWave) void shard_lse_combine_kernel(int S, int Hq,
+                                                                  const float* __restrict__ shard_out,
+                                                                  const float* __restrict__ shard_lse,
+                                                                  float* __restrict__ out,
+                                                                  float* __restrict__ lse) {
+  const int bp = blockIdx.x, h = blockIdx.y, half = blockIdx.z, lane = threadIdx.x;
+  const float ls = lane < S ? shard_lse[((size_t)bp * S + lane) * Hq + h] : -INFINITY;
+  float M = max_rows16(ls);
+  M = fmaxf(M, __shfl_xor(M, 1));
+  M = fmaxf(M, __shfl_xor(M, 2));
+  M = fmaxf(M, __shfl_xor(M, 4));
+  M = fmaxf(M, __shfl_xor(M, 8));
+  const float w = (M != -INFINITY && ls != -INFINITY) ? expf(ls - M) : 0.f;
+  float L = sum_rows16(w);
+  L += __shfl_xor(L, 1);
+  L += __shfl_xor(L, 2);
+  L += __shfl_xor(L, 4);
+  L += __shfl_xor(L, 8);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sh = 0; sh < S; ++sh) {
+    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sh));
+    const float4 v = reinterpret_cast<const float4*>(
+        shard_out + (((size_t)bp * S + sh) * Hq + h) * kDVal + 256 * half)[lane];
+    acc.x = fmaf(v.x, ws, acc.x);
+    acc.y = fmaf(v.y, ws, acc.y);
+    acc.z = fmaf(v.z, ws, acc.z);
+    acc.w = fmaf(v.w, ws, acc.w);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  reinterpret_cast<float4*>(out + ((size_t)bp * Hq + h) * kDVal + 256 * half)[lane] =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (lse && half == 0 && lane == 0)
+    lse[(size_t)bp * Hq + h] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
 }  // namespace
 
-// Splits of the K rows so that one launch of L layers fills about
-// kMlaTargetWGs workgroups, with at most kMlaMaxSplitRows rows per slice (a
-// slice's tiles run one after another: at 256 request-positions one slice
+// Splits of the K rows so that one launch of L layers and G head groups fills
+// about kMlaTargetWGs workgroups, with at most kMlaMaxSplitRows rows per slice
+// (a slice's tiles run one after another: at 256 request-positions one slice
 // each would walk 32 tiles).
-int mla_num_splits(int B, int P, int K, int L) {
-  const int BPL = B * P * L;
+int mla_num_splits(int B, int P, int K, int L, int G) {
+  const int BPL = B * P * L * G;
   const int max_split = (K + kTile - 1) / kTile;
   static_assert(8192 / kTile <= kCombineMaxSplit, "one lane per slice in the combine");
   int ns = (kMlaTargetWGs + BPL - 1) / BPL;
@@ -549,65 +720,132 @@ int mla_num_splits(int B, int P, int K, int L) {
 }
 
 size_t mla_workspace_bytes(int B, int P, int K, int Hq, int L) {
-  const int ns = mla_num_splits(B, P, K, L);
+  const int G = Hq / kHq;
+  const int ns = mla_num_splits(B, P, K, L, G);
   if (ns <= 1) return 0;
   const size_t parts = (size_t)L * B * P * ns * Hq;
   return parts * kDVal * 4 + parts * 2 * 4;
 }
 
-hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, int L, int64_t pool_layer_rows,
+hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, int L, int Hq, int64_t pool_layer_rows,
                                 const uint16_t* q, const uint8_t* pool, const float* row_scale,
                                 const int32_t* row_ids, float sm_scale, float* out, float* lse,
                                 void* ws, hipStream_t s) {
-  const int BP = d.B * d.P;
-  const int ns = mla_num_splits(d.B, d.P, K, L);
+  const int G = Hq / kHq;
+  const int BPG = d.B * d.P * G;
+  const int ns = mla_num_splits(d.B, d.P, K, L, G);
   const int rps = rows_per_split_for(K, ns);
   const float qk = sm_scale * kLog2e;
   if (ns == 1) {
-    hipLaunchKernelGGL((mla_bf16_e4m3_kernel<false>), dim3(1, BP, L), dim3(kMlaNT), 0, s, q, pool,
-                       row_scale, row_ids, K, rps, 1, qk, out, lse, nullptr, nullptr,
-                       pool_layer_rows);
+    hipLaunchKernelGGL((mla_bf16_e4m3_kernel<false>), dim3(1, BPG, L), dim3(kMlaNT), 0, s, q,
+                       pool, row_scale, row_ids, K, rps, 1, qk, out, lse, nullptr, nullptr,
+                       pool_layer_rows, G, nullptr, nullptr);
     return hipGetLastError();
   }
   float* part_o = static_cast<float*>(ws);
-  float* part_ml = part_o + (size_t)L * BP * ns * kHq * kDVal;
-  hipLaunchKernelGGL((mla_bf16_e4m3_kernel<true>), dim3(ns, BP, L), dim3(kMlaNT), 0, s, q, pool,
+  float* part_ml = part_o + (size_t)L * BPG * ns * kHq * kDVal;
+  hipLaunchKernelGGL((mla_bf16_e4m3_kernel<true>), dim3(ns, BPG, L), dim3(kMlaNT), 0, s, q, pool,
                      row_scale, row_ids, K, rps, ns, qk, out, lse, part_o, part_ml,
-                     pool_layer_rows);
+                     pool_layer_rows, G, nullptr, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq, 2 * L), dim3(kWave), 0, s, ns, part_o,
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(BPG, kHq, 2 * L), dim3(kWave), 0, s, ns, part_o,
                      part_ml, out, lse);
   return hipGetLastError();
 }
 
-hipError_t launch_mla_f32(const BatchDims& d, int K, int L, int64_t pool_layer_rows,
+hipError_t launch_mla_f32(const BatchDims& d, int K, int L, int Hq, int64_t pool_layer_rows,
                           const float* q, const float* pool, const int32_t* row_ids,
                           float sm_scale, float* out, float* lse, void* ws, hipStream_t s) {
-  const int BP = d.B * d.P;
-  const int ns = mla_num_splits(d.B, d.P, K, L);
+  const int G = Hq / kHq;
+  const int BPG = d.B * d.P * G;
+  const int ns = mla_num_splits(d.B, d.P, K, L, G);
   const int rps = rows_per_split_for(K, ns);
   const float qk = sm_scale * kLog2e;
   // one launch per layer; the layers reuse the first layer's partials (same stream)
   float* part_o = static_cast<float*>(ws);
-  float* part_ml = ns > 1 ? part_o + (size_t)BP * ns * kHq * kDVal : nullptr;
+  float* part_ml = ns > 1 ? part_o + (size_t)BPG * ns * kHq * kDVal : nullptr;
   for (int l = 0; l < L; ++l) {
-    const float* ql = q + (size_t)l * BP * kHq * kDLat;
+    const float* ql = q + (size_t)l * BPG * kHq * kDLat;
     const float* pl = pool + (size_t)l * pool_layer_rows * kDLat;
-    float* ol = out + (size_t)l * BP * kHq * kDVal;
-    float* ll = lse ? lse + (size_t)l * BP * kHq : nullptr;
-    hipLaunchKernelGGL(mla_f32_kernel, dim3(ns, BP), dim3(kMlaNT), 0, s, ql, pl, row_ids, K, rps,
-                       ns, qk, ns > 1 ? 1 : 0, ol, ll, part_o, part_ml);
+    float* ol = out + (size_t)l * BPG * kHq * kDVal;
+    float* ll = lse ? lse + (size_t)l * BPG * kHq : nullptr;
+    hipLaunchKernelGGL(mla_f32_kernel, dim3(ns, BPG), dim3(kMlaNT), 0, s, ql, pl, row_ids, K, rps,
+                       ns, qk, ns > 1 ? 1 : 0, ol, ll, part_o, part_ml, G, nullptr, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ns > 1) {
-      hipLaunchKernelGGL(mla_combine_kernel, dim3(BP, kHq, 2), dim3(kWave), 0, s, ns, part_o,
+      hipLaunchKernelGGL(mla_combine_kernel, dim3(BPG, kHq, 2), dim3(kWave), 0, s, ns, part_o,
                          part_ml, ol, ll);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
   return hipSuccess;
+}
+
+namespace {
+struct ShardWs {
+  int cmax;
+  int32_t *chunk_lo, *chunk_hi, *chunk_first;
+  float *part_o, *part_ml;
+};
+__host__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+__host__ inline ShardWs shard_ws(void* base, int BP, int K, int S, int Hq) {
+  ShardWs w;
+  w.cmax = (K + kShardChunk - 1) / kShardChunk + S;
+  char* p = static_cast<char*>(base);
+  const size_t nc = (size_t)BP * w.cmax;
+  w.chunk_lo = reinterpret_cast<int32_t*>(p);
+  p += align256(nc * 4);
+  w.chunk_hi = reinterpret_cast<int32_t*>(p);
+  p += align256(nc * 4);
+  w.chunk_first = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)BP * (S + 1) * 4);
+  w.part_o = reinterpret_cast<float*>(p);
+  p += align256(nc * Hq * kDVal * 4);
+  w.part_ml = reinterpret_cast<float*>(p);
+  p += align256(nc * Hq * 2 * 4);
+  return w;
+}
+}  // namespace
+
+size_t mla_sharded_workspace_bytes(int B, int P, int K, int S, int Hq) {
+  ShardWs w = shard_ws(nullptr, B * P, K, S, Hq);
+  return reinterpret_cast<size_t>(w.part_ml) +
+         align256((size_t)B * P * w.cmax * Hq * 2 * 4);
+}
+
+hipError_t launch_mla_sharded(const BatchDims& d, int K, int S, int Hq, bool f32, const void* q,
+                              const void* pool, const float* row_scale, const int32_t* topk,
+                              const int32_t* row_ids, float sm_scale, float* shard_out,
+                              float* shard_lse, float* out, float* lse, void* ws, hipStream_t s) {
+  const int BP = d.B * d.P, G = Hq / kHq;
+  ShardWs w = shard_ws(ws, BP, K, S, Hq);
+  const float qk = sm_scale * kLog2e;
+  hipLaunchKernelGGL(shard_chunks_kernel, dim3(BP), dim3(256), 0, s, topk, K, S, d.T_stride / S,
+                     w.cmax, w.chunk_lo, w.chunk_hi, w.chunk_first);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (f32)
+    hipLaunchKernelGGL(mla_f32_kernel, dim3(w.cmax, BP * G), dim3(kMlaNT), 0, s,
+                       static_cast<const float*>(q), static_cast<const float*>(pool), row_ids, K,
+                       kShardChunk, w.cmax, qk, 1, nullptr, nullptr, w.part_o, w.part_ml, G,
+                       w.chunk_lo, w.chunk_hi);
+  else
+    hipLaunchKernelGGL((mla_bf16_e4m3_kernel<true>), dim3(w.cmax, BP * G, 1), dim3(kMlaNT), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(pool),
+                       row_scale, row_ids, K, kShardChunk, w.cmax, qk, nullptr, nullptr, w.part_o,
+                       w.part_ml, (int64_t)0, G, w.chunk_lo, w.chunk_hi);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(shard_merge_kernel, dim3(BP * S, Hq, 2), dim3(kWave), 0, s, S, Hq, w.cmax,
+                     w.chunk_first, w.part_o, w.part_ml, shard_out, shard_lse);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(shard_lse_combine_kernel, dim3(BP, Hq, 2), dim3(kWave), 0, s, S, Hq,
+                     shard_out, shard_lse, out, lse);
+  return hipGetLastError();
 }
 
 }  // namespace hs

@@ -343,7 +343,8 @@ hs_status hs_copy_faults(const hs_batch* batch, int32_t K, const hs_residency* r
  *   pool    [rows, 576] one layer's rows; row_scale [rows] fp32 (E4M3 only,
  *           NULL for F32)
  *   out     [B, P, Hq, 512] fp32; lse [B, P, Hq] fp32 or NULL
- * Hq = 16 (one head shard).  1 <= K <= 8192.
+ * Hq is a multiple of 16 in [16, 128]: the heads one GPU holds, taken by the
+ * kernels in groups of 16 that share every row gather.  1 <= K <= 8192.
  * Workspace: hs_workspace_bytes(HS_OP_MLA, ...). */
 hs_status hs_sparse_mla_decode(const hs_batch* batch, int32_t K, int32_t Hq, hs_dtype q_t,
                                const void* q, hs_dtype kv_t, const void* pool,
@@ -372,6 +373,37 @@ hs_status hs_sparse_mla_decode_layers(const hs_batch* batch, int32_t K, int32_t 
                                       float sm_scale, float* out, float* lse, void* ws,
                                       size_t ws_bytes, void* stream);
 size_t hs_mla_layers_workspace_bytes(int32_t B, int32_t P, int32_t K, int32_t Hq, int32_t L);
+
+/* Token-sharded attention: the attention as a KV cache split across GPUs by
+ * tokens computes it (page "vLLM sert GLM-5.3 en contexte 1M sur 16 H200",
+ * section "Le mécanisme": DCP splits the KV cache by tokens across GPUs and
+ * gathers the fragments at every layer), emulated on one GPU.  Each request's
+ * tokens are cut into S contiguous shards of T_stride / S tokens; shard s
+ * attends over the selected tokens it holds and hands over its fragment, and
+ * the fragments are merged in shard order by their log-sum-exp:
+ *   shard_out[b,p,s,h,:], shard_lse[b,p,s,h]: hs_sparse_mla_decode's out and
+ *       lse over the entries j of topk[b,p,:] with topk[b,p,j] / (T_stride/S)
+ *       = s (0 and -inf for a shard with none);
+ *   lse[b,p,h] = ln sum_s exp(shard_lse[b,p,s,h]),
+ *   out[b,p,h,:] = sum_s exp(shard_lse[b,p,s,h] - lse[b,p,h]) shard_out[b,p,s,h,:]
+ * which is the unsharded attention up to rounding.
+ *   topk    [B, P, K] token ids in ascending order, -1 entries last (hs_topk's
+ *           or hs_topk_sharded's output): they say which shard holds each row;
+ *           another order gives unspecified (but in-bounds) results
+ *   row_ids [B, P, K] pool rows of those tokens (-1 = skipped), as for
+ *           hs_sparse_mla_decode; q, pool, row_scale, out, lse likewise
+ *   shard_out [B, P, S, Hq, 512] fp32 output, shard_lse [B, P, S, Hq] fp32 output
+ * 1 <= S <= 64 and S divides T_stride; Hq a multiple of 16 in [16, 128];
+ * 1 <= K <= 8192.  Workspace: hs_mla_sharded_workspace_bytes(B, P, K, S, Hq),
+ * 16-byte aligned; its contents on entry do not matter. */
+hs_status hs_sparse_mla_decode_sharded(const hs_batch* batch, int32_t K, int32_t S, int32_t Hq,
+                                       hs_dtype q_t, const void* q, hs_dtype kv_t,
+                                       const void* pool, const float* row_scale,
+                                       const int32_t* topk, const int32_t* row_ids,
+                                       float sm_scale, float* shard_out, float* shard_lse,
+                                       float* out, float* lse, void* ws, size_t ws_bytes,
+                                       void* stream);
+size_t hs_mla_sharded_workspace_bytes(int32_t B, int32_t P, int32_t K, int32_t S, int32_t Hq);
 
 #define HS_OP_INDEXER 0
 #define HS_OP_TOPK 1

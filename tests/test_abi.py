@@ -115,11 +115,30 @@ def test_host_validation_rejects_bad_arguments_without_launching():
     res.C = 100
     assert lib.hs_resolve_rows(ctypes.byref(b), 64, fake, ctypes.byref(res), fake, fake, fake,
                                None, 0, None) == 2
-    # attention: one shard of 16 heads; workspace
-    assert lib.hs_sparse_mla_decode(ctypes.byref(b), 2048, 32, 1, fake, 2, fake, fake, fake,
-                                    0.1, fake, None, None, 0, None) == 2
-    assert lib.hs_sparse_mla_decode(ctypes.byref(b), 2048, 16, 1, fake, 2, fake, fake, fake,
-                                    0.1, fake, None, None, 0, None) == 5
+    # attention: heads in groups of 16, at most 128; workspace
+    for bad_hq in (8, 24, 144):
+        assert lib.hs_sparse_mla_decode(ctypes.byref(b), 2048, bad_hq, 1, fake, 2, fake, fake,
+                                        fake, 0.1, fake, None, None, 0, None) == 2
+    for hq in (16, 32, 128):
+        assert lib.hs_sparse_mla_decode(ctypes.byref(b), 2048, hq, 1, fake, 2, fake, fake, fake,
+                                        0.1, fake, None, None, 0, None) == 5
+    assert lib.hs_mla_layers_workspace_bytes(8, 1, 2048, 24, 1) == 0
+    # token-sharded attention: S in [1, 64] dividing T_stride, outputs required
+    def sharded(K=2048, S=4, Hq=16, q_t=1, kv_t=2, rs=fake, so=fake, ws=None, ws_bytes=0):
+        return lib.hs_sparse_mla_decode_sharded(ctypes.byref(b), K, S, Hq, q_t, fake, kv_t, fake,
+                                                rs, fake, fake, 0.1, so, fake, fake, None, ws,
+                                                ws_bytes, None)
+    assert sharded(S=0) == 2 and sharded(S=65) == 2 and sharded(S=3) == 2
+    assert sharded(Hq=40) == 2 and sharded(K=8193) == 2
+    assert sharded(so=None) == 1
+    assert sharded() == 5
+    need = lib.hs_mla_sharded_workspace_bytes(2, 1, 2048, 4, 16)
+    assert need > 0 and lib.hs_mla_sharded_workspace_bytes(8, 1, 2048, 65, 16) == 0
+    big = ctypes.c_void_p(1 << 20)
+    assert sharded(ws=big, ws_bytes=need - 1) == 5
+    assert sharded(q_t=0, ws=big, ws_bytes=need) == 3
+    assert sharded(q_t=0, kv_t=0, ws=big, ws_bytes=need) == 3     # F32 rows take no scale
+    assert sharded(rs=None, ws=big, ws_bytes=need) == 1           # E4M3 rows need scales
 
 
 def test_cache_operations_validate_on_the_host():
