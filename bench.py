@@ -432,6 +432,15 @@ def main():
                     help="request chunks of the pipelined step (1 = one stream, no overlap)")
     ap.add_argument("--copy-wgs", type=int, default=32,
                     help="workgroups of the fault copy in the pipelined step")
+    ap.add_argument("--layer-pipeline", action="store_true",
+                    help="layers of the shared selection overlapped: fault copies layer by "
+                         "layer on a second stream, each layer's attention as soon as its rows "
+                         "are in (workloads with several layers)")
+    ap.add_argument("--layer-groups", type=int, default=0,
+                    help="layer groups of --layer-pipeline (a divisor of L; 0 = one per layer)")
+    ap.add_argument("--layer-copy-wgs", type=int, default=0,
+                    help="workgroups of each layer's fault copy with --layer-pipeline "
+                         "(0 = every compute unit)")
     ap.add_argument("--topk-shards", type=int, default=0,
                     help="also time the token-sharded top-K with this many shards (P = 1)")
     ap.add_argument("--cache-ops", action="store_true",
@@ -450,8 +459,8 @@ def main():
                          "head every step (fp8 x fp8 matrix cores)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path does not "
-              "shard across GPUs in this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}): the sharded top-K "
+              "and attention emulate the shards of several GPUs on one.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -483,11 +492,13 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] device state ready at {time.time() - t0:.1f}s")
 
-    def step_eager(nchunks):
-        if nchunks == 1:
+    def step_eager(mode):
+        if mode == "layers":
+            ds.run_layer_pipelined(a.layer_copy_wgs, a.layer_groups)
+        elif mode == 1:
             ds.run()
         else:
-            ds.run_pipelined(nchunks, a.copy_wgs)
+            ds.run_pipelined(mode, a.copy_wgs)
 
     def capture(nchunks):
         g = torch.cuda.CUDAGraph()
@@ -504,13 +515,14 @@ def main():
         torch.cuda.synchronize()
         return g
 
+    mode = "layers" if a.layer_pipeline else a.chunks
     if a.no_graph:
-        step_fn = lambda: step_eager(a.chunks)
+        step_fn = lambda: step_eager(mode)
         single_fn = lambda: step_eager(1)
     else:
-        graph = capture(a.chunks)
+        graph = capture(mode)
         step_fn = graph.replay
-        single_graph = capture(1) if a.chunks != 1 else graph
+        single_graph = capture(1) if mode != 1 else graph
         single_fn = single_graph.replay
     for _ in range(a.warmup):
         restore()
@@ -649,6 +661,9 @@ def main():
                    "indexer_queries": ds.indexer_q, "host_layout": ds.host_layout,
                    "append_loop": a.append,
                    "graph": not a.no_graph, "pipeline_chunks": a.chunks,
+                   "layer_pipeline": a.layer_pipeline,
+                   "layer_copy_workgroups": a.layer_copy_wgs if a.layer_pipeline else None,
+                   "layer_groups": (a.layer_groups or wl.L) if a.layer_pipeline else None,
                    "pipeline_copy_workgroups": a.copy_wgs if a.chunks > 1 else None},
         "roofline": {"bound": "hbm",
                      "kernel": ("indexer_e4m3_kernel" if e4m3 else "indexer_bf16_e4m3_kernel")

@@ -23,7 +23,7 @@ DEVERR_APPEND_RANGE, DEVERR_APPEND_NO_BLOCK, DEVERR_DEMOTE_FULL = 4, 8, 16
 
 EXPORTS = ["hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk",
            "hs_indexer_topk_noalloc", "hs_indexer_topk_scores", "hs_indexer_topk_select",
-           "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults",
+           "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults", "hs_copy_faults_layers",
            "hs_sparse_mla_decode", "hs_sparse_mla_decode_layers", "hs_mla_layers_workspace_bytes",
            "hs_topk_sharded", "hs_topk_sharded_workspace_bytes",
            "hs_sparse_mla_decode_sharded", "hs_mla_sharded_workspace_bytes",
@@ -87,6 +87,7 @@ def load() -> ctypes.CDLL:
     lib.hs_resolve_rows.argtypes = [P, c_int32, P, P, P, P, P, P, c_size_t, P]
     lib.hs_resolve_tables.argtypes = [P, c_int32, P, P, P, P, P, P]
     lib.hs_copy_faults.argtypes = [P, c_int32, P, P, P, c_int32, P]
+    lib.hs_copy_faults_layers.argtypes = [P, c_int32, P, P, P, c_int32, c_int32, c_int32, P]
     lib.hs_sparse_mla_decode.argtypes = [P, c_int32, c_int32, c_int32, P, c_int32, P, P, P,
                                          c_float, P, P, P, c_size_t, P]
     lib.hs_sparse_mla_decode_layers.argtypes = [P, c_int32, c_int32, c_int32, c_int32, P, c_int32,
@@ -110,8 +111,8 @@ def load() -> ctypes.CDLL:
         getattr(lib, f).restype = c_int32
     for f in ("hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_topk",
               "hs_indexer_topk_noalloc", "hs_indexer_topk_scores", "hs_indexer_topk_select",
-           "hs_resolve_rows", "hs_resolve_tables",
-              "hs_copy_faults", "hs_sparse_mla_decode", "hs_host_device_ptr"):
+              "hs_resolve_rows", "hs_resolve_tables", "hs_copy_faults", "hs_copy_faults_layers",
+              "hs_sparse_mla_decode", "hs_host_device_ptr"):
         getattr(lib, f).restype = c_int32
     lib.hs_workspace_bytes.argtypes = [c_int32] * 6
     lib.hs_workspace_bytes.restype = c_size_t
@@ -230,6 +231,13 @@ def copy_faults(batch: Batch, K: int, res: Residency, faults, counts, workgroups
                 stream=None):
     _check(load().hs_copy_faults(ctypes.byref(batch), K, ctypes.byref(res), _ptr(faults),
                                  _ptr(counts), workgroups, _stream(stream)))
+
+
+def copy_faults_layers(batch: Batch, K: int, res: Residency, faults, counts, layer0: int,
+                       n_layers: int, workgroups: int = 0, stream=None):
+    _check(load().hs_copy_faults_layers(ctypes.byref(batch), K, ctypes.byref(res), _ptr(faults),
+                                        _ptr(counts), layer0, n_layers, workgroups,
+                                        _stream(stream)))
 
 
 def sparse_mla_decode(batch: Batch, K: int, Hq: int, q_t: str, q, kv_t: str, pool, row_scale,

@@ -412,9 +412,9 @@ hs_status hs_resolve_tables(const hs_batch* batch, int32_t K, const int32_t* top
                   "resolve");
 }
 
-hs_status hs_copy_faults(const hs_batch* batch, int32_t K, const hs_residency* res,
-                         const int32_t* faults, const int32_t* counts, int32_t workgroups,
-                         void* stream) {
+hs_status hs_copy_faults_layers(const hs_batch* batch, int32_t K, const hs_residency* res,
+                                const int32_t* faults, const int32_t* counts, int32_t layer0,
+                                int32_t n_layers, int32_t workgroups, void* stream) {
   hs::BatchDims d;
   if (hs_status st = check_batch(batch, &d)) return st;
   if (!faults || !counts) return fail(HS_ERR_NULL, "hs_copy_faults: faults and counts are required");
@@ -422,9 +422,19 @@ hs_status hs_copy_faults(const hs_batch* batch, int32_t K, const hs_residency* r
     return fail(HS_ERR_SHAPE, "hs_copy_faults: workgroups=%d out of [0, 1024]", workgroups);
   hs::ResidencyArgs r;
   if (hs_status st = check_residency(d, K, res, &r)) return st;
-  return launched(hs::launch_fault_copy(d, K, r, faults, counts, workgroups,
+  if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > r.L)
+    return fail(HS_ERR_SHAPE, "hs_copy_faults_layers: layers [%d, %d) outside [0, L=%d)", layer0,
+                layer0 + n_layers, r.L);
+  return launched(hs::launch_fault_copy(d, K, r, faults, counts, layer0, n_layers, workgroups,
                                         static_cast<hipStream_t>(stream)),
                   "fault copy");
+}
+
+hs_status hs_copy_faults(const hs_batch* batch, int32_t K, const hs_residency* res,
+                         const int32_t* faults, const int32_t* counts, int32_t workgroups,
+                         void* stream) {
+  const int32_t L = res ? res->L : 1;
+  return hs_copy_faults_layers(batch, K, res, faults, counts, 0, L, workgroups, stream);
 }
 
 hs_status hs_resolve_rows(const hs_batch* batch, int32_t K, const int32_t* topk,

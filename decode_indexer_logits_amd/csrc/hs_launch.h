@@ -66,10 +66,11 @@ struct ResidencyArgs {
 hipError_t launch_resolve_tables(const BatchDims& d, int K, const int32_t* topk,
                                  const ResidencyArgs& r, int32_t* row_ids, int32_t* faults,
                                  int32_t* counts, hipStream_t s);
-// workgroups = 0: the default grid (every CU)
+// Layers l0 .. l0 + nl - 1 of every fault (the call with l0 + nl == L advances
+// the step); workgroups = 0: the default grid (every CU)
 hipError_t launch_fault_copy(const BatchDims& d, int K, const ResidencyArgs& r,
-                             const int32_t* faults, const int32_t* counts, int workgroups,
-                             hipStream_t s);
+                             const int32_t* faults, const int32_t* counts, int l0, int nl,
+                             int workgroups, hipStream_t s);
 
 // Device error bits of the cache operations (the HS_DEVERR_* values of hs.h).
 constexpr int kDevErrAppendRange = 4;

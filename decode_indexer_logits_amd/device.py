@@ -254,6 +254,49 @@ class DeviceStep:
         else:
             self.run_attention(0, stream)
 
+    def run_layer_pipelined(self, copy_workgroups: int = 0, groups: int = 0):
+        """One decode step with the layers of one shared selection overlapped:
+        indexer + top-K and resolve tables on the current stream, then the
+        fault copies one group of layers at a time on a copy stream, and each
+        group's attention on the current stream as soon as that group's rows
+        are in, so that group g's attention runs while group g + 1's rows cross
+        the host link.  groups: layer groups (a divisor of L; 0 = one per
+        layer).  Same tables, pool rows and step as run()."""
+        torch = _torch()
+        wl = self.wl
+        G = groups or wl.L
+        if wl.L % G:
+            raise ValueError(f"groups={G} does not divide L={wl.L}")
+        lg = wl.L // G
+        if self._streams is None:
+            self._streams = (torch.cuda.Stream(device=self.device),
+                             torch.cuda.Stream(device=self.device))
+        need = _lib.mla_layers_workspace_bytes(wl.B, wl.P, wl.K, wl.Hq, lg)
+        if self.ws_mla is None or self.ws_mla.numel() < need:
+            self.ws_mla = torch.empty(need, dtype=torch.uint8, device=self.device)
+        xs = self._streams[1]
+        main = torch.cuda.current_stream(self.device)
+        self.run_indexer_topk()
+        self.run_resolve_tables()
+        xs.wait_stream(main)
+        done = []
+        with torch.cuda.stream(xs):
+            for g in range(G):
+                _lib.copy_faults_layers(self.batch, wl.K, self.res, self.faults, self.counts,
+                                        g * lg, lg, copy_workgroups)
+                ev = torch.cuda.Event()
+                ev.record(xs)
+                done.append(ev)
+        for g in range(G):
+            main.wait_event(done[g])
+            ls = slice(g * lg, (g + 1) * lg)
+            _lib.sparse_mla_decode_layers(self.batch, wl.K, wl.Hq, lg, wl.q_dtype, self.q[ls],
+                                          wl.kv_dtype, self.pool[ls], self.n_rows,
+                                          None if self.row_scale is None else self.row_scale[ls],
+                                          self.row_ids, wl.sm_scale, self.out[ls], self.lse[ls],
+                                          self.ws_mla)
+        main.wait_stream(xs)
+
     def append(self, s: int, stream=None):
         """KV append after step s of a decode-loop workload: one token per request
         (its latent rows in every layer and its indexer key) through

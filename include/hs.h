@@ -328,6 +328,19 @@ hs_status hs_copy_faults(const hs_batch* batch, int32_t K, const hs_residency* r
                          const int32_t* faults, const int32_t* counts, int32_t workgroups,
                          void* stream);
 
+/* hs_copy_faults for layers layer0 .. layer0 + n_layers - 1 of every fault
+ * only, for callers that let a layer's attention start as soon as its rows
+ * are in (IndexShare on page "Un contexte d'un million sur huit H200",
+ * section "Ce qui se passe": one selection feeds several attention layers, so
+ * layer l's attention needs only layer l's faulted rows).  Calls that cover
+ * every layer once, in any grouping, do what one hs_copy_faults does; the
+ * call whose range ends at layer L - 1 advances res->step, so it comes last
+ * (or the next hs_resolve_tables waits for all of them).
+ * 0 <= layer0, 1 <= n_layers, layer0 + n_layers <= res->L. */
+hs_status hs_copy_faults_layers(const hs_batch* batch, int32_t K, const hs_residency* res,
+                                const int32_t* faults, const int32_t* counts, int32_t layer0,
+                                int32_t n_layers, int32_t workgroups, void* stream);
+
 /* Sparse MLA decode attention in the absorbed (MQA) form that the
  * sparse_mla_force_mqa option keeps on the sparse kernel (page "vLLM sert
  * GLM-5.3 en contexte 1M sur 16 H200", section "Comment s'y prendre"): all Hq

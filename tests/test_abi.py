@@ -115,6 +115,12 @@ def test_host_validation_rejects_bad_arguments_without_launching():
     res.C = 100
     assert lib.hs_resolve_rows(ctypes.byref(b), 64, fake, ctypes.byref(res), fake, fake, fake,
                                None, 0, None) == 2
+    # layer-range copies: the range must lie inside [0, L)
+    res.C = 128
+    for l0, nl in ((1, 1), (0, 2), (-1, 1), (0, 0)):
+        assert lib.hs_copy_faults_layers(ctypes.byref(b), 64, ctypes.byref(res), fake, fake, l0,
+                                         nl, 0, None) == 2, (l0, nl)
+        assert "layers" in _lib.last_error()
     # attention: heads in groups of 16, at most 128; workspace
     for bad_hq in (8, 24, 144):
         assert lib.hs_sparse_mla_decode(ctypes.byref(b), 2048, bad_hq, 1, fake, 2, fake, fake,

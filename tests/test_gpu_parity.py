@@ -187,6 +187,58 @@ def test_norescache_small_hit_rate_warms_up(layout):
     assert rates[0] == 0.0 and rates[-1] > 0.5
 
 
+@pytest.mark.parametrize("layout,groups", [("interleaved", 0), ("layer_major", 0),
+                                           ("interleaved", 2)])
+def test_layer_pipelined_step_against_oracle(layout, groups):
+    """The layers of one selection overlapped (fault copies one layer at a time
+    on a second stream, each layer's attention behind its layer's copy): three
+    steps from an empty hot buffer with four layers, every stage of every step
+    against the oracle (tables, faulted rows of every layer, every layer's
+    attention); tables, pool and step equal to the single-stream step's; then
+    a captured graph of the first step replayed three times."""
+    _say(f"layer-pipelined step, 4 layers, host pool {layout}, groups {groups}")
+    wl = gen.norescache_1m(B=2, T=32768, K=256, L=4, steps=3)
+    from decode_indexer_logits_amd.device import DeviceStep
+    ds = DeviceStep(wl, host_layout=layout)
+    ref = DeviceStep(wl, host_layout=layout)
+    snap = ds.snapshot()
+    ost = gc.oracle_state(wl)
+    first = None
+    for s in range(1, wl.steps + 1):
+        ds.set_queries(s)
+        ds.run_layer_pipelined(groups=groups)
+        ref.set_queries(s)
+        ref.run()
+        ost, rr, info = gc.full_check(ds, wl, ost, s=s, attn_tol=2e-2)
+        g, r = gc.gpu_outputs(ds), gc.gpu_outputs(ref)
+        for k in ("topk", "row_ids", "counts", "tok2slot", "slot2tok", "stamp"):
+            assert np.array_equal(g[k], r[k]), (s, k)
+        assert g["step"] == r["step"] == wl.step + s and g["err"] == 0
+        assert torch.equal(ds.pool, ref.pool) and torch.equal(ds.row_scale, ref.row_scale)
+        if s == 1:
+            first = g
+        _say(s, info["counts"].tolist())
+    ds.restore(snap)
+    ds.set_queries(1)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(graph, stream=st):
+            ds.run_layer_pipelined(groups=groups)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ds.restore(snap)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = gc.gpu_outputs(ds)
+        for k in ("topk", "row_ids", "counts", "out", "lse", "tok2slot", "slot2tok", "stamp"):
+            assert np.array_equal(got[k], first[k]), ("graph", rep, k)
+        assert got["step"] == first["step"]
+
+
 def _relayout(wl, mode, seed=5):
     """The same logical data with every page resident ("full") or none ("none")."""
     B, nb = wl.B, wl.T_stride // 64
