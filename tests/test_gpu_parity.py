@@ -553,6 +553,37 @@ def test_topk_planted_ties_against_oracle(case, T_stride):
     assert len(bad) == 0, f"rows {bad[:4].tolist()}"
 
 
+@pytest.mark.parametrize("case", ["quarter_steps", "signed_zeros", "all_equal", "distinct"])
+@pytest.mark.parametrize("T_stride", [65536, 1 << 18])
+def test_topk_many_rows_planted_ties_against_oracle(case, T_stride):
+    """hs_topk on 32 rows of 64K and 2^18 tokens, planted ties included,
+    bit-exact against the oracle (the all-equal and signed-zero rows hold more
+    threshold-bin keys than the finalize pass stages in LDS); contexts short of
+    K, at K + 1, mid-row and full; a workspace zero on entry comes back zero."""
+    _say(f"topk 32 rows, {case} T_stride={T_stride}")
+    from decode_indexer_logits_amd import _lib
+    from oracle import topk as o_topk
+    seed = ["quarter_steps", "signed_zeros", "all_equal", "distinct"].index(case)
+    rng = np.random.default_rng(300 + 2 * seed + (T_stride > 65536))
+    B, P, K = 16, 2, 2048
+    ctx = rng.integers(K + 2, T_stride + 1, size=B).astype(np.int32)
+    ctx[:4] = [T_stride, K - 5, K + 2, 2500]        # full, short of K, K + 1 visible at p=1
+    S = _planted_scores(case, rng, B, P, T_stride)
+    d_ctx = torch.from_numpy(ctx).cuda()
+    d_s = torch.from_numpy(S).cuda()
+    out = torch.empty((B, P, K), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, P, T_stride, K), dtype=torch.uint8,
+                     device="cuda")
+    batch = _lib.make_batch(B, P, T_stride, d_ctx)
+    _lib.topk(batch, K, d_s, out, ws)
+    got = out.cpu().numpy()
+    ref = o_topk.topk(S.astype(np.float64), ctx, K)
+    bad = np.argwhere(np.any(ref != got, axis=2))
+    assert len(bad) == 0, f"rows {bad[:4].tolist()}"
+    # a workspace zero on entry comes back zero (the next call needs no clearing)
+    assert int(ws.count_nonzero().item()) == 0
+
+
 @pytest.mark.parametrize("B", [256, 64, 12])
 def test_indexer_many_requests_long_tiles(B):
     """Requests over a 16K-token stride, as many as select each tile size of the
