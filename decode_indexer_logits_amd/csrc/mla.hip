@@ -5,28 +5,38 @@
 // sparse_mla_force_mqa; the selected rows come from the indexer's top-K, page
 // "Un contexte d'un million sur huit H200", section "Ce qui se passe").
 //
-// bf16 x E4M3 path, one workgroup = 4 waves on one (request, position) and a
-// contiguous slice of its K selected rows, in 64-row tiles:
-//   QK   wave w takes rows 16w..16w+15 of the tile: S^T[rows x 16 heads] on
-//        the matrix cores (18 steps of v_mfma_f32_16x16x32_bf16 over the 576
-//        values).  Lane (n, g) reads bytes 16g .. 16g+15 of every 64-byte
-//        chunk of its row straight from HBM (the gather by row id; row ids
-//        are read one tile ahead), so one wave load covers whole 64-byte
-//        chunks of 16 rows; the contraction index is permuted the same way in
-//        the query fragments, which a sum allows.  It converts E4M3 -> bf16 in
-//        registers and also stores its value entries row-major into LDS at
-//        their own dims (16-byte writes).
-//   softmax  online, per head; the tile maximum is combined across the four
-//        waves through LDS; the row's scale is folded into the logit and
-//        into the probability that multiplies its value codes.
-//   PV   wave w owns output dims 128w..128w+127: O^T[dims x heads] +=
-//        V^T[dims x 64 rows] . P^T[64 rows x heads], operands read from LDS;
-//        the V^T fragments come out of the row-major tile through gfx950's
-//        transposing LDS read (ds_read_b64_tr_b16), so no transposed stores.
-// A workgroup covers rows [split*R, split*R + R) in ascending k.  With one
-// slice it writes out/lse directly; otherwise the combine kernel merges the
-// slices' (O, max, sum) in slice order, so the reduction order depends only on
-// the order of row_ids, never on where a row is stored.
+// bf16 x E4M3 path, one workgroup = 4 waves on one (request, position, group
+// of 16 heads) and a slice of its K selected rows; each wave works alone on
+// its quarter of the slice, in 16-row tiles, and the four waves merge at the
+// end:
+//   gather   a ring of 4 tiles of row loads in registers, every load issued
+//            unconditionally (a slot past the last tile reads one line of a
+//            valid row) so that the compiler waits for the oldest tile only.
+//            Lane (n, g) reads bytes 16g .. 16g+15 of every 64-byte chunk of
+//            row n, so one wave load covers whole 64-byte chunks of 16 rows;
+//            the contraction index is permuted the same way in the query
+//            fragments, which a sum allows.
+//   QK       two tiles at a time, two independent product chains: S^T[16 rows
+//            x 16 heads] over the 576 values (18 steps of
+//            v_mfma_f32_16x16x32_bf16), E4M3 converted to bf16 in registers;
+//            the queries sit once per workgroup in LDS (rows padded so that
+//            the 16 heads' fragment reads fall on distinct banks).  The value
+//            parts go row-major into the wave's own LDS stash.
+//   softmax  online per head over the two tiles' 32 rows, in the log2 domain,
+//            the row scale folded into logit and probability; the running
+//            output is rescaled only when some maximum moved.
+//   PV       O^T[512 dims x 16 heads] += V^T . P^T with the 32 rows as the
+//            contraction: laid out as rows 4g..4g+3 of each tile in lane group
+//            g, the probabilities already are this lane's B operand; the V^T
+//            fragments come out of the row-major stash through gfx950's
+//            transposing LDS read (ds_read_b64_tr_b16).  The 512 x 16 outputs
+//            live in the accumulation registers.
+//   merge    the four waves' (O, max, sum) through LDS in wave order.
+// A workgroup covers rows [split*R, split*R + R) in ascending k (or one chunk
+// of a chunk list: the token-sharded path).  With one slice it writes out/lse
+// directly; otherwise the combine kernel merges the slices' (O, max, sum) in
+// slice order, so the reduction order depends only on the order of row_ids,
+// never on where a row is stored.
 #include "hs_common.h"
 #include "hs_launch.h"
 
@@ -39,7 +49,7 @@ constexpr int kMlaMaxSplitRows = 1024;   // and no slice walks more than 16 tile
 constexpr int kMlaRing = 4;              // tiles of row gathers in flight per workgroup
 constexpr int kMaxShards = 64;           // token shards of the sharded attention
 constexpr int kTile = 64;
-constexpr int kPtStride = 72;
+constexpr int kPtStride = 72;   // bf16 per head of the probability tile (mla_tile_kernel)
 constexpr int kHq = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -371,6 +381,189 @@ __global__ __launch_bounds__(kMlaNT, 1) void mla_bf16_e4m3_kernel(
       const size_t base = ((size_t)bp * nsplit + split) * kHq + h;
       part_ml[base * 2] = M;
       part_ml[base * 2 + 1] = L;
+    }
+  }
+}
+
+// Long slices (more than kMlaRing tiles per wave): the four waves share each
+// 64-row tile (wave w gathers rows 16w..16w+15 and owns output dims
+// 128w..128w+127), one tile of gathers in flight, the tile maximum combined
+// through LDS, two workgroups per CU.  Its 32 accumulator registers leave room
+// for the next tile's loads, where the per-wave kernel's 128 do not.
+template <bool SPLIT>
+__global__ __launch_bounds__(kMlaNT, 2) void mla_tile_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ pool,
+    const float* __restrict__ row_scale, const int32_t* __restrict__ row_ids, int K,
+    int rows_per_split, int nsplit, float qk_scale_log2, float* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int64_t pool_layer_rows, int hgroups) {
+  __shared__ __attribute__((aligned(16))) uint16_t Vr[kTile * kVrStride];   // value tile, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t Pt[kHq * kPtStride];
+  __shared__ float red[4][kHq];
+
+  // blockIdx.y = (request position) * hgroups + (group of 16 heads)
+  const int bp = blockIdx.y, split = blockIdx.x;
+  const int rbp = bp / hgroups;
+  // layer blockIdx.z of a multi-layer call: its queries, pool rows, scales,
+  // outputs and partials sit one layer stride further (same row ids)
+  {
+    const size_t layer = blockIdx.z, BPn = gridDim.y;
+    q += layer * BPn * kHq * kDLat;
+    pool += layer * (size_t)pool_layer_rows * kDLat;
+    if (row_scale) row_scale += layer * (size_t)pool_layer_rows;
+    out += layer * BPn * kHq * kDVal;
+    if (lse) lse += layer * BPn * kHq;
+    if (SPLIT) {
+      part_o += layer * BPn * nsplit * kHq * kDVal;
+      part_ml += layer * BPn * nsplit * kHq * 2;
+    }
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int kb = split * rows_per_split;
+  const int ke = min(K, kb + rows_per_split);
+
+  // contraction step s takes dims dim0(s) .. +8 of head n (Q) and of row n (X)
+  auto dim0 = [&](int s) { return 64 * (s >> 1) + 16 * g + 8 * (s & 1); };
+  const int32_t* rid_p = row_ids + (size_t)rbp * K;
+  const int r_local = 16 * wave + n;
+  // row ids run one tile ahead of the row loads, so a tile's rows wait for one
+  // round of loads, not two; this lane gathers row r_local, bytes 64v + 16g .. +16
+  auto load_rid = [&](int kt) {
+    const int kk = kt + r_local;
+    return (kk < ke) ? rid_p[kk] : -1;
+  };
+  // the first row ids go out before the queries: loads complete in order, so
+  // the first gather then waits for its row ids only
+  int rid = load_rid(kb), rid_n = load_rid(kb + kTile);
+  bf16x8_t qf[18];
+  {
+    const uint16_t* qp = q + ((size_t)bp * kHq + n) * kDLat;
+#pragma unroll
+    for (int s = 0; s < 18; ++s)
+      qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + dim0(s)));
+  }
+  f32x4_t o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+  auto gather = [&](int rid, float& rs, uint4* raw) {
+    rs = 0.f;
+    if (rid >= 0) {
+      const uint8_t* src = pool + (size_t)rid * kDLat + 16 * g;
+#pragma unroll
+      for (int v = 0; v < 9; ++v) raw[v] = *reinterpret_cast<const uint4*>(src + 64 * v);
+      rs = row_scale ? row_scale[rid] : 1.f;
+    } else {
+#pragma unroll
+      for (int v = 0; v < 9; ++v) raw[v] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  float rs, rs_n = 0.f;
+  uint4 raw[9], raw_n[9];
+  gather(rid, rs, raw);
+  for (int kt = kb; kt < ke; kt += kTile) {
+    int rid_nn = -1;
+    if (kt + kTile < ke) {
+      gather(rid_n, rs_n, raw_n);
+      rid_nn = load_rid(kt + 2 * kTile);
+    }
+    // S^T = X . Q^T over 576 values; stash the value part (row-major) in LDS
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 18; ++s) {
+      const uint4 c = raw[s >> 1];
+      const uint32_t lo = (s & 1) ? c.z : c.x;
+      const uint32_t hi = (s & 1) ? c.w : c.y;
+      u32x4_t xb;
+      xb[0] = e4m3x2_to_bf16x2(lo, false);
+      xb[1] = e4m3x2_to_bf16x2(lo, true);
+      xb[2] = e4m3x2_to_bf16x2(hi, false);
+      xb[3] = e4m3x2_to_bf16x2(hi, true);
+      acc = mfma16x16x32(as_bf16x8(xb), qf[s], acc);
+      if (dim0(s) < kDVal)
+        *reinterpret_cast<uint4*>(Vr + r_local * kVrStride + dim0(s)) =
+            make_uint4(xb[0], xb[1], xb[2], xb[3]);
+    }
+    // logits of this lane's rows 4g+i (head n), log2 domain
+    float z[4];
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int src_lane = 4 * g + i;
+      const int r_i = __shfl(rid, src_lane);
+      sc[i] = __shfl(rs, src_lane);
+      z[i] = (r_i >= 0) ? acc[i] * qk_scale_log2 * sc[i] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mx = max_rows16(mx);
+    if (g == 0) red[wave][n] = mx;
+    __syncthreads();
+    const float mt = fmaxf(fmaxf(red[0][n], red[1][n]), fmaxf(red[2][n], red[3][n]));
+    const float m_new = fmaxf(m_run, mt);
+    float alpha = 1.f, p[4] = {0.f, 0.f, 0.f, 0.f};
+    if (m_new != -INFINITY) {
+      alpha = exp2f(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = exp2f(z[i] - m_new);
+    }
+    l_part = l_part * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    {
+      const uint32_t w0 = f32_to_bf16_rne(p[0] * sc[0]) | (f32_to_bf16_rne(p[1] * sc[1]) << 16);
+      const uint32_t w1 = f32_to_bf16_rne(p[2] * sc[2]) | (f32_to_bf16_rne(p[3] * sc[3]) << 16);
+      *reinterpret_cast<uint2*>(Pt + n * kPtStride + 16 * wave + 4 * g) = make_uint2(w0, w1);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    m_run = m_new;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8_t pb = as_bf16x8(*reinterpret_cast<const uint4*>(Pt + n * kPtStride + 32 * c + 8 * g));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int d0 = 128 * wave + 16 * dt;
+        const lds_v4i16 lo = vr_read_tr(Vr, 32 * c + 8 * g, d0, n);
+        const lds_v4i16 hi = vr_read_tr(Vr, 32 * c + 8 * g + 4, d0, n);
+        u32x4_t w;
+        w[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+        w[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+        w[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+        w[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+        o[dt] = mfma16x16x32(as_bf16x8(w), pb, o[dt]);
+      }
+    }
+    __syncthreads();
+    rid = rid_n;
+    rs = rs_n;
+    rid_n = rid_nn;
+#pragma unroll
+    for (int v = 0; v < 9; ++v) raw[v] = raw_n[v];
+  }
+
+  float lp = l_part;
+  lp = sum_rows16(lp);
+  if (g == 0) red[wave][n] = lp;
+  __syncthreads();
+  const float l_tot = (red[0][n] + red[1][n]) + (red[2][n] + red[3][n]);
+  if (!SPLIT) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* op = out + ((size_t)bp * kHq + n) * kDVal + 128 * wave + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(op + 16 * dt) =
+          make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    if (lse && wave == 0 && g == 0)
+      lse[(size_t)bp * kHq + n] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    const size_t base = ((size_t)bp * nsplit + split) * kHq + n;
+    float* op = part_o + base * kDVal + 128 * wave + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (wave == 0 && g == 0) {
+      part_ml[base * 2] = m_run;
+      part_ml[base * 2 + 1] = l_tot;
     }
   }
 }
@@ -736,17 +929,30 @@ hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, int L, int Hq, int64_
   const int ns = mla_num_splits(d.B, d.P, K, L, G);
   const int rps = rows_per_split_for(K, ns);
   const float qk = sm_scale * kLog2e;
+  // slices of at most kMlaRing tiles per wave go to the per-wave kernel, whose
+  // whole slice is in flight at once; longer ones to the shared-tile kernel
+  const bool tiles = rps > kMlaRing * 16 * 4;
   if (ns == 1) {
-    hipLaunchKernelGGL((mla_bf16_e4m3_kernel<false>), dim3(1, BPG, L), dim3(kMlaNT), 0, s, q,
-                       pool, row_scale, row_ids, K, rps, 1, qk, out, lse, nullptr, nullptr,
-                       pool_layer_rows, G, nullptr, nullptr);
+    if (tiles)
+      hipLaunchKernelGGL((mla_tile_kernel<false>), dim3(1, BPG, L), dim3(kMlaNT), 0, s, q, pool,
+                         row_scale, row_ids, K, rps, 1, qk, out, lse, nullptr, nullptr,
+                         pool_layer_rows, G);
+    else
+      hipLaunchKernelGGL((mla_bf16_e4m3_kernel<false>), dim3(1, BPG, L), dim3(kMlaNT), 0, s, q,
+                         pool, row_scale, row_ids, K, rps, 1, qk, out, lse, nullptr, nullptr,
+                         pool_layer_rows, G, nullptr, nullptr);
     return hipGetLastError();
   }
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + (size_t)L * BPG * ns * kHq * kDVal;
-  hipLaunchKernelGGL((mla_bf16_e4m3_kernel<true>), dim3(ns, BPG, L), dim3(kMlaNT), 0, s, q, pool,
-                     row_scale, row_ids, K, rps, ns, qk, out, lse, part_o, part_ml,
-                     pool_layer_rows, G, nullptr, nullptr);
+  if (tiles)
+    hipLaunchKernelGGL((mla_tile_kernel<true>), dim3(ns, BPG, L), dim3(kMlaNT), 0, s, q, pool,
+                       row_scale, row_ids, K, rps, ns, qk, out, lse, part_o, part_ml,
+                       pool_layer_rows, G);
+  else
+    hipLaunchKernelGGL((mla_bf16_e4m3_kernel<true>), dim3(ns, BPG, L), dim3(kMlaNT), 0, s, q,
+                       pool, row_scale, row_ids, K, rps, ns, qk, out, lse, part_o, part_ml,
+                       pool_layer_rows, G, nullptr, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_combine_kernel, dim3(BPG, kHq, 2 * L), dim3(kWave), 0, s, ns, part_o,

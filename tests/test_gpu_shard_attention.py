@@ -243,3 +243,38 @@ def test_head_groups_single_and_layers_calls(kv, Hq):
                     continue
                 assert o_attn.max_rel_err(o[b, p], ro) <= tol, (l, b, p)
                 assert np.all(np.abs(ls[b, p] - rl) <= gc.lse_bound(tol, rl)), (l, b, p)
+
+
+def test_head_groups_long_slices_shared_tile_kernel():
+    """Many request-positions and 32 heads: slices of 1024 rows, which go to the
+    shared-tile attention kernel; every head of every position against the
+    oracle over the same rows."""
+    from decode_indexer_logits_amd import _lib
+    rng = np.random.default_rng(77)
+    B, P, K, Hq, n_rows = 32, 4, 2048, 32, 16384
+    ctx = torch.tensor([4096] * B, dtype=torch.int32, device="cuda")
+    batch = _lib.make_batch(B, P, 4096, ctx)
+    rid = np.stack([rng.choice(n_rows, K, replace=False) for _ in range(B * P)]).astype(np.int32)
+    rid[5, 1500:] = -1
+    rid = rid.reshape(B, P, K)
+    qn = gen.bf16_bits(rng.standard_normal((B, P, Hq, 576)))
+    pn = rng.integers(0, 256, (n_rows, 576), dtype=np.uint8)
+    pn[(pn & 0x7F) == 0x7F] = 0
+    rsn = (rng.random(n_rows) * 0.02).astype(np.float32)
+    ws = torch.empty(max(_lib.workspace_bytes(_lib.HS_OP_MLA, B, P, 4096, K, Hq), 16),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full((B, P, Hq, 512), float("nan"), device="cuda")
+    lse = torch.full((B, P, Hq), float("nan"), device="cuda")
+    _say("head groups, long slices: B=32 P=4 K=2048 Hq=32")
+    _lib.sparse_mla_decode(batch, K, Hq, "bf16", torch.from_numpy(qn.view(np.int16)).cuda(), "e4m3",
+                           torch.from_numpy(pn).cuda(), torch.from_numpy(rsn).cuda(),
+                           torch.from_numpy(rid).cuda(), SM, out, lse, ws)
+    torch.cuda.synchronize()
+    o, ls = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        for p in range(P):
+            sel = rid[b, p][rid[b, p] >= 0]
+            x = o_num.to_f64(pn[sel], "e4m3") * rsn[sel].astype(np.float64)[:, None]
+            ro, rl = o_attn.attend(o_num.to_f64(qn[b, p], "bf16"), x, SM)
+            assert o_attn.max_rel_err(o[b, p], ro) <= 2e-2, (b, p)
+            assert np.all(np.abs(ls[b, p] - rl) <= gc.lse_bound(2e-2, rl)), (b, p)
