@@ -929,9 +929,11 @@ hipError_t launch_mla_bf16_e4m3(const BatchDims& d, int K, int L, int Hq, int64_
   const int ns = mla_num_splits(d.B, d.P, K, L, G);
   const int rps = rows_per_split_for(K, ns);
   const float qk = sm_scale * kLog2e;
-  // slices of at most kMlaRing tiles per wave go to the per-wave kernel, whose
-  // whole slice is in flight at once; longer ones to the shared-tile kernel
-  const bool tiles = rps > kMlaRing * 16 * 4;
+  // slices of three or four tiles per wave go to the per-wave kernel, whose
+  // whole slice is in flight at once; longer ones, and short ones (whose waves
+  // would not repay the per-wave kernel's query staging and four-way merge),
+  // to the shared-tile kernel
+  const bool tiles = rps > kMlaRing * 16 * 4 || rps <= 2 * 16 * 4;
   if (ns == 1) {
     if (tiles)
       hipLaunchKernelGGL((mla_tile_kernel<false>), dim3(1, BPG, L), dim3(kMlaNT), 0, s, q, pool,
