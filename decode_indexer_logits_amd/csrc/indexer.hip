@@ -29,6 +29,9 @@
 #include "hs_common.h"
 #include "hs_launch.h"
 
+#include <algorithm>
+#include <mutex>
+
 namespace hs {
 namespace {
 
@@ -39,6 +42,10 @@ struct IdxCfg {
   static constexpr int NT = NW * kWave;
   static constexpr int TILE = 4096;                              // tokens per workgroup
 };
+
+// The multi-position kernels take a tile size at run time: up to this many
+// pages per workgroup (block ids of pages l and 64 + l in lane l).
+constexpr int kMpMaxPages = 2 * kWave;
 
 template <int P, int DK, int HT, bool HIST, int TILE>
 __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
@@ -213,17 +220,17 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
 // (WPP = 4/P of them, groups split between them) read the fragments back and
 // run the products against their position's queries.  One barrier per page.
 // Raw key loads run three pages ahead in registers (8 bytes per token-row per
-// lane, a quarter page per wave).  The histogram epilogue packs two 16-bit
-// bins per LDS word (a position sees at most 4096 tokens of a tile).
+// lane, a quarter page per wave).  The tile (tokens per workgroup, up to
+// kMpMaxPages pages) is chosen at launch.  The histogram epilogue packs two
+// 16-bit bins per LDS word (a position sees at most 8192 tokens of a tile).
 template <int P, int DK, int HT, bool HIST>
 __global__ __launch_bounds__(256) void indexer_mp_kernel(
     const int32_t* __restrict__ ctx_len, int T_stride, int max_blocks,
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint8_t* __restrict__ pool, const float* __restrict__ scale,
     const int32_t* __restrict__ bt, const float* __restrict__ bias,
-    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+    float* __restrict__ scores, uint32_t* __restrict__ hist, int tile) {
   static_assert(P >= 2 && P <= 4, "multi-position kernel");
-  constexpr int TILE = 4096;
   constexpr int WPP = (P == 2) ? 2 : 1;      // waves per position (P = 3: wave 3 only converts)
   constexpr int H = 16 * HT;
   constexpr int KS = DK / 32;
@@ -232,9 +239,10 @@ __global__ __launch_bounds__(256) void indexer_mp_kernel(
   __shared__ bf16x8_t sk[2][FR][kWave];      // two converted pages
   __shared__ float sbias[2][4][kWave];       // the two pages' token biases, per wave
   __shared__ uint32_t sh_hist[HIST ? P * 1024 : 1];
+  __shared__ float s_scale[kMpMaxPages];     // the tile's page scales
   const int b = blockIdx.y;
   const int T = ctx_len[b];
-  const int tile0 = blockIdx.x * TILE;
+  const int tile0 = blockIdx.x * tile;
   if (tile0 >= T) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
@@ -244,14 +252,22 @@ __global__ __launch_bounds__(256) void indexer_mp_kernel(
   const int lim_any = T - 1;                 // last token any position sees
   if (HIST)
     for (int i = threadIdx.x; i < P * 1024; i += 256) sh_hist[i] = 0;
-  const int npages = min(TILE / kBlock, (lim_any - tile0) / kBlock + 1);
+  const int npages = min(tile / kBlock, (lim_any - tile0) / kBlock + 1);
   const int32_t* btb = bt + (size_t)b * max_blocks + tile0 / kBlock;
+  // block ids of pages l and 64 + l in lane l (read back with readlane); the
+  // scales go to LDS, read once per page by the epilogue (visible after the
+  // barrier that precedes the first page)
   const int blk_l = lane < npages ? btb[lane] : 0;
-  const float sc_l = (scale && lane < npages) ? scale[blk_l] : 1.f;
-  auto page_blk = [&](int pi) { return __builtin_amdgcn_readlane(blk_l, pi); };
-  auto page_scale = [&](int pi) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
+  const int blk_h = kWave + lane < npages ? btb[kWave + lane] : 0;
+  if (wave == 0) {
+    s_scale[lane] = (scale && lane < npages) ? scale[blk_l] : 1.f;
+    s_scale[kWave + lane] = (scale && kWave + lane < npages) ? scale[blk_h] : 1.f;
+  }
+  auto page_blk = [&](int pi) {
+    return pi >= kWave ? __builtin_amdgcn_readlane(blk_h, pi - kWave)
+                       : __builtin_amdgcn_readlane(blk_l, pi);
   };
+  auto page_scale = [&](int pi) { return s_scale[pi]; };
   // query fragments of this wave's position (same contraction order as the
   // one-position kernel)
   auto dim0 = [&](int s) { return 16 * g + 64 * (s >> 1) + 8 * (s & 1); };
@@ -513,26 +529,27 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
 // the page before is multiplied; the waves of position p (4/P of them at
 // P = 2, one otherwise; at P = 3 wave 3 only loads) read every group back
 // and run their products.  One barrier per page; raw loads run three pages
-// ahead in registers.  The histogram epilogue packs two 16-bit bins per LDS
-// word (a position sees at most 4096 tokens of a tile).
+// ahead in registers.  The tile (up to kMpMaxPages pages) is chosen at
+// launch.  The histogram epilogue packs two 16-bit bins per LDS word (a
+// position sees at most 8192 tokens of a tile).
 template <int P, int HT, bool HIST>
 __global__ __launch_bounds__(256) void indexer_e4m3_mp_kernel(
     const int32_t* __restrict__ ctx_len, int T_stride, int max_blocks,
     const uint8_t* __restrict__ q8, const float* __restrict__ w,
     const uint8_t* __restrict__ pool, const float* __restrict__ scale,
     const int32_t* __restrict__ bt, const float* __restrict__ bias,
-    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+    float* __restrict__ scores, uint32_t* __restrict__ hist, int tile) {
   static_assert(P >= 2 && P <= 4, "multi-position kernel");
-  constexpr int TILE = 4096;
   constexpr int DK = 128;
   constexpr int WPP = (P == 2) ? 2 : 1;
   constexpr int H = 16 * HT;
   __shared__ uint4 sk[2][4][2][kWave];       // two pages: [group][half][lane]
   __shared__ float sbias[2][4][kWave];       // the two pages' token biases, per wave
   __shared__ uint32_t sh_hist[HIST ? P * 1024 : 1];
+  __shared__ float s_scale[kMpMaxPages];     // the tile's page scales
   const int b = blockIdx.y;
   const int T = ctx_len[b];
-  const int tile0 = blockIdx.x * TILE;
+  const int tile0 = blockIdx.x * tile;
   if (tile0 >= T) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
@@ -542,14 +559,22 @@ __global__ __launch_bounds__(256) void indexer_e4m3_mp_kernel(
   const int lim_any = T - 1;
   if (HIST)
     for (int i = threadIdx.x; i < P * 1024; i += 256) sh_hist[i] = 0;
-  const int npages = min(TILE / kBlock, (lim_any - tile0) / kBlock + 1);
+  const int npages = min(tile / kBlock, (lim_any - tile0) / kBlock + 1);
   const int32_t* btb = bt + (size_t)b * max_blocks + tile0 / kBlock;
+  // block ids of pages l and 64 + l in lane l (read back with readlane); the
+  // scales go to LDS, read once per page by the epilogue (visible after the
+  // barrier that precedes the first page)
   const int blk_l = lane < npages ? btb[lane] : 0;
-  const float sc_l = (scale && lane < npages) ? scale[blk_l] : 1.f;
-  auto page_blk = [&](int pi) { return __builtin_amdgcn_readlane(blk_l, pi); };
-  auto page_scale = [&](int pi) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
+  const int blk_h = kWave + lane < npages ? btb[kWave + lane] : 0;
+  if (wave == 0) {
+    s_scale[lane] = (scale && lane < npages) ? scale[blk_l] : 1.f;
+    s_scale[kWave + lane] = (scale && kWave + lane < npages) ? scale[blk_h] : 1.f;
+  }
+  auto page_blk = [&](int pi) {
+    return pi >= kWave ? __builtin_amdgcn_readlane(blk_h, pi - kWave)
+                       : __builtin_amdgcn_readlane(blk_l, pi);
   };
+  auto page_scale = [&](int pi) { return s_scale[pi]; };
   const int pq = active ? p : 0;
   i32x8_t qa[HT];
   float wv[HT][4];
@@ -721,6 +746,38 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(
   scores[(size_t)bp * T_stride + t] = acc;
 }
 
+// Workgroups of `kernel` (256 threads) resident on the current device at
+// once: its occupancy per CU times the CUs, cached per kernel and device.
+int resident_workgroups(const void* kernel) {
+  struct Entry { const void* k; int dev, n; };
+  static Entry cache[64];
+  static int used = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].k == kernel && cache[i].dev == dev) return cache[i].n;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess) per_cu = 1;
+  const int n = std::max(cus, 1) * std::max(per_cu, 1);
+  if (used < 64) cache[used++] = Entry{kernel, dev, n};
+  return n;
+}
+
+// Tokens per workgroup of the multi-position kernels: every request gets an
+// equal share of one round of resident workgroups (one start-up and one tail
+// per CU slot instead of a partly filled second round: MTP3, 64 requests of
+// up to 86K tokens at four workgroups per CU, went from 22 tiles of 4096 tokens
+// per request to 16 of 5440), in whole pages, at most kMpMaxPages pages.
+int mp_tile(const BatchDims& d, const void* kernel) {
+  const int per_req = std::max(1, resident_workgroups(kernel) / std::max(d.B, 1));
+  int tile = (d.T_stride + per_req - 1) / per_req;
+  tile = (tile + kBlock - 1) / kBlock * kBlock;
+  return std::min(std::max(tile, kBlock), kMpMaxPages * kBlock);
+}
+
 template <int P, int DK, int HT>
 hipError_t launch_mfma(const BatchDims& d, const uint16_t* q, const float* w, const uint8_t* pool,
                        const float* scale, const int32_t* bt, const float* bias, float* scores,
@@ -728,14 +785,17 @@ hipError_t launch_mfma(const BatchDims& d, const uint16_t* q, const float* w, co
   using Cfg = IdxCfg<P>;
   dim3 grid((d.T_stride + Cfg::TILE - 1) / Cfg::TILE, d.B);
   if (P > 1) {
+    constexpr int PM = P > 1 ? P : 2;
+    const void* k = hist ? reinterpret_cast<const void*>(&indexer_mp_kernel<PM, DK, HT, true>)
+                         : reinterpret_cast<const void*>(&indexer_mp_kernel<PM, DK, HT, false>);
+    const int tile = mp_tile(d, k);
+    const dim3 gm((d.T_stride + tile - 1) / tile, d.B);
     if (hist)
-      hipLaunchKernelGGL((indexer_mp_kernel<(P > 1 ? P : 2), DK, HT, true>), grid, dim3(256), 0, s,
-                         d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias, scores,
-                         hist);
+      hipLaunchKernelGGL((indexer_mp_kernel<PM, DK, HT, true>), gm, dim3(256), 0, s, d.ctx_len,
+                         d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias, scores, hist, tile);
     else
-      hipLaunchKernelGGL((indexer_mp_kernel<(P > 1 ? P : 2), DK, HT, false>), grid, dim3(256), 0,
-                         s, d.ctx_len, d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias,
-                         scores, hist);
+      hipLaunchKernelGGL((indexer_mp_kernel<PM, DK, HT, false>), gm, dim3(256), 0, s, d.ctx_len,
+                         d.T_stride, d.max_blocks, q, w, pool, scale, bt, bias, scores, hist, tile);
     return hipGetLastError();
   }
   // 128-page tiles when they still give every CU two workgroups (one round of
@@ -825,14 +885,18 @@ hipError_t launch_e4m3_ht(const BatchDims& d, const uint8_t* q8, const float* w,
   dim3 grid((d.T_stride + Cfg::TILE - 1) / Cfg::TILE, d.B);
   if (P > 1) {
     constexpr int PM = P > 1 ? P : 2;
+    const void* k = hist ? reinterpret_cast<const void*>(&indexer_e4m3_mp_kernel<PM, HT, true>)
+                         : reinterpret_cast<const void*>(&indexer_e4m3_mp_kernel<PM, HT, false>);
+    const int tile = mp_tile(d, k);
+    const dim3 gm((d.T_stride + tile - 1) / tile, d.B);
     if (hist)
-      hipLaunchKernelGGL((indexer_e4m3_mp_kernel<PM, HT, true>), grid, dim3(256), 0, s,
-                         d.ctx_len, d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias,
-                         scores, hist);
+      hipLaunchKernelGGL((indexer_e4m3_mp_kernel<PM, HT, true>), gm, dim3(256), 0, s, d.ctx_len,
+                         d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias, scores, hist,
+                         tile);
     else
-      hipLaunchKernelGGL((indexer_e4m3_mp_kernel<PM, HT, false>), grid, dim3(256), 0, s,
-                         d.ctx_len, d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias,
-                         scores, hist);
+      hipLaunchKernelGGL((indexer_e4m3_mp_kernel<PM, HT, false>), gm, dim3(256), 0, s, d.ctx_len,
+                         d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias, scores, hist,
+                         tile);
     return hipGetLastError();
   }
   if (hist)

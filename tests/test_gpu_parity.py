@@ -644,6 +644,74 @@ def test_indexer_many_requests_long_tiles(B):
     _say(f"worst score error {worst:.2e}, near-tie swaps {swaps}")
 
 
+@pytest.mark.parametrize("q_t", ["bf16", "e4m3"])
+def test_multi_position_indexer_long_tiles_against_oracle(q_t):
+    """Four positions on 256 requests of up to 32768 tokens: the multi-position
+    kernels (bf16 and E4M3 queries) size their tiles to one round of resident
+    workgroups, which here is 128 pages, so pages 64..127 of a tile take the
+    second block-id register and the scales of every page come from LDS.
+    Ragged contexts (a page or less, on and off the tile boundaries).  Fused
+    and separate indexer calls give the same scores bit for bit; every visible
+    score of eight requests against the oracle; the top-K of every row exact
+    on the GPU scores."""
+    from decode_indexer_logits_amd import _lib
+    from oracle import indexer as o_idx, quant as o_quant, topk as o_topk
+    rng = np.random.default_rng(31)
+    B, P, Ts, K = 256, 4, 32768, 512
+    ctx = rng.integers(16384, Ts + 1, B).astype(np.int32)
+    ctx[:8] = [Ts, 4, 64, 65, 8192, 8195, 16384 + 4096, 24577]
+    _say(f"multi-position indexer long tiles: B={B} P={P} T_stride={Ts} q={q_t}")
+    x = gen.indexer_inputs(2200, ctx, Ts, P=P)
+    dev = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).cuda()
+           for k, v in x.items() if isinstance(v, np.ndarray)}
+    batch = _lib.make_batch(B, P, Ts, dev["ctx_len"])
+    H, D = x["H"], x["D"]
+    q_ref, w_ref = x["q_idx"], x["w"]
+    if q_t == "e4m3":
+        q8 = torch.empty((B, P, H, D), dtype=torch.uint8, device="cuda")
+        w8 = torch.empty((B, P, H), dtype=torch.float32, device="cuda")
+        _lib.quantize_queries(batch, H, D, dev["q_idx"], dev["w"], q8, w8)
+        q_dev, w_dev = q8, w8
+        q_ref, w_ref, _ = o_quant.quantize_queries(x["q_idx"], x["w"])
+        torch.cuda.synchronize()
+        gc.check_quantized(x["q_idx"], x["w"], q8.cpu().numpy(), w8.cpu().numpy())
+    else:
+        q_dev, w_dev = dev["q_idx"], dev["w"]
+    s1 = torch.empty((B, P, Ts), dtype=torch.float32, device="cuda")
+    s2 = torch.empty_like(s1)
+    topk = torch.empty((B, P, K), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, P, Ts, K), dtype=torch.uint8,
+                     device="cuda")
+    args = (H, D, q_t, q_dev, w_dev, "e4m3", dev["idx_pool"], dev["idx_scale"], dev["idx_bt"],
+            dev["bias"])
+    _lib.indexer_scores(batch, *args, s1)
+    _lib.indexer_topk(batch, *args, s2, K, topk, ws)
+    torch.cuda.synchronize()
+    g1, g2, gt = s1.cpu().numpy(), s2.cpu().numpy(), topk.cpu().numpy()
+    for b in range(B):
+        for p in range(P):
+            n = max(int(ctx[b]) - P + p + 1, 0)
+            assert np.array_equal(g1[b, p, :n].view(np.uint32), g2[b, p, :n].view(np.uint32)), (b, p)
+    rows = [0, 1, 2, 3, 5, 7, 100, 255]
+    S = o_idx.indexer_scores(q_ref[rows], q_t, w_ref[rows], x["idx_pool"], "e4m3",
+                             x["idx_scale"], x["idx_bt"][rows], ctx[rows], x["bias"][rows],
+                             T_stride=Ts)
+    worst = 0.0
+    for i, b in enumerate(rows):
+        for p in range(P):
+            n = max(int(ctx[b]) - P + p + 1, 0)
+            if n == 0:
+                continue
+            ref = S[i, p, :n]
+            err = float(np.max(np.abs(g2[b, p, :n] - ref)) / max(np.max(np.abs(ref)), 1e-30))
+            worst = max(worst, err)
+            assert err <= gc.SCORE_RTOL, (b, p, err)
+    ref_t = o_topk.topk(g2.astype(np.float64), ctx, K)
+    bad = np.argwhere(np.any(ref_t != gt, axis=2))
+    assert len(bad) == 0, f"top-K rows {bad[:4].tolist()}"
+    _say(f"worst score error {worst:.2e}")
+
+
 def test_resolve_merge_path_long_stride():
     """Several positions on a token stride past 262144 take the resolve kernel's
     list merge (binary searches and a dedup scan) instead of its token bitmap;

@@ -680,16 +680,16 @@ def norescache_1m(seed: int = 1005, B: int = 4, T: int = 1 << 20, K: int = 2048,
 
 
 def indexer_inputs(seed: int, ctx_len, T_stride: int, H: int = 64, D: int = 128,
-                   bias: bool = True) -> dict:
+                   bias: bool = True, P: int = 1) -> dict:
     """Indexer-only inputs (no latent cache) for many-request cases: bf16
-    queries [B,1,H,D] ~N(0,1), head weights U[0,1), fp8 keys with per-block
+    queries [B,P,H,D] ~N(0,1), head weights U[0,1), fp8 keys with per-block
     scales in a permuted paged pool, and a bias U[0,1) per token, or None."""
     ch = _children(seed)
     ctx = np.asarray(ctx_len, dtype=np.int32)
     B = len(ctx)
     idx_pool, idx_scale, idx_bt = _indexer_cache(ch, B, ctx, T_stride, D, fp8=True)
-    return {"ctx_len": ctx, "T_stride": T_stride, "H": H, "D": D,
-            "q_idx": _queries(ch[4], (B, 1, H, D), "bf16"), "w": uniform_f32(ch[5], (B, 1, H)),
+    return {"ctx_len": ctx, "T_stride": T_stride, "H": H, "D": D, "P": P,
+            "q_idx": _queries(ch[4], (B, P, H, D), "bf16"), "w": uniform_f32(ch[5], (B, P, H)),
             "idx_pool": idx_pool, "idx_scale": idx_scale, "idx_bt": idx_bt,
             "bias": uniform_f32(ch[8], (B, T_stride)) if bias else None}
 
