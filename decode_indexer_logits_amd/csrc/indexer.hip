@@ -759,9 +759,17 @@ int resident_workgroups(const void* kernel) {
   for (int i = 0; i < used; ++i)
     if (cache[i].k == kernel && cache[i].dev == dev) return cache[i].n;
   int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess) per_cu = 1;
-  const int n = std::max(cus, 1) * std::max(per_cu, 1);
+  const bool ok =
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess &&
+      cus > 0 && per_cu > 0;
+  if (!ok) {
+    // not cached; the error it left is cleared so that the launch reports its own.
+    // Fallback: four workgroups on each of 256 CUs.
+    (void)hipGetLastError();
+    return 1024;
+  }
+  const int n = cus * per_cu;
   if (used < 64) cache[used++] = Entry{kernel, dev, n};
   return n;
 }
