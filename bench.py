@@ -40,7 +40,7 @@ KV_ROW = 576
 INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.11e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
-                   "sha256": "4637495306c4878956527295468e9452d87aa15c85adf6fb860c3f408f624249"}
+                   "sha256": "6eef1e49b43042e2ab2f769a2d02bc04aed37c8077a2ac5826c9dd5de740ef1d"}
 
 
 def _indexer_traffic(workload: str, indexer_q: str):
