@@ -40,7 +40,7 @@ KV_ROW = 576
 INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.11e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
-                   "sha256": "6eef1e49b43042e2ab2f769a2d02bc04aed37c8077a2ac5826c9dd5de740ef1d"}
+                   "sha256": "ac7a6e25efb98ce8d5e865572d867258722a99e6f754c12d5d972bf27a2eff88"}
 
 
 def _indexer_traffic(workload: str, indexer_q: str):

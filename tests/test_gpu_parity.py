@@ -645,21 +645,23 @@ def test_indexer_many_requests_long_tiles(B):
 
 
 @pytest.mark.parametrize("q_t", ["bf16", "e4m3"])
-def test_multi_position_indexer_long_tiles_against_oracle(q_t):
-    """Four positions on 256 requests of up to 32768 tokens: the multi-position
-    kernels (bf16 and E4M3 queries) size their tiles to one round of resident
-    workgroups, which here is 128 pages, so pages 64..127 of a tile take the
-    second block-id register and the scales of every page come from LDS.
+@pytest.mark.parametrize("B,Ts", [(256, 32768), (64, 16384)])
+def test_multi_position_indexer_long_tiles_against_oracle(q_t, B, Ts):
+    """Four positions on many requests: the multi-position kernels (bf16 and
+    E4M3 queries) size their tiles to one round of resident workgroups.  256
+    requests of up to 32768 tokens take 128-page tiles, so pages 64..127 of a
+    tile take the second block-id register and the scales of every page come
+    from LDS; 64 requests of up to 16384 tokens take tiles of 16 to 22 pages.
     Ragged contexts (a page or less, on and off the tile boundaries).  Fused
     and separate indexer calls give the same scores bit for bit; every visible
     score of eight requests against the oracle; the top-K of every row exact
     on the GPU scores."""
     from decode_indexer_logits_amd import _lib
     from oracle import indexer as o_idx, quant as o_quant, topk as o_topk
-    rng = np.random.default_rng(31)
-    B, P, Ts, K = 256, 4, 32768, 512
-    ctx = rng.integers(16384, Ts + 1, B).astype(np.int32)
-    ctx[:8] = [Ts, 4, 64, 65, 8192, 8195, 16384 + 4096, 24577]
+    rng = np.random.default_rng(31 + B)
+    P, K = 4, 512
+    ctx = rng.integers(Ts // 2, Ts + 1, B).astype(np.int32)
+    ctx[:8] = [Ts, 4, 64, 65, Ts // 4, Ts // 4 + 3, Ts // 2 + 1024, Ts - 8191]
     _say(f"multi-position indexer long tiles: B={B} P={P} T_stride={Ts} q={q_t}")
     x = gen.indexer_inputs(2200, ctx, Ts, P=P)
     dev = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).cuda()
@@ -692,7 +694,7 @@ def test_multi_position_indexer_long_tiles_against_oracle(q_t):
         for p in range(P):
             n = max(int(ctx[b]) - P + p + 1, 0)
             assert np.array_equal(g1[b, p, :n].view(np.uint32), g2[b, p, :n].view(np.uint32)), (b, p)
-    rows = [0, 1, 2, 3, 5, 7, 100, 255]
+    rows = [0, 1, 2, 3, 5, 7, B // 2, B - 1]
     S = o_idx.indexer_scores(q_ref[rows], q_t, w_ref[rows], x["idx_pool"], "e4m3",
                              x["idx_scale"], x["idx_bt"][rows], ctx[rows], x["bias"][rows],
                              T_stride=Ts)
