@@ -40,7 +40,7 @@ KV_ROW = 576
 INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.11e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
-                   "sha256": "ac7a6e25efb98ce8d5e865572d867258722a99e6f754c12d5d972bf27a2eff88"}
+                   "sha256": "9a867b115b91fbb29f5835476a05f147a046dfce838a649d01736a5fb2b4645e"}
 
 
 def _indexer_traffic(workload: str, indexer_q: str):

@@ -399,10 +399,11 @@ __global__ __launch_bounds__(256) void indexer_mp_kernel(
 // head n's query and of token n's key (the same permutation of the
 // contraction index in both operands), so each of its two 16-byte key loads
 // covers whole 64-byte halves of 16 key rows.
-// One position (P = 1): four waves split the tile's pages, each keeping the
-// queries in registers (HT x 8 dwords) with two pages in flight.  Several
-// positions use indexer_e4m3_mp_kernel below.
-template <int P, int HT, bool HIST>
+// One position (P = 1): four waves split the tile's pages (8, 64 or 128 pages
+// per workgroup, as in the bf16 kernel), each keeping the queries in registers
+// (HT x 8 dwords) with two pages in flight.  Several positions use
+// indexer_e4m3_mp_kernel below.
+template <int P, int HT, bool HIST, int TILE>
 __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
     const int32_t* __restrict__ ctx_len, int T_stride, int max_blocks,
     const uint8_t* __restrict__ q8, const float* __restrict__ w,
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
   constexpr int H = 16 * HT;
   const int b = blockIdx.y;
   const int T = ctx_len[b];
-  const int tile0 = blockIdx.x * Cfg::TILE;
+  const int tile0 = blockIdx.x * TILE;
   if (tile0 >= T) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
   // The tile's scores are gathered in LDS and leave in one contiguous burst
   // at the end: 256-byte score stores interleaved with the key stream cost
   // far more HBM time than their bytes.
-  __shared__ __attribute__((aligned(16))) float s_out[Cfg::TILE];
+  __shared__ __attribute__((aligned(16))) float s_out[TILE];
   __shared__ float4 sw4[P][H / 4];
   if (HIST)
     for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT) sh_hist[i] = 0;
@@ -441,16 +442,25 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
     const uint8_t* r = qp + (16 * mt + n) * DK;
     qa[mt] = as_i32x8(*reinterpret_cast<const uint4*>(r), *reinterpret_cast<const uint4*>(r + 64));
   }
-  const int npages = min(Cfg::TILE / kBlock, (lim - tile0) / kBlock + 1);
+  const int npages = min(TILE / kBlock, (lim - tile0) / kBlock + 1);
   const int32_t* btb = bt + (size_t)b * max_blocks + tile0 / kBlock;
   const float* biasb = bias ? bias + (size_t)b * T_stride + tile0 : nullptr;
   const int lim_t = lim - tile0;
-  static_assert(Cfg::TILE / kBlock <= kWave, "one page per lane");
+  // block and scale of pages l and 64 + l in lane l (read back with readlane)
+  static_assert(TILE == 512 || TILE == 4096 || TILE == 8192, "tile of 8, 64 or 128 pages");
+  constexpr bool kTwo = TILE > 4096;
   const int blk_l = lane < npages ? btb[lane] : 0;
   const float sc_l = (scale && lane < npages) ? scale[blk_l] : 1.f;
-  auto page_blk = [&](int pi) { return __builtin_amdgcn_readlane(blk_l, pi); };
+  const int blk_h = (kTwo && kWave + lane < npages) ? btb[kWave + lane] : 0;
+  const float sc_h = (kTwo && scale && kWave + lane < npages) ? scale[blk_h] : 1.f;
+  auto page_blk = [&](int pi) {
+    return (kTwo && pi >= kWave) ? __builtin_amdgcn_readlane(blk_h, pi - kWave)
+                                 : __builtin_amdgcn_readlane(blk_l, pi);
+  };
   auto page_scale = [&](int pi) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
+    return __int_as_float((kTwo && pi >= kWave)
+                              ? __builtin_amdgcn_readlane(__float_as_int(sc_h), pi - kWave)
+                              : __builtin_amdgcn_readlane(__float_as_int(sc_l), pi));
   };
   // token 16j + n of the page: bytes 16g .. +16 and 64 + 16g .. +16
   auto load_page = [&](int pi, uint4* buf, float& bs) {
@@ -511,7 +521,7 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
   __syncthreads();
   if (lim >= tile0) {
     // whole pages: entries past the visible limit are unspecified
-    const int nt = min(Cfg::TILE, ((lim - tile0) / kBlock + 1) * kBlock);
+    const int nt = min(TILE, ((lim - tile0) / kBlock + 1) * kBlock);
     float* o = scores + (size_t)(b * P + p) * T_stride + tile0;
     for (int i = 4 * threadIdx.x; i < nt; i += 4 * Cfg::NT)
       *reinterpret_cast<float4*>(o + i) = *reinterpret_cast<const float4*>(s_out + i);
@@ -888,13 +898,28 @@ hipError_t launch_indexer_bf16_e4m3(const BatchDims& d, int H, int DK, const uin
 
 namespace {
 
+template <int P, int HT, int TILE>
+hipError_t launch_e4m3_one(const BatchDims& d, const uint8_t* q8, const float* w,
+                           const uint8_t* pool, const float* scale, const int32_t* bt,
+                           const float* bias, float* scores, uint32_t* hist, hipStream_t s) {
+  using Cfg = IdxCfg<P>;
+  const dim3 grid((d.T_stride + TILE - 1) / TILE, d.B);
+  if (hist)
+    hipLaunchKernelGGL((indexer_e4m3_kernel<P, HT, true, TILE>), grid, dim3(Cfg::NT), 0, s,
+                       d.ctx_len, d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias, scores,
+                       hist);
+  else
+    hipLaunchKernelGGL((indexer_e4m3_kernel<P, HT, false, TILE>), grid, dim3(Cfg::NT), 0, s,
+                       d.ctx_len, d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias, scores,
+                       hist);
+  return hipGetLastError();
+}
+
 template <int P, int HT>
 hipError_t launch_e4m3_ht(const BatchDims& d, const uint8_t* q8, const float* w,
                           const uint8_t* pool, const float* scale, const int32_t* bt,
                           const float* bias, float* scores, uint32_t* hist, hipStream_t s) {
-  using Cfg = IdxCfg<P>;
-  dim3 grid((d.T_stride + Cfg::TILE - 1) / Cfg::TILE, d.B);
-  if (P > 1) {
+  if constexpr (P > 1) {
     constexpr int PM = P > 1 ? P : 2;
     const void* k = hist ? reinterpret_cast<const void*>(&indexer_e4m3_mp_kernel<PM, HT, true>)
                          : reinterpret_cast<const void*>(&indexer_e4m3_mp_kernel<PM, HT, false>);
@@ -909,14 +934,17 @@ hipError_t launch_e4m3_ht(const BatchDims& d, const uint8_t* q8, const float* w,
                          d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias, scores, hist,
                          tile);
     return hipGetLastError();
+  } else {
+    // the one-position kernel takes the bf16 kernel's tiles: 128 pages when that
+    // still gives two workgroups per CU, 8 when 64 would leave most CUs idle
+    // (128K: 106.6 against 108.7 us with 64-page tiles)
+    const size_t B = d.B;
+    if (B * ((d.T_stride + 4095) / 4096) < 256)
+      return launch_e4m3_one<P, HT, 512>(d, q8, w, pool, scale, bt, bias, scores, hist, s);
+    if (B * ((d.T_stride + 8191) / 8192) >= 512)
+      return launch_e4m3_one<P, HT, 8192>(d, q8, w, pool, scale, bt, bias, scores, hist, s);
+    return launch_e4m3_one<P, HT, 4096>(d, q8, w, pool, scale, bt, bias, scores, hist, s);
   }
-  if (hist)
-    hipLaunchKernelGGL((indexer_e4m3_kernel<P, HT, true>), grid, dim3(Cfg::NT), 0, s, d.ctx_len,
-                       d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias, scores, hist);
-  else
-    hipLaunchKernelGGL((indexer_e4m3_kernel<P, HT, false>), grid, dim3(Cfg::NT), 0, s, d.ctx_len,
-                       d.T_stride, d.max_blocks, q8, w, pool, scale, bt, bias, scores, hist);
-  return hipGetLastError();
 }
 
 template <int P>

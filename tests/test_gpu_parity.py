@@ -584,24 +584,26 @@ def test_topk_many_rows_planted_ties_against_oracle(case, T_stride):
     assert int(ws.count_nonzero().item()) == 0
 
 
+@pytest.mark.parametrize("q_t", ["bf16", "e4m3"])
 @pytest.mark.parametrize("B", [256, 64, 12])
-def test_indexer_many_requests_long_tiles(B):
+def test_indexer_many_requests_long_tiles(B, q_t):
     """Requests over a 16K-token stride, as many as select each tile size of the
     one-position indexer: 256 requests take 128-page tiles, 64 take 64-page
     tiles, 12 take 8-page tiles (and 1024-token top-K filter chunks).  Ragged
     contexts (empty, one token, on and off the 512/4096/8192 boundaries); fused
     and separate indexer calls give the same scores bit for bit; every visible
     score against the oracle; top-K exact on the GPU scores and within the
-    near-tie rule on the oracle's."""
+    near-tie rule on the oracle's.  Both query types: bf16, and E4M3 codes
+    quantized on the GPU (the one-position E4M3 kernel takes the same tiles)."""
     from decode_indexer_logits_amd import _lib
-    from oracle import indexer as o_idx, topk as o_topk
+    from oracle import indexer as o_idx, quant as o_quant, topk as o_topk
     rng = np.random.default_rng(21 + B)
     Ts, K = 16384, 512
     ctx = rng.integers(1, 12001, B).astype(np.int32)
     ctx[:8] = [0, 1, 64, 4096, 8191, 8192, 8193, 16384]
     if B > 11:
         ctx[8:12] = [511, 512, 513, 4097]
-    _say(f"indexer many requests B={B} T_stride={Ts}")
+    _say(f"indexer many requests B={B} T_stride={Ts} q={q_t}")
     x = gen.indexer_inputs(2100, ctx, Ts)
     dev = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).cuda()
            for k, v in x.items() if isinstance(v, np.ndarray)}
@@ -611,13 +613,20 @@ def test_indexer_many_requests_long_tiles(B):
     topk = torch.empty((B, 1, K), dtype=torch.int32, device="cuda")
     ws = torch.zeros(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, 1, Ts, K), dtype=torch.uint8,
                      device="cuda")
-    args = (x["H"], x["D"], "bf16", dev["q_idx"], dev["w"], "e4m3", dev["idx_pool"],
+    q_dev, w_dev, q_ref, w_ref = dev["q_idx"], dev["w"], x["q_idx"], x["w"]
+    if q_t == "e4m3":
+        H, D = x["H"], x["D"]
+        q_dev = torch.empty((B, 1, H, D), dtype=torch.uint8, device="cuda")
+        w_dev = torch.empty((B, 1, H), dtype=torch.float32, device="cuda")
+        _lib.quantize_queries(batch, H, D, dev["q_idx"], dev["w"], q_dev, w_dev)
+        q_ref, w_ref, _ = o_quant.quantize_queries(x["q_idx"], x["w"])
+    args = (x["H"], x["D"], q_t, q_dev, w_dev, "e4m3", dev["idx_pool"],
             dev["idx_scale"], dev["idx_bt"], dev["bias"])
     _lib.indexer_scores(batch, *args, s1)
     _lib.indexer_topk(batch, *args, s2, K, topk, ws)
     torch.cuda.synchronize()
     g1, g2, gt = s1.cpu().numpy(), s2.cpu().numpy(), topk.cpu().numpy()
-    S = o_idx.indexer_scores(x["q_idx"], "bf16", x["w"], x["idx_pool"], "e4m3", x["idx_scale"],
+    S = o_idx.indexer_scores(q_ref, q_t, w_ref, x["idx_pool"], "e4m3", x["idx_scale"],
                              x["idx_bt"], ctx, x["bias"], T_stride=Ts)
     worst, swaps = 0.0, 0
     for b in range(B):
