@@ -18,7 +18,10 @@
  *     pools are pinned host memory passed by their device-accessible address
  *     (see hs_host_device_ptr).  The caller owns every buffer, including the
  *     workspace; the library allocates nothing and keeps no state between calls
- *     except the thread-local error message.
+ *     except the thread-local error message, a per-device memo of how many
+ *     workgroups of each multi-position indexer kernel fit the GPU at once
+ *     (from the runtime's occupancy query; it sizes their tiles and changes no
+ *     result), and the static workspace of hs_indexer_topk_noalloc.
  *   - Every call only enqueues kernels on `stream` (a hipStream_t; NULL = the
  *     default stream).  No call synchronizes, reads device memory on the host,
  *     allocates, or issues a memset, so a whole step can be captured in a HIP
