@@ -310,8 +310,17 @@ __global__ __launch_bounds__(kScanNT) void topk_filter_kernel(const int32_t* __r
       s_wsum[w] = total;
       total += x;
     }
-    s_base_sel = (total & 0xFFFF) ? atomicAdd(&ws.cnt[r * kCnt + 0], (uint32_t)(total & 0xFFFF)) : 0u;
-    s_base_cand = (total >> 16) ? atomicAdd(&ws.cnt[r * kCnt + 1], (uint32_t)(total >> 16)) : 0u;
+    // both ranges with one 64-bit atomic on the adjacent counter pair (selections
+    // in the low word, candidates in the high word; neither can carry into the
+    // other): same-address atomics from every die serialize, so one per
+    // workgroup instead of two
+    const uint64_t inc = (uint64_t)(total & 0xFFFF) | ((uint64_t)((uint32_t)total >> 16) << 32);
+    uint64_t old = 0;
+    if (inc)
+      old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.cnt + r * kCnt),
+                      (unsigned long long)inc);
+    s_base_sel = (uint32_t)old;
+    s_base_cand = (uint32_t)(old >> 32);
   }
   __syncthreads();
   if (!packed) return;
