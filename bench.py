@@ -40,7 +40,7 @@ KV_ROW = 576
 INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.11e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
-                   "sha256": "9a867b115b91fbb29f5835476a05f147a046dfce838a649d01736a5fb2b4645e"}
+                   "sha256": "a11d86834d0c788e929ee3ede4d6b9236bb9f81a2027e714969c28519261ff8f"}
 
 
 def _indexer_traffic(workload: str, indexer_q: str):

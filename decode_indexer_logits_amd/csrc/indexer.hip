@@ -47,6 +47,16 @@ struct IdxCfg {
 // pages per workgroup (block ids of pages l and 64 + l in lane l).
 constexpr int kMpMaxPages = 2 * kWave;
 
+// Adds two adjacent bins of a row's top-K histogram (the even one first) with
+// one 64-bit atomic: same-address atomics from every die serialize, so one per
+// non-empty pair instead of one per bin.  A bin counts at most 2^24 tokens, so
+// the low word never carries into the high one.
+__device__ __forceinline__ void hist_add_pair(uint32_t* even_bin, uint32_t lo, uint32_t hi) {
+  if (lo | hi)
+    atomicAdd(reinterpret_cast<unsigned long long*>(even_bin),
+              (unsigned long long)lo | ((unsigned long long)hi << 32));
+}
+
 template <int P, int DK, int HT, bool HIST, int TILE>
 __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
     const int32_t* __restrict__ ctx_len, int T_stride, int max_blocks,
@@ -207,8 +217,11 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
       *reinterpret_cast<float4*>(o + i) = *reinterpret_cast<const float4*>(s_out + i);
   }
   if (HIST) {
-    for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT)
-      if (sh_hist[i]) atomicAdd(&hist[(size_t)(b * P + i / 2048) * 2048 + (i % 2048)], sh_hist[i]);
+    for (int i = threadIdx.x; i < P * 1024; i += Cfg::NT) {
+      const int pos = i / 1024, bin = 2 * (i % 1024);
+      hist_add_pair(&hist[(size_t)(b * P + pos) * 2048 + bin], sh_hist[pos * 2048 + bin],
+                    sh_hist[pos * 2048 + bin + 1]);
+    }
   }
 }
 
@@ -384,9 +397,7 @@ __global__ __launch_bounds__(256) void indexer_mp_kernel(
     for (int i = threadIdx.x; i < P * 1024; i += 256) {
       const uint32_t x = sh_hist[i];
       const int pos = i / 1024, bin = 2 * (i % 1024);
-      uint32_t* hrow = hist + (size_t)(b * P + pos) * 2048;
-      if (x & 0xFFFFu) atomicAdd(&hrow[bin], x & 0xFFFFu);
-      if (x >> 16) atomicAdd(&hrow[bin + 1], x >> 16);
+      hist_add_pair(hist + (size_t)(b * P + pos) * 2048 + bin, x & 0xFFFFu, x >> 16);
     }
   }
 }
@@ -527,8 +538,11 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
       *reinterpret_cast<float4*>(o + i) = *reinterpret_cast<const float4*>(s_out + i);
   }
   if (HIST) {
-    for (int i = threadIdx.x; i < P * 2048; i += Cfg::NT)
-      if (sh_hist[i]) atomicAdd(&hist[(size_t)(b * P + i / 2048) * 2048 + (i % 2048)], sh_hist[i]);
+    for (int i = threadIdx.x; i < P * 1024; i += Cfg::NT) {
+      const int pos = i / 1024, bin = 2 * (i % 1024);
+      hist_add_pair(&hist[(size_t)(b * P + pos) * 2048 + bin], sh_hist[pos * 2048 + bin],
+                    sh_hist[pos * 2048 + bin + 1]);
+    }
   }
 }
 
@@ -675,9 +689,7 @@ __global__ __launch_bounds__(256) void indexer_e4m3_mp_kernel(
     for (int i = threadIdx.x; i < P * 1024; i += 256) {
       const uint32_t x = sh_hist[i];
       const int pos = i / 1024, bin = 2 * (i % 1024);
-      uint32_t* hrow = hist + (size_t)(b * P + pos) * 2048;
-      if (x & 0xFFFFu) atomicAdd(&hrow[bin], x & 0xFFFFu);
-      if (x >> 16) atomicAdd(&hrow[bin + 1], x >> 16);
+      hist_add_pair(hist + (size_t)(b * P + pos) * 2048 + bin, x & 0xFFFFu, x >> 16);
     }
   }
 }

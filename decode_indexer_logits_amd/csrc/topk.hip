@@ -183,8 +183,12 @@ __global__ __launch_bounds__(kScanNT) void topk_hist_kernel(const int32_t* __res
   for (int i = 0; i < kPer; ++i)
     if (bins[i] != 0xFFFFFFFFu) atomicAdd(&h[bins[i]], 1u);
   __syncthreads();
-  for (int i = threadIdx.x; i < kBins1; i += kScanNT)
-    if (h[i]) atomicAdd(&ws.hist[(size_t)r * kBins1 + i], h[i]);
+  // adjacent bins in pairs, one 64-bit atomic per non-empty pair (same-address
+  // atomics from every die serialize; a bin never exceeds 2^24)
+  for (int i = threadIdx.x; i < kBins1 / 2; i += kScanNT)
+    if (h[2 * i] | h[2 * i + 1])
+      atomicAdd(reinterpret_cast<unsigned long long*>(ws.hist + (size_t)r * kBins1 + 2 * i),
+                (unsigned long long)h[2 * i] | ((unsigned long long)h[2 * i + 1] << 32));
 }
 
 // Exact threshold among the candidates ck/ct[0, nc) (every key has top bits
