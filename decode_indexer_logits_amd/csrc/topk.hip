@@ -404,40 +404,45 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(const int32_t* __
   const uint32_t b1 = ws.cnt[r * kCnt + 2];
   const uint32_t above = min(ws.cnt[r * kCnt + 3], (uint32_t)K);
   const int nc = (int)min(ws.cnt[r * kCnt + 1], (uint32_t)T_stride);
-  // the outright selections and (when they fit) the candidates go to LDS
-  // with one pass of independent loads
+  // the outright selections and (when they fit) the candidates go to LDS with
+  // one round of independent loads: every load is issued before the first one
+  // is used (indices past the end are clamped and their values dropped)
   // loops over global memory issue kLd independent loads per thread before
   // using any of them (the candidates' order does not matter to the result)
   constexpr int kLd = 8;
   static_assert(kLd * kFinNT >= kMaxK, "one round of loads covers the outright selections");
+  constexpr int kStage = kFinCand / kFinNT;
+  static_assert(kStage * kFinNT == kFinCand, "one round of loads stages every candidate in LDS");
+  const bool in_lds = nc <= kFinCand;
   {
     int32_t sx[kLd];
+    uint32_t kx[kStage];
+    int32_t tx[kStage];
 #pragma unroll
     for (int u = 0; u < kLd; ++u) sx[u] = sel[min(tid + u * kFinNT, max((int)above - 1, 0))];
+    if (in_lds) {
+      const int last = max(nc - 1, 0);
 #pragma unroll
-    for (int u = 0; u < kLd; ++u)
-      if (tid + u * kFinNT < (int)above) outl[tid + u * kFinNT] = sx[u];
-  }
-  const bool in_lds = nc <= kFinCand;
-  if (in_lds)
-    for (int i0 = tid; i0 < nc; i0 += kLd * kFinNT) {
-      uint32_t kx[kLd];
-      int32_t tx[kLd];
-#pragma unroll
-      for (int u = 0; u < kLd; ++u) {
-        const int i = min(i0 + u * kFinNT, nc - 1);
+      for (int u = 0; u < kStage; ++u) {
+        const int i = min(tid + u * kFinNT, last);
         kx[u] = gk[i];
         tx[u] = gt[i];
       }
+    }
 #pragma unroll
-      for (int u = 0; u < kLd; ++u) {
-        const int i = i0 + u * kFinNT;
+    for (int u = 0; u < kLd; ++u)
+      if (tid + u * kFinNT < (int)above) outl[tid + u * kFinNT] = sx[u];
+    if (in_lds) {
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int i = tid + u * kFinNT;
         if (i < nc) {
           s_ck[i] = kx[u];
           s_ct[i] = tx[u];
         }
       }
     }
+  }
   if (tid == 0) {
     s_pos = (int)above;
     s_stage = 0;                  // staging cursor of the two-pass path below
