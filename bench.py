@@ -575,6 +575,14 @@ def main():
     stage_ms["resolve_tables"], _ = _time_launches(ds.run_resolve_tables, a.kernel_reps, torch,
                                                    restore, flush)
 
+    def restore_scored():   # the state and the indexer's histograms, ready for the selection
+        restore()
+        ds.run_indexer_topk_scores(quantize=False)
+    # the top-K selection half and the resolve tables in one call, as the step runs them
+    stage_ms["topk_select_resolve"], _ = _time_launches(ds.run_indexer_topk_select_resolve,
+                                                        a.kernel_reps, torch, restore_scored,
+                                                        flush)
+
     def restore_resolved():
         restore()
         ds.run_resolve_tables()
@@ -587,8 +595,8 @@ def main():
     # but the fault copies (indexer + top-K, resolve tables, attention), timed per replay
     # from the restored state with the MALL flushed
     def phase_eager():
-        ds.run_indexer_topk()
-        ds.run_resolve_tables()
+        ds.run_indexer_topk_scores()
+        ds.run_indexer_topk_select_resolve()
         if wl.L > 1:
             ds.run_attention_layers()
         else:

@@ -27,6 +27,7 @@ EXPORTS = ["hs_indexer_scores", "hs_quantize_queries", "hs_topk", "hs_indexer_to
            "hs_sparse_mla_decode", "hs_sparse_mla_decode_layers", "hs_mla_layers_workspace_bytes",
            "hs_topk_sharded", "hs_topk_sharded_workspace_bytes",
            "hs_sparse_mla_decode_sharded", "hs_mla_sharded_workspace_bytes",
+           "hs_indexer_topk_select_resolve",
            "hs_append_tokens", "hs_precopy_pages", "hs_demote_pages",
            "hs_workspace_bytes", "hs_host_device_ptr", "hs_last_error", "hs_abi_version"]
 
@@ -86,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.hs_indexer_topk_select.argtypes = [P, c_int32, c_int32, P, P, P, c_size_t, P]
     lib.hs_resolve_rows.argtypes = [P, c_int32, P, P, P, P, P, P, c_size_t, P]
     lib.hs_resolve_tables.argtypes = [P, c_int32, P, P, P, P, P, P]
+    lib.hs_indexer_topk_select_resolve.argtypes = [P, c_int32, c_int32, P, P, P, c_size_t, P, P,
+                                                   P, P, P]
     lib.hs_copy_faults.argtypes = [P, c_int32, P, P, P, c_int32, P]
     lib.hs_copy_faults_layers.argtypes = [P, c_int32, P, P, P, c_int32, c_int32, c_int32, P]
     lib.hs_sparse_mla_decode.argtypes = [P, c_int32, c_int32, c_int32, P, c_int32, P, P, P,
@@ -225,6 +228,14 @@ def resolve_tables(batch: Batch, K: int, topk_t, res: Residency, row_ids, faults
                    stream=None):
     _check(load().hs_resolve_tables(ctypes.byref(batch), K, _ptr(topk_t), ctypes.byref(res),
                                     _ptr(row_ids), _ptr(faults), _ptr(counts), _stream(stream)))
+
+
+def indexer_topk_select_resolve(batch: Batch, q_t: str, K: int, scores, topk_t, ws,
+                                res: Residency, row_ids, faults, counts, stream=None):
+    _check(load().hs_indexer_topk_select_resolve(
+        ctypes.byref(batch), DTYPES[q_t], K, _ptr(scores), _ptr(topk_t), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), ctypes.byref(res), _ptr(row_ids),
+        _ptr(faults), _ptr(counts), _stream(stream)))
 
 
 def copy_faults(batch: Batch, K: int, res: Residency, faults, counts, workgroups: int = 0,

@@ -412,6 +412,37 @@ hs_status hs_resolve_tables(const hs_batch* batch, int32_t K, const int32_t* top
                   "resolve");
 }
 
+hs_status hs_indexer_topk_select_resolve(const hs_batch* batch, hs_dtype q_t, int32_t K,
+                                         const float* scores, int32_t* topk, void* ws,
+                                         size_t ws_bytes, const hs_residency* res,
+                                         int32_t* row_ids, int32_t* faults, int32_t* counts,
+                                         void* stream) {
+  hs::BatchDims d;
+  if (hs_status st = check_batch(batch, &d)) return st;
+  if (!scores) return fail(HS_ERR_NULL, "hs_indexer_topk_select_resolve: scores is required");
+  if (!aligned16(scores))
+    return fail(HS_ERR_ALIGN, "hs_indexer_topk_select_resolve: scores need 16-byte alignment");
+  if (q_t != HS_F32 && q_t != HS_BF16 && q_t != HS_E4M3)
+    return fail(HS_ERR_DTYPE, "hs_indexer_topk_select_resolve: q_t=%d is not a query type",
+                (int)q_t);
+  if (hs_status st = check_topk(d, K, topk, ws, ws_bytes)) return st;
+  if (!row_ids || !faults || !counts)
+    return fail(HS_ERR_NULL, "resolve: row_ids, faults and counts are required");
+  hs::ResidencyArgs r;
+  if (hs_status st = check_residency(d, K, res, &r)) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (q_t == HS_F32) {
+    // no histogram from the indexer: the whole selection, then the tables
+    hipError_t e = hs::launch_topk(d, K, scores, topk, ws, s);
+    if (e == hipSuccess) e = hs::launch_resolve_tables(d, K, topk, r, row_ids, faults, counts, s);
+    return launched(e, "top-K + resolve");
+  }
+  hipError_t e = hs::launch_topk_filter(d, K, scores, ws, s);
+  if (e == hipSuccess)
+    e = hs::launch_finalize_resolve(d, K, topk, ws, r, row_ids, faults, counts, s);
+  return launched(e, "top-K + resolve");
+}
+
 hs_status hs_copy_faults_layers(const hs_batch* batch, int32_t K, const hs_residency* res,
                                 const int32_t* faults, const int32_t* counts, int32_t layer0,
                                 int32_t n_layers, int32_t workgroups, void* stream) {

@@ -45,6 +45,10 @@ uint32_t* topk_histograms(void* ws);
 hipError_t launch_topk_zero(const BatchDims& d, int K, void* ws, uint32_t** hist, hipStream_t s);
 hipError_t launch_topk_select(const BatchDims& d, int K, const float* scores, int32_t* topk,
                               void* ws, hipStream_t s);
+// The filter pass of the selection alone (the finalize then runs on its own or
+// fused with the resolve tables).
+hipError_t launch_topk_filter(const BatchDims& d, int K, const float* scores, void* ws,
+                              hipStream_t s);
 
 struct ResidencyArgs {
   int C, L, kv_bytes;               // kv_bytes: bytes per latent element (1 or 4)
@@ -66,6 +70,14 @@ struct ResidencyArgs {
 hipError_t launch_resolve_tables(const BatchDims& d, int K, const int32_t* topk,
                                  const ResidencyArgs& r, int32_t* row_ids, int32_t* faults,
                                  int32_t* counts, hipStream_t s);
+// The top-K finalize followed by the resolve tables, after the filter pass
+// (launch_topk_filter) on a workspace laid out as topk_workspace_bytes says:
+// one kernel for one query position, the two launches otherwise.
+hipError_t launch_finalize_resolve(const BatchDims& d, int K, int32_t* topk, void* topk_ws,
+                                   const ResidencyArgs& r, int32_t* row_ids, int32_t* faults,
+                                   int32_t* counts, hipStream_t s);
+hipError_t launch_topk_finalize(const BatchDims& d, int K, int32_t* topk, void* ws,
+                                hipStream_t s);
 // Layers l0 .. l0 + nl - 1 of every fault (the call with l0 + nl == L advances
 // the step); workgroups = 0: the default grid (every CU)
 hipError_t launch_fault_copy(const BatchDims& d, int K, const ResidencyArgs& r,

@@ -23,6 +23,7 @@
 //              counter.
 #include "hs_common.h"
 #include "hs_launch.h"
+#include "topk_select.h"
 
 namespace hs {
 namespace {
@@ -134,18 +135,33 @@ __device__ __forceinline__ int field16(const uint32_t* w, int j) {
 // for its code size in instruction fetches.  ONE: one query position (P = 1),
 // whose list is already U: entry i * 1024 + t stays with thread t from its load
 // to its row id, so the table lookups go out as soon as the list arrives.
-template <int NT, int MAXS, int MAXE, bool ONE>
+// FUSED (one position): the workgroup first finishes its row's top-K selection
+// (topk_sel::finalize_row, after the filter pass; it writes topk_out and
+// returns the selection's workspace row to zero) and then resolves that list,
+// read back from topk_out, in the same LDS.  topk is unused then.
+template <int NT, int MAXS, int MAXE, bool ONE, bool FUSED>
 __global__ __launch_bounds__(NT) void resolve_kernel(
     int T_stride, int max_blocks, int P, int K, const int32_t* __restrict__ topk, int C,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ hot_blocks,
     int32_t* __restrict__ tok2slot, int32_t* __restrict__ slot2tok, int32_t* __restrict__ stamp,
     const int32_t* __restrict__ step, int32_t* __restrict__ err,
     const int64_t* __restrict__ host_bt, int32_t* __restrict__ row_ids,
-    int32_t* __restrict__ faults, int32_t* __restrict__ counts) {
-  // R1: merge lists, then victims (slots, or sorted 64-bit keys on the general path)
-  __shared__ __attribute__((aligned(16))) uint64_t sA64[kMaxSel];
-  __shared__ int32_t sU[kMaxSel];          // U when P > 1
-  __shared__ int32_t sF[kMaxSel];          // faulting tokens, ascending
+    int32_t* __restrict__ faults, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ ctx_len, topk_sel::TopkWs tws, int32_t* topk_out) {
+  static_assert(!FUSED || ONE, "the fused selection serves one query position");
+  // R1: merge lists, then victims (slots, or sorted 64-bit keys on the general path).
+  // Fused: these three arrays share their LDS with the selection's, which is
+  // dead once the row's top-K is written.
+  constexpr int kResLds = 16 * kMaxSel;
+  constexpr int kFusedLds = kResLds > (int)topk_sel::kFinLdsBytes ? kResLds
+                                                                  : (int)topk_sel::kFinLdsBytes;
+  __shared__ __attribute__((aligned(16))) uint64_t sA64_[FUSED ? 1 : kMaxSel];
+  __shared__ int32_t sU_[FUSED ? 1 : kMaxSel];   // U when P > 1
+  __shared__ int32_t sF_[FUSED ? 1 : kMaxSel];   // faulting tokens, ascending
+  __shared__ __attribute__((aligned(16))) unsigned char arena[FUSED ? kFusedLds : 16];
+  uint64_t* const sA64 = FUSED ? reinterpret_cast<uint64_t*>(arena) : sA64_;
+  int32_t* const sU = FUSED ? reinterpret_cast<int32_t*>(arena + 8 * kMaxSel) : sU_;
+  int32_t* const sF = FUSED ? reinterpret_cast<int32_t*>(arena + 12 * kMaxSel) : sF_;
   __shared__ int32_t sHot[kMaxHotBlocks];  // this request's hot blocks
   __shared__ uint32_t sHitMask[kMaxHotBlocks * 2];   // slots hit at this step (C bits)
   __shared__ int scratch[NT / kWave + 1];
@@ -161,12 +177,16 @@ __global__ __launch_bounds__(NT) void resolve_kernel(
   __shared__ int s_wsig[NT / kWave];                          // oldest stamp below s, per wave
   int32_t* sA = reinterpret_cast<int32_t*>(sA64);
 
+  if constexpr (FUSED) {
+    topk_sel::finalize_row(blockIdx.x, ctx_len, 1, T_stride, K, tws, topk_out, arena);
+    __syncthreads();   // the row's top-K (this workgroup's global writes) and the LDS handed over
+  }
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int s = step[0] + 1;
   const int PK = P * K;
-  const int32_t* tk = topk + (size_t)b * PK;
+  const int32_t* tk = (FUSED ? topk_out : topk) + (size_t)b * PK;
   const int32_t* btb = bt + (size_t)b * max_blocks;
   const int64_t* hbt = host_bt ? host_bt + (size_t)b * max_blocks : nullptr;
   int32_t* t2s = tok2slot + (size_t)b * T_stride;
@@ -895,9 +915,10 @@ hipError_t launch_resolve_tables(const BatchDims& d, int K, const int32_t* topk,
                                  const ResidencyArgs& r, int32_t* row_ids, int32_t* faults,
                                  int32_t* counts, hipStream_t s) {
 #define HS_RESOLVE(NT_, S_, E_, ONE_)                                                         \
-  hipLaunchKernelGGL((resolve_kernel<NT_, S_, E_, ONE_>), dim3(d.B), dim3(NT_), 0, s, d.T_stride, \
-                     d.max_blocks, d.P, K, topk, r.C, r.bt, r.hot_blocks, r.tok2slot, r.slot2tok, \
-                     r.stamp, r.step, r.err, r.host_bt, row_ids, faults, counts)
+  hipLaunchKernelGGL((resolve_kernel<NT_, S_, E_, ONE_, false>), dim3(d.B), dim3(NT_), 0, s,     \
+                     d.T_stride, d.max_blocks, d.P, K, topk, r.C, r.bt, r.hot_blocks, r.tok2slot,  \
+                     r.slot2tok, r.stamp, r.step, r.err, r.host_bt, row_ids, faults, counts,       \
+                     nullptr, topk_sel::TopkWs{}, nullptr)
   const int slots = (r.C + kResNT - 1) / kResNT, entries = (d.P * K + kResNT - 1) / kResNT;
   static_assert(kMaxSlotsPerThread == 16 && kMaxEntriesPerThread == 8, "instances below");
   if (d.P == 1) {
@@ -913,6 +934,28 @@ hipError_t launch_resolve_tables(const BatchDims& d, int K, const int32_t* topk,
     else HS_RESOLVE(kResNT, 16, 8, false);
   }
 #undef HS_RESOLVE
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_resolve(const BatchDims& d, int K, int32_t* topk, void* ws,
+                                   const ResidencyArgs& r, int32_t* row_ids, int32_t* faults,
+                                   int32_t* counts, hipStream_t s) {
+  if (d.P != 1) {
+    hipError_t e = launch_topk_finalize(d, K, topk, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_resolve_tables(d, K, topk, r, row_ids, faults, counts, s);
+  }
+  const topk_sel::TopkWs w = topk_sel::topk_ws(ws, d.B, d.T_stride, K);
+#define HS_FUSED(S_, E_)                                                                     \
+  hipLaunchKernelGGL((resolve_kernel<kResNT, S_, E_, true, true>), dim3(d.B), dim3(kResNT), 0, s, \
+                     d.T_stride, d.max_blocks, 1, K, nullptr, r.C, r.bt, r.hot_blocks,            \
+                     r.tok2slot, r.slot2tok, r.stamp, r.step, r.err, r.host_bt, row_ids, faults,  \
+                     counts, d.ctx_len, w, topk)
+  const int slots = (r.C + kResNT - 1) / kResNT, entries = (K + kResNT - 1) / kResNT;
+  if (slots <= 4 && entries <= 2) HS_FUSED(4, 2);
+  else if (slots <= 16 && entries <= 2) HS_FUSED(16, 2);
+  else HS_FUSED(16, 8);
+#undef HS_FUSED
   return hipGetLastError();
 }
 

@@ -216,6 +216,13 @@ class DeviceStep:
         _lib.indexer_topk_select(self.batch, self.indexer_q, self.wl.K, self.scores, self.topk,
                                  self.ws_topk, stream)
 
+    def run_indexer_topk_select_resolve(self, stream=None):
+        """The selection half of run_indexer_topk followed by the resolve tables, in
+        one call (one kernel for the finalize and the tables with one position)."""
+        _lib.indexer_topk_select_resolve(self.batch, self.indexer_q, self.wl.K, self.scores,
+                                         self.topk, self.ws_topk, self.res, self.row_ids,
+                                         self.faults, self.counts, stream)
+
     def run_resolve(self, stream=None):
         _lib.resolve_rows(self.batch, self.wl.K, self.topk, self.res, self.row_ids, self.faults,
                           self.counts, stream)
@@ -244,11 +251,18 @@ class DeviceStep:
                                       self.row_ids, wl.sm_scale, self.out, self.lse, self.ws_mla,
                                       stream)
 
-    def run(self, stream=None):
+    def run(self, stream=None, fused_resolve: bool = True):
         """One whole decode step: indexer + top-K, resolve (+ fault copies), attention of
-        the L layers (one call for several layers)."""
-        self.run_indexer_topk(stream)
-        self.run_resolve(stream)
+        the L layers (one call for several layers).  fused_resolve: the top-K's
+        selection half and the resolve tables in one call (hs_indexer_topk_select_resolve),
+        else hs_indexer_topk then hs_resolve_rows; the results are the same."""
+        if fused_resolve:
+            self.run_indexer_topk_scores(stream)
+            self.run_indexer_topk_select_resolve(stream)
+            self.run_copy_faults(stream=stream)
+        else:
+            self.run_indexer_topk(stream)
+            self.run_resolve(stream)
         if self.wl.L > 1:
             self.run_attention_layers(stream)
         else:

@@ -331,6 +331,23 @@ hs_status hs_copy_faults(const hs_batch* batch, int32_t K, const hs_residency* r
                          const int32_t* faults, const int32_t* counts, int32_t workgroups,
                          void* stream);
 
+/* hs_indexer_topk_select followed by hs_resolve_tables, the fused resolve
+ * step of page "Un contexte d'un million sur huit H200", section "Les trois
+ * états de résidence", right behind the selection it consumes: with one query
+ * position (batch->P == 1) each request's workgroup finishes its top-K and
+ * resolves that list in the same kernel, so no launch separates the two; with
+ * several positions it enqueues the two calls.  Arguments as the two calls
+ * (q_t, K, scores, topk, ws, ws_bytes of hs_indexer_topk_select after the
+ * matching hs_indexer_topk_scores; res, row_ids, faults, counts of
+ * hs_resolve_tables), with the same results: topk, the workspace returned to
+ * zero, tables, row ids, fault list and counts.  hs_copy_faults then follows
+ * as after hs_resolve_tables. */
+hs_status hs_indexer_topk_select_resolve(const hs_batch* batch, hs_dtype q_t, int32_t K,
+                                         const float* scores, int32_t* topk, void* ws,
+                                         size_t ws_bytes, const hs_residency* res,
+                                         int32_t* row_ids, int32_t* faults, int32_t* counts,
+                                         void* stream);
+
 /* hs_copy_faults for layers layer0 .. layer0 + n_layers - 1 of every fault
  * only, for callers that let a layer's attention start as soon as its rows
  * are in (IndexShare on page "Un contexte d'un million sur huit H200",

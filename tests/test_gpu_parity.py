@@ -723,6 +723,76 @@ def test_multi_position_indexer_long_tiles_against_oracle(q_t, B, Ts):
     _say(f"worst score error {worst:.2e}")
 
 
+def _select_resolve_workload(name):
+    if name == "mixed_small":
+        beta, hot, _ = calibrate(seed=1003, B=4, T=16384, K=512, tail=1024)
+        return gen.mixed_128k(seed=1003, B=4, T=16384, K=512, tail=1024, beta=beta,
+                              hot_tokens=hot)
+    if name == "one_position_c8192":
+        return gen.mtp3_agentic(B=3, K=1024, steps=2, first_turn=40000, per_turn=300, turns=5,
+                                out_max=50, P=1, C=8192)
+    if name == "resident_k4096":
+        return gen.resident_fp8(B=4, K=4096)
+    if name == "two_positions":
+        return gen.mtp3_agentic(B=3, K=128, steps=2, first_turn=9000, per_turn=300, turns=5,
+                                out_max=50, P=2)
+    if name == "tiny_fp32":
+        return gen.tiny_fp32(K=256)
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["mixed_small", "one_position_c8192", "resident_k4096",
+                                  "two_positions", "tiny_fp32"])
+def test_select_resolve_matches_separate_calls(name):
+    """hs_indexer_topk_select_resolve gives what hs_indexer_topk_select followed
+    by hs_resolve_tables give, bit for bit: the top-K, row ids, fault lists,
+    counts, hot tables, device error word, and the selection workspace back to
+    zero.  One query position takes the fused kernel (all three of its
+    instances: up to 4096 hot rows with K <= 2048, up to 16384 hot rows, and
+    K > 2048); several positions and fp32 queries take the two launches.  Every
+    step of the workload, each from the state the previous one left."""
+    from decode_indexer_logits_amd.device import DeviceStep
+    wl = _select_resolve_workload(name)
+    _say(f"select + resolve {name}: B={wl.B} P={wl.P} K={wl.K} C={wl.C} q={wl.q_dtype}")
+    ds = DeviceStep(wl)
+
+    def outputs():
+        torch.cuda.synchronize()
+        o = {"topk": ds.topk.clone(), "row_ids": ds.row_ids.clone(), "counts": ds.counts.clone(),
+             "err": ds.err.clone(), "ws_zero": bool((ds.ws_topk == 0).all())}
+        c = ds.counts.cpu().numpy()
+        f = ds.faults.cpu().numpy()
+        o["faults"] = [f[b, :int(c[b, 2])].copy() for b in range(wl.B)]
+        for k in ("tok2slot", "slot2tok", "stamp"):
+            t = getattr(ds, k, None)
+            o[k] = None if t is None else t.clone()
+        return o
+
+    for s in range(1, wl.steps + 1):
+        if s > 1:
+            ds.set_queries(s)
+        snap = ds.snapshot()
+        ds.run_indexer_topk_scores()
+        ds.run_indexer_topk_select()
+        ds.run_resolve_tables()
+        a = outputs()
+        ds.restore(snap)
+        ds.run_indexer_topk_scores()
+        ds.run_indexer_topk_select_resolve()
+        b = outputs()
+        assert a["ws_zero"] and b["ws_zero"]
+        for k in ("topk", "row_ids", "counts", "err", "tok2slot", "slot2tok", "stamp"):
+            if a[k] is None:
+                assert b[k] is None
+            else:
+                assert torch.equal(a[k], b[k]), (s, k)
+        for x, y in zip(a["faults"], b["faults"]):
+            assert np.array_equal(x, y), s
+        ds.run_copy_faults()
+        torch.cuda.synchronize()
+        _say(f"step {s}: counts {b['counts'].sum(dim=0).tolist()}")
+
+
 def test_resolve_merge_path_long_stride():
     """Several positions on a token stride past 262144 take the resolve kernel's
     list merge (binary searches and a dedup scan) instead of its token bitmap;

@@ -577,7 +577,7 @@ def conversation_lengths(ss, B: int, first_turn: int = 74160, per_turn: int = 97
 def mtp3_agentic(seed: int = 1004, B: int = 64, K: int = 2048, steps: int = 4,
                  rho: float = 0.95, pool_frac: float = 0.40, first_turn: int = 74160,
                  per_turn: int = 973, turns: int = 13, out_max: int = 220,
-                 P: int = 4) -> Workload:
+                 P: int = 4, C: int | None = None) -> Workload:
     """MTP3 agentic mix: 3 speculative tokens, so P = 4 query positions and hot
     buffers of (3 + 2) x K = 10240 rows per request.  Context lengths follow
     13-turn conversations (first turn 74,160 tokens, then +753 input and +220
@@ -586,10 +586,11 @@ def mtp3_agentic(seed: int = 1004, B: int = 64, K: int = 2048, steps: int = 4,
     blocks plus an equal resident tail per request; the rest is host-only.
     Four steps with the indexer queries drifting as AR(1) (rho = 0.95) and fresh
     attention queries per step; hot buffers start empty.  ``P`` other than 4
-    (P - 1 speculative tokens, hot buffers (P + 1) x K) serves smaller tests."""
+    (P - 1 speculative tokens, hot buffers (P + 1) x K) serves smaller tests, as
+    does ``C`` (hot rows per request, a multiple of 64 of at least P x K)."""
     ch = _children(seed)
     Hq, H, D, L = 16, 64, 128, 1
-    C = (P + 1) * K
+    C = (P + 1) * K if C is None else int(C)
     ctx = conversation_lengths(ch[0], B, first_turn, per_turn, turns, out_max)
     Ts = _round_up(int(ctx.max()), BLOCK)
     nblk = -(-ctx.astype(np.int64) // BLOCK)
