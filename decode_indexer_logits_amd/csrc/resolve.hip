@@ -177,14 +177,9 @@ __global__ __launch_bounds__(NT) void resolve_kernel(
   __shared__ int s_wsig[NT / kWave];                          // oldest stamp below s, per wave
   int32_t* sA = reinterpret_cast<int32_t*>(sA64);
 
-  if constexpr (FUSED) {
-    topk_sel::finalize_row(blockIdx.x, ctx_len, 1, T_stride, K, tws, topk_out, arena);
-    __syncthreads();   // the row's top-K (this workgroup's global writes) and the LDS handed over
-  }
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int s = step[0] + 1;
   const int PK = P * K;
   const int32_t* tk = (FUSED ? topk_out : topk) + (size_t)b * PK;
   const int32_t* btb = bt + (size_t)b * max_blocks;
@@ -192,6 +187,30 @@ __global__ __launch_bounds__(NT) void resolve_kernel(
   int32_t* t2s = tok2slot + (size_t)b * T_stride;
   int32_t* s2t = slot2tok + (size_t)b * C;
   int32_t* stp = stamp + (size_t)b * C;
+  // this request's hot blocks (LDS), a cleared hit mask, and the stamps of this
+  // thread's contiguous run of slots for the victim choice, read before the
+  // hits of this step are known (they are masked in from sHitMask later
+  // instead of read back).  ONE: the slots' owners too, so that an evicted
+  // token is known without another round of loads.
+  const int S = (C + NT - 1) / NT;
+  int st_reg[MAXS], ow_reg[MAXS];
+  auto load_slots = [&]() {
+    for (int i = tid; i < (C >> 6); i += NT) sHot[i] = hot_blocks[(size_t)b * (C >> 6) + i];
+    for (int i = tid; i < (C >> 5); i += NT) sHitMask[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < MAXS; ++j) {
+      const int v = tid * S + j;
+      st_reg[j] = (j < S && v < C) ? stp[v] : 0x7FFFFFFF;
+      if constexpr (ONE) ow_reg[j] = (j < S && v < C) ? s2t[v] : -1;
+    }
+  };
+  if constexpr (FUSED) {
+    // the slot state does not depend on the selection: its loads overlap it
+    load_slots();
+    topk_sel::finalize_row(b, ctx_len, 1, T_stride, K, tws, topk_out, arena);
+    __syncthreads();   // the row's top-K (this workgroup's global writes) and the LDS handed over
+  }
+  const int s = step[0] + 1;
 
   if (tid == 0) {
     s_res = 0;
@@ -222,20 +241,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(
       vs[i] = (t >= 0 && C > 0) ? t2s[t] : -1;
     }
   }
-  for (int i = tid; i < (C >> 6); i += NT) sHot[i] = hot_blocks[(size_t)b * (C >> 6) + i];
-  for (int i = tid; i < (C >> 5); i += NT) sHitMask[i] = 0u;
-  // stamps of this thread's contiguous run of slots, for the victim choice;
-  // loaded now, before the hits of this step are known (they are masked in
-  // from sHitMask later instead of read back).  ONE: the slots' owners too, so
-  // that an evicted token is known without another round of loads.
-  const int S = (C + NT - 1) / NT;
-  int st_reg[MAXS], ow_reg[MAXS];
-#pragma unroll
-  for (int j = 0; j < MAXS; ++j) {
-    const int v = tid * S + j;
-    st_reg[j] = (j < S && v < C) ? stp[v] : 0x7FFFFFFF;
-    if constexpr (ONE) ow_reg[j] = (j < S && v < C) ? s2t[v] : -1;
-  }
+  if constexpr (!FUSED) load_slots();
   int32_t* sOld = sU;   // ONE: the previous owner of victim i (sU is not used)
   // the oldest stamp below s before this step's hits: no candidate victim is
   // older (published to LDS here, read after a later barrier)
