@@ -577,6 +577,7 @@ def main():
 
     def restore_scored():   # the state and the indexer's histograms, ready for the selection
         restore()
+        flush()
         ds.run_indexer_topk_scores(quantize=False)
     # the top-K selection half and the resolve tables in one call, as the step runs them
     stage_ms["topk_select_resolve"], _ = _time_launches(ds.run_indexer_topk_select_resolve,
