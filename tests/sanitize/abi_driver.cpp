@@ -113,6 +113,17 @@ int main() {
   EXPECT(hs_copy_faults(&b, 64, &r, fi, fi, 2000, nullptr), HS_ERR_SHAPE);
   EXPECT(hs_copy_faults_layers(&b, 64, &r, fi, fi, 1, 1, 0, nullptr), HS_ERR_SHAPE);
   EXPECT(hs_copy_faults_layers(&b, 64, &r, fi, fi, 0, 0, 0, nullptr), HS_ERR_SHAPE);
+  // selection half + resolve tables: each half's checks
+  EXPECT(hs_indexer_topk_select_resolve(&b, HS_BF16, 64, ff, fi, f, tk - 1, &r, fi, fi, fi,
+                                        nullptr), HS_ERR_WORKSPACE);
+  EXPECT(hs_indexer_topk_select_resolve(&b, HS_BF16, 64, nullptr, fi, f, tk, &r, fi, fi, fi,
+                                        nullptr), HS_ERR_NULL);
+  EXPECT(hs_indexer_topk_select_resolve(&b, HS_BF16, 64, ff, fi, f, tk, &r, nullptr, fi, fi,
+                                        nullptr), HS_ERR_NULL);
+  EXPECT(hs_indexer_topk_select_resolve(&b, HS_BF16, 64, ff, fi, f, tk, &r2, fi, fi, fi,
+                                        nullptr), HS_ERR_DTYPE);
+  EXPECT(hs_indexer_topk_select_resolve(&b, HS_BF16, 256, ff, fi, f, 1 << 30, &r, fi, fi, fi,
+                                        nullptr), HS_ERR_CAPACITY);
 
   // ---- attention
   EXPECT(hs_sparse_mla_decode(&b, 2048, 24, HS_BF16, f, HS_E4M3, f, ff, fi, 0.1f, ff, nullptr,
