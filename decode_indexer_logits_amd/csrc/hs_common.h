@@ -103,6 +103,22 @@ __device__ __forceinline__ float sum_rows16(float v) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// Four such sums at once, each landing in one row: v[j] is this lane's part of
+// column-sum j, and row g of the result holds column-sum g, with the same
+// additions in the same order as sum_rows16(v[g]).  Three swaps instead of
+// eight: the first permute pairs rows 0/1 and 2/3 of two sums (odd rows of
+// its first operand trade places with even rows of its second), the second
+// trades the upper half of the first operand with the lower half of the
+// second.
+__device__ __forceinline__ float sum_rows16_x4(float v0, float v1, float v2, float v3) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+  const float x = __uint_as_float(a[0]) + __uint_as_float(a[1]);   // rows 0,2: sum 0; rows 1,3: sum 1
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
+  const float y = __uint_as_float(b[0]) + __uint_as_float(b[1]);   // rows 0,2: sum 2; rows 1,3: sum 3
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Maximum over the four 16-lane rows (same pattern as sum_rows16).
 __device__ __forceinline__ float max_rows16(float v) {
   const uint32_t x = __float_as_uint(v);

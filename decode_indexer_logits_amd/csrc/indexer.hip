@@ -178,11 +178,10 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_bf16_e4m3_kernel(
         v = fmaf(wq.z, relu_bits(acc[mt][2]), v);
         v = fmaf(wq.w, relu_bits(acc[mt][3]), v);
       }
-      v = sum_rows16(v);
-      vj[j] = v;                  // every lane of column n holds token 16j + n
+      vj[j] = v;                  // this lane's part of token 16j + n
     }
     // lane 16g + n stores token 16g + n of the page: one coalesced 256-byte store
-    const float mine = g == 0 ? vj[0] : (g == 1 ? vj[1] : (g == 2 ? vj[2] : vj[3]));
+    const float mine = sum_rows16_x4(vj[0], vj[1], vj[2], vj[3]);
     const int tl = pi * kBlock + lane;
     if (tl <= lim_t) {
       const float val = (scale ? mine * page_scale(pi) : mine) + bs;
@@ -356,11 +355,11 @@ __global__ __launch_bounds__(256) void indexer_mp_kernel(
       for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) v = fmaf(wv[mt][i], relu_bits(acc[mt][i]), v);
-      v = sum_rows16(v);
       vj[j] = v;
     }
     // lane 16g + n stores token 16g + n when group g is one of this wave's
-    const float mine = g == 0 ? vj[0] : (g == 1 ? vj[1] : (g == 2 ? vj[2] : vj[3]));
+    // (the other groups' parts are zero)
+    const float mine = sum_rows16_x4(vj[0], vj[1], vj[2], vj[3]);
     if (g % WPP == sub && tl <= lim_t) {
       const float val = (scale ? mine * page_scale(pi) : mine) + bs;
       out[tl] = val;
@@ -505,9 +504,9 @@ __global__ __launch_bounds__(IdxCfg<P>::NT) void indexer_e4m3_kernel(
         v = fmaf(wq.z, relu_bits(acc[j][mt][2]), v);
         v = fmaf(wq.w, relu_bits(acc[j][mt][3]), v);
       }
-      vj[j] = sum_rows16(v);      // every lane of column n holds token 16j + n
+      vj[j] = v;                  // this lane's part of token 16j + n
     }
-    const float mine = g == 0 ? vj[0] : (g == 1 ? vj[1] : (g == 2 ? vj[2] : vj[3]));
+    const float mine = sum_rows16_x4(vj[0], vj[1], vj[2], vj[3]);
     const int tl = pi * kBlock + lane;
     if (tl <= lim_t) {
       const float val = (scale ? mine * page_scale(pi) : mine) + bs;
@@ -653,9 +652,9 @@ __global__ __launch_bounds__(256) void indexer_e4m3_mp_kernel(
       for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) v = fmaf(wv[mt][i], relu_bits(acc[mt][i]), v);
-      vj[j] = sum_rows16(v);
+      vj[j] = v;
     }
-    const float mine = g == 0 ? vj[0] : (g == 1 ? vj[1] : (g == 2 ? vj[2] : vj[3]));
+    const float mine = sum_rows16_x4(vj[0], vj[1], vj[2], vj[3]);
     if (g % WPP == sub && tl <= lim_t) {
       const float val = (scale ? mine * page_scale(pi) : mine) + bs;
       out[tl] = val;
