@@ -37,10 +37,10 @@ KV_ROW = 576
 # factors calibrated with a 512 MiB read and a 512 MiB fill in the same runs;
 # profiles/hbm_counters_mixed_128k.txt).  Reported only while the kernel's sources are the
 # ones the counters were taken on.
-INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.11e6,
+INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.10e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
-                   "sha256": "a11d86834d0c788e929ee3ede4d6b9236bb9f81a2027e714969c28519261ff8f"}
+                   "sha256": "f0615eeef80fce65422b0551c367020b61053eac218d0db09ab9f3dc6b1ab738"}
 
 
 def _indexer_traffic(workload: str, indexer_q: str):
