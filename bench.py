@@ -40,7 +40,7 @@ KV_ROW = 576
 INDEXER_TRAFFIC = {"workload": "mixed_128k", "indexer_q": "bf16", "bytes": 577.10e6,
                    "sources": ("decode_indexer_logits_amd/csrc/indexer.hip",
                                "decode_indexer_logits_amd/csrc/hs_common.h"),
-                   "sha256": "f0615eeef80fce65422b0551c367020b61053eac218d0db09ab9f3dc6b1ab738"}
+                   "sha256": "05902fcbcb3cfcac15f7c6e9c2e1736863f7ffbb8daddb142c1135b06605ad3b"}
 
 
 def _indexer_traffic(workload: str, indexer_q: str):

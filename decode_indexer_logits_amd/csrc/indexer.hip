@@ -9,7 +9,9 @@
 // [H heads x D] . [D x T tokens] runs on the matrix cores
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulation) with heads as the M dimension
 // and tokens as N, so that after the product each lane holds four heads of
-// one token and the ReLU / weighted head sum needs only two cross-lane adds.
+// one token and the ReLU / weighted head sum is lane-local but for one sum
+// over the wave's four 16-lane rows (three row-swap permutes per page cover
+// its four 16-token groups).
 // Keys are streamed once from HBM a 64-token page (64 x D bytes) at a time: for
 // each 16-token group every lane loads 16 bytes of its token from each 64-byte
 // half of the key row, so that a wave's load covers whole 64-byte halves of 16
