@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}   # dense matrix-core peaks
 KV_ROW = 576
 
 # HBM bytes per launch of the in-step indexer instance (with the top-K histogram epilogue)
@@ -120,6 +121,41 @@ def _time_launches(fn, n, torch, restore=None, flush=None, after=None):
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in ts]
     return sum(ms) / len(ms), ms
+
+
+def _indexer_roofline(wl, e4m3: bool, idx_bytes, idx_gbs, idx_sa_gbs, traffic, stage_ms):
+    """Roofline of the indexer as the step runs it: against HBM at one query position
+    (the keys stream once per product), against the matrix cores with several positions
+    (the same keys feed P times the products).  Algorithmic flops: 2 * heads * dim per
+    visible (position, token) pair."""
+    common = {"traffic": traffic,
+              "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE)",
+              "algorithmic_bytes": idx_bytes,
+              "algorithmic_note": "keys, key scales, block table, bias, queries and head "
+                                  "weights; the score writes are implementation traffic",
+              "avg_ms": round(stage_ms["indexer"], 4),
+              "standalone_avg_ms": round(stage_ms["indexer_standalone"], 4)}
+    if wl.P == 1:
+        return {"bound": "hbm",
+                "kernel": ("indexer_e4m3_kernel" if e4m3 else "indexer_bf16_e4m3_kernel")
+                          + " (in-step instance with the top-K histogram epilogue)",
+                "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(idx_gbs / HBM_PEAK_GBS, 4), **common,
+                "standalone_frac": round(idx_sa_gbs / HBM_PEAK_GBS, 4)}
+    P = wl.P
+    pairs = sum(P * int(t) - P * (P - 1) // 2 for t in wl.ctx_len)
+    flops = 2.0 * wl.H_idx * wl.D_idx * pairs
+    peak = MFMA_PEAK_TFLOPS["e4m3" if e4m3 else "bf16"]
+    tf = flops / (stage_ms["indexer"] / 1e3) / 1e12
+    tf_sa = flops / (stage_ms["indexer_standalone"] / 1e3) / 1e12
+    return {"bound": "mfma",
+            "kernel": ("indexer_e4m3_mp_kernel" if e4m3 else "indexer_mp_kernel")
+                      + " (in-step instance with the top-K histogram epilogue)",
+            "achieved": round(tf, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(tf / peak, 4), "algorithmic_flops": flops,
+            "hbm_achieved_GBs": round(idx_gbs, 1),
+            "hbm_frac": round(idx_gbs / HBM_PEAK_GBS, 4), **common,
+            "standalone_frac": round(tf_sa / peak, 4)}
 
 
 def _request_slice(wl, n: int):
@@ -674,18 +710,8 @@ def main():
                    "layer_copy_workgroups": a.layer_copy_wgs if a.layer_pipeline else None,
                    "layer_groups": (a.layer_groups or wl.L) if a.layer_pipeline else None,
                    "pipeline_copy_workgroups": a.copy_wgs if a.chunks > 1 else None},
-        "roofline": {"bound": "hbm",
-                     "kernel": ("indexer_e4m3_kernel" if e4m3 else "indexer_bf16_e4m3_kernel")
-                               + " (in-step instance with the top-K histogram epilogue)",
-                     "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE)",
-                     "algorithmic_bytes": idx_bytes,
-                     "algorithmic_note": "keys, key scales, block table, bias, queries and head "
-                                         "weights; the score writes are implementation traffic",
-                     "avg_ms": round(stage_ms["indexer"], 4),
-                     "standalone_avg_ms": round(stage_ms["indexer_standalone"], 4),
-                     "standalone_frac": round(idx_sa_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": _indexer_roofline(wl, e4m3, idx_bytes, idx_gbs, idx_sa_gbs, traffic,
+                                      stage_ms),
         "step_bandwidth": {
             "whole_step_GBs": round(hbm_phase_bytes / step_s / 1e9, 1),
             "whole_step_frac": round(hbm_phase_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
