@@ -427,7 +427,8 @@ hs_status hs_indexer_topk_select_resolve(const hs_batch* batch, hs_dtype q_t, in
                 (int)q_t);
   if (hs_status st = check_topk(d, K, topk, ws, ws_bytes)) return st;
   if (!row_ids || !faults || !counts)
-    return fail(HS_ERR_NULL, "resolve: row_ids, faults and counts are required");
+    return fail(HS_ERR_NULL,
+                "hs_indexer_topk_select_resolve: row_ids, faults and counts are required");
   hs::ResidencyArgs r;
   if (hs_status st = check_residency(d, K, res, &r)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
