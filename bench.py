@@ -158,6 +158,19 @@ def _indexer_roofline(wl, e4m3: bool, idx_bytes, idx_gbs, idx_sa_gbs, traffic, s
             "standalone_frac": round(tf_sa / peak, 4)}
 
 
+def _capture(fn, torch):
+    """fn's launches captured once as a HIP graph (on a side stream)."""
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def _request_slice(wl, n: int):
     """The first n requests of a workload, as a workload of their own (array views)."""
     import dataclasses
@@ -605,6 +618,15 @@ def main():
                             dtype=torch.uint8, device="cuda")
         run_sh = lambda: _lib.topk_sharded(ds.batch, wl.K, S, ds.scores, sh_out, sh_ws)
         stage_ms[f"topk_sharded_{S}"], _ = _time_launches(run_sh, a.kernel_reps, torch, None, flush)
+        # both selections as captured graphs too: eleven launches against four, so that
+        # eager timing also counts the host's launch latency
+        if not a.no_graph:
+            g_sh, g_tk = _capture(run_sh, torch), _capture(ds.run_topk, torch)
+            stage_ms[f"topk_sharded_{S}_graph"], _ = _time_launches(g_sh.replay, a.kernel_reps,
+                                                                   torch, None, flush)
+            stage_ms["topk_graph"], _ = _time_launches(g_tk.replay, a.kernel_reps, torch, None,
+                                                      flush)
+            g_sh.replay()
         ds.run_topk()
         torch.cuda.synchronize()
         assert torch.equal(sh_out, ds.topk), "sharded top-K differs from hs_topk"

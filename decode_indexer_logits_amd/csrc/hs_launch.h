@@ -45,6 +45,10 @@ uint32_t* topk_histograms(void* ws);
 hipError_t launch_topk_zero(const BatchDims& d, int K, void* ws, uint32_t** hist, hipStream_t s);
 hipError_t launch_topk_select(const BatchDims& d, int K, const float* scores, int32_t* topk,
                               void* ws, hipStream_t s);
+// The histogram pass of hs_topk alone, into a workspace whose histograms and
+// counters are zero (a selection leaves them so).
+hipError_t launch_topk_hist(const BatchDims& d, int K, const float* scores, void* ws,
+                            hipStream_t s);
 // The filter pass of the selection alone (the finalize then runs on its own or
 // fused with the resolve tables).
 hipError_t launch_topk_filter(const BatchDims& d, int K, const float* scores, void* ws,

@@ -259,6 +259,16 @@ hipError_t launch_topk(const BatchDims& d, int K, const float* scores, int32_t* 
   return launch_topk_select(d, K, scores, topk, ws, s);
 }
 
+hipError_t launch_topk_hist(const BatchDims& d, int K, const float* scores, void* ws,
+                            hipStream_t s) {
+  const int R = d.B * d.P;
+  TopkWs w = topk_ws(ws, R, d.T_stride, K);
+  const int nchunk = (d.T_stride + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL(topk_hist_kernel, dim3(nchunk, R), dim3(kScanNT), 0, s, d.ctx_len, d.P,
+                     d.T_stride, K, scores, w);
+  return hipGetLastError();
+}
+
 uint32_t* topk_histograms(void* ws) { return static_cast<uint32_t*>(ws); }
 
 hipError_t launch_topk_zero(const BatchDims& d, int K, void* ws, uint32_t** hist, hipStream_t s) {
