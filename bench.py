@@ -490,6 +490,8 @@ def main():
     ap.add_argument("--layer-copy-wgs", type=int, default=0,
                     help="workgroups of each layer's fault copy with --layer-pipeline "
                          "(0 = every compute unit)")
+    ap.add_argument("--attn-shards", type=int, default=0,
+                    help="also time the token-sharded attention of layer 0 with this many shards")
     ap.add_argument("--topk-shards", type=int, default=0,
                     help="also time the token-sharded top-K with this many shards (P = 1)")
     ap.add_argument("--cache-ops", action="store_true",
@@ -630,6 +632,35 @@ def main():
         ds.run_topk()
         torch.cuda.synchronize()
         assert torch.equal(sh_out, ds.topk), "sharded top-K differs from hs_topk"
+    if a.attn_shards and not a.no_graph:
+        # token-sharded attention of layer 0 over the step's own selection and rows (one
+        # whole step replayed first), as S shards' fragments merged by log-sum-exp,
+        # against the unsharded attention; both as captured graphs
+        from decode_indexer_logits_amd import _lib
+        S = a.attn_shards
+        restore()
+        step_fn()
+        torch.cuda.synchronize()
+        so = torch.empty((wl.B, wl.P, S, wl.Hq, 512), device="cuda")
+        sl = torch.empty((wl.B, wl.P, S, wl.Hq), device="cuda")
+        o2 = torch.empty_like(ds.out[0])
+        l2 = torch.empty_like(ds.lse[0])
+        sa_ws = torch.empty(_lib.mla_sharded_workspace_bytes(wl.B, wl.P, wl.K, S, wl.Hq),
+                            dtype=torch.uint8, device="cuda")
+        rs0 = None if ds.row_scale is None else ds.row_scale[0]
+        run_sa = lambda: _lib.sparse_mla_decode_sharded(
+            ds.batch, wl.K, S, wl.Hq, wl.q_dtype, ds.q[0], wl.kv_dtype, ds.pool[0], rs0, ds.topk,
+            ds.row_ids, wl.sm_scale, so, sl, o2, l2, sa_ws)
+        g_sa, g_at = _capture(run_sa, torch), _capture(lambda: ds.run_attention(0), torch)
+        stage_ms[f"attention_sharded_{S}_graph"], _ = _time_launches(g_sa.replay, a.kernel_reps,
+                                                                    torch, None, flush)
+        stage_ms["attention_graph"], _ = _time_launches(g_at.replay, a.kernel_reps, torch, None,
+                                                        flush)
+        torch.cuda.synchronize()
+        tol = 2e-2 if wl.kv_dtype == "e4m3" else 1e-5
+        err = ((o2 - ds.out[0]).abs().max() / ds.out[0].abs().max().clamp_min(1e-30)).item()
+        assert err <= tol, f"sharded attention differs from the unsharded one ({err:.2e})"
+        stage_ms[f"attention_sharded_{S}_max_rel_diff"] = err
     stage_ms["resolve_tables"], _ = _time_launches(ds.run_resolve_tables, a.kernel_reps, torch,
                                                    restore, flush)
 
