@@ -76,6 +76,9 @@ def _check_step(ds, wl, ost, s, rng, score_sample, oracle_topk_requests=(), attn
 
 @pytest.mark.timeout(600)
 def test_mixed_128k_full_size_graph():
+    """The full-size 128K step as a captured graph replay, against the oracle; then the
+    same step launched on its stream (how bench.py times it) from the same state gives
+    the same results bit for bit."""
     _say("mixed_128k full size (B=32, T=131072, K=2048), captured graph")
     from decode_indexer_logits_amd.device import DeviceStep
     wl = gen.mixed_128k()
@@ -97,6 +100,9 @@ def test_mixed_128k_full_size_graph():
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
+    replayed = {k: getattr(ds, k).clone() for k in ("topk", "row_ids", "faults", "counts")}
+    replayed["out"] = ds.out[0].clone()
+    replayed["lse"] = ds.lse[0].clone()
     _say("replayed; checking against the oracle")
     rng = np.random.default_rng(11)
     _, _, info = _check_step(ds, wl, gc.oracle_state(wl), 1, rng, score_sample=None)
@@ -106,6 +112,14 @@ def test_mixed_128k_full_size_graph():
     assert np.all(c[:, 1] >= 900)                     # pre-seeded: about half of the top-K hits
     assert np.all(c[:, 2] > 0) and np.all(c[:, 3] == c[:, 2])
     assert np.all(c[:, 0] + c[:, 1] + c[:, 2] == wl.K)
+    _say("the same step launched on the stream")
+    ds.restore(snap)
+    ds.run()
+    torch.cuda.synchronize()
+    launched = {k: getattr(ds, k) for k in ("topk", "row_ids", "faults", "counts")}
+    launched["out"], launched["lse"] = ds.out[0], ds.lse[0]
+    for k, v in replayed.items():
+        assert torch.equal(v, launched[k]), f"{k} differs between the replay and the launches"
     del ds, g
     _gc.collect()
     torch.cuda.empty_cache()
