@@ -174,7 +174,8 @@ hs_status hs_topk(const hs_batch* batch, int32_t K, const float* scores, int32_t
  * become S times as many short ones for the radix select.
  * One query position (batch->P == 1); 1 <= S <= 64 and T_stride a multiple of
  * 64*S; 1 <= K <= 8192; scores 16-byte aligned.  Workspace:
- * hs_topk_sharded_workspace_bytes(B, T_stride, K, S), 16-byte aligned. */
+ * hs_topk_sharded_workspace_bytes(B, T_stride, K, S), 16-byte aligned; its
+ * contents on entry do not matter (the call clears what it needs). */
 hs_status hs_topk_sharded(const hs_batch* batch, int32_t K, int32_t S, const float* scores,
                           int32_t* topk, void* ws, size_t ws_bytes, void* stream);
 size_t hs_topk_sharded_workspace_bytes(int32_t B, int32_t T_stride, int32_t K, int32_t S);
