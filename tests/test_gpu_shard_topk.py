@@ -39,8 +39,9 @@ def _run(S_rows, ctx, K, S):
     batch = _lib.make_batch(B, 1, Ts, d_ctx)
     out_s = torch.empty((B, 1, K), dtype=torch.int32, device="cuda")
     out_g = torch.empty_like(out_s)
-    ws_s = torch.empty(_lib.topk_sharded_workspace_bytes(B, Ts, K, S), dtype=torch.uint8,
-                       device="cuda")
+    # the call must not depend on what the workspace holds on entry
+    ws_s = torch.full((_lib.topk_sharded_workspace_bytes(B, Ts, K, S),), 0xA5, dtype=torch.uint8,
+                      device="cuda")
     ws_g = torch.empty(_lib.workspace_bytes(_lib.HS_OP_TOPK, B, 1, Ts, K), dtype=torch.uint8,
                        device="cuda")
     _lib.topk_sharded(batch, K, S, d_s, out_s, ws_s)
