@@ -573,8 +573,8 @@ def main():
     mode = "layers" if a.layer_pipeline else a.chunks
     # the headline times the step as launched on its stream (the host runs ahead of the
     # device, as in a decode loop); the same step captured as one HIP graph is timed
-    # beside it (measured 7-9 us slower per replay on this ROCm: the same kernels, so the
-    # difference lies in how the runtime sequences a graph's nodes)
+    # beside it (measured 7-9 us slower per replay on this ROCm; the kernels run back to
+    # back either way, the difference lies outside their span: the graph's launch)
     use_graph = a.graph and not a.no_graph
     eager_fn = lambda: step_eager(mode)
     graph = None if a.no_graph else capture(mode)
